@@ -1,0 +1,159 @@
+/*
+ * itl.h -- C ABI of the invariant token-logprob library (MI355X / gfx950).
+ *
+ * The library computes, on one GPU, each sampled token's log-probability
+ * from final hidden states (an LM-head contraction, a log-softmax over the
+ * vocabulary and a gather of the sampled token), the REINFORCE Zero loss on
+ * top of it, and the loss's gradient with respect to the hidden states and
+ * the head weights.
+ *
+ * Sources (web pages, cited by title and section):
+ *  [RZ] "vLLM says aligned kernels make asynchronous RL stable at lag 64",
+ *       section "REINFORCE Zero removes the mismatch first": the rollout
+ *       records each sampled token's logprob; the learner divides its own
+ *       probability by that record, at token level and without clipping;
+ *       the advantage is the response's reward minus its group's mean
+ *       reward; tokens are averaged within a response; plain REINFORCE.
+ *  [BC] "vLLM Train-Inference Consistency Release Notes", section
+ *       "Achieving Bitwise Consistency": kernel determinism, batch
+ *       independence and prefill/decode phase consistency; section
+ *       "Overview": bitwise-identical sampled-token logprobs (diff = 0)
+ *       between rollout and training.
+ *
+ * Determinism contract [BC]. For one build of this library (see
+ * itl_build_info) and one (vocab, d, dtype):
+ *  - each token's logprob and lse are bitwise identical whatever n_tok,
+ *    the token's row position, its batch-mates, the stream, or concurrent
+ *    load. A decode step (n_tok = 1) and a prefill over many tokens give the
+ *    same bits for the same hidden state: there is one code path.
+ *  - each resp_loss[i] is a bitwise function of response i's own
+ *    (logprob, rollout_logprob, advantage, T_i) only;
+ *  - loss, coef, advantages, dH and dW are run-to-run deterministic (no
+ *    atomics, no split-K, fixed reduction orders).
+ *
+ * Conventions shared by every entry point.
+ *  - All array pointers are DEVICE memory owned by the caller. The library
+ *    never allocates, frees or synchronises (itl_check_inputs excepted).
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream).
+ *  - Layouts are dense row-major: H [n_tok, d], W [vocab, d] (the usual
+ *    `lm_head.weight` layout), dH [n_tok, d], dW [vocab, d].
+ *  - dtype selects the element type of H and W: ITL_BF16 (bfloat16 bits)
+ *    or ITL_F32. Accumulation is always fp32. d must be a positive
+ *    multiple of 64 (otherwise ITL_ERR_UNSUPPORTED); vocab is any value in
+ *    [1, 2^31 - 256].
+ *  - n_tok == 0 (or n_resp / n_groups == 0) is a no-op returning ITL_OK.
+ *  - Host-detectable errors return before anything is launched.
+ *    A failed launch returns ITL_ERR_HIP; itl_last_error() describes it.
+ *  - Preconditions on device-resident values (0 <= tokens[t] < vocab,
+ *    increasing offsets, no empty response or group) are NOT checked by
+ *    the compute entry points; itl_check_inputs checks them on request.
+ *    Violating them gives unspecified values, never an out-of-bounds
+ *    access.
+ *  - No C++ exception crosses this interface; nothing aborts.
+ */
+#ifndef ITL_H_
+#define ITL_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum itl_status {
+  ITL_OK = 0,
+  ITL_ERR_INVALID_ARG = 1, /* null pointer, negative size, size overflow */
+  ITL_ERR_UNSUPPORTED = 2, /* a shape or dtype this build does not handle */
+  ITL_ERR_WORKSPACE = 3,   /* workspace missing or too small */
+  ITL_ERR_HIP = 4,         /* a HIP runtime call or launch failed */
+  ITL_ERR_BAD_INPUT = 5    /* itl_check_inputs found an invalid value */
+} itl_status;
+
+typedef enum itl_dtype { ITL_BF16 = 0, ITL_F32 = 1 } itl_dtype;
+
+/* Bytes of device workspace itl_lmhead_logprob needs for (n_tok, vocab).
+ * Returns 0 for n_tok == 0 and SIZE_MAX for invalid sizes. */
+size_t itl_lmhead_logprob_workspace_bytes(int64_t n_tok, int64_t vocab);
+
+/* Sampled-token logprob [RZ][BC]:
+ *   z[t, v]  = sum_k H[t, k] * W[v, k]           (fp32 accumulate, ascending k)
+ *   lse[t]   = log sum_v exp(z[t, v])
+ *   logprob[t] = z[t, tokens[t]] - lse[t]
+ * H [n_tok, d], W [vocab, d] of `dtype`; tokens int32 [n_tok] with
+ * 0 <= tokens[t] < vocab. Outputs fp32: logprob [n_tok]; lse [n_tok] may be
+ * NULL. workspace: >= itl_lmhead_logprob_workspace_bytes(n_tok, vocab)
+ * bytes, 256-byte aligned; its contents on entry do not matter.
+ * The logits never leave the chip: the contraction is fused with an online
+ * log-sum-exp over fixed vocabulary slices and the sampled-token gather.
+ * Because the sampled logit and the normaliser come from the same fp32
+ * accumulators, logprob <= 0 holds in fp32. */
+itl_status itl_lmhead_logprob(const void* H, const void* W, itl_dtype dtype,
+                              int64_t n_tok, int64_t d, int64_t vocab,
+                              const int32_t* tokens, float* logprob, float* lse,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Group-mean baseline [RZ]: advantages[i] = rewards[i] - mean of the
+ * rewards of i's group. Group g owns responses group_offsets[g] ..
+ * group_offsets[g+1]-1; group_offsets int32 [n_groups+1], starting at 0 and
+ * ending at n_resp. rewards and advantages fp32 [n_resp] (device offsets
+ * are clamped to [0, n_resp], so bad offsets cannot index out of bounds).
+ * One wavefront reduces one group; the summation order depends only on the
+ * group's size, so a group's advantages do not depend on where it sits in
+ * the batch. */
+itl_status itl_group_advantage(const float* rewards, const int32_t* group_offsets,
+                               int32_t n_groups, int32_t n_resp, float* advantages, void* stream);
+
+/* REINFORCE Zero loss [RZ]. Response i owns tokens resp_offsets[i] ..
+ * resp_offsets[i+1]-1 (int64 [n_resp+1], starting at 0, ending at n_tok),
+ * T_i of them. With ratio_t = exp(logprob[t] - rollout_logprob[t])
+ * (unclipped):
+ *   resp_loss[i] = -advantages[i] * (sum_{t in i} ratio_t) / T_i
+ *   loss[0]      = (1/n_resp) * sum_i resp_loss[i]     (ascending i)
+ *   coef[t]      = dloss/dlogprob[t] = -ratio_t * advantages[i] / (n_resp * T_i)
+ * All fp32. coef may be NULL. resp_loss[i] excludes 1/n_resp, so it is
+ * batch-invariant; loss and coef depend on n_resp by definition. */
+itl_status itl_reinforce_zero_loss(const float* logprob, const float* rollout_logprob,
+                                   const float* advantages, const int64_t* resp_offsets,
+                                   int32_t n_resp, int64_t n_tok,
+                                   float* resp_loss, float* loss, float* coef, void* stream);
+
+/* Bytes of device workspace itl_reinforce_zero_backward needs. */
+size_t itl_reinforce_zero_backward_workspace_bytes(int64_t n_tok, int64_t d, int64_t vocab);
+
+/* Gradient of the REINFORCE Zero loss through the head [RZ]:
+ *   G[t, v] = coef[t] * (onehot(tokens[t])[v] - exp(z[t, v] - lse[t]))
+ *   dH = G W   (fp32 [n_tok, d], overwritten)
+ *   dW = G^T H (fp32 [vocab, d], overwritten)
+ * lse and coef as produced by itl_lmhead_logprob / itl_reinforce_zero_loss.
+ * The logits are recomputed with the forward's contraction. dW's sum over
+ * tokens runs in ascending token order with no atomics. */
+itl_status itl_reinforce_zero_backward(const void* H, const void* W, itl_dtype dtype,
+                                       int64_t n_tok, int64_t d, int64_t vocab,
+                                       const int32_t* tokens, const float* lse, const float* coef,
+                                       float* dH, float* dW,
+                                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Opt-in validation of device-resident inputs (synchronises `stream`):
+ * 0 <= tokens[t] < vocab for all t (tokens may be NULL to skip), and, when
+ * resp_offsets is not NULL, resp_offsets[0] == 0, resp_offsets[n_resp] ==
+ * n_tok and T_i >= 1. Returns ITL_OK or ITL_ERR_BAD_INPUT. */
+itl_status itl_check_inputs(const int32_t* tokens, int64_t n_tok, int64_t vocab,
+                            const int64_t* resp_offsets, int32_t n_resp, void* stream);
+
+/* Static description of a status code. */
+const char* itl_status_string(itl_status status);
+
+/* Detail of the last error on the calling thread ("" if none). */
+const char* itl_last_error(void);
+
+/* Compile-time tile, slice and chunk constants and the target arch, so a
+ * rollout process and a learner process can assert they run the same
+ * arithmetic. */
+const char* itl_build_info(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ITL_H_ */

@@ -1,0 +1,239 @@
+"""Python binding of libitl.so: the invariant token-logprob library (MI355X).
+
+Thin ctypes marshalling over the C ABI declared in include/itl.h: every
+function checks tensor dtypes, devices and contiguity, allocates outputs and
+workspace with torch (PyTorch supplies device memory and the current stream
+only) and calls the library; every step of the computation runs in the
+library's HIP kernels. There is no fallback: if libitl.so is missing, importing
+this package fails.
+
+Entry points (same names as the C ABI without the ``itl_`` prefix):
+
+* ``lmhead_logprob(H, W, tokens) -> (logprob, lse)``
+* ``group_advantage(rewards, group_offsets) -> advantages``
+* ``reinforce_zero_loss(logprob, rollout_logprob, advantages, resp_offsets) -> (resp_loss, loss, coef)``
+* ``reinforce_zero_backward(H, W, tokens, lse, coef) -> (dH, dW)``
+* ``check_inputs(tokens, vocab, resp_offsets=None)``, ``build_info()``
+"""
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libitl.so")
+
+ITL_OK = 0
+ITL_BF16 = 0
+ITL_F32 = 1
+
+_c_void_p = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int32
+_size = ctypes.c_size_t
+
+
+class ItlError(RuntimeError):
+    """A non-OK status from the library."""
+
+    def __init__(self, status, message):
+        super().__init__(message)
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run `python -m invariant_token_logprobs_lm_amd.build` "
+            "(there is no fallback implementation)"
+        )
+    lib = ctypes.CDLL(LIB_PATH)
+    sig = {
+        "itl_lmhead_logprob_workspace_bytes": (_size, [_i64, _i64]),
+        "itl_lmhead_logprob": (ctypes.c_int, [_c_void_p, _c_void_p, ctypes.c_int, _i64, _i64, _i64, _c_void_p,
+                                              _c_void_p, _c_void_p, _c_void_p, _size, _c_void_p]),
+        "itl_group_advantage": (ctypes.c_int, [_c_void_p, _c_void_p, _i32, _i32, _c_void_p, _c_void_p]),
+        "itl_reinforce_zero_loss": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _i64,
+                                                   _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
+        "itl_reinforce_zero_backward_workspace_bytes": (_size, [_i64, _i64, _i64]),
+        "itl_reinforce_zero_backward": (ctypes.c_int, [_c_void_p, _c_void_p, ctypes.c_int, _i64, _i64, _i64,
+                                                       _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                                       _c_void_p, _size, _c_void_p]),
+        "itl_check_inputs": (ctypes.c_int, [_c_void_p, _i64, _i64, _c_void_p, _i32, _c_void_p]),
+        "itl_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "itl_last_error": (ctypes.c_char_p, []),
+        "itl_build_info": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+
+EXPORTS = (
+    "itl_lmhead_logprob_workspace_bytes",
+    "itl_lmhead_logprob",
+    "itl_group_advantage",
+    "itl_reinforce_zero_loss",
+    "itl_reinforce_zero_backward_workspace_bytes",
+    "itl_reinforce_zero_backward",
+    "itl_check_inputs",
+    "itl_status_string",
+    "itl_last_error",
+    "itl_build_info",
+)
+
+
+def build_info():
+    return lib.itl_build_info().decode()
+
+
+def _check(status):
+    if status != ITL_OK:
+        msg = lib.itl_status_string(status).decode()
+        detail = lib.itl_last_error().decode()
+        raise ItlError(status, f"{msg}: {detail}" if detail else msg)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t, name, dtypes, device=None, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}; expected one of {dtypes}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a HIP device, got {t.device}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got {t.dim()}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+_HEAD_DTYPES = {torch.bfloat16: ITL_BF16, torch.float32: ITL_F32}
+
+
+def lmhead_workspace_bytes(n_tok, vocab):
+    return int(lib.itl_lmhead_logprob_workspace_bytes(n_tok, vocab))
+
+
+def lmhead_logprob(H, W, tokens, *, logprob=None, lse=None, workspace=None, want_lse=True):
+    """Sampled-token logprob and log-normaliser of every row of H.
+
+    H [n_tok, d] and W [vocab, d] (bf16 or fp32, same dtype), tokens int32
+    [n_tok]. Returns (logprob fp32 [n_tok], lse fp32 [n_tok] or None).
+    """
+    _need(H, "H", tuple(_HEAD_DTYPES), ndim=2)
+    _need(W, "W", (H.dtype,), device=H.device, ndim=2)
+    _need(tokens, "tokens", (torch.int32,), device=H.device, ndim=1)
+    n_tok, d = H.shape
+    vocab = W.shape[0]
+    if W.shape[1] != d or tokens.shape[0] != n_tok:
+        raise ValueError(f"shape mismatch: H {tuple(H.shape)}, W {tuple(W.shape)}, tokens {tuple(tokens.shape)}")
+    if logprob is None:
+        logprob = torch.empty(n_tok, dtype=torch.float32, device=H.device)
+    if lse is None and want_lse:
+        lse = torch.empty(n_tok, dtype=torch.float32, device=H.device)
+    for name, t in (("logprob", logprob), ("lse", lse)):
+        if t is not None:
+            _need(t, name, (torch.float32,), device=H.device, ndim=1)
+            if t.shape[0] != n_tok:
+                raise ValueError(f"{name} must have {n_tok} elements")
+    need = lmhead_workspace_bytes(n_tok, vocab)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=H.device)
+    _need(workspace, "workspace", (torch.uint8,), device=H.device)
+    _check(lib.itl_lmhead_logprob(_ptr(H), _ptr(W), _HEAD_DTYPES[H.dtype], n_tok, d, vocab, _ptr(tokens),
+                                  _ptr(logprob), _ptr(lse), _ptr(workspace), workspace.numel(),
+                                  _stream(H.device)))
+    return logprob, lse
+
+
+def group_advantage(rewards, group_offsets, *, advantages=None):
+    """advantages[i] = rewards[i] - mean reward of i's group (fp32)."""
+    _need(rewards, "rewards", (torch.float32,), ndim=1)
+    _need(group_offsets, "group_offsets", (torch.int32,), device=rewards.device, ndim=1)
+    n_resp = rewards.shape[0]
+    n_groups = group_offsets.shape[0] - 1
+    if n_groups < 0:
+        raise ValueError("group_offsets needs at least one element")
+    if advantages is None:
+        advantages = torch.empty_like(rewards)
+    _need(advantages, "advantages", (torch.float32,), device=rewards.device, ndim=1)
+    _check(lib.itl_group_advantage(_ptr(rewards), _ptr(group_offsets), n_groups, n_resp, _ptr(advantages),
+                                   _stream(rewards.device)))
+    return advantages
+
+
+def reinforce_zero_loss(logprob, rollout_logprob, advantages, resp_offsets, *, want_coef=True):
+    """(resp_loss fp32 [N], loss fp32 [1], coef fp32 [n_tok] or None)."""
+    _need(logprob, "logprob", (torch.float32,), ndim=1)
+    dev = logprob.device
+    _need(rollout_logprob, "rollout_logprob", (torch.float32,), device=dev, ndim=1)
+    _need(advantages, "advantages", (torch.float32,), device=dev, ndim=1)
+    _need(resp_offsets, "resp_offsets", (torch.int64,), device=dev, ndim=1)
+    n_tok = logprob.shape[0]
+    n_resp = advantages.shape[0]
+    if rollout_logprob.shape[0] != n_tok or resp_offsets.shape[0] != n_resp + 1:
+        raise ValueError("shape mismatch between logprobs, advantages and resp_offsets")
+    resp_loss = torch.empty(n_resp, dtype=torch.float32, device=dev)
+    loss = torch.empty(1, dtype=torch.float32, device=dev)
+    coef = torch.empty(n_tok, dtype=torch.float32, device=dev) if want_coef else None
+    _check(lib.itl_reinforce_zero_loss(_ptr(logprob), _ptr(rollout_logprob), _ptr(advantages), _ptr(resp_offsets),
+                                       n_resp, n_tok, _ptr(resp_loss), _ptr(loss), _ptr(coef), _stream(dev)))
+    return resp_loss, loss, coef
+
+
+def backward_workspace_bytes(n_tok, d, vocab):
+    return int(lib.itl_reinforce_zero_backward_workspace_bytes(n_tok, d, vocab))
+
+
+def reinforce_zero_backward(H, W, tokens, lse, coef, *, dH=None, dW=None, workspace=None):
+    """(dH fp32 [n_tok, d], dW fp32 [vocab, d]) of the REINFORCE Zero loss."""
+    _need(H, "H", tuple(_HEAD_DTYPES), ndim=2)
+    dev = H.device
+    _need(W, "W", (H.dtype,), device=dev, ndim=2)
+    _need(tokens, "tokens", (torch.int32,), device=dev, ndim=1)
+    _need(lse, "lse", (torch.float32,), device=dev, ndim=1)
+    _need(coef, "coef", (torch.float32,), device=dev, ndim=1)
+    n_tok, d = H.shape
+    vocab = W.shape[0]
+    if W.shape[1] != d or tokens.shape[0] != n_tok or lse.shape[0] != n_tok or coef.shape[0] != n_tok:
+        raise ValueError("shape mismatch between H, W, tokens, lse and coef")
+    if dH is None:
+        dH = torch.empty((n_tok, d), dtype=torch.float32, device=dev)
+    if dW is None:
+        dW = torch.empty((vocab, d), dtype=torch.float32, device=dev)
+    _need(dH, "dH", (torch.float32,), device=dev, ndim=2)
+    _need(dW, "dW", (torch.float32,), device=dev, ndim=2)
+    need = backward_workspace_bytes(n_tok, d, vocab)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", (torch.uint8,), device=dev)
+    _check(lib.itl_reinforce_zero_backward(_ptr(H), _ptr(W), _HEAD_DTYPES[H.dtype], n_tok, d, vocab, _ptr(tokens),
+                                           _ptr(lse), _ptr(coef), _ptr(dH), _ptr(dW), _ptr(workspace),
+                                           workspace.numel(), _stream(dev)))
+    return dH, dW
+
+
+def check_inputs(tokens, vocab, resp_offsets=None):
+    """Validate device-resident token ids and offsets (synchronises)."""
+    _need(tokens, "tokens", (torch.int32,), ndim=1)
+    n_resp = 0
+    if resp_offsets is not None:
+        _need(resp_offsets, "resp_offsets", (torch.int64,), device=tokens.device, ndim=1)
+        n_resp = resp_offsets.shape[0] - 1
+    _check(lib.itl_check_inputs(_ptr(tokens), tokens.shape[0], vocab, _ptr(resp_offsets), n_resp,
+                                _stream(tokens.device)))

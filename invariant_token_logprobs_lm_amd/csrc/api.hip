@@ -1,0 +1,173 @@
+// C ABI of the library (declared in include/itl.h): argument validation,
+// workspace sizing, status codes. Every host-detectable error returns before
+// anything is enqueued; nothing here allocates, frees or synchronises except
+// itl_check_inputs.
+
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "itl.h"
+#include "itl_config.h"
+#include "itl_launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+itl_status fail(itl_status s, const char* what) {
+  g_last_error = what;
+  return s;
+}
+
+itl_status hip_fail(hipError_t e, const char* where) {
+  g_last_error = std::string(where) + ": " + hipGetErrorName(e) + " (" + hipGetErrorString(e) + ")";
+  return ITL_ERR_HIP;
+}
+
+constexpr int64_t kMaxTok = (int64_t)INT32_MAX - itl::kBT;
+constexpr int64_t kMaxVocab = (int64_t)INT32_MAX - itl::kBV;
+
+int elem_size(itl_dtype dt) { return dt == ITL_BF16 ? 2 : 4; }
+
+// Shared shape checks of the head entry points.
+itl_status check_head(itl_dtype dtype, int64_t n_tok, int64_t d, int64_t vocab) {
+  if (n_tok < 0 || d <= 0 || vocab <= 0) return fail(ITL_ERR_INVALID_ARG, "n_tok must be >= 0, d and vocab > 0");
+  if (dtype != ITL_BF16 && dtype != ITL_F32) return fail(ITL_ERR_UNSUPPORTED, "dtype must be ITL_BF16 or ITL_F32");
+  if (d % itl::kDMultiple != 0) return fail(ITL_ERR_UNSUPPORTED, "d must be a multiple of 64");
+  if (n_tok > kMaxTok) return fail(ITL_ERR_UNSUPPORTED, "n_tok too large for one call");
+  if (vocab > kMaxVocab) return fail(ITL_ERR_UNSUPPORTED, "vocab too large");
+  // a 256-row operand block must be addressable with 32-bit buffer offsets
+  if (d * elem_size(dtype) * (int64_t)itl::kBT >= ((int64_t)1 << 31)) return fail(ITL_ERR_UNSUPPORTED, "d too large");
+  const int64_t grid = itl::ceil_div(n_tok, itl::kBT) * itl::n_slices(vocab);
+  if (grid > INT32_MAX) return fail(ITL_ERR_UNSUPPORTED, "problem too large for one launch");
+  return ITL_OK;
+}
+
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255) != 0; }
+
+}  // namespace
+
+extern "C" {
+
+size_t itl_lmhead_logprob_workspace_bytes(int64_t n_tok, int64_t vocab) {
+  if (n_tok < 0 || vocab <= 0 || n_tok > kMaxTok || vocab > kMaxVocab) return SIZE_MAX;
+  return itl::lmhead_workspace_bytes(n_tok, vocab);
+}
+
+itl_status itl_lmhead_logprob(const void* H, const void* W, itl_dtype dtype, int64_t n_tok, int64_t d, int64_t vocab,
+                              const int32_t* tokens, float* logprob, float* lse, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  itl_status st = check_head(dtype, n_tok, d, vocab);
+  if (st != ITL_OK) return st;
+  if (n_tok == 0) return ITL_OK;
+  if (!H || !W || !tokens || !logprob) return fail(ITL_ERR_INVALID_ARG, "null H, W, tokens or logprob");
+  if (!workspace || workspace_bytes < itl::lmhead_workspace_bytes(n_tok, vocab))
+    return fail(ITL_ERR_WORKSPACE, "workspace missing or smaller than itl_lmhead_logprob_workspace_bytes()");
+  if (misaligned(workspace)) return fail(ITL_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  hipError_t e = itl::launch_lmhead_logprob(H, W, (int)dtype, (int)n_tok, (int)d, (int)vocab, tokens, logprob, lse,
+                                            workspace, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ITL_OK : hip_fail(e, "itl_lmhead_logprob");
+}
+
+itl_status itl_group_advantage(const float* rewards, const int32_t* group_offsets, int32_t n_groups, int32_t n_resp,
+                               float* advantages, void* stream) {
+  g_last_error.clear();
+  if (n_groups < 0 || n_resp < 0) return fail(ITL_ERR_INVALID_ARG, "n_groups and n_resp must be >= 0");
+  if (n_groups == 0 || n_resp == 0) return ITL_OK;
+  if (!rewards || !group_offsets || !advantages) return fail(ITL_ERR_INVALID_ARG, "null rewards, offsets or output");
+  hipError_t e = itl::launch_group_advantage(rewards, group_offsets, n_groups, n_resp, advantages,
+                                             static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ITL_OK : hip_fail(e, "itl_group_advantage");
+}
+
+itl_status itl_reinforce_zero_loss(const float* logprob, const float* rollout_logprob, const float* advantages,
+                                   const int64_t* resp_offsets, int32_t n_resp, int64_t n_tok, float* resp_loss,
+                                   float* loss, float* coef, void* stream) {
+  g_last_error.clear();
+  if (n_resp < 0 || n_tok < 0) return fail(ITL_ERR_INVALID_ARG, "n_resp and n_tok must be >= 0");
+  if (n_resp == 0) return ITL_OK;
+  if (!resp_offsets || !advantages || !resp_loss || !loss)
+    return fail(ITL_ERR_INVALID_ARG, "null offsets, advantages or outputs");
+  if (n_tok > 0 && (!logprob || !rollout_logprob)) return fail(ITL_ERR_INVALID_ARG, "null logprob arrays");
+  hipError_t e = itl::launch_reinforce_zero_loss(logprob, rollout_logprob, advantages, resp_offsets, n_resp, n_tok,
+                                                 resp_loss, loss, coef, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ITL_OK : hip_fail(e, "itl_reinforce_zero_loss");
+}
+
+size_t itl_reinforce_zero_backward_workspace_bytes(int64_t n_tok, int64_t d, int64_t vocab) {
+  if (n_tok < 0 || d <= 0 || vocab <= 0 || n_tok > kMaxTok || vocab > kMaxVocab) return SIZE_MAX;
+  return itl::backward_workspace_bytes(n_tok, d, vocab);
+}
+
+itl_status itl_reinforce_zero_backward(const void* H, const void* W, itl_dtype dtype, int64_t n_tok, int64_t d,
+                                       int64_t vocab, const int32_t* tokens, const float* lse, const float* coef,
+                                       float* dH, float* dW, void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  itl_status st = check_head(dtype, n_tok, d, vocab);
+  if (st != ITL_OK) return st;
+  if (!W || !dW) return fail(ITL_ERR_INVALID_ARG, "null W or dW");
+  if (n_tok > 0 && (!H || !tokens || !lse || !coef || !dH))
+    return fail(ITL_ERR_INVALID_ARG, "null H, tokens, lse, coef or dH");
+  const size_t need = itl::backward_workspace_bytes(n_tok, d, vocab);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(ITL_ERR_WORKSPACE, "workspace missing or smaller than itl_reinforce_zero_backward_workspace_bytes()");
+  if (need > 0 && misaligned(workspace)) return fail(ITL_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  hipError_t e = itl::launch_reinforce_zero_backward(H, W, (int)dtype, (int)n_tok, (int)d, (int)vocab, tokens, lse,
+                                                     coef, dH, dW, workspace, static_cast<hipStream_t>(stream));
+  if (e == hipErrorNotSupported) return fail(ITL_ERR_UNSUPPORTED, "backward not available for this shape");
+  return e == hipSuccess ? ITL_OK : hip_fail(e, "itl_reinforce_zero_backward");
+}
+
+itl_status itl_check_inputs(const int32_t* tokens, int64_t n_tok, int64_t vocab, const int64_t* resp_offsets,
+                            int32_t n_resp, void* stream) {
+  g_last_error.clear();
+  if (n_tok < 0 || n_resp < 0 || vocab <= 0 || vocab > kMaxVocab)
+    return fail(ITL_ERR_INVALID_ARG, "bad sizes");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int* flag = nullptr;
+  hipError_t e = hipMalloc(&flag, sizeof(int));
+  if (e != hipSuccess) return hip_fail(e, "itl_check_inputs");
+  int host = 0;
+  e = hipMemcpyAsync(flag, &host, sizeof(int), hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = itl::launch_check_inputs(tokens, n_tok, (int)vocab, resp_offsets, n_resp, flag, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(&host, flag, sizeof(int), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  hipFree(flag);
+  if (e != hipSuccess) return hip_fail(e, "itl_check_inputs");
+  if (host == 1) return fail(ITL_ERR_BAD_INPUT, "a token id is outside [0, vocab)");
+  if (host == 2) return fail(ITL_ERR_BAD_INPUT, "response offsets must start at 0, end at n_tok and increase");
+  return ITL_OK;
+}
+
+const char* itl_status_string(itl_status status) {
+  switch (status) {
+    case ITL_OK: return "ITL_OK";
+    case ITL_ERR_INVALID_ARG: return "ITL_ERR_INVALID_ARG: invalid argument";
+    case ITL_ERR_UNSUPPORTED: return "ITL_ERR_UNSUPPORTED: shape or dtype not supported by this build";
+    case ITL_ERR_WORKSPACE: return "ITL_ERR_WORKSPACE: workspace missing, too small or misaligned";
+    case ITL_ERR_HIP: return "ITL_ERR_HIP: HIP runtime error";
+    case ITL_ERR_BAD_INPUT: return "ITL_ERR_BAD_INPUT: invalid device-resident input";
+  }
+  return "unknown itl_status";
+}
+
+const char* itl_last_error(void) { return g_last_error.c_str(); }
+
+const char* itl_build_info(void) {
+  static const std::string info = [] {
+    char buf[512];
+    snprintf(buf, sizeof buf,
+             "itl 0.1 arch=gfx950 threads=%d token_block=%d vocab_tile=%d k_step_bytes=%d tiles_per_slice=%d "
+             "slice_rows=%d mfma_bf16=32x32x16 mfma_f32=32x32x2 loss_threads=%d mean_threads=%d",
+             itl::kThreads, itl::kBT, itl::kBV, itl::kRowBytes, itl::kTilesPerSlice, itl::kSliceRows,
+             itl::kLossThreads, itl::kMeanThreads);
+    return std::string(buf);
+  }();
+  return info.c_str();
+}
+
+}  // extern "C"

@@ -1,0 +1,39 @@
+// Host-side launchers of the library's kernels. Arguments are already
+// validated by the C ABI layer (api.hip); these only size grids and launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace itl {
+
+// Workspace layout of the forward: per-(slice, token) partial (max, sumexp)
+// pairs, then the per-token sampled logit.
+size_t lmhead_workspace_bytes(long long n_tok, long long vocab);
+
+hipError_t launch_lmhead_logprob(const void* H, const void* W, int dtype, int n_tok, int d, int vocab,
+                                 const int32_t* tokens, float* logprob, float* lse, void* workspace,
+                                 hipStream_t stream);
+
+hipError_t launch_group_advantage(const float* rewards, const int32_t* group_offsets, int n_groups,
+                                  int n_resp, float* advantages, hipStream_t stream);
+
+hipError_t launch_reinforce_zero_loss(const float* logprob, const float* rollout_logprob,
+                                      const float* advantages, const int64_t* resp_offsets, int n_resp,
+                                      long long n_tok, float* resp_loss, float* loss, float* coef,
+                                      hipStream_t stream);
+
+size_t backward_workspace_bytes(long long n_tok, long long d, long long vocab);
+
+hipError_t launch_reinforce_zero_backward(const void* H, const void* W, int dtype, int n_tok, int d, int vocab,
+                                          const int32_t* tokens, const float* lse, const float* coef,
+                                          float* dH, float* dW, void* workspace, hipStream_t stream);
+
+// Device-side validation; writes a nonzero value to *flag on a violation.
+hipError_t launch_check_inputs(const int32_t* tokens, long long n_tok, int vocab, const int64_t* resp_offsets,
+                               int n_resp, int* flag, hipStream_t stream);
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+}  // namespace itl

@@ -1,0 +1,138 @@
+"""Host-side tests of the C ABI (no GPU needed, no kernel launched).
+
+The library loads, exports every function include/itl.h declares, and
+rejects invalid arguments with the documented status before touching the
+device. Also static checks on the sources: no float atomics in kernels, and
+the oracle and the product path never import each other.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "itl.h")
+CSRC = os.path.join(ROOT, "invariant_token_logprobs_lm_amd", "csrc")
+LIB = os.path.join(ROOT, "invariant_token_logprobs_lm_amd", "libitl.so")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(itl_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libitl.so is not built (run python -m invariant_token_logprobs_lm_amd.build)")
+    import invariant_token_logprobs_lm_amd as itl
+
+    return itl.lib
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for n in ["itl_lmhead_logprob", "itl_group_advantage", "itl_reinforce_zero_loss",
+              "itl_reinforce_zero_backward", "itl_check_inputs", "itl_build_info"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared():
+        assert hasattr(lib, name), name
+    import invariant_token_logprobs_lm_amd as itl
+
+    assert sorted(itl.EXPORTS) == _declared()
+
+
+def test_build_info_and_status_strings(lib):
+    info = lib.itl_build_info().decode()
+    assert "gfx950" in info and "tiles_per_slice=16" in info
+    for s in range(6):
+        assert lib.itl_status_string(s)
+
+
+def _lmhead(lib, H=1, W=1, dtype=0, n=4, d=64, V=10, y=1, lp=1, ws=256, wsb=1 << 20):
+    v = ctypes.c_void_p
+    return lib.itl_lmhead_logprob(v(H), v(W), dtype, n, d, V, v(y), v(lp), None, v(ws), wsb, None)
+
+
+def test_lmhead_argument_validation(lib):
+    assert _lmhead(lib, n=-1) == INVALID
+    assert _lmhead(lib, d=0) == INVALID
+    assert _lmhead(lib, V=0) == INVALID
+    assert _lmhead(lib, d=96) == UNSUPPORTED
+    assert _lmhead(lib, dtype=7) == UNSUPPORTED
+    assert _lmhead(lib, H=0) == INVALID
+    assert _lmhead(lib, y=0) == INVALID
+    assert _lmhead(lib, ws=0) == WORKSPACE
+    assert _lmhead(lib, wsb=16) == WORKSPACE
+    assert _lmhead(lib, ws=255) == WORKSPACE
+    assert "workspace" in lib.itl_last_error().decode()
+    assert _lmhead(lib, n=0, H=0, W=0, y=0, lp=0, ws=0) == OK  # empty call is a no-op
+    assert lib.itl_last_error().decode() == ""
+
+
+def test_workspace_sizes(lib):
+    assert lib.itl_lmhead_logprob_workspace_bytes(0, 100) == 0
+    n, V = 1000, 151936
+    slices = -(-(-(-V // 256)) // 16)
+    want = -(-slices * n * 8 // 256) * 256 + -(-n * 4 // 256) * 256
+    assert lib.itl_lmhead_logprob_workspace_bytes(n, V) == want
+    assert lib.itl_lmhead_logprob_workspace_bytes(-1, V) == ctypes.c_size_t(-1).value
+
+
+def test_loss_and_advantage_validation(lib):
+    v = ctypes.c_void_p
+    assert lib.itl_group_advantage(v(1), v(1), -1, 4, v(1), None) == INVALID
+    assert lib.itl_group_advantage(None, v(1), 2, 4, v(1), None) == INVALID
+    assert lib.itl_group_advantage(None, None, 0, 0, None, None) == OK
+    assert lib.itl_reinforce_zero_loss(v(1), v(1), v(1), v(1), -1, 4, v(1), v(1), None, None) == INVALID
+    assert lib.itl_reinforce_zero_loss(v(1), v(1), v(1), None, 2, 4, v(1), v(1), None, None) == INVALID
+    assert lib.itl_reinforce_zero_loss(None, None, None, None, 0, 0, None, None, None, None) == OK
+    assert lib.itl_reinforce_zero_backward(v(1), v(1), 0, 4, 100, 10, v(1), v(1), v(1), v(1), v(1),
+                                           v(256), 1 << 30, None) == UNSUPPORTED
+    assert lib.itl_reinforce_zero_backward(v(1), None, 0, 4, 64, 10, v(1), v(1), v(1), v(1), v(1),
+                                           v(256), 1 << 30, None) == INVALID
+
+
+def test_binding_rejects_bad_tensors():
+    import torch
+    import invariant_token_logprobs_lm_amd as itl
+
+    H = torch.zeros(4, 64, dtype=torch.bfloat16)
+    W = torch.zeros(10, 64, dtype=torch.bfloat16)
+    y = torch.zeros(4, dtype=torch.int32)
+    with pytest.raises(ValueError):  # CPU tensors are not device memory
+        itl.lmhead_logprob(H, W, y)
+    with pytest.raises(ValueError):
+        itl.lmhead_logprob(H.float(), W, y)
+    with pytest.raises(TypeError):
+        itl.group_advantage([1.0], torch.zeros(2, dtype=torch.int32))
+
+
+def _sources(folder, exts):
+    for dp, _, fs in os.walk(folder):
+        for f in fs:
+            if f.endswith(exts):
+                yield os.path.join(dp, f)
+
+
+def test_no_float_atomics_in_kernels():
+    for p in _sources(CSRC, (".hip", ".h")):
+        text = open(p).read()
+        assert not re.search(r"\batomic\w*\s*\(", text), p
+        assert "unsafeAtomic" not in text, p
+
+
+def test_oracle_and_product_are_independent():
+    pkg = os.path.join(ROOT, "invariant_token_logprobs_lm_amd")
+    for p in _sources(pkg, (".py", ".hip", ".h", ".cpp")):
+        assert not re.search(r"\boracle\b", open(p).read()), p
+    for p in _sources(os.path.join(ROOT, "oracle"), (".py", ".c", ".h")):
+        text = open(p).read()
+        assert "invariant_token_logprobs_lm_amd" not in text and "import synth" not in text, p
