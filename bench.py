@@ -118,7 +118,7 @@ def time_steps(step, steps, warmup):
     return total_ms / steps, sum(head_ms) / steps, wall
 
 
-def cpu_baseline(wl, n_sample=1024):
+def cpu_baseline(wl, n_sample=6144):
     """The float64 oracle timed on a seeded sample of the same workload's
     tokens (forward + loss over the sampled tokens)."""
     import numpy as np
