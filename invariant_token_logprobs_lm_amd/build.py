@@ -30,9 +30,6 @@ DEVICE_FLAGS = [
     "-Wall",
     "-Wno-unused-function",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # MFMA results in the VGPR form: with the accumulators handled by the
-    # register allocator this avoids scratch spills around the epilogues.
-    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-I", os.path.join(ROOT, "include"),
     "-I", CSRC,
 ]

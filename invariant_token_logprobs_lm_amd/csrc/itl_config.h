@@ -10,14 +10,17 @@
 // of itl_build_info().
 #pragma once
 
+#include <hip/hip_runtime.h>
+
 namespace itl {
 
 constexpr int kThreads = 256;        // 4 wavefronts of 64 lanes
 constexpr int kBT = 256;             // tokens per block (MFMA B operand)
 constexpr int kBV = 256;             // vocabulary rows per tile (MFMA A operand)
-constexpr int kRowBytes = 128;       // bytes of one operand row per K step (64 bf16 / 32 fp32)
-constexpr int kTilesPerSlice = 16;   // vocabulary tiles per slice (4096 rows)
-constexpr int kSliceRows = kBV * kTilesPerSlice;
+constexpr int kStepBytes = 64;       // bytes of one operand row per K step (32 bf16 / 16 fp32)
+constexpr int kStages = 4;           // LDS ring depth of the K-step pipeline
+constexpr int kTilesPerSlice = 16;   // at most this many vocabulary tiles per slice
+constexpr int kSuperBand = 32;       // token blocks walked together, slice by slice (workgroup order)
 constexpr int kDMultiple = 64;       // d must be a multiple of this
 
 constexpr int kLossThreads = 256;    // threads per response in the loss kernel
@@ -27,5 +30,11 @@ inline long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
 
 inline int n_vocab_tiles(long long vocab) { return (int)ceil_div(vocab, kBV); }
 inline int n_slices(long long vocab) { return (int)ceil_div(n_vocab_tiles(vocab), kTilesPerSlice); }
+
+// Slice s covers vocabulary tiles [slice_tile(s), slice_tile(s + 1)): the
+// tiles are split as evenly as possible, so a slice holds
+// floor(n_vt / S) or ceil(n_vt / S) <= kTilesPerSlice tiles. This is a pure
+// function of the vocabulary size.
+__host__ __device__ inline int slice_tile(int s, int n_vt, int S) { return (int)(((long long)s * n_vt) / S); }
 
 }  // namespace itl

@@ -40,7 +40,8 @@ namespace itl {
 
 namespace {
 
-// One 16-byte fragment per lane and operand feeds one K sub-step.
+// One 16-byte fragment per lane and operand feeds one K sub-step. first()
+// starts a tile's accumulation from zero (the MFMA takes a zero C operand).
 template <int kDtype>
 struct Mma;
 
@@ -49,6 +50,10 @@ struct Mma<0> {  // bf16: 8 elements per lane, k16 per instruction
   __device__ static __forceinline__ void step(floatx16& acc, uint4 a, uint4 b) {
     acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                   __builtin_bit_cast(bf16x8_t, b), acc, 0, 0, 0);
+  }
+  __device__ static __forceinline__ void first(floatx16& acc, uint4 a, uint4 b) {
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                  __builtin_bit_cast(bf16x8_t, b), floatx16{}, 0, 0, 0);
   }
 };
 
@@ -60,48 +65,168 @@ struct Mma<1> {  // fp32: 4 elements per lane; instruction j takes element j (k2
     acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.z), __uint_as_float(b.z), acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.w), __uint_as_float(b.w), acc, 0, 0, 0);
   }
+  __device__ static __forceinline__ void first(floatx16& acc, uint4 a, uint4 b) {
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.x), __uint_as_float(b.x), floatx16{}, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.y), __uint_as_float(b.y), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.z), __uint_as_float(b.z), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.w), __uint_as_float(b.w), acc, 0, 0, 0);
+  }
 };
 
-// LDS tile: 256 rows x 8 chunks of 16 bytes. Chunk c of row r is stored at
-// position c ^ (r & 7), so the eight lanes that read one logical chunk of
-// eight consecutive rows hit eight different bank groups.
-constexpr int kTileChunks = kBV * (kRowBytes / 16);
+// LDS ring: kStages stages, each holding one K step of the W tile (256 rows)
+// and of the H block (256 rows), 64 bytes per row = 4 chunks of 16 bytes.
+// Chunk c of row r sits at position c ^ swz(r). For the MFMA operand reads
+// (lanes 0-31 take rows r0..r0+31 at one chunk, lanes 32-63 the next chunk)
+// any 8 or 16 consecutive lanes then touch distinct 16-byte bank groups.
+constexpr int kRowChunks = kStepBytes / 16;      // 4
+constexpr int kTileChunks = kBV * kRowChunks;    // 1024 chunks per operand per stage
+constexpr int kStageChunks = 2 * kTileChunks;    // W tile, then H block
+constexpr int kStageBytes = kStageChunks * 16;   // 32 KiB
+constexpr int kDmaRows = 64 * 16 / kStepBytes;   // rows one wavefront-wide 16-byte load fills (16)
+static_assert(kBV == kBT && kThreads == 256 && kStages == 4, "the loop below assumes this geometry");
+static_assert(kBV == 4 * 4 * kDmaRows, "4 wavefronts x 4 loads cover a 256-row tile");
+
+__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+
+// Raw buffer resource words over [base, base + nbytes) (gfx9-family raw
+// buffer: no stride, no swizzle, 32-bit data format). Loads whose row lies
+// past nbytes return zeros and touch no memory.
+__device__ __forceinline__ int4v rsrc_words(const void* base, uint32_t nbytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return int4v{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xffffu), (int)nbytes, 0x00020000};
+}
+
+// One wavefront-wide 16-byte-per-lane load from global memory straight into
+// LDS: lane i's 16 bytes land at LDS address lds + 16 i. The LDS base goes
+// through M0 (saved and restored here, so the compiler's view of M0 holds).
+// The load is issued from inline assembly so the compiler does not order
+// every later LDS read behind it; the K-step loop waits for it explicitly
+// (vmcnt) before the barrier that publishes the stage.
+__device__ __forceinline__ void dma16(int4v rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %4\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, %3 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(rsrc), "s"(soff), "s"(lds)
+      : "memory");
+}
+
+// Wait until at most kInFlight of this wavefront's LDS loads are pending and
+// all of its LDS reads are done, then meet the other wavefronts.
+template <int kInFlight>
+__device__ __forceinline__ void wait_and_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kInFlight) : "memory");
+}
+
+// Copy accumulator register i of a 32x32 MFMA result into a VGPR at this
+// point of the program. Issued from inline assembly so that each copy
+// happens where it is used; left to the compiler, all 256 copies are made at
+// once at the end of the K loop and spill.
+__device__ __forceinline__ float acc_read(const floatx16& v, int i) {
+  float r;
+  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(r) : "a"(v[i]));
+  return r;
+}
+
+// The accumulator copies above are invisible to the compiler's hazard
+// tracking: give the last MFMA (16 passes) the wait states a VALU read of
+// its result needs before the first copy.
+__device__ __forceinline__ void mfma_result_wait() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
+
+// z[8 b3 + 4 b2 + 2 b1 + b0] by a tree of selects.
+__device__ __forceinline__ float select16(const floatx16& z, bool b0, bool b1, bool b2, bool b3) {
+  const float a0 = b0 ? z[1] : z[0], a1 = b0 ? z[3] : z[2], a2 = b0 ? z[5] : z[4], a3 = b0 ? z[7] : z[6];
+  const float a4 = b0 ? z[9] : z[8], a5 = b0 ? z[11] : z[10], a6 = b0 ? z[13] : z[12], a7 = b0 ? z[15] : z[14];
+  const float c0 = b1 ? a1 : a0, c1 = b1 ? a3 : a2, c2 = b1 ? a5 : a4, c3 = b1 ? a7 : a6;
+  const float e0 = b2 ? c1 : c0, e1 = b2 ? c3 : c2;
+  return b3 ? e1 : e0;
+}
 
 template <int kDtype>
 __global__ __launch_bounds__(kThreads, 1) void lmhead_lse_partial_kernel(
     const char* __restrict__ H, const char* __restrict__ W, const int32_t* __restrict__ tokens, int n_tok,
-    int row_bytes, int vocab, int n_slices, float2* __restrict__ part, float* __restrict__ zy_out) {
-  __shared__ uint4 lds[2][2][kTileChunks];  // [stage][0 = W tile, 1 = H block][chunk]
+    int row_bytes, int vocab, int n_tb, int n_slices, float2* __restrict__ part, float* __restrict__ zy_out) {
+  __shared__ uint4 smem[kStages * kStageChunks];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wv = wave & 1;   // which 128 vocabulary rows of the tile
   const int wt = wave >> 1;  // which 128 tokens of the block
   const int half = lane >> 5;
   const int col = lane & 31;
 
-  const int slice = blockIdx.x % n_slices;
-  const int tb = blockIdx.x / n_slices;
-  const int t0 = tb * kBT;
+  // Workgroup order: super-bands of kSuperBand token blocks, walked slice by
+  // slice with the token block fastest. Workgroups are dispatched to the 8
+  // XCDs round-robin, so the 32 workgroups an XCD runs at once hold 4 token
+  // blocks x 8 slices (each H block read by 8 of them, each W tile by 4,
+  // through the XCD's L2), and all XCDs walk the same slices at the same
+  // time (W shared through the Infinity Cache). The order changes only which
+  // workgroup runs when, never any arithmetic.
+  const int S = n_slices;
+  const int b = blockIdx.x;
+  const int band = b / (kSuperBand * S);
+  const int tb_first = band * kSuperBand;
+  const int nb = min(kSuperBand, n_tb - tb_first);
+  const int rem = b - band * kSuperBand * S;
+  const int slice = rem / nb;
+  const int t0 = (tb_first + rem % nb) * kBT;
   const int n_vt = (vocab + kBV - 1) / kBV;
-  const int tile_begin = slice * kTilesPerSlice;
-  const int tile_end = min(tile_begin + kTilesPerSlice, n_vt);
-  const int nks = row_bytes / kRowBytes;
+  const int tile_begin = slice_tile(slice, n_vt, S);
+  const int tile_end = slice_tile(slice + 1, n_vt, S);
+  const int nks = row_bytes / kStepBytes;
 
-  // Loader mapping: thread -> (row = tid/8 + 32 j, chunk = tid % 8), j < 8.
-  const int ld_row = tid >> 3;
-  const int ld_col = tid & 7;
-  const int st_base = ld_row * 8 + (ld_col ^ (ld_row & 7));
-  uint32_t voff[8];
+  // Loader: wavefront w fills rows 64 w .. 64 w + 63 of both operands with
+  // four loads each; lane i fetches row (i / 4) of a 16-row group, logical
+  // chunk (i % 4) ^ swz(row), so that it lands in its swizzled position.
+  const int lr = lane >> 2;
+  const int lc = (lane & 3) ^ swz(lr);
+  uint32_t voff[4];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) voff[j] = (uint32_t)(ld_row + 32 * j) * (uint32_t)row_bytes + ld_col * 16;
+  for (int j = 0; j < 4; ++j) voff[j] = (uint32_t)(wave * 64 + j * kDmaRows + lr) * (uint32_t)row_bytes + lc * 16;
+  const uint32_t lds_wave =
+      (uint32_t)(size_t)((__attribute__((address_space(3))) uint4*)smem) + wave * 64 * kStepBytes;
+  const int4v hr = rsrc_words(H + (size_t)t0 * row_bytes, (uint32_t)min(kBT, n_tok - t0) * row_bytes);
 
-  const int h_rows = min(kBT, n_tok - t0);
-  const __amdgpu_buffer_rsrc_t hr = make_rsrc(H + (size_t)t0 * row_bytes, (uint32_t)h_rows * row_bytes);
+  int is_tile = tile_begin, is_ks = 0, is_g = 0;  // next K step to load
   auto w_rsrc = [&](int tile) {
     const int v0 = tile * kBV;
-    return make_rsrc(W + (size_t)v0 * row_bytes, (uint32_t)min(kBV, vocab - v0) * row_bytes);
+    return rsrc_words(W + (size_t)v0 * row_bytes, (uint32_t)min(kBV, vocab - v0) * row_bytes);
+  };
+  int4v wr = w_rsrc(is_tile);
+  auto issue = [&]() {
+    const uint32_t soff = (uint32_t)is_ks * kStepBytes;
+    const uint32_t m = lds_wave + (uint32_t)(is_g & (kStages - 1)) * kStageBytes;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dma16(wr, voff[j], soff, m + j * 1024);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dma16(hr, voff[j], soff, m + kTileChunks * 16 + j * 1024);
+    ++is_g;
+    if (++is_ks == nks) {
+      is_ks = 0;
+      if (++is_tile < tile_end) wr = w_rsrc(is_tile);
+    }
+  };
+
+  // MFMA operand reads: lane l takes row (l mod 32) of each 32-row block at
+  // logical chunk 2 kk + l / 32 (kk = K sub-step); swz(row) = swz(l mod 32).
+  int a_off[2], b_off[2];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    const int pc = (2 * kk + half) ^ swz(col);
+    a_off[kk] = (wv * 128 + col) * kRowChunks + pc;
+    b_off[kk] = kTileChunks + (wt * 128 + col) * kRowChunks + pc;
+  }
+  auto read_frags = [&](int stage, int kk, uint4 (&A)[4], uint4 (&B)[4]) {
+    const uint4* st = smem + stage * kStageChunks;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) A[m] = st[a_off[kk] + m * 32 * kRowChunks];
+#pragma unroll
+    for (int n = 0; n < 4; ++n) B[n] = st[b_off[kk] + n * 32 * kRowChunks];
   };
 
   int y[4];
@@ -117,128 +242,104 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_lse_partial_kernel(
     found[bn] = false;
   }
 
-  // Prologue: the slice's first K step into stage 0.
-  __amdgpu_buffer_rsrc_t wr = w_rsrc(tile_begin);
-  uint4 ra[8], rb[8];
+  // Prologue: kStages K steps in flight, then publish step 0. Loads past
+  // the workgroup's last step re-read a valid step into a stage nobody
+  // reads again, so every wavefront always has exactly three steps in
+  // flight when it waits: one wait count, no tail cases.
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    ra[j] = buffer_load16(wr, voff[j], 0);
-    rb[j] = buffer_load16(hr, voff[j], 0);
-  }
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    lds[0][0][st_base + 256 * j] = ra[j];
-    lds[0][1][st_base + 256 * j] = rb[j];
-  }
-  __syncthreads();
+  for (int p = 0; p < kStages; ++p) issue();
+  wait_and_barrier<8 * (kStages - 1)>();
 
-  int stage = 0;
-  for (int tile = tile_begin; tile < tile_end; ++tile) {
-    const bool more_tiles = tile + 1 < tile_end;
-    const __amdgpu_buffer_rsrc_t wr_next = more_tiles ? w_rsrc(tile + 1) : wr;
+  uint4 fa[4], fb[4];  // sub-step 0 operands of the current K step
+  read_frags(0, 0, fa, fb);
 
-    floatx16 acc[4][4];
-#pragma unroll
-    for (int bm = 0; bm < 4; ++bm)
-#pragma unroll
-      for (int bn = 0; bn < 4; ++bn) acc[bm][bn] = floatx16{};
-
-    for (int ks = 0; ks < nks; ++ks) {
-      // Prefetch the next K step (the next tile's first after the last one).
-      // The loads and stores are unconditional: after the slice's last step
-      // they re-read a valid step into the idle stage, which nobody reads.
-      const bool in_tile = ks + 1 < nks;
-      const __amdgpu_buffer_rsrc_t wn = in_tile ? wr : wr_next;
-      const uint32_t koff = in_tile ? (uint32_t)(ks + 1) * kRowBytes : 0u;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        ra[j] = buffer_load16(wn, voff[j] + koff, 0);
-        rb[j] = buffer_load16(hr, voff[j] + koff, 0);
-      }
-
-      // 4 K sub-steps of 32 bytes per row from the current stage.
-      const uint4* sw = lds[stage][0];
-      const uint4* sh = lds[stage][1];
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int pc = (kk * 2 + half) ^ (lane & 7);
-        uint4 a[4], b[4];
-#pragma unroll
-        for (int bm = 0; bm < 4; ++bm) a[bm] = sw[(wv * 128 + bm * 32 + col) * 8 + pc];
-#pragma unroll
-        for (int bn = 0; bn < 4; ++bn) b[bn] = sh[(wt * 128 + bn * 32 + col) * 8 + pc];
-#pragma unroll
-        for (int bm = 0; bm < 4; ++bm)
-#pragma unroll
-          for (int bn = 0; bn < 4; ++bn) Mma<kDtype>::step(acc[bm][bn], a[bm], b[bn]);
-      }
-
-      {
-        uint4* dw = lds[stage ^ 1][0];
-        uint4* dh = lds[stage ^ 1][1];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          dw[st_base + 256 * j] = ra[j];
-          dh[st_base + 256 * j] = rb[j];
-        }
-      }
-      __syncthreads();
-      stage ^= 1;
-    }
-
-    // Tile epilogue: fold this tile's logits into the running state, one
-    // token column (64 logits per lane) at a time.
-    const int vw = tile * kBV + wv * 128;  // first vocabulary row of this wavefront
-    const bool partial = tile * kBV + kBV > vocab;
-#pragma unroll
-    for (int bn = 0; bn < 4; ++bn) {
-      float z[64];
+  // One K step g: sub-step 0 from fa/fb (read during the previous step),
+  // sub-step 1 from stage g; between them, publish step g + 1, refill stage
+  // g with step g + 4 and read step g + 1's sub-step 0 operands.
+  auto k_step = [&](floatx16 (&acc)[4][4], int g, bool first) {
+    const int stage = g & (kStages - 1);
+    uint4 ga[4], gb[4];
+    read_frags(stage, 1, ga, gb);
+    if (first) {
 #pragma unroll
       for (int bm = 0; bm < 4; ++bm)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) z[bm * 16 + i] = acc[bm][bn][i];
+        for (int bn = 0; bn < 4; ++bn) Mma<kDtype>::first(acc[bm][bn], fa[bm], fb[bn]);
+    } else {
+#pragma unroll
+      for (int bm = 0; bm < 4; ++bm)
+#pragma unroll
+        for (int bn = 0; bn < 4; ++bn) Mma<kDtype>::step(acc[bm][bn], fa[bm], fb[bn]);
+    }
+    wait_and_barrier<8 * (kStages - 2)>();
+    issue();
+    read_frags((g + 1) & (kStages - 1), 0, fa, fb);
+#pragma unroll
+    for (int bm = 0; bm < 4; ++bm)
+#pragma unroll
+      for (int bn = 0; bn < 4; ++bn) Mma<kDtype>::step(acc[bm][bn], ga[bm], gb[bn]);
+  };
 
-      // Register q = 16 bm + i of this lane holds vocabulary row
-      // vw + 32 bm + 8 (i / 4) + 4 half + (i % 4).
-      const int o = y[bn] - vw;
-      if (o >= 0 && o < 128) {
-        const int r = o & 31;
-        if (((r >> 2) & 1) == half) {
-          const int idx = (o >> 5) * 16 + ((r >> 3) << 2) + (r & 3);
-          float v = 0.0f;
+  int g = 0;
+  for (int tile = tile_begin; tile < tile_end; ++tile) {
+    floatx16 acc[4][4];
+    k_step(acc, g++, true);
+    for (int ks = 1; ks < nks; ++ks) k_step(acc, g++, false);
+
+    // Tile epilogue: fold this tile's logits into the running state, one
+    // token column (64 logits per lane) at a time. Register q = 16 bm + i of
+    // a lane holds vocabulary row vw + 32 bm + 8 (i / 4) + 4 half + (i % 4).
+    // Each lane folds its 16 logits of one 32x32 block at a time into the
+    // running (max, sum of exp) of that token column. The logits are copied
+    // out of the matrix-core registers 16 at a time, where they are used
+    // (acc_read), so the epilogue needs few VGPRs next to the 256
+    // accumulators. The sampled logit is picked with a select tree keyed on
+    // the bits of its row, without a branch.
+    const int vw = tile * kBV + wv * 128;
+    const bool partial = tile * kBV + kBV > vocab;  // only the vocabulary's last tile
+    mfma_result_wait();
 #pragma unroll
-          for (int q = 0; q < 64; ++q) v = (q == idx) ? z[q] : v;
-          zy[bn] = v;
-          found[bn] = true;
+    for (int bn = 0; bn < 4; ++bn) {
+      const int o = y[bn] - vw;  // sampled row relative to this wavefront's 128 rows
+      // Register i of a lane holds row 32 bm + 8 (i / 4) + 4 half + (i % 4):
+      // bits 0, 1, 3, 4 of the row pick i, bit 2 picks the lane half.
+      const bool b0 = (o & 1) != 0, b1 = (o & 2) != 0, b2 = (o & 8) != 0, b3 = (o & 16) != 0;
+      const bool mine = (unsigned)o < 128u && ((o >> 2) & 1) == half;
+#pragma unroll
+      for (int bm = 0; bm < 4; ++bm) {
+        floatx16 z;  // a vector, not an array: it must stay in registers
+#pragma unroll
+        for (int i = 0; i < 16; ++i) z[i] = acc_read(acc[bm][bn], i);
+        if (partial) {
+          const int lim = vocab - (vw + bm * 32 + 4 * half);  // rows at or past this offset do not exist
+#pragma unroll
+          for (int i = 0; i < 16; ++i) z[i] = (8 * (i >> 2) + (i & 3) >= lim) ? -INFINITY : z[i];
         }
-      }
-      if (partial) {
+        const float pick = select16(z, b0, b1, b2, b3);
+        const bool here = mine && (o >> 5) == bm;
+        zy[bn] = here ? pick : zy[bn];
+        found[bn] = found[bn] || here;
+
+        float bmax = z[0];
 #pragma unroll
-        for (int q = 0; q < 64; ++q) {
-          const int v = vw + (q >> 4) * 32 + ((q & 15) >> 2) * 8 + half * 4 + (q & 3);
-          if (v >= vocab) z[q] = -INFINITY;
+        for (int i = 1; i < 16; ++i) bmax = fmaxf(bmax, z[i]);
+        const float mnew = fmaxf(mrun[bn], bmax);
+        // A lane whose rows so far are all absent has mnew = -inf; it then
+        // scales by exp2(-inf) = 0 around 0 and keeps (m, s) = (-inf, 0).
+        const float mref = mnew == -INFINITY ? 0.0f : mnew;
+        // (z - m) is exactly 0 for the running maximum, so its term is
+        // exactly 1 and stays 1 (later rescales by exp2(0)): the final sum
+        // is >= 1 and logprob <= 0 holds in fp32.
+        float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) {
+          s0 += fast_exp2((z[i] - mref) * kLog2e);
+          s1 += fast_exp2((z[i + 1] - mref) * kLog2e);
         }
-      }
-      float tmax = -INFINITY;
-#pragma unroll
-      for (int q = 0; q < 64; ++q) tmax = fmaxf(tmax, z[q]);
-      const float mnew = fmaxf(mrun[bn], tmax);
-      if (mnew != -INFINITY) {
-        // (z - m) is exactly 0 for the maximum, so its term is exactly 1
-        // and the final sum is >= 1: logprob <= 0 holds in fp32.
-        float s[4];
-#pragma unroll
-        for (int bm = 0; bm < 4; ++bm) {
-          s[bm] = 0.0f;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) s[bm] += fast_exp2((z[bm * 16 + i] - mnew) * kLog2e);
-        }
-        const float tsum = (s[0] + s[1]) + (s[2] + s[3]);
-        srun[bn] = srun[bn] * fast_exp2((mrun[bn] - mnew) * kLog2e) + tsum;
+        srun[bn] = srun[bn] * fast_exp2((mrun[bn] - mref) * kLog2e) + (s0 + s1);
         mrun[bn] = mnew;
       }
     }
-    wr = wr_next;
   }
 
   // Slice end. Lanes l and l^32 hold the same tokens (different rows).
@@ -249,8 +350,11 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_lse_partial_kernel(
     lse_merge(mrun[bn], srun[bn], m2, s2);
     if (found[bn]) zy_out[t0 + wt * 128 + bn * 32 + col] = zy[bn];
   }
-  // Wavefronts wv = 0 and wv = 1 hold the same tokens; merge through LDS.
-  float2* xch = reinterpret_cast<float2*>(&lds[0][0][0]);
+  // Wavefronts wv = 0 and wv = 1 hold the same tokens; merge through LDS
+  // once every wavefront is done with the ring.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  float2* xch = reinterpret_cast<float2*>(smem);
   if (wv == 1 && half == 0) {
 #pragma unroll
     for (int bn = 0; bn < 4; ++bn) xch[wt * 128 + bn * 32 + col] = make_float2(mrun[bn], srun[bn]);
@@ -307,10 +411,10 @@ hipError_t launch_lmhead_logprob(const void* H, const void* W, int dtype, int n_
   const dim3 grid((unsigned)ntb * (unsigned)S);
   if (dtype == 0)
     hipLaunchKernelGGL(lmhead_lse_partial_kernel<0>, grid, dim3(kThreads), 0, stream, static_cast<const char*>(H),
-                       static_cast<const char*>(W), tokens, n_tok, row_bytes, vocab, S, part, zy);
+                       static_cast<const char*>(W), tokens, n_tok, row_bytes, vocab, ntb, S, part, zy);
   else
     hipLaunchKernelGGL(lmhead_lse_partial_kernel<1>, grid, dim3(kThreads), 0, stream, static_cast<const char*>(H),
-                       static_cast<const char*>(W), tokens, n_tok, row_bytes, vocab, S, part, zy);
+                       static_cast<const char*>(W), tokens, n_tok, row_bytes, vocab, ntb, S, part, zy);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(lse_combine_kernel, dim3((unsigned)ceil_div(n_tok, 256)), dim3(256), 0, stream, part, zy, n_tok,
