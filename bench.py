@@ -173,6 +173,9 @@ def main():
     ap.add_argument("--workload", default="qwen3-4b-head")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="before timing, run one plain 1 GiB device-to-device copy: the reference whose "
+                         "FETCH_SIZE / WRITE_SIZE counters calibrate the HBM traffic figures")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: the path is built and timed on a single MI355X "
@@ -185,6 +188,13 @@ def main():
 
     device = torch.device("cuda:0")
     wl = WORKLOADS[args.workload]
+    if args.copy_probe:
+        src = torch.ones(1 << 30, dtype=torch.uint8, device=device)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] copy probe: 1073741824 bytes read, 1073741824 bytes written")
+        del src, dst
     s = setup_forward(wl, device)
     n_tok = s["lay"].n_tok
     ms_step, ms_head, wall = time_steps(lambda ev: forward_step(s, ev), args.steps, args.warmup)

@@ -161,10 +161,10 @@ const char* itl_build_info(void) {
   static const std::string info = [] {
     char buf[512];
     snprintf(buf, sizeof buf,
-             "itl 0.2 arch=gfx950 threads=%d token_block=%d vocab_tile=%d k_step_bytes=%d stages=%d "
+             "itl 0.2 arch=gfx950 threads=%d token_block=%d vocab_tile=%d k_step_bytes=%d w_slots=%d h_slots=%d "
              "tiles_per_slice=%d slices=balanced mfma_bf16=32x32x16 mfma_f32=32x32x2 loss_threads=%d "
              "mean_threads=%d",
-             itl::kThreads, itl::kBT, itl::kBV, itl::kStepBytes, itl::kStages, itl::kTilesPerSlice,
+             itl::kThreads, itl::kBT, itl::kBV, itl::kStepBytes, itl::kWSlots, itl::kHSlots, itl::kTilesPerSlice,
              itl::kLossThreads, itl::kMeanThreads);
     return std::string(buf);
   }();

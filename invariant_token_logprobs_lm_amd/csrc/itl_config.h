@@ -17,8 +17,9 @@ namespace itl {
 constexpr int kThreads = 256;        // 4 wavefronts of 64 lanes
 constexpr int kBT = 256;             // tokens per block (MFMA B operand)
 constexpr int kBV = 256;             // vocabulary rows per tile (MFMA A operand)
-constexpr int kStepBytes = 64;       // bytes of one operand row per K step (32 bf16 / 16 fp32)
-constexpr int kStages = 4;           // LDS ring depth of the K-step pipeline
+constexpr int kStepBytes = 128;      // bytes of one operand row per K step (64 bf16 / 32 fp32)
+constexpr int kWSlots = 3;           // LDS slots of the W-tile ring (loads two K steps ahead)
+constexpr int kHSlots = 2;           // LDS slots of the H-block ring (loads one K step ahead)
 constexpr int kTilesPerSlice = 16;   // at most this many vocabulary tiles per slice
 constexpr int kSuperBand = 32;       // token blocks walked together, slice by slice (workgroup order)
 constexpr int kDMultiple = 64;       // d must be a multiple of this
