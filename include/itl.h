@@ -118,16 +118,28 @@ itl_status itl_reinforce_zero_loss(const float* logprob, const float* rollout_lo
                                    int32_t n_resp, int64_t n_tok,
                                    float* resp_loss, float* loss, float* coef, void* stream);
 
-/* Bytes of device workspace itl_reinforce_zero_backward needs. */
-size_t itl_reinforce_zero_backward_workspace_bytes(int64_t n_tok, int64_t d, int64_t vocab);
+/* Bytes of device workspace itl_reinforce_zero_backward needs for (n_tok,
+ * d, vocab, dtype). Returns SIZE_MAX for invalid sizes or dtype. */
+size_t itl_reinforce_zero_backward_workspace_bytes(int64_t n_tok, int64_t d, int64_t vocab, itl_dtype dtype);
 
 /* Gradient of the REINFORCE Zero loss through the head [RZ]:
  *   G[t, v] = coef[t] * (onehot(tokens[t])[v] - exp(z[t, v] - lse[t]))
  *   dH = G W   (fp32 [n_tok, d], overwritten)
- *   dW = G^T H (fp32 [vocab, d], overwritten)
- * lse and coef as produced by itl_lmhead_logprob / itl_reinforce_zero_loss.
- * The logits are recomputed with the forward's contraction. dW's sum over
- * tokens runs in ascending token order with no atomics. */
+ *   dW = G^T H (fp32 [vocab, d], overwritten; all zeros when n_tok == 0)
+ * H, W, tokens as for itl_lmhead_logprob; lse and coef fp32 [n_tok] as
+ * produced by itl_lmhead_logprob / itl_reinforce_zero_loss. The logits are
+ * recomputed with the forward's contraction. The sampled-token entries
+ * (+coef[t]) are applied exactly in fp32; the dense part -coef[t] p[t, v] is
+ * rounded to the head's dtype before its contractions (for bf16 heads a
+ * relative error of about 2^-9 per element). Every sum has a fixed order and
+ * there are no atomics, so dH and dW are run-to-run deterministic; dW's sum
+ * over tokens runs in ascending token order in chunks of a fixed size.
+ * workspace: >= itl_reinforce_zero_backward_workspace_bytes(n_tok, d,
+ * vocab, dtype) bytes, 256-byte aligned (it holds transposed copies of W
+ * and of a chunk of H, two copies of the chunk's dense dlogits, and a sort
+ * of the token ids). vocab above about 2.1e6 returns ITL_ERR_UNSUPPORTED.
+ * Out-of-range token ids give unspecified values, never an out-of-bounds
+ * access. */
 itl_status itl_reinforce_zero_backward(const void* H, const void* W, itl_dtype dtype,
                                        int64_t n_tok, int64_t d, int64_t vocab,
                                        const int32_t* tokens, const float* lse, const float* coef,

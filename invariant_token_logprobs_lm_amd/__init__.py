@@ -56,7 +56,7 @@ def _load():
         "itl_group_advantage": (ctypes.c_int, [_c_void_p, _c_void_p, _i32, _i32, _c_void_p, _c_void_p]),
         "itl_reinforce_zero_loss": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _i64,
                                                    _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
-        "itl_reinforce_zero_backward_workspace_bytes": (_size, [_i64, _i64, _i64]),
+        "itl_reinforce_zero_backward_workspace_bytes": (_size, [_i64, _i64, _i64, ctypes.c_int]),
         "itl_reinforce_zero_backward": (ctypes.c_int, [_c_void_p, _c_void_p, ctypes.c_int, _i64, _i64, _i64,
                                                        _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                                        _c_void_p, _size, _c_void_p]),
@@ -196,8 +196,8 @@ def reinforce_zero_loss(logprob, rollout_logprob, advantages, resp_offsets, *, w
     return resp_loss, loss, coef
 
 
-def backward_workspace_bytes(n_tok, d, vocab):
-    return int(lib.itl_reinforce_zero_backward_workspace_bytes(n_tok, d, vocab))
+def backward_workspace_bytes(n_tok, d, vocab, dtype=torch.bfloat16):
+    return int(lib.itl_reinforce_zero_backward_workspace_bytes(n_tok, d, vocab, _HEAD_DTYPES[dtype]))
 
 
 def reinforce_zero_backward(H, W, tokens, lse, coef, *, dH=None, dW=None, workspace=None):
@@ -218,7 +218,7 @@ def reinforce_zero_backward(H, W, tokens, lse, coef, *, dH=None, dW=None, worksp
         dW = torch.empty((vocab, d), dtype=torch.float32, device=dev)
     _need(dH, "dH", (torch.float32,), device=dev, ndim=2)
     _need(dW, "dW", (torch.float32,), device=dev, ndim=2)
-    need = backward_workspace_bytes(n_tok, d, vocab)
+    need = backward_workspace_bytes(n_tok, d, vocab, H.dtype)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     _need(workspace, "workspace", (torch.uint8,), device=dev)

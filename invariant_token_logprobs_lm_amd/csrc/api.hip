@@ -98,9 +98,10 @@ itl_status itl_reinforce_zero_loss(const float* logprob, const float* rollout_lo
   return e == hipSuccess ? ITL_OK : hip_fail(e, "itl_reinforce_zero_loss");
 }
 
-size_t itl_reinforce_zero_backward_workspace_bytes(int64_t n_tok, int64_t d, int64_t vocab) {
+size_t itl_reinforce_zero_backward_workspace_bytes(int64_t n_tok, int64_t d, int64_t vocab, itl_dtype dtype) {
   if (n_tok < 0 || d <= 0 || vocab <= 0 || n_tok > kMaxTok || vocab > kMaxVocab) return SIZE_MAX;
-  return itl::backward_workspace_bytes(n_tok, d, vocab);
+  if (dtype != ITL_BF16 && dtype != ITL_F32) return SIZE_MAX;
+  return itl::backward_workspace_bytes(n_tok, d, vocab, (int)dtype);
 }
 
 itl_status itl_reinforce_zero_backward(const void* H, const void* W, itl_dtype dtype, int64_t n_tok, int64_t d,
@@ -112,13 +113,13 @@ itl_status itl_reinforce_zero_backward(const void* H, const void* W, itl_dtype d
   if (!W || !dW) return fail(ITL_ERR_INVALID_ARG, "null W or dW");
   if (n_tok > 0 && (!H || !tokens || !lse || !coef || !dH))
     return fail(ITL_ERR_INVALID_ARG, "null H, tokens, lse, coef or dH");
-  const size_t need = itl::backward_workspace_bytes(n_tok, d, vocab);
+  if (vocab > itl::kBwdMaxVocab) return fail(ITL_ERR_UNSUPPORTED, "vocab too large for the backward");
+  const size_t need = itl::backward_workspace_bytes(n_tok, d, vocab, (int)dtype);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(ITL_ERR_WORKSPACE, "workspace missing or smaller than itl_reinforce_zero_backward_workspace_bytes()");
   if (need > 0 && misaligned(workspace)) return fail(ITL_ERR_WORKSPACE, "workspace must be 256-byte aligned");
   hipError_t e = itl::launch_reinforce_zero_backward(H, W, (int)dtype, (int)n_tok, (int)d, (int)vocab, tokens, lse,
                                                      coef, dH, dW, workspace, static_cast<hipStream_t>(stream));
-  if (e == hipErrorNotSupported) return fail(ITL_ERR_UNSUPPORTED, "backward not available for this shape");
   return e == hipSuccess ? ITL_OK : hip_fail(e, "itl_reinforce_zero_backward");
 }
 

@@ -1,14 +1,440 @@
-// Gradient of the REINFORCE Zero loss through the LM head (not yet built:
-// the entry point reports ITL_ERR_UNSUPPORTED).
+// Gradient of the REINFORCE Zero loss through the LM head ("vLLM says aligned
+// kernels make asynchronous RL stable at lag 64", section "REINFORCE Zero
+// removes the mismatch first": plain REINFORCE, so dloss/dlogprob_t = coef[t]
+// and the logprob is a log-softmax of the head's logits):
+//
+//   G[t, v] = dloss/dz[t, v] = coef[t] (onehot(y_t)[v] - p[t, v]),
+//   p[t, v] = exp(z[t, v] - lse[t])
+//   dH = G W,   dW = G^T H
+//
+// G splits into a dense part -coef[t] p[t, v] and one sampled entry
+// +coef[t] per token. The sampled entries are applied exactly, in fp32:
+//   dH[t]    += coef[t] W[y_t]
+//   dW[v]    += sum over tokens t with y_t = v, ascending t, of coef[t] H[t]
+// The dense part g[t, v] = -coef[t] p[t, v] is formed in the head's dtype
+// (bf16 for bf16 heads: the MFMA operand) and contracted on the matrix cores
+// with the tile engine, one chunk of kBwdChunk tokens at a time:
+//   1. dlogits: z recomputed by the forward's contraction, g written twice:
+//      token-major Gd [chunk, Vpad] (for dH) and vocabulary-major GdT
+//      [Vpad, chunk] (for dW); padding rows and columns hold zeros.
+//   2. dH rows of the chunk = Gd W^T-rows (K = Vpad ascending) + sampled term.
+//   3. dW += GdT H^T-rows of the chunk (K = the chunk's tokens ascending).
+// dW starts as zeros plus the sampled term; chunks are added in token order.
+// Every sum has a fixed order (no atomics, no split-K): run-to-run bitwise
+// deterministic. The transposed copies W^T [d, Vpad] and H^T [d, chunk] make
+// every contraction "both operands K-contiguous", the form the engine runs.
+
+#include <algorithm>
+
+#include <hipcub/hipcub.hpp>
+
 #include "itl_launch.h"
+#include "tile_engine.h"
 
 namespace itl {
 
-size_t backward_workspace_bytes(long long, long long, long long) { return 0; }
+namespace {
 
-hipError_t launch_reinforce_zero_backward(const void*, const void*, int, int, int, int, const int32_t*, const float*,
-                                          const float*, float*, float*, void*, hipStream_t) {
-  return hipErrorNotSupported;
+constexpr int kBwdChunk = 16384;  // tokens per chunk (a multiple of kBT)
+static_assert(kBwdChunk % kBT == 0, "chunks hold whole token blocks");
+
+template <int kDtype>
+struct Elem;
+template <>
+struct Elem<0> {
+  using T = uint16_t;  // bf16 bits
+  static constexpr int kSize = 2;
+  __device__ static __forceinline__ float to_f(T x) { return __uint_as_float((uint32_t)x << 16); }
+  // Round to nearest even (inputs here are finite).
+  __device__ static __forceinline__ T from_f(float f) {
+    const uint32_t u = __float_as_uint(f);
+    return (T)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+  }
+};
+template <>
+struct Elem<1> {
+  using T = float;
+  static constexpr int kSize = 4;
+  __device__ static __forceinline__ float to_f(T x) { return x; }
+  __device__ static __forceinline__ T from_f(float f) { return f; }
+};
+
+long long round_up(long long x, long long m) { return (x + m - 1) / m * m; }
+
+// out[c, r] = in[r, c] for r < rows, 0 for rows <= r < out_cols; c < cols.
+// in: [rows, cols] row-major (row stride in_stride elements); out: [cols,
+// out_cols] row-major. 64 x 64 element tiles through LDS.
+template <typename T>
+__global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ in, long long in_stride, int rows,
+                                                        int cols, T* __restrict__ out, int out_cols) {
+  __shared__ T tile[64][65];
+  const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int i = ty; i < 64; i += 4) {
+    const int r = r0 + i, c = c0 + tx;
+    tile[i][tx] = (r < rows && c < cols) ? in[(size_t)r * in_stride + c] : T(0);
+  }
+  __syncthreads();
+  for (int i = ty; i < 64; i += 4) {
+    const int c = c0 + i, r = r0 + tx;
+    if (c < cols && r < out_cols) out[(size_t)c * out_cols + r] = tile[tx][i];
+  }
+}
+
+__global__ __launch_bounds__(256) void fill_zero_kernel(float4* __restrict__ p, size_t n4) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (size_t)gridDim.x * 256)
+    p[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+__global__ __launch_bounds__(256) void iota_kernel(uint32_t* __restrict__ p, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = (uint32_t)i;
+}
+
+// Sampled term of dW. ys/ts: token ids sorted by id, ties in ascending token
+// order (a stable sort). One wavefront per sorted position; the wavefront at
+// the first position of a run of equal ids sums coef[t] H[t] over the run, in
+// order, and writes the vocabulary row (dW is all zeros before).
+template <int kDtype>
+__global__ __launch_bounds__(256) void dw_sampled_kernel(const uint32_t* __restrict__ ys,
+                                                         const uint32_t* __restrict__ ts, int n_tok,
+                                                         const typename Elem<kDtype>::T* __restrict__ H,
+                                                         const float* __restrict__ coef, int d, int vocab,
+                                                         float* __restrict__ dW) {
+  const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (i >= n_tok) return;
+  const uint32_t v = ys[i];
+  if ((i > 0 && ys[i - 1] == v) || v >= (uint32_t)vocab) return;
+  int end = i + 1;
+  while (end < n_tok && ys[end] == v) ++end;
+  for (int k0 = 0; k0 < d; k0 += 64 * 8) {
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+    for (int j = i; j < end; ++j) {
+      const uint32_t t = ts[j];
+      const float c = coef[t];
+      const typename Elem<kDtype>::T* h = H + (size_t)t * d;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int k = k0 + e * 64 + lane;
+        if (k < d) acc[e] = fmaf(c, Elem<kDtype>::to_f(h[k]), acc[e]);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int k = k0 + e * 64 + lane;
+      if (k < d) dW[(size_t)v * d + k] = acc[e];
+    }
+  }
+}
+
+// Workgroup order shared by the three contractions: the grid is n_fast x
+// n_slow blocks; super-bands of kSuperBand fast indices are walked with the
+// slow index outer, so the workgroups an XCD runs together share operands.
+__device__ __forceinline__ void band_order(int b, int n_fast, int n_slow, int& fast, int& slow) {
+  const int band = b / (kSuperBand * n_slow);
+  const int first = band * kSuperBand;
+  const int nb = min(kSuperBand, n_fast - first);
+  const int rem = b - band * kSuperBand * n_slow;
+  slow = rem / nb;
+  fast = first + rem % nb;
+}
+
+// 1. dlogits. A = W tiles (vocabulary), B = the chunk's H block (tokens); as
+// in the forward. Grid: token blocks (fast) x vocabulary slices (slow).
+template <int kDtype>
+__global__ __launch_bounds__(kThreads, 1) void dlogits_kernel(
+    const char* __restrict__ Hc, int len, const char* __restrict__ W, int row_bytes, int vocab, int vpad,
+    int n_tb, int n_slices, const int32_t* __restrict__ y, const float* __restrict__ lse,
+    const float* __restrict__ coef, typename Elem<kDtype>::T* __restrict__ Gd, typename Elem<kDtype>::T* __restrict__ GdT) {
+  using E = Elem<kDtype>;
+  __shared__ uint4 smem[kEngineSmemChunks];
+  const Lanes L = lanes();
+  int tb, slice;
+  band_order(blockIdx.x, n_tb, n_slices, tb, slice);
+  const int t0 = tb * kBT;
+  const int n_vt = vpad / kBV;
+  const int tile_begin = slice_tile(slice, n_vt, n_slices);
+  const int tile_end = slice_tile(slice + 1, n_vt, n_slices);
+  float l2e_lse[4], negc[4];
+#pragma unroll
+  for (int bn = 0; bn < 4; ++bn) {
+    const int t = t0 + L.wt * 128 + bn * 32 + L.col;
+    const bool ok = t < len;
+    l2e_lse[bn] = ok ? lse[t] * kLog2e : 0.0f;
+    negc[bn] = ok ? -coef[t] : 0.0f;  // padding tokens get g = 0
+  }
+  auto w_rsrc = [&](int tile) {
+    const int v0 = tile * kBV;
+    return rsrc_words(W + (size_t)v0 * row_bytes, (uint32_t)max(0, min(kBV, vocab - v0)) * row_bytes);
+  };
+  const int4v hr = rsrc_words(Hc + (size_t)t0 * row_bytes, (uint32_t)min(kBT, len - t0) * row_bytes);
+  auto epilogue = [&](int tile, floatx16 (&acc)[4][4]) {
+    mfma_result_wait();
+    const int vw = tile * kBV + L.wv * 128 + 4 * L.half;
+#pragma unroll
+    for (int bn = 0; bn < 4; ++bn) {
+      const int t = t0 + L.wt * 128 + bn * 32 + L.col;  // < chunk's padded length
+#pragma unroll
+      for (int bm = 0; bm < 4; ++bm) {
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int v = vw + bm * 32 + 8 * i4;  // rows v .. v + 3
+          typename E::T g[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float z = acc_read(acc[bm][bn], 4 * i4 + r);
+            const float p = fast_exp2(z * kLog2e - l2e_lse[bn]);
+            g[r] = E::from_f(v + r < vocab ? negc[bn] * p : 0.0f);
+            GdT[(size_t)(v + r) * kBwdChunk + t] = g[r];
+          }
+          if constexpr (kDtype == 0) {
+            uint2 pk;
+            pk.x = (uint32_t)g[0] | ((uint32_t)g[1] << 16);
+            pk.y = (uint32_t)g[2] | ((uint32_t)g[3] << 16);
+            *reinterpret_cast<uint2*>(Gd + (size_t)t * vpad + v) = pk;
+          } else {
+            *reinterpret_cast<float4*>(Gd + (size_t)t * vpad + v) = make_float4(g[0], g[1], g[2], g[3]);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+  run_tiles<kDtype>(smem, L, row_bytes, tile_begin, tile_end, row_bytes / kStepBytes, w_rsrc, hr, epilogue);
+}
+
+// 2. dH for the chunk. A = W^T tile (d rows, K = Vpad), B = Gd token block.
+// Grid: token blocks (fast) x d tiles (slow). Lane l's accumulators are d
+// rows of token t0 + 128 wt + 32 bn + (l mod 32).
+template <int kDtype>
+__global__ __launch_bounds__(kThreads, 1) void dh_kernel(const char* __restrict__ WT, const char* __restrict__ Gd,
+                                                        int vpad, int d, int vocab, int len, int n_tb, int n_dt,
+                                                        const int32_t* __restrict__ y, const float* __restrict__ coef,
+                                                        const typename Elem<kDtype>::T* __restrict__ W,
+                                                        float* __restrict__ dH) {
+  using E = Elem<kDtype>;
+  __shared__ uint4 smem[kEngineSmemChunks];
+  const Lanes L = lanes();
+  int tb, dt;
+  band_order(blockIdx.x, n_tb, n_dt, tb, dt);
+  const int t0 = tb * kBT;
+  const int row_bytes = vpad * E::kSize;
+  auto a_rsrc = [&](int tile) {
+    const int k0 = tile * kBV;
+    return rsrc_words(WT + (size_t)k0 * row_bytes, (uint32_t)min(kBV, d - k0) * row_bytes);
+  };
+  const int4v br = rsrc_words(Gd + (size_t)t0 * row_bytes, (uint32_t)min(kBT, len - t0) * row_bytes);
+  auto epilogue = [&](int tile, floatx16 (&acc)[4][4]) {
+    mfma_result_wait();
+    const int kw = tile * kBV + L.wv * 128 + 4 * L.half;
+#pragma unroll
+    for (int bn = 0; bn < 4; ++bn) {
+      const int t = t0 + L.wt * 128 + bn * 32 + L.col;
+      const bool ok = t < len;
+      const int yr = ok ? y[t] : 0;
+      const bool yok = (unsigned)yr < (unsigned)vocab;  // an invalid id contributes no sampled term
+      const float c = ok && yok ? coef[t] : 0.0f;
+      const int yt = yok ? yr : 0;
+#pragma unroll
+      for (int bm = 0; bm < 4; ++bm) {
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int k = kw + bm * 32 + 8 * i4;  // d rows k .. k + 3 (d is a multiple of 64)
+          float o[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o[r] = acc_read(acc[bm][bn], 4 * i4 + r);
+          if (ok && k < d) {
+            const typename E::T* wy = W + (size_t)yt * d + k;
+            float4 out;
+            out.x = o[0] + c * E::to_f(wy[0]);
+            out.y = o[1] + c * E::to_f(wy[1]);
+            out.z = o[2] + c * E::to_f(wy[2]);
+            out.w = o[3] + c * E::to_f(wy[3]);
+            *reinterpret_cast<float4*>(dH + (size_t)t * d + k) = out;
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+  run_tiles<kDtype>(smem, L, row_bytes, dt, dt + 1, row_bytes / kStepBytes, a_rsrc, br, epilogue);
+}
+
+// 3. dW += the chunk's part. A = GdT vocabulary tile (K = chunk tokens), B =
+// H^T d block. Grid: vocabulary tiles (fast) x d tiles (slow). Lane l's
+// accumulators are vocabulary rows at d column 128 wt + 32 bn + (l mod 32).
+template <int kDtype>
+__global__ __launch_bounds__(kThreads, 1) void dw_kernel(const char* __restrict__ GdT, const char* __restrict__ HT,
+                                                        int kpad, int vocab, int d, int n_vt, int n_dt,
+                                                        float* __restrict__ dW) {
+  using E = Elem<kDtype>;
+  __shared__ uint4 smem[kEngineSmemChunks];
+  const Lanes L = lanes();
+  int vt, dt;
+  band_order(blockIdx.x, n_vt, n_dt, vt, dt);
+  const int row_bytes = kBwdChunk * E::kSize;
+  const int k0 = dt * kBT;
+  auto a_rsrc = [&](int tile) {
+    const int v0 = tile * kBV;
+    return rsrc_words(GdT + (size_t)v0 * row_bytes, (uint32_t)kBV * row_bytes);
+  };
+  const int4v br = rsrc_words(HT + (size_t)k0 * row_bytes, (uint32_t)min(kBT, d - k0) * row_bytes);
+  auto epilogue = [&](int tile, floatx16 (&acc)[4][4]) {
+    mfma_result_wait();
+    const int vw = tile * kBV + L.wv * 128 + 4 * L.half;
+#pragma unroll
+    for (int bn = 0; bn < 4; ++bn) {
+      const int k = k0 + L.wt * 128 + bn * 32 + L.col;
+#pragma unroll
+      for (int bm = 0; bm < 4; ++bm) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float a = acc_read(acc[bm][bn], i);
+          const int v = vw + bm * 32 + 8 * (i >> 2) + (i & 3);
+          if (v < vocab && k < d) {
+            float* p = dW + (size_t)v * d + k;
+            *p = *p + a;
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+  run_tiles<kDtype>(smem, L, row_bytes, vt, vt + 1, kpad * E::kSize / kStepBytes, a_rsrc, br, epilogue);
+}
+
+// Workspace layout of the backward (each region 256-byte aligned).
+struct BwdLayout {
+  size_t wt, ht, gd, gdt, keys, vals, keys_out, vals_out, sort_tmp, sort_tmp_bytes, total;
+};
+
+size_t sort_temp_bytes(long long n_tok) {
+  size_t bytes = 0;
+  hipcub::DeviceRadixSort::SortPairs(nullptr, bytes, (const uint32_t*)nullptr, (uint32_t*)nullptr,
+                                     (const uint32_t*)nullptr, (uint32_t*)nullptr, (int)n_tok, 0, 32, nullptr);
+  return bytes;
+}
+
+BwdLayout bwd_layout(long long n_tok, long long d, long long vocab, int es) {
+  BwdLayout L{};
+  const long long vpad = round_up(vocab, kBV);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += align256(bytes);
+    return at;
+  };
+  L.wt = take((size_t)d * vpad * es);
+  L.ht = take((size_t)d * kBwdChunk * es);
+  L.gd = take((size_t)kBwdChunk * vpad * es);
+  L.gdt = take((size_t)vpad * kBwdChunk * es);
+  L.keys = take((size_t)n_tok * 4);
+  L.vals = take((size_t)n_tok * 4);
+  L.keys_out = take((size_t)n_tok * 4);
+  L.vals_out = take((size_t)n_tok * 4);
+  L.sort_tmp_bytes = sort_temp_bytes(n_tok);
+  L.sort_tmp = take(L.sort_tmp_bytes);
+  L.total = off;
+  return L;
+}
+
+template <int kDtype>
+hipError_t run_backward(const void* H, const void* W, int n_tok, int d, int vocab, const int32_t* tokens,
+                        const float* lse, const float* coef, float* dH, float* dW, void* workspace,
+                        hipStream_t stream) {
+  using E = Elem<kDtype>;
+  using T = typename E::T;
+  const int es = E::kSize;
+  const int vpad = (int)round_up(vocab, kBV);
+  const BwdLayout Ly = bwd_layout(n_tok, d, vocab, es);
+  char* ws = static_cast<char*>(workspace);
+  T* WT = reinterpret_cast<T*>(ws + Ly.wt);
+  T* HT = reinterpret_cast<T*>(ws + Ly.ht);
+  T* Gd = reinterpret_cast<T*>(ws + Ly.gd);
+  T* GdT = reinterpret_cast<T*>(ws + Ly.gdt);
+  const T* Hp = static_cast<const T*>(H);
+  const T* Wp = static_cast<const T*>(W);
+  hipError_t e;
+#define ITL_CHECK_LAUNCH()           \
+  do {                               \
+    e = hipGetLastError();           \
+    if (e != hipSuccess) return e;   \
+  } while (0)
+
+  // dW = 0, then the sampled term.
+  const size_t dw4 = (size_t)vocab * d / 4;  // d is a multiple of 64
+  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)std::min<size_t>(65536, (dw4 + 255) / 256)), dim3(256), 0, stream,
+                     reinterpret_cast<float4*>(dW), dw4);
+  ITL_CHECK_LAUNCH();
+  if (n_tok > 0) {
+    uint32_t* keys = reinterpret_cast<uint32_t*>(ws + Ly.keys);
+    uint32_t* vals = reinterpret_cast<uint32_t*>(ws + Ly.vals);
+    uint32_t* keys_out = reinterpret_cast<uint32_t*>(ws + Ly.keys_out);
+    uint32_t* vals_out = reinterpret_cast<uint32_t*>(ws + Ly.vals_out);
+    e = hipMemcpyAsync(keys, tokens, (size_t)n_tok * 4, hipMemcpyDeviceToDevice, stream);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(iota_kernel, dim3((unsigned)ceil_div(n_tok, 256)), dim3(256), 0, stream, vals, n_tok);
+    ITL_CHECK_LAUNCH();
+    size_t tmp = Ly.sort_tmp_bytes;
+    e = hipcub::DeviceRadixSort::SortPairs(ws + Ly.sort_tmp, tmp, keys, keys_out, vals, vals_out, n_tok, 0, 32,
+                                           stream);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(dw_sampled_kernel<kDtype>, dim3((unsigned)ceil_div(n_tok, 4)), dim3(256), 0, stream, keys_out,
+                       vals_out, n_tok, Hp, coef, d, vocab, dW);
+    ITL_CHECK_LAUNCH();
+  }
+  if (n_tok == 0) return hipSuccess;
+
+  // W^T [d, Vpad], zero-padded.
+  hipLaunchKernelGGL(transpose_kernel<T>, dim3((unsigned)ceil_div(vpad, 64), (unsigned)ceil_div(d, 64)), dim3(256), 0,
+                     stream, Wp, (long long)d, vocab, d, WT, vpad);
+  ITL_CHECK_LAUNCH();
+
+  const int S = n_slices(vpad);
+  const int n_dt = (int)ceil_div(d, kBT);
+  const int n_vt = vpad / kBV;
+  const int row_bytes = d * es;
+  for (int c0 = 0; c0 < n_tok; c0 += kBwdChunk) {
+    const int len = std::min(kBwdChunk, n_tok - c0);
+    const int kpad = (int)round_up(len, kBT);
+    const int n_tb = kpad / kBT;
+    const char* Hc = static_cast<const char*>(H) + (size_t)c0 * row_bytes;
+    hipLaunchKernelGGL(dlogits_kernel<kDtype>, dim3((unsigned)(n_tb * S)), dim3(kThreads), 0, stream, Hc, len,
+                       static_cast<const char*>(W), row_bytes, vocab, vpad, n_tb, S, tokens + c0, lse + c0, coef + c0,
+                       Gd, GdT);
+    ITL_CHECK_LAUNCH();
+    hipLaunchKernelGGL(dh_kernel<kDtype>, dim3((unsigned)(n_tb * n_dt)), dim3(kThreads), 0, stream,
+                       reinterpret_cast<const char*>(WT), reinterpret_cast<const char*>(Gd), vpad, d, vocab, len, n_tb, n_dt,
+                       tokens + c0, coef + c0, Wp, dH + (size_t)c0 * d);
+    ITL_CHECK_LAUNCH();
+    // H^T of the chunk [d, kBwdChunk], tokens past len zero.
+    hipLaunchKernelGGL(transpose_kernel<T>, dim3((unsigned)(kBwdChunk / 64), (unsigned)ceil_div(d, 64)), dim3(256), 0,
+                       stream, Hp + (size_t)c0 * d, (long long)d, len, d, HT, kBwdChunk);
+    ITL_CHECK_LAUNCH();
+    hipLaunchKernelGGL(dw_kernel<kDtype>, dim3((unsigned)(n_vt * n_dt)), dim3(kThreads), 0, stream,
+                       reinterpret_cast<const char*>(GdT), reinterpret_cast<const char*>(HT), kpad, vocab, d, n_vt,
+                       n_dt, dW);
+    ITL_CHECK_LAUNCH();
+  }
+#undef ITL_CHECK_LAUNCH
+  return hipSuccess;
+}
+
+}  // namespace
+
+size_t backward_workspace_bytes(long long n_tok, long long d, long long vocab, int dtype) {
+  return bwd_layout(n_tok, d, vocab, dtype == 0 ? 2 : 4).total;
+}
+
+hipError_t launch_reinforce_zero_backward(const void* H, const void* W, int dtype, int n_tok, int d, int vocab,
+                                          const int32_t* tokens, const float* lse, const float* coef, float* dH,
+                                          float* dW, void* workspace, hipStream_t stream) {
+  if (dtype == 0)
+    return run_backward<0>(H, W, n_tok, d, vocab, tokens, lse, coef, dH, dW, workspace, stream);
+  return run_backward<1>(H, W, n_tok, d, vocab, tokens, lse, coef, dH, dW, workspace, stream);
 }
 
 }  // namespace itl

@@ -24,7 +24,11 @@ hipError_t launch_reinforce_zero_loss(const float* logprob, const float* rollout
                                       long long n_tok, float* resp_loss, float* loss, float* coef,
                                       hipStream_t stream);
 
-size_t backward_workspace_bytes(long long n_tok, long long d, long long vocab);
+size_t backward_workspace_bytes(long long n_tok, long long d, long long vocab, int dtype);
+
+// Largest vocabulary the backward handles (its padded rows must be
+// addressable by 32-bit buffer offsets over 256-row tiles).
+constexpr long long kBwdMaxVocab = (1LL << 31) / (256LL * 4) - 256;
 
 hipError_t launch_reinforce_zero_backward(const void* H, const void* W, int dtype, int n_tok, int d, int vocab,
                                           const int32_t* tokens, const float* lse, const float* coef,

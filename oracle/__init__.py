@@ -42,6 +42,7 @@ from .reinforce_zero import (
     importance_ratio,
     reinforce_zero_loss,
     reinforce_zero_backward,
+    reinforce_zero_backward_rows,
     reinforce_zero_objective,
 )
 
@@ -54,5 +55,6 @@ __all__ = [
     "importance_ratio",
     "reinforce_zero_loss",
     "reinforce_zero_backward",
+    "reinforce_zero_backward_rows",
     "reinforce_zero_objective",
 ]

@@ -127,3 +127,49 @@ def reinforce_zero_backward(H, W, y, coef, vocab_chunk=8192):
         dH += G[:, v0:v1] @ Wc
         dW[v0:v1] = G[:, v0:v1].T @ H64
     return dH, dW
+
+
+def reinforce_zero_backward_rows(H, W, y, coef, tok_idx, vocab_idx, vocab_chunk=8192):
+    """Selected rows of the loss gradient: (dH[tok_idx], dW[vocab_idx]).
+
+    The same definitions as reinforce_zero_backward, evaluated for a subset:
+    dH[t] = sum_v G[t, v] W[v] needs token t's full row of G, and
+    dW[v] = sum_t G[t, v] H[t] needs column v of G for every token, which in
+    turn needs every token's log-normaliser over the whole vocabulary. For
+    full-size heads where the full gradient does not fit in memory.
+    """
+    H64 = to_f64(H)
+    W = np.asarray(W)
+    y = np.asarray(y, dtype=np.int64)
+    c = np.asarray(coef, dtype=np.float64)
+    tok_idx = np.asarray(tok_idx, dtype=np.int64)
+    vocab_idx = np.asarray(vocab_idx, dtype=np.int64)
+    n, d = H64.shape
+    V = W.shape[0]
+    if y.shape != (n,) or c.shape != (n,):
+        raise ValueError("tokens / coef do not match the rows of H")
+    if n and (y.min() < 0 or y.max() >= V):
+        raise ValueError("token id out of range")
+    # log-normaliser of every token, one vocabulary chunk at a time (running max / sum)
+    m = np.full(n, -np.inf)
+    s = np.zeros(n)
+    for v0 in range(0, V, vocab_chunk):
+        z = H64 @ to_f64(W[v0:v0 + vocab_chunk]).T
+        m_new = np.maximum(m, z.max(axis=1))
+        s = s * np.exp(m - m_new) + np.exp(z - m_new[:, None]).sum(axis=1)
+        m = m_new
+    lse = m + np.log(s)
+    # dH rows: G[t, :] W over the whole vocabulary
+    dH = np.zeros((tok_idx.size, d))
+    Ht = H64[tok_idx]
+    for v0 in range(0, V, vocab_chunk):
+        Wc = to_f64(W[v0:v0 + vocab_chunk])
+        G = -c[tok_idx, None] * np.exp(Ht @ Wc.T - lse[tok_idx, None])
+        dH += G @ Wc
+    dH += c[tok_idx, None] * to_f64(W[y[tok_idx]])
+    # dW rows: G[:, v]^T H for the selected vocabulary rows
+    Wv = to_f64(W[vocab_idx])
+    Gv = -c[:, None] * np.exp(H64 @ Wv.T - lse[:, None])
+    Gv += c[:, None] * (y[:, None] == vocab_idx[None, :])
+    dW = Gv.T @ H64
+    return dH, dW

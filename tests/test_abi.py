@@ -98,6 +98,22 @@ def test_loss_and_advantage_validation(lib):
                                            v(256), 1 << 30, None) == UNSUPPORTED
     assert lib.itl_reinforce_zero_backward(v(1), None, 0, 4, 64, 10, v(1), v(1), v(1), v(1), v(1),
                                            v(256), 1 << 30, None) == INVALID
+    # workspace checked before anything is launched
+    assert lib.itl_reinforce_zero_backward(v(1), v(1), 0, 4, 64, 10, v(1), v(1), v(1), v(1), v(1),
+                                           v(256), 16, None) == WORKSPACE
+    assert lib.itl_reinforce_zero_backward(v(1), v(1), 0, 4, 64, 10, v(1), v(1), v(1), v(1), v(1),
+                                           v(257), 1 << 40, None) == WORKSPACE
+
+
+def test_backward_workspace_sizes(lib):
+    f = lib.itl_reinforce_zero_backward_workspace_bytes
+    bf16 = f(1000, 256, 5000, 0)
+    f32 = f(1000, 256, 5000, 1)
+    assert 0 < bf16 < f32 < (1 << 40)
+    assert f(-1, 256, 5000, 0) == ctypes.c_size_t(-1).value
+    assert f(10, 256, 5000, 7) == ctypes.c_size_t(-1).value
+    # transposed W and chunk buffers dominate: at least W^T plus two dlogit copies
+    assert bf16 >= 256 * 5120 * 2 + 2 * 16384 * 5120 * 2
 
 
 def test_binding_rejects_bad_tensors():

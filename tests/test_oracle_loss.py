@@ -197,3 +197,20 @@ def test_dW_columns_sum_to_zero_over_vocab():
     _, _, coef = oracle.reinforce_zero_loss(lp, lpr, A, off)
     _, dW = oracle.reinforce_zero_backward(H, W, y, coef)
     assert np.max(np.abs(dW.sum(axis=0))) <= 1e-13 * max(1e-12, np.abs(dW).max()) * 300
+
+
+def test_gradient_rows_match_full_gradient():
+    """The subset evaluator agrees with the full gradient (itself pinned by
+    finite differences and float64 autograd above), including repeated
+    token ids and vocabulary rows nobody sampled."""
+    rng = np.random.default_rng(61)
+    H, W, y, lpr, A, off = _tiny_problem(rng, n_groups=2, gs=3, lo=3, hi=7, d=10, V=57)
+    y[:4] = y[0]
+    lp, _ = oracle.lmhead_logprob(H, W, y)
+    _, _, coef = oracle.reinforce_zero_loss(lp, lpr, A, off)
+    dH, dW = oracle.reinforce_zero_backward(H, W, y, coef)
+    tok = np.array([0, 3, len(y) - 1])
+    voc = np.array([int(y[0]), 0, 56, 13])
+    dHr, dWr = oracle.reinforce_zero_backward_rows(H, W, y, coef, tok, voc, vocab_chunk=8)
+    assert np.max(np.abs(dHr - dH[tok])) <= 1e-13 * np.abs(dH).max()
+    assert np.max(np.abs(dWr - dW[voc])) <= 1e-13 * np.abs(dW).max()
