@@ -29,6 +29,7 @@ PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 dense bf16 flop/clk/CU (pub
 PEAK_HBM_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["invariant_token_logprobs_lm_amd/csrc/lmhead.hip",
+                  "invariant_token_logprobs_lm_amd/csrc/tile_engine.h",
                   "invariant_token_logprobs_lm_amd/csrc/itl_config.h",
                   "invariant_token_logprobs_lm_amd/csrc/device_common.h",
                   "invariant_token_logprobs_lm_amd/build.py"]
@@ -116,6 +117,32 @@ def time_steps(step, steps, warmup):
     total_ms = start.elapsed_time(end)
     head_ms = [a.elapsed_time(b) for a, b in head]
     return total_ms / steps, sum(head_ms) / steps, wall
+
+
+def setup_backward(wl, device):
+    """Inputs of the forward + backward step on a head with a backward."""
+    import torch
+    import invariant_token_logprobs_lm_amd as itl
+
+    s = setup_forward(wl, device)
+    lay = s["lay"]
+    s["bws"] = torch.empty(itl.backward_workspace_bytes(lay.n_tok, wl.d, wl.vocab, s["H"].dtype), dtype=torch.uint8,
+                           device=device)
+    s["dH"] = torch.empty((lay.n_tok, wl.d), dtype=torch.float32, device=device)
+    s["dW"] = torch.empty((wl.vocab, wl.d), dtype=torch.float32, device=device)
+    return s
+
+
+def fwd_bwd_step(s, ev=None):
+    """Forward logprob, advantage, loss and backward; ev brackets the backward."""
+    import invariant_token_logprobs_lm_amd as itl
+
+    rl, L, coef = forward_step(s)
+    if ev is not None:
+        ev[0].record()
+    itl.reinforce_zero_backward(s["H"], s["W"], s["y"], s["lse"], coef, dH=s["dH"], dW=s["dW"], workspace=s["bws"])
+    if ev is not None:
+        ev[1].record()
 
 
 def cpu_baseline(wl, n_sample=6144):
@@ -238,6 +265,32 @@ def main():
     }
     del s
     torch.cuda.empty_cache()
+    if not args.no_backward:
+        wb = WORKLOADS["large-moe-head"]
+        sb = setup_backward(wb, device)
+        nb = sb["lay"].n_tok
+        bsteps = max(1, min(args.steps, 3))
+        ms_fb, ms_bwd, wall_b = time_steps(lambda ev: fwd_bwd_step(sb, ev), bsteps, 1)
+        fl_alg = 6.0 * wb.d * wb.vocab * nb  # forward 2dV + dH 2dV + dW 2dV per token (recompute not credited)
+        tf = fl_alg / (ms_fb * 1e-3) / 1e12
+        log(f"[bench] {wb.key} fwd+bwd step {ms_fb:.1f} ms (backward {ms_bwd:.1f} ms) -> {nb / (ms_fb * 1e-3):.0f} "
+            f"tokens/s, {tf:.1f} TFLOP/s algorithmic ({100 * tf / PEAK_BF16_TFLOPS:.1f}% of bf16 peak)")
+        out["fwd_bwd"] = {
+            "workload": f"{wb.key} forward logprob + group advantage + REINFORCE Zero loss + backward (dH, dW)",
+            "d": wb.d,
+            "vocab": wb.vocab,
+            "responses": sb["lay"].n_resp,
+            "n_tok": nb,
+            "steps": bsteps,
+            "ms_per_step": ms_fb,
+            "ms_backward": ms_bwd,
+            "value": nb / (ms_fb * 1e-3),
+            "unit": "sampled tokens/s (forward + backward)",
+            "tflops_algorithmic": tf,
+            "frac_bf16_peak": tf / PEAK_BF16_TFLOPS,
+        }
+        del sb
+        torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on a bounded sample ...")
         out["cpu_baseline"] = cpu_baseline(wl)
