@@ -209,22 +209,13 @@ __device__ __forceinline__ void run_tiles(uint4* smem, const Lanes& L, int row_b
 
   // K-step pipeline over the workgroup's steps g (all its tiles, K
   // fastest). In the names below W is the walked operand A and H the fixed
-  // operand B: W(g) sits in W slot g % 3, H(g) in H slot g % 2. Right after
-  // the barrier that publishes step g, H(g + 1) and W(g + 2) are issued into
-  // the slots step g - 1 used. A step is four sub-steps of 16 MFMAs; during
-  // one sub-step's MFMAs the wavefront reads the next sub-step's 8 operand
-  // fragments from LDS, and each step's last sub-step is multiplied after
-  // the next barrier, while the next step's loads are issued and its first
-  // operands read: the matrix cores keep busy across the barrier. The
-  // order is pinned with scheduling barriers: left alone, the compiler
-  // issues each sub-step's LDS reads after its MFMAs and then waits for
-  // them.
-  auto mma_all = [&](floatx16 (&acc)[4][4], const uint4 (&A)[4], const uint4 (&B)[4]) {
-#pragma unroll
-    for (int bm = 0; bm < 4; ++bm)
-#pragma unroll
-      for (int bn = 0; bn < 4; ++bn) Mma<kDtype>::step(acc[bm][bn], A[bm], B[bn]);
-  };
+  // operand B: W(g) sits in W slot g % 3, H(g) in H slot g % 2. A step is
+  // four sub-steps of 16 MFMAs; each sub-step's 8 operand fragments are read
+  // from LDS two sub-steps ahead, spread over the MFMAs in between, so that
+  // the LDS read pipe (about 64 B/clk per CU, which a 128 x 128 wavefront
+  // tile needs in full at the MFMA peak) is never waited on. The order is
+  // pinned with scheduling barriers: left alone, the compiler issues each
+  // sub-step's LDS reads after its MFMAs and then waits for them.
   int w_tile = tile_begin, w_ks = 0;  // next W step to load
   int h_ks = 0;                        // next H step to load (H rows do not depend on the tile)
   int w_slot_next = 0, h_slot_next = 0;
@@ -285,7 +276,8 @@ __device__ __forceinline__ void run_tiles(uint4* smem, const Lanes& L, int row_b
 
   using T = std::true_type;
   using F = std::false_type;
-  // Prologue: W(0), H(0), W(1).
+  // Prologue: W(0), H(0), W(1); publish step 0; H(1), W(2); read the first
+  // two sub-steps' operands.
   {
     const int4v wr0 = w_rsrc(w_tile);
 #pragma unroll
@@ -299,29 +291,53 @@ __device__ __forceinline__ void run_tiles(uint4* smem, const Lanes& L, int row_b
     for (int j = 0; j < kDmaPerWave; ++j) dma16(wr1, voff[j], (uint32_t)w_ks * kStepBytes, w_slot_lds(1) + j * 1024);
     next_w();
   }
+  wait_and_barrier<kDmaPerWave>();  // W(0), H(0) landed
+  {
+    const int4v wr = w_rsrc(w_tile);
+    const uint32_t hm = h_slot_lds(h_slot_next), wm = w_slot_lds(w_slot_next);
+#pragma unroll
+    for (int j = 0; j < kDmaPerWave; ++j) dma16(hr, voff[j], (uint32_t)h_ks * kStepBytes, hm + j * 1024);
+#pragma unroll
+    for (int j = 0; j < kDmaPerWave; ++j) dma16(wr, voff[j], (uint32_t)w_ks * kStepBytes, wm + j * 1024);
+    next_h();
+    next_w();
+  }
+  // Operand sets of the four sub-steps of the current K step: S0 and S1 are
+  // read two sub-steps ahead, during the previous step's sub-steps 2 and 3.
+  uint4 a0[4], b0[4], a1[4], b1[4], a2[4], b2[4], a3[4], b3[4];
+  {
+    const uint4* sa = smem;
+    const uint4* sb = smem + kWSlots * kSlotChunks;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      a0[m] = sa[a_off[0] + m * 32 * kRowChunks];
+      b0[m] = sb[b_off[0] + m * 32 * kRowChunks];
+      a1[m] = sa[a_off[1] + m * 32 * kRowChunks];
+      b1[m] = sb[b_off[1] + m * 32 * kRowChunks];
+    }
+  }
   int wslot = 0, hslot = 0;  // slots of the step being multiplied
-  uint4 pa[4], pb[4];        // kk = 3 operands of the previous step, multiplied late
-  // One K step; kFirst = the tile's first step (fresh accumulators, no
-  // deferred sub-step from the previous tile). The next steps' loads are
-  // always issued: past the workgroup's last step they re-read a valid
-  // step into a free slot, which nothing reads again.
+  // One K step g. Sub-steps 0 and 1 multiply S0, S1 while S2, S3 (this
+  // step's sub-steps 2, 3) are read; the barrier then publishes step g + 1,
+  // whose loads were issued one (H) or two (W) steps earlier; step g's slots
+  // are free after it (all of step g is in registers), so H(g + 2) and
+  // W(g + 3) are loaded into them during sub-step 2, while sub-steps 2 and 3
+  // read step g + 1's first two operand sets into S0, S1. kFirst = the
+  // tile's first step (fresh accumulators). Loads past the workgroup's last
+  // step re-read a valid step into a free slot, which nothing reads again.
   auto k_step = [&](floatx16 (&acc)[4][4], auto first) {
-    constexpr bool kFirst = decltype(first)::value;
-    wait_and_barrier<kDmaPerWave>();  // W(g), H(g) landed; W(g + 1) may still be in flight
-    uint4 fa[4], fb[4], ga[4], gb[4];
-    if constexpr (kFirst) phase(acc, pa, pb, F{}, F{}, F{}, T{}, wslot, hslot, 0, fa, fb);
-    else phase(acc, pa, pb, F{}, T{}, F{}, T{}, wslot, hslot, 0, fa, fb);
-    phase(acc, fa, fb, first, T{}, F{}, F{}, wslot, hslot, 1, ga, gb);
-    phase(acc, ga, gb, F{}, T{}, F{}, F{}, wslot, hslot, 2, fa, fb);
-    phase(acc, fa, fb, F{}, T{}, T{}, F{}, wslot, hslot, 3, pa, pb);
+    phase(acc, a0, b0, first, T{}, F{}, F{}, wslot, hslot, 2, a2, b2);
+    phase(acc, a1, b1, F{}, T{}, T{}, F{}, wslot, hslot, 3, a3, b3);
+    wait_and_barrier<kDmaPerWave>();  // W(g + 1), H(g + 1) landed; W(g + 2) may still be in flight
     wslot = wslot == kWSlots - 1 ? 0 : wslot + 1;
     hslot ^= 1;
+    phase(acc, a2, b2, F{}, T{}, F{}, T{}, wslot, hslot, 0, a0, b0);
+    phase(acc, a3, b3, F{}, T{}, F{}, F{}, wslot, hslot, 1, a1, b1);
   };
   for (int tile = tile_begin; tile < tile_end; ++tile) {
     floatx16 acc[4][4];
     k_step(acc, T{});
     for (int ks = 1; ks < nks; ++ks) k_step(acc, F{});
-    mma_all(acc, pa, pb);  // the tile's last sub-step
     epi(tile, acc);
   }
   // Every wavefront is done with the LDS ring (and its loads) on return.
