@@ -145,6 +145,69 @@ def fwd_bwd_step(s, ev=None):
         ev[1].record()
 
 
+def decode_leg(wl, device, batch_sizes=(1, 8, 64, 256), calls=20):
+    """Decode-shaped calls (a rollout engine's step: one new token for each of
+    M sequences) on the head: the invariant kernel against a non-invariant
+    fast baseline run as a library (hipBLASLt GEMM with bf16 logits, then
+    torch log_softmax in fp32 and a gather). Also reports how far the
+    baseline's logprob of one fixed token moves with the batch it runs in,
+    against the invariant kernel's bit-identical results."""
+    import torch
+    import invariant_token_logprobs_lm_amd as itl
+    from synth import draw_head, draw_layout
+
+    M_max = max(batch_sizes)
+    H, W = draw_head(wl, M_max, device=device, salt=3)
+    g = torch.Generator(device=device)
+    g.manual_seed(4000 + wl.index)
+    y = torch.randint(0, wl.vocab, (M_max,), generator=g, device=device, dtype=torch.int32)
+
+    def baseline(Hm, ym):
+        z = torch.mm(Hm, W.t())
+        return torch.log_softmax(z.float(), dim=1).gather(1, ym.long()[:, None])[:, 0]
+
+    def timed(fn, n):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(n):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
+    rows = []
+    ours_ref = itl.lmhead_logprob(H[:1], W, y[:1], want_lse=False)[0]
+    base_ref = baseline(H[:1], y[:1])
+    max_base_drift = 0.0
+    ours_identical = True
+    for M in batch_sizes:
+        Hm, ym = H[:M].contiguous(), y[:M].contiguous()
+        ws = torch.empty(itl.lmhead_workspace_bytes(M, wl.vocab), dtype=torch.uint8, device=device)
+        lp = torch.empty(M, dtype=torch.float32, device=device)
+        ms_ours = timed(lambda: itl.lmhead_logprob(Hm, W, ym, logprob=lp, workspace=ws, want_lse=False), calls)
+        ms_base = timed(lambda: baseline(Hm, ym), calls)
+        lp_b = baseline(Hm, ym)
+        torch.cuda.synchronize()
+        ours_identical &= bool(torch.equal(lp[:1].view(torch.int32), ours_ref.view(torch.int32)))
+        drift = float((lp_b[:1] - base_ref).abs().max())
+        max_base_drift = max(max_base_drift, drift)
+        rows.append({"batch": M, "ms_invariant": ms_ours, "ms_baseline": ms_base,
+                     "tokens_per_s_invariant": M / (ms_ours * 1e-3), "tokens_per_s_baseline": M / (ms_base * 1e-3),
+                     "invariant_over_baseline": ms_base / ms_ours,
+                     "max_abs_lp_gap_to_baseline": float((lp - lp_b).abs().max())})
+        log(f"[bench] decode M={M}: invariant {ms_ours:.3f} ms, baseline {ms_base:.3f} ms "
+            f"(throughput ratio {ms_base / ms_ours:.3f})")
+    return {
+        "workload": f"{wl.key} decode-shaped calls (M sequences x 1 token), {calls} calls per point",
+        "baseline": "torch.mm (hipBLASLt, bf16 logits) + log_softmax (fp32) + gather; not batch-invariant",
+        "points": rows,
+        "invariant_token0_bit_identical_across_batches": ours_identical,
+        "baseline_token0_max_abs_drift_across_batches": max_base_drift,
+    }
+
+
 def cpu_baseline(wl, n_sample=6144):
     """The float64 oracle timed on a seeded sample of the same workload's
     tokens (forward + loss over the sampled tokens)."""
@@ -200,6 +263,7 @@ def main():
     ap.add_argument("--workload", default="qwen3-4b-head")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="before timing, run one plain 1 GiB device-to-device copy: the reference whose "
                          "FETCH_SIZE / WRITE_SIZE counters calibrate the HBM traffic figures")
@@ -265,6 +329,9 @@ def main():
     }
     del s
     torch.cuda.empty_cache()
+    if not args.no_decode:
+        out["decode"] = decode_leg(wl, device)
+        torch.cuda.empty_cache()
     if not args.no_backward:
         wb = WORKLOADS["large-moe-head"]
         sb = setup_backward(wb, device)

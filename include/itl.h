@@ -72,8 +72,11 @@ typedef enum itl_status {
 
 typedef enum itl_dtype { ITL_BF16 = 0, ITL_F32 = 1 } itl_dtype;
 
-/* Bytes of device workspace itl_lmhead_logprob needs for (n_tok, vocab).
- * Returns 0 for n_tok == 0 and SIZE_MAX for invalid sizes. */
+/* Bytes of device workspace itl_lmhead_logprob needs for (n_tok, vocab):
+ * about (16 S + 4) n_tok with S = min(ceil(vocab / 256), 256) vocabulary
+ * slices (one fp32 (max, sum of exp) pair per token, slice and wavefront,
+ * then the sampled logits). Returns 0 for n_tok == 0 and SIZE_MAX for
+ * invalid sizes. */
 size_t itl_lmhead_logprob_workspace_bytes(int64_t n_tok, int64_t vocab);
 
 /* Sampled-token logprob [RZ][BC]:

@@ -41,7 +41,7 @@ itl_status check_head(itl_dtype dtype, int64_t n_tok, int64_t d, int64_t vocab) 
   if (vocab > kMaxVocab) return fail(ITL_ERR_UNSUPPORTED, "vocab too large");
   // a 256-row operand block must be addressable with 32-bit buffer offsets
   if (d * elem_size(dtype) * (int64_t)itl::kBT >= ((int64_t)1 << 31)) return fail(ITL_ERR_UNSUPPORTED, "d too large");
-  const int64_t grid = itl::ceil_div(n_tok, itl::kBT) * itl::n_slices(vocab);
+  const int64_t grid = itl::ceil_div(n_tok, itl::kBT) * itl::n_slice_groups(n_tok, vocab);
   if (grid > INT32_MAX) return fail(ITL_ERR_UNSUPPORTED, "problem too large for one launch");
   return ITL_OK;
 }
@@ -163,9 +163,9 @@ const char* itl_build_info(void) {
     char buf[512];
     snprintf(buf, sizeof buf,
              "itl 0.2 arch=gfx950 threads=%d token_block=%d vocab_tile=%d k_step_bytes=%d w_slots=%d h_slots=%d "
-             "tiles_per_slice=%d slices=balanced mfma_bf16=32x32x16 mfma_f32=32x32x2 loss_threads=%d "
+             "max_slices=%d slices=balanced mfma_bf16=32x32x16 mfma_f32=32x32x2 loss_threads=%d "
              "mean_threads=%d",
-             itl::kThreads, itl::kBT, itl::kBV, itl::kStepBytes, itl::kWSlots, itl::kHSlots, itl::kTilesPerSlice,
+             itl::kThreads, itl::kBT, itl::kBV, itl::kStepBytes, itl::kWSlots, itl::kHSlots, itl::kMaxSlices,
              itl::kLossThreads, itl::kMeanThreads);
     return std::string(buf);
   }();

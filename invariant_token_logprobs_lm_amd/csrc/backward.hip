@@ -147,17 +147,17 @@ __device__ __forceinline__ void band_order(int b, int n_fast, int n_slow, int& f
 template <int kDtype>
 __global__ __launch_bounds__(kThreads, 1) void dlogits_kernel(
     const char* __restrict__ Hc, int len, const char* __restrict__ W, int row_bytes, int vocab, int vpad,
-    int n_tb, int n_slices, const int32_t* __restrict__ y, const float* __restrict__ lse,
+    int n_tb, int n_slices, int group, const int32_t* __restrict__ y, const float* __restrict__ lse,
     const float* __restrict__ coef, typename Elem<kDtype>::T* __restrict__ Gd, typename Elem<kDtype>::T* __restrict__ GdT) {
   using E = Elem<kDtype>;
   __shared__ uint4 smem[kEngineSmemChunks];
   const Lanes L = lanes();
-  int tb, slice;
-  band_order(blockIdx.x, n_tb, n_slices, tb, slice);
+  int tb, grp;
+  band_order(blockIdx.x, n_tb, (n_slices + group - 1) / group, tb, grp);
   const int t0 = tb * kBT;
   const int n_vt = vpad / kBV;
-  const int tile_begin = slice_tile(slice, n_vt, n_slices);
-  const int tile_end = slice_tile(slice + 1, n_vt, n_slices);
+  const int tile_begin = slice_tile(grp * group, n_vt, n_slices);
+  const int tile_end = slice_tile(min(grp * group + group, n_slices), n_vt, n_slices);
   float l2e_lse[4], negc[4];
 #pragma unroll
   for (int bn = 0; bn < 4; ++bn) {
@@ -394,6 +394,8 @@ hipError_t run_backward(const void* H, const void* W, int n_tok, int d, int voca
   ITL_CHECK_LAUNCH();
 
   const int S = n_slices(vpad);
+  const int G = std::max(1, kTilesPerGroup * S / (vpad / kBV));  // about kTilesPerGroup tiles per workgroup
+  const int n_groups = (S + G - 1) / G;
   const int n_dt = (int)ceil_div(d, kBT);
   const int n_vt = vpad / kBV;
   const int row_bytes = d * es;
@@ -402,8 +404,8 @@ hipError_t run_backward(const void* H, const void* W, int n_tok, int d, int voca
     const int kpad = (int)round_up(len, kBT);
     const int n_tb = kpad / kBT;
     const char* Hc = static_cast<const char*>(H) + (size_t)c0 * row_bytes;
-    hipLaunchKernelGGL(dlogits_kernel<kDtype>, dim3((unsigned)(n_tb * S)), dim3(kThreads), 0, stream, Hc, len,
-                       static_cast<const char*>(W), row_bytes, vocab, vpad, n_tb, S, tokens + c0, lse + c0, coef + c0,
+    hipLaunchKernelGGL(dlogits_kernel<kDtype>, dim3((unsigned)(n_tb * n_groups)), dim3(kThreads), 0, stream, Hc, len,
+                       static_cast<const char*>(W), row_bytes, vocab, vpad, n_tb, S, G, tokens + c0, lse + c0, coef + c0,
                        Gd, GdT);
     ITL_CHECK_LAUNCH();
     hipLaunchKernelGGL(dh_kernel<kDtype>, dim3((unsigned)(n_tb * n_dt)), dim3(kThreads), 0, stream,

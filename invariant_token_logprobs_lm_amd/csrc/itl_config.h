@@ -20,8 +20,10 @@ constexpr int kBV = 256;             // vocabulary rows per tile (MFMA A operand
 constexpr int kStepBytes = 128;      // bytes of one operand row per K step (64 bf16 / 32 fp32)
 constexpr int kWSlots = 3;           // LDS slots of the W-tile ring (loads two K steps ahead)
 constexpr int kHSlots = 2;           // LDS slots of the H-block ring (loads one K step ahead)
-constexpr int kTilesPerSlice = 16;   // at most this many vocabulary tiles per slice
-constexpr int kSuperBand = 32;       // token blocks walked together, slice by slice (workgroup order)
+constexpr int kMaxSlices = 256;      // vocabulary slices: min(tiles, this), a function of the vocabulary only
+constexpr int kTilesPerGroup = 16;   // grid shape only: a workgroup walks about this many tiles of consecutive
+                                     // slices when the batch is large (the arithmetic per slice is the same)
+constexpr int kSuperBand = 32;       // token blocks walked together, slice group by slice group (workgroup order)
 constexpr int kDMultiple = 64;       // d must be a multiple of this
 
 constexpr int kLossThreads = 256;    // threads per response in the loss kernel
@@ -30,12 +32,31 @@ constexpr int kMeanThreads = 1024;   // threads of the single-block mean
 inline long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
 
 inline int n_vocab_tiles(long long vocab) { return (int)ceil_div(vocab, kBV); }
-inline int n_slices(long long vocab) { return (int)ceil_div(n_vocab_tiles(vocab), kTilesPerSlice); }
+inline int n_slices(long long vocab) {
+  const long long nvt = n_vocab_tiles(vocab);
+  return (int)(nvt < kMaxSlices ? nvt : kMaxSlices);
+}
+
+// Slices per workgroup: 1 while the grid is small (decode-shaped calls keep
+// one workgroup per slice, so every CU streams W), else the largest power of
+// two g with g slices holding at most 1.5 kTilesPerGroup tiles (a power of
+// two divides S = 256 evenly). Changes which workgroup computes a slice,
+// never how: each slice's partial is the same instruction sequence.
+inline int slices_per_group(long long n_tok, long long vocab) {
+  const long long ntb = ceil_div(n_tok, kBT);
+  const long long S = n_slices(vocab), nvt = n_vocab_tiles(vocab);
+  if (ntb * S <= 2048) return 1;
+  long long g = 1;
+  while (2 * g <= S && 2 * g * nvt * 2 <= 3LL * kTilesPerGroup * S) g *= 2;
+  return (int)g;
+}
+inline int n_slice_groups(long long n_tok, long long vocab) {
+  return (int)ceil_div(n_slices(vocab), slices_per_group(n_tok, vocab));
+}
 
 // Slice s covers vocabulary tiles [slice_tile(s), slice_tile(s + 1)): the
-// tiles are split as evenly as possible, so a slice holds
-// floor(n_vt / S) or ceil(n_vt / S) <= kTilesPerSlice tiles. This is a pure
-// function of the vocabulary size.
+// tiles are split as evenly as possible, so a slice holds floor(n_vt / S)
+// or ceil(n_vt / S) tiles. This is a pure function of the vocabulary size.
 __host__ __device__ inline int slice_tile(int s, int n_vt, int S) { return (int)(((long long)s * n_vt) / S); }
 
 }  // namespace itl

@@ -12,14 +12,17 @@
 //
 // Kernel 1 (lmhead_lse_partial) computes z^T tiles on the matrix cores: the
 // MFMA A operand is a 256-row tile of W, the B operand a 256-token block of
-// H, both read K-contiguous. A workgroup owns one token block and one
-// vocabulary slice of kTilesPerSlice tiles and walks the slice's tiles in
-// ascending order; after each tile its lanes fold the tile into a running
-// (max, sum of exp) per token and pick out z[t, y_t] if y_t falls in the
-// tile. The logits never leave registers. At the end of the slice the two
-// lane halves and the two wavefronts that share a token are merged in a
-// fixed order and one (max, sumexp) pair per (slice, token) is written.
-// Kernel 2 (lse_combine) merges a token's slice partials in slice order.
+// H, both read K-contiguous. The vocabulary is cut into S = min(tiles, 256)
+// balanced slices, a function of V alone. A workgroup owns one token block
+// and a run of consecutive slices and walks their tiles in ascending order;
+// after each tile its lanes fold the tile into a running (max, sum of exp)
+// per token and pick out z[t, y_t] if y_t falls in the tile. The logits never
+// leave registers. At each slice end the two lane halves that share a token
+// are merged and each wavefront writes one (max, sumexp) pair per token, then
+// starts the next slice afresh, so the 2 S partials of a token are the same
+// whether a workgroup walks one slice (small batches: every CU streams W) or
+// several (large batches: fewer, longer workgroups).
+// Kernel 2 (lse_combine) merges a token's 2 S partials in a fixed order.
 //
 // Why the bits do not depend on the batch: the tile shapes, K order, slice
 // width and every reduction tree are compile-time constants; a token's
@@ -42,29 +45,34 @@ namespace {
 template <int kDtype>
 __global__ __launch_bounds__(kThreads, 1) void lmhead_lse_partial_kernel(
     const char* __restrict__ H, const char* __restrict__ W, const int32_t* __restrict__ tokens, int n_tok,
-    int row_bytes, int vocab, int n_tb, int n_slices, float2* __restrict__ part, float* __restrict__ zy_out) {
+    int row_bytes, int vocab, int n_tb, int n_slices, int group, float2* __restrict__ part,
+    float* __restrict__ zy_out) {
   __shared__ uint4 smem[kEngineSmemChunks];
   const Lanes L = lanes();
   const int wv = L.wv, wt = L.wt, half = L.half, col = L.col;
 
-  // Workgroup order: super-bands of kSuperBand token blocks, walked slice by
-  // slice with the token block fastest. Workgroups are dispatched to the 8
-  // XCDs round-robin, so the 32 workgroups an XCD runs at once hold 4 token
-  // blocks x 8 slices (each H block read by 8 of them, each W tile by 4,
-  // through the XCD's L2), and all XCDs walk the same slices at the same
-  // time (W shared through the Infinity Cache). The order changes only which
-  // workgroup runs when, never any arithmetic.
+  // Workgroup order: super-bands of kSuperBand token blocks, walked slice
+  // group by slice group with the token block fastest. Workgroups are
+  // dispatched to the 8 XCDs round-robin, so the 32 workgroups an XCD runs
+  // at once hold 4 token blocks x 8 slice groups (each H block read by 8 of
+  // them, each W tile by 4, through the XCD's L2), and all XCDs walk the same
+  // slices at the same time (W shared through the Infinity Cache). The order
+  // and the grouping change only which workgroup computes a slice when,
+  // never any arithmetic.
   const int S = n_slices;
+  const int n_groups = (S + group - 1) / group;
   const int b = blockIdx.x;
-  const int band = b / (kSuperBand * S);
+  const int band = b / (kSuperBand * n_groups);
   const int tb_first = band * kSuperBand;
   const int nb = min(kSuperBand, n_tb - tb_first);
-  const int rem = b - band * kSuperBand * S;
-  const int slice = rem / nb;
+  const int rem = b - band * kSuperBand * n_groups;
+  const int grp = rem / nb;
   const int t0 = (tb_first + rem % nb) * kBT;
   const int n_vt = (vocab + kBV - 1) / kBV;
-  const int tile_begin = slice_tile(slice, n_vt, S);
-  const int tile_end = slice_tile(slice + 1, n_vt, S);
+  const int slice_first = grp * group;
+  const int slice_end = min(slice_first + group, S);
+  const int tile_begin = slice_tile(slice_first, n_vt, S);
+  const int tile_end = slice_tile(slice_end, n_vt, S);
   const int nks = row_bytes / kStepBytes;
 
   // The engine's A operand is the W tile (vocabulary rows), its B operand
@@ -96,6 +104,8 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_lse_partial_kernel(
   // the epilogue needs few VGPRs next to the 256 accumulators. The sampled
   // logit is picked with a select tree keyed on the bits of its row,
   // without a branch.
+  int slice = slice_first;                              // slice of the tiles being folded
+  int slice_last_tile = slice_tile(slice + 1, n_vt, S) - 1;
   auto epilogue = [&](int tile, floatx16 (&acc)[4][4]) {
     const int vw = tile * kBV + wv * 128;
     const bool partial = tile * kBV + kBV > vocab;  // only the vocabulary's last tile
@@ -142,48 +152,41 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_lse_partial_kernel(
         mrun[bn] = mnew;
       }
     }
+    if (tile == slice_last_tile) {
+      // Slice end: lanes l and l^32 hold the same tokens (different rows);
+      // each wavefront writes its own partial (wv = 0, 1) and starts over.
+#pragma unroll
+      for (int bn = 0; bn < 4; ++bn) {
+        const float m2 = __shfl_xor(mrun[bn], 32, 64);
+        const float s2 = __shfl_xor(srun[bn], 32, 64);
+        lse_merge(mrun[bn], srun[bn], m2, s2);
+        const int tok = t0 + wt * 128 + bn * 32 + col;
+        if (half == 0 && tok < n_tok) part[((size_t)slice * 2 + wv) * n_tok + tok] = make_float2(mrun[bn], srun[bn]);
+        mrun[bn] = -INFINITY;
+        srun[bn] = 0.0f;
+      }
+      ++slice;
+      slice_last_tile = slice_tile(slice + 1, n_vt, S) - 1;
+    }
   };
   run_tiles<kDtype>(smem, L, row_bytes, tile_begin, tile_end, nks, w_rsrc, hr, epilogue);
 
-  // Slice end. Lanes l and l^32 hold the same tokens (different rows).
 #pragma unroll
-  for (int bn = 0; bn < 4; ++bn) {
-    const float m2 = __shfl_xor(mrun[bn], 32, 64);
-    const float s2 = __shfl_xor(srun[bn], 32, 64);
-    lse_merge(mrun[bn], srun[bn], m2, s2);
+  for (int bn = 0; bn < 4; ++bn)
     if (found[bn]) zy_out[t0 + wt * 128 + bn * 32 + col] = zy[bn];
-  }
-  // Wavefronts wv = 0 and wv = 1 hold the same tokens; merge through LDS
-  // (run_tiles returns with every wavefront done with the ring).
-  float2* xch = reinterpret_cast<float2*>(smem);
-  if (wv == 1 && half == 0) {
-#pragma unroll
-    for (int bn = 0; bn < 4; ++bn) xch[wt * 128 + bn * 32 + col] = make_float2(mrun[bn], srun[bn]);
-  }
-  __syncthreads();
-  if (wv == 0 && half == 0) {
-#pragma unroll
-    for (int bn = 0; bn < 4; ++bn) {
-      const int tok = t0 + wt * 128 + bn * 32 + col;
-      const float2 o = xch[wt * 128 + bn * 32 + col];
-      float m = mrun[bn], s = srun[bn];
-      lse_merge(m, s, o.x, o.y);
-      if (tok < n_tok) part[(size_t)slice * n_tok + tok] = make_float2(m, s);
-    }
-  }
 }
 
-// Per token: merge the slice partials in ascending slice order.
+// Per token: merge the 2 S partials (slice-major, then wavefront) in order.
 __global__ __launch_bounds__(256) void lse_combine_kernel(const float2* __restrict__ part,
                                                           const float* __restrict__ zy, int n_tok,
-                                                          int n_slices, float* __restrict__ logprob,
+                                                          int n_parts, float* __restrict__ logprob,
                                                           float* __restrict__ lse) {
   const int t = blockIdx.x * 256 + threadIdx.x;
   if (t >= n_tok) return;
   float M = -INFINITY;
-  for (int s = 0; s < n_slices; ++s) M = fmaxf(M, part[(size_t)s * n_tok + t].x);
+  for (int s = 0; s < n_parts; ++s) M = fmaxf(M, part[(size_t)s * n_tok + t].x);
   float S = 0.0f;
-  for (int s = 0; s < n_slices; ++s) {
+  for (int s = 0; s < n_parts; ++s) {
     const float2 p = part[(size_t)s * n_tok + t];
     S += p.y * fast_exp2((p.x - M) * kLog2e);
   }
@@ -196,7 +199,7 @@ __global__ __launch_bounds__(256) void lse_combine_kernel(const float2* __restri
 
 size_t lmhead_workspace_bytes(long long n_tok, long long vocab) {
   if (n_tok <= 0) return 0;
-  return align256((size_t)n_slices(vocab) * (size_t)n_tok * sizeof(float2)) + align256((size_t)n_tok * sizeof(float));
+  return align256((size_t)2 * n_slices(vocab) * (size_t)n_tok * sizeof(float2)) + align256((size_t)n_tok * sizeof(float));
 }
 
 hipError_t launch_lmhead_logprob(const void* H, const void* W, int dtype, int n_tok, int d, int vocab,
@@ -205,21 +208,22 @@ hipError_t launch_lmhead_logprob(const void* H, const void* W, int dtype, int n_
   const int es = dtype == 0 ? 2 : 4;
   const int row_bytes = d * es;
   const int S = n_slices(vocab);
+  const int G = slices_per_group(n_tok, vocab);
   const int ntb = (int)ceil_div(n_tok, kBT);
   float2* part = static_cast<float2*>(workspace);
   float* zy = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                       align256((size_t)S * (size_t)n_tok * sizeof(float2)));
-  const dim3 grid((unsigned)ntb * (unsigned)S);
+                                       align256((size_t)2 * S * (size_t)n_tok * sizeof(float2)));
+  const dim3 grid((unsigned)ntb * (unsigned)n_slice_groups(n_tok, vocab));
   if (dtype == 0)
     hipLaunchKernelGGL(lmhead_lse_partial_kernel<0>, grid, dim3(kThreads), 0, stream, static_cast<const char*>(H),
-                       static_cast<const char*>(W), tokens, n_tok, row_bytes, vocab, ntb, S, part, zy);
+                       static_cast<const char*>(W), tokens, n_tok, row_bytes, vocab, ntb, S, G, part, zy);
   else
     hipLaunchKernelGGL(lmhead_lse_partial_kernel<1>, grid, dim3(kThreads), 0, stream, static_cast<const char*>(H),
-                       static_cast<const char*>(W), tokens, n_tok, row_bytes, vocab, ntb, S, part, zy);
+                       static_cast<const char*>(W), tokens, n_tok, row_bytes, vocab, ntb, S, G, part, zy);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(lse_combine_kernel, dim3((unsigned)ceil_div(n_tok, 256)), dim3(256), 0, stream, part, zy, n_tok,
-                     S, logprob, lse);
+                     2 * S, logprob, lse);
   return hipGetLastError();
 }
 

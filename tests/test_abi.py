@@ -51,7 +51,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_build_info_and_status_strings(lib):
     info = lib.itl_build_info().decode()
-    assert "gfx950" in info and "tiles_per_slice=16" in info
+    assert "gfx950" in info and "max_slices=256" in info
     for s in range(6):
         assert lib.itl_status_string(s)
 
@@ -79,10 +79,11 @@ def test_lmhead_argument_validation(lib):
 
 def test_workspace_sizes(lib):
     assert lib.itl_lmhead_logprob_workspace_bytes(0, 100) == 0
-    n, V = 1000, 151936
-    slices = -(-(-(-V // 256)) // 16)
-    want = -(-slices * n * 8 // 256) * 256 + -(-n * 4 // 256) * 256
-    assert lib.itl_lmhead_logprob_workspace_bytes(n, V) == want
+    # one (max, sumexp) float pair per token, slice and wavefront (2 per
+    # slice), slices = min(vocabulary tiles, 256); then one float per token
+    for n, V, slices in ((1000, 151936, 256), (1000, 5000, 20), (3, 1, 1)):
+        want = -(-2 * slices * n * 8 // 256) * 256 + -(-n * 4 // 256) * 256
+        assert lib.itl_lmhead_logprob_workspace_bytes(n, V) == want
     assert lib.itl_lmhead_logprob_workspace_bytes(-1, V) == ctypes.c_size_t(-1).value
 
 

@@ -63,13 +63,14 @@ def test_tiny_workload_all_tokens(cuda):
 @pytest.mark.parametrize(
     "n_tok,d,vocab,dtype_name",
     [
-        (700, 256, 5000, "bf16"),    # 3 token blocks (ragged), 20 vocab tiles, 2 slices, ragged tail
-        (300, 128, 4096 + 37, "bf16"),  # last slice = one partial tile of 37 rows
+        (700, 256, 5000, "bf16"),    # 3 token blocks (ragged), 20 vocab tiles = 20 slices, ragged tail
+        (300, 128, 4096 + 37, "bf16"),  # last tile (and slice) holds 37 rows
         (257, 64, 1000, "f32"),      # one K step per tile, fp32 MFMA
         (1, 192, 300, "bf16"),       # one token
         (5, 64, 1, "bf16"),          # vocabulary of one: logprob = 0 exactly
         (64, 64, 3, "f32"),          # tiny vocabulary, mostly masked tile
-        (513, 320, 8192 + 256, "bf16"),  # 3 slices, the last one a single full tile
+        (513, 320, 8192 + 256, "bf16"),  # 33 slices of one tile, d not a multiple of 256
+        (5200, 64, 150 * 256 - 17, "bf16"),  # 21 x 150 > 2048: 8 slices per workgroup, last group of 6
     ],
 )
 def test_shapes_ragged_and_degenerate(cuda, n_tok, d, vocab, dtype_name):
