@@ -145,7 +145,7 @@ def fwd_bwd_step(s, ev=None):
         ev[1].record()
 
 
-def decode_leg(wl, device, batch_sizes=(1, 8, 64, 256), calls=20):
+def decode_leg(wl, device, batch_sizes=(1, 8, 64, 128, 256), calls=20):
     """Decode-shaped calls (a rollout engine's step: one new token for each of
     M sequences) on the head: the invariant kernel against a non-invariant
     fast baseline run as a library (hipBLASLt GEMM with bf16 logits, then

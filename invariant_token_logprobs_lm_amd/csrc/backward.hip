@@ -313,7 +313,8 @@ struct BwdLayout {
 
 size_t sort_temp_bytes(long long n_tok) {
   size_t bytes = 0;
-  hipcub::DeviceRadixSort::SortPairs(nullptr, bytes, (const uint32_t*)nullptr, (uint32_t*)nullptr,
+  // A size query (null temp storage): computes `bytes`, launches nothing.
+  (void)hipcub::DeviceRadixSort::SortPairs(nullptr, bytes, (const uint32_t*)nullptr, (uint32_t*)nullptr,
                                      (const uint32_t*)nullptr, (uint32_t*)nullptr, (int)n_tok, 0, 32, nullptr);
   return bytes;
 }

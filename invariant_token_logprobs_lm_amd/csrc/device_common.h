@@ -31,8 +31,9 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
 // Merge two partial log-sum-exp states (m = running max, s = sum of
-// exp(z - m)). The result depends only on the two inputs (fp add and max are
-// commutative), so callers fix the tree shape and get fixed bits.
+// exp(z - m)) as s exp(m - M) + s2 exp(m2 - M), the first product fused
+// into the add. The result is a fixed function of the two states in this
+// argument order, so callers fix the merge tree and get fixed bits.
 __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
   const float M = fmaxf(m, m2);
   if (M == -INFINITY) {  // both sides empty
@@ -40,7 +41,7 @@ __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2
     s = 0.0f;
     return;
   }
-  s = s * fast_exp2((m - M) * kLog2e) + s2 * fast_exp2((m2 - M) * kLog2e);
+  s = __builtin_fmaf(s, fast_exp2((m - M) * kLog2e), s2 * fast_exp2((m2 - M) * kLog2e));
   m = M;
 }
 

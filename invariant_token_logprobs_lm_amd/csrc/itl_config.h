@@ -23,6 +23,8 @@ constexpr int kHSlots = 2;           // LDS slots of the H-block ring (loads one
 constexpr int kMaxSlices = 256;      // vocabulary slices: min(tiles, this), a function of the vocabulary only
 constexpr int kTilesPerGroup = 16;   // grid shape only: a workgroup walks about this many tiles of consecutive
                                      // slices when the batch is large (the arithmetic per slice is the same)
+constexpr int kNarrowBRows = 64;      // tokens per block of the narrow (few-token) kernel
+constexpr int kNarrowMaxTokens = 64;   // calls with at most this many tokens use the narrow kernel
 constexpr int kSuperBand = 32;       // token blocks walked together, slice group by slice group (workgroup order)
 constexpr int kDMultiple = 64;       // d must be a multiple of this
 

@@ -42,6 +42,74 @@ namespace itl {
 
 namespace {
 
+// Online log-sum-exp state of one token column in one lane: the running
+// (max, sum of exp) of the slice so far, and the sampled logit once seen.
+struct Col {
+  int y;          // sampled row, -1 past the last token
+  float m, s;     // running max and sum of exp(z - m)
+  float zy;       // the sampled logit
+  bool found;
+};
+
+// Fold one 32 x 32 accumulator block (rows vw + 32 bm + ..., this lane's
+// token column) into the state. The lane's 16 logits are copied out of the
+// matrix-core registers where they are used (acc_read), so the fold needs
+// few VGPRs next to the accumulators. The sampled logit is picked with a
+// select tree keyed on the bits of its row, without a branch. Every kernel
+// folds with this one function, in the same block order, so a token's state
+// has the same bits whichever kernel computed it.
+__device__ __forceinline__ void fold_block(Col& c, const floatx16& a, int bm, int vw, int half, int vocab,
+                                           bool partial) {
+  const int o = c.y - vw;  // sampled row relative to this wavefront's 128 rows
+  // Register i of a lane holds row 32 bm + 8 (i / 4) + 4 half + (i % 4):
+  // bits 0, 1, 3, 4 of the row pick i, bit 2 picks the lane half.
+  const bool b0 = (o & 1) != 0, b1 = (o & 2) != 0, b2 = (o & 8) != 0, b3 = (o & 16) != 0;
+  const bool here = (unsigned)o < 128u && ((o >> 2) & 1) == half && (o >> 5) == bm;
+  floatx16 z;  // a vector, not an array: it must stay in registers
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = acc_read(a, i);
+  if (partial) {
+    const int lim = vocab - (vw + bm * 32 + 4 * half);  // rows at or past this offset do not exist
+#pragma unroll
+    for (int i = 0; i < 16; ++i) z[i] = (8 * (i >> 2) + (i & 3) >= lim) ? -INFINITY : z[i];
+  }
+  const float pick = select16(z, b0, b1, b2, b3);
+  c.zy = here ? pick : c.zy;
+  c.found = c.found || here;
+
+  float bmax = z[0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) bmax = fmaxf(bmax, z[i]);
+  const float mnew = fmaxf(c.m, bmax);
+  // A lane whose rows so far are all absent has mnew = -inf; it then scales
+  // by exp2(-inf) = 0 around 0 and keeps (m, s) = (-inf, 0).
+  const float mref = mnew == -INFINITY ? 0.0f : mnew;
+  // (z - m) is exactly 0 for the running maximum, so its term is exactly 1
+  // and stays 1 (later rescales by exp2(0)): the final sum is >= 1 and
+  // logprob <= 0 holds in fp32.
+  float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; i += 2) {
+    s0 += fast_exp2((z[i] - mref) * kLog2e);
+    s1 += fast_exp2((z[i + 1] - mref) * kLog2e);
+  }
+  c.s = __builtin_fmaf(c.s, fast_exp2((c.m - mref) * kLog2e), s0 + s1);
+  c.m = mnew;
+}
+
+// Slice end: lanes l and l ^ 32 hold the same token (different rows); the
+// lower lane merges the upper lane's state into its own and writes the
+// wavefront's partial of the slice; every lane starts the next slice afresh.
+__device__ __forceinline__ void flush_slice(Col& c, int tok, int n_tok, int half, size_t part_index,
+                                            float2* __restrict__ part) {
+  const float m2 = __shfl_xor(c.m, 32, 64);
+  const float s2 = __shfl_xor(c.s, 32, 64);
+  lse_merge(c.m, c.s, m2, s2);
+  if (half == 0 && tok < n_tok) part[part_index] = make_float2(c.m, c.s);
+  c.m = -INFINITY;
+  c.s = 0.0f;
+}
+
 template <int kDtype>
 __global__ __launch_bounds__(kThreads, 1) void lmhead_lse_partial_kernel(
     const char* __restrict__ H, const char* __restrict__ W, const int32_t* __restrict__ tokens, int n_tok,
@@ -78,17 +146,11 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_lse_partial_kernel(
   // The engine's A operand is the W tile (vocabulary rows), its B operand
   // the H block (tokens): lane l's accumulators are vocabulary rows of token
   // t0 + 128 wt + 32 bn + (l mod 32).
-  int y[4];
-  float mrun[4], srun[4], zy[4];
-  bool found[4];
+  Col c[4];
 #pragma unroll
   for (int bn = 0; bn < 4; ++bn) {
     const int tok = t0 + wt * 128 + bn * 32 + col;
-    y[bn] = tok < n_tok ? tokens[tok] : -1;
-    mrun[bn] = -INFINITY;
-    srun[bn] = 0.0f;
-    zy[bn] = 0.0f;
-    found[bn] = false;
+    c[bn] = Col{tok < n_tok ? tokens[tok] : -1, -INFINITY, 0.0f, 0.0f, false};
   }
 
   auto w_rsrc = [&](int tile) {
@@ -97,73 +159,21 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_lse_partial_kernel(
   };
   const int4v hr = rsrc_words(H + (size_t)t0 * row_bytes, (uint32_t)min(kBT, n_tok - t0) * row_bytes);
 
-  // Tile epilogue: fold the tile's logits into the running state. Each lane
-  // folds its 16 logits of one 32x32 block at a time into the running (max,
-  // sum of exp) of that token column; the logits are copied out of the
-  // matrix-core registers 16 at a time, where they are used (acc_read), so
-  // the epilogue needs few VGPRs next to the 256 accumulators. The sampled
-  // logit is picked with a select tree keyed on the bits of its row,
-  // without a branch.
-  int slice = slice_first;                              // slice of the tiles being folded
+  int slice = slice_first;  // slice of the tiles being folded
   int slice_last_tile = slice_tile(slice + 1, n_vt, S) - 1;
   auto epilogue = [&](int tile, floatx16 (&acc)[4][4]) {
     const int vw = tile * kBV + wv * 128;
     const bool partial = tile * kBV + kBV > vocab;  // only the vocabulary's last tile
     mfma_result_wait();
 #pragma unroll
-    for (int bn = 0; bn < 4; ++bn) {
-      const int o = y[bn] - vw;  // sampled row relative to this wavefront's 128 rows
-      // Register i of a lane holds row 32 bm + 8 (i / 4) + 4 half + (i % 4):
-      // bits 0, 1, 3, 4 of the row pick i, bit 2 picks the lane half.
-      const bool b0 = (o & 1) != 0, b1 = (o & 2) != 0, b2 = (o & 8) != 0, b3 = (o & 16) != 0;
-      const bool mine = (unsigned)o < 128u && ((o >> 2) & 1) == half;
+    for (int bn = 0; bn < 4; ++bn)
 #pragma unroll
-      for (int bm = 0; bm < 4; ++bm) {
-        floatx16 z;  // a vector, not an array: it must stay in registers
-#pragma unroll
-        for (int i = 0; i < 16; ++i) z[i] = acc_read(acc[bm][bn], i);
-        if (partial) {
-          const int lim = vocab - (vw + bm * 32 + 4 * half);  // rows at or past this offset do not exist
-#pragma unroll
-          for (int i = 0; i < 16; ++i) z[i] = (8 * (i >> 2) + (i & 3) >= lim) ? -INFINITY : z[i];
-        }
-        const float pick = select16(z, b0, b1, b2, b3);
-        const bool here = mine && (o >> 5) == bm;
-        zy[bn] = here ? pick : zy[bn];
-        found[bn] = found[bn] || here;
-
-        float bmax = z[0];
-#pragma unroll
-        for (int i = 1; i < 16; ++i) bmax = fmaxf(bmax, z[i]);
-        const float mnew = fmaxf(mrun[bn], bmax);
-        // A lane whose rows so far are all absent has mnew = -inf; it then
-        // scales by exp2(-inf) = 0 around 0 and keeps (m, s) = (-inf, 0).
-        const float mref = mnew == -INFINITY ? 0.0f : mnew;
-        // (z - m) is exactly 0 for the running maximum, so its term is
-        // exactly 1 and stays 1 (later rescales by exp2(0)): the final sum
-        // is >= 1 and logprob <= 0 holds in fp32.
-        float s0 = 0.0f, s1 = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 16; i += 2) {
-          s0 += fast_exp2((z[i] - mref) * kLog2e);
-          s1 += fast_exp2((z[i + 1] - mref) * kLog2e);
-        }
-        srun[bn] = srun[bn] * fast_exp2((mrun[bn] - mref) * kLog2e) + (s0 + s1);
-        mrun[bn] = mnew;
-      }
-    }
+      for (int bm = 0; bm < 4; ++bm) fold_block(c[bn], acc[bm][bn], bm, vw, half, vocab, partial);
     if (tile == slice_last_tile) {
-      // Slice end: lanes l and l^32 hold the same tokens (different rows);
-      // each wavefront writes its own partial (wv = 0, 1) and starts over.
 #pragma unroll
       for (int bn = 0; bn < 4; ++bn) {
-        const float m2 = __shfl_xor(mrun[bn], 32, 64);
-        const float s2 = __shfl_xor(srun[bn], 32, 64);
-        lse_merge(mrun[bn], srun[bn], m2, s2);
         const int tok = t0 + wt * 128 + bn * 32 + col;
-        if (half == 0 && tok < n_tok) part[((size_t)slice * 2 + wv) * n_tok + tok] = make_float2(mrun[bn], srun[bn]);
-        mrun[bn] = -INFINITY;
-        srun[bn] = 0.0f;
+        flush_slice(c[bn], tok, n_tok, half, ((size_t)slice * 2 + wv) * n_tok + tok, part);
       }
       ++slice;
       slice_last_tile = slice_tile(slice + 1, n_vt, S) - 1;
@@ -173,24 +183,83 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_lse_partial_kernel(
 
 #pragma unroll
   for (int bn = 0; bn < 4; ++bn)
-    if (found[bn]) zy_out[t0 + wt * 128 + bn * 32 + col] = zy[bn];
+    if (c[bn].found) zy_out[t0 + wt * 128 + bn * 32 + col] = c[bn].zy;
 }
 
-// Per token: merge the 2 S partials (slice-major, then wavefront) in order.
-__global__ __launch_bounds__(256) void lse_combine_kernel(const float2* __restrict__ part,
-                                                          const float* __restrict__ zy, int n_tok,
-                                                          int n_parts, float* __restrict__ logprob,
-                                                          float* __restrict__ lse) {
-  const int t = blockIdx.x * 256 + threadIdx.x;
-  if (t >= n_tok) return;
-  float M = -INFINITY;
-  for (int s = 0; s < n_parts; ++s) M = fmaxf(M, part[(size_t)s * n_tok + t].x);
-  float S = 0.0f;
-  for (int s = 0; s < n_parts; ++s) {
-    const float2 p = part[(size_t)s * n_tok + t];
-    S += p.y * fast_exp2((p.x - M) * kLog2e);
+// The same partials for few tokens: 64-token blocks, one workgroup per
+// (token block, slice), the workgroup's slice walked by run_tiles_narrow.
+// Lane l of wavefront (wv, wt) holds token t0 + 32 wt + (l mod 32) against
+// the same W rows, with the same fold, as in lmhead_lse_partial_kernel, so
+// the partials (and the logprobs) have the same bits.
+template <int kDtype>
+__global__ __launch_bounds__(kThreads, 1) void lmhead_lse_partial_narrow_kernel(
+    const char* __restrict__ H, const char* __restrict__ W, const int32_t* __restrict__ tokens, int n_tok,
+    int row_bytes, int vocab, int n_slices, float2* __restrict__ part, float* __restrict__ zy_out) {
+  __shared__ uint4 smem[kEngineSmemChunks];
+  const Lanes L = lanes();
+  const int wv = L.wv, wt = L.wt, half = L.half, col = L.col;
+  // Token block fastest-varying after the slice: with 256 slices the token
+  // blocks of a slice share an XCD (blockIdx mod 8) and its L2.
+  const int S = n_slices;
+  const int slice = blockIdx.x % S;
+  const int t0 = (blockIdx.x / S) * kNarrowBRows;
+  const int n_vt = (vocab + kBV - 1) / kBV;
+  const int tile_begin = slice_tile(slice, n_vt, S);
+  const int tile_end = slice_tile(slice + 1, n_vt, S);
+  const int nks = row_bytes / kStepBytes;
+  const int tok = t0 + wt * 32 + col;
+  Col c = Col{tok < n_tok ? tokens[tok] : -1, -INFINITY, 0.0f, 0.0f, false};
+
+  auto w_rsrc = [&](int tile) {
+    const int v0 = tile * kBV;
+    return rsrc_words(W + (size_t)v0 * row_bytes, (uint32_t)min(kBV, vocab - v0) * row_bytes);
+  };
+  const int4v hr = rsrc_words(H + (size_t)t0 * row_bytes, (uint32_t)min(kNarrowBRows, n_tok - t0) * row_bytes);
+  auto epilogue = [&](int tile, floatx16 (&acc)[4]) {
+    const int vw = tile * kBV + wv * 128;
+    const bool partial = tile * kBV + kBV > vocab;
+    mfma_result_wait();
+#pragma unroll
+    for (int bm = 0; bm < 4; ++bm) fold_block(c, acc[bm], bm, vw, half, vocab, partial);
+  };
+  run_tiles_narrow<kDtype>(smem, L, row_bytes, tile_begin, tile_end, nks, w_rsrc, hr, epilogue);
+  flush_slice(c, tok, n_tok, half, ((size_t)slice * 2 + wv) * n_tok + tok, part);
+  if (c.found) zy_out[tok] = c.zy;
+}
+
+// Per token: merge the 2 S partials (slice-major, then wavefront). A
+// 1024-thread workgroup takes 64 tokens (lane = token, so every load is one
+// coalesced 512-byte row of the partial table); its 16 wavefronts split the
+// partials into 16 fixed consecutive runs, fold each run in order, and the
+// 16 run states are merged in run order. The run boundaries depend on S only,
+// so a token's result has the same bits whatever n_tok; with few tokens the
+// 16 runs keep the latency chain short (at most 32 dependent merges).
+constexpr int kCombineWaves = 16;
+
+__global__ __launch_bounds__(64 * kCombineWaves) void lse_combine_kernel(const float2* __restrict__ part,
+                                                                         const float* __restrict__ zy, int n_tok,
+                                                                         int n_parts, float* __restrict__ logprob,
+                                                                         float* __restrict__ lse) {
+  __shared__ float2 run_state[kCombineWaves][64];
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int t = blockIdx.x * 64 + lane;
+  const int run = (n_parts + kCombineWaves - 1) / kCombineWaves;
+  const int p0 = min(w * run, n_parts), p1 = min(p0 + run, n_parts);
+  float m = -INFINITY, s = 0.0f;
+  if (t < n_tok) {
+#pragma unroll 8
+    for (int p = p0; p < p1; ++p) {
+      const float2 v = part[(size_t)p * n_tok + t];
+      lse_merge(m, s, v.x, v.y);
+    }
   }
-  const float l = M + fast_log2(S) * kLn2;
+  run_state[w][lane] = make_float2(m, s);
+  __syncthreads();
+  if (w != 0 || t >= n_tok) return;
+#pragma unroll
+  for (int r = 1; r < kCombineWaves; ++r) lse_merge(m, s, run_state[r][lane].x, run_state[r][lane].y);
+  const float l = m + fast_log2(s) * kLn2;
   logprob[t] = zy[t] - l;
   if (lse) lse[t] = l;
 }
@@ -213,17 +282,29 @@ hipError_t launch_lmhead_logprob(const void* H, const void* W, int dtype, int n_
   float2* part = static_cast<float2*>(workspace);
   float* zy = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                        align256((size_t)2 * S * (size_t)n_tok * sizeof(float2)));
-  const dim3 grid((unsigned)ntb * (unsigned)n_slice_groups(n_tok, vocab));
-  if (dtype == 0)
-    hipLaunchKernelGGL(lmhead_lse_partial_kernel<0>, grid, dim3(kThreads), 0, stream, static_cast<const char*>(H),
-                       static_cast<const char*>(W), tokens, n_tok, row_bytes, vocab, ntb, S, G, part, zy);
-  else
-    hipLaunchKernelGGL(lmhead_lse_partial_kernel<1>, grid, dim3(kThreads), 0, stream, static_cast<const char*>(H),
-                       static_cast<const char*>(W), tokens, n_tok, row_bytes, vocab, ntb, S, G, part, zy);
+  if (n_tok <= kNarrowMaxTokens) {
+    const dim3 grid((unsigned)ceil_div(n_tok, kNarrowBRows) * (unsigned)S);
+    if (dtype == 0)
+      hipLaunchKernelGGL(lmhead_lse_partial_narrow_kernel<0>, grid, dim3(kThreads), 0, stream,
+                         static_cast<const char*>(H), static_cast<const char*>(W), tokens, n_tok, row_bytes, vocab, S,
+                         part, zy);
+    else
+      hipLaunchKernelGGL(lmhead_lse_partial_narrow_kernel<1>, grid, dim3(kThreads), 0, stream,
+                         static_cast<const char*>(H), static_cast<const char*>(W), tokens, n_tok, row_bytes, vocab, S,
+                         part, zy);
+  } else {
+    const dim3 grid((unsigned)ntb * (unsigned)n_slice_groups(n_tok, vocab));
+    if (dtype == 0)
+      hipLaunchKernelGGL(lmhead_lse_partial_kernel<0>, grid, dim3(kThreads), 0, stream, static_cast<const char*>(H),
+                         static_cast<const char*>(W), tokens, n_tok, row_bytes, vocab, ntb, S, G, part, zy);
+    else
+      hipLaunchKernelGGL(lmhead_lse_partial_kernel<1>, grid, dim3(kThreads), 0, stream, static_cast<const char*>(H),
+                         static_cast<const char*>(W), tokens, n_tok, row_bytes, vocab, ntb, S, G, part, zy);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(lse_combine_kernel, dim3((unsigned)ceil_div(n_tok, 256)), dim3(256), 0, stream, part, zy, n_tok,
-                     2 * S, logprob, lse);
+  hipLaunchKernelGGL(lse_combine_kernel, dim3((unsigned)ceil_div(n_tok, 64)), dim3(64 * kCombineWaves), 0, stream,
+                     part, zy, n_tok, 2 * S, logprob, lse);
   return hipGetLastError();
 }
 

@@ -345,4 +345,113 @@ __device__ __forceinline__ void run_tiles(uint4* smem, const Lanes& L, int row_b
   __syncthreads();
 }
 
+// Narrow variant for few B rows (decode-shaped calls): the same A tiles
+// against a 64-row B block. Wavefront (wv, wt) holds rows 128 wv .. 128 wv +
+// 127 of the A tile against B rows 32 wt .. 32 wt + 31 as 4 blocks of 32 x 32.
+// Every MFMA of an accumulator block takes the same operand fragments, in
+// the same order, as in run_tiles (same slot layout and swizzle, same K
+// sub-step order, fresh accumulators at a tile's first step), so an output
+// element has the same bits in both. The work per A tile is a quarter of
+// run_tiles': the loop streams A from memory, so both operands rotate through
+// four slots and are loaded three K steps ahead.
+constexpr int kNarrowSlots = 4;
+constexpr int kNarrowBSlotChunks = kNarrowBRows * kRowChunks;  // 512 chunks = 8 KiB
+constexpr int kNarrowBDmaPerWave = kNarrowBRows / 4 / kDmaRows;  // 2
+static_assert(kNarrowSlots * (kSlotChunks + kNarrowBSlotChunks) <= kEngineSmemChunks, "LDS budget");
+
+template <int kDtype, class ARsrc, class Epi>
+__device__ __forceinline__ void run_tiles_narrow(uint4* smem, const Lanes& L, int row_bytes, int tile_begin,
+                                                 int tile_end, int nks, const ARsrc& a_rsrc, int4v b_rsrc, Epi&& epi) {
+  const int lane = L.lane, wave = L.wave, wv = L.wv, wt = L.wt, half = L.half, col = L.col;
+  // Loader: wavefront w fills A rows 64 w .. 64 w + 63 (8 loads) and B rows
+  // 16 w .. 16 w + 15 (2 loads) of a slot; lane i fetches row (i / 8) of an
+  // 8-row group at logical chunk (i % 8) ^ swz(row), as in run_tiles.
+  const int lr = lane >> 3;
+  uint32_t avoff[kDmaPerWave], bvoff[kNarrowBDmaPerWave];
+#pragma unroll
+  for (int j = 0; j < kDmaPerWave; ++j)
+    avoff[j] = (uint32_t)(wave * 64 + j * kDmaRows + lr) * (uint32_t)row_bytes + (((lane & 7) ^ lr ^ (j & 1)) * 16);
+#pragma unroll
+  for (int j = 0; j < kNarrowBDmaPerWave; ++j)
+    bvoff[j] = (uint32_t)(wave * 16 + j * kDmaRows + lr) * (uint32_t)row_bytes + (((lane & 7) ^ lr ^ (j & 1)) * 16);
+  const uint32_t lds0 = (uint32_t)(size_t)((__attribute__((address_space(3))) uint4*)smem);
+  auto a_lds = [&](int slot) { return lds0 + (uint32_t)slot * kSlotBytes + (uint32_t)wave * 64 * kStepBytes; };
+  auto b_lds = [&](int slot) {
+    return lds0 + (uint32_t)kNarrowSlots * kSlotBytes + (uint32_t)slot * kNarrowBSlotChunks * 16 +
+           (uint32_t)wave * 16 * kStepBytes;
+  };
+  // Load K step (tile, ks) of both operands into a slot: B first, then A.
+  auto load_step = [&](int tile, int ks, int slot) {
+    const int4v ar = a_rsrc(tile);
+    const uint32_t so = (uint32_t)ks * kStepBytes;
+#pragma unroll
+    for (int j = 0; j < kNarrowBDmaPerWave; ++j) dma16(b_rsrc, bvoff[j], so, b_lds(slot) + j * 1024);
+#pragma unroll
+    for (int j = 0; j < kDmaPerWave; ++j) dma16(ar, avoff[j], so, a_lds(slot) + j * 1024);
+  };
+  // Loads run over the steps (tile, ks), K fastest, clamped at the last step
+  // (a clamped load refills a free slot that nothing reads again).
+  int ld_tile = tile_begin, ld_ks = 0;
+  auto next_load = [&]() {
+    if (++ld_ks == nks) {
+      ld_ks = 0;
+      if (ld_tile + 1 < tile_end) ++ld_tile;
+      else ld_ks = nks - 1;
+    }
+  };
+#pragma unroll
+  for (int p = 0; p < kNarrowSlots - 1; ++p) {
+    load_step(ld_tile, ld_ks, p);
+    next_load();
+  }
+  // MFMA operand reads: row (l mod 32) of each 32-row block at logical chunk
+  // 2 kk + l / 32 of sub-step kk, as in run_tiles.
+  int a_off[4], b_off[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const int pc = (2 * kk + half) ^ swz(col);
+    a_off[kk] = (wv * 128 + col) * kRowChunks + pc;
+    b_off[kk] = (wt * 32 + col) * kRowChunks + pc;
+  }
+  constexpr int kPending = (kNarrowSlots - 2) * (kDmaPerWave + kNarrowBDmaPerWave);
+  int slot = 0;
+  // One K step; kFirst = the tile's first (fresh accumulators).
+  auto k_step = [&](floatx16 (&acc)[4], auto first) {
+    // This step's loads landed (the next two steps' may be in flight);
+    // every wavefront is done reading the previous step's slot.
+    wait_and_barrier<kPending>();
+    load_step(ld_tile, ld_ks, slot == 0 ? kNarrowSlots - 1 : slot - 1);
+    next_load();
+    const uint4* sa = smem + slot * kSlotChunks;
+    const uint4* sb = smem + kNarrowSlots * kSlotChunks + slot * kNarrowBSlotChunks;
+    // All 20 fragments of the step are read up front (one LDS round trip
+    // per step rather than one per sub-step), then the 16 MFMAs.
+    uint4 A[4][4], B[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) A[kk][m] = sa[a_off[kk] + m * 32 * kRowChunks];
+      B[kk] = sb[b_off[kk]];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        if (decltype(first)::value && kk == 0) Mma<kDtype>::first(acc[m], A[kk][m], B[kk]);
+        else Mma<kDtype>::step(acc[m], A[kk][m], B[kk]);
+      }
+    }
+    slot = slot == kNarrowSlots - 1 ? 0 : slot + 1;
+  };
+  for (int tile = tile_begin; tile < tile_end; ++tile) {
+    floatx16 acc[4];
+    k_step(acc, std::true_type{});
+    for (int ks = 1; ks < nks; ++ks) k_step(acc, std::false_type{});
+    epi(tile, acc);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+}
+
 }  // namespace itl

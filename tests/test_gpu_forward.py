@@ -133,6 +133,42 @@ def test_row_position_invariance(cuda):
         assert same_bits(lp[pos:pos + 1], alone_lp) and same_bits(lse[pos:pos + 1], alone_lse), pos
 
 
+@pytest.mark.parametrize(
+    "d,vocab,dtype_name",
+    [
+        (2560, 151936, "bf16"),   # 256 slices of 2 or 3 tiles, partial last tile
+        (128, 4096 + 37, "bf16"),  # one tile per slice, last tile of 37 rows
+        (64, 1000, "f32"),        # fp32 MFMA
+    ],
+)
+def test_narrow_and_wide_kernels_agree(cuda, d, vocab, dtype_name):
+    """Calls of at most narrow_max_tokens tokens (build info) run the narrow
+    kernel (64-token blocks), larger ones the 256-token block kernel: the
+    same tokens give the same bits either way, at every row of a narrow
+    block and across blocks."""
+    import re
+    import torch
+
+    dt = torch.bfloat16 if dtype_name == "bf16" else torch.float32
+    H, W, y = _random_head(600, d, vocab, dt, seed=d + vocab, device=cuda)
+    itl = _itl()
+    limit = int(re.search(r"narrow_max_tokens=(\d+)", itl.build_info()).group(1))
+    assert limit >= 1
+    lp, lse = itl.lmhead_logprob(H, W, y)  # wide kernel
+    for lo, n in ((0, 1), (5, 7), (100, min(limit, 33)), (300, limit), (472, limit + 1), (200, 129)):
+        lp_n, lse_n = itl.lmhead_logprob(H[lo:lo + n], W, y[lo:lo + n])
+        assert same_bits(lp_n, lp[lo:lo + n]) and same_bits(lse_n, lse[lo:lo + n]), (lo, n)
+    # a narrow call at every row position of the 64-token block
+    probe_lp = lp[17:18]
+    for pos in range(min(limit, 64)):
+        Hp = H[:min(limit, 64)].clone()
+        yp = y[:min(limit, 64)].clone()
+        Hp[pos] = H[17]
+        yp[pos] = y[17]
+        lp_p, _ = itl.lmhead_logprob(Hp, W, yp)
+        assert same_bits(lp_p[pos:pos + 1], probe_lp), pos
+
+
 def test_run_to_run_determinism(cuda):
     import torch
 
