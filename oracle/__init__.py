@@ -26,6 +26,10 @@ Every function evaluates its definition in float64 on the exact values of
 its inputs: bfloat16 bit patterns (numpy uint16) and float32 numbers both
 convert to float64 without rounding.
 
+The mismatch diagnostics (oracle/diagnostics.py) follow the pages' split of
+the learner/rollout logprob gap into weight lag and kernel mismatch; their
+readings and pins are listed in that module.
+
 Pins (see tests/test_oracle_*.py): brute force in 60-digit decimal
 arithmetic on tiny vocabularies, exact rational dot products, closed forms
 (uniform logits, one dominant logit), shift invariance, lp <= 0, the
@@ -37,6 +41,7 @@ any inputs: parity against the pages' own figures is unpinned.
 """
 
 from .lmhead import to_f64, logits, log_softmax_at, lmhead_logprob
+from .diagnostics import STAT_NAMES, mismatch_stats
 from .reinforce_zero import (
     group_advantage,
     importance_ratio,
@@ -57,4 +62,6 @@ __all__ = [
     "reinforce_zero_backward",
     "reinforce_zero_backward_rows",
     "reinforce_zero_objective",
+    "STAT_NAMES",
+    "mismatch_stats",
 ]

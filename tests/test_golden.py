@@ -63,3 +63,16 @@ def test_ratio_unclipped():
     assert r[0] == 1.0
     assert r[1] == pytest.approx(math.exp(5.0), rel=1e-15)
     assert r[2] == pytest.approx(math.exp(30.0), rel=1e-15)
+
+
+def test_mismatch_stats_mixed():
+    c = CASES["mismatch_stats_mixed"]
+    lr = np.array(c["rollout_logprob"])
+    ln2 = math.log(2.0)
+    lp = lr + np.array([ln2, 0.0, -ln2, ln2])
+    s = oracle.mismatch_stats(lp, lr)
+    want = {"kl_k1": -ln2 / 4, "kl_k2": 3 * ln2 * ln2 / 8, "kl_k3": (1.5 - ln2) / 4, "weight_mean": 11 / 8,
+            "weight_max": 2.0, "weight_min": 0.5, "deviation_max": 1.0, "deviation_median": 0.75,
+            "deviation_peak_over_median": 4 / 3}
+    for k, v in want.items():
+        assert abs(s[k] - v) <= 1e-15 * max(1.0, abs(v)), k
