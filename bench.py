@@ -208,6 +208,69 @@ def decode_leg(wl, device, batch_sizes=(1, 8, 64, 128, 256), calls=20):
     }
 
 
+def mismatch_leg(s, device, calls=20, n_demo=4096, batch=64):
+    """The mismatch diagnostics: (1) itl_mismatch_stats timed on the whole
+    batch (learner logprobs, the rollout record with the workload's lag
+    noise, the aligned same-weights logprobs); (2) the kernel part of the gap
+    at equal weights on a seeded subset of tokens, for two rollouts of the
+    same tokens in decode-shaped calls of `batch` tokens: this library
+    (aligned) and the fast non-invariant path (bf16 logits + log_softmax)."""
+    import torch
+    import invariant_token_logprobs_lm_amd as itl
+    from synth import token_subset
+
+    lp, lpr = s["lp"], s["lpr"]
+    n = lp.shape[0]
+    st = torch.empty(len(itl.STAT_FIELDS), dtype=torch.float64, device=device)
+    ws = torch.empty(max(itl.mismatch_stats_workspace_bytes(n), 1), dtype=torch.uint8, device=device)
+    same = lpr.clone()
+    itl.mismatch_stats(lp, lpr, same, stats=st, workspace=ws)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(calls):
+        itl.mismatch_stats(lp, lpr, same, stats=st, workspace=ws)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / calls
+    full = itl.stats_dict(st)
+    log(f"[bench] mismatch stats over {n} tokens: {ms * 1e3:.1f} us/call ({12.0 * n / (ms * 1e-3) / 1e9:.1f} GB/s of "
+        f"input); lag k3 {full['kl_k3']:.3e}, weight deviation peak/median {full['deviation_peak_over_median']:.2f}")
+
+    idx = torch.from_numpy(token_subset(n, n_demo, seed=77)).to(device)
+    H, W, y = s["H"].index_select(0, idx).contiguous(), s["W"], s["y"].index_select(0, idx).contiguous()
+    learner, _ = itl.lmhead_logprob(H, W, y)  # the learner: one call over the whole subset
+    aligned = torch.empty_like(learner)
+    fast = torch.empty_like(learner)
+    for c0 in range(0, n_demo, batch):
+        sl = slice(c0, min(c0 + batch, n_demo))
+        aligned[sl] = itl.lmhead_logprob(H[sl], W, y[sl], want_lse=False)[0]
+        z = torch.mm(H[sl], W.t())
+        fast[sl] = torch.log_softmax(z.float(), dim=1).gather(1, y[sl].long()[:, None])[:, 0]
+    rows = {}
+    for name, roll in (("aligned", aligned), ("fast_non_invariant", fast)):
+        # equal weights: the learner's computation at the rollout's weights
+        # is the learner's own result, so the whole gap is the kernel part
+        d = itl.stats_dict(itl.mismatch_stats(learner, roll, learner))
+        rows[name] = {k: d[k] for k in ("kernel_nonzero", "kernel_abs_max", "kernel_kl_k3", "deviation_max",
+                                         "deviation_median", "deviation_peak_over_median")}
+        log(f"[bench] kernel mismatch, {name} rollout: {int(d['kernel_nonzero'])}/{n_demo} tokens differ, "
+            f"max |dlp| {d['kernel_abs_max']:.3e}, weight deviation peak/median {d['deviation_peak_over_median']:.2f}")
+    return {
+        "kernel": "itl_mismatch_stats (terms + radix sort + finalize)",
+        "n_tok": n,
+        "us_per_call": ms * 1e3,
+        "input_gb_per_s": 12.0 * n / (ms * 1e-3) / 1e9,
+        "stats_full_batch": full,
+        "kernel_part_at_equal_weights": {
+            "tokens": n_demo,
+            "rollout_calls_of": batch,
+            "learner": "this library, one call over all the tokens",
+            **rows,
+        },
+    }
+
+
 def cpu_baseline(wl, n_sample=6144):
     """The float64 oracle timed on a seeded sample of the same workload's
     tokens (forward + loss over the sampled tokens)."""
@@ -264,6 +327,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-mismatch", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="before timing, run one plain 1 GiB device-to-device copy: the reference whose "
                          "FETCH_SIZE / WRITE_SIZE counters calibrate the HBM traffic figures")
@@ -327,6 +391,8 @@ def main():
             "ms_per_launch": ms_head,
         },
     }
+    if not args.no_mismatch:
+        out["mismatch"] = mismatch_leg(s, device)
     del s
     torch.cuda.empty_cache()
     if not args.no_decode:

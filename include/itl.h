@@ -19,13 +19,23 @@
  *       independence and prefill/decode phase consistency; section
  *       "Overview": bitwise-identical sampled-token logprobs (diff = 0)
  *       between rollout and training.
+ *  [GAP] "vLLM says aligned kernels make asynchronous RL stable at lag 64",
+ *       section "Asynchronous training has two different gaps": the
+ *       learner/rollout logprob gap splits into weight lag and kernel
+ *       mismatch; the importance-weight deviation is judged by its peak over
+ *       its median. "vLLM Train-Inference Consistency Release Notes", section
+ *       "The Technical Challenge: Train-Inference Mismatch": the
+ *       train-inference KL divergence.
  *
  * Determinism contract [BC]. For one build of this library (see
  * itl_build_info) and one (vocab, d, dtype):
  *  - each token's logprob and lse are bitwise identical whatever n_tok,
  *    the token's row position, its batch-mates, the stream, or concurrent
  *    load. A decode step (n_tok = 1) and a prefill over many tokens give the
- *    same bits for the same hidden state: there is one code path.
+ *    same bits for the same hidden state: calls of at most 64 tokens run a
+ *    narrow kernel that performs, per token, the same matrix-core
+ *    instructions on the same operand fragments and the same fold sequence
+ *    as the kernel for larger calls.
  *  - each resp_loss[i] is a bitwise function of response i's own
  *    (logprob, rollout_logprob, advantage, T_i) only;
  *  - loss, coef, advantages, dH and dW are run-to-run deterministic (no
@@ -148,6 +158,52 @@ itl_status itl_reinforce_zero_backward(const void* H, const void* W, itl_dtype d
                                        const int32_t* tokens, const float* lse, const float* coef,
                                        float* dH, float* dW,
                                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Statistics written by itl_mismatch_stats (fp64, indices into `stats`). */
+typedef enum itl_stat {
+  ITL_STAT_N_TOK = 0,
+  ITL_STAT_KL_K1,                      /* mean of -delta                   */
+  ITL_STAT_KL_K2,                      /* mean of delta^2 / 2              */
+  ITL_STAT_KL_K3,                      /* mean of expm1(delta) - delta     */
+  ITL_STAT_WEIGHT_MEAN,                /* mean of w = exp(delta)           */
+  ITL_STAT_WEIGHT_MAX,
+  ITL_STAT_WEIGHT_MIN,
+  ITL_STAT_DEVIATION_MAX,              /* max of |w - 1|                   */
+  ITL_STAT_DEVIATION_MEDIAN,           /* median of |w - 1|                */
+  ITL_STAT_DEVIATION_PEAK_OVER_MEDIAN, /* max / median (1 if both 0, +inf if only the median is) */
+  ITL_STAT_LAG_ABS_MEAN,               /* lag = logprob - same_weights     */
+  ITL_STAT_LAG_ABS_MAX,
+  ITL_STAT_LAG_KL_K3,
+  ITL_STAT_KERNEL_ABS_MEAN,            /* kernel = same_weights - rollout  */
+  ITL_STAT_KERNEL_ABS_MAX,
+  ITL_STAT_KERNEL_KL_K3,
+  ITL_STAT_KERNEL_NONZERO,             /* tokens whose two fp32 values differ in any bit */
+  ITL_STAT_COUNT
+} itl_stat;
+
+/* Bytes of device workspace itl_mismatch_stats needs for n_tok tokens
+ * (about 16 n_tok plus sort scratch). SIZE_MAX for invalid sizes. */
+size_t itl_mismatch_stats_workspace_bytes(int64_t n_tok);
+
+/* Train/inference mismatch diagnostics of one batch of sampled tokens [GAP].
+ * logprob: the learner's fp32 [n_tok]; rollout_logprob: the rollout's
+ * record fp32 [n_tok]; same_weights_logprob (nullable): the learner's
+ * computation at the rollout's weights, which splits the gap into weight lag
+ * (logprob - same_weights) and kernel mismatch (same_weights - rollout). Per
+ * token, in fp64 from the exact fp32 values: delta = logprob -
+ * rollout_logprob, w = exp(delta); KL(rollout || learner) by the sample
+ * estimators k1, k2, k3 of J. Schulman's "Approximating KL Divergence"
+ * (tokens are drawn from the rollout policy). The median is exact (a radix
+ * sort of |w - 1|; the mean of the two middle values for even n_tok).
+ * stats: DEVICE fp64 [ITL_STAT_COUNT], written on `stream`; the split
+ * fields are NaN without same_weights_logprob, every field but N_TOK is
+ * NaN when n_tok == 0. Run-to-run deterministic (fixed reduction order for
+ * a given n_tok). workspace: >= itl_mismatch_stats_workspace_bytes(n_tok)
+ * bytes, 256-byte aligned. n_tok above 2^31 - 1 returns
+ * ITL_ERR_UNSUPPORTED. */
+itl_status itl_mismatch_stats(const float* logprob, const float* rollout_logprob,
+                              const float* same_weights_logprob, int64_t n_tok, double* stats,
+                              void* workspace, size_t workspace_bytes, void* stream);
 
 /* Opt-in validation of device-resident inputs (synchronises `stream`):
  * 0 <= tokens[t] < vocab for all t (tokens may be NULL to skip), and, when

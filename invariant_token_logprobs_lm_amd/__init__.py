@@ -13,6 +13,7 @@ Entry points (same names as the C ABI without the ``itl_`` prefix):
 * ``group_advantage(rewards, group_offsets) -> advantages``
 * ``reinforce_zero_loss(logprob, rollout_logprob, advantages, resp_offsets) -> (resp_loss, loss, coef)``
 * ``reinforce_zero_backward(H, W, tokens, lse, coef) -> (dH, dW)``
+* ``mismatch_stats(logprob, rollout_logprob, same_weights_logprob=None) -> stats``
 * ``check_inputs(tokens, vocab, resp_offsets=None)``, ``build_info()``
 """
 
@@ -60,6 +61,9 @@ def _load():
         "itl_reinforce_zero_backward": (ctypes.c_int, [_c_void_p, _c_void_p, ctypes.c_int, _i64, _i64, _i64,
                                                        _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                                        _c_void_p, _size, _c_void_p]),
+        "itl_mismatch_stats_workspace_bytes": (_size, [_i64]),
+        "itl_mismatch_stats": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _i64, _c_void_p, _c_void_p, _size,
+                                              _c_void_p]),
         "itl_check_inputs": (ctypes.c_int, [_c_void_p, _i64, _i64, _c_void_p, _i32, _c_void_p]),
         "itl_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "itl_last_error": (ctypes.c_char_p, []),
@@ -81,6 +85,8 @@ EXPORTS = (
     "itl_reinforce_zero_loss",
     "itl_reinforce_zero_backward_workspace_bytes",
     "itl_reinforce_zero_backward",
+    "itl_mismatch_stats_workspace_bytes",
+    "itl_mismatch_stats",
     "itl_check_inputs",
     "itl_status_string",
     "itl_last_error",
@@ -226,6 +232,65 @@ def reinforce_zero_backward(H, W, tokens, lse, coef, *, dH=None, dW=None, worksp
                                            _ptr(lse), _ptr(coef), _ptr(dH), _ptr(dW), _ptr(workspace),
                                            workspace.numel(), _stream(dev)))
     return dH, dW
+
+
+# Field order of itl_mismatch_stats' output (the itl_stat enum of include/itl.h).
+STAT_FIELDS = (
+    "n_tok",
+    "kl_k1",
+    "kl_k2",
+    "kl_k3",
+    "weight_mean",
+    "weight_max",
+    "weight_min",
+    "deviation_max",
+    "deviation_median",
+    "deviation_peak_over_median",
+    "lag_abs_mean",
+    "lag_abs_max",
+    "lag_kl_k3",
+    "kernel_abs_mean",
+    "kernel_abs_max",
+    "kernel_kl_k3",
+    "kernel_nonzero",
+)
+
+
+def mismatch_stats_workspace_bytes(n_tok):
+    return int(lib.itl_mismatch_stats_workspace_bytes(n_tok))
+
+
+def mismatch_stats(logprob, rollout_logprob, same_weights_logprob=None, *, stats=None, workspace=None):
+    """Mismatch diagnostics of one batch: fp64 device tensor [len(STAT_FIELDS)]
+    in STAT_FIELDS order (use ``stats_dict`` to read it on the host)."""
+    _need(logprob, "logprob", (torch.float32,), ndim=1)
+    dev = logprob.device
+    _need(rollout_logprob, "rollout_logprob", (torch.float32,), device=dev, ndim=1)
+    n_tok = logprob.shape[0]
+    if rollout_logprob.shape[0] != n_tok:
+        raise ValueError("logprob and rollout_logprob differ in length")
+    if same_weights_logprob is not None:
+        _need(same_weights_logprob, "same_weights_logprob", (torch.float32,), device=dev, ndim=1)
+        if same_weights_logprob.shape[0] != n_tok:
+            raise ValueError("same_weights_logprob differs in length")
+    if stats is None:
+        stats = torch.empty(len(STAT_FIELDS), dtype=torch.float64, device=dev)
+    _need(stats, "stats", (torch.float64,), device=dev, ndim=1)
+    if stats.shape[0] < len(STAT_FIELDS):
+        raise ValueError(f"stats needs {len(STAT_FIELDS)} elements")
+    need = mismatch_stats_workspace_bytes(n_tok)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", (torch.uint8,), device=dev)
+    _check(lib.itl_mismatch_stats(_ptr(logprob), _ptr(rollout_logprob), _ptr(same_weights_logprob), n_tok,
+                                  _ptr(stats), _ptr(workspace), workspace.numel(), _stream(dev)))
+    return stats
+
+
+def stats_dict(stats):
+    """Host dict of a mismatch_stats result (synchronises on the copy)."""
+    vals = stats.cpu().tolist()
+    return {k: vals[i] for i, k in enumerate(STAT_FIELDS)}
 
 
 def check_inputs(tokens, vocab, resp_offsets=None):

@@ -123,6 +123,27 @@ itl_status itl_reinforce_zero_backward(const void* H, const void* W, itl_dtype d
   return e == hipSuccess ? ITL_OK : hip_fail(e, "itl_reinforce_zero_backward");
 }
 
+size_t itl_mismatch_stats_workspace_bytes(int64_t n_tok) {
+  if (n_tok < 0 || n_tok > INT32_MAX) return SIZE_MAX;
+  return n_tok == 0 ? 0 : itl::mismatch_stats_workspace_bytes(n_tok);
+}
+
+itl_status itl_mismatch_stats(const float* logprob, const float* rollout_logprob, const float* same_weights_logprob,
+                              int64_t n_tok, double* stats, void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  if (n_tok < 0) return fail(ITL_ERR_INVALID_ARG, "n_tok must be >= 0");
+  if (n_tok > INT32_MAX) return fail(ITL_ERR_UNSUPPORTED, "n_tok too large for one call");
+  if (!stats) return fail(ITL_ERR_INVALID_ARG, "null stats");
+  if (n_tok > 0 && (!logprob || !rollout_logprob)) return fail(ITL_ERR_INVALID_ARG, "null logprob arrays");
+  const size_t need = n_tok == 0 ? 0 : itl::mismatch_stats_workspace_bytes(n_tok);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(ITL_ERR_WORKSPACE, "workspace missing or smaller than itl_mismatch_stats_workspace_bytes()");
+  if (need > 0 && misaligned(workspace)) return fail(ITL_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  hipError_t e = itl::launch_mismatch_stats(logprob, rollout_logprob, same_weights_logprob, n_tok, stats, workspace,
+                                            static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ITL_OK : hip_fail(e, "itl_mismatch_stats");
+}
+
 itl_status itl_check_inputs(const int32_t* tokens, int64_t n_tok, int64_t vocab, const int64_t* resp_offsets,
                             int32_t n_resp, void* stream) {
   g_last_error.clear();

@@ -34,6 +34,11 @@ hipError_t launch_reinforce_zero_backward(const void* H, const void* W, int dtyp
                                           const int32_t* tokens, const float* lse, const float* coef,
                                           float* dH, float* dW, void* workspace, hipStream_t stream);
 
+size_t mismatch_stats_workspace_bytes(long long n_tok);
+
+hipError_t launch_mismatch_stats(const float* lp, const float* lpr, const float* lps, long long n, double* stats,
+                                 void* workspace, hipStream_t stream);
+
 // Device-side validation; writes a nonzero value to *flag on a violation.
 hipError_t launch_check_inputs(const int32_t* tokens, long long n_tok, int vocab, const int64_t* resp_offsets,
                                int n_resp, int* flag, hipStream_t stream);

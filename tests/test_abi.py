@@ -153,3 +153,27 @@ def test_oracle_and_product_are_independent():
     for p in _sources(os.path.join(ROOT, "oracle"), (".py", ".c", ".h")):
         text = open(p).read()
         assert "invariant_token_logprobs_lm_amd" not in text and "import synth" not in text, p
+
+
+def test_mismatch_stats_validation(lib):
+    v = ctypes.c_void_p
+    f = lib.itl_mismatch_stats
+    assert f(v(1), v(1), None, -1, v(8), v(256), 1 << 20, None) == INVALID
+    assert f(v(1), v(1), None, 10, None, v(256), 1 << 20, None) == INVALID
+    assert f(None, v(1), None, 10, v(8), v(256), 1 << 20, None) == INVALID
+    assert f(v(1), v(1), None, 1 << 31, v(8), v(256), 1 << 40, None) == UNSUPPORTED
+    assert f(v(1), v(1), None, 10, v(8), v(256), 16, None) == WORKSPACE
+    assert f(v(1), v(1), None, 10, v(8), v(257), 1 << 20, None) == WORKSPACE
+    w = lib.itl_mismatch_stats_workspace_bytes
+    assert w(0) == 0 and w(-1) == ctypes.c_size_t(-1).value and w(1 << 31) == ctypes.c_size_t(-1).value
+    assert w(1000) >= 16 * 1000 and w(100000) > w(1000)
+
+
+def test_mismatch_stat_fields_match_header_and_oracle():
+    import invariant_token_logprobs_lm_amd as itl
+    import oracle
+
+    text = open(HEADER).read()
+    enum = re.findall(r"\bITL_STAT_([A-Z0-9_]+)\b", text)
+    enum = [e.lower() for e in dict.fromkeys(enum) if e != "COUNT"]
+    assert tuple(enum) == itl.STAT_FIELDS == oracle.STAT_NAMES
