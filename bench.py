@@ -271,6 +271,41 @@ def mismatch_leg(s, device, calls=20, n_demo=4096, batch=64):
     }
 
 
+def sustained_mfma_probe(device, blocks=1024, iters=40000):
+    """TFLOP/s that v_mfma_f32_32x32x16_bf16 sustains on this chip with
+    operands that change every instruction (random normal bf16 values, a
+    4 x 4 block tile per wavefront, one wavefront per SIMD) and no memory
+    traffic: the power-limited ceiling a real contraction meets, measured
+    with the probe library built beside libitl.so."""
+    import ctypes
+    import torch
+
+    path = os.path.join(ROOT, "invariant_token_logprobs_lm_amd", "libitl_probe.so")
+    lib = ctypes.CDLL(path)
+    lib.itl_probe_operand_bytes.restype = ctypes.c_size_t
+    lib.itl_probe_flops.restype = ctypes.c_double
+    lib.itl_probe_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.itl_probe_mfma_bf16.restype = ctypes.c_int
+    lib.itl_probe_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    g = torch.Generator(device="cpu").manual_seed(5150)
+    n = lib.itl_probe_operand_bytes() // 2
+    ops = torch.randn(n, generator=g).to(torch.bfloat16).to(device)
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=device)
+    st = ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+    assert lib.itl_probe_mfma_bf16(ctypes.c_void_p(ops.data_ptr()), ctypes.c_void_p(out.data_ptr()), blocks, 100, st) == 0
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    assert lib.itl_probe_mfma_bf16(ctypes.c_void_p(ops.data_ptr()), ctypes.c_void_p(out.data_ptr()), blocks, iters, st) == 0
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b)
+    tf = lib.itl_probe_flops(blocks, iters) / (ms * 1e-3) / 1e12
+    log(f"[bench] matrix-core probe (random bf16 operands, no memory traffic): {tf:.1f} TFLOP/s "
+        f"({100 * tf / PEAK_BF16_TFLOPS:.1f}% of the published peak) in {ms:.1f} ms")
+    return tf
+
+
 def cpu_baseline(wl, n_sample=6144):
     """The float64 oracle timed on a seeded sample of the same workload's
     tokens (forward + loss over the sampled tokens)."""
@@ -358,6 +393,7 @@ def main():
     log(f"[bench] step {ms_step:.3f} ms, lmhead {ms_head:.3f} ms -> {achieved:.1f} TFLOP/s "
         f"({100 * achieved / PEAK_BF16_TFLOPS:.1f}% of bf16 peak), wall {wall:.2f}s")
     traffic = measured_traffic(wl.key)
+    sustained = sustained_mfma_probe(device)
     out = {
         "metric": METRIC,
         "value": n_tok / (ms_step * 1e-3),
@@ -389,6 +425,13 @@ def main():
             "traffic": traffic,
             "flop_per_launch": flops,
             "ms_per_launch": ms_head,
+            "sustained_mfma_probe": {
+                "value": sustained,
+                "unit": "TFLOP/s",
+                "what": "v_mfma_f32_32x32x16_bf16 with random bf16 operands changing every instruction, "
+                        "4x4 block tile per wavefront, no memory traffic (power-limited clock)",
+                "frac_of_probe": achieved / sustained,
+            },
         },
     }
     if not args.no_mismatch:

@@ -4,7 +4,9 @@
 
 Each csrc/*.hip file is compiled separately (in parallel) with hipcc for
 gfx950 only, then linked into invariant_token_logprobs_lm_amd/libitl.so.
-Packed-fp32 instruction selection is disabled for device code.
+The benchmark's matrix-core probe (probe/*.hip) is linked separately into
+libitl_probe.so; the library never uses it. Packed-fp32 instruction
+selection is disabled for device code.
 """
 
 import concurrent.futures
@@ -18,6 +20,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libitl.so")
+PROBE_LIB = os.path.join(PKG, "libitl_probe.so")
+PROBE_SRC = os.path.join(PKG, "probe")
 ARCH = "gfx950"
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
@@ -35,12 +39,12 @@ DEVICE_FLAGS = [
 ]
 
 
-def sources():
-    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+def sources(folder=CSRC):
+    return sorted(os.path.join(folder, f) for f in os.listdir(folder) if f.endswith(".hip"))
 
 
 def _compile(src, verbose):
-    obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
+    obj = os.path.join(BUILD, os.path.basename(os.path.dirname(src)) + "_" + os.path.basename(src)[:-4] + ".o")
     cmd = [HIPCC, *DEVICE_FLAGS, "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -54,13 +58,8 @@ def _compile(src, verbose):
     return obj
 
 
-def build(verbose=False):
-    """Compile every HIP source and link libitl.so. Always recompiles."""
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = sources()
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
-    tmp = LIB + ".tmp"
+def _link(objs, lib, verbose):
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs,
            "-Wl,-rpath,/opt/rocm/lib", "-Wl,--no-undefined"]
     if verbose:
@@ -68,7 +67,19 @@ def build(verbose=False):
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose=False):
+    """Compile every HIP source and link libitl.so (and the probe library).
+    Always recompiles."""
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = sources()
+    probe = sources(PROBE_SRC)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs) + len(probe))) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), srcs + probe))
+    _link(objs[:len(srcs)], LIB, verbose)
+    _link(objs[len(srcs):], PROBE_LIB, verbose)
     return LIB
 
 

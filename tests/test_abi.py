@@ -177,3 +177,16 @@ def test_mismatch_stat_fields_match_header_and_oracle():
     enum = re.findall(r"\bITL_STAT_([A-Z0-9_]+)\b", text)
     enum = [e.lower() for e in dict.fromkeys(enum) if e != "COUNT"]
     assert tuple(enum) == itl.STAT_FIELDS == oracle.STAT_NAMES
+
+
+def test_probe_library_is_separate_and_loads():
+    """The benchmark's matrix-core probe lives in its own library; libitl.so
+    does not export it."""
+    probe = ctypes.CDLL(os.path.join(ROOT, "invariant_token_logprobs_lm_amd", "libitl_probe.so"))
+    for name in ("itl_probe_operand_bytes", "itl_probe_flops", "itl_probe_mfma_bf16"):
+        assert hasattr(probe, name)
+    probe.itl_probe_operand_bytes.restype = ctypes.c_size_t
+    assert probe.itl_probe_operand_bytes() == 4096 * 8 * 16
+    import invariant_token_logprobs_lm_amd as itl
+
+    assert not hasattr(itl.lib, "itl_probe_mfma_bf16")
