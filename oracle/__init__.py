@@ -42,6 +42,7 @@ any inputs: parity against the pages' own figures is unpinned.
 
 from .lmhead import to_f64, logits, log_softmax_at, lmhead_logprob
 from .diagnostics import STAT_NAMES, mismatch_stats
+from .fp8 import e4m3_decode, e4m3_encode, quantize_rows_fp8, lmhead_logprob_fp8
 from .reinforce_zero import (
     group_advantage,
     importance_ratio,
@@ -64,4 +65,8 @@ __all__ = [
     "reinforce_zero_objective",
     "STAT_NAMES",
     "mismatch_stats",
+    "e4m3_decode",
+    "e4m3_encode",
+    "quantize_rows_fp8",
+    "lmhead_logprob_fp8",
 ]
