@@ -25,6 +25,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "sampled-token logprobs/sec (fwd, fwd+bwd) at 1 GPU; % bf16 MFMA peak"
+PEAK_FP8_TFLOPS = 5033.2  # MI355X dense FP8 matrix-core peak (2 x the bf16 figure)
 PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 dense bf16 flop/clk/CU (published 2.5 PFLOP/s)
 PEAK_HBM_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
@@ -271,6 +272,56 @@ def mismatch_leg(s, device, calls=20, n_demo=4096, batch=64):
     }
 
 
+def fp8_leg(s, device, steps=5):
+    """The same workload on the FP8 (E4M3, per-row scales) head: W quantised
+    once (not timed); a step = quantise H + the fp8 logprob kernel."""
+    import torch
+    import invariant_token_logprobs_lm_amd as itl
+
+    H, W, y, lp_bf16 = s["H"], s["W"], s["y"], s["lp"]
+    n, d = H.shape
+    V = W.shape[0]
+    Wq, ws = itl.quantize_rows_fp8(W)
+    Hq = torch.empty((n, d), dtype=torch.uint8, device=device)
+    hs = torch.empty(n, dtype=torch.float32, device=device)
+    lp = torch.empty(n, dtype=torch.float32, device=device)
+    wsp = torch.empty(itl.lmhead_workspace_bytes(n, V), dtype=torch.uint8, device=device)
+
+    def step():
+        itl.quantize_rows_fp8(H, Xq=Hq, scale=hs)
+        itl.lmhead_logprob_fp8(Hq, hs, Wq, ws, y, logprob=lp, workspace=wsp, want_lse=False)
+
+    step()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    q0, q1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        step()
+    b.record()
+    q0.record()
+    itl.quantize_rows_fp8(H, Xq=Hq, scale=hs)
+    q1.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    ms_q = q0.elapsed_time(q1)
+    tf = 2.0 * d * V * n / ((ms - ms_q) * 1e-3) / 1e12
+    gap = float((lp - lp_bf16).abs().max())
+    log(f"[bench] fp8 head: step {ms:.2f} ms (H quantisation {ms_q:.2f} ms) -> {n / (ms * 1e-3):.0f} tokens/s, "
+        f"logprob kernel {tf:.1f} TFLOP/s ({100 * tf / PEAK_FP8_TFLOPS:.1f}% of fp8 peak); max |lp_fp8 - lp_bf16| {gap:.3e}")
+    return {
+        "workload": "same tokens and head; W quantised once to E4M3 with per-row scales, H per step",
+        "ms_per_step": ms,
+        "ms_quantize_h": ms_q,
+        "value": n / (ms * 1e-3),
+        "unit": "sampled-token logprobs/s",
+        "tflops_logprob_kernel": tf,
+        "peak_fp8_tflops": PEAK_FP8_TFLOPS,
+        "frac_fp8_peak": tf / PEAK_FP8_TFLOPS,
+        "max_abs_lp_gap_to_bf16_head": gap,
+    }
+
+
 def sustained_mfma_probe(device, blocks=1024, iters=40000):
     """TFLOP/s that v_mfma_f32_32x32x16_bf16 sustains on this chip with
     operands that change every instruction (random normal bf16 values, a
@@ -363,6 +414,7 @@ def main():
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-mismatch", action="store_true")
+    ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="before timing, run one plain 1 GiB device-to-device copy: the reference whose "
                          "FETCH_SIZE / WRITE_SIZE counters calibrate the HBM traffic figures")
@@ -436,6 +488,8 @@ def main():
     }
     if not args.no_mismatch:
         out["mismatch"] = mismatch_leg(s, device)
+    if not args.no_fp8:
+        out["fp8"] = fp8_leg(s, device)
     del s
     torch.cuda.empty_cache()
     if not args.no_decode:

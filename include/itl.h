@@ -19,6 +19,9 @@
  *       independence and prefill/decode phase consistency; section
  *       "Overview": bitwise-identical sampled-token logprobs (diff = 0)
  *       between rollout and training.
+ *  [FP8] "vLLM says aligned kernels make asynchronous RL stable at lag 64",
+ *       section "Zero mismatch expands to newer models": the consistent path
+ *       of the newest model runs FP8 (and MXFP4) weights.
  *  [GAP] "vLLM says aligned kernels make asynchronous RL stable at lag 64",
  *       section "Asynchronous training has two different gaps": the
  *       learner/rollout logprob gap splits into weight lag and kernel
@@ -158,6 +161,35 @@ itl_status itl_reinforce_zero_backward(const void* H, const void* W, itl_dtype d
                                        const int32_t* tokens, const float* lse, const float* coef,
                                        float* dH, float* dW,
                                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Per-row FP8 quantisation [FP8] (OCP E4M3: bias 7, no infinities, largest
+ * finite value 448). For each row r of X [n_rows, d] (dtype bf16 or fp32):
+ *   scale[r] = amax_r / 448 in fp32 (correctly rounded; 1 for an all-zero row)
+ *   Xq[r, k] = E4M3 code of X[r, k] / scale[r] (fp32 division, correctly
+ *              rounded; round to nearest, ties to even; saturating at +-448)
+ * so the codes and scales are a fixed function of the input bits (rows of W
+ * are quantised once; rows of H, per call, are batch-independent). X must
+ * be finite. Xq uint8 [n_rows, d] (4-byte aligned), scale fp32 [n_rows]. d
+ * must be a multiple of 128 (ITL_ERR_UNSUPPORTED otherwise). */
+itl_status itl_quantize_rows_fp8(const void* X, itl_dtype dtype, int64_t n_rows, int64_t d,
+                                 uint8_t* Xq, float* scale, void* stream);
+
+/* Sampled-token logprob from an FP8 head [FP8][RZ][BC]: Hq [n_tok, d] and Wq
+ * [vocab, d] E4M3 codes with per-row scales h_scale [n_tok], w_scale [vocab]
+ * (as written by itl_quantize_rows_fp8), on the FP8 matrix cores:
+ *   z[t, v]    = (acc[t, v] * w_scale[v]) * h_scale[t],
+ *   acc[t, v]  = sum_k e4m3(Hq[t, k]) e4m3(Wq[v, k])   (fp32, fixed K order)
+ *   logprob[t] = z[t, tokens[t]] - log sum_v exp(z[t, v])
+ * with the same fused log-sum-exp, vocabulary slices and combine as
+ * itl_lmhead_logprob, and the same determinism contract (one kernel for
+ * every n_tok). d must be a multiple of 128; Hq, Wq 16-byte aligned.
+ * workspace: >= itl_lmhead_logprob_workspace_bytes(n_tok, vocab) bytes,
+ * 256-byte aligned. lse may be NULL. */
+itl_status itl_lmhead_logprob_fp8(const uint8_t* Hq, const float* h_scale,
+                                  const uint8_t* Wq, const float* w_scale,
+                                  int64_t n_tok, int64_t d, int64_t vocab,
+                                  const int32_t* tokens, float* logprob, float* lse,
+                                  void* workspace, size_t workspace_bytes, void* stream);
 
 /* Statistics written by itl_mismatch_stats (fp64, indices into `stats`). */
 typedef enum itl_stat {

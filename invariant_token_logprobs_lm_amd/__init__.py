@@ -14,6 +14,8 @@ Entry points (same names as the C ABI without the ``itl_`` prefix):
 * ``reinforce_zero_loss(logprob, rollout_logprob, advantages, resp_offsets) -> (resp_loss, loss, coef)``
 * ``reinforce_zero_backward(H, W, tokens, lse, coef) -> (dH, dW)``
 * ``mismatch_stats(logprob, rollout_logprob, same_weights_logprob=None) -> stats``
+* ``quantize_rows_fp8(X) -> (Xq, scale)``,
+  ``lmhead_logprob_fp8(Hq, h_scale, Wq, w_scale, tokens) -> (logprob, lse)``
 * ``check_inputs(tokens, vocab, resp_offsets=None)``, ``build_info()``
 """
 
@@ -61,6 +63,10 @@ def _load():
         "itl_reinforce_zero_backward": (ctypes.c_int, [_c_void_p, _c_void_p, ctypes.c_int, _i64, _i64, _i64,
                                                        _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                                        _c_void_p, _size, _c_void_p]),
+        "itl_quantize_rows_fp8": (ctypes.c_int, [_c_void_p, ctypes.c_int, _i64, _i64, _c_void_p, _c_void_p,
+                                                 _c_void_p]),
+        "itl_lmhead_logprob_fp8": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i64, _i64,
+                                                  _c_void_p, _c_void_p, _c_void_p, _c_void_p, _size, _c_void_p]),
         "itl_mismatch_stats_workspace_bytes": (_size, [_i64]),
         "itl_mismatch_stats": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _i64, _c_void_p, _c_void_p, _size,
                                               _c_void_p]),
@@ -85,6 +91,8 @@ EXPORTS = (
     "itl_reinforce_zero_loss",
     "itl_reinforce_zero_backward_workspace_bytes",
     "itl_reinforce_zero_backward",
+    "itl_quantize_rows_fp8",
+    "itl_lmhead_logprob_fp8",
     "itl_mismatch_stats_workspace_bytes",
     "itl_mismatch_stats",
     "itl_check_inputs",
@@ -232,6 +240,50 @@ def reinforce_zero_backward(H, W, tokens, lse, coef, *, dH=None, dW=None, worksp
                                            _ptr(lse), _ptr(coef), _ptr(dH), _ptr(dW), _ptr(workspace),
                                            workspace.numel(), _stream(dev)))
     return dH, dW
+
+
+def quantize_rows_fp8(X, *, Xq=None, scale=None):
+    """Per-row E4M3 codes (uint8 [n, d]) and fp32 scales [n] of a bf16 or
+    fp32 matrix [n, d] (d a multiple of 128)."""
+    _need(X, "X", tuple(_HEAD_DTYPES), ndim=2)
+    n, d = X.shape
+    if Xq is None:
+        Xq = torch.empty((n, d), dtype=torch.uint8, device=X.device)
+    if scale is None:
+        scale = torch.empty(n, dtype=torch.float32, device=X.device)
+    _need(Xq, "Xq", (torch.uint8,), device=X.device, ndim=2)
+    _need(scale, "scale", (torch.float32,), device=X.device, ndim=1)
+    if tuple(Xq.shape) != (n, d) or scale.shape[0] != n:
+        raise ValueError("Xq must be [n, d] and scale [n]")
+    _check(lib.itl_quantize_rows_fp8(_ptr(X), _HEAD_DTYPES[X.dtype], n, d, _ptr(Xq), _ptr(scale), _stream(X.device)))
+    return Xq, scale
+
+
+def lmhead_logprob_fp8(Hq, h_scale, Wq, w_scale, tokens, *, logprob=None, lse=None, workspace=None, want_lse=True):
+    """Sampled-token logprob and lse from an E4M3 head with per-row scales
+    (as written by quantize_rows_fp8)."""
+    _need(Hq, "Hq", (torch.uint8,), ndim=2)
+    dev = Hq.device
+    _need(h_scale, "h_scale", (torch.float32,), device=dev, ndim=1)
+    _need(Wq, "Wq", (torch.uint8,), device=dev, ndim=2)
+    _need(w_scale, "w_scale", (torch.float32,), device=dev, ndim=1)
+    _need(tokens, "tokens", (torch.int32,), device=dev, ndim=1)
+    n_tok, d = Hq.shape
+    vocab = Wq.shape[0]
+    if Wq.shape[1] != d or h_scale.shape[0] != n_tok or w_scale.shape[0] != vocab or tokens.shape[0] != n_tok:
+        raise ValueError("shape mismatch between Hq, h_scale, Wq, w_scale and tokens")
+    if logprob is None:
+        logprob = torch.empty(n_tok, dtype=torch.float32, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty(n_tok, dtype=torch.float32, device=dev)
+    need = lmhead_workspace_bytes(n_tok, vocab)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", (torch.uint8,), device=dev)
+    _check(lib.itl_lmhead_logprob_fp8(_ptr(Hq), _ptr(h_scale), _ptr(Wq), _ptr(w_scale), n_tok, d, vocab,
+                                      _ptr(tokens), _ptr(logprob), _ptr(lse), _ptr(workspace), workspace.numel(),
+                                      _stream(dev)))
+    return logprob, lse
 
 
 # Field order of itl_mismatch_stats' output (the itl_stat enum of include/itl.h).

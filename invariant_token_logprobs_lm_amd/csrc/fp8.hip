@@ -1,0 +1,193 @@
+// FP8 (E4M3) head: per-row quantisation and the sampled-token logprob from
+// E4M3 operands on the FP8 matrix cores.
+//
+// "vLLM says aligned kernels make asynchronous RL stable at lag 64", section
+// "Zero mismatch expands to newer models": the consistent path of the newest
+// model runs FP8 (and MXFP4) weights; the aligned logprob must then come from
+// the low-precision head with the same invariance. Readings (the pages give
+// no format details): OCP E4M3 ("E4M3FN": bias 7, no infinities, max 448),
+// one float32 scale per row (a vocabulary row of W, a token row of H):
+//   scale[r] = amax_r / 448 (1 for an all-zero row), code = E4M3(x / scale)
+// with the division in float32 (correctly rounded) and the conversion
+// rounding to nearest, ties to even, saturating at +-448. The conversion is
+// written out from the format's fields (exact power-of-two scaling and a
+// round-to-nearest-even to 3 mantissa bits), not left to a conversion
+// instruction, so the codes are a fixed function of the input bits.
+//   z[t, v] = (acc[t, v] * w_scale[v]) * h_scale[t],
+//   acc[t, v] = sum_k E4M3(Hq[t, k]) E4M3(Wq[v, k]) (fp32, fixed K order)
+// then the same online log-sum-exp, slice partials and combine as the bf16
+// head (shared fold, lse_fold.h). One kernel serves every n_tok, so a
+// token's logprob does not depend on the batch.
+
+#include "itl_launch.h"
+#include "lse_fold.h"
+#include "tile_engine.h"
+
+namespace itl {
+
+namespace {
+
+// E4M3 code of a finite float32, round to nearest even, saturating.
+__device__ __forceinline__ uint32_t e4m3_rne(float x) {
+  const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
+  const float a = fabsf(x);
+  uint32_t code;
+  if (a < 0x1p-6f) {
+    code = (uint32_t)rintf(a * 512.0f);  // subnormal multiples of 2^-9; 8 is the smallest normal (0x08)
+  } else {
+    int e = (int)((__float_as_uint(a) >> 23) & 0xffu) - 127;  // a >= 2^-6 is a normal float32
+    float r = rintf(ldexpf(a, 3 - e));                       // 1.mmm x 8, in [8, 16]
+    if (r == 16.0f) {
+      e += 1;
+      r = 8.0f;
+    }
+    if (e > 8 || (e == 8 && r > 14.0f)) code = 0x7Eu;  // beyond 448 = 1.75 x 2^8: saturate
+    else code = ((uint32_t)(e + 7) << 3) | ((uint32_t)r - 8u);
+  }
+  return sign | code;
+}
+
+template <int kDtype>
+__device__ __forceinline__ float load_elem(const void* X, size_t i) {
+  if constexpr (kDtype == 0) return __uint_as_float((uint32_t)static_cast<const uint16_t*>(X)[i] << 16);
+  else return static_cast<const float*>(X)[i];
+}
+
+// One wavefront per row: amax by a butterfly of maxima (exact, so any tree
+// gives the same value), then four codes per lane packed into one store.
+template <int kDtype>
+__global__ __launch_bounds__(256) void quantize_rows_fp8_kernel(const void* __restrict__ X, long long n_rows, int d,
+                                                                uint8_t* __restrict__ Xq, float* __restrict__ scale) {
+  const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= n_rows) return;
+  const size_t base = (size_t)row * d;
+  float amax = 0.0f;
+  for (int k = lane * 4; k < d; k += 256)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) amax = fmaxf(amax, fabsf(load_elem<kDtype>(X, base + k + j)));
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+  const float s = amax > 0.0f ? __fdiv_rn(amax, 448.0f) : 1.0f;
+  if (lane == 0) scale[row] = s;
+  for (int k = lane * 4; k < d; k += 256) {
+    uint32_t packed = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) packed |= e4m3_rne(__fdiv_rn(load_elem<kDtype>(X, base + k + j), s)) << (8 * j);
+    *reinterpret_cast<uint32_t*>(Xq + base + k) = packed;
+  }
+}
+
+// The bf16 head's partial kernel with E4M3 operands: same workgroup order,
+// slices and fold; the epilogue scales each accumulator by its vocabulary
+// row's and its token's scale before folding.
+__global__ __launch_bounds__(kThreads, 1) void lmhead_fp8_partial_kernel(
+    const uint8_t* __restrict__ Hq, const float* __restrict__ h_scale, const uint8_t* __restrict__ Wq,
+    const float* __restrict__ w_scale, const int32_t* __restrict__ tokens, int n_tok, int d, int vocab, int n_tb,
+    int n_slices, int group, float2* __restrict__ part, float* __restrict__ zy_out) {
+  __shared__ uint4 smem[kEngineSmemChunks];
+  const Lanes L = lanes();
+  const int wv = L.wv, wt = L.wt, half = L.half, col = L.col;
+  const int S = n_slices;
+  const int n_groups = (S + group - 1) / group;
+  const int b = blockIdx.x;
+  const int band = b / (kSuperBand * n_groups);
+  const int tb_first = band * kSuperBand;
+  const int nb = min(kSuperBand, n_tb - tb_first);
+  const int rem = b - band * kSuperBand * n_groups;
+  const int grp = rem / nb;
+  const int t0 = (tb_first + rem % nb) * kBT;
+  const int n_vt = (vocab + kBV - 1) / kBV;
+  const int slice_first = grp * group;
+  const int slice_end = min(slice_first + group, S);
+  const int tile_begin = slice_tile(slice_first, n_vt, S);
+  const int tile_end = slice_tile(slice_end, n_vt, S);
+  const int row_bytes = d;
+  const int nks = row_bytes / kStepBytes;
+
+  Col c[4];
+  float hs[4];
+#pragma unroll
+  for (int bn = 0; bn < 4; ++bn) {
+    const int tok = t0 + wt * 128 + bn * 32 + col;
+    c[bn] = Col{tok < n_tok ? tokens[tok] : -1, -INFINITY, 0.0f, 0.0f, false};
+    hs[bn] = tok < n_tok ? h_scale[tok] : 0.0f;
+  }
+  auto w_rsrc = [&](int tile) {
+    const int v0 = tile * kBV;
+    return rsrc_words(Wq + (size_t)v0 * row_bytes, (uint32_t)min(kBV, vocab - v0) * row_bytes);
+  };
+  const int4v hr = rsrc_words(Hq + (size_t)t0 * row_bytes, (uint32_t)min(kBT, n_tok - t0) * row_bytes);
+  // Row scales through a bounded buffer: rows past the vocabulary read 0.
+  const __amdgpu_buffer_rsrc_t ws_rsrc = make_rsrc(w_scale, (uint32_t)vocab * 4u);
+
+  int slice = slice_first;
+  int slice_last_tile = slice_tile(slice + 1, n_vt, S) - 1;
+  auto epilogue = [&](int tile, floatx16 (&acc)[4][4]) {
+    const int vw = tile * kBV + wv * 128;
+    const bool partial = tile * kBV + kBV > vocab;
+    mfma_result_wait();
+#pragma unroll
+    for (int bn = 0; bn < 4; ++bn) {
+#pragma unroll
+      for (int bm = 0; bm < 4; ++bm) {
+        // z = (acc * scale of the row) * scale of the token; the row scales
+        // of this lane's 16 rows (vw + 32 bm + 8 (i / 4) + 4 half + i % 4)
+        // come one range-checked load each: rows past the vocabulary read 0
+        // and are masked by the fold
+        floatx16 z;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float w = buffer_load4(ws_rsrc, (uint32_t)(vw + bm * 32 + 8 * (i >> 2) + 4 * half + (i & 3)) * 4u);
+          z[i] = (acc_read(acc[bm][bn], i) * w) * hs[bn];
+        }
+        fold_values(c[bn], z, bm, vw, half, vocab, partial);
+      }
+    }
+    if (tile == slice_last_tile) {
+#pragma unroll
+      for (int bn = 0; bn < 4; ++bn) {
+        const int tok = t0 + wt * 128 + bn * 32 + col;
+        flush_slice(c[bn], tok, n_tok, half, ((size_t)slice * 2 + wv) * n_tok + tok, part);
+      }
+      ++slice;
+      slice_last_tile = slice_tile(slice + 1, n_vt, S) - 1;
+    }
+  };
+  run_tiles_f8(smem, L, row_bytes, tile_begin, tile_end, nks, w_rsrc, hr, epilogue);
+
+#pragma unroll
+  for (int bn = 0; bn < 4; ++bn)
+    if (c[bn].found) zy_out[t0 + wt * 128 + bn * 32 + col] = c[bn].zy;
+}
+
+}  // namespace
+
+hipError_t launch_quantize_rows_fp8(const void* X, int dtype, long long n_rows, int d, uint8_t* Xq, float* scale,
+                                    hipStream_t stream) {
+  const dim3 grid((unsigned)ceil_div(n_rows, 4));
+  if (dtype == 0)
+    hipLaunchKernelGGL(quantize_rows_fp8_kernel<0>, grid, dim3(256), 0, stream, X, n_rows, d, Xq, scale);
+  else
+    hipLaunchKernelGGL(quantize_rows_fp8_kernel<1>, grid, dim3(256), 0, stream, X, n_rows, d, Xq, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_lmhead_logprob_fp8(const uint8_t* Hq, const float* h_scale, const uint8_t* Wq, const float* w_scale,
+                                     int n_tok, int d, int vocab, const int32_t* tokens, float* logprob, float* lse,
+                                     void* workspace, hipStream_t stream) {
+  const int S = n_slices(vocab);
+  const int G = slices_per_group(n_tok, vocab);
+  const int ntb = (int)ceil_div(n_tok, kBT);
+  float2* part = static_cast<float2*>(workspace);
+  float* zy = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                       align256((size_t)2 * S * (size_t)n_tok * sizeof(float2)));
+  const dim3 grid((unsigned)ntb * (unsigned)n_slice_groups(n_tok, vocab));
+  hipLaunchKernelGGL(lmhead_fp8_partial_kernel, grid, dim3(kThreads), 0, stream, Hq, h_scale, Wq, w_scale, tokens,
+                     n_tok, d, vocab, ntb, S, G, part, zy);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_lse_combine(part, zy, n_tok, 2 * S, logprob, lse, stream);
+}
+
+}  // namespace itl

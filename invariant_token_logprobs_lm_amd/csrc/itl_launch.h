@@ -16,6 +16,11 @@ hipError_t launch_lmhead_logprob(const void* H, const void* W, int dtype, int n_
                                  const int32_t* tokens, float* logprob, float* lse, void* workspace,
                                  hipStream_t stream);
 
+// Merge each token's n_parts (max, sumexp) partials (slice-major) into its
+// logprob (z_y - lse) and lse (nullable).
+hipError_t launch_lse_combine(const float2* part, const float* zy, int n_tok, int n_parts, float* logprob, float* lse,
+                              hipStream_t stream);
+
 hipError_t launch_group_advantage(const float* rewards, const int32_t* group_offsets, int n_groups,
                                   int n_resp, float* advantages, hipStream_t stream);
 
@@ -33,6 +38,13 @@ constexpr long long kBwdMaxVocab = (1LL << 31) / (256LL * 4) - 256;
 hipError_t launch_reinforce_zero_backward(const void* H, const void* W, int dtype, int n_tok, int d, int vocab,
                                           const int32_t* tokens, const float* lse, const float* coef,
                                           float* dH, float* dW, void* workspace, hipStream_t stream);
+
+hipError_t launch_quantize_rows_fp8(const void* X, int dtype, long long n_rows, int d, uint8_t* Xq, float* scale,
+                                    hipStream_t stream);
+
+hipError_t launch_lmhead_logprob_fp8(const uint8_t* Hq, const float* h_scale, const uint8_t* Wq, const float* w_scale,
+                                     int n_tok, int d, int vocab, const int32_t* tokens, float* logprob, float* lse,
+                                     void* workspace, hipStream_t stream);
 
 size_t mismatch_stats_workspace_bytes(long long n_tok);
 

@@ -36,79 +36,12 @@
 // holds row 8*(i/4) + 4*(l/32) + (i mod 4), column (l mod 32).
 
 #include "itl_launch.h"
+#include "lse_fold.h"
 #include "tile_engine.h"
 
 namespace itl {
 
 namespace {
-
-// Online log-sum-exp state of one token column in one lane: the running
-// (max, sum of exp) of the slice so far, and the sampled logit once seen.
-struct Col {
-  int y;          // sampled row, -1 past the last token
-  float m, s;     // running max and sum of exp(z - m)
-  float zy;       // the sampled logit
-  bool found;
-};
-
-// Fold one 32 x 32 accumulator block (rows vw + 32 bm + ..., this lane's
-// token column) into the state. The lane's 16 logits are copied out of the
-// matrix-core registers where they are used (acc_read), so the fold needs
-// few VGPRs next to the accumulators. The sampled logit is picked with a
-// select tree keyed on the bits of its row, without a branch. Every kernel
-// folds with this one function, in the same block order, so a token's state
-// has the same bits whichever kernel computed it.
-__device__ __forceinline__ void fold_block(Col& c, const floatx16& a, int bm, int vw, int half, int vocab,
-                                           bool partial) {
-  const int o = c.y - vw;  // sampled row relative to this wavefront's 128 rows
-  // Register i of a lane holds row 32 bm + 8 (i / 4) + 4 half + (i % 4):
-  // bits 0, 1, 3, 4 of the row pick i, bit 2 picks the lane half.
-  const bool b0 = (o & 1) != 0, b1 = (o & 2) != 0, b2 = (o & 8) != 0, b3 = (o & 16) != 0;
-  const bool here = (unsigned)o < 128u && ((o >> 2) & 1) == half && (o >> 5) == bm;
-  floatx16 z;  // a vector, not an array: it must stay in registers
-#pragma unroll
-  for (int i = 0; i < 16; ++i) z[i] = acc_read(a, i);
-  if (partial) {
-    const int lim = vocab - (vw + bm * 32 + 4 * half);  // rows at or past this offset do not exist
-#pragma unroll
-    for (int i = 0; i < 16; ++i) z[i] = (8 * (i >> 2) + (i & 3) >= lim) ? -INFINITY : z[i];
-  }
-  const float pick = select16(z, b0, b1, b2, b3);
-  c.zy = here ? pick : c.zy;
-  c.found = c.found || here;
-
-  float bmax = z[0];
-#pragma unroll
-  for (int i = 1; i < 16; ++i) bmax = fmaxf(bmax, z[i]);
-  const float mnew = fmaxf(c.m, bmax);
-  // A lane whose rows so far are all absent has mnew = -inf; it then scales
-  // by exp2(-inf) = 0 around 0 and keeps (m, s) = (-inf, 0).
-  const float mref = mnew == -INFINITY ? 0.0f : mnew;
-  // (z - m) is exactly 0 for the running maximum, so its term is exactly 1
-  // and stays 1 (later rescales by exp2(0)): the final sum is >= 1 and
-  // logprob <= 0 holds in fp32.
-  float s0 = 0.0f, s1 = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 16; i += 2) {
-    s0 += fast_exp2((z[i] - mref) * kLog2e);
-    s1 += fast_exp2((z[i + 1] - mref) * kLog2e);
-  }
-  c.s = __builtin_fmaf(c.s, fast_exp2((c.m - mref) * kLog2e), s0 + s1);
-  c.m = mnew;
-}
-
-// Slice end: lanes l and l ^ 32 hold the same token (different rows); the
-// lower lane merges the upper lane's state into its own and writes the
-// wavefront's partial of the slice; every lane starts the next slice afresh.
-__device__ __forceinline__ void flush_slice(Col& c, int tok, int n_tok, int half, size_t part_index,
-                                            float2* __restrict__ part) {
-  const float m2 = __shfl_xor(c.m, 32, 64);
-  const float s2 = __shfl_xor(c.s, 32, 64);
-  lse_merge(c.m, c.s, m2, s2);
-  if (half == 0 && tok < n_tok) part[part_index] = make_float2(c.m, c.s);
-  c.m = -INFINITY;
-  c.s = 0.0f;
-}
 
 template <int kDtype>
 __global__ __launch_bounds__(kThreads, 1) void lmhead_lse_partial_kernel(
@@ -227,6 +160,8 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_lse_partial_narrow_kernel(
   if (c.found) zy_out[tok] = c.zy;
 }
 
+}  // namespace
+
 // Per token: merge the 2 S partials (slice-major, then wavefront). A
 // 1024-thread workgroup takes 64 tokens (lane = token, so every load is one
 // coalesced 512-byte row of the partial table); its 16 wavefronts split the
@@ -235,6 +170,8 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_lse_partial_narrow_kernel(
 // so a token's result has the same bits whatever n_tok; with few tokens the
 // 16 runs keep the latency chain short (at most 32 dependent merges).
 constexpr int kCombineWaves = 16;
+
+namespace {
 
 __global__ __launch_bounds__(64 * kCombineWaves) void lse_combine_kernel(const float2* __restrict__ part,
                                                                          const float* __restrict__ zy, int n_tok,
@@ -265,6 +202,13 @@ __global__ __launch_bounds__(64 * kCombineWaves) void lse_combine_kernel(const f
 }
 
 }  // namespace
+
+hipError_t launch_lse_combine(const float2* part, const float* zy, int n_tok, int n_parts, float* logprob, float* lse,
+                              hipStream_t stream) {
+  hipLaunchKernelGGL(lse_combine_kernel, dim3((unsigned)ceil_div(n_tok, 64)), dim3(64 * kCombineWaves), 0, stream,
+                     part, zy, n_tok, n_parts, logprob, lse);
+  return hipGetLastError();
+}
 
 size_t lmhead_workspace_bytes(long long n_tok, long long vocab) {
   if (n_tok <= 0) return 0;
@@ -303,9 +247,7 @@ hipError_t launch_lmhead_logprob(const void* H, const void* W, int dtype, int n_
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(lse_combine_kernel, dim3((unsigned)ceil_div(n_tok, 64)), dim3(64 * kCombineWaves), 0, stream,
-                     part, zy, n_tok, 2 * S, logprob, lse);
-  return hipGetLastError();
+  return launch_lse_combine(part, zy, n_tok, 2 * S, logprob, lse, stream);
 }
 
 }  // namespace itl

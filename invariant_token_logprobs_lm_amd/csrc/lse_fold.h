@@ -1,0 +1,88 @@
+// Per-lane online log-sum-exp fold of the head's logits, shared by every
+// logprob kernel of the library: a token's partials, and so its logprob,
+// have the same bits whichever kernel produced them, as long as the
+// kernels feed the same logit values in the same block order.
+#pragma once
+
+#include "device_common.h"
+#include "tile_engine.h"
+
+namespace itl {
+
+// Online log-sum-exp state of one token column in one lane: the running
+// (max, sum of exp) of the slice so far, and the sampled logit once seen.
+struct Col {
+  int y;          // sampled row, -1 past the last token
+  float m, s;     // running max and sum of exp(z - m)
+  float zy;       // the sampled logit
+  bool found;
+};
+
+// Fold one 32 x 32 block of logits (rows vw + 32 bm + ..., this lane's
+// token column; z[i] = row 32 bm + 8 (i / 4) + 4 half + (i % 4)) into the
+// state. The sampled logit is picked with a select tree keyed on the bits of
+// its row, without a branch. Every kernel folds with this one function, in
+// the same block order, so a token's state has the same bits whichever
+// kernel computed it.
+__device__ __forceinline__ void fold_values(Col& c, floatx16 z, int bm, int vw, int half, int vocab,
+                                            bool partial) {
+  const int o = c.y - vw;  // sampled row relative to this wavefront's 128 rows
+  // Register i of a lane holds row 32 bm + 8 (i / 4) + 4 half + (i % 4):
+  // bits 0, 1, 3, 4 of the row pick i, bit 2 picks the lane half.
+  const bool b0 = (o & 1) != 0, b1 = (o & 2) != 0, b2 = (o & 8) != 0, b3 = (o & 16) != 0;
+  const bool here = (unsigned)o < 128u && ((o >> 2) & 1) == half && (o >> 5) == bm;
+  if (partial) {
+    const int lim = vocab - (vw + bm * 32 + 4 * half);  // rows at or past this offset do not exist
+#pragma unroll
+    for (int i = 0; i < 16; ++i) z[i] = (8 * (i >> 2) + (i & 3) >= lim) ? -INFINITY : z[i];
+  }
+  const float pick = select16(z, b0, b1, b2, b3);
+  c.zy = here ? pick : c.zy;
+  c.found = c.found || here;
+
+  float bmax = z[0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) bmax = fmaxf(bmax, z[i]);
+  const float mnew = fmaxf(c.m, bmax);
+  // A lane whose rows so far are all absent has mnew = -inf; it then scales
+  // by exp2(-inf) = 0 around 0 and keeps (m, s) = (-inf, 0).
+  const float mref = mnew == -INFINITY ? 0.0f : mnew;
+  // (z - m) is exactly 0 for the running maximum, so its term is exactly 1
+  // and stays 1 (later rescales by exp2(0)): the final sum is >= 1 and
+  // logprob <= 0 holds in fp32.
+  float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; i += 2) {
+    s0 += fast_exp2((z[i] - mref) * kLog2e);
+    s1 += fast_exp2((z[i + 1] - mref) * kLog2e);
+  }
+  c.s = __builtin_fmaf(c.s, fast_exp2((c.m - mref) * kLog2e), s0 + s1);
+  c.m = mnew;
+}
+
+// Slice end: lanes l and l ^ 32 hold the same token (different rows); the
+// lower lane merges the upper lane's state into its own and writes the
+// wavefront's partial of the slice; every lane starts the next slice afresh.
+__device__ __forceinline__ void flush_slice(Col& c, int tok, int n_tok, int half, size_t part_index,
+                                            float2* __restrict__ part) {
+  const float m2 = __shfl_xor(c.m, 32, 64);
+  const float s2 = __shfl_xor(c.s, 32, 64);
+  lse_merge(c.m, c.s, m2, s2);
+  if (half == 0 && tok < n_tok) part[part_index] = make_float2(c.m, c.s);
+  c.m = -INFINITY;
+  c.s = 0.0f;
+}
+
+
+// Fold one accumulator block as it stands (the bf16 / fp32 heads). The
+// lane's 16 logits are copied out of the matrix-core registers where they
+// are used (acc_read), so the fold needs few VGPRs next to the accumulators.
+__device__ __forceinline__ void fold_block(Col& c, const floatx16& a, int bm, int vw, int half, int vocab,
+                                           bool partial) {
+  floatx16 z;  // a vector, not an array: it must stay in registers
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = acc_read(a, i);
+  fold_values(c, z, bm, vw, half, vocab, partial);
+}
+
+}  // namespace itl

@@ -454,4 +454,178 @@ __device__ __forceinline__ void run_tiles_narrow(uint4* smem, const Lanes& L, in
   __syncthreads();
 }
 
+// FP8 (E4M3) variant of run_tiles: the same slots, swizzle, loads and
+// barrier cadence, with v_mfma_scale_f32_32x32x64_f8f6f4 (both operands
+// E4M3, block scales 1). A 128-byte K step is 128 values: two sub-steps of
+// 64, each MFMA taking 32 bytes per lane (lane half h of sub-step j: chunks
+// 4 j + 2 h and 4 j + 2 h + 1 of its row, i.e. 32 consecutive K values).
+// The instruction sums its 64 products as one dot product whatever order
+// the K values sit in the lanes (A and B use the same placement), so the
+// result is sum_k A[r, k] B[c, k]; the K order of the accumulation is fixed.
+struct Frag8 {
+  uint4 lo, hi;
+};
+
+typedef int intx8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ void mma_f8(floatx16& acc, const Frag8& a, const Frag8& b) {
+  acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(__builtin_bit_cast(intx8, a), __builtin_bit_cast(intx8, b),
+                                                        acc, 0, 0, 0, 127, 0, 127);
+}
+__device__ __forceinline__ void mma_f8_first(floatx16& acc, const Frag8& a, const Frag8& b) {
+  acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(__builtin_bit_cast(intx8, a), __builtin_bit_cast(intx8, b),
+                                                        floatx16{}, 0, 0, 0, 127, 0, 127);
+}
+
+template <class ARsrc, class Epi>
+__device__ __forceinline__ void run_tiles_f8(uint4* smem, const Lanes& L, int row_bytes, int tile_begin, int tile_end,
+                                             int nks, const ARsrc& a_rsrc, int4v b_rsrc, Epi&& epi) {
+  const int lane = L.lane, wave = L.wave, wv = L.wv, wt = L.wt, half = L.half, col = L.col;
+  const int lr = lane >> 3;
+  uint32_t voff[kDmaPerWave];
+#pragma unroll
+  for (int j = 0; j < kDmaPerWave; ++j)
+    voff[j] = (uint32_t)(wave * 64 + j * kDmaRows + lr) * (uint32_t)row_bytes + (((lane & 7) ^ lr ^ (j & 1)) * 16);
+  const uint32_t lds_wave =
+      (uint32_t)(size_t)((__attribute__((address_space(3))) uint4*)smem) + wave * 64 * kStepBytes;
+  const int4v hr = b_rsrc;
+  auto w_slot_lds = [&](int slot) { return lds_wave + (uint32_t)slot * kSlotBytes; };
+  auto h_slot_lds = [&](int slot) { return lds_wave + (uint32_t)(kWSlots + slot) * kSlotBytes; };
+
+  // Fragment reads: sub-step j, piece p (0 = low 16 bytes, 1 = high) of
+  // lane (half, col) is logical chunk 4 j + 2 half + p of row col.
+  int a_off[2][2], b_off[2][2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int pc = (4 * j + 2 * half + p) ^ swz(col);
+      a_off[j][p] = (wv * 128 + col) * kRowChunks + pc;
+      b_off[j][p] = (wt * 128 + col) * kRowChunks + pc;
+    }
+
+  int w_tile = tile_begin, w_ks = 0;
+  int h_ks = 0;
+  int w_slot_next = 0, h_slot_next = 0;
+  auto next_w = [&]() {
+    if (++w_ks == nks) {
+      w_ks = 0;
+      w_tile = min(w_tile + 1, tile_end - 1);
+    }
+    w_slot_next = w_slot_next == kWSlots - 1 ? 0 : w_slot_next + 1;
+  };
+  auto next_h = [&]() {
+    h_ks = h_ks + 1 == nks ? 0 : h_ks + 1;
+    h_slot_next ^= 1;
+  };
+  // One sub-step: MFMA q (q = 4 bm + bn) on (A, B), interleaved with the 16
+  // reads of the next sub-step's fragments (order A0 B0 B1 B2 B3 A1 A2 A3,
+  // low then high half) from slots (wsl, hsl), sub-step rj: one per MFMA, or
+  // two per MFMA in the first 8 when kFront (they must land before the
+  // barrier). With kDma, the 8 loads of H(g + 2) and then the 8 of W(g + 3)
+  // go one per MFMA.
+  auto phase = [&](floatx16 (&acc)[4][4], const Frag8 (&A)[4], const Frag8 (&B)[4], auto first, auto front,
+                   auto dma, int wsl, int hsl, int rj, Frag8 (&RA)[4], Frag8 (&RB)[4]) {
+    const uint4* sa = smem + wsl * kSlotChunks;
+    const uint4* sb = smem + (kWSlots + hsl) * kSlotChunks;
+    int4v wr;
+    uint32_t wsoff = 0, hsoff = 0, wm = 0, hm = 0;
+    if constexpr (decltype(dma)::value) {
+      wr = a_rsrc(w_tile);
+      wsoff = (uint32_t)w_ks * kStepBytes;
+      hsoff = (uint32_t)h_ks * kStepBytes;
+      wm = w_slot_lds(w_slot_next);
+      hm = h_slot_lds(h_slot_next);
+    }
+    auto read = [&](int r) {  // read number r = 0..15 of the next sub-step
+      const int f = r >> 1, p = r & 1;
+      if (f == 0) (p ? RA[0].hi : RA[0].lo) = sa[a_off[rj][p]];
+      else if (f <= 4) (p ? RB[f - 1].hi : RB[f - 1].lo) = sb[b_off[rj][p] + (f - 1) * 32 * kRowChunks];
+      else (p ? RA[f - 4].hi : RA[f - 4].lo) = sa[a_off[rj][p] + (f - 4) * 32 * kRowChunks];
+    };
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      if constexpr (decltype(first)::value) mma_f8_first(acc[q >> 2][q & 3], A[q >> 2], B[q & 3]);
+      else mma_f8(acc[q >> 2][q & 3], A[q >> 2], B[q & 3]);
+      if constexpr (decltype(front)::value) {
+        if (q < 8) {
+          read(2 * q);
+          read(2 * q + 1);
+        }
+      } else {
+        read(q);
+      }
+      if constexpr (decltype(dma)::value) {
+        if (q < 8) dma16(hr, voff[q], hsoff, hm + q * 1024);
+        else dma16(wr, voff[q - 8], wsoff, wm + (q - 8) * 1024);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (decltype(dma)::value) {
+      next_h();
+      next_w();
+    }
+  };
+
+  using T = std::true_type;
+  using F = std::false_type;
+  {
+    const int4v wr0 = a_rsrc(w_tile);
+#pragma unroll
+    for (int j = 0; j < kDmaPerWave; ++j) dma16(wr0, voff[j], (uint32_t)w_ks * kStepBytes, w_slot_lds(0) + j * 1024);
+#pragma unroll
+    for (int j = 0; j < kDmaPerWave; ++j) dma16(hr, voff[j], 0, h_slot_lds(0) + j * 1024);
+    next_w();
+    next_h();
+    const int4v wr1 = a_rsrc(w_tile);
+#pragma unroll
+    for (int j = 0; j < kDmaPerWave; ++j) dma16(wr1, voff[j], (uint32_t)w_ks * kStepBytes, w_slot_lds(1) + j * 1024);
+    next_w();
+  }
+  wait_and_barrier<kDmaPerWave>();  // W(0), H(0) landed
+  {
+    const int4v wr = a_rsrc(w_tile);
+    const uint32_t hm = h_slot_lds(h_slot_next), wm = w_slot_lds(w_slot_next);
+#pragma unroll
+    for (int j = 0; j < kDmaPerWave; ++j) dma16(hr, voff[j], (uint32_t)h_ks * kStepBytes, hm + j * 1024);
+#pragma unroll
+    for (int j = 0; j < kDmaPerWave; ++j) dma16(wr, voff[j], (uint32_t)w_ks * kStepBytes, wm + j * 1024);
+    next_h();
+    next_w();
+  }
+  // X: the current sub-step's fragments, Y: the next one's.
+  Frag8 xa[4], xb[4], ya[4], yb[4];
+  {
+    const uint4* sa = smem;
+    const uint4* sb = smem + kWSlots * kSlotChunks;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      xa[m].lo = sa[a_off[0][0] + m * 32 * kRowChunks];
+      xa[m].hi = sa[a_off[0][1] + m * 32 * kRowChunks];
+      xb[m].lo = sb[b_off[0][0] + m * 32 * kRowChunks];
+      xb[m].hi = sb[b_off[0][1] + m * 32 * kRowChunks];
+    }
+  }
+  int wslot = 0, hslot = 0;
+  // One K step g: sub-step 0 (X) while sub-step 1 is read into Y; the
+  // barrier then publishes step g + 1 (step g is all in registers, so its
+  // slots are free); sub-step 1 (Y) while step g + 1's sub-step 0 is read
+  // into X and H(g + 2), W(g + 3) are loaded into step g's slots.
+  auto k_step = [&](floatx16 (&acc)[4][4], auto first) {
+    phase(acc, xa, xb, first, T{}, F{}, wslot, hslot, 1, ya, yb);
+    wait_and_barrier<kDmaPerWave>();  // W(g + 1), H(g + 1) landed; W(g + 2) may still be in flight
+    wslot = wslot == kWSlots - 1 ? 0 : wslot + 1;
+    hslot ^= 1;
+    phase(acc, ya, yb, F{}, F{}, T{}, wslot, hslot, 0, xa, xb);
+  };
+  for (int tile = tile_begin; tile < tile_end; ++tile) {
+    floatx16 acc[4][4];
+    k_step(acc, T{});
+    for (int ks = 1; ks < nks; ++ks) k_step(acc, F{});
+    epi(tile, acc);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+}
+
 }  // namespace itl

@@ -22,7 +22,7 @@ OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
 
 def _declared():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"\b(itl_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(itl_[a-z0-9_]+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -190,3 +190,23 @@ def test_probe_library_is_separate_and_loads():
     import invariant_token_logprobs_lm_amd as itl
 
     assert not hasattr(itl.lib, "itl_probe_mfma_bf16")
+
+
+def test_fp8_validation(lib):
+    v = ctypes.c_void_p
+    q = lib.itl_quantize_rows_fp8
+    assert q(v(1), 0, -1, 128, v(4), v(4), None) == INVALID
+    assert q(v(1), 0, 4, 96, v(4), v(4), None) == UNSUPPORTED
+    assert q(v(1), 7, 4, 128, v(4), v(4), None) == UNSUPPORTED
+    assert q(v(1), 0, 4, 128, v(5), v(4), None) == INVALID  # Xq misaligned
+    assert q(None, 0, 4, 128, v(4), v(4), None) == INVALID
+    assert q(None, 0, 0, 128, None, None, None) == OK
+    f = lib.itl_lmhead_logprob_fp8
+    args = lambda **k: [v(k.get("Hq", 16)), v(4), v(k.get("Wq", 16)), v(4), k.get("n", 4), k.get("d", 128),
+                        k.get("V", 10), v(4), v(4), None, v(k.get("ws", 256)), k.get("wsb", 1 << 20), None]
+    assert f(*args(d=64)) == UNSUPPORTED
+    assert f(*args(n=-1)) == INVALID
+    assert f(*args(Hq=8)) == INVALID       # 16-byte alignment
+    assert f(*args(wsb=16)) == WORKSPACE
+    assert f(*args(ws=255)) == WORKSPACE
+    assert f(*args(n=0, Hq=0, Wq=0)) == OK

@@ -1,0 +1,150 @@
+"""GPU parity of the FP8 (E4M3) head: itl_quantize_rows_fp8 bit for bit
+against the oracle's quantisation (codes and scales are integer decisions
+taken in float32 on both sides), and itl_lmhead_logprob_fp8 within 1e-3 of
+the float64 oracle on the oracle's own codes. Small cases compare every
+token; the qwen3-4b head at full size compares all of W's codes and a seeded
+sample of tokens. Batch and position invariance and run-to-run bits too."""
+
+import numpy as np
+import pytest
+
+from helpers import same_bits, say
+
+pytestmark = pytest.mark.gpu
+
+TOL_LP = 1e-3
+
+
+def _itl():
+    import invariant_token_logprobs_lm_amd as itl
+
+    return itl
+
+
+def _host_f32(X):
+    import torch
+
+    return X.float().cpu().numpy()
+
+
+@pytest.mark.parametrize("n,d,dtype_name,scale_pow", [
+    (37, 128, "bf16", 0), (200, 256, "f32", 0), (64, 2560, "bf16", 0),
+    (50, 384, "f32", -30),   # tiny values: scales far below 1, many subnormal codes
+    (50, 128, "f32", 20),    # large values
+])
+def test_quantize_rows_bit_exact(cuda, n, d, dtype_name, scale_pow):
+    import torch
+    from oracle import fp8
+
+    g = torch.Generator(device="cpu").manual_seed(n * 31 + d)
+    X = torch.randn(n, d, generator=g) * (2.0 ** scale_pow)
+    X[3] = 0.0                     # an all-zero row
+    X[5, ::7] = 0.0
+    X[6] = X[6] * 1e-3             # a row with a different range
+    X[7, 1] = -X[7].abs().max() * 2  # a negative maximum
+    dt = torch.bfloat16 if dtype_name == "bf16" else torch.float32
+    X = X.to(dt)
+    itl = _itl()
+    Xq, s = itl.quantize_rows_fp8(X.to(cuda))
+    q_o, s_o = fp8.quantize_rows_fp8(_host_f32(X))
+    assert np.array_equal(Xq.cpu().numpy(), q_o)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), s_o.view(np.uint32))
+    say(f"[fp8 quantize] {n}x{d} {dtype_name} 2^{scale_pow}: codes and scales bit-identical")
+
+
+def _oracle_quantized_head(n_tok, d, vocab, seed, w_std=0.05):
+    import torch
+    from oracle import fp8
+
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    H = torch.randn(n_tok, d, generator=g).to(torch.bfloat16)
+    W = (torch.randn(vocab, d, generator=g) * w_std).to(torch.bfloat16)
+    y = torch.randint(0, vocab, (n_tok,), generator=g, dtype=torch.int32)
+    Hq, hs = fp8.quantize_rows_fp8(_host_f32(H))
+    Wq, ws = fp8.quantize_rows_fp8(_host_f32(W))
+    return Hq, hs, Wq, ws, y.numpy()
+
+
+def _to_dev(cuda, *arrays):
+    import torch
+
+    return [torch.from_numpy(np.ascontiguousarray(a)).to(cuda) for a in arrays]
+
+
+@pytest.mark.parametrize("n_tok,d,vocab", [
+    (700, 256, 5000),          # 3 token blocks (ragged), 20 tiles
+    (300, 128, 4096 + 37),     # one K step; last tile of 37 rows (scale loads past the end)
+    (1, 128, 300),             # one token
+    (513, 384, 8192 + 256),    # d = 3 K steps
+    (5200, 128, 150 * 256 - 17),  # 21 x 150 > 2048: several slices per workgroup
+])
+def test_lmhead_fp8_parity(cuda, n_tok, d, vocab):
+    from oracle import fp8
+
+    Hq, hs, Wq, ws, y = _oracle_quantized_head(n_tok, d, vocab, seed=n_tok + vocab)
+    lp_o, lse_o = fp8.lmhead_logprob_fp8(Hq, hs, Wq, ws, y)
+    itl = _itl()
+    Hq_d, hs_d, Wq_d, ws_d, y_d = _to_dev(cuda, Hq, hs, Wq, ws, y)
+    lp, lse = itl.lmhead_logprob_fp8(Hq_d, hs_d, Wq_d, ws_d, y_d)
+    e_lp = float(np.max(np.abs(lp.cpu().numpy() - lp_o)))
+    e_lse = float(np.max(np.abs(lse.cpu().numpy() - lse_o)))
+    say(f"[fp8 parity {n_tok}x{d}x{vocab}] max|dlp|={e_lp:.3e} max|dlse|={e_lse:.3e}")
+    assert e_lp <= TOL_LP and e_lse <= TOL_LP
+    assert float(lp.max()) <= 0.0
+
+
+def test_lmhead_fp8_invariance(cuda):
+    """The same token gives the same bits alone, at every row of a block, in
+    any sub-batch; and run to run."""
+    import torch
+
+    Hq, hs, Wq, ws, y = _oracle_quantized_head(600, 256, 3000, seed=5)
+    itl = _itl()
+    Hq_d, hs_d, Wq_d, ws_d, y_d = _to_dev(cuda, Hq, hs, Wq, ws, y)
+    lp, lse = itl.lmhead_logprob_fp8(Hq_d, hs_d, Wq_d, ws_d, y_d)
+    for lo, n in ((0, 1), (17, 5), (100, 64), (300, 257)):
+        a, b = itl.lmhead_logprob_fp8(Hq_d[lo:lo + n], hs_d[lo:lo + n], Wq_d, ws_d, y_d[lo:lo + n])
+        assert same_bits(a, lp[lo:lo + n]) and same_bits(b, lse[lo:lo + n]), (lo, n)
+    for pos in (0, 1, 31, 32, 127, 128, 200, 255):
+        Hp, hp, yp = Hq_d[:256].clone(), hs_d[:256].clone(), y_d[:256].clone()
+        Hp[pos], hp[pos], yp[pos] = Hq_d[17], hs_d[17], y_d[17]
+        a, _ = itl.lmhead_logprob_fp8(Hp, hp, Wq_d, ws_d, yp)
+        assert same_bits(a[pos:pos + 1], lp[17:18]), pos
+    again = itl.lmhead_logprob_fp8(Hq_d, hs_d, Wq_d, ws_d, y_d)
+    torch.cuda.synchronize()
+    assert same_bits(again[0], lp) and same_bits(again[1], lse)
+
+
+def test_lmhead_fp8_full_size_head(cuda):
+    """The qwen3-4b head at full size: the GPU's W codes equal the oracle's
+    for every row; sampled tokens' logprobs (their H rows quantised by the
+    oracle too, and checked equal to the GPU's codes) within 1e-3."""
+    import torch
+    from oracle import fp8
+    from synth import WORKLOADS, draw_head, draw_layout, sample_tokens, token_subset
+
+    wl = WORKLOADS["qwen3-4b-head"]
+    lay = draw_layout(wl)
+    H, W = draw_head(wl, lay.n_tok, device=cuda)
+    y = sample_tokens(H, W, wl)
+    itl = _itl()
+    Wq, ws = itl.quantize_rows_fp8(W)
+    Hq, hs = itl.quantize_rows_fp8(H)
+    lp, lse = itl.lmhead_logprob_fp8(Hq, hs, Wq, ws, y)
+    Wq_h, ws_h = Wq.cpu().numpy(), ws.cpu().numpy()
+    Wf = W.float().cpu().numpy()
+    for r0 in range(0, wl.vocab, 16384):
+        q_o, s_o = fp8.quantize_rows_fp8(Wf[r0:r0 + 16384])
+        assert np.array_equal(Wq_h[r0:r0 + 16384], q_o), r0
+        assert np.array_equal(ws_h[r0:r0 + 16384].view(np.uint32), s_o.view(np.uint32)), r0
+    del Wf
+    tok = token_subset(lay.n_tok, 32, seed=11)
+    Hs = H.index_select(0, torch.from_numpy(tok).to(cuda)).float().cpu().numpy()
+    hq_o, hs_o = fp8.quantize_rows_fp8(Hs)
+    assert np.array_equal(Hq.cpu().numpy()[tok], hq_o)
+    assert np.array_equal(hs.cpu().numpy()[tok].view(np.uint32), hs_o.view(np.uint32))
+    lp_o, lse_o = fp8.lmhead_logprob_fp8(hq_o, hs_o, Wq_h, ws_h, y.cpu().numpy()[tok])
+    e_lp = float(np.max(np.abs(lp.cpu().numpy()[tok] - lp_o)))
+    say(f"[fp8 qwen3-4b-head] n_tok={lay.n_tok}: W codes bit-identical; sampled max|dlp|={e_lp:.3e}")
+    assert e_lp <= TOL_LP
+    assert float(lp.max()) <= 0.0
