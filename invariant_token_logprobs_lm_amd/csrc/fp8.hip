@@ -89,19 +89,12 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_fp8_partial_kernel(
   const Lanes L = lanes();
   const int wv = L.wv, wt = L.wt, half = L.half, col = L.col;
   const int S = n_slices;
-  const int n_groups = (S + group - 1) / group;
-  const int b = blockIdx.x;
-  const int band = b / (kSuperBand * n_groups);
-  const int tb_first = band * kSuperBand;
-  const int nb = min(kSuperBand, n_tb - tb_first);
-  const int rem = b - band * kSuperBand * n_groups;
-  const int grp = rem / nb;
-  const int t0 = (tb_first + rem % nb) * kBT;
+  const WideWork work = wide_work(blockIdx.x, n_tb, S, group);
+  const int t0 = work.tb * kBT;
   const int n_vt = (vocab + kBV - 1) / kBV;
-  const int slice_first = grp * group;
-  const int slice_end = min(slice_first + group, S);
-  const int tile_begin = slice_tile(slice_first, n_vt, S);
-  const int tile_end = slice_tile(slice_end, n_vt, S);
+  const int slice_first = work.slice_first;
+  const int tile_begin = slice_tile(work.slice_first, n_vt, S);
+  const int tile_end = slice_tile(work.slice_end, n_vt, S);
   const int row_bytes = d;
   const int nks = row_bytes / kStepBytes;
 

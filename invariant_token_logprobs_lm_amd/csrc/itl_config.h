@@ -61,4 +61,32 @@ inline int n_slice_groups(long long n_tok, long long vocab) {
 // or ceil(n_vt / S) tiles. This is a pure function of the vocabulary size.
 __host__ __device__ inline int slice_tile(int s, int n_vt, int S) { return (int)(((long long)s * n_vt) / S); }
 
+// Work of workgroup b of the wide logprob kernels (grid = n_tb x
+// ceil(S / group)): super-bands of kSuperBand token blocks walked slice group
+// by slice group with the token block fastest. Workgroups are dispatched to
+// the 8 XCDs round-robin, so the 32 workgroups an XCD runs at once hold 4
+// token blocks x 8 slice groups (each H block read by 8 of them, each W tile
+// by 4, through the XCD's L2), and all XCDs walk the same slices at the same
+// time (W shared through the Infinity Cache). Only which workgroup computes
+// a slice when depends on this order, never any arithmetic.
+struct WideWork {
+  int tb;           // token block
+  int slice_first;  // slices [slice_first, slice_end)
+  int slice_end;
+};
+
+__host__ __device__ inline WideWork wide_work(int b, int n_tb, int S, int group) {
+  const int n_groups = (S + group - 1) / group;
+  const int band = b / (kSuperBand * n_groups);
+  const int tb_first = band * kSuperBand;
+  const int nb = n_tb - tb_first < kSuperBand ? n_tb - tb_first : kSuperBand;
+  const int rem = b - band * kSuperBand * n_groups;
+  const int grp = rem / nb;
+  WideWork w;
+  w.tb = tb_first + rem % nb;
+  w.slice_first = grp * group;
+  w.slice_end = w.slice_first + group < S ? w.slice_first + group : S;
+  return w;
+}
+
 }  // namespace itl

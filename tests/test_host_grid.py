@@ -1,0 +1,51 @@
+"""Host-side checks of the logprob kernels' work decomposition: the C++
+functions the kernels use (itl_config.h), compiled into a host program with
+hipcc, over a few thousand (n_tok, vocab) pairs: every (token block, slice)
+pair computed once, slices tiling the vocabulary, the narrow grid's
+coverage. No GPU needed."""
+
+import os
+import shutil
+import subprocess
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def grid_check(tmp_path_factory):
+    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(hipcc):
+        pytest.skip("hipcc not available")
+    out = str(tmp_path_factory.mktemp("grid") / "grid_check")
+    cmd = [hipcc, "-O2", "-std=c++17", "-I", os.path.join(ROOT, "invariant_token_logprobs_lm_amd", "csrc"),
+           os.path.join(ROOT, "tests", "host", "grid_check.cpp"), "-o", out]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    return out
+
+
+def _run(exe, pairs):
+    args = [str(x) for p in pairs for x in p]
+    r = subprocess.run([exe, *args], capture_output=True, text=True)
+    assert r.returncode == 0 and r.stdout.startswith("ok"), r.stdout + r.stderr
+
+
+def test_workload_shapes(grid_check):
+    pairs = [(1, 151936), (64, 151936), (65, 151936), (256, 151936), (2048, 151936), (2049, 151936),
+             (133010, 151936), (294884, 151936), (308010, 129280), (1, 1), (5, 1), (64, 3), (700, 5000),
+             (300, 4133), (513, 8448), (5200, 38383), (16684, 2000), (177, 1024)]
+    _run(grid_check, pairs)
+
+
+def test_random_shapes(grid_check):
+    rng = np.random.default_rng(0)
+    n = rng.integers(1, 40000, 600)
+    v = rng.integers(1, 300000, 600)
+    _run(grid_check, list(zip(n.tolist(), v.tolist())))
+    # around the slice-count and group thresholds
+    pairs = [(nt, vv) for nt in (1, 63, 64, 65, 255, 256, 257, 2048, 2304, 8192)
+             for vv in (255, 256, 257, 65535, 65536, 65537, 65536 + 256, 131071, 200000)]
+    _run(grid_check, pairs)
