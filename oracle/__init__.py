@@ -43,6 +43,7 @@ any inputs: parity against the pages' own figures is unpinned.
 from .lmhead import to_f64, logits, log_softmax_at, lmhead_logprob
 from .diagnostics import STAT_NAMES, mismatch_stats
 from .fp8 import e4m3_decode, e4m3_encode, quantize_rows_fp8, lmhead_logprob_fp8
+from .fp8 import e2m1_decode, e2m1_encode, quantize_rows_mxfp4, mxfp4_decode, lmhead_logprob_mxfp4
 from .reinforce_zero import (
     group_advantage,
     importance_ratio,
@@ -69,4 +70,9 @@ __all__ = [
     "e4m3_encode",
     "quantize_rows_fp8",
     "lmhead_logprob_fp8",
+    "e2m1_decode",
+    "e2m1_encode",
+    "quantize_rows_mxfp4",
+    "mxfp4_decode",
+    "lmhead_logprob_mxfp4",
 ]

@@ -94,3 +94,91 @@ def lmhead_logprob_fp8(Hq, h_scale, Wq, w_scale, tokens, vocab_chunk=8192):
     Hd = e4m3_decode(Hq) * np.asarray(h_scale, dtype=np.float64)[:, None]
     Wd = e4m3_decode(Wq) * np.asarray(w_scale, dtype=np.float64)[:, None]
     return lmhead_logprob(Hd, Wd, tokens, vocab_chunk=vocab_chunk)
+
+
+# --- MXFP4 weights (OCP Microscaling: FP4 E2M1 elements, E8M0 block scales) ---
+#
+# Same section of the same page ("FP8 and MXFP4 weights"). Readings: the OCP
+# MX format, blocks of 32 consecutive values along the contraction dimension
+# (d) sharing one power-of-two scale 2^e stored as E8M0 (e + 127); the scale
+# of a block is 2^(floor(log2 amax) - 2) (2 = the exponent of E2M1's largest
+# value, 6 = 1.5 x 2^2), clamped to [2^-127, 2^127], and 2^-127 (code 0) for
+# an all-zero block; elements are E2M1 of x / 2^e (exact power-of-two
+# scaling), rounding to nearest, ties to even, saturating at +-6. Codes are
+# packed two per byte, element k in the low nibble when k is even. Against an
+# MXFP4 head the activations are E4M3 with per-row scales, as above.
+
+E2M1_VALUES = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def e2m1_decode(codes):
+    """Exact values of E2M1 codes (low 4 bits of each entry)."""
+    c = np.asarray(codes).astype(np.int64) & 15
+    v = E2M1_VALUES[c & 7]
+    return np.where(c & 8, -v, v)
+
+
+def e2m1_encode(x):
+    """E2M1 codes of float32 values: round to nearest, ties to even,
+    saturating at +-6."""
+    x = np.asarray(x, dtype=np.float32)
+    sign = (np.signbit(x)).astype(np.uint8) << 3
+    a = np.abs(x).astype(np.float64)
+    out = np.zeros(x.shape, dtype=np.uint8)
+    sub = a < 1.0
+    out[sub] = np.rint(a[sub] * 2.0).astype(np.uint8)  # 0, 0.5 or (rounded up) 1.0 = code 2
+    nor = ~sub
+    an = a[nor]
+    e = np.floor(np.log2(an)).astype(np.int64)
+    e = np.where(np.ldexp(1.0, e) > an, e - 1, e)
+    e = np.where(np.ldexp(1.0, e + 1) <= an, e + 1, e)
+    r = np.rint(np.ldexp(an, 1 - e))  # in [2, 4], ties to even
+    carry = r == 4
+    e = np.where(carry, e + 1, e)
+    r = np.where(carry, 2, r)
+    code = ((e + 1) << 1) | (r.astype(np.int64) - 2)
+    code = np.where((e > 2) | ((e == 2) & (r > 3)), 7, code)
+    out[nor] = code.astype(np.uint8)
+    return out | sign
+
+
+def quantize_rows_mxfp4(X):
+    """MXFP4 of a matrix [n, d] (d a multiple of 32): (packed codes uint8
+    [n, d/2], E8M0 scale codes uint8 [n, d/32])."""
+    from .lmhead import to_f64
+
+    Xf = to_f64(X).astype(np.float32)
+    n, d = Xf.shape
+    blocks = Xf.reshape(n, d // 32, 32)
+    amax = np.max(np.abs(blocks), axis=2).astype(np.float64)
+    safe = np.where(amax > 0, amax, 1.0)
+    e = np.floor(np.log2(safe)).astype(np.int64)
+    e = np.where(np.ldexp(1.0, e) > safe, e - 1, e)
+    e = np.where(np.ldexp(1.0, e + 1) <= safe, e + 1, e)
+    e = np.clip(e - 2, -127, 127)
+    e = np.where(amax > 0, e, -127)
+    scaled = np.ldexp(blocks.astype(np.float64), -e[:, :, None]).astype(np.float32)  # exact
+    codes = e2m1_encode(scaled).reshape(n, d)
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    return packed, (e + 127).astype(np.uint8)
+
+
+def mxfp4_decode(packed, scale_codes):
+    """Exact float64 values of an MXFP4 matrix."""
+    p = np.asarray(packed, dtype=np.uint8)
+    n, half = p.shape
+    codes = np.empty((n, 2 * half), dtype=np.uint8)
+    codes[:, 0::2] = p & 15
+    codes[:, 1::2] = p >> 4
+    v = e2m1_decode(codes).reshape(n, -1, 32)
+    sc = np.ldexp(1.0, np.asarray(scale_codes, dtype=np.int64) - 127)
+    return (v * sc[:, :, None]).reshape(n, 2 * half)
+
+
+def lmhead_logprob_mxfp4(Hq, h_scale, Wq4, w_scale_codes, tokens, vocab_chunk=8192):
+    """Sampled-token logprob and lse of an MXFP4 head against E4M3 token
+    rows with per-row scales: the head's definition on the exact decoded
+    values."""
+    Hd = e4m3_decode(Hq) * np.asarray(h_scale, dtype=np.float64)[:, None]
+    Wd = mxfp4_decode(Wq4, w_scale_codes)
+    return lmhead_logprob(Hd, Wd, tokens, vocab_chunk=vocab_chunk)

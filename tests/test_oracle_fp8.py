@@ -106,3 +106,78 @@ def test_fp8_logprob_is_the_head_on_dequantised_rows():
     # and near the unquantised head (3 mantissa bits: a few hundredths here)
     lp3, _ = oracle.lmhead_logprob(H, W, y)
     assert np.max(np.abs(lp - lp3)) < 0.2
+
+
+# --- MXFP4 ---
+
+def test_e2m1_table_and_round_trip():
+    # the 16 codes by their bit fields: sign, 2 exponent bits (bias 1), 1 mantissa bit
+    for c in range(16):
+        s = -1.0 if c & 8 else 1.0
+        e, m = (c >> 1) & 3, c & 1
+        want = s * (m * 0.5 if e == 0 else (1 + m / 2) * 2.0 ** (e - 1))
+        assert fp8.e2m1_decode(c) == want, c
+    codes = np.arange(16, dtype=np.uint8)
+    back = fp8.e2m1_encode(fp8.e2m1_decode(codes).astype(np.float32))
+    assert np.array_equal(back[codes != 8], codes[codes != 8]) and back[8] == 8  # -0 keeps its sign
+
+
+@pytest.mark.parametrize("x,code", [
+    (0.25, 0), (0.75, 2), (1.25, 2), (1.75, 4), (2.5, 4), (3.5, 6), (5.0, 6),   # ties to even
+    (0.3, 1), (2.9, 5), (4.9, 6), (5.1, 7), (7.0, 7), (100.0, 7), (-1.0, 10), (-0.0, 8),
+])
+def test_e2m1_roundings(x, code):
+    assert int(fp8.e2m1_encode(np.float32(x))) == code
+
+
+def test_mxfp4_block_scales_by_hand():
+    # block 0: amax 6 -> 2^(2 - 2) = 1 (code 127), values exact; block 1: amax 0.75 -> 2^(-1 - 2)
+    # = 1/8 (code 124), 0.75 * 8 = 6 exact; block 2 all zero -> code 0; block 3: amax 1000 ->
+    # 2^(9 - 2) = 128 (code 134), 1000 / 128 = 7.8 saturates to 6
+    X = np.zeros((1, 128), np.float32)
+    X[0, :8] = [6, -4, 3, 1.5, 1, 0.5, 0, -6]
+    X[0, 32] = 0.75
+    X[0, 33] = -0.0625  # 0.5 after scaling
+    X[0, 96] = 1000.0
+    X[0, 97] = 64.0     # 0.5 after scaling
+    q, s = fp8.quantize_rows_mxfp4(X)
+    assert list(s[0]) == [127, 124, 0, 134]
+    back = fp8.mxfp4_decode(q, s)[0]
+    assert list(back[:8]) == [6, -4, 3, 1.5, 1, 0.5, 0, -6]
+    assert back[32] == 0.75 and back[33] == -0.0625
+    assert back[96] == 768.0 and back[97] == 64.0
+    assert np.all(back[64:96] == 0)
+    # packing: element 0 in the low nibble of byte 0
+    assert q[0, 0] & 15 == 7 and q[0, 0] >> 4 == 14  # 6 -> 7, -4 -> 8|6
+
+
+def test_mxfp4_error_bound():
+    """Every element is within half an E2M1 step of its block's scaled grid:
+    |x - q| <= 2^e * (step at |x| / 2^e) / 2, at most 2^e for the top binade,
+    and saturated values are within 2 * 2^e of 6 * 2^e."""
+    rng = np.random.default_rng(2)
+    X = rng.standard_normal((20, 256)).astype(np.float32)
+    q, s = fp8.quantize_rows_mxfp4(X)
+    back = fp8.mxfp4_decode(q, s).reshape(20, 8, 32)
+    sc = np.ldexp(1.0, s.astype(np.int64) - 127)[:, :, None]
+    err = np.abs(back - X.reshape(20, 8, 32)) / sc
+    assert np.all(err <= 2.0 + 1e-12)
+    assert np.all(np.max(np.abs(back), axis=2) / sc[:, :, 0] >= 4.0)  # the block maximum uses the top binade
+
+
+def test_mxfp4_logprob_is_the_head_on_decoded_rows():
+    rng = np.random.default_rng(3)
+    H = rng.standard_normal((30, 128)).astype(np.float32)
+    W = (rng.standard_normal((200, 128)) * 0.05).astype(np.float32)
+    y = rng.integers(0, 200, 30)
+    Hq, hs = fp8.quantize_rows_fp8(H)
+    Wq, ws = fp8.quantize_rows_mxfp4(W)
+    lp, lse = fp8.lmhead_logprob_mxfp4(Hq, hs, Wq, ws, y)
+    Hd = np.array([[_value_by_definition(int(c)) for c in row] for row in Hq]) * hs[:, None]
+    Wd = np.zeros((200, 128))
+    for r in range(200):
+        for k in range(128):
+            nib = (Wq[r, k // 2] >> (4 * (k % 2))) & 15
+            Wd[r, k] = fp8.e2m1_decode(nib) * 2.0 ** (int(ws[r, k // 32]) - 127)
+    lp2, lse2 = oracle.lmhead_logprob(Hd, Wd, y)
+    assert np.allclose(lp, lp2, rtol=0, atol=1e-12) and np.allclose(lse, lse2, rtol=0, atol=1e-12)
