@@ -309,7 +309,30 @@ def fp8_leg(s, device, steps=5):
     gap = float((lp - lp_bf16).abs().max())
     log(f"[bench] fp8 head: step {ms:.2f} ms (H quantisation {ms_q:.2f} ms) -> {n / (ms * 1e-3):.0f} tokens/s, "
         f"logprob kernel {tf:.1f} TFLOP/s ({100 * tf / PEAK_FP8_TFLOPS:.1f}% of fp8 peak); max |lp_fp8 - lp_bf16| {gap:.3e}")
+    del Wq, ws
+    # MXFP4 weights (E2M1, E8M0 per 32 along d) against the same E4M3 token rows
+    W4, w4s = itl.quantize_rows_mxfp4(W)
+
+    def step4():
+        itl.quantize_rows_fp8(H, Xq=Hq, scale=hs)
+        itl.lmhead_logprob_mxfp4(Hq, hs, W4, w4s, y, logprob=lp, workspace=wsp, want_lse=False)
+
+    step4()
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(steps):
+        step4()
+    b.record()
+    torch.cuda.synchronize()
+    ms4 = a.elapsed_time(b) / steps
+    tf4 = 2.0 * d * V * n / ((ms4 - ms_q) * 1e-3) / 1e12
+    gap4 = float((lp - lp_bf16).abs().max())
+    log(f"[bench] mxfp4 head: step {ms4:.2f} ms -> {n / (ms4 * 1e-3):.0f} tokens/s, logprob kernel {tf4:.1f} "
+        f"TFLOP/s ({100 * tf4 / PEAK_FP8_TFLOPS:.1f}% of the fp8 peak); max |lp_mxfp4 - lp_bf16| {gap4:.3e}")
     return {
+        "mxfp4": {"ms_per_step": ms4, "value": n / (ms4 * 1e-3), "tflops_logprob_kernel": tf4,
+                  "frac_fp8_peak": tf4 / PEAK_FP8_TFLOPS, "max_abs_lp_gap_to_bf16_head": gap4,
+                  "weights": "E2M1 codes + E8M0 scale per 32 along d; tokens E4M3 per-row"},
         "workload": "same tokens and head; W quantised once to E4M3 with per-row scales, H per step",
         "ms_per_step": ms,
         "ms_quantize_h": ms_q,

@@ -191,6 +191,33 @@ itl_status itl_lmhead_logprob_fp8(const uint8_t* Hq, const float* h_scale,
                                   const int32_t* tokens, float* logprob, float* lse,
                                   void* workspace, size_t workspace_bytes, void* stream);
 
+/* MXFP4 quantisation [FP8] (OCP Microscaling: blocks of 32 consecutive
+ * values of a row share an E8M0 power-of-two scale 2^e, e = floor(log2
+ * amax) - 2 clamped to [-127, 127] (-127 for an all-zero block); elements are
+ * E2M1 codes of x / 2^e, round to nearest even, saturating at +-6, two per
+ * byte (even element in the low nibble)). X [n_rows, d] bf16 or fp32, d a
+ * multiple of 128 (ITL_ERR_UNSUPPORTED otherwise); Xq uint8 [n_rows, d / 2]
+ * (16-byte aligned); scale_codes uint8 [n_rows, d / 32] holding e + 127.
+ * Codes and scales are a fixed function of the input bits. X must be
+ * finite. */
+itl_status itl_quantize_rows_mxfp4(const void* X, itl_dtype dtype, int64_t n_rows, int64_t d,
+                                   uint8_t* Xq, uint8_t* scale_codes, void* stream);
+
+/* Sampled-token logprob from an MXFP4 head [FP8][RZ][BC]: Wq4 / w_scale_codes
+ * as written by itl_quantize_rows_mxfp4 (vocab rows), Hq / h_scale E4M3
+ * token rows as written by itl_quantize_rows_fp8, on the FP4 x FP8 matrix
+ * cores (v_mfma_scale_f32_32x32x64_f8f6f4 applies the W block scales):
+ *   z[t, v] = acc[t, v] * h_scale[t],
+ *   acc[t, v] = sum_k e2m1(W)[v, k] 2^(e[v, k / 32]) e4m3(Hq[t, k]) (fp32)
+ * then as itl_lmhead_logprob_fp8 (same slices, fold, combine and
+ * determinism). d a multiple of 128; Hq, Wq4 16-byte aligned; workspace >=
+ * itl_lmhead_logprob_workspace_bytes(n_tok, vocab), 256-byte aligned. */
+itl_status itl_lmhead_logprob_mxfp4(const uint8_t* Hq, const float* h_scale,
+                                    const uint8_t* Wq4, const uint8_t* w_scale_codes,
+                                    int64_t n_tok, int64_t d, int64_t vocab,
+                                    const int32_t* tokens, float* logprob, float* lse,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
 /* Statistics written by itl_mismatch_stats (fp64, indices into `stats`). */
 typedef enum itl_stat {
   ITL_STAT_N_TOK = 0,

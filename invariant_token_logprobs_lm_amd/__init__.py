@@ -16,6 +16,8 @@ Entry points (same names as the C ABI without the ``itl_`` prefix):
 * ``mismatch_stats(logprob, rollout_logprob, same_weights_logprob=None) -> stats``
 * ``quantize_rows_fp8(X) -> (Xq, scale)``,
   ``lmhead_logprob_fp8(Hq, h_scale, Wq, w_scale, tokens) -> (logprob, lse)``
+* ``quantize_rows_mxfp4(X) -> (Xq4, scale_codes)``,
+  ``lmhead_logprob_mxfp4(Hq, h_scale, Wq4, w_scale_codes, tokens) -> (logprob, lse)``
 * ``check_inputs(tokens, vocab, resp_offsets=None)``, ``build_info()``
 """
 
@@ -67,6 +69,10 @@ def _load():
                                                  _c_void_p]),
         "itl_lmhead_logprob_fp8": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i64, _i64,
                                                   _c_void_p, _c_void_p, _c_void_p, _c_void_p, _size, _c_void_p]),
+        "itl_quantize_rows_mxfp4": (ctypes.c_int, [_c_void_p, ctypes.c_int, _i64, _i64, _c_void_p, _c_void_p,
+                                                   _c_void_p]),
+        "itl_lmhead_logprob_mxfp4": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i64, _i64,
+                                                    _c_void_p, _c_void_p, _c_void_p, _c_void_p, _size, _c_void_p]),
         "itl_mismatch_stats_workspace_bytes": (_size, [_i64]),
         "itl_mismatch_stats": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _i64, _c_void_p, _c_void_p, _size,
                                               _c_void_p]),
@@ -93,6 +99,8 @@ EXPORTS = (
     "itl_reinforce_zero_backward",
     "itl_quantize_rows_fp8",
     "itl_lmhead_logprob_fp8",
+    "itl_quantize_rows_mxfp4",
+    "itl_lmhead_logprob_mxfp4",
     "itl_mismatch_stats_workspace_bytes",
     "itl_mismatch_stats",
     "itl_check_inputs",
@@ -283,6 +291,53 @@ def lmhead_logprob_fp8(Hq, h_scale, Wq, w_scale, tokens, *, logprob=None, lse=No
     _check(lib.itl_lmhead_logprob_fp8(_ptr(Hq), _ptr(h_scale), _ptr(Wq), _ptr(w_scale), n_tok, d, vocab,
                                       _ptr(tokens), _ptr(logprob), _ptr(lse), _ptr(workspace), workspace.numel(),
                                       _stream(dev)))
+    return logprob, lse
+
+
+def quantize_rows_mxfp4(X, *, Xq=None, scale_codes=None):
+    """MXFP4 of a bf16 or fp32 matrix [n, d] (d a multiple of 128): packed
+    E2M1 codes uint8 [n, d / 2] and E8M0 scale codes uint8 [n, d / 32]."""
+    _need(X, "X", tuple(_HEAD_DTYPES), ndim=2)
+    n, d = X.shape
+    if Xq is None:
+        Xq = torch.empty((n, d // 2), dtype=torch.uint8, device=X.device)
+    if scale_codes is None:
+        scale_codes = torch.empty((n, d // 32), dtype=torch.uint8, device=X.device)
+    _need(Xq, "Xq", (torch.uint8,), device=X.device, ndim=2)
+    _need(scale_codes, "scale_codes", (torch.uint8,), device=X.device, ndim=2)
+    if tuple(Xq.shape) != (n, d // 2) or tuple(scale_codes.shape) != (n, d // 32):
+        raise ValueError("Xq must be [n, d/2] and scale_codes [n, d/32]")
+    _check(lib.itl_quantize_rows_mxfp4(_ptr(X), _HEAD_DTYPES[X.dtype], n, d, _ptr(Xq), _ptr(scale_codes),
+                                       _stream(X.device)))
+    return Xq, scale_codes
+
+
+def lmhead_logprob_mxfp4(Hq, h_scale, Wq4, w_scale_codes, tokens, *, logprob=None, lse=None, workspace=None,
+                         want_lse=True):
+    """Sampled-token logprob and lse from an MXFP4 head against E4M3 token
+    rows (quantize_rows_mxfp4 / quantize_rows_fp8)."""
+    _need(Hq, "Hq", (torch.uint8,), ndim=2)
+    dev = Hq.device
+    _need(h_scale, "h_scale", (torch.float32,), device=dev, ndim=1)
+    _need(Wq4, "Wq4", (torch.uint8,), device=dev, ndim=2)
+    _need(w_scale_codes, "w_scale_codes", (torch.uint8,), device=dev, ndim=2)
+    _need(tokens, "tokens", (torch.int32,), device=dev, ndim=1)
+    n_tok, d = Hq.shape
+    vocab = Wq4.shape[0]
+    if (Wq4.shape[1] * 2 != d or tuple(w_scale_codes.shape) != (vocab, d // 32) or h_scale.shape[0] != n_tok
+            or tokens.shape[0] != n_tok):
+        raise ValueError("shape mismatch between Hq, h_scale, Wq4, w_scale_codes and tokens")
+    if logprob is None:
+        logprob = torch.empty(n_tok, dtype=torch.float32, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty(n_tok, dtype=torch.float32, device=dev)
+    need = lmhead_workspace_bytes(n_tok, vocab)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", (torch.uint8,), device=dev)
+    _check(lib.itl_lmhead_logprob_mxfp4(_ptr(Hq), _ptr(h_scale), _ptr(Wq4), _ptr(w_scale_codes), n_tok, d, vocab,
+                                        _ptr(tokens), _ptr(logprob), _ptr(lse), _ptr(workspace), workspace.numel(),
+                                        _stream(dev)))
     return logprob, lse
 
 

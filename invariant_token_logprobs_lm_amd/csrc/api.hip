@@ -164,6 +164,48 @@ itl_status itl_lmhead_logprob_fp8(const uint8_t* Hq, const float* h_scale, const
   return e == hipSuccess ? ITL_OK : hip_fail(e, "itl_lmhead_logprob_fp8");
 }
 
+itl_status itl_quantize_rows_mxfp4(const void* X, itl_dtype dtype, int64_t n_rows, int64_t d, uint8_t* Xq,
+                                   uint8_t* scale_codes, void* stream) {
+  g_last_error.clear();
+  if (n_rows < 0 || d <= 0) return fail(ITL_ERR_INVALID_ARG, "n_rows must be >= 0 and d > 0");
+  if (dtype != ITL_BF16 && dtype != ITL_F32) return fail(ITL_ERR_UNSUPPORTED, "dtype must be ITL_BF16 or ITL_F32");
+  if (d % kFp8DMultiple != 0) return fail(ITL_ERR_UNSUPPORTED, "d must be a multiple of 128");
+  if (n_rows * (d / 32) > (int64_t)INT32_MAX * 256) return fail(ITL_ERR_UNSUPPORTED, "too many rows");
+  if (n_rows == 0) return ITL_OK;
+  if (!X || !Xq || !scale_codes) return fail(ITL_ERR_INVALID_ARG, "null X, Xq or scale_codes");
+  if ((reinterpret_cast<uintptr_t>(Xq) & 15) != 0) return fail(ITL_ERR_INVALID_ARG, "Xq must be 16-byte aligned");
+  hipError_t e = itl::launch_quantize_rows_mxfp4(X, (int)dtype, n_rows, (int)d, Xq, scale_codes,
+                                                 static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ITL_OK : hip_fail(e, "itl_quantize_rows_mxfp4");
+}
+
+itl_status itl_lmhead_logprob_mxfp4(const uint8_t* Hq, const float* h_scale, const uint8_t* Wq4,
+                                    const uint8_t* w_scale_codes, int64_t n_tok, int64_t d, int64_t vocab,
+                                    const int32_t* tokens, float* logprob, float* lse, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  if (n_tok < 0 || d <= 0 || vocab <= 0) return fail(ITL_ERR_INVALID_ARG, "n_tok must be >= 0, d and vocab > 0");
+  if (d % kFp8DMultiple != 0) return fail(ITL_ERR_UNSUPPORTED, "d must be a multiple of 128");
+  if (n_tok > kMaxTok) return fail(ITL_ERR_UNSUPPORTED, "n_tok too large for one call");
+  if (vocab > kMaxVocab) return fail(ITL_ERR_UNSUPPORTED, "vocab too large");
+  if (d * (int64_t)itl::kBT >= ((int64_t)1 << 31)) return fail(ITL_ERR_UNSUPPORTED, "d too large");
+  const int64_t grid = itl::ceil_div(n_tok, itl::kBT) * itl::n_slice_groups(n_tok, vocab);
+  if (grid > INT32_MAX) return fail(ITL_ERR_UNSUPPORTED, "problem too large for one launch");
+  if (n_tok == 0) return ITL_OK;
+  if (!Hq || !h_scale || !Wq4 || !w_scale_codes || !tokens || !logprob)
+    return fail(ITL_ERR_INVALID_ARG, "null Hq, h_scale, Wq4, w_scale_codes, tokens or logprob");
+  if (((reinterpret_cast<uintptr_t>(Hq) | reinterpret_cast<uintptr_t>(Wq4)) & 15) != 0)
+    return fail(ITL_ERR_INVALID_ARG, "Hq and Wq4 must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(w_scale_codes) & 3) != 0)
+    return fail(ITL_ERR_INVALID_ARG, "w_scale_codes must be 4-byte aligned");
+  if (!workspace || workspace_bytes < itl::lmhead_workspace_bytes(n_tok, vocab))
+    return fail(ITL_ERR_WORKSPACE, "workspace missing or smaller than itl_lmhead_logprob_workspace_bytes()");
+  if (misaligned(workspace)) return fail(ITL_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  hipError_t e = itl::launch_lmhead_logprob_mxfp4(Hq, h_scale, Wq4, w_scale_codes, (int)n_tok, (int)d, (int)vocab,
+                                                  tokens, logprob, lse, workspace, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ITL_OK : hip_fail(e, "itl_lmhead_logprob_mxfp4");
+}
+
 size_t itl_mismatch_stats_workspace_bytes(int64_t n_tok) {
   if (n_tok < 0 || n_tok > INT32_MAX) return SIZE_MAX;
   return n_tok == 0 ? 0 : itl::mismatch_stats_workspace_bytes(n_tok);
@@ -226,7 +268,7 @@ const char* itl_build_info(void) {
     snprintf(buf, sizeof buf,
              "itl 0.2 arch=gfx950 threads=%d token_block=%d vocab_tile=%d k_step_bytes=%d w_slots=%d h_slots=%d "
              "max_slices=%d slices=balanced narrow_max_tokens=%d narrow_token_block=%d mfma_bf16=32x32x16 "
-             "mfma_f32=32x32x2 fp8=e4m3_row_scaled mfma_fp8=32x32x64 loss_threads=%d mean_threads=%d",
+             "mfma_f32=32x32x2 fp8=e4m3_row_scaled mfma_fp8=32x32x64 mxfp4=e2m1_e8m0_32 loss_threads=%d mean_threads=%d",
              itl::kThreads, itl::kBT, itl::kBV, itl::kStepBytes, itl::kWSlots, itl::kHSlots, itl::kMaxSlices,
              itl::kNarrowMaxTokens, itl::kNarrowBRows, itl::kLossThreads, itl::kMeanThreads);
     return std::string(buf);

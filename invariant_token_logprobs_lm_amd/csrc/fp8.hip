@@ -154,6 +154,127 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_fp8_partial_kernel(
     if (c[bn].found) zy_out[t0 + wt * 128 + bn * 32 + col] = c[bn].zy;
 }
 
+// ---- MXFP4 weights ("FP8 and MXFP4 weights", same section) ----
+// OCP MX: blocks of 32 consecutive values along d share a power-of-two scale
+// 2^e, e = floor(log2 amax) - 2 clamped to [-127, 127] (-127 for an all-zero
+// block), stored as the E8M0 byte e + 127; elements are E2M1 (values 0, 0.5,
+// 1, 1.5, 2, 3, 4, 6) of x / 2^e, round to nearest even, saturating at 6,
+// packed two per byte (even element in the low nibble).
+
+// E2M1 code of a finite float32, round to nearest even, saturating.
+__device__ __forceinline__ uint32_t e2m1_rne(float x) {
+  const uint32_t sign = (__float_as_uint(x) >> 28) & 8u;
+  const float a = fabsf(x);
+  if (a < 1.0f) return sign | (uint32_t)rintf(a * 2.0f);  // 0, 0.5 or (rounded up) 1.0 = code 2
+  int e = (int)((__float_as_uint(a) >> 23) & 0xffu) - 127;
+  float r = rintf(ldexpf(a, 1 - e));  // 1.m x 2, in [2, 4]
+  if (r == 4.0f) {
+    e += 1;
+    r = 2.0f;
+  }
+  if (e > 2 || (e == 2 && r > 3.0f)) return sign | 7u;
+  return sign | ((uint32_t)(e + 1) << 1) | ((uint32_t)r - 2u);
+}
+
+// One lane per 32-value block: amax, the block exponent, 32 codes packed
+// into 16 bytes, one scale byte.
+template <int kDtype>
+__global__ __launch_bounds__(256) void quantize_rows_mxfp4_kernel(const void* __restrict__ X, long long n_rows, int d,
+                                                                  uint8_t* __restrict__ Xq, uint8_t* __restrict__ sc) {
+  const long long nb = (long long)n_rows * (d / 32);
+  const long long blk = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (blk >= nb) return;
+  const size_t base = (size_t)blk * 32;  // rows are whole blocks: block b of the matrix starts at element 32 b
+  float v[32];
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    v[i] = load_elem<kDtype>(X, base + i);
+    amax = fmaxf(amax, fabsf(v[i]));
+  }
+  int e = -127;
+  if (amax > 0.0f) {
+    const int fl = (int)((__float_as_uint(amax) >> 23) & 0xffu) - 127;  // floor(log2 amax); <= -127 when subnormal
+    e = fl - 2 < -127 ? -127 : (fl - 2 > 127 ? 127 : fl - 2);
+  }
+  uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 32; ++i) w[i >> 3] |= e2m1_rne(ldexpf(v[i], -e)) << (4 * (i & 7));
+  *reinterpret_cast<uint4*>(Xq + (size_t)blk * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+  sc[blk] = (uint8_t)(e + 127);
+}
+
+// The fp8 head's partial kernel with MXFP4 weights: the W block scales are
+// applied by the matrix cores; the epilogue scales by the token's scale.
+__global__ __launch_bounds__(kThreads, 1) void lmhead_mxfp4_partial_kernel(
+    const uint8_t* __restrict__ Hq, const float* __restrict__ h_scale, const uint8_t* __restrict__ Wq4,
+    const uint8_t* __restrict__ w_sc, const int32_t* __restrict__ tokens, int n_tok, int d, int vocab, int n_tb,
+    int n_slices, int group, float2* __restrict__ part, float* __restrict__ zy_out) {
+  __shared__ uint4 smem[kEngineSmemChunks];
+  const Lanes L = lanes();
+  const int wv = L.wv, wt = L.wt, half = L.half, col = L.col;
+  const int S = n_slices;
+  const WideWork work = wide_work(blockIdx.x, n_tb, S, group);
+  const int t0 = work.tb * kBT;
+  const int n_vt = (vocab + kBV - 1) / kBV;
+  const int slice_first = work.slice_first;
+  const int tile_begin = slice_tile(work.slice_first, n_vt, S);
+  const int tile_end = slice_tile(work.slice_end, n_vt, S);
+  const int w_row_bytes = d / 2, s_row_bytes = d / 32, h_row_bytes = d;
+  const int nks = d / 128;
+
+  Col c[4];
+  float hs[4];
+#pragma unroll
+  for (int bn = 0; bn < 4; ++bn) {
+    const int tok = t0 + wt * 128 + bn * 32 + col;
+    c[bn] = Col{tok < n_tok ? tokens[tok] : -1, -INFINITY, 0.0f, 0.0f, false};
+    hs[bn] = tok < n_tok ? h_scale[tok] : 0.0f;
+  }
+  auto w_rsrc = [&](int tile) {
+    const int v0 = tile * kBV;
+    return rsrc_words(Wq4 + (size_t)v0 * w_row_bytes, (uint32_t)min(kBV, vocab - v0) * w_row_bytes);
+  };
+  auto s_rsrc = [&](int tile) {
+    const int v0 = tile * kBV;
+    return rsrc_words(w_sc + (size_t)v0 * s_row_bytes, (uint32_t)min(kBV, vocab - v0) * s_row_bytes);
+  };
+  const int4v hr = rsrc_words(Hq + (size_t)t0 * h_row_bytes, (uint32_t)min(kBT, n_tok - t0) * h_row_bytes);
+
+  int slice = slice_first;
+  int slice_last_tile = slice_tile(slice + 1, n_vt, S) - 1;
+  auto epilogue = [&](int tile, floatx16 (&acc)[4][4]) {
+    const int vw = tile * kBV + wv * 128;
+    const bool partial = tile * kBV + kBV > vocab;
+    mfma_result_wait();
+#pragma unroll
+    for (int bn = 0; bn < 4; ++bn) {
+#pragma unroll
+      for (int bm = 0; bm < 4; ++bm) {
+        floatx16 z;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) z[i] = acc_read(acc[bm][bn], i) * hs[bn];
+        fold_values(c[bn], z, bm, vw, half, vocab, partial);
+      }
+    }
+    if (tile == slice_last_tile) {
+#pragma unroll
+      for (int bn = 0; bn < 4; ++bn) {
+        const int tok = t0 + wt * 128 + bn * 32 + col;
+        flush_slice(c[bn], tok, n_tok, half, ((size_t)slice * 2 + wv) * n_tok + tok, part);
+      }
+      ++slice;
+      slice_last_tile = slice_tile(slice + 1, n_vt, S) - 1;
+    }
+  };
+  run_tiles_mx4(smem, L, w_row_bytes, s_row_bytes, h_row_bytes, tile_begin, tile_end, nks, w_rsrc, s_rsrc, hr,
+                epilogue);
+
+#pragma unroll
+  for (int bn = 0; bn < 4; ++bn)
+    if (c[bn].found) zy_out[t0 + wt * 128 + bn * 32 + col] = c[bn].zy;
+}
+
 }  // namespace
 
 hipError_t launch_quantize_rows_fp8(const void* X, int dtype, long long n_rows, int d, uint8_t* Xq, float* scale,
@@ -177,6 +298,38 @@ hipError_t launch_lmhead_logprob_fp8(const uint8_t* Hq, const float* h_scale, co
                                        align256((size_t)2 * S * (size_t)n_tok * sizeof(float2)));
   const dim3 grid((unsigned)ntb * (unsigned)n_slice_groups(n_tok, vocab));
   hipLaunchKernelGGL(lmhead_fp8_partial_kernel, grid, dim3(kThreads), 0, stream, Hq, h_scale, Wq, w_scale, tokens,
+                     n_tok, d, vocab, ntb, S, G, part, zy);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_lse_combine(part, zy, n_tok, 2 * S, logprob, lse, stream);
+}
+
+}  // namespace itl
+
+namespace itl {
+
+hipError_t launch_quantize_rows_mxfp4(const void* X, int dtype, long long n_rows, int d, uint8_t* Xq, uint8_t* sc,
+                                      hipStream_t stream) {
+  const long long nb = n_rows * (d / 32);
+  const dim3 grid((unsigned)ceil_div(nb, 256));
+  if (dtype == 0)
+    hipLaunchKernelGGL(quantize_rows_mxfp4_kernel<0>, grid, dim3(256), 0, stream, X, n_rows, d, Xq, sc);
+  else
+    hipLaunchKernelGGL(quantize_rows_mxfp4_kernel<1>, grid, dim3(256), 0, stream, X, n_rows, d, Xq, sc);
+  return hipGetLastError();
+}
+
+hipError_t launch_lmhead_logprob_mxfp4(const uint8_t* Hq, const float* h_scale, const uint8_t* Wq4,
+                                       const uint8_t* w_sc, int n_tok, int d, int vocab, const int32_t* tokens,
+                                       float* logprob, float* lse, void* workspace, hipStream_t stream) {
+  const int S = n_slices(vocab);
+  const int G = slices_per_group(n_tok, vocab);
+  const int ntb = (int)ceil_div(n_tok, kBT);
+  float2* part = static_cast<float2*>(workspace);
+  float* zy = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                       align256((size_t)2 * S * (size_t)n_tok * sizeof(float2)));
+  const dim3 grid((unsigned)ntb * (unsigned)n_slice_groups(n_tok, vocab));
+  hipLaunchKernelGGL(lmhead_mxfp4_partial_kernel, grid, dim3(kThreads), 0, stream, Hq, h_scale, Wq4, w_sc, tokens,
                      n_tok, d, vocab, ntb, S, G, part, zy);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

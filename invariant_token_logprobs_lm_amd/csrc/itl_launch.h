@@ -46,6 +46,13 @@ hipError_t launch_lmhead_logprob_fp8(const uint8_t* Hq, const float* h_scale, co
                                      int n_tok, int d, int vocab, const int32_t* tokens, float* logprob, float* lse,
                                      void* workspace, hipStream_t stream);
 
+hipError_t launch_quantize_rows_mxfp4(const void* X, int dtype, long long n_rows, int d, uint8_t* Xq, uint8_t* sc,
+                                      hipStream_t stream);
+
+hipError_t launch_lmhead_logprob_mxfp4(const uint8_t* Hq, const float* h_scale, const uint8_t* Wq4,
+                                       const uint8_t* w_sc, int n_tok, int d, int vocab, const int32_t* tokens,
+                                       float* logprob, float* lse, void* workspace, hipStream_t stream);
+
 size_t mismatch_stats_workspace_bytes(long long n_tok);
 
 hipError_t launch_mismatch_stats(const float* lp, const float* lpr, const float* lps, long long n, double* stats,

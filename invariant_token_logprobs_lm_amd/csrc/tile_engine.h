@@ -628,4 +628,222 @@ __device__ __forceinline__ void run_tiles_f8(uint4* smem, const Lanes& L, int ro
   __syncthreads();
 }
 
+// MXFP4-weight variant (A = W in OCP MXFP4: E2M1 codes, two per byte, one
+// E8M0 scale per 32 values along K; B = H in E4M3), on
+// v_mfma_scale_f32_32x32x64_f8f6f4 with A in FP4 format and the A block
+// scales applied by the instruction. A K step is 128 values: 64 bytes of W
+// and 4 scale bytes per W row, 128 bytes of H per H row; two sub-steps of
+// 64. Lane half h of sub-step j carries W values 64 j + 32 h .. + 31 (one
+// 16-byte chunk, one MX block, the lane's scale byte) and the H values the
+// instruction pairs with them: 16-byte chunks 4 j + h and 4 j + 2 + h of
+// the H row segment (the FP4 operand's halves pair with the FP8 operand's
+// chunks that way: a measured property of the instruction).
+//
+// LDS: W slots of 256 rows x 64 bytes (chunk c of row r at c ^ ((r >> 1) & 3)
+// so that 8 consecutive rows at one chunk hit distinct 16-byte bank groups)
+// followed by the slot's 256 x 4 scale bytes; H slots as in run_tiles.
+constexpr int kMx4RowChunks = 4;                        // 64-byte W rows
+constexpr int kMx4WDataBytes = kBV * 64;                // 16 KiB
+constexpr int kMx4WSlotBytes = kMx4WDataBytes + kBV * 4;  // + 1 KiB of scales
+constexpr int kMx4HBase = kWSlots * kMx4WSlotBytes;     // H slots after the W slots
+constexpr int kMx4WDataLoads = kBV * 64 / 1024 / 4;     // wavefront-wide loads per wavefront per step (4)
+constexpr int kMx4WLoads = kMx4WDataLoads + 1;          // + one 4-byte-per-lane load of scales
+static_assert(kMx4HBase + kHSlots * kSlotBytes <= kEngineSmemChunks * 16, "LDS budget");
+static_assert(kMx4WSlotBytes % 16 == 0, "slot alignment");
+
+__device__ __forceinline__ int swz4(int r) { return (r >> 1) & 3; }
+
+// As dma16, 4 bytes per lane: lane i's dword lands at LDS address lds + 4 i.
+__device__ __forceinline__ void dma4(int4v rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
+  const int4v r = {__builtin_amdgcn_readfirstlane(rsrc[0]), __builtin_amdgcn_readfirstlane(rsrc[1]),
+                   __builtin_amdgcn_readfirstlane(rsrc[2]), __builtin_amdgcn_readfirstlane(rsrc[3])};
+  const uint32_t so = __builtin_amdgcn_readfirstlane(soff);
+  const uint32_t l = __builtin_amdgcn_readfirstlane(lds);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %4\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dword %1, %2, %3 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(r), "s"(so), "s"(l)
+      : "memory");
+}
+
+__device__ __forceinline__ void mma_mx4(floatx16& acc, const uint4& a, const Frag8& b, int scale_a) {
+  const intx8 av = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+  acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, __builtin_bit_cast(intx8, b), acc, 4, 0, 0, scale_a, 0,
+                                                        127);
+}
+__device__ __forceinline__ void mma_mx4_first(floatx16& acc, const uint4& a, const Frag8& b, int scale_a) {
+  const intx8 av = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+  acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, __builtin_bit_cast(intx8, b), floatx16{}, 4, 0, 0,
+                                                        scale_a, 0, 127);
+}
+
+// a_rsrc(t) / s_rsrc(t): W codes and W scale bytes of tile t (rows at
+// w_row_bytes and s_row_bytes apart); b_rsrc: the H block (rows at
+// h_row_bytes). nks K steps of 128 values.
+template <class ARsrc, class SRsrc, class Epi>
+__device__ __forceinline__ void run_tiles_mx4(uint4* smem, const Lanes& L, int w_row_bytes, int s_row_bytes,
+                                              int h_row_bytes, int tile_begin, int tile_end, int nks,
+                                              const ARsrc& a_rsrc, const SRsrc& s_rsrc, int4v b_rsrc, Epi&& epi) {
+  const int lane = L.lane, wave = L.wave, wv = L.wv, wt = L.wt, half = L.half, col = L.col;
+  const int lr = lane >> 3;
+  // H loads (as run_tiles): rows 64 wave + 8 j + lane / 8.
+  uint32_t hvoff[kDmaPerWave];
+#pragma unroll
+  for (int j = 0; j < kDmaPerWave; ++j)
+    hvoff[j] = (uint32_t)(wave * 64 + j * kDmaRows + lr) * (uint32_t)h_row_bytes + (((lane & 7) ^ lr ^ (j & 1)) * 16);
+  // W code loads: rows 64 wave + 16 j + lane / 4, logical chunk (lane % 4) ^ swz4(row).
+  uint32_t wvoff[kMx4WDataLoads];
+#pragma unroll
+  for (int j = 0; j < kMx4WDataLoads; ++j) {
+    const int row = wave * 64 + j * 16 + (lane >> 2);
+    wvoff[j] = (uint32_t)row * (uint32_t)w_row_bytes + (uint32_t)(((lane & 3) ^ swz4(row)) * 16);
+  }
+  // W scale loads: row 64 wave + lane, the step's 4 bytes.
+  const uint32_t svoff = (uint32_t)(wave * 64 + lane) * (uint32_t)s_row_bytes;
+  const uint32_t lds0 = (uint32_t)(size_t)((__attribute__((address_space(3))) uint4*)smem);
+  auto w_slot = [&](int slot) { return lds0 + (uint32_t)slot * kMx4WSlotBytes; };
+  auto h_slot = [&](int slot) { return lds0 + (uint32_t)kMx4HBase + (uint32_t)slot * kSlotBytes; };
+  const int4v hr = b_rsrc;
+
+  // Fragment offsets (uint4 units from a slot's base): A chunk 2 j + half of
+  // row 128 wv + 32 m + col; B chunks 4 j + half and 4 j + 2 + half of row
+  // 128 wt + 32 m + col; the scale dword of row 128 wv + 32 m + col.
+  int a_off[2], b_off[2][2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int ra = wv * 128 + col;
+    a_off[j] = ra * kMx4RowChunks + ((2 * j + half) ^ swz4(ra));
+#pragma unroll
+    for (int p = 0; p < 2; ++p) b_off[j][p] = (wt * 128 + col) * kRowChunks + ((4 * j + 2 * p + half) ^ swz(col));
+  }
+  // swz4 of rows 128 wv + 32 m + col equals swz4(col + 32 m + 128 wv) = swz4(col)
+  // only when 32 m + 128 wv keeps bits 1-2: it does (multiples of 32).
+
+  int w_tile = tile_begin, w_ks = 0;
+  int h_ks = 0;
+  int w_slot_next = 0, h_slot_next = 0;
+  auto next_w = [&]() {
+    if (++w_ks == nks) {
+      w_ks = 0;
+      w_tile = min(w_tile + 1, tile_end - 1);
+    }
+    w_slot_next = w_slot_next == kWSlots - 1 ? 0 : w_slot_next + 1;
+  };
+  auto next_h = [&]() {
+    h_ks = h_ks + 1 == nks ? 0 : h_ks + 1;
+    h_slot_next ^= 1;
+  };
+  auto load_w = [&](int slot) {  // W(w_tile, w_ks): codes then scales
+    const int4v ar = a_rsrc(w_tile);
+    const int4v sr = s_rsrc(w_tile);
+    const uint32_t base = w_slot(slot) + (uint32_t)wave * 64 * 64;
+#pragma unroll
+    for (int j = 0; j < kMx4WDataLoads; ++j) dma16(ar, wvoff[j], (uint32_t)w_ks * 64, base + j * 1024);
+    dma4(sr, svoff, (uint32_t)w_ks * 4, w_slot(slot) + kMx4WDataBytes + (uint32_t)wave * 256);
+  };
+  auto load_h = [&](int slot) {
+    const uint32_t base = h_slot(slot) + (uint32_t)wave * 64 * kStepBytes;
+#pragma unroll
+    for (int j = 0; j < kDmaPerWave; ++j) dma16(hr, hvoff[j], (uint32_t)h_ks * kStepBytes, base + j * 1024);
+  };
+
+  // One sub-step: MFMA q (q = 4 bm + bn) with A[bm] (scale byte of sub-step
+  // sj from SC[bm]), B[bn]; the 12 reads of the next sub-step (A0 B0 B1 B2
+  // B3 A1 A2 A3, B in two halves) from slots (wsl, hsl), sub-step rj, one
+  // per MFMA (kFront: in the first 12 MFMAs, the same), plus with kScales the
+  // 4 scale dwords of the next step into NSC, and with kDma the loads of
+  // H(g + 2) and W(g + 3), one per MFMA.
+  auto phase = [&](floatx16 (&acc)[4][4], const uint4 (&A)[4], const Frag8 (&B)[4], const uint32_t (&SC)[4], int sj,
+                   auto first, auto scales, auto dma, int wsl, int hsl, int rj, uint4 (&RA)[4], Frag8 (&RB)[4],
+                   uint32_t (&NSC)[4]) {
+    const uint4* sa = smem + (wsl * kMx4WSlotBytes) / 16;
+    const uint32_t* ss = reinterpret_cast<const uint32_t*>(smem) + (wsl * kMx4WSlotBytes + kMx4WDataBytes) / 4;
+    const uint4* sb = smem + (kMx4HBase + hsl * kSlotBytes) / 16;
+    auto read = [&](int r) {
+      if (r == 0) RA[0] = sa[a_off[rj]];
+      else if (r <= 8) {
+        const int f = (r - 1) >> 1, p = (r - 1) & 1;
+        (p ? RB[f].hi : RB[f].lo) = sb[b_off[rj][p] + f * 32 * kRowChunks];
+      } else RA[r - 8] = sa[a_off[rj] + (r - 8) * 32 * kMx4RowChunks];
+    };
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int sa_byte = (int)((SC[q >> 2] >> (8 * (2 * sj + half))) & 0xffu);
+      if constexpr (decltype(first)::value) mma_mx4_first(acc[q >> 2][q & 3], A[q >> 2], B[q & 3], sa_byte);
+      else mma_mx4(acc[q >> 2][q & 3], A[q >> 2], B[q & 3], sa_byte);
+      if (q < 12) read(q);
+      if constexpr (decltype(scales)::value) {
+        if (q >= 12) NSC[q - 12] = ss[wv * 128 + (q - 12) * 32 + col];
+      }
+      if constexpr (decltype(dma)::value) {
+        if (q < 8) {
+          dma16(hr, hvoff[q], (uint32_t)h_ks * kStepBytes, h_slot(h_slot_next) + (uint32_t)wave * 64 * kStepBytes + q * 1024);
+        } else if (q < 8 + kMx4WDataLoads) {
+          const int j = q - 8;
+          dma16(a_rsrc(w_tile), wvoff[j], (uint32_t)w_ks * 64, w_slot(w_slot_next) + (uint32_t)wave * 64 * 64 + j * 1024);
+        } else if (q == 8 + kMx4WDataLoads) {
+          dma4(s_rsrc(w_tile), svoff, (uint32_t)w_ks * 4, w_slot(w_slot_next) + kMx4WDataBytes + (uint32_t)wave * 256);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (decltype(dma)::value) {
+      next_h();
+      next_w();
+    }
+  };
+
+  using T = std::true_type;
+  using F = std::false_type;
+  load_w(0);
+  load_h(0);
+  next_w();
+  next_h();
+  load_w(1);
+  next_w();
+  wait_and_barrier<kMx4WLoads>();  // W(0), H(0) landed
+  load_h(h_slot_next);
+  load_w(w_slot_next);
+  next_h();
+  next_w();
+  uint4 xa[4], ya[4];
+  Frag8 xb[4], yb[4];
+  uint32_t sc[4], nsc[4];
+  {
+    const uint4* sa = smem;
+    const uint32_t* ss = reinterpret_cast<const uint32_t*>(smem) + kMx4WDataBytes / 4;
+    const uint4* sb = smem + kMx4HBase / 16;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      xa[m] = sa[a_off[0] + m * 32 * kMx4RowChunks];
+      xb[m].lo = sb[b_off[0][0] + m * 32 * kRowChunks];
+      xb[m].hi = sb[b_off[0][1] + m * 32 * kRowChunks];
+      sc[m] = ss[wv * 128 + m * 32 + col];
+    }
+  }
+  int wslot = 0, hslot = 0;
+  auto k_step = [&](floatx16 (&acc)[4][4], auto first) {
+    phase(acc, xa, xb, sc, 0, first, F{}, F{}, wslot, hslot, 1, ya, yb, nsc);
+    wait_and_barrier<kMx4WLoads>();  // W(g + 1), H(g + 1) landed; W(g + 2) may still be in flight
+    wslot = wslot == kWSlots - 1 ? 0 : wslot + 1;
+    hslot ^= 1;
+    phase(acc, ya, yb, sc, 1, F{}, T{}, T{}, wslot, hslot, 0, xa, xb, nsc);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) sc[m] = nsc[m];
+  };
+  for (int tile = tile_begin; tile < tile_end; ++tile) {
+    floatx16 acc[4][4];
+    k_step(acc, T{});
+    for (int ks = 1; ks < nks; ++ks) k_step(acc, F{});
+    epi(tile, acc);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+}
+
 }  // namespace itl

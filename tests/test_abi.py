@@ -210,3 +210,18 @@ def test_fp8_validation(lib):
     assert f(*args(wsb=16)) == WORKSPACE
     assert f(*args(ws=255)) == WORKSPACE
     assert f(*args(n=0, Hq=0, Wq=0)) == OK
+
+
+def test_mxfp4_validation(lib):
+    v = ctypes.c_void_p
+    q = lib.itl_quantize_rows_mxfp4
+    assert q(v(1), 0, 4, 96, v(16), v(4), None) == UNSUPPORTED
+    assert q(v(1), 0, 4, 128, v(8), v(4), None) == INVALID   # Xq must be 16-byte aligned
+    assert q(None, 0, 0, 128, None, None, None) == OK
+    f = lib.itl_lmhead_logprob_mxfp4
+    args = lambda **k: [v(16), v(4), v(k.get("Wq", 16)), v(k.get("sc", 4)), k.get("n", 4), k.get("d", 128), 10,
+                        v(4), v(4), None, v(256), 1 << 20, None]
+    assert f(*args(d=64)) == UNSUPPORTED
+    assert f(*args(Wq=8)) == INVALID
+    assert f(*args(sc=2)) == INVALID
+    assert f(*args(n=0)) == OK

@@ -148,3 +148,110 @@ def test_lmhead_fp8_full_size_head(cuda):
     say(f"[fp8 qwen3-4b-head] n_tok={lay.n_tok}: W codes bit-identical; sampled max|dlp|={e_lp:.3e}")
     assert e_lp <= TOL_LP
     assert float(lp.max()) <= 0.0
+
+
+# ---- MXFP4 weights ----
+
+@pytest.mark.parametrize("n,d,dtype_name,scale_pow", [
+    (37, 128, "bf16", 0), (64, 2560, "bf16", 0), (50, 384, "f32", -128),  # subnormal-range values
+    (50, 256, "f32", 100), (20, 128, "f32", -3)])
+def test_quantize_mxfp4_bit_exact(cuda, n, d, dtype_name, scale_pow):
+    import torch
+    from oracle import fp8
+
+    g = torch.Generator(device="cpu").manual_seed(n * 13 + d)
+    X = torch.randn(n, d, generator=g, dtype=torch.float64) * (2.0 ** scale_pow)
+    X[2] = 0.0
+    X[4, :32] = 0.0                 # one all-zero block
+    X[5, 32:64] = X[5, 32:64] * 1e-6
+    X = X.float()
+    dt = torch.bfloat16 if dtype_name == "bf16" else torch.float32
+    X = X.to(dt)
+    itl = _itl()
+    q, s = itl.quantize_rows_mxfp4(X.to(cuda))
+    q_o, s_o = fp8.quantize_rows_mxfp4(_host_f32(X))
+    assert np.array_equal(s.cpu().numpy(), s_o)
+    assert np.array_equal(q.cpu().numpy(), q_o)
+    say(f"[mxfp4 quantize] {n}x{d} {dtype_name} 2^{scale_pow}: codes and scales bit-identical")
+
+
+def _oracle_mxfp4_head(n_tok, d, vocab, seed, w_std=0.05):
+    import torch
+    from oracle import fp8
+
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    H = torch.randn(n_tok, d, generator=g).to(torch.bfloat16)
+    W = (torch.randn(vocab, d, generator=g) * w_std).to(torch.bfloat16)
+    y = torch.randint(0, vocab, (n_tok,), generator=g, dtype=torch.int32)
+    Hq, hs = fp8.quantize_rows_fp8(_host_f32(H))
+    Wq, ws = fp8.quantize_rows_mxfp4(_host_f32(W))
+    return Hq, hs, Wq, ws, y.numpy()
+
+
+@pytest.mark.parametrize("n_tok,d,vocab", [
+    (700, 256, 5000), (300, 128, 4096 + 37), (1, 128, 300), (513, 384, 8192 + 256), (5200, 128, 150 * 256 - 17)])
+def test_lmhead_mxfp4_parity(cuda, n_tok, d, vocab):
+    from oracle import fp8
+
+    Hq, hs, Wq, ws, y = _oracle_mxfp4_head(n_tok, d, vocab, seed=2 * n_tok + vocab)
+    lp_o, lse_o = fp8.lmhead_logprob_mxfp4(Hq, hs, Wq, ws, y)
+    itl = _itl()
+    Hq_d, hs_d, Wq_d, ws_d, y_d = _to_dev(cuda, Hq, hs, Wq, ws, y)
+    lp, lse = itl.lmhead_logprob_mxfp4(Hq_d, hs_d, Wq_d, ws_d, y_d)
+    e_lp = float(np.max(np.abs(lp.cpu().numpy() - lp_o)))
+    e_lse = float(np.max(np.abs(lse.cpu().numpy() - lse_o)))
+    say(f"[mxfp4 parity {n_tok}x{d}x{vocab}] max|dlp|={e_lp:.3e} max|dlse|={e_lse:.3e}")
+    assert e_lp <= TOL_LP and e_lse <= TOL_LP
+    assert float(lp.max()) <= 0.0
+
+
+def test_lmhead_mxfp4_invariance(cuda):
+    import torch
+
+    Hq, hs, Wq, ws, y = _oracle_mxfp4_head(600, 256, 3000, seed=9)
+    itl = _itl()
+    Hq_d, hs_d, Wq_d, ws_d, y_d = _to_dev(cuda, Hq, hs, Wq, ws, y)
+    lp, lse = itl.lmhead_logprob_mxfp4(Hq_d, hs_d, Wq_d, ws_d, y_d)
+    for lo, n in ((0, 1), (17, 5), (100, 64), (300, 257)):
+        a, b = itl.lmhead_logprob_mxfp4(Hq_d[lo:lo + n], hs_d[lo:lo + n], Wq_d, ws_d, y_d[lo:lo + n])
+        assert same_bits(a, lp[lo:lo + n]) and same_bits(b, lse[lo:lo + n]), (lo, n)
+    for pos in (0, 31, 32, 128, 255):
+        Hp, hp, yp = Hq_d[:256].clone(), hs_d[:256].clone(), y_d[:256].clone()
+        Hp[pos], hp[pos], yp[pos] = Hq_d[17], hs_d[17], y_d[17]
+        a, _ = itl.lmhead_logprob_mxfp4(Hp, hp, Wq_d, ws_d, yp)
+        assert same_bits(a[pos:pos + 1], lp[17:18]), pos
+    again = itl.lmhead_logprob_mxfp4(Hq_d, hs_d, Wq_d, ws_d, y_d)
+    torch.cuda.synchronize()
+    assert same_bits(again[0], lp) and same_bits(again[1], lse)
+
+
+def test_lmhead_mxfp4_full_size_head(cuda):
+    """The qwen3-4b head at full size with MXFP4 weights: every W code and
+    scale equal to the oracle's; sampled tokens within 1e-3."""
+    import torch
+    from oracle import fp8
+    from synth import WORKLOADS, draw_head, draw_layout, sample_tokens, token_subset
+
+    wl = WORKLOADS["qwen3-4b-head"]
+    lay = draw_layout(wl)
+    H, W = draw_head(wl, lay.n_tok, device=cuda)
+    y = sample_tokens(H, W, wl)
+    itl = _itl()
+    Wq, ws = itl.quantize_rows_mxfp4(W)
+    Hq, hs = itl.quantize_rows_fp8(H)
+    lp, lse = itl.lmhead_logprob_mxfp4(Hq, hs, Wq, ws, y)
+    Wq_h, ws_h = Wq.cpu().numpy(), ws.cpu().numpy()
+    Wf = W.float().cpu().numpy()
+    for r0 in range(0, wl.vocab, 16384):
+        q_o, s_o = fp8.quantize_rows_mxfp4(Wf[r0:r0 + 16384])
+        assert np.array_equal(Wq_h[r0:r0 + 16384], q_o) and np.array_equal(ws_h[r0:r0 + 16384], s_o), r0
+    del Wf
+    tok = token_subset(lay.n_tok, 32, seed=12)
+    Hs = H.index_select(0, torch.from_numpy(tok).to(cuda)).float().cpu().numpy()
+    hq_o, hs_o = fp8.quantize_rows_fp8(Hs)
+    assert np.array_equal(Hq.cpu().numpy()[tok], hq_o)
+    lp_o, _ = fp8.lmhead_logprob_mxfp4(hq_o, hs_o, Wq_h, ws_h, y.cpu().numpy()[tok])
+    e_lp = float(np.max(np.abs(lp.cpu().numpy()[tok] - lp_o)))
+    say(f"[mxfp4 qwen3-4b-head] n_tok={lay.n_tok}: W codes bit-identical; sampled max|dlp|={e_lp:.3e}")
+    assert e_lp <= TOL_LP
+    assert float(lp.max()) <= 0.0
