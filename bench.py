@@ -178,6 +178,8 @@ def decode_leg(wl, device, batch_sizes=(1, 8, 64, 128, 256), calls=20):
         torch.cuda.synchronize()
         return a.elapsed_time(b) / n
 
+    Wq8, ws8 = itl.quantize_rows_fp8(W)
+    Wq4, ws4 = itl.quantize_rows_mxfp4(W)
     rows = []
     ours_ref = itl.lmhead_logprob(H[:1], W, y[:1], want_lse=False)[0]
     base_ref = baseline(H[:1], y[:1])
@@ -189,6 +191,20 @@ def decode_leg(wl, device, batch_sizes=(1, 8, 64, 128, 256), calls=20):
         lp = torch.empty(M, dtype=torch.float32, device=device)
         ms_ours = timed(lambda: itl.lmhead_logprob(Hm, W, ym, logprob=lp, workspace=ws, want_lse=False), calls)
         ms_base = timed(lambda: baseline(Hm, ym), calls)
+        Hq = torch.empty((M, wl.d), dtype=torch.uint8, device=device)
+        hs = torch.empty(M, dtype=torch.float32, device=device)
+
+        def q8():
+            itl.quantize_rows_fp8(Hm, Xq=Hq, scale=hs)
+            itl.lmhead_logprob_fp8(Hq, hs, Wq8, ws8, ym, logprob=lp, workspace=ws, want_lse=False)
+
+        def q4():
+            itl.quantize_rows_fp8(Hm, Xq=Hq, scale=hs)
+            itl.lmhead_logprob_mxfp4(Hq, hs, Wq4, ws4, ym, logprob=lp, workspace=ws, want_lse=False)
+
+        ms_fp8 = timed(q8, calls)
+        ms_mx4 = timed(q4, calls)
+        itl.lmhead_logprob(Hm, W, ym, logprob=lp, workspace=ws, want_lse=False)
         lp_b = baseline(Hm, ym)
         torch.cuda.synchronize()
         ours_identical &= bool(torch.equal(lp[:1].view(torch.int32), ours_ref.view(torch.int32)))
@@ -197,9 +213,10 @@ def decode_leg(wl, device, batch_sizes=(1, 8, 64, 128, 256), calls=20):
         rows.append({"batch": M, "ms_invariant": ms_ours, "ms_baseline": ms_base,
                      "tokens_per_s_invariant": M / (ms_ours * 1e-3), "tokens_per_s_baseline": M / (ms_base * 1e-3),
                      "invariant_over_baseline": ms_base / ms_ours,
+                     "ms_invariant_fp8_weights": ms_fp8, "ms_invariant_mxfp4_weights": ms_mx4,
                      "max_abs_lp_gap_to_baseline": float((lp - lp_b).abs().max())})
         log(f"[bench] decode M={M}: invariant {ms_ours:.3f} ms, baseline {ms_base:.3f} ms "
-            f"(throughput ratio {ms_base / ms_ours:.3f})")
+            f"(throughput ratio {ms_base / ms_ours:.3f}); with FP8 weights {ms_fp8:.3f} ms, MXFP4 {ms_mx4:.3f} ms")
     return {
         "workload": f"{wl.key} decode-shaped calls (M sequences x 1 token), {calls} calls per point",
         "baseline": "torch.mm (hipBLASLt, bf16 logits) + log_softmax (fp32) + gather; not batch-invariant",

@@ -16,8 +16,10 @@
 //   z[t, v] = (acc[t, v] * w_scale[v]) * h_scale[t],
 //   acc[t, v] = sum_k E4M3(Hq[t, k]) E4M3(Wq[v, k]) (fp32, fixed K order)
 // then the same online log-sum-exp, slice partials and combine as the bf16
-// head (shared fold, lse_fold.h). One kernel serves every n_tok, so a
-// token's logprob does not depend on the batch.
+// head (shared fold, lse_fold.h). Calls of at most 64 tokens run narrow
+// kernels that perform, per token, the same matrix-core instructions on the
+// same fragments and the same fold, so a token's logprob does not depend on
+// the batch.
 
 #include "itl_launch.h"
 #include "lse_fold.h"
@@ -275,6 +277,68 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_mxfp4_partial_kernel(
     if (c[bn].found) zy_out[t0 + wt * 128 + bn * 32 + col] = c[bn].zy;
 }
 
+// Decode-shaped calls (at most kNarrowMaxTokens tokens) on the quantised
+// heads: 64-token blocks, one workgroup per (token block, slice), the narrow
+// engine. Lane l of wavefront (wv, wt) holds token t0 + 32 wt + (l mod 32)
+// against the same W rows, with the same MFMA fragments, scales and fold, as
+// in the wide kernels, so the partials and logprobs have the same bits.
+template <bool kMx4>
+__global__ __launch_bounds__(kThreads, 1) void lmhead_q_partial_narrow_kernel(
+    const uint8_t* __restrict__ Hq, const float* __restrict__ h_scale, const uint8_t* __restrict__ Wq,
+    const void* __restrict__ w_sc, const int32_t* __restrict__ tokens, int n_tok, int d, int vocab, int n_slices,
+    float2* __restrict__ part, float* __restrict__ zy_out) {
+  __shared__ uint4 smem[kEngineSmemChunks];
+  const Lanes L = lanes();
+  const int wv = L.wv, wt = L.wt, half = L.half, col = L.col;
+  const int S = n_slices;
+  const int slice = blockIdx.x % S;
+  const int t0 = (blockIdx.x / S) * kNarrowBRows;
+  const int n_vt = (vocab + kBV - 1) / kBV;
+  const int tile_begin = slice_tile(slice, n_vt, S);
+  const int tile_end = slice_tile(slice + 1, n_vt, S);
+  const int w_row_bytes = kMx4 ? d / 2 : d, s_row_bytes = d / 32, h_row_bytes = d;
+  const int nks = d / 128;
+  const int tok = t0 + wt * 32 + col;
+  Col c = Col{tok < n_tok ? tokens[tok] : -1, -INFINITY, 0.0f, 0.0f, false};
+  const float hs = tok < n_tok ? h_scale[tok] : 0.0f;
+  auto w_rsrc = [&](int tile) {
+    const int v0 = tile * kBV;
+    return rsrc_words(Wq + (size_t)v0 * w_row_bytes, (uint32_t)min(kBV, vocab - v0) * w_row_bytes);
+  };
+  auto s_rsrc = [&](int tile) {
+    const int v0 = tile * kBV;
+    return rsrc_words(static_cast<const uint8_t*>(w_sc) + (size_t)v0 * s_row_bytes,
+                      (uint32_t)min(kBV, vocab - v0) * s_row_bytes);
+  };
+  const int4v hr =
+      rsrc_words(Hq + (size_t)t0 * h_row_bytes, (uint32_t)min(kNarrowBRows, n_tok - t0) * h_row_bytes);
+  const __amdgpu_buffer_rsrc_t ws_rsrc = make_rsrc(w_sc, (uint32_t)vocab * 4u);  // fp8: per-row float scales
+  auto epilogue = [&](int tile, floatx16 (&acc)[4]) {
+    const int vw = tile * kBV + wv * 128;
+    const bool partial = tile * kBV + kBV > vocab;
+    mfma_result_wait();
+#pragma unroll
+    for (int bm = 0; bm < 4; ++bm) {
+      floatx16 z;
+      if constexpr (kMx4) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) z[i] = acc_read(acc[bm], i) * hs;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float w = buffer_load4(ws_rsrc, (uint32_t)(vw + bm * 32 + 8 * (i >> 2) + 4 * half + (i & 3)) * 4u);
+          z[i] = (acc_read(acc[bm], i) * w) * hs;
+        }
+      }
+      fold_values(c, z, bm, vw, half, vocab, partial);
+    }
+  };
+  run_tiles_narrow_q<kMx4>(smem, L, w_row_bytes, s_row_bytes, h_row_bytes, tile_begin, tile_end, nks, w_rsrc, s_rsrc,
+                           hr, epilogue);
+  flush_slice(c, tok, n_tok, half, ((size_t)slice * 2 + wv) * n_tok + tok, part);
+  if (c.found) zy_out[tok] = c.zy;
+}
+
 }  // namespace
 
 hipError_t launch_quantize_rows_fp8(const void* X, int dtype, long long n_rows, int d, uint8_t* Xq, float* scale,
@@ -296,9 +360,15 @@ hipError_t launch_lmhead_logprob_fp8(const uint8_t* Hq, const float* h_scale, co
   float2* part = static_cast<float2*>(workspace);
   float* zy = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                        align256((size_t)2 * S * (size_t)n_tok * sizeof(float2)));
-  const dim3 grid((unsigned)ntb * (unsigned)n_slice_groups(n_tok, vocab));
-  hipLaunchKernelGGL(lmhead_fp8_partial_kernel, grid, dim3(kThreads), 0, stream, Hq, h_scale, Wq, w_scale, tokens,
-                     n_tok, d, vocab, ntb, S, G, part, zy);
+  if (n_tok <= kNarrowMaxTokens) {
+    const dim3 grid((unsigned)ceil_div(n_tok, kNarrowBRows) * (unsigned)S);
+    hipLaunchKernelGGL(lmhead_q_partial_narrow_kernel<false>, grid, dim3(kThreads), 0, stream, Hq, h_scale, Wq,
+                       static_cast<const void*>(w_scale), tokens, n_tok, d, vocab, S, part, zy);
+  } else {
+    const dim3 grid((unsigned)ntb * (unsigned)n_slice_groups(n_tok, vocab));
+    hipLaunchKernelGGL(lmhead_fp8_partial_kernel, grid, dim3(kThreads), 0, stream, Hq, h_scale, Wq, w_scale, tokens,
+                       n_tok, d, vocab, ntb, S, G, part, zy);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_lse_combine(part, zy, n_tok, 2 * S, logprob, lse, stream);
@@ -328,9 +398,15 @@ hipError_t launch_lmhead_logprob_mxfp4(const uint8_t* Hq, const float* h_scale, 
   float2* part = static_cast<float2*>(workspace);
   float* zy = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                        align256((size_t)2 * S * (size_t)n_tok * sizeof(float2)));
-  const dim3 grid((unsigned)ntb * (unsigned)n_slice_groups(n_tok, vocab));
-  hipLaunchKernelGGL(lmhead_mxfp4_partial_kernel, grid, dim3(kThreads), 0, stream, Hq, h_scale, Wq4, w_sc, tokens,
-                     n_tok, d, vocab, ntb, S, G, part, zy);
+  if (n_tok <= kNarrowMaxTokens) {
+    const dim3 grid((unsigned)ceil_div(n_tok, kNarrowBRows) * (unsigned)S);
+    hipLaunchKernelGGL(lmhead_q_partial_narrow_kernel<true>, grid, dim3(kThreads), 0, stream, Hq, h_scale, Wq4,
+                       static_cast<const void*>(w_sc), tokens, n_tok, d, vocab, S, part, zy);
+  } else {
+    const dim3 grid((unsigned)ntb * (unsigned)n_slice_groups(n_tok, vocab));
+    hipLaunchKernelGGL(lmhead_mxfp4_partial_kernel, grid, dim3(kThreads), 0, stream, Hq, h_scale, Wq4, w_sc, tokens,
+                       n_tok, d, vocab, ntb, S, G, part, zy);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_lse_combine(part, zy, n_tok, 2 * S, logprob, lse, stream);

@@ -846,4 +846,134 @@ __device__ __forceinline__ void run_tiles_mx4(uint4* smem, const Lanes& L, int w
   __syncthreads();
 }
 
+// Narrow variants of run_tiles_f8 (kMx4 = false: E4M3 W) and run_tiles_mx4
+// (kMx4 = true: MXFP4 W) for decode-shaped calls: the same W tiles against
+// a 64-row block of E4M3 token rows, wavefront (wv, wt) = 128 W rows x 32
+// token rows. Every MFMA of an accumulator takes the same fragments (and
+// scale bytes), in the same order, as in the wide engine (same W slot
+// layout and swizzle, same H chunk choice, same sub-step order), so each
+// output element has the same bits. Both operands rotate through 4 slots,
+// loaded three K steps ahead; all of a step's fragments are read up front.
+template <bool kMx4, class ARsrc, class SRsrc, class Epi>
+__device__ __forceinline__ void run_tiles_narrow_q(uint4* smem, const Lanes& L, int w_row_bytes, int s_row_bytes,
+                                                   int h_row_bytes, int tile_begin, int tile_end, int nks,
+                                                   const ARsrc& a_rsrc, const SRsrc& s_rsrc, int4v b_rsrc,
+                                                   Epi&& epi) {
+  const int lane = L.lane, wave = L.wave, wv = L.wv, wt = L.wt, half = L.half, col = L.col;
+  const int lr = lane >> 3;
+  constexpr int kWSlotBytes = kMx4 ? kMx4WSlotBytes : kSlotBytes;
+  constexpr int kWLoads = kMx4 ? kMx4WDataLoads : kDmaPerWave;      // W code loads per wavefront per step
+  constexpr int kLoads = kWLoads + (kMx4 ? 1 : 0) + kNarrowBDmaPerWave;
+  constexpr int kHBase = kNarrowSlots * kWSlotBytes;
+  static_assert(kHBase + kNarrowSlots * kNarrowBSlotChunks * 16 <= kEngineSmemChunks * 16, "LDS budget");
+  uint32_t wvoff[kWLoads];
+#pragma unroll
+  for (int j = 0; j < kWLoads; ++j) {
+    if constexpr (kMx4) {
+      const int row = wave * 64 + j * 16 + (lane >> 2);
+      wvoff[j] = (uint32_t)row * (uint32_t)w_row_bytes + (uint32_t)(((lane & 3) ^ swz4(row)) * 16);
+    } else {
+      wvoff[j] = (uint32_t)(wave * 64 + j * kDmaRows + lr) * (uint32_t)w_row_bytes + (((lane & 7) ^ lr ^ (j & 1)) * 16);
+    }
+  }
+  const uint32_t svoff = (uint32_t)(wave * 64 + lane) * (uint32_t)s_row_bytes;
+  uint32_t hvoff[kNarrowBDmaPerWave];
+#pragma unroll
+  for (int j = 0; j < kNarrowBDmaPerWave; ++j)
+    hvoff[j] = (uint32_t)(wave * 16 + j * kDmaRows + lr) * (uint32_t)h_row_bytes + (((lane & 7) ^ lr ^ (j & 1)) * 16);
+  const uint32_t lds0 = (uint32_t)(size_t)((__attribute__((address_space(3))) uint4*)smem);
+  auto w_slot = [&](int slot) { return lds0 + (uint32_t)slot * kWSlotBytes; };
+  auto h_slot = [&](int slot) { return lds0 + (uint32_t)kHBase + (uint32_t)slot * kNarrowBSlotChunks * 16; };
+  constexpr uint32_t kWStepBytes = kMx4 ? 64 : kStepBytes;  // W bytes per row per K step
+  auto load_step = [&](int tile, int ks, int slot) {
+    const int4v ar = a_rsrc(tile);
+#pragma unroll
+    for (int j = 0; j < kNarrowBDmaPerWave; ++j)
+      dma16(b_rsrc, hvoff[j], (uint32_t)ks * kStepBytes, h_slot(slot) + (uint32_t)wave * 16 * kStepBytes + j * 1024);
+#pragma unroll
+    for (int j = 0; j < kWLoads; ++j)
+      dma16(ar, wvoff[j], (uint32_t)ks * kWStepBytes, w_slot(slot) + (uint32_t)wave * 64 * kWStepBytes + j * 1024);
+    if constexpr (kMx4) dma4(s_rsrc(tile), svoff, (uint32_t)ks * 4, w_slot(slot) + kMx4WDataBytes + (uint32_t)wave * 256);
+  };
+  int ld_tile = tile_begin, ld_ks = 0;
+  auto next_load = [&]() {
+    if (++ld_ks == nks) {
+      ld_ks = 0;
+      if (ld_tile + 1 < tile_end) ++ld_tile;
+      else ld_ks = nks - 1;
+    }
+  };
+#pragma unroll
+  for (int p = 0; p < kNarrowSlots - 1; ++p) {
+    load_step(ld_tile, ld_ks, p);
+    next_load();
+  }
+  // Fragment offsets (uint4 units from a slot's base), as in the wide engines.
+  int a_off[2][2], b_off[2][2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      if constexpr (kMx4) {
+        const int ra = wv * 128 + col;
+        a_off[j][p] = ra * kMx4RowChunks + ((2 * j + half) ^ swz4(ra));  // p unused: one chunk per fragment
+        b_off[j][p] = (wt * 32 + col) * kRowChunks + ((4 * j + 2 * p + half) ^ swz(col));
+      } else {
+        const int pc = (4 * j + 2 * half + p) ^ swz(col);
+        a_off[j][p] = (wv * 128 + col) * kRowChunks + pc;
+        b_off[j][p] = (wt * 32 + col) * kRowChunks + pc;
+      }
+    }
+  constexpr int kPending = (kNarrowSlots - 2) * kLoads;
+  constexpr int kARowChunks = kMx4 ? kMx4RowChunks : kRowChunks;
+  int slot = 0;
+  auto k_step = [&](floatx16 (&acc)[4], auto first) {
+    wait_and_barrier<kPending>();
+    load_step(ld_tile, ld_ks, slot == 0 ? kNarrowSlots - 1 : slot - 1);
+    next_load();
+    const uint4* sa = smem + (slot * kWSlotBytes) / 16;
+    const uint4* sb = smem + (kHBase + slot * kNarrowBSlotChunks * 16) / 16;
+    Frag8 A[2][4], B[2];
+    uint32_t SC[4];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        A[j][m].lo = sa[a_off[j][0] + m * 32 * kARowChunks];
+        if constexpr (!kMx4) A[j][m].hi = sa[a_off[j][1] + m * 32 * kARowChunks];
+      }
+      B[j].lo = sb[b_off[j][0]];
+      B[j].hi = sb[b_off[j][1]];
+    }
+    if constexpr (kMx4) {
+      const uint32_t* ss = reinterpret_cast<const uint32_t*>(smem) + (slot * kWSlotBytes + kMx4WDataBytes) / 4;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) SC[m] = ss[wv * 128 + m * 32 + col];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        if constexpr (kMx4) {
+          const int sbyte = (int)((SC[m] >> (8 * (2 * j + half))) & 0xffu);
+          if (decltype(first)::value && j == 0) mma_mx4_first(acc[m], A[j][m].lo, B[j], sbyte);
+          else mma_mx4(acc[m], A[j][m].lo, B[j], sbyte);
+        } else {
+          if (decltype(first)::value && j == 0) mma_f8_first(acc[m], A[j][m], B[j]);
+          else mma_f8(acc[m], A[j][m], B[j]);
+        }
+      }
+    slot = slot == kNarrowSlots - 1 ? 0 : slot + 1;
+  };
+  for (int tile = tile_begin; tile < tile_end; ++tile) {
+    floatx16 acc[4];
+    k_step(acc, std::true_type{});
+    for (int ks = 1; ks < nks; ++ks) k_step(acc, std::false_type{});
+    epi(tile, acc);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+}
+
 }  // namespace itl

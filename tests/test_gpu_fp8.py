@@ -74,7 +74,8 @@ def _to_dev(cuda, *arrays):
 @pytest.mark.parametrize("n_tok,d,vocab", [
     (700, 256, 5000),          # 3 token blocks (ragged), 20 tiles
     (300, 128, 4096 + 37),     # one K step; last tile of 37 rows (scale loads past the end)
-    (1, 128, 300),             # one token
+    (1, 128, 300),             # one token (narrow kernel)
+    (64, 256, 3000),           # a full narrow block
     (513, 384, 8192 + 256),    # d = 3 K steps
     (5200, 128, 150 * 256 - 17),  # 21 x 150 > 2048: several slices per workgroup
 ])
@@ -110,6 +111,12 @@ def test_lmhead_fp8_invariance(cuda):
         Hp[pos], hp[pos], yp[pos] = Hq_d[17], hs_d[17], y_d[17]
         a, _ = itl.lmhead_logprob_fp8(Hp, hp, Wq_d, ws_d, yp)
         assert same_bits(a[pos:pos + 1], lp[17:18]), pos
+    # narrow kernel (calls of at most 64 tokens): every row of a 64-token block
+    for pos in range(64):
+        Hp, hp, yp = Hq_d[:64].clone(), hs_d[:64].clone(), y_d[:64].clone()
+        Hp[pos], hp[pos], yp[pos] = Hq_d[17], hs_d[17], y_d[17]
+        a, _ = itl.lmhead_logprob_fp8(Hp, hp, Wq_d, ws_d, yp)
+        assert same_bits(a[pos:pos + 1], lp[17:18]), ("narrow", pos)
     again = itl.lmhead_logprob_fp8(Hq_d, hs_d, Wq_d, ws_d, y_d)
     torch.cuda.synchronize()
     assert same_bits(again[0], lp) and same_bits(again[1], lse)
@@ -189,7 +196,8 @@ def _oracle_mxfp4_head(n_tok, d, vocab, seed, w_std=0.05):
 
 
 @pytest.mark.parametrize("n_tok,d,vocab", [
-    (700, 256, 5000), (300, 128, 4096 + 37), (1, 128, 300), (513, 384, 8192 + 256), (5200, 128, 150 * 256 - 17)])
+    (700, 256, 5000), (300, 128, 4096 + 37), (1, 128, 300), (64, 256, 3000), (513, 384, 8192 + 256),
+    (5200, 128, 150 * 256 - 17)])
 def test_lmhead_mxfp4_parity(cuda, n_tok, d, vocab):
     from oracle import fp8
 
@@ -220,6 +228,12 @@ def test_lmhead_mxfp4_invariance(cuda):
         Hp[pos], hp[pos], yp[pos] = Hq_d[17], hs_d[17], y_d[17]
         a, _ = itl.lmhead_logprob_mxfp4(Hp, hp, Wq_d, ws_d, yp)
         assert same_bits(a[pos:pos + 1], lp[17:18]), pos
+    # narrow kernel (calls of at most 64 tokens): every row of a 64-token block
+    for pos in range(64):
+        Hp, hp, yp = Hq_d[:64].clone(), hs_d[:64].clone(), y_d[:64].clone()
+        Hp[pos], hp[pos], yp[pos] = Hq_d[17], hs_d[17], y_d[17]
+        a, _ = itl.lmhead_logprob_mxfp4(Hp, hp, Wq_d, ws_d, yp)
+        assert same_bits(a[pos:pos + 1], lp[17:18]), ("narrow", pos)
     again = itl.lmhead_logprob_mxfp4(Hq_d, hs_d, Wq_d, ws_d, y_d)
     torch.cuda.synchronize()
     assert same_bits(again[0], lp) and same_bits(again[1], lse)
