@@ -33,6 +33,11 @@ DEVICE_FLAGS = [
     "-fPIC",
     "-Wall",
     "-Wno-unused-function",
+    # Every rounding is the one the source writes: no a * b + c is fused
+    # unless the code asks for fmaf. Kernels that must give the same bits
+    # (wide and narrow, any batch) would otherwise depend on which products
+    # the compiler chose to fuse in each of them.
+    "-ffp-contract=off",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"),
     "-I", CSRC,

@@ -113,32 +113,58 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_fp8_partial_kernel(
     return rsrc_words(Wq + (size_t)v0 * row_bytes, (uint32_t)min(kBV, vocab - v0) * row_bytes);
   };
   const int4v hr = rsrc_words(Hq + (size_t)t0 * row_bytes, (uint32_t)min(kBT, n_tok - t0) * row_bytes);
-  // Row scales through a bounded buffer: rows past the vocabulary read 0.
-  const __amdgpu_buffer_rsrc_t ws_rsrc = make_rsrc(w_scale, (uint32_t)vocab * 4u);
+  // Row scales: lane l of wavefront (wv, wt) fetches the scales of rows
+  // vw + l and vw + 64 + l of each tile (vw = the wavefront's first row)
+  // into ws_lo, ws_hi, through a bounded buffer (rows past the vocabulary
+  // read 0). The loads are issued from inline assembly in the tile's last K
+  // step, before that step's 16 loads into LDS, and waited for with
+  // vmcnt(16) in the epilogue: a load the compiler can see would make it
+  // wait for every load in flight (vmcnt(0)) and stall on the next steps'
+  // operands at every tile.
+  const int4v ws_words = rsrc_words(w_scale, (uint32_t)vocab * 4u);
+  float ws_lo = 0.0f, ws_hi = 0.0f;
+  auto pre = [&](int tile) {
+    const uint32_t off = (uint32_t)(tile * kBV + wv * 128 + L.lane) * 4u;
+    const uint32_t off_hi = off + 256u;
+    const int4v r = {__builtin_amdgcn_readfirstlane(ws_words[0]), __builtin_amdgcn_readfirstlane(ws_words[1]),
+                     __builtin_amdgcn_readfirstlane(ws_words[2]), __builtin_amdgcn_readfirstlane(ws_words[3])};
+    asm volatile(
+        "buffer_load_dword %0, %2, %4, 0 offen\n\t"
+        "buffer_load_dword %1, %3, %4, 0 offen"
+        : "=&v"(ws_lo), "=&v"(ws_hi)
+        : "v"(off), "v"(off_hi), "s"(r)
+        : "memory");
+  };
 
   int slice = slice_first;
   int slice_last_tile = slice_tile(slice + 1, n_vt, S) - 1;
   auto epilogue = [&](int tile, floatx16 (&acc)[4][4]) {
     const int vw = tile * kBV + wv * 128;
-    const bool partial = tile * kBV + kBV > vocab;
+    asm volatile("s_waitcnt vmcnt(16)" : "+v"(ws_lo), "+v"(ws_hi)::"memory");
     mfma_result_wait();
+    auto fold_tile = [&](auto partial) {
 #pragma unroll
-    for (int bn = 0; bn < 4; ++bn) {
+      for (int bn = 0; bn < 4; ++bn) {
 #pragma unroll
-      for (int bm = 0; bm < 4; ++bm) {
-        // z = (acc * scale of the row) * scale of the token; the row scales
-        // of this lane's 16 rows (vw + 32 bm + 8 (i / 4) + 4 half + i % 4)
-        // come one range-checked load each: rows past the vocabulary read 0
-        // and are masked by the fold
-        floatx16 z;
+        for (int bm = 0; bm < 4; ++bm) {
+          // z = (acc * scale of the row) * scale of the token. Register i
+          // of this lane holds row 32 bm + 8 (i / 4) + 4 half + (i % 4) of
+          // the wavefront's 128: its scale sits in lane (row mod 64) of
+          // ws_lo (rows below 64) or of ws_hi.
+          const int src = __float_as_int(bm < 2 ? ws_lo : ws_hi);
+          floatx16 z;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float w = buffer_load4(ws_rsrc, (uint32_t)(vw + bm * 32 + 8 * (i >> 2) + 4 * half + (i & 3)) * 4u);
-          z[i] = (acc_read(acc[bm][bn], i) * w) * hs[bn];
+          for (int i = 0; i < 16; ++i) {
+            const float w = __int_as_float(
+                __builtin_amdgcn_ds_bpermute((32 * (bm & 1) + 8 * (i >> 2) + 4 * half + (i & 3)) * 4, src));
+            z[i] = (acc_read(acc[bm][bn], i) * w) * hs[bn];
+          }
+          fold_values(c[bn], z, bm, vw, half, vocab, partial);
         }
-        fold_values(c[bn], z, bm, vw, half, vocab, partial);
       }
-    }
+    };
+    if (tile * kBV + kBV > vocab) fold_tile(std::true_type{});
+    else fold_tile(std::false_type{});
     if (tile == slice_last_tile) {
 #pragma unroll
       for (int bn = 0; bn < 4; ++bn) {
@@ -149,7 +175,7 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_fp8_partial_kernel(
       slice_last_tile = slice_tile(slice + 1, n_vt, S) - 1;
     }
   };
-  run_tiles_f8(smem, L, row_bytes, tile_begin, tile_end, nks, w_rsrc, hr, epilogue);
+  run_tiles_f8(smem, L, row_bytes, tile_begin, tile_end, nks, w_rsrc, hr, epilogue, pre);
 
 #pragma unroll
   for (int bn = 0; bn < 4; ++bn)
@@ -247,18 +273,21 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_mxfp4_partial_kernel(
   int slice_last_tile = slice_tile(slice + 1, n_vt, S) - 1;
   auto epilogue = [&](int tile, floatx16 (&acc)[4][4]) {
     const int vw = tile * kBV + wv * 128;
-    const bool partial = tile * kBV + kBV > vocab;
     mfma_result_wait();
+    auto fold_tile = [&](auto partial) {
 #pragma unroll
-    for (int bn = 0; bn < 4; ++bn) {
+      for (int bn = 0; bn < 4; ++bn) {
 #pragma unroll
-      for (int bm = 0; bm < 4; ++bm) {
-        floatx16 z;
+        for (int bm = 0; bm < 4; ++bm) {
+          floatx16 z;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) z[i] = acc_read(acc[bm][bn], i) * hs[bn];
-        fold_values(c[bn], z, bm, vw, half, vocab, partial);
+          for (int i = 0; i < 16; ++i) z[i] = acc_read(acc[bm][bn], i) * hs[bn];
+          fold_values(c[bn], z, bm, vw, half, vocab, partial);
+        }
       }
-    }
+    };
+    if (tile * kBV + kBV > vocab) fold_tile(std::true_type{});
+    else fold_tile(std::false_type{});
     if (tile == slice_last_tile) {
 #pragma unroll
       for (int bn = 0; bn < 4; ++bn) {
@@ -315,23 +344,27 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_q_partial_narrow_kernel(
   const __amdgpu_buffer_rsrc_t ws_rsrc = make_rsrc(w_sc, (uint32_t)vocab * 4u);  // fp8: per-row float scales
   auto epilogue = [&](int tile, floatx16 (&acc)[4]) {
     const int vw = tile * kBV + wv * 128;
-    const bool partial = tile * kBV + kBV > vocab;
     mfma_result_wait();
+    auto fold_tile = [&](auto partial) {
 #pragma unroll
-    for (int bm = 0; bm < 4; ++bm) {
-      floatx16 z;
-      if constexpr (kMx4) {
+      for (int bm = 0; bm < 4; ++bm) {
+        floatx16 z;
+        if constexpr (kMx4) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) z[i] = acc_read(acc[bm], i) * hs;
-      } else {
+          for (int i = 0; i < 16; ++i) z[i] = acc_read(acc[bm], i) * hs;
+        } else {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float w = buffer_load4(ws_rsrc, (uint32_t)(vw + bm * 32 + 8 * (i >> 2) + 4 * half + (i & 3)) * 4u);
-          z[i] = (acc_read(acc[bm], i) * w) * hs;
+          for (int i = 0; i < 16; ++i) {
+            const float w =
+                buffer_load4(ws_rsrc, (uint32_t)(vw + bm * 32 + 8 * (i >> 2) + 4 * half + (i & 3)) * 4u);
+            z[i] = (acc_read(acc[bm], i) * w) * hs;
+          }
         }
+        fold_values(c, z, bm, vw, half, vocab, partial);
       }
-      fold_values(c, z, bm, vw, half, vocab, partial);
-    }
+    };
+    if (tile * kBV + kBV > vocab) fold_tile(std::true_type{});
+    else fold_tile(std::false_type{});
   };
   run_tiles_narrow_q<kMx4>(smem, L, w_row_bytes, s_row_bytes, h_row_bytes, tile_begin, tile_end, nks, w_rsrc, s_rsrc,
                            hr, epilogue);
@@ -360,7 +393,9 @@ hipError_t launch_lmhead_logprob_fp8(const uint8_t* Hq, const float* h_scale, co
   float2* part = static_cast<float2*>(workspace);
   float* zy = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                        align256((size_t)2 * S * (size_t)n_tok * sizeof(float2)));
-  if (n_tok <= kNarrowMaxTokens) {
+  // The wide kernel needs two K steps of 128 values (d >= 256); the narrow
+  // kernel gives the same bits and takes any number of token blocks.
+  if (n_tok <= kNarrowMaxTokens || d < 256) {
     const dim3 grid((unsigned)ceil_div(n_tok, kNarrowBRows) * (unsigned)S);
     hipLaunchKernelGGL(lmhead_q_partial_narrow_kernel<false>, grid, dim3(kThreads), 0, stream, Hq, h_scale, Wq,
                        static_cast<const void*>(w_scale), tokens, n_tok, d, vocab, S, part, zy);

@@ -81,12 +81,15 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_lse_partial_kernel(
   int slice_last_tile = slice_tile(slice + 1, n_vt, S) - 1;
   auto epilogue = [&](int tile, floatx16 (&acc)[4][4]) {
     const int vw = tile * kBV + wv * 128;
-    const bool partial = tile * kBV + kBV > vocab;  // only the vocabulary's last tile
     mfma_result_wait();
+    auto fold_tile = [&](auto partial) {
 #pragma unroll
-    for (int bn = 0; bn < 4; ++bn)
+      for (int bn = 0; bn < 4; ++bn)
 #pragma unroll
-      for (int bm = 0; bm < 4; ++bm) fold_block(c[bn], acc[bm][bn], bm, vw, half, vocab, partial);
+        for (int bm = 0; bm < 4; ++bm) fold_block(c[bn], acc[bm][bn], bm, vw, half, vocab, partial);
+    };
+    if (tile * kBV + kBV > vocab) fold_tile(std::true_type{});  // only the vocabulary's last tile
+    else fold_tile(std::false_type{});
     if (tile == slice_last_tile) {
 #pragma unroll
       for (int bn = 0; bn < 4; ++bn) {
@@ -135,10 +138,13 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_lse_partial_narrow_kernel(
   const int4v hr = rsrc_words(H + (size_t)t0 * row_bytes, (uint32_t)min(kNarrowBRows, n_tok - t0) * row_bytes);
   auto epilogue = [&](int tile, floatx16 (&acc)[4]) {
     const int vw = tile * kBV + wv * 128;
-    const bool partial = tile * kBV + kBV > vocab;
     mfma_result_wait();
+    auto fold_tile = [&](auto partial) {
 #pragma unroll
-    for (int bm = 0; bm < 4; ++bm) fold_block(c, acc[bm], bm, vw, half, vocab, partial);
+      for (int bm = 0; bm < 4; ++bm) fold_block(c, acc[bm], bm, vw, half, vocab, partial);
+    };
+    if (tile * kBV + kBV > vocab) fold_tile(std::true_type{});
+    else fold_tile(std::false_type{});
   };
   run_tiles_narrow<kDtype>(smem, L, row_bytes, tile_begin, tile_end, nks, w_rsrc, hr, epilogue);
   flush_slice(c, tok, n_tok, half, ((size_t)slice * 2 + wv) * n_tok + tok, part);

@@ -24,14 +24,18 @@ struct Col {
 // its row, without a branch. Every kernel folds with this one function, in
 // the same block order, so a token's state has the same bits whichever
 // kernel computed it.
-__device__ __forceinline__ void fold_values(Col& c, floatx16 z, int bm, int vw, int half, int vocab,
-                                            bool partial) {
+//
+// kPartial (a std::bool_constant): the block may hold rows past the
+// vocabulary, which are masked. Callers choose it once per tile, so that a
+// full tile's epilogue has no masking and no branches.
+template <class kPartial>
+__device__ __forceinline__ void fold_values(Col& c, floatx16 z, int bm, int vw, int half, int vocab, kPartial) {
   const int o = c.y - vw;  // sampled row relative to this wavefront's 128 rows
   // Register i of a lane holds row 32 bm + 8 (i / 4) + 4 half + (i % 4):
   // bits 0, 1, 3, 4 of the row pick i, bit 2 picks the lane half.
   const bool b0 = (o & 1) != 0, b1 = (o & 2) != 0, b2 = (o & 8) != 0, b3 = (o & 16) != 0;
   const bool here = (unsigned)o < 128u && ((o >> 2) & 1) == half && (o >> 5) == bm;
-  if (partial) {
+  if constexpr (kPartial::value) {
     const int lim = vocab - (vw + bm * 32 + 4 * half);  // rows at or past this offset do not exist
 #pragma unroll
     for (int i = 0; i < 16; ++i) z[i] = (8 * (i >> 2) + (i & 3) >= lim) ? -INFINITY : z[i];
@@ -50,11 +54,16 @@ __device__ __forceinline__ void fold_values(Col& c, floatx16 z, int bm, int vw, 
   // (z - m) is exactly 0 for the running maximum, so its term is exactly 1
   // and stays 1 (later rescales by exp2(0)): the final sum is >= 1 and
   // logprob <= 0 holds in fp32.
-  float s0 = 0.0f, s1 = 0.0f;
+  // Two interleaved sums, even and odd registers, each in register order
+  // (the first term starts the sum: 0 + t = t exactly).
+  floatx16 t;
 #pragma unroll
-  for (int i = 0; i < 16; i += 2) {
-    s0 += fast_exp2((z[i] - mref) * kLog2e);
-    s1 += fast_exp2((z[i + 1] - mref) * kLog2e);
+  for (int i = 0; i < 16; ++i) t[i] = fast_exp2((z[i] - mref) * kLog2e);
+  float s0 = t[0], s1 = t[1];
+#pragma unroll
+  for (int i = 2; i < 16; i += 2) {
+    s0 += t[i];
+    s1 += t[i + 1];
   }
   c.s = __builtin_fmaf(c.s, fast_exp2((c.m - mref) * kLog2e), s0 + s1);
   c.m = mnew;
@@ -77,8 +86,9 @@ __device__ __forceinline__ void flush_slice(Col& c, int tok, int n_tok, int half
 // Fold one accumulator block as it stands (the bf16 / fp32 heads). The
 // lane's 16 logits are copied out of the matrix-core registers where they
 // are used (acc_read), so the fold needs few VGPRs next to the accumulators.
+template <class kPartial>
 __device__ __forceinline__ void fold_block(Col& c, const floatx16& a, int bm, int vw, int half, int vocab,
-                                           bool partial) {
+                                           kPartial partial) {
   floatx16 z;  // a vector, not an array: it must stay in registers
 #pragma unroll
   for (int i = 0; i < 16; ++i) z[i] = acc_read(a, i);

@@ -237,7 +237,7 @@ __device__ __forceinline__ void run_tiles(uint4* smem, const Lanes& L, int row_b
   // last sub-step's reads must land before the barrier). With kDma, the 8
   // loads of H(g + 1) and then the 8 of W(g + 2) go one per MFMA.
   auto phase = [&](floatx16 (&acc)[4][4], const uint4 (&A)[4], const uint4 (&B)[4], auto first, auto do_mma,
-                   auto front, auto dma, int wsl, int hsl, int rkk, uint4 (&RA)[4], uint4 (&RB)[4]) {
+                   auto front, auto dma, auto do_read, int wsl, int hsl, int rkk, uint4 (&RA)[4], uint4 (&RB)[4]) {
     const uint4* sa = smem + wsl * kSlotChunks;
     const uint4* sb = smem + (kWSlots + hsl) * kSlotChunks;
     int4v wr;
@@ -256,7 +256,7 @@ __device__ __forceinline__ void run_tiles(uint4* smem, const Lanes& L, int row_b
         else Mma<kDtype>::step(acc[q >> 2][q & 3], A[q >> 2], B[q & 3]);
       }
       constexpr bool kFront = decltype(front)::value;
-      if (kFront ? q < 8 : (q & 1) == 0) {
+      if (decltype(do_read)::value && (kFront ? q < 8 : (q & 1) == 0)) {
         const int r = kFront ? q : q >> 1;
         if (r == 0) RA[0] = sa[a_off[rkk]];
         else if (r <= 4) RB[r - 1] = sb[b_off[rkk] + (r - 1) * 32 * kRowChunks];
@@ -325,20 +325,40 @@ __device__ __forceinline__ void run_tiles(uint4* smem, const Lanes& L, int row_b
   // read step g + 1's first two operand sets into S0, S1. kFirst = the
   // tile's first step (fresh accumulators). Loads past the workgroup's last
   // step re-read a valid step into a free slot, which nothing reads again.
-  auto k_step = [&](floatx16 (&acc)[4][4], auto first) {
-    phase(acc, a0, b0, first, T{}, F{}, F{}, wslot, hslot, 2, a2, b2);
-    phase(acc, a1, b1, F{}, T{}, T{}, F{}, wslot, hslot, 3, a3, b3);
+  //
+  // A tile's last step (kLast) leaves S0, S1 of the next step unread: they
+  // are read after the epilogue instead, so that the epilogue has the 64
+  // VGPRs they would hold (the slots of step g + 1 are not overwritten
+  // before every wavefront has passed step g + 1's barrier).
+  auto k_step = [&](floatx16 (&acc)[4][4], auto first, auto last) {
+    using R = std::integral_constant<bool, !decltype(last)::value>;
+    phase(acc, a0, b0, first, T{}, F{}, F{}, T{}, wslot, hslot, 2, a2, b2);
+    phase(acc, a1, b1, F{}, T{}, T{}, F{}, T{}, wslot, hslot, 3, a3, b3);
     wait_and_barrier<kDmaPerWave>();  // W(g + 1), H(g + 1) landed; W(g + 2) may still be in flight
     wslot = wslot == kWSlots - 1 ? 0 : wslot + 1;
     hslot ^= 1;
-    phase(acc, a2, b2, F{}, T{}, F{}, T{}, wslot, hslot, 0, a0, b0);
-    phase(acc, a3, b3, F{}, T{}, F{}, F{}, wslot, hslot, 1, a1, b1);
+    phase(acc, a2, b2, F{}, T{}, F{}, T{}, R{}, wslot, hslot, 0, a0, b0);
+    phase(acc, a3, b3, F{}, T{}, F{}, F{}, R{}, wslot, hslot, 1, a1, b1);
   };
   for (int tile = tile_begin; tile < tile_end; ++tile) {
     floatx16 acc[4][4];
-    k_step(acc, T{});
-    for (int ks = 1; ks < nks; ++ks) k_step(acc, F{});
+    if (nks == 1) {
+      k_step(acc, T{}, T{});
+    } else {
+      k_step(acc, T{}, F{});
+      for (int ks = 2; ks < nks; ++ks) k_step(acc, F{}, F{});
+      k_step(acc, F{}, T{});
+    }
     epi(tile, acc);
+    const uint4* sa = smem + wslot * kSlotChunks;
+    const uint4* sb = smem + (kWSlots + hslot) * kSlotChunks;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      a0[m] = sa[a_off[0] + m * 32 * kRowChunks];
+      b0[m] = sb[b_off[0] + m * 32 * kRowChunks];
+      a1[m] = sa[a_off[1] + m * 32 * kRowChunks];
+      b1[m] = sb[b_off[1] + m * 32 * kRowChunks];
+    }
   }
   // Every wavefront is done with the LDS ring (and its loads) on return.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -477,9 +497,15 @@ __device__ __forceinline__ void mma_f8_first(floatx16& acc, const Frag8& a, cons
                                                         floatx16{}, 0, 0, 0, 127, 0, 127);
 }
 
-template <class ARsrc, class Epi>
+//
+// pre(t) is called in tile t's last K step after its barrier, before the
+// step's 16 loads (H(g + 2), W(g + 3)) are issued: loads it issues there
+// complete before the epilogue once the epilogue waits for vmcnt(16).
+// Needs nks >= 2 (a tile's first and last K steps are distinct code: one
+// path for both would cost the register allocation of the whole loop).
+template <class ARsrc, class Epi, class Pre>
 __device__ __forceinline__ void run_tiles_f8(uint4* smem, const Lanes& L, int row_bytes, int tile_begin, int tile_end,
-                                             int nks, const ARsrc& a_rsrc, int4v b_rsrc, Epi&& epi) {
+                                             int nks, const ARsrc& a_rsrc, int4v b_rsrc, Epi&& epi, Pre&& pre) {
   const int lane = L.lane, wave = L.wave, wv = L.wv, wt = L.wt, half = L.half, col = L.col;
   const int lr = lane >> 3;
   uint32_t voff[kDmaPerWave];
@@ -525,7 +551,7 @@ __device__ __forceinline__ void run_tiles_f8(uint4* smem, const Lanes& L, int ro
   // barrier). With kDma, the 8 loads of H(g + 2) and then the 8 of W(g + 3)
   // go one per MFMA.
   auto phase = [&](floatx16 (&acc)[4][4], const Frag8 (&A)[4], const Frag8 (&B)[4], auto first, auto front,
-                   auto dma, int wsl, int hsl, int rj, Frag8 (&RA)[4], Frag8 (&RB)[4]) {
+                   auto dma, auto do_read, int wsl, int hsl, int rj, Frag8 (&RA)[4], Frag8 (&RB)[4]) {
     const uint4* sa = smem + wsl * kSlotChunks;
     const uint4* sb = smem + (kWSlots + hsl) * kSlotChunks;
     int4v wr;
@@ -547,7 +573,8 @@ __device__ __forceinline__ void run_tiles_f8(uint4* smem, const Lanes& L, int ro
     for (int q = 0; q < 16; ++q) {
       if constexpr (decltype(first)::value) mma_f8_first(acc[q >> 2][q & 3], A[q >> 2], B[q & 3]);
       else mma_f8(acc[q >> 2][q & 3], A[q >> 2], B[q & 3]);
-      if constexpr (decltype(front)::value) {
+      if constexpr (!decltype(do_read)::value) {
+      } else if constexpr (decltype(front)::value) {
         if (q < 8) {
           read(2 * q);
           read(2 * q + 1);
@@ -611,18 +638,32 @@ __device__ __forceinline__ void run_tiles_f8(uint4* smem, const Lanes& L, int ro
   // barrier then publishes step g + 1 (step g is all in registers, so its
   // slots are free); sub-step 1 (Y) while step g + 1's sub-step 0 is read
   // into X and H(g + 2), W(g + 3) are loaded into step g's slots.
-  auto k_step = [&](floatx16 (&acc)[4][4], auto first) {
-    phase(acc, xa, xb, first, T{}, F{}, wslot, hslot, 1, ya, yb);
+  // A tile's last step (kLast) calls pre and leaves X unread: X is read
+  // after the epilogue (as in run_tiles).
+  auto k_step = [&](floatx16 (&acc)[4][4], int tile, auto first, auto last) {
+    using R = std::integral_constant<bool, !decltype(last)::value>;
+    phase(acc, xa, xb, first, T{}, F{}, T{}, wslot, hslot, 1, ya, yb);
     wait_and_barrier<kDmaPerWave>();  // W(g + 1), H(g + 1) landed; W(g + 2) may still be in flight
     wslot = wslot == kWSlots - 1 ? 0 : wslot + 1;
     hslot ^= 1;
-    phase(acc, ya, yb, F{}, F{}, T{}, wslot, hslot, 0, xa, xb);
+    if constexpr (decltype(last)::value) pre(tile);
+    phase(acc, ya, yb, F{}, F{}, T{}, R{}, wslot, hslot, 0, xa, xb);
   };
   for (int tile = tile_begin; tile < tile_end; ++tile) {
     floatx16 acc[4][4];
-    k_step(acc, T{});
-    for (int ks = 1; ks < nks; ++ks) k_step(acc, F{});
+    k_step(acc, tile, T{}, F{});
+    for (int ks = 2; ks < nks; ++ks) k_step(acc, tile, F{}, F{});
+    k_step(acc, tile, F{}, T{});
     epi(tile, acc);
+    const uint4* sa = smem + wslot * kSlotChunks;
+    const uint4* sb = smem + (kWSlots + hslot) * kSlotChunks;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      xa[m].lo = sa[a_off[0][0] + m * 32 * kRowChunks];
+      xa[m].hi = sa[a_off[0][1] + m * 32 * kRowChunks];
+      xb[m].lo = sb[b_off[0][0] + m * 32 * kRowChunks];
+      xb[m].hi = sb[b_off[0][1] + m * 32 * kRowChunks];
+    }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
