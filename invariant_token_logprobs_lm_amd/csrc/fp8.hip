@@ -341,9 +341,28 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_q_partial_narrow_kernel(
   };
   const int4v hr =
       rsrc_words(Hq + (size_t)t0 * h_row_bytes, (uint32_t)min(kNarrowBRows, n_tok - t0) * h_row_bytes);
-  const __amdgpu_buffer_rsrc_t ws_rsrc = make_rsrc(w_sc, (uint32_t)vocab * 4u);  // fp8: per-row float scales
+  // FP8: per-row float scales, fetched in each tile's last K step and spread
+  // to lanes as in the wide kernel (lane l: rows vw + l, vw + 64 + l).
+  const int4v ws_words = rsrc_words(w_sc, kMx4 ? 0u : (uint32_t)vocab * 4u);
+  float ws_lo = 0.0f, ws_hi = 0.0f;
+  auto pre = [&](int tile) {
+    if constexpr (!kMx4) {
+      const uint32_t off = (uint32_t)(tile * kBV + wv * 128 + L.lane) * 4u;
+      const uint32_t off_hi = off + 256u;
+      const int4v r = {__builtin_amdgcn_readfirstlane(ws_words[0]), __builtin_amdgcn_readfirstlane(ws_words[1]),
+                       __builtin_amdgcn_readfirstlane(ws_words[2]), __builtin_amdgcn_readfirstlane(ws_words[3])};
+      asm volatile(
+          "buffer_load_dword %0, %2, %4, 0 offen\n\t"
+          "buffer_load_dword %1, %3, %4, 0 offen"
+          : "=&v"(ws_lo), "=&v"(ws_hi)
+          : "v"(off), "v"(off_hi), "s"(r)
+          : "memory");
+    }
+  };
   auto epilogue = [&](int tile, floatx16 (&acc)[4]) {
     const int vw = tile * kBV + wv * 128;
+    if constexpr (!kMx4)
+      asm volatile("s_waitcnt vmcnt(%2)" : "+v"(ws_lo), "+v"(ws_hi) : "n"(kNarrowQLoadsAfterPre<false>) : "memory");
     mfma_result_wait();
     auto fold_tile = [&](auto partial) {
 #pragma unroll
@@ -353,10 +372,11 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_q_partial_narrow_kernel(
 #pragma unroll
           for (int i = 0; i < 16; ++i) z[i] = acc_read(acc[bm], i) * hs;
         } else {
+          const int src = __float_as_int(bm < 2 ? ws_lo : ws_hi);
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const float w =
-                buffer_load4(ws_rsrc, (uint32_t)(vw + bm * 32 + 8 * (i >> 2) + 4 * half + (i & 3)) * 4u);
+            const float w = __int_as_float(
+                __builtin_amdgcn_ds_bpermute((32 * (bm & 1) + 8 * (i >> 2) + 4 * half + (i & 3)) * 4, src));
             z[i] = (acc_read(acc[bm], i) * w) * hs;
           }
         }
@@ -367,7 +387,7 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_q_partial_narrow_kernel(
     else fold_tile(std::false_type{});
   };
   run_tiles_narrow_q<kMx4>(smem, L, w_row_bytes, s_row_bytes, h_row_bytes, tile_begin, tile_end, nks, w_rsrc, s_rsrc,
-                           hr, epilogue);
+                           hr, epilogue, pre);
   flush_slice(c, tok, n_tok, half, ((size_t)slice * 2 + wv) * n_tok + tok, part);
   if (c.found) zy_out[tok] = c.zy;
 }

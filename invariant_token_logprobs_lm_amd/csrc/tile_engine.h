@@ -895,16 +895,23 @@ __device__ __forceinline__ void run_tiles_mx4(uint4* smem, const Lanes& L, int w
 // layout and swizzle, same H chunk choice, same sub-step order), so each
 // output element has the same bits. Both operands rotate through 4 slots,
 // loaded three K steps ahead; all of a step's fragments are read up front.
-template <bool kMx4, class ARsrc, class SRsrc, class Epi>
+// pre(t) is called in tile t's last K step after its barrier, before the
+// step's loads (kNarrowQLoadsAfterPre<kMx4> of them) are issued; the
+// epilogue may wait for pre's loads with vmcnt(that count).
+template <bool kMx4>
+constexpr int kNarrowQLoadsAfterPre = (kMx4 ? kMx4WDataLoads + 1 : kDmaPerWave) + kNarrowBDmaPerWave;
+
+template <bool kMx4, class ARsrc, class SRsrc, class Epi, class Pre>
 __device__ __forceinline__ void run_tiles_narrow_q(uint4* smem, const Lanes& L, int w_row_bytes, int s_row_bytes,
                                                    int h_row_bytes, int tile_begin, int tile_end, int nks,
                                                    const ARsrc& a_rsrc, const SRsrc& s_rsrc, int4v b_rsrc,
-                                                   Epi&& epi) {
+                                                   Epi&& epi, Pre&& pre) {
   const int lane = L.lane, wave = L.wave, wv = L.wv, wt = L.wt, half = L.half, col = L.col;
   const int lr = lane >> 3;
   constexpr int kWSlotBytes = kMx4 ? kMx4WSlotBytes : kSlotBytes;
   constexpr int kWLoads = kMx4 ? kMx4WDataLoads : kDmaPerWave;      // W code loads per wavefront per step
   constexpr int kLoads = kWLoads + (kMx4 ? 1 : 0) + kNarrowBDmaPerWave;
+  static_assert(kLoads == kNarrowQLoadsAfterPre<kMx4>, "loads per step");
   constexpr int kHBase = kNarrowSlots * kWSlotBytes;
   static_assert(kHBase + kNarrowSlots * kNarrowBSlotChunks * 16 <= kEngineSmemChunks * 16, "LDS budget");
   uint32_t wvoff[kWLoads];
@@ -968,8 +975,9 @@ __device__ __forceinline__ void run_tiles_narrow_q(uint4* smem, const Lanes& L, 
   constexpr int kPending = (kNarrowSlots - 2) * kLoads;
   constexpr int kARowChunks = kMx4 ? kMx4RowChunks : kRowChunks;
   int slot = 0;
-  auto k_step = [&](floatx16 (&acc)[4], auto first) {
+  auto k_step = [&](floatx16 (&acc)[4], int tile, auto first, auto last) {
     wait_and_barrier<kPending>();
+    if constexpr (decltype(last)::value) pre(tile);
     load_step(ld_tile, ld_ks, slot == 0 ? kNarrowSlots - 1 : slot - 1);
     next_load();
     const uint4* sa = smem + (slot * kWSlotBytes) / 16;
@@ -1007,10 +1015,17 @@ __device__ __forceinline__ void run_tiles_narrow_q(uint4* smem, const Lanes& L, 
       }
     slot = slot == kNarrowSlots - 1 ? 0 : slot + 1;
   };
+  using T = std::true_type;
+  using F = std::false_type;
   for (int tile = tile_begin; tile < tile_end; ++tile) {
     floatx16 acc[4];
-    k_step(acc, std::true_type{});
-    for (int ks = 1; ks < nks; ++ks) k_step(acc, std::false_type{});
+    if (nks == 1) {
+      k_step(acc, tile, T{}, T{});
+    } else {
+      k_step(acc, tile, T{}, F{});
+      for (int ks = 2; ks < nks; ++ks) k_step(acc, tile, F{}, F{});
+      k_step(acc, tile, F{}, T{});
+    }
     epi(tile, acc);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
