@@ -33,6 +33,7 @@ KERNEL_SOURCES = ["invariant_token_logprobs_lm_amd/csrc/lmhead.hip",
                   "invariant_token_logprobs_lm_amd/csrc/tile_engine.h",
                   "invariant_token_logprobs_lm_amd/csrc/itl_config.h",
                   "invariant_token_logprobs_lm_amd/csrc/device_common.h",
+                  "invariant_token_logprobs_lm_amd/csrc/lse_fold.h",
                   "invariant_token_logprobs_lm_amd/build.py"]
 
 
