@@ -21,8 +21,10 @@ constexpr int kStepBytes = 128;      // bytes of one operand row per K step (64 
 constexpr int kWSlots = 3;           // LDS slots of the W-tile ring (loads two K steps ahead)
 constexpr int kHSlots = 2;           // LDS slots of the H-block ring (loads one K step ahead)
 constexpr int kMaxSlices = 256;      // vocabulary slices: min(tiles, this), a function of the vocabulary only
-constexpr int kTilesPerGroup = 16;   // grid shape only: a workgroup walks about this many tiles of consecutive
-                                     // slices when the batch is large (the arithmetic per slice is the same)
+constexpr int kTilesPerGroup = 16;   // grid shape only (backward dlogits): a workgroup walks about this many
+                                     // tiles of consecutive slices (the arithmetic per slice is the same)
+constexpr int kWideTilesPerGroup = 4;  // the same for the forward kernels: with the vocabularies of interest
+                                       // (>= 512 tiles) one slice per workgroup, the fastest order measured
 constexpr int kNarrowBRows = 64;      // tokens per block of the narrow (few-token) kernel
 constexpr int kNarrowMaxTokens = 64;   // calls with at most this many tokens use the narrow kernel
 constexpr int kSuperBand = 32;       // token blocks walked together, slice group by slice group (workgroup order)
@@ -41,15 +43,18 @@ inline int n_slices(long long vocab) {
 
 // Slices per workgroup: 1 while the grid is small (decode-shaped calls keep
 // one workgroup per slice, so every CU streams W), else the largest power of
-// two g with g slices holding at most 1.5 kTilesPerGroup tiles (a power of
-// two divides S = 256 evenly). Changes which workgroup computes a slice,
-// never how: each slice's partial is the same instruction sequence.
+// two g with g slices holding at most 1.5 kWideTilesPerGroup tiles (a power
+// of two divides S = 256 evenly). Changes which workgroup computes a slice,
+// never how: each slice's partial is the same instruction sequence. (Walking
+// 2 to 4 slices per workgroup measured 1-3 % slower than 1 on the bf16
+// heads: workgroups that share operands through an XCD's L2 drift apart
+// over long walks.)
 inline int slices_per_group(long long n_tok, long long vocab) {
   const long long ntb = ceil_div(n_tok, kBT);
   const long long S = n_slices(vocab), nvt = n_vocab_tiles(vocab);
   if (ntb * S <= 2048) return 1;
   long long g = 1;
-  while (2 * g <= S && 2 * g * nvt * 2 <= 3LL * kTilesPerGroup * S) g *= 2;
+  while (2 * g <= S && 2 * g * nvt * 2 <= 3LL * kWideTilesPerGroup * S) g *= 2;
   return (int)g;
 }
 inline int n_slice_groups(long long n_tok, long long vocab) {
