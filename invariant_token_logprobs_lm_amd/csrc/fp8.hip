@@ -117,10 +117,10 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_fp8_partial_kernel(
   // vw + l and vw + 64 + l of each tile (vw = the wavefront's first row)
   // into ws_lo, ws_hi, through a bounded buffer (rows past the vocabulary
   // read 0). The loads are issued from inline assembly in the tile's last K
-  // step, before that step's 16 loads into LDS, and waited for with
-  // vmcnt(16) in the epilogue: a load the compiler can see would make it
-  // wait for every load in flight (vmcnt(0)) and stall on the next steps'
-  // operands at every tile.
+  // step, before that step's loads into LDS, and waited for with
+  // vmcnt(kF8LoadsAfterPre) in the epilogue: a load the compiler can see
+  // would make it wait for every load in flight (vmcnt(0)) and stall on the
+  // next steps' operands at every tile.
   const int4v ws_words = rsrc_words(w_scale, (uint32_t)vocab * 4u);
   float ws_lo = 0.0f, ws_hi = 0.0f;
   auto pre = [&](int tile) {
@@ -140,7 +140,7 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_fp8_partial_kernel(
   int slice_last_tile = slice_tile(slice + 1, n_vt, S) - 1;
   auto epilogue = [&](int tile, floatx16 (&acc)[4][4]) {
     const int vw = tile * kBV + wv * 128;
-    asm volatile("s_waitcnt vmcnt(16)" : "+v"(ws_lo), "+v"(ws_hi)::"memory");
+    asm volatile("s_waitcnt vmcnt(%2)" : "+v"(ws_lo), "+v"(ws_hi) : "n"(kF8LoadsAfterPre) : "memory");
     mfma_result_wait();
     auto fold_tile = [&](auto partial) {
 #pragma unroll

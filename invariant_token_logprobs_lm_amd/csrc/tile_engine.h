@@ -499,10 +499,13 @@ __device__ __forceinline__ void mma_f8_first(floatx16& acc, const Frag8& a, cons
 
 //
 // pre(t) is called in tile t's last K step after its barrier, before the
-// step's 16 loads (H(g + 2), W(g + 3)) are issued: loads it issues there
-// complete before the epilogue once the epilogue waits for vmcnt(16).
+// step's kF8LoadsAfterPre loads (H(g + 2), W(g + 3)) are issued: loads it
+// issues there complete before the epilogue once the epilogue waits for
+// vmcnt(kF8LoadsAfterPre).
 // Needs nks >= 2 (a tile's first and last K steps are distinct code: one
 // path for both would cost the register allocation of the whole loop).
+constexpr int kF8LoadsAfterPre = 2 * kDmaPerWave;
+
 template <class ARsrc, class Epi, class Pre>
 __device__ __forceinline__ void run_tiles_f8(uint4* smem, const Lanes& L, int row_bytes, int tile_begin, int tile_end,
                                              int nks, const ARsrc& a_rsrc, int4v b_rsrc, Epi&& epi, Pre&& pre) {

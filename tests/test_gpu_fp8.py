@@ -73,11 +73,12 @@ def _to_dev(cuda, *arrays):
 
 @pytest.mark.parametrize("n_tok,d,vocab", [
     (700, 256, 5000),          # 3 token blocks (ragged), 20 tiles
-    (300, 128, 4096 + 37),     # one K step; last tile of 37 rows (scale loads past the end)
+    (300, 128, 4096 + 37),     # one K step (narrow kernel, 5 token blocks); last tile of 37 rows
     (1, 128, 300),             # one token (narrow kernel)
     (64, 256, 3000),           # a full narrow block
     (513, 384, 8192 + 256),    # d = 3 K steps
-    (5200, 128, 150 * 256 - 17),  # 21 x 150 > 2048: several slices per workgroup
+    (5200, 128, 150 * 256 - 17),  # d = 128 with many tokens: the narrow kernel, 82 token blocks
+    (3400, 256, 150 * 256 - 17),  # 14 x 150 > 2048: several slices per workgroup (wide kernel)
 ])
 def test_lmhead_fp8_parity(cuda, n_tok, d, vocab):
     from oracle import fp8
