@@ -131,13 +131,13 @@ __global__ __launch_bounds__(256) void dw_sampled_kernel(const uint32_t* __restr
 }
 
 // Workgroup order shared by the three contractions: the grid is n_fast x
-// n_slow blocks; super-bands of kSuperBand fast indices are walked with the
+// n_slow blocks; super-bands of kBwdSuperBand fast indices are walked with the
 // slow index outer, so the workgroups an XCD runs together share operands.
 __device__ __forceinline__ void band_order(int b, int n_fast, int n_slow, int& fast, int& slow) {
-  const int band = b / (kSuperBand * n_slow);
-  const int first = band * kSuperBand;
-  const int nb = min(kSuperBand, n_fast - first);
-  const int rem = b - band * kSuperBand * n_slow;
+  const int band = b / (kBwdSuperBand * n_slow);
+  const int first = band * kBwdSuperBand;
+  const int nb = min(kBwdSuperBand, n_fast - first);
+  const int rem = b - band * kBwdSuperBand * n_slow;
   slow = rem / nb;
   fast = first + rem % nb;
 }
