@@ -13,24 +13,6 @@ typedef int int4v __attribute__((ext_vector_type(4)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-// Raw buffer resource over [base, base + nbytes). Loads whose VGPR offset is
-// past nbytes return zeros instead of faulting (callers keep the scalar
-// offset at 0: only the VGPR offset is range-checked), which is how tile rows beyond the last token or
-// vocabulary row are read safely. Word 3 is the gfx9-family raw-buffer
-// configuration (32-bit data format, no swizzle, no index stride).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t nbytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nbytes, 0x00020000);
-}
-
-__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  int4v v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
-  return uint4{(unsigned)v[0], (unsigned)v[1], (unsigned)v[2], (unsigned)v[3]};
-}
-
-__device__ __forceinline__ float buffer_load4(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
-  return __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, 0, 0));
-}
-
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
