@@ -56,14 +56,58 @@ __device__ __forceinline__ float load_elem(const void* X, size_t i) {
 }
 
 // One wavefront per row: amax by a butterfly of maxima (exact, so any tree
-// gives the same value), then four codes per lane packed into one store.
+// gives the same value), then the codes. Rows of up to 512 16-byte chunks
+// (4096 bf16 / 2048 fp32 values) are read once, 16 bytes per lane per load,
+// and kept in registers for the second pass (when X is 16-byte and Xq
+// 8-byte aligned); other rows are read twice, 4 values per lane per step.
+// Both paths compute every code the same way.
 template <int kDtype>
 __global__ __launch_bounds__(256) void quantize_rows_fp8_kernel(const void* __restrict__ X, long long n_rows, int d,
                                                                 uint8_t* __restrict__ Xq, float* __restrict__ scale) {
+  constexpr int kPerChunk = kDtype == 0 ? 8 : 4;  // values per 16-byte chunk
+  constexpr int kMaxChunks = 8;                   // chunks a lane keeps in registers
   const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= n_rows) return;
   const size_t base = (size_t)row * d;
+  const int n_chunks = d / kPerChunk;  // d is a multiple of 128
+  auto value = [&](const uint4& v, int j) {
+    const uint32_t w = (&v.x)[kDtype == 0 ? j >> 1 : j];
+    if constexpr (kDtype == 0) return __uint_as_float((j & 1) ? (w & 0xffff0000u) : (w << 16));
+    else return __uint_as_float(w);
+  };
+  const bool aligned = ((reinterpret_cast<uintptr_t>(X) & 15) | (reinterpret_cast<uintptr_t>(Xq) & 7)) == 0;
+  if (aligned && n_chunks <= 64 * kMaxChunks) {
+    const uint4* src = reinterpret_cast<const uint4*>(static_cast<const char*>(X) + base * (kDtype == 0 ? 2 : 4));
+    uint4 v[kMaxChunks];
+    float amax = 0.0f;
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c) {
+      const int idx = lane + 64 * c;
+      v[c] = idx < n_chunks ? src[idx] : uint4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int j = 0; j < kPerChunk; ++j) amax = fmaxf(amax, fabsf(value(v[c], j)));
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+    const float s = amax > 0.0f ? __fdiv_rn(amax, 448.0f) : 1.0f;
+    if (lane == 0) scale[row] = s;
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c) {
+      const int idx = lane + 64 * c;
+      if (idx >= n_chunks) break;
+      uint32_t lo = 0, hi = 0;
+#pragma unroll
+      for (int j = 0; j < kPerChunk; ++j) {
+        const uint32_t code = e4m3_rne(__fdiv_rn(value(v[c], j), s));
+        if (j < 4) lo |= code << (8 * j);
+        else hi |= code << (8 * (j - 4));
+      }
+      if constexpr (kDtype == 0) *reinterpret_cast<uint2*>(Xq + base + (size_t)idx * 8) = make_uint2(lo, hi);
+      else *reinterpret_cast<uint32_t*>(Xq + base + (size_t)idx * 4) = lo;
+    }
+    return;
+  }
   float amax = 0.0f;
   for (int k = lane * 4; k < d; k += 256)
 #pragma unroll

@@ -31,6 +31,8 @@ def _host_f32(X):
     (37, 128, "bf16", 0), (200, 256, "f32", 0), (64, 2560, "bf16", 0),
     (50, 384, "f32", -30),   # tiny values: scales far below 1, many subnormal codes
     (50, 128, "f32", 20),    # large values
+    (9, 8192, "bf16", 0),    # rows too long to keep in registers: the two-pass path
+    (9, 4096, "f32", 0),
 ])
 def test_quantize_rows_bit_exact(cuda, n, d, dtype_name, scale_pow):
     import torch
@@ -50,6 +52,29 @@ def test_quantize_rows_bit_exact(cuda, n, d, dtype_name, scale_pow):
     assert np.array_equal(Xq.cpu().numpy(), q_o)
     assert np.array_equal(s.cpu().numpy().view(np.uint32), s_o.view(np.uint32))
     say(f"[fp8 quantize] {n}x{d} {dtype_name} 2^{scale_pow}: codes and scales bit-identical")
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("dtype_name", ["bf16", "f32"])
+def test_quantize_rows_unaligned_input(cuda, dtype_name):
+    """X whose base is not 16-byte aligned takes the two-pass path; the codes
+    are the same."""
+    import torch
+    from oracle import fp8
+
+    n, d = 9, 256
+    dt = torch.bfloat16 if dtype_name == "bf16" else torch.float32
+    g = torch.Generator(device="cpu").manual_seed(77)
+    X = (torch.randn(n, d, generator=g) * 3.0).to(dt)
+    buf = torch.zeros(n * d + 8, dtype=dt, device=cuda)
+    buf[1:1 + n * d] = X.reshape(-1).to(cuda)
+    Xv = buf[1:1 + n * d].view(n, d)
+    assert Xv.data_ptr() % 16 != 0
+    itl = _itl()
+    Xq, s = itl.quantize_rows_fp8(Xv)
+    q_o, s_o = fp8.quantize_rows_fp8(_host_f32(X))
+    assert np.array_equal(Xq.cpu().numpy(), q_o)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), s_o.view(np.uint32))
 
 
 def _oracle_quantized_head(n_tok, d, vocab, seed, w_std=0.05):
