@@ -158,9 +158,13 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_lse_partial_narrow_kernel(
 // coalesced 512-byte row of the partial table); its 16 wavefronts split the
 // partials into 16 fixed consecutive runs, fold each run in order, and the
 // 16 run states are merged in run order. The run boundaries depend on S only,
-// so a token's result has the same bits whatever n_tok; with few tokens the
-// 16 runs keep the latency chain short (at most 32 dependent merges).
+// so a token's result has the same bits whatever n_tok. A run is at most 32
+// partials; all of a run's loads are issued before its first merge, so a
+// call waits on one memory round trip, not one per partial (a decode call's
+// combine is latency-bound).
 constexpr int kCombineWaves = 16;
+constexpr int kCombineMaxRun = 32;
+static_assert(2 * kMaxSlices <= kCombineWaves * kCombineMaxRun, "a run must fit the register buffer");
 
 namespace {
 
@@ -176,11 +180,13 @@ __global__ __launch_bounds__(64 * kCombineWaves) void lse_combine_kernel(const f
   const int p0 = min(w * run, n_parts), p1 = min(p0 + run, n_parts);
   float m = -INFINITY, s = 0.0f;
   if (t < n_tok) {
-#pragma unroll 8
-    for (int p = p0; p < p1; ++p) {
-      const float2 v = part[(size_t)p * n_tok + t];
-      lse_merge(m, s, v.x, v.y);
-    }
+    float2 v[kCombineMaxRun];
+#pragma unroll
+    for (int i = 0; i < kCombineMaxRun; ++i)
+      if (p0 + i < p1) v[i] = part[(size_t)(p0 + i) * n_tok + t];
+#pragma unroll
+    for (int i = 0; i < kCombineMaxRun; ++i)
+      if (p0 + i < p1) lse_merge(m, s, v[i].x, v[i].y);
   }
   run_state[w][lane] = make_float2(m, s);
   __syncthreads();
