@@ -235,7 +235,9 @@ __device__ __forceinline__ void run_tiles(uint4* smem, const Lanes& L, int row_b
   // order the next sub-step needs them) from slots (wsl, hsl), sub-step rkk:
   // one read every second MFMA, or in the first 8 MFMAs when kFront (the
   // last sub-step's reads must land before the barrier). With kDma, the 8
-  // loads of H(g + 1) and then the 8 of W(g + 2) go one per MFMA.
+  // loads of H(g + 2) and then the 8 of W(g + 3) go one per MFMA (in that
+  // order: the barrier's vmcnt(8) lets exactly the W loads stay in flight).
+  // Without kRead the sub-step reads nothing.
   auto phase = [&](floatx16 (&acc)[4][4], const uint4 (&A)[4], const uint4 (&B)[4], auto first, auto do_mma,
                    auto front, auto dma, auto do_read, int wsl, int hsl, int rkk, uint4 (&RA)[4], uint4 (&RB)[4]) {
     const uint4* sa = smem + wsl * kSlotChunks;
