@@ -149,7 +149,10 @@ itl_status itl_lmhead_logprob_fp8(const uint8_t* Hq, const float* h_scale, const
   if (vocab > kMaxVocab) return fail(ITL_ERR_UNSUPPORTED, "vocab too large");
   if (d * (int64_t)itl::kBT >= ((int64_t)1 << 31)) return fail(ITL_ERR_UNSUPPORTED, "d too large");
   if (vocab > (int64_t)(UINT32_MAX / 4)) return fail(ITL_ERR_UNSUPPORTED, "vocab too large");
-  const int64_t grid = itl::ceil_div(n_tok, itl::kBT) * itl::n_slice_groups(n_tok, vocab);
+  // the grid of the kernel that runs: narrow for few tokens or d = 128
+  const bool narrow = n_tok <= itl::kNarrowMaxTokens || d < itl::kF8WideMinD;
+  const int64_t grid = narrow ? itl::ceil_div(n_tok, itl::kNarrowBRows) * itl::n_slices(vocab)
+                              : itl::ceil_div(n_tok, itl::kBT) * itl::n_slice_groups(n_tok, vocab);
   if (grid > INT32_MAX) return fail(ITL_ERR_UNSUPPORTED, "problem too large for one launch");
   if (n_tok == 0) return ITL_OK;
   if (!Hq || !h_scale || !Wq || !w_scale || !tokens || !logprob)

@@ -459,7 +459,7 @@ hipError_t launch_lmhead_logprob_fp8(const uint8_t* Hq, const float* h_scale, co
                                        align256((size_t)2 * S * (size_t)n_tok * sizeof(float2)));
   // The wide kernel needs two K steps of 128 values (d >= 256); the narrow
   // kernel gives the same bits and takes any number of token blocks.
-  if (n_tok <= kNarrowMaxTokens || d < 256) {
+  if (n_tok <= kNarrowMaxTokens || d < kF8WideMinD) {
     const dim3 grid((unsigned)ceil_div(n_tok, kNarrowBRows) * (unsigned)S);
     hipLaunchKernelGGL(lmhead_q_partial_narrow_kernel<false>, grid, dim3(kThreads), 0, stream, Hq, h_scale, Wq,
                        static_cast<const void*>(w_scale), tokens, n_tok, d, vocab, S, part, zy);

@@ -30,6 +30,7 @@ constexpr int kNarrowMaxTokens = 64;   // calls with at most this many tokens us
 constexpr int kSuperBand = 64;       // token blocks walked together, slice group by slice group (workgroup order)
 constexpr int kBwdSuperBand = 32;    // the same for the backward kernels' walk (64 measured 3 % slower there)
 constexpr int kDMultiple = 64;       // d must be a multiple of this
+constexpr int kF8WideMinD = 256;     // the wide FP8 kernel needs two K steps of 128 values; smaller d runs narrow
 
 constexpr int kLossThreads = 256;    // threads per response in the loss kernel
 constexpr int kMeanThreads = 1024;   // threads of the single-block mean

@@ -295,3 +295,27 @@ def test_lmhead_mxfp4_full_size_head(cuda):
     say(f"[mxfp4 qwen3-4b-head] n_tok={lay.n_tok}: W codes bit-identical; sampled max|dlp|={e_lp:.3e}")
     assert e_lp <= TOL_LP
     assert float(lp.max()) <= 0.0
+
+
+@pytest.mark.gpu
+def test_quantized_heads_empty_calls(cuda):
+    """Zero rows and zero tokens are no-ops that return empty results."""
+    import torch
+
+    itl = _itl()
+    d, vocab = 256, 3000
+    W = (torch.randn(vocab, d, generator=torch.Generator(device="cpu").manual_seed(3)) * 0.05).to(torch.bfloat16)
+    W = W.to(cuda)
+    Wq, ws = itl.quantize_rows_fp8(W)
+    W4, s4 = itl.quantize_rows_mxfp4(W)
+    H0 = torch.empty(0, d, dtype=torch.bfloat16, device=cuda)
+    Hq0, hs0 = itl.quantize_rows_fp8(H0)
+    assert Hq0.shape == (0, d) and hs0.shape == (0,)
+    W40, s40 = itl.quantize_rows_mxfp4(H0)
+    assert W40.shape == (0, d // 2) and s40.shape == (0, d // 32)
+    y0 = torch.empty(0, dtype=torch.int32, device=cuda)
+    lp, lse = itl.lmhead_logprob_fp8(Hq0, hs0, Wq, ws, y0)
+    assert lp.shape == (0,) and lse.shape == (0,)
+    lp, lse = itl.lmhead_logprob_mxfp4(Hq0, hs0, W4, s4, y0)
+    assert lp.shape == (0,) and lse.shape == (0,)
+    torch.cuda.synchronize()
