@@ -238,21 +238,33 @@ __global__ __launch_bounds__(kThreads, 1) void dh_kernel(const char* __restrict_
       const bool yok = (unsigned)yr < (unsigned)vocab;  // an invalid id contributes no sampled term
       const float c = ok && yok ? coef[t] : 0.0f;
       const int yt = yok ? yr : 0;
+      // The 16 groups of 4 W[y] values this lane needs for token t are
+      // loaded together (one memory round trip per token column, not one
+      // per group), then combined with the accumulators and stored.
+      float wyv[4][4][4];
+#pragma unroll
+      for (int bm = 0; bm < 4; ++bm)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int k = kw + bm * 32 + 8 * i4;  // d rows k .. k + 3 (d is a multiple of 64)
+          const typename E::T* wy = W + (size_t)yt * d + (k < d ? k : 0);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) wyv[bm][i4][r] = E::to_f(wy[r]);
+        }
 #pragma unroll
       for (int bm = 0; bm < 4; ++bm) {
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
-          const int k = kw + bm * 32 + 8 * i4;  // d rows k .. k + 3 (d is a multiple of 64)
+          const int k = kw + bm * 32 + 8 * i4;
           float o[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) o[r] = acc_read(acc[bm][bn], 4 * i4 + r);
           if (ok && k < d) {
-            const typename E::T* wy = W + (size_t)yt * d + k;
             float4 out;
-            out.x = o[0] + c * E::to_f(wy[0]);
-            out.y = o[1] + c * E::to_f(wy[1]);
-            out.z = o[2] + c * E::to_f(wy[2]);
-            out.w = o[3] + c * E::to_f(wy[3]);
+            out.x = o[0] + c * wyv[bm][i4][0];
+            out.y = o[1] + c * wyv[bm][i4][1];
+            out.z = o[2] + c * wyv[bm][i4][2];
+            out.w = o[3] + c * wyv[bm][i4][3];
             *reinterpret_cast<float4*>(dH + (size_t)t * d + k) = out;
           }
         }
@@ -288,16 +300,24 @@ __global__ __launch_bounds__(kThreads, 1) void dw_kernel(const char* __restrict_
 #pragma unroll
     for (int bn = 0; bn < 4; ++bn) {
       const int k = k0 + L.wt * 128 + bn * 32 + L.col;
+      // The 64 dW values of this lane's column k are read together (one
+      // memory round trip per column, not one per 32 x 32 block), then
+      // updated and written back.
+      float old[4][16];
+#pragma unroll
+      for (int bm = 0; bm < 4; ++bm)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int v = vw + bm * 32 + 8 * (i >> 2) + (i & 3);
+          old[bm][i] = v < vocab && k < d ? dW[(size_t)v * d + k] : 0.0f;
+        }
 #pragma unroll
       for (int bm = 0; bm < 4; ++bm) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const float a = acc_read(acc[bm][bn], i);
           const int v = vw + bm * 32 + 8 * (i >> 2) + (i & 3);
-          if (v < vocab && k < d) {
-            float* p = dW + (size_t)v * d + k;
-            *p = *p + a;
-          }
+          if (v < vocab && k < d) dW[(size_t)v * d + k] = old[bm][i] + a;
         }
         __builtin_amdgcn_sched_barrier(0);
       }
