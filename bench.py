@@ -276,7 +276,7 @@ def mismatch_leg(s, device, calls=20, n_demo=4096, batch=64):
         log(f"[bench] kernel mismatch, {name} rollout: {int(d['kernel_nonzero'])}/{n_demo} tokens differ, "
             f"max |dlp| {d['kernel_abs_max']:.3e}, weight deviation peak/median {d['deviation_peak_over_median']:.2f}")
     return {
-        "kernel": "itl_mismatch_stats (terms + radix sort + finalize)",
+        "kernel": "itl_mismatch_stats (terms + exact median by radix selection + finalize)",
         "n_tok": n,
         "us_per_call": ms * 1e3,
         "input_gb_per_s": 12.0 * n / (ms * 1e-3) / 1e9,

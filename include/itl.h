@@ -243,7 +243,7 @@ typedef enum itl_stat {
 } itl_stat;
 
 /* Bytes of device workspace itl_mismatch_stats needs for n_tok tokens
- * (about 16 n_tok plus sort scratch). SIZE_MAX for invalid sizes. */
+ * (about 16 n_tok plus 140 KiB). SIZE_MAX for invalid sizes. */
 size_t itl_mismatch_stats_workspace_bytes(int64_t n_tok);
 
 /* Train/inference mismatch diagnostics of one batch of sampled tokens [GAP].
@@ -254,12 +254,14 @@ size_t itl_mismatch_stats_workspace_bytes(int64_t n_tok);
  * token, in fp64 from the exact fp32 values: delta = logprob -
  * rollout_logprob, w = exp(delta); KL(rollout || learner) by the sample
  * estimators k1, k2, k3 of J. Schulman's "Approximating KL Divergence"
- * (tokens are drawn from the rollout policy). The median is exact (a radix
- * sort of |w - 1|; the mean of the two middle values for even n_tok).
+ * (tokens are drawn from the rollout policy). The median is exact (radix
+ * selection of the middle value(s) of |w - 1| by their fp64 bits; the mean
+ * of the two middle values for even n_tok).
  * stats: DEVICE fp64 [ITL_STAT_COUNT], written on `stream`; the split
  * fields are NaN without same_weights_logprob, every field but N_TOK is
  * NaN when n_tok == 0. Run-to-run deterministic (fixed reduction order for
- * a given n_tok). workspace: >= itl_mismatch_stats_workspace_bytes(n_tok)
+ * a given n_tok; the selection's integer counts do not depend on the order
+ * their atomic additions land in). workspace: >= itl_mismatch_stats_workspace_bytes(n_tok)
  * bytes, 256-byte aligned. n_tok above 2^31 - 1 returns
  * ITL_ERR_UNSUPPORTED. */
 itl_status itl_mismatch_stats(const float* logprob, const float* rollout_logprob,

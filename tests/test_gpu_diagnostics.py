@@ -6,7 +6,8 @@ relative to the sum of the terms' magnitudes; maxima, minima and the median
 are single per-token values and agree to 1e-14 relative; the bit-difference
 count is exact. Cases span one token, odd and even counts, several 2048-token
 workgroups with a ragged tail, the qwen3-4b head's token count with its lag
-noise recipe, zero lag and the empty batch.
+noise recipe, middle values far apart and tied values, zero lag (every key
+equal) and the empty batch.
 """
 
 import math
@@ -98,6 +99,22 @@ def test_parity_random(cuda, n):
     lp, lr, same = _lagged(n, seed=n)
     _run(lp, lr, same, cuda, f"lagged+split n={n}")
     _run(lp, lr, None, cuda, f"lagged n={n}")
+
+
+def test_median_between_far_apart_values(cuda):
+    """The two middle deviations lie in different 16-bit key prefixes (two
+    clusters), and many deviations tie: the median is still exact."""
+    rng = np.random.default_rng(11)
+    n = 4000
+    lp = -np.abs(rng.standard_normal(n)).astype(np.float32)
+    shift = np.where(np.arange(n) < n // 2, 0.25, 1.5).astype(np.float32)  # half small, half large deviations
+    lr = (lp + shift).astype(np.float32)
+    rng.shuffle(lr)  # also breaks the pairing: deviations spread over many values
+    lr[: n // 4] = lp[: n // 4] + np.float32(0.25)  # a block of tied values
+    _run(lp, lr, None, cuda, "two clusters with ties")
+    lr2 = lp + np.where(np.arange(n) % 2 == 0, np.float32(1e-3), np.float32(3.0)).astype(np.float32)
+    got = _run(lp, lr2.astype(np.float32), None, cuda, "two-valued")
+    assert got["deviation_median"] > 0
 
 
 def test_zero_lag_is_exact(cuda):
