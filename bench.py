@@ -227,6 +227,72 @@ def decode_leg(wl, device, batch_sizes=(1, 8, 64, 128, 256), calls=20):
     }
 
 
+def prefill_leg(s, device, chunk=16384, calls=5):
+    """Prefill-shaped calls on the same head: one chunk of the batch's tokens
+    through the invariant kernel, against the library path an inference
+    engine would take (hipBLASLt GEMM to bf16 logits, then torch log_softmax
+    in fp32 and a gather; not batch-invariant), and against the library GEMM
+    alone. The GEMM alone writes the chunk's logits and does nothing else:
+    its rate is the plain contraction's, a practical ceiling for the fused
+    kernel's matrix-core work on this shape."""
+    import torch
+    import invariant_token_logprobs_lm_amd as itl
+
+    H, W, y = s["H"], s["W"], s["y"]
+    n = min(chunk, H.shape[0])
+    d = H.shape[1]
+    V = W.shape[0]
+    Hc, yc = H[:n].contiguous(), y[:n].contiguous()
+    z = torch.empty((n, V), dtype=H.dtype, device=device)
+    ws = torch.empty(itl.lmhead_workspace_bytes(n, V), dtype=torch.uint8, device=device)
+    lp = torch.empty(n, dtype=torch.float32, device=device)
+    Wt = W.t()
+
+    def gemm():
+        torch.mm(Hc, Wt, out=z)
+
+    def fast():
+        torch.mm(Hc, Wt, out=z)
+        return torch.log_softmax(z.float(), dim=1).gather(1, yc.long()[:, None])[:, 0]
+
+    def ours():
+        itl.lmhead_logprob(Hc, W, yc, logprob=lp, workspace=ws, want_lse=False)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(calls):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / calls
+
+    ms_ours, ms_gemm, ms_fast = timed(ours), timed(gemm), timed(fast)
+    lp_fast = fast()
+    ours()
+    torch.cuda.synchronize()
+    gap = float((lp - lp_fast).abs().max())
+    del z
+    flop = 2.0 * d * V * n
+
+    def tf(ms):
+        return flop / (ms * 1e-3) / 1e12
+
+    log(f"[bench] prefill chunk of {n} tokens: invariant {ms_ours:.2f} ms ({tf(ms_ours):.0f} TFLOP/s), "
+        f"library GEMM alone {ms_gemm:.2f} ms ({tf(ms_gemm):.0f} TFLOP/s), "
+        f"GEMM + log_softmax + gather {ms_fast:.2f} ms")
+    return {
+        "workload": f"first {n} tokens of the batch in one call, {calls} calls per point",
+        "baseline": "torch.mm (hipBLASLt, bf16 logits) + log_softmax (fp32) + gather; not batch-invariant",
+        "ms_invariant": ms_ours, "ms_library_gemm_only": ms_gemm, "ms_library_path": ms_fast,
+        "tflops_invariant": tf(ms_ours), "tflops_library_gemm_only": tf(ms_gemm), "tflops_library_path": tf(ms_fast),
+        "invariant_over_library_path": ms_fast / ms_ours,
+        "max_abs_lp_gap_to_library_path": gap,
+    }
+
+
 def mismatch_leg(s, device, calls=20, n_demo=4096, batch=64):
     """The mismatch diagnostics: (1) itl_mismatch_stats timed on the whole
     batch (learner logprobs, the rollout record with the workload's lag
@@ -454,6 +520,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-mismatch", action="store_true")
     ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
@@ -531,6 +598,8 @@ def main():
         out["mismatch"] = mismatch_leg(s, device)
     if not args.no_fp8:
         out["fp8"] = fp8_leg(s, device)
+    if not args.no_prefill:
+        out["prefill"] = prefill_leg(s, device)
     del s
     torch.cuda.empty_cache()
     if not args.no_decode:
