@@ -9,7 +9,9 @@ log-sum-exp + gather), the group advantage and the REINFORCE Zero loss with
 its per-token coefficients. The default workload is the Qwen3-4B-shaped head
 (d = 2560, vocab = 151936, 32 responses of 2048..16384 tokens). The JSON line
 also carries a forward + backward figure on the large-MoE-shaped head
-(d = 7168, vocab = 129280) when the backward entry point is available.
+(d = 7168, vocab = 129280): with the forward's logits kept in HBM when they
+fit (159 GB), else with the backward recomputing them; both are timed when
+memory allows.
 
 Prints progress to stderr and ONE JSON line to stdout.
 """
@@ -143,6 +145,23 @@ def fwd_bwd_step(s, ev=None):
     if ev is not None:
         ev[0].record()
     itl.reinforce_zero_backward(s["H"], s["W"], s["y"], s["lse"], coef, dH=s["dH"], dW=s["dW"], workspace=s["bws"])
+    if ev is not None:
+        ev[1].record()
+
+
+def fwd_bwd_keep_step(s, ev=None):
+    """The same step with the forward's logits kept in HBM and the backward's
+    dlogits formed from them (no recomputed contraction; same bits)."""
+    import invariant_token_logprobs_lm_amd as itl
+
+    itl.lmhead_logprob_keep_logits(s["H"], s["W"], s["y"], logits=s["Z"], logprob=s["lp"], lse=s["lse"],
+                                   workspace=s["ws"])
+    A = itl.group_advantage(s["rewards"], s["goff"])
+    rl, L, coef = itl.reinforce_zero_loss(s["lp"], s["lpr"], A, s["roff"])
+    if ev is not None:
+        ev[0].record()
+    itl.reinforce_zero_backward_from_logits(s["H"], s["W"], s["y"], s["lse"], coef, s["Z"], dH=s["dH"], dW=s["dW"],
+                                            workspace=s["bws"])
     if ev is not None:
         ev[1].record()
 
@@ -628,7 +647,36 @@ def main():
             "unit": "sampled tokens/s (forward + backward)",
             "tflops_algorithmic": tf,
             "frac_bf16_peak": tf / PEAK_BF16_TFLOPS,
+            "path": "the backward recomputes the logits with the forward's contraction",
         }
+        # The same step with the logits kept (4 n_tok vocab bytes of HBM)
+        # when they fit beside everything else.
+        free, _ = torch.cuda.mem_get_info(device)
+        z_bytes = nb * ((wb.vocab + 3) // 4 * 4) * 4
+        if free > z_bytes + (8 << 30):
+            sb["Z"] = torch.empty((nb, (wb.vocab + 3) // 4 * 4), dtype=torch.float32, device=device)
+            ms_k, ms_kb, _ = time_steps(lambda ev: fwd_bwd_keep_step(sb, ev), bsteps, 1)
+            tfk = fl_alg / (ms_k * 1e-3) / 1e12
+            log(f"[bench] {wb.key} fwd+bwd step with kept logits {ms_k:.1f} ms (backward {ms_kb:.1f} ms) -> "
+                f"{nb / (ms_k * 1e-3):.0f} tokens/s, {tfk:.1f} TFLOP/s algorithmic "
+                f"({100 * tfk / PEAK_BF16_TFLOPS:.1f}% of bf16 peak)")
+            # The faster path is the leg's figure; the recomputing one stays beside it.
+            recompute = {k: out["fwd_bwd"][k] for k in ("ms_per_step", "ms_backward", "value", "tflops_algorithmic",
+                                                        "frac_bf16_peak")}
+            recompute["what"] = "the backward recomputes the logits with the forward's contraction"
+            out["fwd_bwd"].update({
+                "path": "kept logits: the forward also writes the fp32 logits and the backward forms its dlogits "
+                        "from them instead of recomputing the contraction (same dH and dW bits)",
+                "logits_bytes": z_bytes,
+                "ms_per_step": ms_k,
+                "ms_backward": ms_kb,
+                "value": nb / (ms_k * 1e-3),
+                "tflops_algorithmic": tfk,
+                "frac_bf16_peak": tfk / PEAK_BF16_TFLOPS,
+                "recompute": recompute,
+            })
+        else:
+            log(f"[bench] kept-logits step skipped: {z_bytes / 2**30:.0f} GiB of logits, {free / 2**30:.0f} GiB free")
         del sb
         torch.cuda.empty_cache()
     if not args.no_cpu_baseline:

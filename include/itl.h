@@ -109,6 +109,24 @@ itl_status itl_lmhead_logprob(const void* H, const void* W, itl_dtype dtype,
                               const int32_t* tokens, float* logprob, float* lse,
                               void* workspace, size_t workspace_bytes, void* stream);
 
+/* The same call as itl_lmhead_logprob, with the same logprob and lse bits,
+ * that also keeps the head's logits for the backward [RZ] (the gradient of
+ * the loss through the log-softmax needs every z[t, v] once more):
+ *   logits[t * ld_logits + v] = z[t, v]     fp32, 0 <= t < n_tok, 0 <= v < vocab
+ * the exact fp32 accumulator values the log-sum-exp folds. logits is a
+ * caller-owned device buffer of n_tok * ld_logits floats, 16-byte aligned,
+ * with ld_logits >= vocab and a multiple of 4 (else ITL_ERR_INVALID_ARG)
+ * and at most 8,388,607 (else ITL_ERR_UNSUPPORTED); entries v >= vocab of a
+ * row are left untouched. It is large (about
+ * 4 n_tok vocab bytes: 159 GB for 308,010 tokens of a 129,280-row head), a
+ * trade of HBM for the contraction itl_reinforce_zero_backward would
+ * otherwise repeat; workspace as for itl_lmhead_logprob. */
+itl_status itl_lmhead_logprob_keep_logits(const void* H, const void* W, itl_dtype dtype,
+                                          int64_t n_tok, int64_t d, int64_t vocab,
+                                          const int32_t* tokens, float* logprob, float* lse,
+                                          float* logits, int64_t ld_logits,
+                                          void* workspace, size_t workspace_bytes, void* stream);
+
 /* Group-mean baseline [RZ]: advantages[i] = rewards[i] - mean of the
  * rewards of i's group. Group g owns responses group_offsets[g] ..
  * group_offsets[g+1]-1; group_offsets int32 [n_groups+1], starting at 0 and
@@ -161,6 +179,20 @@ itl_status itl_reinforce_zero_backward(const void* H, const void* W, itl_dtype d
                                        const int32_t* tokens, const float* lse, const float* coef,
                                        float* dH, float* dW,
                                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* itl_reinforce_zero_backward with the dlogits formed from kept logits
+ * (written by itl_lmhead_logprob_keep_logits for the same H, W, tokens)
+ * instead of recomputing the contraction [RZ]: G, dH and dW have the same
+ * bits as itl_reinforce_zero_backward's, since the kept values are the
+ * recompute's values. logits / ld_logits as there (not read when n_tok is
+ * 0); every other argument, the workspace size and the errors as for
+ * itl_reinforce_zero_backward. */
+itl_status itl_reinforce_zero_backward_from_logits(const void* H, const void* W, itl_dtype dtype,
+                                                   int64_t n_tok, int64_t d, int64_t vocab,
+                                                   const int32_t* tokens, const float* lse, const float* coef,
+                                                   const float* logits, int64_t ld_logits,
+                                                   float* dH, float* dW,
+                                                   void* workspace, size_t workspace_bytes, void* stream);
 
 /* Per-row FP8 quantisation [FP8] (OCP E4M3: bias 7, no infinities, largest
  * finite value 448). For each row r of X [n_rows, d] (dtype bf16 or fp32):

@@ -58,6 +58,9 @@ def _load():
         "itl_lmhead_logprob_workspace_bytes": (_size, [_i64, _i64]),
         "itl_lmhead_logprob": (ctypes.c_int, [_c_void_p, _c_void_p, ctypes.c_int, _i64, _i64, _i64, _c_void_p,
                                               _c_void_p, _c_void_p, _c_void_p, _size, _c_void_p]),
+        "itl_lmhead_logprob_keep_logits": (ctypes.c_int, [_c_void_p, _c_void_p, ctypes.c_int, _i64, _i64, _i64,
+                                                          _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64,
+                                                          _c_void_p, _size, _c_void_p]),
         "itl_group_advantage": (ctypes.c_int, [_c_void_p, _c_void_p, _i32, _i32, _c_void_p, _c_void_p]),
         "itl_reinforce_zero_loss": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _i64,
                                                    _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
@@ -65,6 +68,10 @@ def _load():
         "itl_reinforce_zero_backward": (ctypes.c_int, [_c_void_p, _c_void_p, ctypes.c_int, _i64, _i64, _i64,
                                                        _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                                        _c_void_p, _size, _c_void_p]),
+        "itl_reinforce_zero_backward_from_logits": (ctypes.c_int, [_c_void_p, _c_void_p, ctypes.c_int, _i64, _i64,
+                                                                   _i64, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                                                   _i64, _c_void_p, _c_void_p, _c_void_p, _size,
+                                                                   _c_void_p]),
         "itl_quantize_rows_fp8": (ctypes.c_int, [_c_void_p, ctypes.c_int, _i64, _i64, _c_void_p, _c_void_p,
                                                  _c_void_p]),
         "itl_lmhead_logprob_fp8": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i64, _i64,
@@ -93,10 +100,12 @@ lib = _load()
 EXPORTS = (
     "itl_lmhead_logprob_workspace_bytes",
     "itl_lmhead_logprob",
+    "itl_lmhead_logprob_keep_logits",
     "itl_group_advantage",
     "itl_reinforce_zero_loss",
     "itl_reinforce_zero_backward_workspace_bytes",
     "itl_reinforce_zero_backward",
+    "itl_reinforce_zero_backward_from_logits",
     "itl_quantize_rows_fp8",
     "itl_lmhead_logprob_fp8",
     "itl_quantize_rows_mxfp4",
@@ -183,6 +192,41 @@ def lmhead_logprob(H, W, tokens, *, logprob=None, lse=None, workspace=None, want
     return logprob, lse
 
 
+def lmhead_logprob_keep_logits(H, W, tokens, *, logits=None, logprob=None, lse=None, workspace=None):
+    """lmhead_logprob (same bits) that also returns the logits z [n_tok, ld]
+    fp32 (ld = vocab rounded up to a multiple of 4 when allocated here; a
+    caller's buffer may have any ld >= vocab that is a multiple of 4).
+    Returns (logprob, lse, logits)."""
+    _need(H, "H", tuple(_HEAD_DTYPES), ndim=2)
+    _need(W, "W", (H.dtype,), device=H.device, ndim=2)
+    _need(tokens, "tokens", (torch.int32,), device=H.device, ndim=1)
+    n_tok, d = H.shape
+    vocab = W.shape[0]
+    if W.shape[1] != d or tokens.shape[0] != n_tok:
+        raise ValueError(f"shape mismatch: H {tuple(H.shape)}, W {tuple(W.shape)}, tokens {tuple(tokens.shape)}")
+    if logits is None:
+        logits = torch.empty((n_tok, (vocab + 3) // 4 * 4), dtype=torch.float32, device=H.device)
+    _need(logits, "logits", (torch.float32,), device=H.device, ndim=2)
+    if logits.shape[0] != n_tok:
+        raise ValueError(f"logits must have {n_tok} rows")
+    if logprob is None:
+        logprob = torch.empty(n_tok, dtype=torch.float32, device=H.device)
+    if lse is None:
+        lse = torch.empty(n_tok, dtype=torch.float32, device=H.device)
+    for name, t in (("logprob", logprob), ("lse", lse)):
+        _need(t, name, (torch.float32,), device=H.device, ndim=1)
+        if t.shape[0] != n_tok:
+            raise ValueError(f"{name} must have {n_tok} elements")
+    need = lmhead_workspace_bytes(n_tok, vocab)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=H.device)
+    _need(workspace, "workspace", (torch.uint8,), device=H.device)
+    _check(lib.itl_lmhead_logprob_keep_logits(_ptr(H), _ptr(W), _HEAD_DTYPES[H.dtype], n_tok, d, vocab, _ptr(tokens),
+                                              _ptr(logprob), _ptr(lse), _ptr(logits), logits.shape[1],
+                                              _ptr(workspace), workspace.numel(), _stream(H.device)))
+    return logprob, lse, logits
+
+
 def group_advantage(rewards, group_offsets, *, advantages=None):
     """advantages[i] = rewards[i] - mean reward of i's group (fp32)."""
     _need(rewards, "rewards", (torch.float32,), ndim=1)
@@ -247,6 +291,38 @@ def reinforce_zero_backward(H, W, tokens, lse, coef, *, dH=None, dW=None, worksp
     _check(lib.itl_reinforce_zero_backward(_ptr(H), _ptr(W), _HEAD_DTYPES[H.dtype], n_tok, d, vocab, _ptr(tokens),
                                            _ptr(lse), _ptr(coef), _ptr(dH), _ptr(dW), _ptr(workspace),
                                            workspace.numel(), _stream(dev)))
+    return dH, dW
+
+
+def reinforce_zero_backward_from_logits(H, W, tokens, lse, coef, logits, *, dH=None, dW=None, workspace=None):
+    """reinforce_zero_backward (same bits) with the dlogits formed from the
+    logits kept by lmhead_logprob_keep_logits ([n_tok, ld] fp32)."""
+    _need(H, "H", tuple(_HEAD_DTYPES), ndim=2)
+    dev = H.device
+    _need(W, "W", (H.dtype,), device=dev, ndim=2)
+    _need(tokens, "tokens", (torch.int32,), device=dev, ndim=1)
+    _need(lse, "lse", (torch.float32,), device=dev, ndim=1)
+    _need(coef, "coef", (torch.float32,), device=dev, ndim=1)
+    _need(logits, "logits", (torch.float32,), device=dev, ndim=2)
+    n_tok, d = H.shape
+    vocab = W.shape[0]
+    if (W.shape[1] != d or tokens.shape[0] != n_tok or lse.shape[0] != n_tok or coef.shape[0] != n_tok
+            or logits.shape[0] != n_tok):
+        raise ValueError("shape mismatch between H, W, tokens, lse, coef and logits")
+    if dH is None:
+        dH = torch.empty((n_tok, d), dtype=torch.float32, device=dev)
+    if dW is None:
+        dW = torch.empty((vocab, d), dtype=torch.float32, device=dev)
+    _need(dH, "dH", (torch.float32,), device=dev, ndim=2)
+    _need(dW, "dW", (torch.float32,), device=dev, ndim=2)
+    need = backward_workspace_bytes(n_tok, d, vocab, H.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", (torch.uint8,), device=dev)
+    _check(lib.itl_reinforce_zero_backward_from_logits(_ptr(H), _ptr(W), _HEAD_DTYPES[H.dtype], n_tok, d, vocab,
+                                                       _ptr(tokens), _ptr(lse), _ptr(coef), _ptr(logits),
+                                                       logits.shape[1], _ptr(dH), _ptr(dW), _ptr(workspace),
+                                                       workspace.numel(), _stream(dev)))
     return dH, dW
 
 

@@ -70,8 +70,43 @@ itl_status itl_lmhead_logprob(const void* H, const void* W, itl_dtype dtype, int
     return fail(ITL_ERR_WORKSPACE, "workspace missing or smaller than itl_lmhead_logprob_workspace_bytes()");
   if (misaligned(workspace)) return fail(ITL_ERR_WORKSPACE, "workspace must be 256-byte aligned");
   hipError_t e = itl::launch_lmhead_logprob(H, W, (int)dtype, (int)n_tok, (int)d, (int)vocab, tokens, logprob, lse,
-                                            workspace, static_cast<hipStream_t>(stream));
+                                            nullptr, 0, workspace, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ITL_OK : hip_fail(e, "itl_lmhead_logprob");
+}
+
+namespace {
+
+// The kept-logits buffer: [n_tok, ld] fp32, ld >= vocab and a multiple of 4,
+// 16-byte aligned, every offset t * ld + v addressable.
+itl_status check_logits(const float* logits, int64_t ld, int64_t n_tok, int64_t vocab) {
+  if (!logits) return fail(ITL_ERR_INVALID_ARG, "null logits");
+  if (ld < vocab || ld % 4 != 0) return fail(ITL_ERR_INVALID_ARG, "ld_logits must be >= vocab and a multiple of 4");
+  // 128 token rows of the buffer must be addressable with 32-bit offsets
+  if (ld > (int64_t)(UINT32_MAX / (4u * 128u))) return fail(ITL_ERR_UNSUPPORTED, "ld_logits too large");
+  if ((reinterpret_cast<uintptr_t>(logits) & 15) != 0) return fail(ITL_ERR_INVALID_ARG, "logits must be 16-byte aligned");
+  if (n_tok > 0 && ld > (INT64_MAX / 8) / n_tok) return fail(ITL_ERR_INVALID_ARG, "n_tok * ld_logits overflows");
+  return ITL_OK;
+}
+
+}  // namespace
+
+itl_status itl_lmhead_logprob_keep_logits(const void* H, const void* W, itl_dtype dtype, int64_t n_tok, int64_t d,
+                                          int64_t vocab, const int32_t* tokens, float* logprob, float* lse,
+                                          float* logits, int64_t ld_logits, void* workspace, size_t workspace_bytes,
+                                          void* stream) {
+  g_last_error.clear();
+  itl_status st = check_head(dtype, n_tok, d, vocab);
+  if (st != ITL_OK) return st;
+  if (n_tok == 0) return ITL_OK;
+  if (!H || !W || !tokens || !logprob) return fail(ITL_ERR_INVALID_ARG, "null H, W, tokens or logprob");
+  st = check_logits(logits, ld_logits, n_tok, vocab);
+  if (st != ITL_OK) return st;
+  if (!workspace || workspace_bytes < itl::lmhead_workspace_bytes(n_tok, vocab))
+    return fail(ITL_ERR_WORKSPACE, "workspace missing or smaller than itl_lmhead_logprob_workspace_bytes()");
+  if (misaligned(workspace)) return fail(ITL_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  hipError_t e = itl::launch_lmhead_logprob(H, W, (int)dtype, (int)n_tok, (int)d, (int)vocab, tokens, logprob, lse,
+                                            logits, (long long)ld_logits, workspace, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ITL_OK : hip_fail(e, "itl_lmhead_logprob_keep_logits");
 }
 
 itl_status itl_group_advantage(const float* rewards, const int32_t* group_offsets, int32_t n_groups, int32_t n_resp,
@@ -105,10 +140,11 @@ size_t itl_reinforce_zero_backward_workspace_bytes(int64_t n_tok, int64_t d, int
   return itl::backward_workspace_bytes(n_tok, d, vocab, (int)dtype);
 }
 
-itl_status itl_reinforce_zero_backward(const void* H, const void* W, itl_dtype dtype, int64_t n_tok, int64_t d,
-                                       int64_t vocab, const int32_t* tokens, const float* lse, const float* coef,
-                                       float* dH, float* dW, void* workspace, size_t workspace_bytes, void* stream) {
-  g_last_error.clear();
+namespace {
+
+itl_status backward(const void* H, const void* W, itl_dtype dtype, int64_t n_tok, int64_t d, int64_t vocab,
+                    const int32_t* tokens, const float* lse, const float* coef, const float* logits, int64_t ld,
+                    float* dH, float* dW, void* workspace, size_t workspace_bytes, void* stream, const char* name) {
   itl_status st = check_head(dtype, n_tok, d, vocab);
   if (st != ITL_OK) return st;
   if (!W || !dW) return fail(ITL_ERR_INVALID_ARG, "null W or dW");
@@ -120,8 +156,33 @@ itl_status itl_reinforce_zero_backward(const void* H, const void* W, itl_dtype d
     return fail(ITL_ERR_WORKSPACE, "workspace missing or smaller than itl_reinforce_zero_backward_workspace_bytes()");
   if (need > 0 && misaligned(workspace)) return fail(ITL_ERR_WORKSPACE, "workspace must be 256-byte aligned");
   hipError_t e = itl::launch_reinforce_zero_backward(H, W, (int)dtype, (int)n_tok, (int)d, (int)vocab, tokens, lse,
-                                                     coef, dH, dW, workspace, static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? ITL_OK : hip_fail(e, "itl_reinforce_zero_backward");
+                                                     coef, logits, (long long)ld, dH, dW, workspace,
+                                                     static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ITL_OK : hip_fail(e, name);
+}
+
+}  // namespace
+
+itl_status itl_reinforce_zero_backward_from_logits(const void* H, const void* W, itl_dtype dtype, int64_t n_tok,
+                                                   int64_t d, int64_t vocab, const int32_t* tokens, const float* lse,
+                                                   const float* coef, const float* logits, int64_t ld_logits,
+                                                   float* dH, float* dW, void* workspace, size_t workspace_bytes,
+                                                   void* stream) {
+  g_last_error.clear();
+  if (n_tok > 0) {
+    itl_status st = check_logits(logits, ld_logits, n_tok, vocab);
+    if (st != ITL_OK) return st;
+  }
+  return backward(H, W, dtype, n_tok, d, vocab, tokens, lse, coef, n_tok > 0 ? logits : nullptr, ld_logits, dH, dW,
+                  workspace, workspace_bytes, stream, "itl_reinforce_zero_backward_from_logits");
+}
+
+itl_status itl_reinforce_zero_backward(const void* H, const void* W, itl_dtype dtype, int64_t n_tok, int64_t d,
+                                       int64_t vocab, const int32_t* tokens, const float* lse, const float* coef,
+                                       float* dH, float* dW, void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  return backward(H, W, dtype, n_tok, d, vocab, tokens, lse, coef, nullptr, 0, dH, dW, workspace, workspace_bytes,
+                  stream, "itl_reinforce_zero_backward");
 }
 
 itl_status itl_quantize_rows_fp8(const void* X, itl_dtype dtype, int64_t n_rows, int64_t d, uint8_t* Xq, float* scale,

@@ -17,6 +17,10 @@
 //   1. dlogits: z recomputed by the forward's contraction, g written twice:
 //      token-major Gd [chunk, Vpad] (for dH) and vocabulary-major GdT
 //      [Vpad, chunk] (for dW); padding rows and columns hold zeros.
+//      When the caller kept the forward's logits (fp32, the same bits the
+//      recompute gives), g is formed from them instead: one pass over HBM in
+//      place of a full contraction, with g's arithmetic unchanged, so dH and
+//      dW have the same bits either way.
 //   2. dH rows of the chunk = Gd W^T-rows (K = Vpad ascending) + sampled term.
 //   3. dW += GdT H^T-rows of the chunk (K = the chunk's tokens ascending).
 // dW starts as zeros plus the sampled term; chunks are added in token order.
@@ -206,6 +210,86 @@ __global__ __launch_bounds__(kThreads, 1) void dlogits_kernel(
   run_tiles<kDtype>(smem, L, row_bytes, tile_begin, tile_end, row_bytes / kStepBytes, w_rsrc, hr, epilogue);
 }
 
+// 1'. dlogits from kept logits: the same g as dlogits_kernel, for a tile of
+// 128 tokens x 128 vocabulary rows. z is read token-major (16 bytes per
+// lane, a token row's 512 contiguous bytes per 32 lanes), g is written to
+// Gd directly and to GdT through an LDS transpose (each of GdT's rows gets
+// the tile's 128 tokens contiguously). Tokens at or past len and rows at or
+// past vocab get g = 0, as in dlogits_kernel (their z is never read).
+constexpr int kGTile = 128;
+
+template <int kDtype>
+__global__ __launch_bounds__(256) void dlogits_from_logits_kernel(
+    const float* __restrict__ logits, long long ld, int len, int vocab, int vpad, const float* __restrict__ lse,
+    const float* __restrict__ coef, typename Elem<kDtype>::T* __restrict__ Gd,
+    typename Elem<kDtype>::T* __restrict__ GdT) {
+  using E = Elem<kDtype>;
+  using T = typename E::T;
+  // The transposed tile: element (v, t) at row v; bf16 packs tokens 2 j and
+  // 2 j + 1 into word j. One pad word per row spreads a column over banks.
+  constexpr int kPack = 4 / (int)sizeof(T);  // tokens per 32-bit word
+  constexpr int kRowWords = kGTile / kPack + 1;
+  __shared__ uint32_t tile[kGTile * kRowWords];
+  const int v0 = blockIdx.x * kGTile;
+  const int t0 = blockIdx.y * kGTile;
+  const int vq = threadIdx.x & 31;  // vocabulary rows v0 + 4 vq .. + 3
+  const int tr = threadIdx.x >> 5;  // 0..7
+  const int v = v0 + 4 * vq;
+  for (int p = 0; p < kGTile / (8 * kPack); ++p) {
+    T g[kPack][4];
+#pragma unroll
+    for (int k = 0; k < kPack; ++k) {
+      const int tl = (tr + 8 * p) * kPack + k;  // token within the tile
+      const int t = t0 + tl;
+      if (t < len) {
+        const float l2e_lse = lse[t] * kLog2e;
+        const float negc = -coef[t];
+        const float* row = logits + (size_t)t * (size_t)ld;
+        floatx4 z;
+        if (v + 3 < vocab) {
+          z = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(row + v));
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) z[r] = v + r < vocab ? row[v + r] : 0.0f;
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float pr = fast_exp2(z[r] * kLog2e - l2e_lse);
+          g[k][r] = E::from_f(v + r < vocab ? negc * pr : 0.0f);
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) g[k][r] = E::from_f(0.0f);
+      }
+      if constexpr (kDtype == 0) {
+        uint2 pk;
+        pk.x = (uint32_t)g[k][0] | ((uint32_t)g[k][1] << 16);
+        pk.y = (uint32_t)g[k][2] | ((uint32_t)g[k][3] << 16);
+        *reinterpret_cast<uint2*>(Gd + (size_t)t * vpad + v) = pk;
+      } else {
+        *reinterpret_cast<float4*>(Gd + (size_t)t * vpad + v) = make_float4(g[k][0], g[k][1], g[k][2], g[k][3]);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      uint32_t w;
+      if constexpr (kDtype == 0) w = (uint32_t)g[0][r] | ((uint32_t)g[1][r] << 16);
+      else w = __float_as_uint(g[0][r]);
+      tile[(4 * vq + r) * kRowWords + tr + 8 * p] = w;
+    }
+  }
+  __syncthreads();
+  // GdT rows v0 .. v0 + 127, tokens t0 .. t0 + 127: 16 bytes per lane.
+  constexpr int kLanesPerRow = kGTile / kPack / 4;  // 16 (bf16) or 32 (fp32)
+  constexpr int kRowsPerPass = 256 / kLanesPerRow;
+  const int j = threadIdx.x % kLanesPerRow;
+  for (int vr = threadIdx.x / kLanesPerRow; vr < kGTile; vr += kRowsPerPass) {
+    const uint32_t* src = tile + vr * kRowWords + 4 * j;
+    const uint4 w = make_uint4(src[0], src[1], src[2], src[3]);
+    *reinterpret_cast<uint4*>(reinterpret_cast<char*>(GdT + (size_t)(v0 + vr) * kBwdChunk + t0) + 16 * j) = w;
+  }
+}
+
 // 2. dH for the chunk. A = W^T tile (d rows, K = Vpad), B = Gd token block.
 // Grid: token blocks (fast) x d tiles (slow). Lane l's accumulators are d
 // rows of token t0 + 128 wt + 32 bn + (l mod 32).
@@ -364,8 +448,8 @@ BwdLayout bwd_layout(long long n_tok, long long d, long long vocab, int es) {
 
 template <int kDtype>
 hipError_t run_backward(const void* H, const void* W, int n_tok, int d, int vocab, const int32_t* tokens,
-                        const float* lse, const float* coef, float* dH, float* dW, void* workspace,
-                        hipStream_t stream) {
+                        const float* lse, const float* coef, const float* logits, long long ld, float* dH,
+                        float* dW, void* workspace, hipStream_t stream) {
   using E = Elem<kDtype>;
   using T = typename E::T;
   const int es = E::kSize;
@@ -425,9 +509,14 @@ hipError_t run_backward(const void* H, const void* W, int n_tok, int d, int voca
     const int kpad = (int)round_up(len, kBT);
     const int n_tb = kpad / kBT;
     const char* Hc = static_cast<const char*>(H) + (size_t)c0 * row_bytes;
-    hipLaunchKernelGGL(dlogits_kernel<kDtype>, dim3((unsigned)(n_tb * n_groups)), dim3(kThreads), 0, stream, Hc, len,
-                       static_cast<const char*>(W), row_bytes, vocab, vpad, n_tb, S, G, tokens + c0, lse + c0, coef + c0,
-                       Gd, GdT);
+    if (logits)
+      hipLaunchKernelGGL(dlogits_from_logits_kernel<kDtype>, dim3((unsigned)(vpad / kGTile), (unsigned)(kpad / kGTile)),
+                         dim3(256), 0, stream, logits + (size_t)c0 * (size_t)ld, ld, len, vocab, vpad, lse + c0,
+                         coef + c0, Gd, GdT);
+    else
+      hipLaunchKernelGGL(dlogits_kernel<kDtype>, dim3((unsigned)(n_tb * n_groups)), dim3(kThreads), 0, stream, Hc,
+                         len, static_cast<const char*>(W), row_bytes, vocab, vpad, n_tb, S, G, tokens + c0, lse + c0,
+                         coef + c0, Gd, GdT);
     ITL_CHECK_LAUNCH();
     hipLaunchKernelGGL(dh_kernel<kDtype>, dim3((unsigned)(n_tb * n_dt)), dim3(kThreads), 0, stream,
                        reinterpret_cast<const char*>(WT), reinterpret_cast<const char*>(Gd), vpad, d, vocab, len, n_tb, n_dt,
@@ -453,11 +542,12 @@ size_t backward_workspace_bytes(long long n_tok, long long d, long long vocab, i
 }
 
 hipError_t launch_reinforce_zero_backward(const void* H, const void* W, int dtype, int n_tok, int d, int vocab,
-                                          const int32_t* tokens, const float* lse, const float* coef, float* dH,
-                                          float* dW, void* workspace, hipStream_t stream) {
+                                          const int32_t* tokens, const float* lse, const float* coef,
+                                          const float* logits, long long ld, float* dH, float* dW, void* workspace,
+                                          hipStream_t stream) {
   if (dtype == 0)
-    return run_backward<0>(H, W, n_tok, d, vocab, tokens, lse, coef, dH, dW, workspace, stream);
-  return run_backward<1>(H, W, n_tok, d, vocab, tokens, lse, coef, dH, dW, workspace, stream);
+    return run_backward<0>(H, W, n_tok, d, vocab, tokens, lse, coef, logits, ld, dH, dW, workspace, stream);
+  return run_backward<1>(H, W, n_tok, d, vocab, tokens, lse, coef, logits, ld, dH, dW, workspace, stream);
 }
 
 }  // namespace itl

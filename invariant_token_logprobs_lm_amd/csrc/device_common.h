@@ -8,7 +8,13 @@ namespace itl {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef int int4v __attribute__((ext_vector_type(4)));
+
+// Cache policy of the buffer stores of data read back much later by
+// another kernel: the non-temporal bit (gfx9 SLC position), so the stores
+// do not displace the operands the workgroups of an XCD share in L2.
+constexpr int kStreamStore = 2;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;

@@ -12,9 +12,10 @@ namespace itl {
 // pairs, then the per-token sampled logit.
 size_t lmhead_workspace_bytes(long long n_tok, long long vocab);
 
+// logits (nullable): also write z[t, v] at logits[t * ld + v] for v < vocab.
 hipError_t launch_lmhead_logprob(const void* H, const void* W, int dtype, int n_tok, int d, int vocab,
-                                 const int32_t* tokens, float* logprob, float* lse, void* workspace,
-                                 hipStream_t stream);
+                                 const int32_t* tokens, float* logprob, float* lse, float* logits, long long ld,
+                                 void* workspace, hipStream_t stream);
 
 // Merge each token's n_parts (max, sumexp) partials (slice-major) into its
 // logprob (z_y - lse) and lse (nullable).
@@ -35,9 +36,12 @@ size_t backward_workspace_bytes(long long n_tok, long long d, long long vocab, i
 // addressable by 32-bit buffer offsets over 256-row tiles).
 constexpr long long kBwdMaxVocab = (1LL << 31) / (256LL * 4) - 256;
 
+// logits (nullable): the forward's z[t, v] at logits[t * ld + v]; the dlogits
+// are then formed from them instead of recomputing the contraction (same bits).
 hipError_t launch_reinforce_zero_backward(const void* H, const void* W, int dtype, int n_tok, int d, int vocab,
                                           const int32_t* tokens, const float* lse, const float* coef,
-                                          float* dH, float* dW, void* workspace, hipStream_t stream);
+                                          const float* logits, long long ld, float* dH, float* dW, void* workspace,
+                                          hipStream_t stream);
 
 hipError_t launch_quantize_rows_fp8(const void* X, int dtype, long long n_rows, int d, uint8_t* Xq, float* scale,
                                     hipStream_t stream);

@@ -23,6 +23,10 @@
 // whether a workgroup walks one slice (small batches: every CU streams W) or
 // several (large batches: fewer, longer workgroups).
 // Kernel 2 (lse_combine) merges a token's 2 S partials in a fixed order.
+// With kKeep the same kernels also write every logit z[t, v] (fp32, row
+// stride ld) from the accumulators the fold reads, for a backward that
+// forms the dlogits from them instead of recomputing the contraction; the
+// arithmetic, and so every partial and logprob, is unchanged.
 //
 // Why the bits do not depend on the batch: the tile shapes, K order, slice
 // width and every reduction tree are compile-time constants; a token's
@@ -43,11 +47,94 @@ namespace itl {
 
 namespace {
 
-template <int kDtype>
+// Kept logits are written with buffer stores against a range that ends at
+// the wavefront's last valid token row, so rows past n_tok are dropped by
+// the hardware instead of a branch. LogitRows: the range (SGPRs) and this
+// lane's row offset in bytes, (col * ld + 4 half) * 4 (ld * 4 * 128 < 2^32).
+struct LogitRows {
+  __amdgpu_buffer_rsrc_t rsrc;
+  uint32_t voff;
+  uint32_t bn_stride;  // bytes between the token columns of blocks bn and bn + 1 (32 rows)
+};
+
+// Built in each epilogue, not once per kernel: kept live across the K loop,
+// these registers would push the loop's operands into scratch. The empty asm
+// makes the inputs opaque, so the compiler cannot hoist the build out of
+// the tile loop.
+__device__ __forceinline__ LogitRows logit_rows(float* logits, long long ld, int tok_first, int n_rows, int n_tok,
+                                                int col, int half) {
+  asm volatile("" : "+s"(tok_first));
+  LogitRows r;
+  const int valid = max(0, min(n_rows, n_tok - tok_first));
+  // Raw buffer (stride 0), 32-bit data format: the same descriptor word 3 as
+  // the engine's operand loads. The fields are wave-uniform by construction;
+  // readfirstlane tells the compiler so (a descriptor it takes for divergent
+  // would turn every store into a loop over the lanes' distinct values).
+  const uint64_t base = reinterpret_cast<uint64_t>(logits + (size_t)tok_first * (size_t)ld);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)base);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
+  const int nbytes = __builtin_amdgcn_readfirstlane((int)((uint32_t)valid * (uint32_t)ld * 4u));
+  r.rsrc = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(((uint64_t)hi << 32) | lo), 0, nbytes,
+                                             0x00020000);
+  r.voff = ((uint32_t)col * (uint32_t)ld + 4u * (uint32_t)half) * 4u;
+  r.bn_stride = __builtin_amdgcn_readfirstlane(32u * (uint32_t)ld * 4u);
+  return r;
+}
+
+// Write this lane's 16 logits of a 32 x 32 block: token column bn of the
+// rows, vocabulary rows v0 + 4 half + 8 i + r (r < 4) from register 4 i + r
+// (v0 = the block's first row, the same for the whole wavefront). Four
+// consecutive rows are 16 contiguous bytes of the token's row. In the
+// vocabulary's last tile, rows at or past the vocabulary are not written.
+// Streaming stores: the logits are read back much later by another kernel,
+// and the L2 is better kept for the operands the workgroups share.
+template <int I, class kPartial>
+__device__ __forceinline__ void store_quad(const LogitRows& rows, uint32_t voff, int v0, int half, int vocab,
+                                           const floatx16& z, kPartial) {
+  const uint32_t so = (uint32_t)(v0 + 8 * I) * 4u;
+  if constexpr (!kPartial::value) {
+    __builtin_amdgcn_raw_buffer_store_b128(
+        __builtin_bit_cast(int4v, __builtin_shufflevector(z, z, 4 * I, 4 * I + 1, 4 * I + 2, 4 * I + 3)), rows.rsrc,
+        voff, so, kStreamStore);
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (v0 + 8 * I + 4 * half + r < vocab)
+        __builtin_amdgcn_raw_buffer_store_b32((int)__float_as_uint(z[4 * I + r]), rows.rsrc, voff + 4u * r, so,
+                                              kStreamStore);
+  }
+}
+
+template <class kPartial>
+__device__ __forceinline__ void store_logits(const LogitRows& rows, int bn, int v0, int half, int vocab,
+                                             const floatx16& z, kPartial partial) {
+  const uint32_t voff = rows.voff + (uint32_t)bn * rows.bn_stride;
+  store_quad<0>(rows, voff, v0, half, vocab, z, partial);
+  store_quad<1>(rows, voff, v0, half, vocab, z, partial);
+  store_quad<2>(rows, voff, v0, half, vocab, z, partial);
+  store_quad<3>(rows, voff, v0, half, vocab, z, partial);
+}
+
+// Fold one accumulator block, writing its logits first when kKeep.
+template <bool kKeep, class kPartial>
+__device__ __forceinline__ void fold_keep(Col& c, const floatx16& a, int bm, int bn, int vw, int half, int vocab,
+                                          kPartial partial, const LogitRows& rows) {
+  if constexpr (kKeep) {
+    floatx16 z;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) z[i] = acc_read(a, i);
+    store_logits(rows, bn, vw + bm * 32, half, vocab, z, partial);
+    fold_values(c, z, bm, vw, half, vocab, partial);
+  } else {
+    fold_block(c, a, bm, vw, half, vocab, partial);
+  }
+}
+
+template <int kDtype, bool kKeep>
 __global__ __launch_bounds__(kThreads, 1) void lmhead_lse_partial_kernel(
     const char* __restrict__ H, const char* __restrict__ W, const int32_t* __restrict__ tokens, int n_tok,
     int row_bytes, int vocab, int n_tb, int n_slices, int group, float2* __restrict__ part,
-    float* __restrict__ zy_out) {
+    float* __restrict__ zy_out, float* __restrict__ logits, long long ld) {
   __shared__ uint4 smem[kEngineSmemChunks];
   const Lanes L = lanes();
   const int wv = L.wv, wt = L.wt, half = L.half, col = L.col;
@@ -82,11 +169,13 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_lse_partial_kernel(
   auto epilogue = [&](int tile, floatx16 (&acc)[4][4]) {
     const int vw = tile * kBV + wv * 128;
     mfma_result_wait();
+    LogitRows rows{};
+    if constexpr (kKeep) rows = logit_rows(logits, ld, t0 + wt * 128, 128, n_tok, col, half);
     auto fold_tile = [&](auto partial) {
 #pragma unroll
       for (int bn = 0; bn < 4; ++bn)
 #pragma unroll
-        for (int bm = 0; bm < 4; ++bm) fold_block(c[bn], acc[bm][bn], bm, vw, half, vocab, partial);
+        for (int bm = 0; bm < 4; ++bm) fold_keep<kKeep>(c[bn], acc[bm][bn], bm, bn, vw, half, vocab, partial, rows);
     };
     if (tile * kBV + kBV > vocab) fold_tile(std::true_type{});  // only the vocabulary's last tile
     else fold_tile(std::false_type{});
@@ -112,10 +201,11 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_lse_partial_kernel(
 // Lane l of wavefront (wv, wt) holds token t0 + 32 wt + (l mod 32) against
 // the same W rows, with the same fold, as in lmhead_lse_partial_kernel, so
 // the partials (and the logprobs) have the same bits.
-template <int kDtype>
+template <int kDtype, bool kKeep>
 __global__ __launch_bounds__(kThreads, 1) void lmhead_lse_partial_narrow_kernel(
     const char* __restrict__ H, const char* __restrict__ W, const int32_t* __restrict__ tokens, int n_tok,
-    int row_bytes, int vocab, int n_slices, float2* __restrict__ part, float* __restrict__ zy_out) {
+    int row_bytes, int vocab, int n_slices, float2* __restrict__ part, float* __restrict__ zy_out,
+    float* __restrict__ logits, long long ld) {
   __shared__ uint4 smem[kEngineSmemChunks];
   const Lanes L = lanes();
   const int wv = L.wv, wt = L.wt, half = L.half, col = L.col;
@@ -136,12 +226,13 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_lse_partial_narrow_kernel(
     return rsrc_words(W + (size_t)v0 * row_bytes, (uint32_t)min(kBV, vocab - v0) * row_bytes);
   };
   const int4v hr = rsrc_words(H + (size_t)t0 * row_bytes, (uint32_t)min(kNarrowBRows, n_tok - t0) * row_bytes);
+  const LogitRows rows = logit_rows(logits, ld, t0 + wt * 32, 32, n_tok, col, half);
   auto epilogue = [&](int tile, floatx16 (&acc)[4]) {
     const int vw = tile * kBV + wv * 128;
     mfma_result_wait();
     auto fold_tile = [&](auto partial) {
 #pragma unroll
-      for (int bm = 0; bm < 4; ++bm) fold_block(c, acc[bm], bm, vw, half, vocab, partial);
+      for (int bm = 0; bm < 4; ++bm) fold_keep<kKeep>(c, acc[bm], bm, 0, vw, half, vocab, partial, rows);
     };
     if (tile * kBV + kBV > vocab) fold_tile(std::true_type{});
     else fold_tile(std::false_type{});
@@ -212,35 +303,44 @@ size_t lmhead_workspace_bytes(long long n_tok, long long vocab) {
   return align256((size_t)2 * n_slices(vocab) * (size_t)n_tok * sizeof(float2)) + align256((size_t)n_tok * sizeof(float));
 }
 
+namespace {
+
+template <int kDtype, bool kKeep>
+void launch_partials(const char* H, const char* W, const int32_t* tokens, int n_tok, int row_bytes, int vocab,
+                     float2* part, float* zy, float* logits, long long ld, hipStream_t stream) {
+  const int S = n_slices(vocab);
+  if (n_tok <= kNarrowMaxTokens) {
+    const dim3 grid((unsigned)ceil_div(n_tok, kNarrowBRows) * (unsigned)S);
+    hipLaunchKernelGGL((lmhead_lse_partial_narrow_kernel<kDtype, kKeep>), grid, dim3(kThreads), 0, stream, H, W,
+                       tokens, n_tok, row_bytes, vocab, S, part, zy, logits, ld);
+  } else {
+    const int G = slices_per_group(n_tok, vocab);
+    const int ntb = (int)ceil_div(n_tok, kBT);
+    const dim3 grid((unsigned)ntb * (unsigned)n_slice_groups(n_tok, vocab));
+    hipLaunchKernelGGL((lmhead_lse_partial_kernel<kDtype, kKeep>), grid, dim3(kThreads), 0, stream, H, W, tokens,
+                       n_tok, row_bytes, vocab, ntb, S, G, part, zy, logits, ld);
+  }
+}
+
+}  // namespace
+
 hipError_t launch_lmhead_logprob(const void* H, const void* W, int dtype, int n_tok, int d, int vocab,
-                                 const int32_t* tokens, float* logprob, float* lse, void* workspace,
-                                 hipStream_t stream) {
+                                 const int32_t* tokens, float* logprob, float* lse, float* logits, long long ld,
+                                 void* workspace, hipStream_t stream) {
   const int es = dtype == 0 ? 2 : 4;
   const int row_bytes = d * es;
   const int S = n_slices(vocab);
-  const int G = slices_per_group(n_tok, vocab);
-  const int ntb = (int)ceil_div(n_tok, kBT);
   float2* part = static_cast<float2*>(workspace);
   float* zy = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                        align256((size_t)2 * S * (size_t)n_tok * sizeof(float2)));
-  if (n_tok <= kNarrowMaxTokens) {
-    const dim3 grid((unsigned)ceil_div(n_tok, kNarrowBRows) * (unsigned)S);
-    if (dtype == 0)
-      hipLaunchKernelGGL(lmhead_lse_partial_narrow_kernel<0>, grid, dim3(kThreads), 0, stream,
-                         static_cast<const char*>(H), static_cast<const char*>(W), tokens, n_tok, row_bytes, vocab, S,
-                         part, zy);
-    else
-      hipLaunchKernelGGL(lmhead_lse_partial_narrow_kernel<1>, grid, dim3(kThreads), 0, stream,
-                         static_cast<const char*>(H), static_cast<const char*>(W), tokens, n_tok, row_bytes, vocab, S,
-                         part, zy);
+  const char* Hc = static_cast<const char*>(H);
+  const char* Wc = static_cast<const char*>(W);
+  if (dtype == 0) {
+    if (logits) launch_partials<0, true>(Hc, Wc, tokens, n_tok, row_bytes, vocab, part, zy, logits, ld, stream);
+    else launch_partials<0, false>(Hc, Wc, tokens, n_tok, row_bytes, vocab, part, zy, nullptr, 0, stream);
   } else {
-    const dim3 grid((unsigned)ntb * (unsigned)n_slice_groups(n_tok, vocab));
-    if (dtype == 0)
-      hipLaunchKernelGGL(lmhead_lse_partial_kernel<0>, grid, dim3(kThreads), 0, stream, static_cast<const char*>(H),
-                         static_cast<const char*>(W), tokens, n_tok, row_bytes, vocab, ntb, S, G, part, zy);
-    else
-      hipLaunchKernelGGL(lmhead_lse_partial_kernel<1>, grid, dim3(kThreads), 0, stream, static_cast<const char*>(H),
-                         static_cast<const char*>(W), tokens, n_tok, row_bytes, vocab, ntb, S, G, part, zy);
+    if (logits) launch_partials<1, true>(Hc, Wc, tokens, n_tok, row_bytes, vocab, part, zy, logits, ld, stream);
+    else launch_partials<1, false>(Hc, Wc, tokens, n_tok, row_bytes, vocab, part, zy, nullptr, 0, stream);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

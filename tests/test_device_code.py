@@ -88,7 +88,8 @@ def test_asm_scale_loads_are_not_touched_before_their_wait(tmp_path):
 
 @needs_hipcc
 @pytest.mark.parametrize("src,kernel", [
-    ("lmhead.hip", "lmhead_lse_partial_kernel"),
+    ("lmhead.hip", "lmhead_lse_partial_kernelILi0ELb0E"),  # bf16, logits not kept
+    ("lmhead.hip", "lmhead_lse_partial_kernelILi1ELb0E"),  # fp32, logits not kept
     ("fp8.hip", "lmhead_fp8_partial_kernel"),
     ("fp8.hip", "lmhead_mxfp4_partial_kernel"),
 ])
@@ -107,3 +108,32 @@ def test_wide_kernels_have_no_scratch(tmp_path, src, kernel):
             assert int(m.group(1)) == 0, (current, line)
             seen += 1
     assert seen >= 1, f"no resource report for {kernel}"
+
+
+@needs_hipcc
+def test_kept_logits_kernel_spills_only_outside_the_k_loop(tmp_path):
+    """The forward that also writes the logits runs out of registers in its
+    epilogue (a few dwords per lane go to scratch there); the K loop, where
+    the time goes, must stay free of scratch traffic."""
+    out = str(tmp_path / "lmhead.s")
+    _compile(os.path.join(build.CSRC, "lmhead.hip"), str(tmp_path), ("-S", "-o", out))
+    asm = open(out).read()
+    name = "_ZN3itl12_GLOBAL__N_125lmhead_lse_partial_kernelILi0ELb1E"
+    start = re.search(r"^" + name + r"\S*:", asm, re.M).end()
+    body = asm[start:asm.index("s_endpgm", start)]
+    depth = 0
+    k_loop_lines = 0
+    in_label = False
+    for line in body.splitlines():
+        # a block's loop depth is printed on its label line and the comment
+        # lines right after it; the innermost loop is the K loop
+        if line.startswith(".LBB"):
+            depth, in_label = 0, True
+        elif not line.strip().startswith(";"):
+            in_label = False
+        if in_label:
+            depth = max([depth] + [int(d) for d in re.findall(r"Depth=(\d)", line)])
+        if depth >= 2:
+            k_loop_lines += 1
+            assert "scratch_" not in line, line
+    assert k_loop_lines > 100, "no inner loop found"
