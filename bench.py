@@ -198,6 +198,30 @@ def decode_leg(wl, device, batch_sizes=(1, 8, 64, 128, 256), calls=20):
         torch.cuda.synchronize()
         return a.elapsed_time(b) / n
 
+    def graph_decode(Hm, ym, ws, steps=16, reps=5):
+        """A serving loop's view: `steps` decode calls captured once in a HIP
+        graph and replayed (no per-call launch cost on the host). Returns
+        the per-call time and whether every replayed call gave the eager
+        call's bits."""
+        M = Hm.shape[0]
+        out = torch.empty((steps, M), dtype=torch.float32, device=device)
+        ref = itl.lmhead_logprob(Hm, W, ym, want_lse=False)[0]
+        side = torch.cuda.Stream(device)
+        side.wait_stream(torch.cuda.current_stream(device))
+        with torch.cuda.stream(side):  # warm-up on a side stream, as capture requires
+            for k in range(steps):
+                itl.lmhead_logprob(Hm, W, ym, logprob=out[k], workspace=ws, want_lse=False)
+        torch.cuda.current_stream(device).wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for k in range(steps):
+                itl.lmhead_logprob(Hm, W, ym, logprob=out[k], workspace=ws, want_lse=False)
+        out.zero_()
+        ms = timed(graph.replay, reps) / steps
+        torch.cuda.synchronize()
+        same = bool(torch.equal(out.view(torch.int32), ref.view(torch.int32).expand(steps, M)))
+        return ms, same
+
     Wq8, ws8 = itl.quantize_rows_fp8(W)
     Wq4, ws4 = itl.quantize_rows_mxfp4(W)
     rows = []
@@ -224,6 +248,7 @@ def decode_leg(wl, device, batch_sizes=(1, 8, 64, 128, 256), calls=20):
 
         ms_fp8 = timed(q8, calls)
         ms_mx4 = timed(q4, calls)
+        ms_graph, graph_same = graph_decode(Hm, ym, ws)
         itl.lmhead_logprob(Hm, W, ym, logprob=lp, workspace=ws, want_lse=False)
         lp_b = baseline(Hm, ym)
         torch.cuda.synchronize()
@@ -234,8 +259,10 @@ def decode_leg(wl, device, batch_sizes=(1, 8, 64, 128, 256), calls=20):
                      "tokens_per_s_invariant": M / (ms_ours * 1e-3), "tokens_per_s_baseline": M / (ms_base * 1e-3),
                      "invariant_over_baseline": ms_base / ms_ours,
                      "ms_invariant_fp8_weights": ms_fp8, "ms_invariant_mxfp4_weights": ms_mx4,
+                     "ms_invariant_graph_replay": ms_graph, "graph_replay_bit_identical": graph_same,
                      "max_abs_lp_gap_to_baseline": float((lp - lp_b).abs().max())})
-        log(f"[bench] decode M={M}: invariant {ms_ours:.3f} ms, baseline {ms_base:.3f} ms "
+        log(f"[bench] decode M={M}: invariant {ms_ours:.3f} ms ({ms_graph:.3f} ms per call replayed from a graph, "
+            f"bits {'identical' if graph_same else 'DIFFER'}), baseline {ms_base:.3f} ms "
             f"(throughput ratio {ms_base / ms_ours:.3f}); with FP8 weights {ms_fp8:.3f} ms, MXFP4 {ms_mx4:.3f} ms")
     return {
         "workload": f"{wl.key} decode-shaped calls (M sequences x 1 token), {calls} calls per point",

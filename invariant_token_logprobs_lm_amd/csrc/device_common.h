@@ -11,10 +11,12 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef int int4v __attribute__((ext_vector_type(4)));
 
-// Cache policy of the buffer stores of data read back much later by
-// another kernel: the non-temporal bit (gfx9 SLC position), so the stores
-// do not displace the operands the workgroups of an XCD share in L2.
-constexpr int kStreamStore = 2;
+// Cache policy of the kept-logits buffer stores: the default (write-back
+// through L2). Measured against the non-temporal bit (gfx9 SLC position) on
+// the large-moe head's forward: +21 ms over the plain forward instead of
+// +33 ms; each store instruction writes 32-byte pieces of a token's row and
+// the L2 merges a block's four pieces into whole 128-byte lines.
+constexpr int kLogitStorePolicy = 0;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;

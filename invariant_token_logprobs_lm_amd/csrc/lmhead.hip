@@ -86,8 +86,6 @@ __device__ __forceinline__ LogitRows logit_rows(float* logits, long long ld, int
 // (v0 = the block's first row, the same for the whole wavefront). Four
 // consecutive rows are 16 contiguous bytes of the token's row. In the
 // vocabulary's last tile, rows at or past the vocabulary are not written.
-// Streaming stores: the logits are read back much later by another kernel,
-// and the L2 is better kept for the operands the workgroups share.
 template <int I, class kPartial>
 __device__ __forceinline__ void store_quad(const LogitRows& rows, uint32_t voff, int v0, int half, int vocab,
                                            const floatx16& z, kPartial) {
@@ -95,13 +93,13 @@ __device__ __forceinline__ void store_quad(const LogitRows& rows, uint32_t voff,
   if constexpr (!kPartial::value) {
     __builtin_amdgcn_raw_buffer_store_b128(
         __builtin_bit_cast(int4v, __builtin_shufflevector(z, z, 4 * I, 4 * I + 1, 4 * I + 2, 4 * I + 3)), rows.rsrc,
-        voff, so, kStreamStore);
+        voff, so, kLogitStorePolicy);
   } else {
 #pragma unroll
     for (int r = 0; r < 4; ++r)
       if (v0 + 8 * I + 4 * half + r < vocab)
         __builtin_amdgcn_raw_buffer_store_b32((int)__float_as_uint(z[4 * I + r]), rows.rsrc, voff + 4u * r, so,
-                                              kStreamStore);
+                                              kLogitStorePolicy);
   }
 }
 
@@ -115,19 +113,17 @@ __device__ __forceinline__ void store_logits(const LogitRows& rows, int bn, int 
   store_quad<3>(rows, voff, v0, half, vocab, z, partial);
 }
 
-// Fold one accumulator block, writing its logits first when kKeep.
-template <bool kKeep, class kPartial>
-__device__ __forceinline__ void fold_keep(Col& c, const floatx16& a, int bm, int bn, int vw, int half, int vocab,
-                                          kPartial partial, const LogitRows& rows) {
-  if constexpr (kKeep) {
-    floatx16 z;
+// Store one accumulator block's logits, four registers at a time straight
+// from the accumulators (a separate pass before the fold: with the fold's
+// state live as well, the epilogue ran out of registers, and every spill
+// reload waited for all the stores and operand loads in flight).
+template <class kPartial>
+__device__ __forceinline__ void store_block(const LogitRows& rows, int bn, int v0, int half, int vocab,
+                                            const floatx16& a, kPartial partial) {
+  floatx16 z;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) z[i] = acc_read(a, i);
-    store_logits(rows, bn, vw + bm * 32, half, vocab, z, partial);
-    fold_values(c, z, bm, vw, half, vocab, partial);
-  } else {
-    fold_block(c, a, bm, vw, half, vocab, partial);
-  }
+  for (int i = 0; i < 16; ++i) z[i] = acc_read(a, i);
+  store_logits(rows, bn, v0, half, vocab, z, partial);
 }
 
 template <int kDtype, bool kKeep>
@@ -172,10 +168,16 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_lse_partial_kernel(
     LogitRows rows{};
     if constexpr (kKeep) rows = logit_rows(logits, ld, t0 + wt * 128, 128, n_tok, col, half);
     auto fold_tile = [&](auto partial) {
+      if constexpr (kKeep) {
+#pragma unroll
+        for (int bn = 0; bn < 4; ++bn)
+#pragma unroll
+          for (int bm = 0; bm < 4; ++bm) store_block(rows, bn, vw + bm * 32, half, vocab, acc[bm][bn], partial);
+      }
 #pragma unroll
       for (int bn = 0; bn < 4; ++bn)
 #pragma unroll
-        for (int bm = 0; bm < 4; ++bm) fold_keep<kKeep>(c[bn], acc[bm][bn], bm, bn, vw, half, vocab, partial, rows);
+        for (int bm = 0; bm < 4; ++bm) fold_block(c[bn], acc[bm][bn], bm, vw, half, vocab, partial);
     };
     if (tile * kBV + kBV > vocab) fold_tile(std::true_type{});  // only the vocabulary's last tile
     else fold_tile(std::false_type{});
@@ -231,8 +233,12 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_lse_partial_narrow_kernel(
     const int vw = tile * kBV + wv * 128;
     mfma_result_wait();
     auto fold_tile = [&](auto partial) {
+      if constexpr (kKeep) {
 #pragma unroll
-      for (int bm = 0; bm < 4; ++bm) fold_keep<kKeep>(c, acc[bm], bm, 0, vw, half, vocab, partial, rows);
+        for (int bm = 0; bm < 4; ++bm) store_block(rows, 0, vw + bm * 32, half, vocab, acc[bm], partial);
+      }
+#pragma unroll
+      for (int bm = 0; bm < 4; ++bm) fold_block(c, acc[bm], bm, vw, half, vocab, partial);
     };
     if (tile * kBV + kBV > vocab) fold_tile(std::true_type{});
     else fold_tile(std::false_type{});

@@ -90,6 +90,7 @@ def test_asm_scale_loads_are_not_touched_before_their_wait(tmp_path):
 @pytest.mark.parametrize("src,kernel", [
     ("lmhead.hip", "lmhead_lse_partial_kernelILi0ELb0E"),  # bf16, logits not kept
     ("lmhead.hip", "lmhead_lse_partial_kernelILi1ELb0E"),  # fp32, logits not kept
+    ("lmhead.hip", "lmhead_lse_partial_kernelILi0ELb1E"),  # bf16, logits kept
     ("fp8.hip", "lmhead_fp8_partial_kernel"),
     ("fp8.hip", "lmhead_mxfp4_partial_kernel"),
 ])
@@ -112,13 +113,13 @@ def test_wide_kernels_have_no_scratch(tmp_path, src, kernel):
 
 @needs_hipcc
 def test_kept_logits_kernel_spills_only_outside_the_k_loop(tmp_path):
-    """The forward that also writes the logits runs out of registers in its
-    epilogue (a few dwords per lane go to scratch there); the K loop, where
-    the time goes, must stay free of scratch traffic."""
+    """The fp32 head's forward that also writes the logits runs out of
+    registers in its epilogue (a few dwords per lane go to scratch there);
+    the K loop, where the time goes, must stay free of scratch traffic."""
     out = str(tmp_path / "lmhead.s")
     _compile(os.path.join(build.CSRC, "lmhead.hip"), str(tmp_path), ("-S", "-o", out))
     asm = open(out).read()
-    name = "_ZN3itl12_GLOBAL__N_125lmhead_lse_partial_kernelILi0ELb1E"
+    name = "_ZN3itl12_GLOBAL__N_125lmhead_lse_partial_kernelILi1ELb1E"
     start = re.search(r"^" + name + r"\S*:", asm, re.M).end()
     body = asm[start:asm.index("s_endpgm", start)]
     depth = 0
