@@ -106,6 +106,33 @@ def test_loss_and_advantage_validation(lib):
                                            v(257), 1 << 40, None) == WORKSPACE
 
 
+def test_kept_logits_argument_validation(lib):
+    """The kept-logits entry points check the logits buffer before anything
+    is launched: present, 16-byte aligned, a row stride >= vocab that is a
+    multiple of 4 and small enough for 32-bit offsets over 128 rows."""
+    v = ctypes.c_void_p
+
+    def keep(Z=256, ld=12, n=4, V=10):
+        return lib.itl_lmhead_logprob_keep_logits(v(256), v(256), 0, n, 64, V, v(256), v(256), None, v(Z), ld,
+                                                  v(256), 1 << 20, None)
+
+    assert keep(Z=0) == INVALID
+    assert keep(ld=8) == INVALID          # below vocab
+    assert keep(ld=14) == INVALID         # not a multiple of 4
+    assert keep(Z=264) == INVALID         # not 16-byte aligned
+    assert keep(ld=1 << 24) == UNSUPPORTED
+    assert "ld_logits" in lib.itl_last_error().decode()
+    assert keep(n=0, Z=0) == OK           # empty call is a no-op
+
+    def bwd(Z=256, ld=12, n=4, V=10, ws=1 << 30):
+        return lib.itl_reinforce_zero_backward_from_logits(v(256), v(256), 0, n, 64, V, v(256), v(256), v(256),
+                                                           v(Z), ld, v(256), v(256), v(256), ws, None)
+
+    assert bwd(Z=0) == INVALID
+    assert bwd(ld=9) == INVALID
+    assert bwd(ws=16) == WORKSPACE        # the rest as for itl_reinforce_zero_backward
+
+
 def test_backward_workspace_sizes(lib):
     f = lib.itl_reinforce_zero_backward_workspace_bytes
     bf16 = f(1000, 256, 5000, 0)
