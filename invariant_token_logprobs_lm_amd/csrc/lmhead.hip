@@ -167,7 +167,7 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_lse_partial_kernel(
     mfma_result_wait();
     LogitRows rows{};
     if constexpr (kKeep) rows = logit_rows(logits, ld, t0 + wt * 128, 128, n_tok, col, half);
-    auto fold_tile = [&](auto partial) {
+    auto fold_tile = [&](auto partial, auto pick) {
       if constexpr (kKeep) {
 #pragma unroll
         for (int bn = 0; bn < 4; ++bn)
@@ -177,10 +177,17 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_lse_partial_kernel(
 #pragma unroll
       for (int bn = 0; bn < 4; ++bn)
 #pragma unroll
-        for (int bm = 0; bm < 4; ++bm) fold_block(c[bn], acc[bm][bn], bm, vw, half, vocab, partial);
+        for (int bm = 0; bm < 4; ++bm) fold_block(c[bn], acc[bm][bn], bm, vw, half, vocab, partial, pick);
     };
-    if (tile * kBV + kBV > vocab) fold_tile(std::true_type{});  // only the vocabulary's last tile
-    else fold_tile(std::false_type{});
+    // A lane's sampled row lies in this wavefront's 128 rows of a given tile
+    // for about one tile in V / 128, so most tiles skip the pick (a uniform
+    // branch: the picked values are the same either way).
+    bool mine = false;
+#pragma unroll
+    for (int bn = 0; bn < 4; ++bn) mine = mine || (unsigned)(c[bn].y - vw) < 128u;
+    if (tile * kBV + kBV > vocab) fold_tile(std::true_type{}, std::true_type{});  // only the vocabulary's last tile
+    else if (__builtin_amdgcn_ballot_w64(mine) != 0) fold_tile(std::false_type{}, std::true_type{});
+    else fold_tile(std::false_type{}, std::false_type{});
     if (tile == slice_last_tile) {
 #pragma unroll
       for (int bn = 0; bn < 4; ++bn) {

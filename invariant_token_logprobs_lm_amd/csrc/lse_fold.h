@@ -28,21 +28,28 @@ struct Col {
 // kPartial (a std::bool_constant): the block may hold rows past the
 // vocabulary, which are masked. Callers choose it once per tile, so that a
 // full tile's epilogue has no masking and no branches.
-template <class kPartial>
-__device__ __forceinline__ void fold_values(Col& c, floatx16 z, int bm, int vw, int half, int vocab, kPartial) {
-  const int o = c.y - vw;  // sampled row relative to this wavefront's 128 rows
-  // Register i of a lane holds row 32 bm + 8 (i / 4) + 4 half + (i % 4):
-  // bits 0, 1, 3, 4 of the row pick i, bit 2 picks the lane half.
-  const bool b0 = (o & 1) != 0, b1 = (o & 2) != 0, b2 = (o & 8) != 0, b3 = (o & 16) != 0;
-  const bool here = (unsigned)o < 128u && ((o >> 2) & 1) == half && (o >> 5) == bm;
+//
+// kPick = std::false_type: the caller knows that no lane's sampled row lies
+// in this wavefront's 128 rows of the tile, so the pick is skipped (it would
+// leave zy and found unchanged).
+template <class kPartial, class kPick = std::true_type>
+__device__ __forceinline__ void fold_values(Col& c, floatx16 z, int bm, int vw, int half, int vocab, kPartial,
+                                            kPick = kPick{}) {
   if constexpr (kPartial::value) {
     const int lim = vocab - (vw + bm * 32 + 4 * half);  // rows at or past this offset do not exist
 #pragma unroll
     for (int i = 0; i < 16; ++i) z[i] = (8 * (i >> 2) + (i & 3) >= lim) ? -INFINITY : z[i];
   }
-  const float pick = select16(z, b0, b1, b2, b3);
-  c.zy = here ? pick : c.zy;
-  c.found = c.found || here;
+  if constexpr (kPick::value) {
+    const int o = c.y - vw;  // sampled row relative to this wavefront's 128 rows
+    // Register i of a lane holds row 32 bm + 8 (i / 4) + 4 half + (i % 4):
+    // bits 0, 1, 3, 4 of the row pick i, bit 2 picks the lane half.
+    const bool b0 = (o & 1) != 0, b1 = (o & 2) != 0, b2 = (o & 8) != 0, b3 = (o & 16) != 0;
+    const bool here = (unsigned)o < 128u && ((o >> 2) & 1) == half && (o >> 5) == bm;
+    const float pick = select16(z, b0, b1, b2, b3);
+    c.zy = here ? pick : c.zy;
+    c.found = c.found || here;
+  }
 
   float bmax = z[0];
 #pragma unroll
@@ -86,13 +93,13 @@ __device__ __forceinline__ void flush_slice(Col& c, int tok, int n_tok, int half
 // Fold one accumulator block as it stands (the bf16 / fp32 heads). The
 // lane's 16 logits are copied out of the matrix-core registers where they
 // are used (acc_read), so the fold needs few VGPRs next to the accumulators.
-template <class kPartial>
+template <class kPartial, class kPick = std::true_type>
 __device__ __forceinline__ void fold_block(Col& c, const floatx16& a, int bm, int vw, int half, int vocab,
-                                           kPartial partial) {
+                                           kPartial partial, kPick pick = kPick{}) {
   floatx16 z;  // a vector, not an array: it must stay in registers
 #pragma unroll
   for (int i = 0; i < 16; ++i) z[i] = acc_read(a, i);
-  fold_values(c, z, bm, vw, half, vocab, partial);
+  fold_values(c, z, bm, vw, half, vocab, partial, pick);
 }
 
 }  // namespace itl
