@@ -166,3 +166,28 @@ def test_keep_logits_large_moe_head_full_size(cuda):
     dH_r, dW_r = itl.reinforce_zero_backward(H, W, y, lse, coef)
     torch.cuda.synchronize()
     assert same_bits(dH_k, dH_r) and same_bits(dW_k, dW_r)
+
+
+def test_kept_logits_are_batch_invariant(cuda):
+    """A token's kept logits have the same bits alone (narrow kernel), in a
+    small batch, and in a large batch at another row position (wide kernel),
+    so the dlogits formed from them are batch-invariant per token too."""
+    import torch
+
+    itl = _itl()
+    H, W, y = _random_head(900, 256, 3000, torch.bfloat16, seed=77, device=cuda)
+    _, _, Z_all = itl.lmhead_logprob_keep_logits(H, W, y)
+    pick = [0, 5, 257, 600, 899]
+    idx = torch.tensor(pick, device=cuda)
+    _, _, Z_few = itl.lmhead_logprob_keep_logits(H[idx].contiguous(), W, y[idx].contiguous())
+    perm = torch.randperm(900, generator=torch.Generator(device="cpu").manual_seed(3)).to(cuda)
+    _, _, Z_perm = itl.lmhead_logprob_keep_logits(H[perm].contiguous(), W, y[perm].contiguous())
+    inv = torch.empty_like(perm)
+    inv[perm] = torch.arange(900, device=cuda)
+    torch.cuda.synchronize()
+    for k, t in enumerate(pick):
+        _, _, Z_one = itl.lmhead_logprob_keep_logits(H[t:t + 1].contiguous(), W, y[t:t + 1].contiguous())
+        torch.cuda.synchronize()
+        assert same_bits(Z_one[0, :3000], Z_all[t, :3000])
+        assert same_bits(Z_few[k, :3000], Z_all[t, :3000])
+        assert same_bits(Z_perm[inv[t], :3000], Z_all[t, :3000])
