@@ -148,7 +148,7 @@ __device__ __forceinline__ void band_order(int b, int n_fast, int n_slow, int& f
 
 // 1. dlogits. A = W tiles (vocabulary), B = the chunk's H block (tokens); as
 // in the forward. Grid: token blocks (fast) x vocabulary slices (slow).
-template <int kDtype>
+template <int kDtype, bool kBFar>
 __global__ __launch_bounds__(kThreads, 1) void dlogits_kernel(
     const char* __restrict__ Hc, int len, const char* __restrict__ W, int row_bytes, int vocab, int vpad,
     int n_tb, int n_slices, int group, const int32_t* __restrict__ y, const float* __restrict__ lse,
@@ -207,7 +207,7 @@ __global__ __launch_bounds__(kThreads, 1) void dlogits_kernel(
       }
     }
   };
-  run_tiles<kDtype>(smem, L, row_bytes, tile_begin, tile_end, row_bytes / kStepBytes, w_rsrc, hr, epilogue);
+  run_tiles<kDtype, kBFar>(smem, L, row_bytes, tile_begin, tile_end, row_bytes / kStepBytes, w_rsrc, hr, epilogue);
 }
 
 // 1'. dlogits from kept logits: the same g as dlogits_kernel, for a tile of
@@ -293,7 +293,7 @@ __global__ __launch_bounds__(256) void dlogits_from_logits_kernel(
 // 2. dH for the chunk. A = W^T tile (d rows, K = Vpad), B = Gd token block.
 // Grid: token blocks (fast) x d tiles (slow). Lane l's accumulators are d
 // rows of token t0 + 128 wt + 32 bn + (l mod 32).
-template <int kDtype>
+template <int kDtype, bool kBFar>
 __global__ __launch_bounds__(kThreads, 1) void dh_kernel(const char* __restrict__ WT, const char* __restrict__ Gd,
                                                         int vpad, int d, int vocab, int len, int n_tb, int n_dt,
                                                         const int32_t* __restrict__ y, const float* __restrict__ coef,
@@ -356,13 +356,13 @@ __global__ __launch_bounds__(kThreads, 1) void dh_kernel(const char* __restrict_
       }
     }
   };
-  run_tiles<kDtype>(smem, L, row_bytes, dt, dt + 1, row_bytes / kStepBytes, a_rsrc, br, epilogue);
+  run_tiles<kDtype, kBFar>(smem, L, row_bytes, dt, dt + 1, row_bytes / kStepBytes, a_rsrc, br, epilogue);
 }
 
 // 3. dW += the chunk's part. A = GdT vocabulary tile (K = chunk tokens), B =
 // H^T d block. Grid: vocabulary tiles (fast) x d tiles (slow). Lane l's
 // accumulators are vocabulary rows at d column 128 wt + 32 bn + (l mod 32).
-template <int kDtype>
+template <int kDtype, bool kBFar>
 __global__ __launch_bounds__(kThreads, 1) void dw_kernel(const char* __restrict__ GdT, const char* __restrict__ HT,
                                                         int kpad, int vocab, int d, int n_vt, int n_dt,
                                                         float* __restrict__ dW) {
@@ -407,7 +407,7 @@ __global__ __launch_bounds__(kThreads, 1) void dw_kernel(const char* __restrict_
       }
     }
   };
-  run_tiles<kDtype>(smem, L, row_bytes, vt, vt + 1, kpad * E::kSize / kStepBytes, a_rsrc, br, epilogue);
+  run_tiles<kDtype, kBFar>(smem, L, row_bytes, vt, vt + 1, kpad * E::kSize / kStepBytes, a_rsrc, br, epilogue);
 }
 
 // Workspace layout of the backward (each region 256-byte aligned).
@@ -504,6 +504,13 @@ hipError_t run_backward(const void* H, const void* W, int n_tok, int d, int voca
   const int n_dt = (int)ceil_div(d, kBT);
   const int n_vt = vpad / kBV;
   const int row_bytes = d * es;
+  // Load schedule (no effect on the arithmetic): the recomputing dlogits
+  // kernel follows the forward's rule (its token block two K steps ahead
+  // once the K loop is long); dH stages its dlogits block two ahead on long
+  // loops too (measured 1.5 % faster at 2020 K steps); dW keeps its
+  // vocabulary tile two ahead (the other way measured 3 % slower).
+  const bool dl_far = row_bytes / kStepBytes > kNearBMaxSteps;
+  const bool dh_far = vpad * es / kStepBytes > kNearBMaxSteps;
   for (int c0 = 0; c0 < n_tok; c0 += kBwdChunk) {
     const int len = std::min(kBwdChunk, n_tok - c0);
     const int kpad = (int)round_up(len, kBT);
@@ -514,11 +521,13 @@ hipError_t run_backward(const void* H, const void* W, int n_tok, int d, int voca
                          dim3(256), 0, stream, logits + (size_t)c0 * (size_t)ld, ld, len, vocab, vpad, lse + c0,
                          coef + c0, Gd, GdT);
     else
-      hipLaunchKernelGGL(dlogits_kernel<kDtype>, dim3((unsigned)(n_tb * n_groups)), dim3(kThreads), 0, stream, Hc,
+      hipLaunchKernelGGL((dl_far ? dlogits_kernel<kDtype, true> : dlogits_kernel<kDtype, false>),
+                         dim3((unsigned)(n_tb * n_groups)), dim3(kThreads), 0, stream, Hc,
                          len, static_cast<const char*>(W), row_bytes, vocab, vpad, n_tb, S, G, tokens + c0, lse + c0,
                          coef + c0, Gd, GdT);
     ITL_CHECK_LAUNCH();
-    hipLaunchKernelGGL(dh_kernel<kDtype>, dim3((unsigned)(n_tb * n_dt)), dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL((dh_far ? dh_kernel<kDtype, true> : dh_kernel<kDtype, false>),
+                       dim3((unsigned)(n_tb * n_dt)), dim3(kThreads), 0, stream,
                        reinterpret_cast<const char*>(WT), reinterpret_cast<const char*>(Gd), vpad, d, vocab, len, n_tb, n_dt,
                        tokens + c0, coef + c0, Wp, dH + (size_t)c0 * d);
     ITL_CHECK_LAUNCH();
@@ -526,7 +535,8 @@ hipError_t run_backward(const void* H, const void* W, int n_tok, int d, int voca
     hipLaunchKernelGGL(transpose_kernel<T>, dim3((unsigned)(kBwdChunk / 64), (unsigned)ceil_div(d, 64)), dim3(256), 0,
                        stream, Hp + (size_t)c0 * d, (long long)d, len, d, HT, kBwdChunk);
     ITL_CHECK_LAUNCH();
-    hipLaunchKernelGGL(dw_kernel<kDtype>, dim3((unsigned)(n_vt * n_dt)), dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL((dw_kernel<kDtype, false>),
+                       dim3((unsigned)(n_vt * n_dt)), dim3(kThreads), 0, stream,
                        reinterpret_cast<const char*>(GdT), reinterpret_cast<const char*>(HT), kpad, vocab, d, n_vt,
                        n_dt, dW);
     ITL_CHECK_LAUNCH();

@@ -126,7 +126,7 @@ __device__ __forceinline__ void store_block(const LogitRows& rows, int bn, int v
   store_logits(rows, bn, v0, half, vocab, z, partial);
 }
 
-template <int kDtype, bool kKeep>
+template <int kDtype, bool kKeep, bool kBFar>
 __global__ __launch_bounds__(kThreads, 1) void lmhead_lse_partial_kernel(
     const char* __restrict__ H, const char* __restrict__ W, const int32_t* __restrict__ tokens, int n_tok,
     int row_bytes, int vocab, int n_tb, int n_slices, int group, float2* __restrict__ part,
@@ -198,7 +198,7 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_lse_partial_kernel(
       slice_last_tile = slice_tile(slice + 1, n_vt, S) - 1;
     }
   };
-  run_tiles<kDtype>(smem, L, row_bytes, tile_begin, tile_end, nks, w_rsrc, hr, epilogue);
+  run_tiles<kDtype, kBFar>(smem, L, row_bytes, tile_begin, tile_end, nks, w_rsrc, hr, epilogue);
 
 #pragma unroll
   for (int bn = 0; bn < 4; ++bn)
@@ -330,8 +330,13 @@ void launch_partials(const char* H, const char* W, const int32_t* tokens, int n_
     const int G = slices_per_group(n_tok, vocab);
     const int ntb = (int)ceil_div(n_tok, kBT);
     const dim3 grid((unsigned)ntb * (unsigned)n_slice_groups(n_tok, vocab));
-    hipLaunchKernelGGL((lmhead_lse_partial_kernel<kDtype, kKeep>), grid, dim3(kThreads), 0, stream, H, W, tokens,
-                       n_tok, row_bytes, vocab, ntb, S, G, part, zy, logits, ld);
+    // Long K loops stage the token block two K steps ahead (see run_tiles).
+    if (row_bytes / kStepBytes > kNearBMaxSteps)
+      hipLaunchKernelGGL((lmhead_lse_partial_kernel<kDtype, kKeep, true>), grid, dim3(kThreads), 0, stream, H, W,
+                         tokens, n_tok, row_bytes, vocab, ntb, S, G, part, zy, logits, ld);
+    else
+      hipLaunchKernelGGL((lmhead_lse_partial_kernel<kDtype, kKeep, false>), grid, dim3(kThreads), 0, stream, H, W,
+                         tokens, n_tok, row_bytes, vocab, ntb, S, G, part, zy, logits, ld);
   }
 }
 

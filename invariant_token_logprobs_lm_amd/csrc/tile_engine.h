@@ -59,11 +59,14 @@ struct Mma<1> {  // fp32: 4 elements per lane; instruction j takes element j (k2
 };
 
 // LDS slots hold one K step of one operand: 256 rows x 128 bytes (8 chunks
-// of 16 bytes), so that every global load moves whole 128-byte lines. The
-// tiles of the walked operand (A) rotate through kWSlots slots and are
-// loaded two K steps ahead; the fixed operand (B) rotates through kHSlots
-// slots, one step ahead (a B block is shared by more of the workgroups
-// running together on an XCD, so its lines are more often in L2). Chunk c
+// of 16 bytes), so that every global load moves whole 128-byte lines. Five
+// slots fill the LDS: one operand rotates through three of them, loaded two
+// K steps ahead, the other through two, one step ahead. By default the
+// walked operand (A) is the far one (kWSlots = 3, kHSlots = 2); run_tiles'
+// kBFar swaps the roles. Which pays depends on the K loop's length: the
+// workgroups sharing an operand segment through an XCD's L2 drift apart
+// over a long loop, and the operand that fewer of them share then misses
+// L2 more often and needs the longer lead. Chunk c
 // of row r sits at position c ^ swz(r): for the MFMA operand reads (lanes
 // 0-31 take rows r0..r0+31 at one chunk, lanes 32-63 the next chunk) any 8
 // or 16 consecutive lanes then touch distinct 16-byte bank groups.
@@ -176,9 +179,13 @@ constexpr int kEngineSmemChunks = (kWSlots + kHSlots) * kSlotChunks;
 // epi(t, acc) is called after tile t with its accumulators (read them with
 // acc_read after mfma_result_wait()). Every thread of the workgroup must
 // call this.
-template <int kDtype, class ARsrc, class Epi>
+template <int kDtype, bool kBFar = false, class ARsrc, class Epi>
 __device__ __forceinline__ void run_tiles(uint4* smem, const Lanes& L, int row_bytes, int tile_begin, int tile_end,
                                           int nks, const ARsrc& a_rsrc, int4v b_rsrc, Epi&& epi) {
+  // kBFar: B two K steps ahead in three slots, A one step ahead in two
+  // (the default is the other way round); the same five slots of LDS.
+  constexpr int kAS = kBFar ? kHSlots : kWSlots;
+  constexpr int kBS = kBFar ? kWSlots : kHSlots;
   const int lane = L.lane, wave = L.wave, wv = L.wv, wt = L.wt, half = L.half, col = L.col;
   (void)lane;
   // Loader: wavefront w fills rows 64 w .. 64 w + 63 of both operands with
@@ -195,7 +202,7 @@ __device__ __forceinline__ void run_tiles(uint4* smem, const Lanes& L, int row_b
   const int4v hr = b_rsrc;
   auto w_rsrc = [&](int tile) { return a_rsrc(tile); };
   auto w_slot_lds = [&](int slot) { return lds_wave + (uint32_t)slot * kSlotBytes; };
-  auto h_slot_lds = [&](int slot) { return lds_wave + (uint32_t)(kWSlots + slot) * kSlotBytes; };
+  auto h_slot_lds = [&](int slot) { return lds_wave + (uint32_t)(kAS + slot) * kSlotBytes; };
 
   // MFMA operand reads: lane l takes row (l mod 32) of each 32-row block at
   // logical chunk 2 kk + l / 32 (kk = K sub-step 0..3); swz(row) = swz(l mod 32).
@@ -224,11 +231,11 @@ __device__ __forceinline__ void run_tiles(uint4* smem, const Lanes& L, int row_b
       w_ks = 0;
       w_tile = min(w_tile + 1, tile_end - 1);
     }
-    w_slot_next = w_slot_next == kWSlots - 1 ? 0 : w_slot_next + 1;
+    w_slot_next = w_slot_next == kAS - 1 ? 0 : w_slot_next + 1;
   };
   auto next_h = [&]() {
     h_ks = h_ks + 1 == nks ? 0 : h_ks + 1;
-    h_slot_next ^= 1;
+    h_slot_next = h_slot_next == kBS - 1 ? 0 : h_slot_next + 1;
   };
   // One sub-step: MFMA q (q = 4 bm + bn) on (A, B), interleaved with the 8
   // reads of the next operands (RA, RB; order A0 B0 B1 B2 B3 A1 A2 A3, the
@@ -241,7 +248,7 @@ __device__ __forceinline__ void run_tiles(uint4* smem, const Lanes& L, int row_b
   auto phase = [&](floatx16 (&acc)[4][4], const uint4 (&A)[4], const uint4 (&B)[4], auto first, auto do_mma,
                    auto front, auto dma, auto do_read, int wsl, int hsl, int rkk, uint4 (&RA)[4], uint4 (&RB)[4]) {
     const uint4* sa = smem + wsl * kSlotChunks;
-    const uint4* sb = smem + (kWSlots + hsl) * kSlotChunks;
+    const uint4* sb = smem + (kAS + hsl) * kSlotChunks;
     int4v wr;
     uint32_t wsoff = 0, hsoff = 0, wm = 0, hm = 0;
     if constexpr (decltype(dma)::value) {
@@ -265,8 +272,13 @@ __device__ __forceinline__ void run_tiles(uint4* smem, const Lanes& L, int row_b
         else RA[r - 4] = sa[a_off[rkk] + (r - 4) * 32 * kRowChunks];
       }
       if constexpr (decltype(dma)::value) {
-        if (q < 8) dma16(hr, voff[q], hsoff, hm + q * 1024);
-        else dma16(wr, voff[q - 8], wsoff, wm + (q - 8) * 1024);
+        if constexpr (!kBFar) {
+          if (q < 8) dma16(hr, voff[q], hsoff, hm + q * 1024);
+          else dma16(wr, voff[q - 8], wsoff, wm + (q - 8) * 1024);
+        } else {  // the one-ahead operand first, as above
+          if (q < 8) dma16(wr, voff[q], wsoff, wm + q * 1024);
+          else dma16(hr, voff[q - 8], hsoff, hm + (q - 8) * 1024);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -280,7 +292,7 @@ __device__ __forceinline__ void run_tiles(uint4* smem, const Lanes& L, int row_b
   using F = std::false_type;
   // Prologue: W(0), H(0), W(1); publish step 0; H(1), W(2); read the first
   // two sub-steps' operands.
-  {
+  if constexpr (!kBFar) {
     const int4v wr0 = w_rsrc(w_tile);
 #pragma unroll
     for (int j = 0; j < kDmaPerWave; ++j) dma16(wr0, voff[j], (uint32_t)w_ks * kStepBytes, w_slot_lds(0) + j * 1024);
@@ -292,15 +304,33 @@ __device__ __forceinline__ void run_tiles(uint4* smem, const Lanes& L, int row_b
 #pragma unroll
     for (int j = 0; j < kDmaPerWave; ++j) dma16(wr1, voff[j], (uint32_t)w_ks * kStepBytes, w_slot_lds(1) + j * 1024);
     next_w();
+  } else {  // W(0), H(0), H(1)
+    const int4v wr0 = w_rsrc(w_tile);
+#pragma unroll
+    for (int j = 0; j < kDmaPerWave; ++j) dma16(wr0, voff[j], (uint32_t)w_ks * kStepBytes, w_slot_lds(0) + j * 1024);
+#pragma unroll
+    for (int j = 0; j < kDmaPerWave; ++j) dma16(hr, voff[j], 0, h_slot_lds(0) + j * 1024);
+    next_w();
+    next_h();
+#pragma unroll
+    for (int j = 0; j < kDmaPerWave; ++j) dma16(hr, voff[j], (uint32_t)h_ks * kStepBytes, h_slot_lds(1) + j * 1024);
+    next_h();
   }
   wait_and_barrier<kDmaPerWave>();  // W(0), H(0) landed
   {
     const int4v wr = w_rsrc(w_tile);
     const uint32_t hm = h_slot_lds(h_slot_next), wm = w_slot_lds(w_slot_next);
+    if constexpr (!kBFar) {  // H(1), W(2)
 #pragma unroll
-    for (int j = 0; j < kDmaPerWave; ++j) dma16(hr, voff[j], (uint32_t)h_ks * kStepBytes, hm + j * 1024);
+      for (int j = 0; j < kDmaPerWave; ++j) dma16(hr, voff[j], (uint32_t)h_ks * kStepBytes, hm + j * 1024);
 #pragma unroll
-    for (int j = 0; j < kDmaPerWave; ++j) dma16(wr, voff[j], (uint32_t)w_ks * kStepBytes, wm + j * 1024);
+      for (int j = 0; j < kDmaPerWave; ++j) dma16(wr, voff[j], (uint32_t)w_ks * kStepBytes, wm + j * 1024);
+    } else {  // W(1), H(2)
+#pragma unroll
+      for (int j = 0; j < kDmaPerWave; ++j) dma16(wr, voff[j], (uint32_t)w_ks * kStepBytes, wm + j * 1024);
+#pragma unroll
+      for (int j = 0; j < kDmaPerWave; ++j) dma16(hr, voff[j], (uint32_t)h_ks * kStepBytes, hm + j * 1024);
+    }
     next_h();
     next_w();
   }
@@ -309,7 +339,7 @@ __device__ __forceinline__ void run_tiles(uint4* smem, const Lanes& L, int row_b
   uint4 a0[4], b0[4], a1[4], b1[4], a2[4], b2[4], a3[4], b3[4];
   {
     const uint4* sa = smem;
-    const uint4* sb = smem + kWSlots * kSlotChunks;
+    const uint4* sb = smem + kAS * kSlotChunks;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       a0[m] = sa[a_off[0] + m * 32 * kRowChunks];
@@ -337,8 +367,8 @@ __device__ __forceinline__ void run_tiles(uint4* smem, const Lanes& L, int row_b
     phase(acc, a0, b0, first, T{}, F{}, F{}, T{}, wslot, hslot, 2, a2, b2);
     phase(acc, a1, b1, F{}, T{}, T{}, F{}, T{}, wslot, hslot, 3, a3, b3);
     wait_and_barrier<kDmaPerWave>();  // W(g + 1), H(g + 1) landed; W(g + 2) may still be in flight
-    wslot = wslot == kWSlots - 1 ? 0 : wslot + 1;
-    hslot ^= 1;
+    wslot = wslot == kAS - 1 ? 0 : wslot + 1;
+    hslot = hslot == kBS - 1 ? 0 : hslot + 1;
     phase(acc, a2, b2, F{}, T{}, F{}, T{}, R{}, wslot, hslot, 0, a0, b0);
     phase(acc, a3, b3, F{}, T{}, F{}, F{}, R{}, wslot, hslot, 1, a1, b1);
   };
@@ -353,7 +383,7 @@ __device__ __forceinline__ void run_tiles(uint4* smem, const Lanes& L, int row_b
     }
     epi(tile, acc);
     const uint4* sa = smem + wslot * kSlotChunks;
-    const uint4* sb = smem + (kWSlots + hslot) * kSlotChunks;
+    const uint4* sb = smem + (kAS + hslot) * kSlotChunks;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       a0[m] = sa[a_off[0] + m * 32 * kRowChunks];
