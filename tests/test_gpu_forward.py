@@ -71,6 +71,8 @@ def test_tiny_workload_all_tokens(cuda):
         (64, 64, 3, "f32"),          # tiny vocabulary, mostly masked tile
         (513, 320, 8192 + 256, "bf16"),  # 33 slices of one tile, d not a multiple of 256
         (5200, 64, 150 * 256 - 17, "bf16"),  # 21 x 150 > 2048: 8 slices per workgroup, last group of 6
+        (300, 4160, 3005, "bf16"),   # 65 K steps: the token block staged two K steps ahead
+        (300, 2112, 1000, "f32"),    # 66 K steps of fp32: the same ring order, fp32 MFMA
     ],
 )
 def test_shapes_ragged_and_degenerate(cuda, n_tok, d, vocab, dtype_name):
@@ -137,6 +139,7 @@ def test_row_position_invariance(cuda):
     "d,vocab,dtype_name",
     [
         (2560, 151936, "bf16"),   # 256 slices of 2 or 3 tiles, partial last tile
+        (7168, 129280, "bf16"),   # 112 K steps: the wide kernel stages the token block two steps ahead
         (128, 4096 + 37, "bf16"),  # one tile per slice, last tile of 37 rows
         (64, 1000, "f32"),        # fp32 MFMA
     ],
