@@ -39,7 +39,7 @@ namespace itl {
 
 namespace {
 
-constexpr int kBwdChunk = 16384;  // tokens per chunk (a multiple of kBT)
+constexpr int kBwdChunk = kBwdChunkTokens;  // tokens per chunk (a multiple of kBT)
 static_assert(kBwdChunk % kBT == 0, "chunks hold whole token blocks");
 
 template <int kDtype>

@@ -32,6 +32,11 @@ hipError_t launch_reinforce_zero_loss(const float* logprob, const float* rollout
 
 size_t backward_workspace_bytes(long long n_tok, long long d, long long vocab, int dtype);
 
+// Tokens per chunk of the backward (a multiple of the token block). dW's sum
+// over tokens is carried across chunks in this order, so it is part of dW's
+// bits; the build info reports it.
+constexpr int kBwdChunkTokens = 16384;
+
 // Largest vocabulary the backward handles (its padded rows must be
 // addressable by 32-bit buffer offsets over 256-row tiles).
 constexpr long long kBwdMaxVocab = (1LL << 31) / (256LL * 4) - 256;
