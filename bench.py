@@ -339,6 +339,58 @@ def prefill_leg(s, device, chunk=16384, calls=5):
     }
 
 
+def loss_leg(s, device, calls=20):
+    """The group advantage and the REINFORCE Zero loss (with its per-token
+    coefficients) on their own: at the benchmark batch, and scaled up to
+    ~16.8M tokens as 65,536 responses of 256 tokens, as 2,048 of 8,192, and
+    as 2M of 8 (a degenerate mix: one wavefront per response, eight lanes of
+    it busy), groups of 8. They move a few bytes per token
+    and are HBM-bound in principle; the bytes counted are what the two calls
+    must read and write (logprobs, rollout logprobs, coefficients, offsets,
+    rewards, advantages, per-response losses)."""
+    import torch
+    import invariant_token_logprobs_lm_amd as itl
+
+    def one(lp, lpr, rewards, goff, roff):
+        A = itl.group_advantage(rewards, goff)
+        return itl.reinforce_zero_loss(lp, lpr, A, roff)
+
+    def timed(args):
+        one(*args)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(calls):
+            one(*args)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / calls
+
+    def case(name, lp, lpr, rewards, goff, roff):
+        n_tok, n_resp, n_grp = lp.numel(), rewards.numel(), goff.numel() - 1
+        ms = timed((lp, lpr, rewards, goff, roff))
+        nbytes = 12 * n_tok + (8 + 4 + 4 + 4 + 4) * n_resp + 4 * n_grp
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        log(f"[bench] advantage + loss, {name}: {ms * 1e3:.1f} us per call, {gbs:.1f} GB/s "
+            f"({100 * gbs / PEAK_HBM_GBS:.2f}% of HBM peak)")
+        return {"case": name, "n_tok": n_tok, "responses": n_resp, "us_per_call": ms * 1e3,
+                "bytes_per_call": nbytes, "gb_per_s": gbs, "frac_hbm_peak": gbs / PEAK_HBM_GBS}
+
+    out = [case("benchmark batch", s["lp"], s["lpr"], s["rewards"], s["goff"], s["roff"])]
+    g = torch.Generator(device=device)
+    g.manual_seed(7)
+    for n_resp, T in ((65536, 256), (2048, 8192), (2 * 1024 * 1024, 8)):
+        n = n_resp * T
+        lp = -torch.rand(n, generator=g, device=device) * 20
+        lpr = lp + torch.randn(n, generator=g, device=device) * 0.05
+        rewards = torch.rand(n_resp, generator=g, device=device)
+        roff = torch.arange(0, n + 1, T, dtype=torch.int64, device=device)
+        goff = torch.arange(0, n_resp + 1, 8, dtype=torch.int32, device=device)
+        out.append(case(f"{n_resp} responses x {T} tokens", lp, lpr, rewards, goff, roff))
+        del lp, lpr, rewards, roff, goff
+    return out
+
+
 def mismatch_leg(s, device, calls=20, n_demo=4096, batch=64):
     """The mismatch diagnostics: (1) itl_mismatch_stats timed on the whole
     batch (learner logprobs, the rollout record with the workload's lag
@@ -567,6 +619,7 @@ def main():
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-loss", action="store_true")
     ap.add_argument("--no-mismatch", action="store_true")
     ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
@@ -646,6 +699,8 @@ def main():
         out["fp8"] = fp8_leg(s, device)
     if not args.no_prefill:
         out["prefill"] = prefill_leg(s, device)
+    if not args.no_loss:
+        out["loss"] = loss_leg(s, device)
     del s
     torch.cuda.empty_cache()
     if not args.no_decode:

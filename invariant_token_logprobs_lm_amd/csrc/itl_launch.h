@@ -32,6 +32,11 @@ hipError_t launch_reinforce_zero_loss(const float* logprob, const float* rollout
 
 size_t backward_workspace_bytes(long long n_tok, long long d, long long vocab, int dtype);
 
+// Responses of at most this many tokens are summed by one wavefront (a
+// 64-lane tree), longer ones by a 256-thread workgroup; the choice depends
+// on the response's length alone. Part of resp_loss's bits.
+constexpr int kShortResponse = 256;
+
 // Tokens per chunk of the backward (a multiple of the token block). dW's sum
 // over tokens is carried across chunks in this order, so it is part of dW's
 // bits; the build info reports it.

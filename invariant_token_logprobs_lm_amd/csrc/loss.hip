@@ -14,21 +14,27 @@
 // a few bytes per token and are bound by HBM bandwidth (or launch latency at
 // small sizes); lanes read consecutive elements.
 
+#include <algorithm>
+
 #include "device_common.h"
 #include "itl_config.h"
 #include "itl_launch.h"
 
 namespace itl {
 
+constexpr int kLongLossBlocks = 65536;  // workgroups walking the long responses (grid shape only)
+
 namespace {
 
-// One wavefront per group: lane j adds elements j, j+64, ... of the group in
-// ascending order, then a fixed xor butterfly combines the lanes.
-__global__ __launch_bounds__(64) void group_advantage_kernel(const float* __restrict__ rewards,
-                                                             const int32_t* __restrict__ goff, int n_resp,
-                                                             float* __restrict__ adv) {
-  const int g = blockIdx.x;
-  const int lane = threadIdx.x;
+// One wavefront per group (four per workgroup): lane j adds elements j,
+// j+64, ... of the group in ascending order, then a fixed xor butterfly
+// combines the lanes.
+__global__ __launch_bounds__(256) void group_advantage_kernel(const float* __restrict__ rewards,
+                                                              const int32_t* __restrict__ goff, int n_groups,
+                                                              int n_resp, float* __restrict__ adv) {
+  const int g = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (g >= n_groups) return;
   const int s = min(max(goff[g], 0), n_resp);
   const int e = min(max(goff[g + 1], s), n_resp);
   const int n = e - s;
@@ -53,36 +59,91 @@ __device__ __forceinline__ float block_sum256(float x, float* red) {
 
 __device__ __forceinline__ float ratio_of(float lp, float lpr) { return fast_exp2((lp - lpr) * kLog2e); }
 
-// One workgroup per response: thread j handles tokens j, j+256, ... of the
-// response in ascending order.
-__global__ __launch_bounds__(kLossThreads) void response_loss_kernel(
+// A response's tokens are summed by one of two fixed trees, chosen by its
+// length alone (so the bits still depend on nothing but the response):
+// up to kShortResponse tokens, one wavefront (lane j adds tokens j, j+64,
+// ... in ascending order, then the xor butterfly); longer ones, one
+// 256-thread workgroup (thread j adds tokens j, j+256, ..., then the
+// wavefront butterflies and the four wave sums in a fixed tree).
+__device__ __forceinline__ void finish_response(int i, long long s, long long e, float S, const float* lp,
+                                                const float* lpr, const float* adv, int n_resp, int tid, int stride,
+                                                float* resp_loss, float* coef) {
+  const long long T = e - s;
+  if (T <= 0) return;
+  const float A = adv[i];
+  if (tid == 0) resp_loss[i] = -A * (S / (float)T);
+  if (coef) {
+    const float k = (float)(-(double)A / ((double)n_resp * (double)T));
+    for (long long t = s + tid; t < e; t += stride) coef[t] = ratio_of(lp[t], lpr[t]) * k;
+  }
+}
+
+// Short responses: four per workgroup, one wavefront each.
+__global__ __launch_bounds__(256) void response_loss_short_kernel(
+    const float* __restrict__ lp, const float* __restrict__ lpr, const float* __restrict__ adv,
+    const int64_t* __restrict__ off, int n_resp, long long n_tok, float* __restrict__ resp_loss,
+    float* __restrict__ coef) {
+  const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (i >= n_resp) return;
+  const long long s = min(max(off[i], 0LL), n_tok);
+  const long long e = min(max(off[i + 1], s), n_tok);
+  if (e - s > kShortResponse) return;  // the long kernel's
+  float acc = 0.0f;
+  for (long long t = s + lane; t < e; t += 64) acc += ratio_of(lp[t], lpr[t]);
+  finish_response(i, s, e, wave_sum(acc), lp, lpr, adv, n_resp, lane, 64, resp_loss, coef);
+}
+
+// Long responses: one workgroup each, the workgroups walking the responses.
+__global__ __launch_bounds__(kLossThreads) void response_loss_long_kernel(
     const float* __restrict__ lp, const float* __restrict__ lpr, const float* __restrict__ adv,
     const int64_t* __restrict__ off, int n_resp, long long n_tok, float* __restrict__ resp_loss,
     float* __restrict__ coef) {
   __shared__ float red[4];
-  const int i = blockIdx.x;
-  const long long s = min(max(off[i], 0LL), n_tok);
-  const long long e = min(max(off[i + 1], s), n_tok);
-  const long long T = e - s;
-  float acc = 0.0f;
-  for (long long t = s + threadIdx.x; t < e; t += kLossThreads) acc += ratio_of(lp[t], lpr[t]);
-  const float S = block_sum256(acc, red);
-  if (T <= 0) return;
-  const float A = adv[i];
-  if (threadIdx.x == 0) resp_loss[i] = -A * (S / (float)T);
-  if (coef) {
-    const float k = (float)(-(double)A / ((double)n_resp * (double)T));
-    for (long long t = s + threadIdx.x; t < e; t += kLossThreads) coef[t] = ratio_of(lp[t], lpr[t]) * k;
+  for (int i = blockIdx.x; i < n_resp; i += gridDim.x) {
+    const long long s = min(max(off[i], 0LL), n_tok);
+    const long long e = min(max(off[i + 1], s), n_tok);
+    if (e - s <= kShortResponse) continue;  // the short kernel's (uniform across the workgroup)
+    float acc = 0.0f;
+    for (long long t = s + threadIdx.x; t < e; t += kLossThreads) acc += ratio_of(lp[t], lpr[t]);
+    finish_response(i, s, e, block_sum256(acc, red), lp, lpr, adv, n_resp, threadIdx.x, kLossThreads, resp_loss,
+                    coef);
   }
 }
 
-// Single workgroup: mean of the per-response losses in a fixed order.
+// Single workgroup: mean of the per-response losses in a fixed order. The
+// array is read as 16-byte groups of four, thread j taking groups j, j +
+// kMeanThreads, ... (each pass of the workgroup reads one contiguous 16 KiB
+// run) into four accumulators, one per position in the group, combined in a
+// fixed order; the last n_resp mod 4 values go to thread 0's accumulators;
+// then the wavefront butterflies and the wave sums in order. A fixed
+// function of n_resp.
 __global__ __launch_bounds__(kMeanThreads) void loss_mean_kernel(const float* __restrict__ resp_loss, int n_resp,
                                                                  float* __restrict__ loss) {
   __shared__ float red[kMeanThreads / 64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  float acc = 0.0f;
-  for (int i = threadIdx.x; i < n_resp; i += kMeanThreads) acc += resp_loss[i];
+  const int n4 = n_resp / 4;
+  const bool vec = (reinterpret_cast<uintptr_t>(resp_loss) & 15) == 0;
+  float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
+  for (int g = threadIdx.x; g < n4; g += kMeanThreads) {
+    float4 v;
+    if (vec) {
+      v = reinterpret_cast<const float4*>(resp_loss)[g];
+    } else {
+      v = make_float4(resp_loss[4 * g], resp_loss[4 * g + 1], resp_loss[4 * g + 2], resp_loss[4 * g + 3]);
+    }
+    a0 += v.x;
+    a1 += v.y;
+    a2 += v.z;
+    a3 += v.w;
+  }
+  if (threadIdx.x == 0) {
+    const int r = 4 * n4;
+    if (r < n_resp) a0 += resp_loss[r];
+    if (r + 1 < n_resp) a1 += resp_loss[r + 1];
+    if (r + 2 < n_resp) a2 += resp_loss[r + 2];
+  }
+  float acc = (a0 + a1) + (a2 + a3);
   acc = wave_sum(acc);
   if (lane == 0) red[wave] = acc;
   __syncthreads();
@@ -111,17 +172,21 @@ __global__ void check_offsets_kernel(const int64_t* __restrict__ off, int n_resp
 
 hipError_t launch_group_advantage(const float* rewards, const int32_t* group_offsets, int n_groups, int n_resp,
                                   float* advantages, hipStream_t stream) {
-  hipLaunchKernelGGL(group_advantage_kernel, dim3(n_groups), dim3(64), 0, stream, rewards, group_offsets, n_resp,
-                     advantages);
+  hipLaunchKernelGGL(group_advantage_kernel, dim3((unsigned)ceil_div(n_groups, 4)), dim3(256), 0, stream, rewards,
+                     group_offsets, n_groups, n_resp, advantages);
   return hipGetLastError();
 }
 
 hipError_t launch_reinforce_zero_loss(const float* logprob, const float* rollout_logprob, const float* advantages,
                                       const int64_t* resp_offsets, int n_resp, long long n_tok, float* resp_loss,
                                       float* loss, float* coef, hipStream_t stream) {
-  hipLaunchKernelGGL(response_loss_kernel, dim3(n_resp), dim3(kLossThreads), 0, stream, logprob, rollout_logprob,
-                     advantages, resp_offsets, n_resp, n_tok, resp_loss, coef);
+  hipLaunchKernelGGL(response_loss_short_kernel, dim3((unsigned)ceil_div(n_resp, 4)), dim3(256), 0, stream, logprob,
+                     rollout_logprob, advantages, resp_offsets, n_resp, n_tok, resp_loss, coef);
   hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(response_loss_long_kernel, dim3((unsigned)std::min(n_resp, kLongLossBlocks)), dim3(kLossThreads),
+                     0, stream, logprob, rollout_logprob, advantages, resp_offsets, n_resp, n_tok, resp_loss, coef);
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(loss_mean_kernel, dim3(1), dim3(kMeanThreads), 0, stream, resp_loss, n_resp, loss);
   return hipGetLastError();
