@@ -199,3 +199,48 @@ def test_response_loss_batch_invariance(cuda):
     off2 = np.concatenate([[0], np.cumsum(T[perm])]).astype(np.int64)
     rl2, _, _ = _gpu_loss(lp[idx], lpr[idx], A[perm], off2, cuda)
     assert same_bits(rl[torch.from_numpy(perm).to(cuda)], rl2)
+
+
+def test_response_loss_across_the_short_long_boundary(cuda):
+    """Responses just below, at and above the length where the sum changes
+    from one wavefront to one workgroup (256 tokens), mixed with tiny and
+    long ones: parity with the oracle, and each response's loss has the same
+    bits alone, in the batch, and in a permuted sub-batch."""
+    import re
+    import torch
+
+    itl = _itl()
+    short = int(re.search(r"short_response=(\d+)", itl.build_info()).group(1))
+    lens = [1, 63, 64, 65, short - 1, short, short + 1, 1000, 2 * short + 3, 7]
+    rng = np.random.default_rng(21)
+    T = np.array(lens * 3)
+    N = T.size
+    off = np.concatenate([[0], np.cumsum(T)]).astype(np.int64)
+    lp = -np.abs(rng.normal(6, 2, off[-1])).astype(np.float32)
+    lpr = (lp + rng.normal(0, 0.05, off[-1])).astype(np.float32)
+    A = rng.normal(0, 1, N).astype(np.float32)
+    rl, _, c = _check_loss(lp, lpr, A, off, cuda, "short/long boundary")
+    for i in range(len(lens)):
+        rl1, _, _ = _gpu_loss(lp[off[i]:off[i + 1]], lpr[off[i]:off[i + 1]], A[i:i + 1],
+                              np.array([0, T[i]], dtype=np.int64), cuda)
+        assert same_bits(rl1, rl[i:i + 1]), lens[i]
+    perm = rng.permutation(N)[:11]
+    idx = np.concatenate([np.arange(off[i], off[i + 1]) for i in perm])
+    off2 = np.concatenate([[0], np.cumsum(T[perm])]).astype(np.int64)
+    rl2, _, _ = _gpu_loss(lp[idx], lpr[idx], A[perm], off2, cuda)
+    assert same_bits(rl[torch.from_numpy(perm).to(cuda)], rl2)
+
+
+def test_loss_many_responses_mean(cuda):
+    """Many responses (the mean's 16-byte passes and its ragged end): parity
+    of the loss and run-to-run bit equality."""
+    rng = np.random.default_rng(8)
+    N = 100003
+    T = rng.integers(1, 40, N)
+    off = np.concatenate([[0], np.cumsum(T)]).astype(np.int64)
+    lp = -np.abs(rng.normal(5, 2, off[-1])).astype(np.float32)
+    lpr = (lp + rng.normal(0, 0.1, off[-1])).astype(np.float32)
+    A = rng.normal(0, 1, N).astype(np.float32)
+    _, L, _ = _check_loss(lp, lpr, A, off, cuda, "many responses")
+    _, L2, _ = _gpu_loss(lp, lpr, A, off, cuda)
+    assert same_bits(L, L2)
