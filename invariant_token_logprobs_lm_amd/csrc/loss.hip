@@ -22,7 +22,7 @@
 
 namespace itl {
 
-constexpr int kLongLossBlocks = 65536;  // workgroups walking the long responses (grid shape only)
+constexpr int kLongLossBlocks = 4096;  // workgroups of the long-response kernel (grid shape only)
 
 namespace {
 
@@ -94,20 +94,40 @@ __global__ __launch_bounds__(256) void response_loss_short_kernel(
   finish_response(i, s, e, wave_sum(acc), lp, lpr, adv, n_resp, lane, 64, resp_loss, coef);
 }
 
-// Long responses: one workgroup each, the workgroups walking the responses.
+// Long responses: one workgroup each. Workgroup b owns a contiguous run of
+// responses (one response per workgroup up to kLongLossBlocks responses);
+// its threads read the run's lengths 256 at a time and the workgroup then
+// sums the long ones in order (the short kernel has the others).
 __global__ __launch_bounds__(kLossThreads) void response_loss_long_kernel(
     const float* __restrict__ lp, const float* __restrict__ lpr, const float* __restrict__ adv,
     const int64_t* __restrict__ off, int n_resp, long long n_tok, float* __restrict__ resp_loss,
     float* __restrict__ coef) {
   __shared__ float red[4];
-  for (int i = blockIdx.x; i < n_resp; i += gridDim.x) {
-    const long long s = min(max(off[i], 0LL), n_tok);
-    const long long e = min(max(off[i + 1], s), n_tok);
-    if (e - s <= kShortResponse) continue;  // the short kernel's (uniform across the workgroup)
-    float acc = 0.0f;
-    for (long long t = s + threadIdx.x; t < e; t += kLossThreads) acc += ratio_of(lp[t], lpr[t]);
-    finish_response(i, s, e, block_sum256(acc, red), lp, lpr, adv, n_resp, threadIdx.x, kLossThreads, resp_loss,
-                    coef);
+  __shared__ int is_long[kLossThreads];
+  const int per = (n_resp + (int)gridDim.x - 1) / (int)gridDim.x;
+  const int r0 = min((int)blockIdx.x * per, n_resp), r1 = min(r0 + per, n_resp);
+  for (int c0 = r0; c0 < r1; c0 += kLossThreads) {
+    const int i = c0 + (int)threadIdx.x;
+    int lg = 0;
+    if (i < r1) {
+      const long long s = min(max(off[i], 0LL), n_tok);
+      const long long e = min(max(off[i + 1], s), n_tok);
+      lg = e - s > kShortResponse;
+    }
+    is_long[threadIdx.x] = lg;
+    __syncthreads();
+    const int m = min(kLossThreads, r1 - c0);
+    for (int j = 0; j < m; ++j) {
+      if (!is_long[j]) continue;  // the same value in every thread
+      const int r = c0 + j;
+      const long long s = min(max(off[r], 0LL), n_tok);
+      const long long e = min(max(off[r + 1], s), n_tok);
+      float acc = 0.0f;
+      for (long long t = s + threadIdx.x; t < e; t += kLossThreads) acc += ratio_of(lp[t], lpr[t]);
+      finish_response(r, s, e, block_sum256(acc, red), lp, lpr, adv, n_resp, threadIdx.x, kLossThreads, resp_loss,
+                      coef);
+    }
+    __syncthreads();  // every thread is done with is_long before it is refilled
   }
 }
 
