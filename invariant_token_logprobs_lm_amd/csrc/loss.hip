@@ -145,18 +145,28 @@ __global__ __launch_bounds__(kMeanThreads) void loss_mean_kernel(const float* __
   const int n4 = n_resp / 4;
   const bool vec = (reinterpret_cast<uintptr_t>(resp_loss) & 15) == 0;
   float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
-  for (int g = threadIdx.x; g < n4; g += kMeanThreads) {
-    float4 v;
-    if (vec) {
-      v = reinterpret_cast<const float4*>(resp_loss)[g];
-    } else {
-      v = make_float4(resp_loss[4 * g], resp_loss[4 * g + 1], resp_loss[4 * g + 2], resp_loss[4 * g + 3]);
-    }
+  auto group = [&](int g) {
+    return vec ? reinterpret_cast<const float4*>(resp_loss)[g]
+               : make_float4(resp_loss[4 * g], resp_loss[4 * g + 1], resp_loss[4 * g + 2], resp_loss[4 * g + 3]);
+  };
+  auto add = [&](float4 v) {
     a0 += v.x;
     a1 += v.y;
     a2 += v.z;
     a3 += v.w;
+  };
+  int g = threadIdx.x;
+  // Four groups loaded before any is added (the same additions in the same
+  // order as one group at a time): four loads in flight per thread.
+  for (; g + 3 * kMeanThreads < n4; g += 4 * kMeanThreads) {
+    const float4 v0 = group(g), v1 = group(g + kMeanThreads), v2 = group(g + 2 * kMeanThreads),
+                 v3 = group(g + 3 * kMeanThreads);
+    add(v0);
+    add(v1);
+    add(v2);
+    add(v3);
   }
+  for (; g < n4; g += kMeanThreads) add(group(g));
   if (threadIdx.x == 0) {
     const int r = 4 * n4;
     if (r < n_resp) a0 += resp_loss[r];
