@@ -333,9 +333,9 @@ const char* itl_build_info(void) {
              "itl 0.2 arch=gfx950 threads=%d token_block=%d vocab_tile=%d k_step_bytes=%d w_slots=%d h_slots=%d "
              "swap_slots_over_k_steps=%d max_slices=%d slices=balanced narrow_max_tokens=%d narrow_token_block=%d "
              "mfma_bf16=32x32x16 mfma_f32=32x32x2 fp8=e4m3_row_scaled mfma_fp8=32x32x64 mxfp4=e2m1_e8m0_32 "
-             "bwd_chunk_tokens=%d short_response=%d loss_threads=%d mean_threads=%d",
+             "bwd_chunk_tokens=%d tiny_response=%d short_response=%d loss_threads=%d mean_threads=%d",
              itl::kThreads, itl::kBT, itl::kBV, itl::kStepBytes, itl::kWSlots, itl::kHSlots, itl::kNearBMaxSteps,
-             itl::kMaxSlices, itl::kNarrowMaxTokens, itl::kNarrowBRows, itl::kBwdChunkTokens, itl::kShortResponse, itl::kLossThreads,
+             itl::kMaxSlices, itl::kNarrowMaxTokens, itl::kNarrowBRows, itl::kBwdChunkTokens, itl::kTinyResponse, itl::kShortResponse, itl::kLossThreads,
              itl::kMeanThreads);
     return std::string(buf);
   }();

@@ -32,9 +32,11 @@ hipError_t launch_reinforce_zero_loss(const float* logprob, const float* rollout
 
 size_t backward_workspace_bytes(long long n_tok, long long d, long long vocab, int dtype);
 
-// Responses of at most this many tokens are summed by one wavefront (a
-// 64-lane tree), longer ones by a 256-thread workgroup; the choice depends
-// on the response's length alone. Part of resp_loss's bits.
+// Responses of at most kTinyResponse tokens are summed by eight lanes, of
+// at most kShortResponse by one wavefront (a 64-lane tree), longer ones by a
+// 256-thread workgroup; the choice depends on the response's length alone.
+// Part of resp_loss's bits.
+constexpr int kTinyResponse = 8;
 constexpr int kShortResponse = 256;
 
 // Tokens per chunk of the backward (a multiple of the token block). dW's sum

@@ -22,7 +22,8 @@
 
 namespace itl {
 
-constexpr int kLongLossBlocks = 4096;  // workgroups of the long-response kernel (grid shape only)
+constexpr int kLongLossBlocks = 4096;    // workgroups of the long-response kernel (grid shape only)
+constexpr int kShortLossBlocks = 16384;  // workgroups of the short-response kernel (grid shape only)
 
 namespace {
 
@@ -59,12 +60,14 @@ __device__ __forceinline__ float block_sum256(float x, float* red) {
 
 __device__ __forceinline__ float ratio_of(float lp, float lpr) { return fast_exp2((lp - lpr) * kLog2e); }
 
-// A response's tokens are summed by one of two fixed trees, chosen by its
-// length alone (so the bits still depend on nothing but the response):
-// up to kShortResponse tokens, one wavefront (lane j adds tokens j, j+64,
-// ... in ascending order, then the xor butterfly); longer ones, one
-// 256-thread workgroup (thread j adds tokens j, j+256, ..., then the
-// wavefront butterflies and the four wave sums in a fixed tree).
+// A response's tokens are summed by one of three fixed trees, chosen by its
+// length alone (so the bits still depend on nothing but the response): up
+// to kTinyResponse tokens, eight lanes (lane j holds token j; an xor
+// butterfly over the eight); up to kShortResponse tokens, one wavefront
+// (lane j adds tokens j, j+64, ... in ascending order, then the xor
+// butterfly); longer ones, one 256-thread workgroup (thread j adds tokens j,
+// j+256, ..., then the wavefront butterflies and the four wave sums in a
+// fixed tree).
 __device__ __forceinline__ void finish_response(int i, long long s, long long e, float S, const float* lp,
                                                 const float* lpr, const float* adv, int n_resp, int tid, int stride,
                                                 float* resp_loss, float* coef) {
@@ -78,20 +81,63 @@ __device__ __forceinline__ void finish_response(int i, long long s, long long e,
   }
 }
 
-// Short responses: four per workgroup, one wavefront each.
+// Tiny responses: eight per wavefront, eight lanes each.
+__global__ __launch_bounds__(256) void response_loss_tiny_kernel(
+    const float* __restrict__ lp, const float* __restrict__ lpr, const float* __restrict__ adv,
+    const int64_t* __restrict__ off, int n_resp, long long n_tok, float* __restrict__ resp_loss,
+    float* __restrict__ coef) {
+  const int i = blockIdx.x * 32 + (threadIdx.x >> 3);
+  const int j = threadIdx.x & 7;
+  long long s = 0, e = 0;
+  if (i < n_resp) {
+    s = min(max(off[i], 0LL), n_tok);
+    e = min(max(off[i + 1], s), n_tok);
+  }
+  const long long T = e - s;
+  const bool mine = T >= 1 && T <= kTinyResponse;
+  const float r = mine && j < T ? ratio_of(lp[s + j], lpr[s + j]) : 0.0f;
+  // every lane takes part in the shuffles; xor offsets below 8 stay in the
+  // eight-lane segment
+  float S = r;
+  S += __shfl_xor(S, 4, 64);
+  S += __shfl_xor(S, 2, 64);
+  S += __shfl_xor(S, 1, 64);
+  if (!mine) return;
+  const float A = adv[i];
+  if (j == 0) resp_loss[i] = -A * (S / (float)T);
+  if (coef && j < T) coef[s + j] = r * (float)(-(double)A / ((double)n_resp * (double)T));
+}
+
+// Short responses: each wavefront owns a contiguous run of responses, reads
+// their lengths 64 at a time and sums the short ones in order, one at a time.
 __global__ __launch_bounds__(256) void response_loss_short_kernel(
     const float* __restrict__ lp, const float* __restrict__ lpr, const float* __restrict__ adv,
     const int64_t* __restrict__ off, int n_resp, long long n_tok, float* __restrict__ resp_loss,
     float* __restrict__ coef) {
-  const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  if (i >= n_resp) return;
-  const long long s = min(max(off[i], 0LL), n_tok);
-  const long long e = min(max(off[i + 1], s), n_tok);
-  if (e - s > kShortResponse) return;  // the long kernel's
-  float acc = 0.0f;
-  for (long long t = s + lane; t < e; t += 64) acc += ratio_of(lp[t], lpr[t]);
-  finish_response(i, s, e, wave_sum(acc), lp, lpr, adv, n_resp, lane, 64, resp_loss, coef);
+  const int n_waves = (int)gridDim.x * 4;
+  const int wv = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6);
+  const int per = (n_resp + n_waves - 1) / n_waves;
+  const int r0 = min(wv * per, n_resp), r1 = min(r0 + per, n_resp);
+  for (int c0 = r0; c0 < r1; c0 += 64) {
+    bool mine = false;
+    if (c0 + lane < r1) {
+      const long long s = min(max(off[c0 + lane], 0LL), n_tok);
+      const long long e = min(max(off[c0 + lane + 1], s), n_tok);
+      mine = e - s > kTinyResponse && e - s <= kShortResponse;
+    }
+    uint64_t todo = __builtin_amdgcn_ballot_w64(mine);
+    while (todo) {  // ascending response order
+      const int k = __builtin_ctzll(todo);
+      todo &= todo - 1;
+      const int i = c0 + k;
+      const long long s = min(max(off[i], 0LL), n_tok);
+      const long long e = min(max(off[i + 1], s), n_tok);
+      float acc = 0.0f;
+      for (long long t = s + lane; t < e; t += 64) acc += ratio_of(lp[t], lpr[t]);
+      finish_response(i, s, e, wave_sum(acc), lp, lpr, adv, n_resp, lane, 64, resp_loss, coef);
+    }
+  }
 }
 
 // Long responses: one workgroup each. Workgroup b owns a contiguous run of
@@ -210,9 +256,14 @@ hipError_t launch_group_advantage(const float* rewards, const int32_t* group_off
 hipError_t launch_reinforce_zero_loss(const float* logprob, const float* rollout_logprob, const float* advantages,
                                       const int64_t* resp_offsets, int n_resp, long long n_tok, float* resp_loss,
                                       float* loss, float* coef, hipStream_t stream) {
-  hipLaunchKernelGGL(response_loss_short_kernel, dim3((unsigned)ceil_div(n_resp, 4)), dim3(256), 0, stream, logprob,
+  hipLaunchKernelGGL(response_loss_tiny_kernel, dim3((unsigned)ceil_div(n_resp, 32)), dim3(256), 0, stream, logprob,
                      rollout_logprob, advantages, resp_offsets, n_resp, n_tok, resp_loss, coef);
   hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(response_loss_short_kernel, dim3((unsigned)std::min<long long>(ceil_div(n_resp, 4), kShortLossBlocks)),
+                     dim3(256), 0, stream, logprob, rollout_logprob, advantages, resp_offsets, n_resp, n_tok, resp_loss,
+                     coef);
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(response_loss_long_kernel, dim3((unsigned)std::min(n_resp, kLongLossBlocks)), dim3(kLossThreads),
                      0, stream, logprob, rollout_logprob, advantages, resp_offsets, n_resp, n_tok, resp_loss, coef);
