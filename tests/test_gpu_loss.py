@@ -202,16 +202,16 @@ def test_response_loss_batch_invariance(cuda):
 
 
 def test_response_loss_across_the_short_long_boundary(cuda):
-    """Responses just below, at and above the length where the sum changes
-    from one wavefront to one workgroup (256 tokens), mixed with tiny and
-    long ones: parity with the oracle, and each response's loss has the same
+    """Responses just below, at and above the lengths where the sum changes
+    tree (eight lanes / one wavefront / one workgroup), mixed with others: parity with the oracle, and each response's loss has the same
     bits alone, in the batch, and in a permuted sub-batch."""
     import re
     import torch
 
     itl = _itl()
     short = int(re.search(r"short_response=(\d+)", itl.build_info()).group(1))
-    lens = [1, 63, 64, 65, short - 1, short, short + 1, 1000, 2 * short + 3, 7]
+    tiny = int(re.search(r"tiny_response=(\d+)", itl.build_info()).group(1))
+    lens = [1, tiny - 1, tiny, tiny + 1, 63, 64, 65, short - 1, short, short + 1, 1000, 2 * short + 3, 7]
     rng = np.random.default_rng(21)
     T = np.array(lens * 3)
     N = T.size
