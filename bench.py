@@ -343,17 +343,24 @@ def loss_leg(s, device, calls=20):
     """The group advantage and the REINFORCE Zero loss (with its per-token
     coefficients) on their own: at the benchmark batch, and scaled up to
     ~16.8M tokens as 65,536 responses of 256 tokens, as 2,048 of 8,192, and
-    as 2M of 8 (a degenerate mix: one wavefront per response, eight lanes of
-    it busy), groups of 8. They move a few bytes per token
+    as 2M of 8, groups of 8. The loss runs a token pass (one workgroup per
+    2048-token window of the packed batch, summing the response-relative
+    segments that start in it: one lane per segment of up to 32 tokens, a
+    wavefront up to 256, the workgroup beyond), a finishing pass over chunks
+    of 1024 responses and, past one chunk, a final sum; the advantage reduces
+    groups of up to 8 with eight lanes each. They move a few bytes per token
     and are HBM-bound in principle; the bytes counted are what the two calls
     must read and write (logprobs, rollout logprobs, coefficients, offsets,
-    rewards, advantages, per-response losses)."""
+    rewards, advantages, per-response losses). Each case is timed twice: as
+    eager calls (host launch cost included, which dominates a small batch)
+    and as the same calls captured once in a HIP graph and replayed (the
+    device's own time; the figure reported as us_per_call)."""
     import torch
     import invariant_token_logprobs_lm_amd as itl
 
-    def one(lp, lpr, rewards, goff, roff):
+    def one(lp, lpr, rewards, goff, roff, ws):
         A = itl.group_advantage(rewards, goff)
-        return itl.reinforce_zero_loss(lp, lpr, A, roff)
+        return itl.reinforce_zero_loss(lp, lpr, A, roff, workspace=ws)
 
     def timed(args):
         one(*args)
@@ -366,15 +373,41 @@ def loss_leg(s, device, calls=20):
         torch.cuda.synchronize()
         return a.elapsed_time(b) / calls
 
+    def timed_graph(args, reps=5):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            one(*args)  # warm the allocator on the capture stream
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(calls):
+                one(*args)
+        graph.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            graph.replay()
+        b.record()
+        torch.cuda.synchronize()
+        del graph
+        return a.elapsed_time(b) / (reps * calls)
+
     def case(name, lp, lpr, rewards, goff, roff):
         n_tok, n_resp, n_grp = lp.numel(), rewards.numel(), goff.numel() - 1
-        ms = timed((lp, lpr, rewards, goff, roff))
+        ws = torch.empty(max(itl.loss_workspace_bytes(n_tok, n_resp), 1), dtype=torch.uint8, device=device)
+        args = (lp, lpr, rewards, goff, roff, ws)
+        ms_eager = timed(args)
+        ms = timed_graph(args)
         nbytes = 12 * n_tok + (8 + 4 + 4 + 4 + 4) * n_resp + 4 * n_grp
         gbs = nbytes / (ms * 1e-3) / 1e9
-        log(f"[bench] advantage + loss, {name}: {ms * 1e3:.1f} us per call, {gbs:.1f} GB/s "
-            f"({100 * gbs / PEAK_HBM_GBS:.2f}% of HBM peak)")
+        log(f"[bench] advantage + loss, {name}: {ms * 1e3:.1f} us per call replayed from a graph "
+            f"({ms_eager * 1e3:.1f} us eager), {gbs:.1f} GB/s ({100 * gbs / PEAK_HBM_GBS:.2f}% of HBM peak)")
         return {"case": name, "n_tok": n_tok, "responses": n_resp, "us_per_call": ms * 1e3,
-                "bytes_per_call": nbytes, "gb_per_s": gbs, "frac_hbm_peak": gbs / PEAK_HBM_GBS}
+                "us_per_call_eager": ms_eager * 1e3, "bytes_per_call": nbytes, "gb_per_s": gbs,
+                "frac_hbm_peak": gbs / PEAK_HBM_GBS}
 
     out = [case("benchmark batch", s["lp"], s["lpr"], s["rewards"], s["goff"], s["roff"])]
     g = torch.Generator(device=device)

@@ -62,8 +62,9 @@ def _load():
                                                           _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64,
                                                           _c_void_p, _size, _c_void_p]),
         "itl_group_advantage": (ctypes.c_int, [_c_void_p, _c_void_p, _i32, _i32, _c_void_p, _c_void_p]),
+        "itl_reinforce_zero_loss_workspace_bytes": (_size, [_i64, _i32]),
         "itl_reinforce_zero_loss": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _i64,
-                                                   _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
+                                                   _c_void_p, _c_void_p, _c_void_p, _c_void_p, _size, _c_void_p]),
         "itl_reinforce_zero_backward_workspace_bytes": (_size, [_i64, _i64, _i64, ctypes.c_int]),
         "itl_reinforce_zero_backward": (ctypes.c_int, [_c_void_p, _c_void_p, ctypes.c_int, _i64, _i64, _i64,
                                                        _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
@@ -102,6 +103,7 @@ EXPORTS = (
     "itl_lmhead_logprob",
     "itl_lmhead_logprob_keep_logits",
     "itl_group_advantage",
+    "itl_reinforce_zero_loss_workspace_bytes",
     "itl_reinforce_zero_loss",
     "itl_reinforce_zero_backward_workspace_bytes",
     "itl_reinforce_zero_backward",
@@ -243,7 +245,11 @@ def group_advantage(rewards, group_offsets, *, advantages=None):
     return advantages
 
 
-def reinforce_zero_loss(logprob, rollout_logprob, advantages, resp_offsets, *, want_coef=True):
+def loss_workspace_bytes(n_tok, n_resp):
+    return int(lib.itl_reinforce_zero_loss_workspace_bytes(n_tok, n_resp))
+
+
+def reinforce_zero_loss(logprob, rollout_logprob, advantages, resp_offsets, *, want_coef=True, workspace=None):
     """(resp_loss fp32 [N], loss fp32 [1], coef fp32 [n_tok] or None)."""
     _need(logprob, "logprob", (torch.float32,), ndim=1)
     dev = logprob.device
@@ -257,8 +263,13 @@ def reinforce_zero_loss(logprob, rollout_logprob, advantages, resp_offsets, *, w
     resp_loss = torch.empty(n_resp, dtype=torch.float32, device=dev)
     loss = torch.empty(1, dtype=torch.float32, device=dev)
     coef = torch.empty(n_tok, dtype=torch.float32, device=dev) if want_coef else None
+    need = loss_workspace_bytes(n_tok, n_resp)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", (torch.uint8,), device=dev)
     _check(lib.itl_reinforce_zero_loss(_ptr(logprob), _ptr(rollout_logprob), _ptr(advantages), _ptr(resp_offsets),
-                                       n_resp, n_tok, _ptr(resp_loss), _ptr(loss), _ptr(coef), _stream(dev)))
+                                       n_resp, n_tok, _ptr(resp_loss), _ptr(loss), _ptr(coef), _ptr(workspace),
+                                       workspace.numel(), _stream(dev)))
     return resp_loss, loss, coef
 
 

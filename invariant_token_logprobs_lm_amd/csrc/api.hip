@@ -30,6 +30,8 @@ itl_status hip_fail(hipError_t e, const char* where) {
 constexpr int64_t kMaxTok = (int64_t)INT32_MAX - itl::kBT;
 constexpr int64_t kMaxVocab = (int64_t)INT32_MAX - itl::kBV;
 constexpr int64_t kFp8DMultiple = 128;  // one 128-byte K step = 128 E4M3 values
+// the loss's token pass has one workgroup per 2048-token window
+constexpr int64_t kMaxLossTok = (int64_t)INT32_MAX * itl::kSegTokens;
 
 int elem_size(itl_dtype dt) { return dt == ITL_BF16 ? 2 : 4; }
 
@@ -120,17 +122,26 @@ itl_status itl_group_advantage(const float* rewards, const int32_t* group_offset
   return e == hipSuccess ? ITL_OK : hip_fail(e, "itl_group_advantage");
 }
 
+size_t itl_reinforce_zero_loss_workspace_bytes(int64_t n_tok, int32_t n_resp) {
+  if (n_tok < 0 || n_resp < 0 || n_tok > kMaxLossTok) return SIZE_MAX;
+  return itl::loss_workspace_bytes(n_tok, n_resp);
+}
+
 itl_status itl_reinforce_zero_loss(const float* logprob, const float* rollout_logprob, const float* advantages,
                                    const int64_t* resp_offsets, int32_t n_resp, int64_t n_tok, float* resp_loss,
-                                   float* loss, float* coef, void* stream) {
+                                   float* loss, float* coef, void* workspace, size_t workspace_bytes, void* stream) {
   g_last_error.clear();
   if (n_resp < 0 || n_tok < 0) return fail(ITL_ERR_INVALID_ARG, "n_resp and n_tok must be >= 0");
+  if (n_tok > kMaxLossTok) return fail(ITL_ERR_UNSUPPORTED, "n_tok too large for one call");
   if (n_resp == 0) return ITL_OK;
   if (!resp_offsets || !advantages || !resp_loss || !loss)
     return fail(ITL_ERR_INVALID_ARG, "null offsets, advantages or outputs");
   if (n_tok > 0 && (!logprob || !rollout_logprob)) return fail(ITL_ERR_INVALID_ARG, "null logprob arrays");
+  if (!workspace || workspace_bytes < itl::loss_workspace_bytes(n_tok, n_resp))
+    return fail(ITL_ERR_WORKSPACE, "workspace missing or smaller than itl_reinforce_zero_loss_workspace_bytes()");
+  if (misaligned(workspace)) return fail(ITL_ERR_WORKSPACE, "workspace must be 256-byte aligned");
   hipError_t e = itl::launch_reinforce_zero_loss(logprob, rollout_logprob, advantages, resp_offsets, n_resp, n_tok,
-                                                 resp_loss, loss, coef, static_cast<hipStream_t>(stream));
+                                                 resp_loss, loss, coef, workspace, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ITL_OK : hip_fail(e, "itl_reinforce_zero_loss");
 }
 
@@ -328,15 +339,16 @@ const char* itl_last_error(void) { return g_last_error.c_str(); }
 
 const char* itl_build_info(void) {
   static const std::string info = [] {
-    char buf[512];
+    char buf[768];
     snprintf(buf, sizeof buf,
              "itl 0.2 arch=gfx950 threads=%d token_block=%d vocab_tile=%d k_step_bytes=%d w_slots=%d h_slots=%d "
              "swap_slots_over_k_steps=%d max_slices=%d slices=balanced narrow_max_tokens=%d narrow_token_block=%d "
              "mfma_bf16=32x32x16 mfma_f32=32x32x2 fp8=e4m3_row_scaled mfma_fp8=32x32x64 mxfp4=e2m1_e8m0_32 "
-             "bwd_chunk_tokens=%d tiny_response=%d short_response=%d loss_threads=%d mean_threads=%d",
+             "bwd_chunk_tokens=%d loss_segment_tokens=%d loss_lane_segment=%d loss_wave_segment=%d loss_threads=%d "
+             "loss_mean_chunk=%d loss_sums=f64",
              itl::kThreads, itl::kBT, itl::kBV, itl::kStepBytes, itl::kWSlots, itl::kHSlots, itl::kNearBMaxSteps,
-             itl::kMaxSlices, itl::kNarrowMaxTokens, itl::kNarrowBRows, itl::kBwdChunkTokens, itl::kTinyResponse, itl::kShortResponse, itl::kLossThreads,
-             itl::kMeanThreads);
+             itl::kMaxSlices, itl::kNarrowMaxTokens, itl::kNarrowBRows, itl::kBwdChunkTokens, itl::kSegTokens,
+             itl::kLaneSeg, itl::kWaveSeg, itl::kLossThreads, itl::kFinishChunk);
     return std::string(buf);
   }();
   return info.c_str();

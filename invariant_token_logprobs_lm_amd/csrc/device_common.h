@@ -48,4 +48,11 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
+// The same butterfly in fp64.
+__device__ __forceinline__ double wave_sum_d(double x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+
 }  // namespace itl

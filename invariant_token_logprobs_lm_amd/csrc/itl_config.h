@@ -34,8 +34,19 @@ constexpr int kNearBMaxSteps = 64;   // load schedule only: K loops longer than 
 constexpr int kDMultiple = 64;       // d must be a multiple of this
 constexpr int kF8WideMinD = 256;     // the wide FP8 kernel needs two K steps of 128 values; smaller d runs narrow
 
-constexpr int kLossThreads = 256;    // threads per response in the loss kernel
-constexpr int kMeanThreads = 1024;   // threads of the single-block mean
+// REINFORCE Zero loss. A response is cut into segments of kSegTokens tokens
+// counted from its first token; a segment is summed by one of three trees
+// chosen by its length alone (up to kLaneSeg tokens: one lane in token order;
+// up to kWaveSeg: one wavefront, lane j adding tokens j, j + 64, ...; longer:
+// the token pass's workgroup, thread j adding tokens j, j + kLossThreads, ...);
+// the segments are added in order. The mean over responses is taken over
+// chunks of kFinishChunk consecutive responses, then over the chunks in
+// order. All of it is part of the loss's bits.
+constexpr int kSegTokens = 2048;
+constexpr int kLaneSeg = 32;
+constexpr int kWaveSeg = 256;
+constexpr int kLossThreads = 512;    // threads of a token-pass workgroup
+constexpr int kFinishChunk = 1024;   // responses per workgroup of the finishing pass (4 per thread)
 
 inline long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
 

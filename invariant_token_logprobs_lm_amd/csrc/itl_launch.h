@@ -25,19 +25,16 @@ hipError_t launch_lse_combine(const float2* part, const float* zy, int n_tok, in
 hipError_t launch_group_advantage(const float* rewards, const int32_t* group_offsets, int n_groups,
                                   int n_resp, float* advantages, hipStream_t stream);
 
+// Workspace of the loss: the fp64 per-response losses, the fp64 segment sums
+// of responses longer than one segment, and the fp64 partial sums of the mean.
+size_t loss_workspace_bytes(long long n_tok, long long n_resp);
+
 hipError_t launch_reinforce_zero_loss(const float* logprob, const float* rollout_logprob,
                                       const float* advantages, const int64_t* resp_offsets, int n_resp,
                                       long long n_tok, float* resp_loss, float* loss, float* coef,
-                                      hipStream_t stream);
+                                      void* workspace, hipStream_t stream);
 
 size_t backward_workspace_bytes(long long n_tok, long long d, long long vocab, int dtype);
-
-// Responses of at most kTinyResponse tokens are summed by eight lanes, of
-// at most kShortResponse by one wavefront (a 64-lane tree), longer ones by a
-// 256-thread workgroup; the choice depends on the response's length alone.
-// Part of resp_loss's bits.
-constexpr int kTinyResponse = 8;
-constexpr int kShortResponse = 256;
 
 // Tokens per chunk of the backward (a multiple of the token block). dW's sum
 // over tokens is carried across chunks in this order, so it is part of dW's

@@ -8,225 +8,407 @@
 //   loss         = (1/N) sum_i resp_loss[i]                  (then over responses)
 //   coef[t]      = -ratio_t * A_i / (N * T_i)                (dloss/dlogprob_t, plain REINFORCE)
 //
-// Every sum runs over a segment-relative index with a tree fixed by the
-// segment's length: a group's advantages and a response's loss are the same
-// bits wherever the group or response sits in the batch. These kernels move
-// a few bytes per token and are bound by HBM bandwidth (or launch latency at
-// small sizes); lanes read consecutive elements.
+// Precision. ratio_t and coef[t] are fp32 values; every sum is fp64. The mean
+// over responses nearly cancels when the advantages are centred within their
+// groups (it can be 1e-5 of the typical |resp_loss|), so it is formed from the
+// fp64 per-response losses, not from their fp32 roundings: rounding each
+// resp_loss to fp32 first would alone move the mean by a few 1e-4 of itself.
+//
+// Invariance. A response is cut into segments of kSegTokens tokens counted
+// from its first token; a segment is summed by one of three fixed trees
+// chosen by its length (one lane in token order; one wavefront, lane j adding
+// tokens j, j + 64, ... then an xor butterfly; the workgroup, thread j adding
+// tokens j, j + 512, ..., then the wavefront butterflies and the eight wave
+// sums in a fixed tree), and a response's segments are added in order. So a
+// response's loss is a function of the response alone, wherever it sits in
+// the batch. The mean's tree depends on the number of responses only.
+//
+// Work. Token pass: workgroup b owns the segments that start in tokens
+// [b kSeg, (b + 1) kSeg) of the packed batch. They tile a contiguous span of
+// fewer than 2 kSeg tokens, which the workgroup reads once, coalesced, into
+// LDS as ratios, sums segment by segment (turning each segment's ratios into
+// its coefficients in place) and then writes the coefficients, coalesced.
+// A response of one segment is finished there; the segment sums of longer
+// ones go to the workspace. Finishing pass: per chunk of kFinishChunk
+// responses, the longer responses' segment sums are added in order, and the
+// chunk's fp64 losses are summed; a last single-workgroup pass adds the chunk
+// sums in order (skipped when there is one chunk).
 
 #include <algorithm>
 
 #include "device_common.h"
 #include "itl_config.h"
 #include "itl_launch.h"
+#include "loss_plan.h"
 
 namespace itl {
 
-constexpr int kLongLossBlocks = 4096;    // workgroups of the long-response kernel (grid shape only)
-constexpr int kShortLossBlocks = 16384;  // workgroups of the short-response kernel (grid shape only)
-
 namespace {
 
-// One wavefront per group (four per workgroup): lane j adds elements j,
-// j+64, ... of the group in ascending order, then a fixed xor butterfly
-// combines the lanes.
-__global__ __launch_bounds__(256) void group_advantage_kernel(const float* __restrict__ rewards,
-                                                              const int32_t* __restrict__ goff, int n_groups,
-                                                              int n_resp, float* __restrict__ adv) {
-  const int g = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (g >= n_groups) return;
-  const int s = min(max(goff[g], 0), n_resp);
-  const int e = min(max(goff[g + 1], s), n_resp);
-  const int n = e - s;
-  if (n <= 0) return;
-  float acc = 0.0f;
-  for (int i = s + lane; i < e; i += 64) acc += rewards[i];
-  const float mean = wave_sum(acc) / (float)n;
-  for (int i = s + lane; i < e; i += 64) adv[i] = rewards[i] - mean;
-}
+constexpr int kSpan = 2 * kSegTokens;                  // a token-pass span is shorter than this
+constexpr int kLossWaves = kLossThreads / 64;
+constexpr int kSpanPerThread = kSpan / kLossThreads;   // ratios staged per thread
+constexpr int kMaxLaneSegs = kSpan;                    // segments of >= 1 token in a span
+constexpr int kMaxWaveSegs = kSpan / (kLaneSeg + 1) + 1;
+constexpr int kMaxGroupSegs = kSpan / (kWaveSeg + 1) + 1;
+constexpr int kMaxRounds = 64;                         // response rounds of the enumeration (valid input: <= 9)
+static_assert(kSpan % kLossThreads == 0 && kLossThreads % 64 == 0, "span geometry");
+static_assert(kSpan <= 32767, "span offsets are stored in 16 bits");
 
-// Sum over a 256-thread block: wavefront butterflies, then the four wave
-// sums in a fixed tree. Every thread gets the same bits.
-__device__ __forceinline__ float block_sum256(float x, float* red) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  x = wave_sum(x);
-  if (lane == 0) red[wave] = x;
-  __syncthreads();
-  const float r = (red[0] + red[1]) + (red[2] + red[3]);
-  __syncthreads();
-  return r;
+// Response i's token range, clamped into [0, n_tok] (bad offsets cannot
+// index out of bounds; they give unspecified values).
+__device__ __forceinline__ void resp_bounds(const int64_t* __restrict__ off, int i, long long n_tok, long long& s,
+                                            long long& e) {
+  s = plan_clamp(off[i], 0, n_tok);
+  e = plan_clamp(off[i + 1], s, n_tok);
 }
 
 __device__ __forceinline__ float ratio_of(float lp, float lpr) { return fast_exp2((lp - lpr) * kLog2e); }
 
-// A response's tokens are summed by one of three fixed trees, chosen by its
-// length alone (so the bits still depend on nothing but the response): up
-// to kTinyResponse tokens, eight lanes (lane j holds token j; an xor
-// butterfly over the eight); up to kShortResponse tokens, one wavefront
-// (lane j adds tokens j, j+64, ... in ascending order, then the xor
-// butterfly); longer ones, one 256-thread workgroup (thread j adds tokens j,
-// j+256, ..., then the wavefront butterflies and the four wave sums in a
-// fixed tree).
-__device__ __forceinline__ void finish_response(int i, long long s, long long e, float S, const float* lp,
-                                                const float* lpr, const float* adv, int n_resp, int tid, int stride,
-                                                float* resp_loss, float* coef) {
-  const long long T = e - s;
-  if (T <= 0) return;
-  const float A = adv[i];
-  if (tid == 0) resp_loss[i] = -A * (S / (float)T);
-  if (coef) {
-    const float k = (float)(-(double)A / ((double)n_resp * (double)T));
-    for (long long t = s + tid; t < e; t += stride) coef[t] = ratio_of(lp[t], lpr[t]) * k;
-  }
+// d loss / d logprob of a response's tokens, per unit ratio.
+__device__ __forceinline__ float coef_scale(float A, int n_resp, long long T) {
+  return (float)(-(double)A / ((double)n_resp * (double)T));
 }
 
-// Tiny responses: eight per wavefront, eight lanes each.
-__global__ __launch_bounds__(256) void response_loss_tiny_kernel(
-    const float* __restrict__ lp, const float* __restrict__ lpr, const float* __restrict__ adv,
-    const int64_t* __restrict__ off, int n_resp, long long n_tok, float* __restrict__ resp_loss,
-    float* __restrict__ coef) {
-  const int i = blockIdx.x * 32 + (threadIdx.x >> 3);
-  const int j = threadIdx.x & 7;
-  long long s = 0, e = 0;
-  if (i < n_resp) {
-    s = min(max(off[i], 0LL), n_tok);
-    e = min(max(off[i + 1], s), n_tok);
+// For two token positions ta <= tb, the largest i in [0, n_resp) with
+// off[i] <= t, for both at once: a 512-way search (each round the
+// workgroup's threads probe evenly spaced offsets of both ranges). Every
+// thread must call it; the results are uniform.
+__device__ void find_responses(const int64_t* __restrict__ off, int n_resp, long long ta, long long tb, int& ia,
+                               int& ib) {
+  int lo_a = 0, hi_a = n_resp, lo_b = 0, hi_b = n_resp;
+  while (hi_a - lo_a > 1 || hi_b - lo_b > 1) {
+    const int step_a = (hi_a - lo_a + kLossThreads - 1) / kLossThreads;
+    const int step_b = (hi_b - lo_b + kLossThreads - 1) / kLossThreads;
+    const long long ja = lo_a + (long long)(threadIdx.x + 1) * step_a;
+    const long long jb = lo_b + (long long)(threadIdx.x + 1) * step_b;
+    const bool la = ja < hi_a && off[ja] <= ta;
+    const bool lb = jb < hi_b && off[jb] <= tb;
+    // probes past the answer fail and (for increasing offsets) so do all
+    // later ones: the count of hits is the answer's bracket
+    const int ca = __syncthreads_count(la);
+    const int cb = __syncthreads_count(lb);
+    lo_a += ca * step_a;
+    hi_a = min(hi_a, lo_a + step_a);
+    lo_b += cb * step_b;
+    hi_b = min(hi_b, lo_b + step_b);
   }
-  const long long T = e - s;
-  const bool mine = T >= 1 && T <= kTinyResponse;
-  const float r = mine && j < T ? ratio_of(lp[s + j], lpr[s + j]) : 0.0f;
-  // every lane takes part in the shuffles; xor offsets below 8 stay in the
-  // eight-lane segment
-  float S = r;
-  S += __shfl_xor(S, 4, 64);
-  S += __shfl_xor(S, 2, 64);
-  S += __shfl_xor(S, 1, 64);
-  if (!mine) return;
-  const float A = adv[i];
-  if (j == 0) resp_loss[i] = -A * (S / (float)T);
-  if (coef && j < T) coef[s + j] = r * (float)(-(double)A / ((double)n_resp * (double)T));
+  ia = lo_a;
+  ib = lo_b;
 }
 
-// Short responses: each wavefront owns a contiguous run of responses, reads
-// their lengths 64 at a time and sums the short ones in order, one at a time.
-__global__ __launch_bounds__(256) void response_loss_short_kernel(
-    const float* __restrict__ lp, const float* __restrict__ lpr, const float* __restrict__ adv,
-    const int64_t* __restrict__ off, int n_resp, long long n_tok, float* __restrict__ resp_loss,
-    float* __restrict__ coef) {
-  const int lane = threadIdx.x & 63;
-  const int n_waves = (int)gridDim.x * 4;
-  const int wv = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6);
-  const int per = (n_resp + n_waves - 1) / n_waves;
-  const int r0 = min(wv * per, n_resp), r1 = min(r0 + per, n_resp);
-  for (int c0 = r0; c0 < r1; c0 += 64) {
-    bool mine = false;
-    if (c0 + lane < r1) {
-      const long long s = min(max(off[c0 + lane], 0LL), n_tok);
-      const long long e = min(max(off[c0 + lane + 1], s), n_tok);
-      mine = e - s > kTinyResponse && e - s <= kShortResponse;
-    }
-    uint64_t todo = __builtin_amdgcn_ballot_w64(mine);
-    while (todo) {  // ascending response order
-      const int k = __builtin_ctzll(todo);
-      todo &= todo - 1;
-      const int i = c0 + k;
-      const long long s = min(max(off[i], 0LL), n_tok);
-      const long long e = min(max(off[i + 1], s), n_tok);
-      float acc = 0.0f;
-      for (long long t = s + lane; t < e; t += 64) acc += ratio_of(lp[t], lpr[t]);
-      finish_response(i, s, e, wave_sum(acc), lp, lpr, adv, n_resp, lane, 64, resp_loss, coef);
-    }
-  }
-}
-
-// Long responses: one workgroup each. Workgroup b owns a contiguous run of
-// responses (one response per workgroup up to kLongLossBlocks responses);
-// its threads read the run's lengths 256 at a time and the workgroup then
-// sums the long ones in order (the short kernel has the others).
-__global__ __launch_bounds__(kLossThreads) void response_loss_long_kernel(
-    const float* __restrict__ lp, const float* __restrict__ lpr, const float* __restrict__ adv,
-    const int64_t* __restrict__ off, int n_resp, long long n_tok, float* __restrict__ resp_loss,
-    float* __restrict__ coef) {
-  __shared__ float red[4];
-  __shared__ int is_long[kLossThreads];
-  const int per = (n_resp + (int)gridDim.x - 1) / (int)gridDim.x;
-  const int r0 = min((int)blockIdx.x * per, n_resp), r1 = min(r0 + per, n_resp);
-  for (int c0 = r0; c0 < r1; c0 += kLossThreads) {
-    const int i = c0 + (int)threadIdx.x;
-    int lg = 0;
-    if (i < r1) {
-      const long long s = min(max(off[i], 0LL), n_tok);
-      const long long e = min(max(off[i + 1], s), n_tok);
-      lg = e - s > kShortResponse;
-    }
-    is_long[threadIdx.x] = lg;
-    __syncthreads();
-    const int m = min(kLossThreads, r1 - c0);
-    for (int j = 0; j < m; ++j) {
-      if (!is_long[j]) continue;  // the same value in every thread
-      const int r = c0 + j;
-      const long long s = min(max(off[r], 0LL), n_tok);
-      const long long e = min(max(off[r + 1], s), n_tok);
-      float acc = 0.0f;
-      for (long long t = s + threadIdx.x; t < e; t += kLossThreads) acc += ratio_of(lp[t], lpr[t]);
-      finish_response(r, s, e, block_sum256(acc, red), lp, lpr, adv, n_resp, threadIdx.x, kLossThreads, resp_loss,
-                      coef);
-    }
-    __syncthreads();  // every thread is done with is_long before it is refilled
-  }
-}
-
-// Single workgroup: mean of the per-response losses in a fixed order. The
-// array is read as 16-byte groups of four, thread j taking groups j, j +
-// kMeanThreads, ... (each pass of the workgroup reads one contiguous 16 KiB
-// run) into four accumulators, one per position in the group, combined in a
-// fixed order; the last n_resp mod 4 values go to thread 0's accumulators;
-// then the wavefront butterflies and the wave sums in order. A fixed
-// function of n_resp.
-__global__ __launch_bounds__(kMeanThreads) void loss_mean_kernel(const float* __restrict__ resp_loss, int n_resp,
-                                                                 float* __restrict__ loss) {
-  __shared__ float red[kMeanThreads / 64];
+// Fixed trees over the workgroup (eight wavefronts): butterflies, then the
+// eight wave sums as ((w0 + w1) + (w2 + w3)) + ((w4 + w5) + (w6 + w7)).
+// Every thread gets the same bits.
+__device__ __forceinline__ double group_sum(double x, double* red) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n4 = n_resp / 4;
-  const bool vec = (reinterpret_cast<uintptr_t>(resp_loss) & 15) == 0;
-  float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
-  auto group = [&](int g) {
-    return vec ? reinterpret_cast<const float4*>(resp_loss)[g]
-               : make_float4(resp_loss[4 * g], resp_loss[4 * g + 1], resp_loss[4 * g + 2], resp_loss[4 * g + 3]);
-  };
-  auto add = [&](float4 v) {
-    a0 += v.x;
-    a1 += v.y;
-    a2 += v.z;
-    a3 += v.w;
-  };
-  int g = threadIdx.x;
-  // Four groups loaded before any is added (the same additions in the same
-  // order as one group at a time): four loads in flight per thread.
-  for (; g + 3 * kMeanThreads < n4; g += 4 * kMeanThreads) {
-    const float4 v0 = group(g), v1 = group(g + kMeanThreads), v2 = group(g + 2 * kMeanThreads),
-                 v3 = group(g + 3 * kMeanThreads);
-    add(v0);
-    add(v1);
-    add(v2);
-    add(v3);
-  }
-  for (; g < n4; g += kMeanThreads) add(group(g));
-  if (threadIdx.x == 0) {
-    const int r = 4 * n4;
-    if (r < n_resp) a0 += resp_loss[r];
-    if (r + 1 < n_resp) a1 += resp_loss[r + 1];
-    if (r + 2 < n_resp) a2 += resp_loss[r + 2];
-  }
-  float acc = (a0 + a1) + (a2 + a3);
-  acc = wave_sum(acc);
-  if (lane == 0) red[wave] = acc;
+  x = wave_sum_d(x);
+  if (lane == 0) red[wave] = x;
   __syncthreads();
+  static_assert(kLossWaves == 8, "the tree below is written for eight wavefronts");
+  const double r = ((red[0] + red[1]) + (red[2] + red[3])) + ((red[4] + red[5]) + (red[6] + red[7]));
+  __syncthreads();
+  return r;
+}
+
+// Block exclusive prefix of per-thread flags (0 or 1) for three classes at
+// once. Returns this thread's offsets; totals[c] gets the sums.
+struct Prefix3 {
+  int at[3];
+};
+__device__ __forceinline__ Prefix3 prefix3(const int (&n)[3], int (*wave_tot)[3], int (&totals)[3]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  Prefix3 out;
+#pragma unroll
+  for (int c = 0; c < 3; ++c) {
+    const uint64_t b = __builtin_amdgcn_ballot_w64(n[c] != 0);
+    out.at[c] = __popcll(b & below);
+    if (lane == 0) wave_tot[wave][c] = __popcll(b);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int c = 0; c < 3; ++c) {
+    int before = 0, all = 0;
+    for (int w = 0; w < kLossWaves; ++w) {
+      const int v = wave_tot[w][c];
+      before += w < wave ? v : 0;
+      all += v;
+    }
+    out.at[c] += before;
+    totals[c] = all;
+  }
+  __syncthreads();
+  return out;
+}
+
+struct SegLists {
+  short lane_rel[kMaxLaneSegs];  // start of the segment - span start
+  int lane_resp[kMaxLaneSegs];
+  short wave_rel[kMaxWaveSegs];
+  int wave_resp[kMaxWaveSegs];
+  short group_rel[kMaxGroupSegs];
+  int group_resp[kMaxGroupSegs];
+};
+
+// A segment's sum is known: finish its response if the segment is all of it,
+// else park the sum for the finishing pass (segment_slot: the slots of
+// different responses never meet).
+__device__ __forceinline__ void emit_segment(int i, long long s, long long e, long long c, double S,
+                                             const float* __restrict__ adv, float* __restrict__ resp_loss,
+                                             double* __restrict__ l64, double* __restrict__ segp, long long n_segp) {
+  const long long T = e - s;
+  if (T <= kSegTokens) {
+    const double l = -(double)adv[i] * (S / (double)T);
+    resp_loss[i] = (float)l;
+    l64[i] = l;
+  } else {
+    const long long slot = segment_slot(s, c);
+    if (slot < n_segp) segp[slot] = S;
+  }
+}
+
+__global__ __launch_bounds__(kLossThreads) void loss_tokens_kernel(
+    const float* __restrict__ lp, const float* __restrict__ lpr, const float* __restrict__ adv,
+    const int64_t* __restrict__ off, int n_resp, long long n_tok, float* __restrict__ resp_loss,
+    float* __restrict__ coef, double* __restrict__ l64, double* __restrict__ segp, long long n_segp) {
+  // the span's ratios; a segment's entries become its coefficients once
+  // the segment is summed
+  __shared__ float ratio_s[kSpan];
+  __shared__ SegLists L;
+  __shared__ int wave_tot[kLossWaves][3];
+  __shared__ double red[kLossWaves];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  // The span [p, q): from the first segment start at or after W0 to the
+  // first at or after W1 (the end of the batch if W1 is past it).
+  const long long W0 = (long long)blockIdx.x * kSegTokens, W1 = W0 + kSegTokens;
+  int ia, ib;
+  find_responses(off, n_resp, W0, W1 < n_tok ? W1 : W0, ia, ib);
+  long long sa, ea, sb, eb;
+  resp_bounds(off, ia, n_tok, sa, ea);
+  resp_bounds(off, ib, n_tok, sb, eb);
+  const Span sp = window_span(W0, n_tok, sa, ea, sb, eb);
+  const long long p = sp.p, q = sp.q;
+  const int span = (int)(q - p);
+
+  // Ratios of the span into LDS (all loads issued before any is used).
+  {
+    float a[kSpanPerThread], b[kSpanPerThread];
+#pragma unroll
+    for (int k = 0; k < kSpanPerThread; ++k) {
+      const int r = tid + k * kLossThreads;
+      a[k] = r < span ? lp[p + r] : 0.0f;
+      b[k] = r < span ? lpr[p + r] : 0.0f;
+    }
+#pragma unroll
+    for (int k = 0; k < kSpanPerThread; ++k) {
+      const int r = tid + k * kLossThreads;
+      if (r < span) ratio_s[r] = ratio_of(a[k], b[k]);
+    }
+  }
+
+  // The segments that start in the span, by class, from the responses that
+  // overlap it (kLossThreads responses per round).
+  int n_cls[3] = {0, 0, 0};  // uniform
+  const int i0 = (p < ea || ia + 1 >= n_resp) ? ia : ia + 1;
+  for (int base = i0, round = 0; base < n_resp && round < kMaxRounds; base += kLossThreads, ++round) {
+    const int i = base + tid;
+    int n[3] = {0, 0, 0};
+    long long st = 0;
+    int cls = 0;
+    bool has = false;
+    if (i < n_resp) {
+      long long s, e;
+      resp_bounds(off, i, n_tok, s, e);
+      has = segment_in_span(s, e, p, q, st);
+      if (has) {
+        cls = segment_class(segment_len(e, st, q));
+        n[cls] = 1;
+      }
+    }
+    int tot[3];
+    const Prefix3 at = prefix3(n, wave_tot, tot);
+    if (has) {
+      const int c = cls;
+      const int slot = n_cls[c] + at.at[c];
+      const short rel = (short)(st - p);
+      if (c == 0 && slot < kMaxLaneSegs) {
+        L.lane_rel[slot] = rel;
+        L.lane_resp[slot] = i;
+      } else if (c == 1 && slot < kMaxWaveSegs) {
+        L.wave_rel[slot] = rel;
+        L.wave_resp[slot] = i;
+      } else if (c == 2 && slot < kMaxGroupSegs) {
+        L.group_rel[slot] = rel;
+        L.group_resp[slot] = i;
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < 3; ++c) n_cls[c] += tot[c];
+    // another round if the next response still starts before q
+    const int nxt = base + kLossThreads;
+    if (nxt >= n_resp || plan_clamp(off[nxt], 0, n_tok) >= q) break;
+  }
+  __syncthreads();
+  const int n_lane = std::min(n_cls[0], kMaxLaneSegs);
+  const int n_wave = std::min(n_cls[1], kMaxWaveSegs);
+  const int n_group = std::min(n_cls[2], kMaxGroupSegs);
+
+  // Long segments: the whole workgroup, one at a time.
+  for (int g = 0; g < n_group; ++g) {
+    const int rel = L.group_rel[g], i = L.group_resp[g];
+    long long s, e;
+    resp_bounds(off, i, n_tok, s, e);
+    const long long c = p + rel;
+    const int len = (int)segment_len(e, c, q);
+    double acc = 0.0;
+    for (int r = tid; r < len; r += kLossThreads) acc += (double)ratio_s[rel + r];
+    const double S = group_sum(acc, red);  // every ratio of the segment has been read
+    const float k = coef_scale(adv[i], n_resp, e - s);
+    for (int r = tid; r < len; r += kLossThreads) ratio_s[rel + r] *= k;
+    if (tid == 0) emit_segment(i, s, e, c, S, adv, resp_loss, l64, segp, n_segp);
+  }
+  // Middle segments: one wavefront each.
+  for (int g = wave; g < n_wave; g += kLossWaves) {
+    const int rel = L.wave_rel[g], i = L.wave_resp[g];
+    long long s, e;
+    resp_bounds(off, i, n_tok, s, e);
+    const long long c = p + rel;
+    const int len = (int)segment_len(e, c, q);
+    double acc = 0.0;
+    for (int r = lane; r < len; r += 64) acc += (double)ratio_s[rel + r];
+    const double S = wave_sum_d(acc);  // every lane's reads are in S
+    const float k = coef_scale(adv[i], n_resp, e - s);
+    for (int r = lane; r < len; r += 64) ratio_s[rel + r] *= k;
+    if (lane == 0) emit_segment(i, s, e, c, S, adv, resp_loss, l64, segp, n_segp);
+  }
+  // Short segments: one lane each, in token order.
+  for (int g = tid; g < n_lane; g += kLossThreads) {
+    const int rel = L.lane_rel[g], i = L.lane_resp[g];
+    long long s, e;
+    resp_bounds(off, i, n_tok, s, e);
+    const long long c = p + rel;
+    const int len = (int)segment_len(e, c, q);
+    double S = 0.0;
+    for (int r = 0; r < len; ++r) S += (double)ratio_s[rel + r];
+    const float k = coef_scale(adv[i], n_resp, e - s);
+    for (int r = 0; r < len; ++r) ratio_s[rel + r] *= k;
+    emit_segment(i, s, e, c, S, adv, resp_loss, l64, segp, n_segp);
+  }
+  if (coef == nullptr) return;
+  __syncthreads();
+  for (int r = tid; r < span; r += kLossThreads) coef[p + r] = ratio_s[r];
+}
+
+// Finishing pass: chunk c of kFinishChunk responses, four per thread (thread
+// j: responses j, j + 256, j + 512, j + 768 of the chunk, added in that
+// order), then the chunk's tree (butterflies, then the four wave sums).
+constexpr int kFinishThreads = 256;
+static_assert(kFinishChunk % kFinishThreads == 0, "finish geometry");
+
+__device__ __forceinline__ double block_sum_d256(double x, double* red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  x = wave_sum_d(x);
+  if (lane == 0) red[wave] = x;
+  __syncthreads();
+  const double r = (red[0] + red[1]) + (red[2] + red[3]);
+  __syncthreads();
+  return r;
+}
+
+__global__ __launch_bounds__(kFinishThreads) void loss_finish_kernel(
+    const float* __restrict__ adv, const int64_t* __restrict__ off, int n_resp, long long n_tok,
+    float* __restrict__ resp_loss, const double* __restrict__ l64, const double* __restrict__ segp, long long n_segp,
+    double* __restrict__ part, float* __restrict__ loss) {
+  __shared__ double red[kFinishThreads / 64];
+  const int c0 = blockIdx.x * kFinishChunk;
+  double sum = 0.0;
+#pragma unroll
+  for (int r = 0; r < kFinishChunk / kFinishThreads; ++r) {
+    const int i = c0 + (int)threadIdx.x + r * kFinishThreads;
+    if (i >= n_resp) continue;
+    long long s, e;
+    resp_bounds(off, i, n_tok, s, e);
+    const long long T = e - s;
+    double l;
+    if (T <= 0) {  // an empty response (invalid input): a zero loss
+      l = 0.0;
+      resp_loss[i] = 0.0f;
+    } else if (T <= kSegTokens) {
+      l = l64[i];
+    } else {  // the segment sums in order, eight loads in flight at a time
+      const long long base = 2 * (s / kSegTokens);
+      const long long nseg = (T + kSegTokens - 1) / kSegTokens;
+      double S = 0.0;
+      for (long long j = 0; j < nseg; j += 8) {
+        double v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = (j + u < nseg && base + j + u < n_segp) ? segp[base + j + u] : 0.0;
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (j + u < nseg) S += v[u];
+      }
+      l = -(double)adv[i] * (S / (double)T);
+      resp_loss[i] = (float)l;
+    }
+    sum += l;
+  }
+  const double tot = block_sum_d256(sum, red);
   if (threadIdx.x == 0) {
-    float total = 0.0f;
-    for (int w = 0; w < kMeanThreads / 64; ++w) total += red[w];
-    loss[0] = total / (float)n_resp;
+    if (gridDim.x == 1) loss[0] = (float)(tot / (double)n_resp);
+    else part[blockIdx.x] = tot;
+  }
+}
+
+// The chunk sums in order (thread j adds chunks j, j + 256, ...), then the
+// tree of the finishing pass.
+__global__ __launch_bounds__(kFinishThreads) void loss_final_kernel(const double* __restrict__ part, int n_part,
+                                                                    int n_resp, float* __restrict__ loss) {
+  __shared__ double red[kFinishThreads / 64];
+  double acc = 0.0;
+  for (int c = threadIdx.x; c < n_part; c += kFinishThreads) acc += part[c];
+  const double tot = block_sum_d256(acc, red);
+  if (threadIdx.x == 0) loss[0] = (float)(tot / (double)n_resp);
+}
+
+// Group advantage. A wavefront owns eight consecutive groups. Groups of at
+// most 8 responses are reduced by eight lanes each (lane j holds response j;
+// an xor butterfly 4, 2, 1); larger ones by the whole wavefront, one at a
+// time (lane j adds responses j, j + 64, ... in order, then the 64-lane xor
+// butterfly). For groups of at most 8 the two trees give the same bits (the
+// 64-lane butterfly only adds exact zeros in its first three steps), so the
+// choice depends on the group's size alone.
+__global__ __launch_bounds__(256) void group_advantage_kernel(const float* __restrict__ rewards,
+                                                              const int32_t* __restrict__ goff, int n_groups,
+                                                              int n_resp, float* __restrict__ adv) {
+  const int lane = threadIdx.x & 63;
+  const int wv = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int sub = lane >> 3, j = lane & 7;
+  const int g = wv * 8 + sub;
+  int s = 0, n = 0;
+  if (g < n_groups) {
+    s = min(max(goff[g], 0), n_resp);
+    n = min(max(goff[g + 1], s), n_resp) - s;
+  }
+  const bool small = n >= 1 && n <= 8;
+  const float r = small && j < n ? rewards[s + j] : 0.0f;
+  float x = 0.0f + r;
+  x += __shfl_xor(x, 4, 64);
+  x += __shfl_xor(x, 2, 64);
+  x += __shfl_xor(x, 1, 64);
+  if (small && j < n) adv[s + j] = r - x / (float)n;
+  uint64_t big = __builtin_amdgcn_ballot_w64(j == 0 && n > 8);
+  while (big) {  // ascending group order
+    const int k = __builtin_ctzll(big) >> 3;
+    big &= big - 1;
+    const int gb = wv * 8 + k;
+    const int sb = min(max(goff[gb], 0), n_resp);
+    const int eb = min(max(goff[gb + 1], sb), n_resp);
+    float acc = 0.0f;
+    for (int i = sb + lane; i < eb; i += 64) acc += rewards[i];
+    const float mean = wave_sum(acc) / (float)(eb - sb);
+    for (int i = sb + lane; i < eb; i += 64) adv[i] = rewards[i] - mean;
   }
 }
 
@@ -244,32 +426,44 @@ __global__ void check_offsets_kernel(const int64_t* __restrict__ off, int n_resp
   if (i < n_resp && off[i + 1] <= off[i]) flag[0] = 2;
 }
 
+long long n_finish_chunks(long long n_resp) { return ceil_div(n_resp, kFinishChunk); }
+
 }  // namespace
 
 hipError_t launch_group_advantage(const float* rewards, const int32_t* group_offsets, int n_groups, int n_resp,
                                   float* advantages, hipStream_t stream) {
-  hipLaunchKernelGGL(group_advantage_kernel, dim3((unsigned)ceil_div(n_groups, 4)), dim3(256), 0, stream, rewards,
+  hipLaunchKernelGGL(group_advantage_kernel, dim3((unsigned)ceil_div(n_groups, 32)), dim3(256), 0, stream, rewards,
                      group_offsets, n_groups, n_resp, advantages);
   return hipGetLastError();
 }
 
+size_t loss_workspace_bytes(long long n_tok, long long n_resp) {
+  if (n_resp <= 0) return 0;
+  return align256((size_t)n_resp * sizeof(double)) + align256((size_t)n_segment_slots(n_tok) * sizeof(double)) +
+         align256((size_t)n_finish_chunks(n_resp) * sizeof(double));
+}
+
 hipError_t launch_reinforce_zero_loss(const float* logprob, const float* rollout_logprob, const float* advantages,
                                       const int64_t* resp_offsets, int n_resp, long long n_tok, float* resp_loss,
-                                      float* loss, float* coef, hipStream_t stream) {
-  hipLaunchKernelGGL(response_loss_tiny_kernel, dim3((unsigned)ceil_div(n_resp, 32)), dim3(256), 0, stream, logprob,
-                     rollout_logprob, advantages, resp_offsets, n_resp, n_tok, resp_loss, coef);
+                                      float* loss, float* coef, void* workspace, hipStream_t stream) {
+  char* ws = static_cast<char*>(workspace);
+  double* l64 = reinterpret_cast<double*>(ws);
+  double* segp = reinterpret_cast<double*>(ws + align256((size_t)n_resp * sizeof(double)));
+  const long long n_segp = n_segment_slots(n_tok);
+  double* part = reinterpret_cast<double*>(reinterpret_cast<char*>(segp) + align256((size_t)n_segp * sizeof(double)));
+  if (n_tok > 0) {
+    hipLaunchKernelGGL(loss_tokens_kernel, dim3((unsigned)ceil_div(n_tok, kSegTokens)), dim3(kLossThreads), 0,
+                       stream, logprob, rollout_logprob, advantages, resp_offsets, n_resp, n_tok, resp_loss, coef,
+                       l64, segp, n_segp);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int n_chunks = (int)n_finish_chunks(n_resp);
+  hipLaunchKernelGGL(loss_finish_kernel, dim3((unsigned)n_chunks), dim3(kFinishThreads), 0, stream, advantages,
+                     resp_offsets, n_resp, n_tok, resp_loss, l64, segp, n_segp, part, loss);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(response_loss_short_kernel, dim3((unsigned)std::min<long long>(ceil_div(n_resp, 4), kShortLossBlocks)),
-                     dim3(256), 0, stream, logprob, rollout_logprob, advantages, resp_offsets, n_resp, n_tok, resp_loss,
-                     coef);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(response_loss_long_kernel, dim3((unsigned)std::min(n_resp, kLongLossBlocks)), dim3(kLossThreads),
-                     0, stream, logprob, rollout_logprob, advantages, resp_offsets, n_resp, n_tok, resp_loss, coef);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(loss_mean_kernel, dim3(1), dim3(kMeanThreads), 0, stream, resp_loss, n_resp, loss);
+  if (e != hipSuccess || n_chunks == 1) return e;
+  hipLaunchKernelGGL(loss_final_kernel, dim3(1), dim3(kFinishThreads), 0, stream, part, n_chunks, n_resp, loss);
   return hipGetLastError();
 }
 

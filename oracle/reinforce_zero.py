@@ -150,14 +150,15 @@ def reinforce_zero_backward_rows(H, W, y, coef, tok_idx, vocab_idx, vocab_chunk=
         raise ValueError("tokens / coef do not match the rows of H")
     if n and (y.min() < 0 or y.max() >= V):
         raise ValueError("token id out of range")
-    # log-normaliser of every token, one vocabulary chunk at a time (running max / sum)
+    # log-normaliser of every token in two plain passes over the vocabulary
+    # (one chunk of rows at a time): the largest logit, then the sum of
+    # exp(z - max); lse = max + log(sum)
     m = np.full(n, -np.inf)
+    for v0 in range(0, V, vocab_chunk):
+        m = np.maximum(m, (H64 @ to_f64(W[v0:v0 + vocab_chunk]).T).max(axis=1))
     s = np.zeros(n)
     for v0 in range(0, V, vocab_chunk):
-        z = H64 @ to_f64(W[v0:v0 + vocab_chunk]).T
-        m_new = np.maximum(m, z.max(axis=1))
-        s = s * np.exp(m - m_new) + np.exp(z - m_new[:, None]).sum(axis=1)
-        m = m_new
+        s += np.exp(H64 @ to_f64(W[v0:v0 + vocab_chunk]).T - m[:, None]).sum(axis=1)
     lse = m + np.log(s)
     # dH rows: G[t, :] W over the whole vocabulary
     dH = np.zeros((tok_idx.size, d))

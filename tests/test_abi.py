@@ -87,14 +87,31 @@ def test_workspace_sizes(lib):
     assert lib.itl_lmhead_logprob_workspace_bytes(-1, V) == ctypes.c_size_t(-1).value
 
 
+def test_loss_workspace_sizes(lib):
+    w = lib.itl_reinforce_zero_loss_workspace_bytes
+    r = lambda x: -(-x // 256) * 256
+    assert w(0, 0) == 0 and w(100, 0) == 0
+    # fp64 per-response losses, two fp64 slots per 2048-token window (+2),
+    # one fp64 partial per 1024 responses
+    for n_tok, n_resp in ((10, 3), (294884, 32), (16 * 2 ** 20, 2 ** 21)):
+        want = r(8 * n_resp) + r(8 * 2 * (-(-n_tok // 2048) + 1)) + r(8 * -(-n_resp // 1024))
+        assert w(n_tok, n_resp) == want
+    assert w(-1, 3) == ctypes.c_size_t(-1).value and w(3, -1) == ctypes.c_size_t(-1).value
+
+
 def test_loss_and_advantage_validation(lib):
     v = ctypes.c_void_p
     assert lib.itl_group_advantage(v(1), v(1), -1, 4, v(1), None) == INVALID
     assert lib.itl_group_advantage(None, v(1), 2, 4, v(1), None) == INVALID
     assert lib.itl_group_advantage(None, None, 0, 0, None, None) == OK
-    assert lib.itl_reinforce_zero_loss(v(1), v(1), v(1), v(1), -1, 4, v(1), v(1), None, None) == INVALID
-    assert lib.itl_reinforce_zero_loss(v(1), v(1), v(1), None, 2, 4, v(1), v(1), None, None) == INVALID
-    assert lib.itl_reinforce_zero_loss(None, None, None, None, 0, 0, None, None, None, None) == OK
+    loss = lib.itl_reinforce_zero_loss
+    assert loss(v(1), v(1), v(1), v(1), -1, 4, v(1), v(1), None, v(256), 1 << 20, None) == INVALID
+    assert loss(v(1), v(1), v(1), None, 2, 4, v(1), v(1), None, v(256), 1 << 20, None) == INVALID
+    assert loss(None, None, None, None, 0, 0, None, None, None, None, 0, None) == OK
+    # workspace checked before anything is launched
+    assert loss(v(1), v(1), v(1), v(1), 2, 4, v(1), v(1), None, None, 1 << 20, None) == WORKSPACE
+    assert loss(v(1), v(1), v(1), v(1), 2, 4, v(1), v(1), None, v(256), 8, None) == WORKSPACE
+    assert loss(v(1), v(1), v(1), v(1), 2, 4, v(1), v(1), None, v(257), 1 << 20, None) == WORKSPACE
     assert lib.itl_reinforce_zero_backward(v(1), v(1), 0, 4, 100, 10, v(1), v(1), v(1), v(1), v(1),
                                            v(256), 1 << 30, None) == UNSUPPORTED
     assert lib.itl_reinforce_zero_backward(v(1), None, 0, 4, 64, 10, v(1), v(1), v(1), v(1), v(1),

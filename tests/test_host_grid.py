@@ -1,8 +1,9 @@
-"""Host-side checks of the logprob kernels' work decomposition: the C++
-functions the kernels use (itl_config.h), compiled into a host program with
-hipcc, over a few thousand (n_tok, vocab) pairs: every (token block, slice)
-pair computed once, slices tiling the vocabulary, the narrow grid's
-coverage. No GPU needed."""
+"""Host-side checks of the kernels' work decomposition: the C++ functions
+the kernels use (itl_config.h, loss_plan.h), compiled into host programs
+with hipcc. The logprob kernels over a few thousand (n_tok, vocab) pairs:
+every (token block, slice) pair computed once, slices tiling the vocabulary,
+the narrow grid's coverage. The loss's token pass over seeded response
+layouts. No GPU needed."""
 
 import os
 import shutil
@@ -49,3 +50,27 @@ def test_random_shapes(grid_check):
     pairs = [(nt, vv) for nt in (1, 63, 64, 65, 255, 256, 257, 2048, 2304, 8192)
              for vv in (255, 256, 257, 65535, 65536, 65537, 65536 + 256, 131071, 200000)]
     _run(grid_check, pairs)
+
+
+@pytest.fixture(scope="module")
+def loss_plan_check(tmp_path_factory):
+    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(hipcc):
+        pytest.skip("hipcc not available")
+    out = str(tmp_path_factory.mktemp("loss") / "loss_plan_check")
+    cmd = [hipcc, "-O2", "-std=c++17", "-I", os.path.join(ROOT, "invariant_token_logprobs_lm_amd", "csrc"),
+           os.path.join(ROOT, "tests", "host", "loss_plan_check.cpp"), "-o", out]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    return out
+
+
+@pytest.mark.parametrize("seed", [1, 2, 3])
+def test_loss_token_pass_decomposition(loss_plan_check, seed):
+    """The loss's token pass (loss_plan.h): spans tile the batch, every token
+    in exactly one response-relative segment owned by one window, at most one
+    start of a response per span, every overlapping response enumerated, the
+    segment-sum slots of different responses disjoint; 300 seeded layouts
+    (tiny, short, around one segment, long, mixed, a single long response)."""
+    r = subprocess.run([loss_plan_check, str(seed), "300"], capture_output=True, text=True)
+    assert r.returncode == 0 and r.stdout.startswith("ok"), r.stdout + r.stderr

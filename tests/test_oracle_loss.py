@@ -199,14 +199,20 @@ def test_dW_columns_sum_to_zero_over_vocab():
     assert np.max(np.abs(dW.sum(axis=0))) <= 1e-13 * max(1e-12, np.abs(dW).max()) * 300
 
 
-def test_gradient_rows_match_full_gradient():
+@pytest.mark.parametrize("w_scale", [1.0, 5000.0])
+def test_gradient_rows_match_full_gradient(w_scale):
     """The subset evaluator agrees with the full gradient (itself pinned by
-    finite differences and float64 autograd above), including repeated
-    token ids and vocabulary rows nobody sampled."""
+    finite differences and float64 autograd above) over a vocabulary of
+    several chunks with a ragged last one, including repeated token ids,
+    vocabulary rows nobody sampled, and (w_scale 5000) logits spread over
+    thousands of units, where exp overflows unless every chunk is shifted by
+    the row's true maximum."""
     rng = np.random.default_rng(61)
     H, W, y, lpr, A, off = _tiny_problem(rng, n_groups=2, gs=3, lo=3, hi=7, d=10, V=57)
+    W = W * w_scale
     y[:4] = y[0]
     lp, _ = oracle.lmhead_logprob(H, W, y)
+    lpr = lp + rng.normal(0, 0.3, lp.size)  # ratios near 1 whatever the scale: every coefficient counts
     _, _, coef = oracle.reinforce_zero_loss(lp, lpr, A, off)
     dH, dW = oracle.reinforce_zero_backward(H, W, y, coef)
     tok = np.array([0, 3, len(y) - 1])
