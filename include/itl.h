@@ -109,6 +109,25 @@ itl_status itl_lmhead_logprob(const void* H, const void* W, itl_dtype dtype,
                               const int32_t* tokens, float* logprob, float* lse,
                               void* workspace, size_t workspace_bytes, void* stream);
 
+/* itl_lmhead_logprob for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation. It takes no workspace: its scratch is a static 64 MiB device
+ * array inside this library (one copy per GPU, held until the process ends;
+ * its device address is looked up once per device on the first call). The
+ * call itself allocates and frees nothing. Same arguments (minus the
+ * workspace), same kernels, same logprob and lse bits as itl_lmhead_logprob.
+ * Limit: itl_lmhead_logprob_workspace_bytes(n_tok, vocab) <= 64 MiB, i.e.
+ * at most 16,368 tokens per call for vocab >= 65,281 (more for smaller
+ * vocabularies); larger calls return ITL_ERR_UNSUPPORTED before anything is
+ * launched. Every call on one GPU uses that GPU's one scratch array: calls
+ * that may overlap on one GPU (different streams, different host threads
+ * without ordering) race and give unspecified values; calls ordered on one
+ * stream are safe. The scratch needs no clearing (every value read is
+ * written earlier in the same call). */
+itl_status itl_lmhead_logprob_noalloc(const void* H, const void* W, itl_dtype dtype,
+                                      int64_t n_tok, int64_t d, int64_t vocab,
+                                      const int32_t* tokens, float* logprob, float* lse, void* stream);
+
 /* The same call as itl_lmhead_logprob, with the same logprob and lse bits,
  * that also keeps the head's logits for the backward [RZ] (the gradient of
  * the loss through the log-softmax needs every z[t, v] once more):

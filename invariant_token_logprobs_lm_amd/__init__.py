@@ -58,6 +58,8 @@ def _load():
         "itl_lmhead_logprob_workspace_bytes": (_size, [_i64, _i64]),
         "itl_lmhead_logprob": (ctypes.c_int, [_c_void_p, _c_void_p, ctypes.c_int, _i64, _i64, _i64, _c_void_p,
                                               _c_void_p, _c_void_p, _c_void_p, _size, _c_void_p]),
+        "itl_lmhead_logprob_noalloc": (ctypes.c_int, [_c_void_p, _c_void_p, ctypes.c_int, _i64, _i64, _i64,
+                                                      _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
         "itl_lmhead_logprob_keep_logits": (ctypes.c_int, [_c_void_p, _c_void_p, ctypes.c_int, _i64, _i64, _i64,
                                                           _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64,
                                                           _c_void_p, _size, _c_void_p]),
@@ -101,6 +103,7 @@ lib = _load()
 EXPORTS = (
     "itl_lmhead_logprob_workspace_bytes",
     "itl_lmhead_logprob",
+    "itl_lmhead_logprob_noalloc",
     "itl_lmhead_logprob_keep_logits",
     "itl_group_advantage",
     "itl_reinforce_zero_loss_workspace_bytes",
@@ -191,6 +194,30 @@ def lmhead_logprob(H, W, tokens, *, logprob=None, lse=None, workspace=None, want
     _check(lib.itl_lmhead_logprob(_ptr(H), _ptr(W), _HEAD_DTYPES[H.dtype], n_tok, d, vocab, _ptr(tokens),
                                   _ptr(logprob), _ptr(lse), _ptr(workspace), workspace.numel(),
                                   _stream(H.device)))
+    return logprob, lse
+
+
+def lmhead_logprob_noalloc(H, W, tokens, *, logprob=None, lse=None, want_lse=True):
+    """lmhead_logprob without a workspace (the library's static per-GPU
+    scratch; at most 16,368 tokens for large vocabularies). Same bits."""
+    _need(H, "H", tuple(_HEAD_DTYPES), ndim=2)
+    _need(W, "W", (H.dtype,), device=H.device, ndim=2)
+    _need(tokens, "tokens", (torch.int32,), device=H.device, ndim=1)
+    n_tok, d = H.shape
+    vocab = W.shape[0]
+    if W.shape[1] != d or tokens.shape[0] != n_tok:
+        raise ValueError(f"shape mismatch: H {tuple(H.shape)}, W {tuple(W.shape)}, tokens {tuple(tokens.shape)}")
+    if logprob is None:
+        logprob = torch.empty(n_tok, dtype=torch.float32, device=H.device)
+    if lse is None and want_lse:
+        lse = torch.empty(n_tok, dtype=torch.float32, device=H.device)
+    for name, t in (("logprob", logprob), ("lse", lse)):
+        if t is not None:
+            _need(t, name, (torch.float32,), device=H.device, ndim=1)
+            if t.shape[0] != n_tok:
+                raise ValueError(f"{name} must have {n_tok} elements")
+    _check(lib.itl_lmhead_logprob_noalloc(_ptr(H), _ptr(W), _HEAD_DTYPES[H.dtype], n_tok, d, vocab, _ptr(tokens),
+                                          _ptr(logprob), _ptr(lse), _stream(H.device)))
     return logprob, lse
 
 

@@ -7,6 +7,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 
 #include "itl.h"
@@ -51,6 +52,49 @@ itl_status check_head(itl_dtype dtype, int64_t n_tok, int64_t d, int64_t vocab) 
 
 bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255) != 0; }
 
+// Scratch of itl_lmhead_logprob_noalloc: a file-scope device array, one
+// copy per GPU, held until the process ends. Host code never uses its name
+// as an address: the device address comes from hipGetSymbolAddress, once per
+// device, with that device current.
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+constexpr int kMaxDevices = 64;
+
+}  // namespace
+
+__device__ __align__(256) unsigned char itl_noalloc_scratch[kNoAllocScratchBytes];
+
+namespace {
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch's device address on the device `stream` belongs to (the
+// current device for the null stream).
+itl_status noalloc_scratch(hipStream_t stream, void** out) {
+  int dev = -1;
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "itl_lmhead_logprob_noalloc: device of the stream");
+  if (dev < 0 || dev >= kMaxDevices) return fail(ITL_ERR_UNSUPPORTED, "device index beyond the scratch table");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int cur = -1;
+    e = hipGetDevice(&cur);
+    if (e != hipSuccess) return hip_fail(e, "itl_lmhead_logprob_noalloc: current device");
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return hip_fail(e, "itl_lmhead_logprob_noalloc: set device");
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(itl_noalloc_scratch));
+    if (cur != dev) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess || p == nullptr)
+      return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol, "itl_lmhead_logprob_noalloc: scratch address");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return ITL_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -74,6 +118,26 @@ itl_status itl_lmhead_logprob(const void* H, const void* W, itl_dtype dtype, int
   hipError_t e = itl::launch_lmhead_logprob(H, W, (int)dtype, (int)n_tok, (int)d, (int)vocab, tokens, logprob, lse,
                                             nullptr, 0, workspace, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ITL_OK : hip_fail(e, "itl_lmhead_logprob");
+}
+
+itl_status itl_lmhead_logprob_noalloc(const void* H, const void* W, itl_dtype dtype, int64_t n_tok, int64_t d,
+                                      int64_t vocab, const int32_t* tokens, float* logprob, float* lse, void* stream) {
+  g_last_error.clear();
+  itl_status st = check_head(dtype, n_tok, d, vocab);
+  if (st != ITL_OK) return st;
+  if (n_tok == 0) return ITL_OK;
+  if (!H || !W || !tokens || !logprob) return fail(ITL_ERR_INVALID_ARG, "null H, W, tokens or logprob");
+  if (itl::lmhead_workspace_bytes(n_tok, vocab) > kNoAllocScratchBytes)
+    return fail(ITL_ERR_UNSUPPORTED,
+                "n_tok too large for itl_lmhead_logprob_noalloc's 64 MiB scratch (at most 16,368 tokens for "
+                "vocab >= 65,281; use itl_lmhead_logprob with a workspace)");
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  void* scratch = nullptr;
+  st = noalloc_scratch(s, &scratch);
+  if (st != ITL_OK) return st;
+  hipError_t e = itl::launch_lmhead_logprob(H, W, (int)dtype, (int)n_tok, (int)d, (int)vocab, tokens, logprob, lse,
+                                            nullptr, 0, scratch, s);
+  return e == hipSuccess ? ITL_OK : hip_fail(e, "itl_lmhead_logprob_noalloc");
 }
 
 namespace {

@@ -77,6 +77,20 @@ def test_lmhead_argument_validation(lib):
     assert lib.itl_last_error().decode() == ""
 
 
+def test_noalloc_argument_validation(lib):
+    """Host-side checks of itl_lmhead_logprob_noalloc, all before any HIP call."""
+    v = ctypes.c_void_p
+    f = lib.itl_lmhead_logprob_noalloc
+    assert f(v(1), v(1), 0, -1, 64, 10, v(1), v(1), None, None) == INVALID
+    assert f(v(1), v(1), 0, 4, 96, 10, v(1), v(1), None, None) == UNSUPPORTED
+    assert f(None, v(1), 0, 4, 64, 10, v(1), v(1), None, None) == INVALID
+    assert f(None, None, 0, 0, 64, 10, None, None, None, None) == OK
+    # the static scratch holds 64 MiB: 16,368 tokens at 256 slices
+    assert f(v(1), v(1), 0, 16369, 64, 151936, v(1), v(1), None, None) == UNSUPPORTED
+    assert "scratch" in lib.itl_last_error().decode()
+    assert lib.itl_lmhead_logprob_workspace_bytes(16368, 151936) == 64 << 20
+
+
 def test_workspace_sizes(lib):
     assert lib.itl_lmhead_logprob_workspace_bytes(0, 100) == 0
     # one (max, sumexp) float pair per token, slice and wavefront (2 per
