@@ -48,7 +48,6 @@ namespace {
 constexpr int kSpan = 2 * kSegTokens;                  // a token-pass span is shorter than this
 constexpr int kLossWaves = kLossThreads / 64;
 constexpr int kSpanPerThread = kSpan / kLossThreads;   // ratios staged per thread
-constexpr int kMaxLaneSegs = kSpan;                    // segments of >= 1 token in a span
 constexpr int kMaxWaveSegs = kSpan / (kLaneSeg + 1) + 1;
 constexpr int kMaxGroupSegs = kSpan / (kWaveSeg + 1) + 1;
 constexpr int kMaxRounds = 64;                         // response rounds of the enumeration (valid input: <= 9)
@@ -111,55 +110,49 @@ __device__ __forceinline__ double group_sum(double x, double* red) {
   return r;
 }
 
-// Block exclusive prefix of per-thread flags (0 or 1) for three classes at
-// once. Returns this thread's offsets; totals[c] gets the sums.
-struct Prefix3 {
-  int at[3];
-};
-__device__ __forceinline__ Prefix3 prefix3(const int (&n)[3], int (*wave_tot)[3], int (&totals)[3]) {
+// Block exclusive prefix of per-thread flags for two classes at once:
+// at0 / at1 get this thread's offsets, tot0 / tot1 the sums.
+__device__ __forceinline__ void prefix2(bool f0, bool f1, int (*wave_tot)[2], int& at0, int& at1, int& tot0,
+                                        int& tot1) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
-  Prefix3 out;
-#pragma unroll
-  for (int c = 0; c < 3; ++c) {
-    const uint64_t b = __builtin_amdgcn_ballot_w64(n[c] != 0);
-    out.at[c] = __popcll(b & below);
-    if (lane == 0) wave_tot[wave][c] = __popcll(b);
+  const uint64_t b0 = __builtin_amdgcn_ballot_w64(f0), b1 = __builtin_amdgcn_ballot_w64(f1);
+  at0 = __popcll(b0 & below);
+  at1 = __popcll(b1 & below);
+  if (lane == 0) {
+    wave_tot[wave][0] = __popcll(b0);
+    wave_tot[wave][1] = __popcll(b1);
   }
   __syncthreads();
-#pragma unroll
-  for (int c = 0; c < 3; ++c) {
-    int before = 0, all = 0;
-    for (int w = 0; w < kLossWaves; ++w) {
-      const int v = wave_tot[w][c];
-      before += w < wave ? v : 0;
-      all += v;
-    }
-    out.at[c] += before;
-    totals[c] = all;
+  tot0 = tot1 = 0;
+  for (int w = 0; w < kLossWaves; ++w) {
+    const int v0 = wave_tot[w][0], v1 = wave_tot[w][1];
+    at0 += w < wave ? v0 : 0;
+    at1 += w < wave ? v1 : 0;
+    tot0 += v0;
+    tot1 += v1;
   }
   __syncthreads();
-  return out;
 }
 
-struct SegLists {
-  short lane_rel[kMaxLaneSegs];  // start of the segment - span start
-  int lane_resp[kMaxLaneSegs];
-  short wave_rel[kMaxWaveSegs];
-  int wave_resp[kMaxWaveSegs];
-  short group_rel[kMaxGroupSegs];
-  int group_resp[kMaxGroupSegs];
+// A segment summed by a wavefront or by the workgroup, as listed for the
+// second phase of the token pass.
+struct SegEntry {
+  long long s, e;  // its response's tokens
+  float A;         // its response's advantage
+  int i;           // its response
+  int rel;         // its start - the span's start
 };
 
 // A segment's sum is known: finish its response if the segment is all of it,
 // else park the sum for the finishing pass (segment_slot: the slots of
 // different responses never meet).
-__device__ __forceinline__ void emit_segment(int i, long long s, long long e, long long c, double S,
-                                             const float* __restrict__ adv, float* __restrict__ resp_loss,
-                                             double* __restrict__ l64, double* __restrict__ segp, long long n_segp) {
+__device__ __forceinline__ void emit_segment(int i, long long s, long long e, long long c, double S, float A,
+                                             float* __restrict__ resp_loss, double* __restrict__ l64,
+                                             double* __restrict__ segp, long long n_segp) {
   const long long T = e - s;
   if (T <= kSegTokens) {
-    const double l = -(double)adv[i] * (S / (double)T);
+    const double l = -(double)A * (S / (double)T);
     resp_loss[i] = (float)l;
     l64[i] = l;
   } else {
@@ -172,11 +165,12 @@ __global__ __launch_bounds__(kLossThreads) void loss_tokens_kernel(
     const float* __restrict__ lp, const float* __restrict__ lpr, const float* __restrict__ adv,
     const int64_t* __restrict__ off, int n_resp, long long n_tok, float* __restrict__ resp_loss,
     float* __restrict__ coef, double* __restrict__ l64, double* __restrict__ segp, long long n_segp) {
-  // the span's ratios; a segment's entries become its coefficients once
-  // the segment is summed
+  // the span's ratios; a segment's entries become its coefficients once the
+  // segment is summed
   __shared__ float ratio_s[kSpan];
-  __shared__ SegLists L;
-  __shared__ int wave_tot[kLossWaves][3];
+  __shared__ SegEntry wave_list[kMaxWaveSegs];
+  __shared__ SegEntry group_list[kMaxGroupSegs];
+  __shared__ int wave_tot[kLossWaves][2];
   __shared__ double red[kLossWaves];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
@@ -191,110 +185,95 @@ __global__ __launch_bounds__(kLossThreads) void loss_tokens_kernel(
   const Span sp = window_span(W0, n_tok, sa, ea, sb, eb);
   const long long p = sp.p, q = sp.q;
   const int span = (int)(q - p);
+  const int i0 = (p < ea || ia + 1 >= n_resp) ? ia : ia + 1;
 
-  // Ratios of the span into LDS (all loads issued before any is used).
-  {
-    float a[kSpanPerThread], b[kSpanPerThread];
+  // One memory round trip for the span's logprobs and the first round of
+  // responses (offsets and advantages); then the ratios into LDS.
+  float a[kSpanPerThread], b[kSpanPerThread];
 #pragma unroll
-    for (int k = 0; k < kSpanPerThread; ++k) {
-      const int r = tid + k * kLossThreads;
-      a[k] = r < span ? lp[p + r] : 0.0f;
-      b[k] = r < span ? lpr[p + r] : 0.0f;
+  for (int k = 0; k < kSpanPerThread; ++k) {
+    const int r = tid + k * kLossThreads;
+    a[k] = r < span ? lp[p + r] : 0.0f;
+    b[k] = r < span ? lpr[p + r] : 0.0f;
+  }
+  auto load_round = [&](int base, long long& s, long long& e, float& A) {
+    const int i = base + tid;
+    if (i < n_resp) {
+      resp_bounds(off, i, n_tok, s, e);
+      A = adv[i];
+    } else {
+      s = e = n_tok;
+      A = 0.0f;
     }
+  };
+  long long rs, re;
+  float rA;
+  load_round(i0, rs, re, rA);
 #pragma unroll
-    for (int k = 0; k < kSpanPerThread; ++k) {
-      const int r = tid + k * kLossThreads;
-      if (r < span) ratio_s[r] = ratio_of(a[k], b[k]);
-    }
+  for (int k = 0; k < kSpanPerThread; ++k) {
+    const int r = tid + k * kLossThreads;
+    if (r < span) ratio_s[r] = ratio_of(a[k], b[k]);
   }
 
-  // The segments that start in the span, by class, from the responses that
-  // overlap it (kLossThreads responses per round).
-  int n_cls[3] = {0, 0, 0};  // uniform
-  const int i0 = (p < ea || ia + 1 >= n_resp) ? ia : ia + 1;
+  // Rounds of kLossThreads responses from the one holding p. A response's
+  // segment in the span (at most one) of up to kLaneSeg tokens is summed at
+  // once by its thread, in token order; longer ones are listed by class.
+  int n_wave = 0, n_group = 0;  // uniform
   for (int base = i0, round = 0; base < n_resp && round < kMaxRounds; base += kLossThreads, ++round) {
+    if (round > 0) load_round(base, rs, re, rA);
     const int i = base + tid;
-    int n[3] = {0, 0, 0};
-    long long st = 0;
-    int cls = 0;
-    bool has = false;
-    if (i < n_resp) {
-      long long s, e;
-      resp_bounds(off, i, n_tok, s, e);
-      has = segment_in_span(s, e, p, q, st);
-      if (has) {
-        cls = segment_class(segment_len(e, st, q));
-        n[cls] = 1;
-      }
+    long long c = 0;
+    int cls = -1;
+    if (i < n_resp && segment_in_span(rs, re, p, q, c)) cls = segment_class(segment_len(re, c, q));
+    int at0, at1, tot0, tot1;
+    prefix2(cls == 1, cls == 2, wave_tot, at0, at1, tot0, tot1);  // (its barrier also publishes the ratios)
+    if (cls == 0) {
+      const int rel = (int)(c - p), len = (int)segment_len(re, c, q);
+      double S = 0.0;
+      for (int r = 0; r < len; ++r) S += (double)ratio_s[rel + r];
+      const float k = coef_scale(rA, n_resp, re - rs);
+      for (int r = 0; r < len; ++r) ratio_s[rel + r] *= k;
+      emit_segment(i, rs, re, c, S, rA, resp_loss, l64, segp, n_segp);
+    } else if (cls > 0) {
+      const int slot = cls == 1 ? n_wave + at0 : n_group + at1;
+      const SegEntry ent{rs, re, rA, i, (int)(c - p)};
+      if (cls == 1 && slot < kMaxWaveSegs) wave_list[slot] = ent;
+      if (cls == 2 && slot < kMaxGroupSegs) group_list[slot] = ent;
     }
-    int tot[3];
-    const Prefix3 at = prefix3(n, wave_tot, tot);
-    if (has) {
-      const int c = cls;
-      const int slot = n_cls[c] + at.at[c];
-      const short rel = (short)(st - p);
-      if (c == 0 && slot < kMaxLaneSegs) {
-        L.lane_rel[slot] = rel;
-        L.lane_resp[slot] = i;
-      } else if (c == 1 && slot < kMaxWaveSegs) {
-        L.wave_rel[slot] = rel;
-        L.wave_resp[slot] = i;
-      } else if (c == 2 && slot < kMaxGroupSegs) {
-        L.group_rel[slot] = rel;
-        L.group_resp[slot] = i;
-      }
-    }
-#pragma unroll
-    for (int c = 0; c < 3; ++c) n_cls[c] += tot[c];
-    // another round if the next response still starts before q
-    const int nxt = base + kLossThreads;
-    if (nxt >= n_resp || plan_clamp(off[nxt], 0, n_tok) >= q) break;
+    n_wave += tot0;
+    n_group += tot1;
+    // another round if the response after this round's last one starts
+    // before q (that thread has its start as its round's end offset)
+    const bool more = tid == kLossThreads - 1 && i + 1 < n_resp && re < q;
+    if (!__syncthreads_or(more)) break;
   }
   __syncthreads();
-  const int n_lane = std::min(n_cls[0], kMaxLaneSegs);
-  const int n_wave = std::min(n_cls[1], kMaxWaveSegs);
-  const int n_group = std::min(n_cls[2], kMaxGroupSegs);
+  n_wave = std::min(n_wave, kMaxWaveSegs);
+  n_group = std::min(n_group, kMaxGroupSegs);
 
   // Long segments: the whole workgroup, one at a time.
   for (int g = 0; g < n_group; ++g) {
-    const int rel = L.group_rel[g], i = L.group_resp[g];
-    long long s, e;
-    resp_bounds(off, i, n_tok, s, e);
-    const long long c = p + rel;
-    const int len = (int)segment_len(e, c, q);
+    const SegEntry ent = group_list[g];
+    const long long c = p + ent.rel;
+    const int len = (int)segment_len(ent.e, c, q);
     double acc = 0.0;
-    for (int r = tid; r < len; r += kLossThreads) acc += (double)ratio_s[rel + r];
+    for (int r = tid; r < len; r += kLossThreads) acc += (double)ratio_s[ent.rel + r];
     const double S = group_sum(acc, red);  // every ratio of the segment has been read
-    const float k = coef_scale(adv[i], n_resp, e - s);
-    for (int r = tid; r < len; r += kLossThreads) ratio_s[rel + r] *= k;
-    if (tid == 0) emit_segment(i, s, e, c, S, adv, resp_loss, l64, segp, n_segp);
+    const float k = coef_scale(ent.A, n_resp, ent.e - ent.s);
+    for (int r = tid; r < len; r += kLossThreads) ratio_s[ent.rel + r] *= k;
+    if (tid == 0) emit_segment(ent.i, ent.s, ent.e, c, S, ent.A, resp_loss, l64, segp, n_segp);
   }
   // Middle segments: one wavefront each.
   for (int g = wave; g < n_wave; g += kLossWaves) {
-    const int rel = L.wave_rel[g], i = L.wave_resp[g];
-    long long s, e;
-    resp_bounds(off, i, n_tok, s, e);
-    const long long c = p + rel;
-    const int len = (int)segment_len(e, c, q);
+    const SegEntry ent = wave_list[g];
+    const long long c = p + ent.rel;
+    const int len = (int)segment_len(ent.e, c, q);
     double acc = 0.0;
-    for (int r = lane; r < len; r += 64) acc += (double)ratio_s[rel + r];
+    for (int r = lane; r < len; r += 64) acc += (double)ratio_s[ent.rel + r];
     const double S = wave_sum_d(acc);  // every lane's reads are in S
-    const float k = coef_scale(adv[i], n_resp, e - s);
-    for (int r = lane; r < len; r += 64) ratio_s[rel + r] *= k;
-    if (lane == 0) emit_segment(i, s, e, c, S, adv, resp_loss, l64, segp, n_segp);
-  }
-  // Short segments: one lane each, in token order.
-  for (int g = tid; g < n_lane; g += kLossThreads) {
-    const int rel = L.lane_rel[g], i = L.lane_resp[g];
-    long long s, e;
-    resp_bounds(off, i, n_tok, s, e);
-    const long long c = p + rel;
-    const int len = (int)segment_len(e, c, q);
-    double S = 0.0;
-    for (int r = 0; r < len; ++r) S += (double)ratio_s[rel + r];
-    const float k = coef_scale(adv[i], n_resp, e - s);
-    for (int r = 0; r < len; ++r) ratio_s[rel + r] *= k;
-    emit_segment(i, s, e, c, S, adv, resp_loss, l64, segp, n_segp);
+    const float k = coef_scale(ent.A, n_resp, ent.e - ent.s);
+    for (int r = lane; r < len; r += 64) ratio_s[ent.rel + r] *= k;
+    if (lane == 0) emit_segment(ent.i, ent.s, ent.e, c, S, ent.A, resp_loss, l64, segp, n_segp);
   }
   if (coef == nullptr) return;
   __syncthreads();
