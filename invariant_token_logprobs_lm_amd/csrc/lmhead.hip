@@ -10,14 +10,15 @@
 //   lse[t]     = log sum_v exp(z[t, v])
 //   logprob[t] = z[t, y_t] - lse[t]
 //
-// Kernel 1 (lmhead_lse_partial) computes z^T tiles on the matrix cores: the
-// MFMA A operand is a 256-row tile of W, the B operand a 256-token block of
-// H, both read K-contiguous. The vocabulary is cut into S = min(tiles, 256)
-// balanced slices, a function of V alone. A workgroup owns one token block
-// and a run of consecutive slices and walks their tiles in ascending order;
-// after each tile its lanes fold the tile into a running (max, sum of exp)
-// per token and pick out z[t, y_t] if y_t falls in the tile. The logits never
-// leave registers. At each slice end the two lane halves that share a token
+// Kernel 1 (lmhead_lse_partial8, or the narrow kernel for calls of at most
+// 64 tokens) computes z^T tiles on the matrix cores: the MFMA A operand is a
+// 256-row tile of W, the B operand a 256-token block of H, both read
+// K-contiguous, on the eight-wavefront engine (tile_engine8.h). The
+// vocabulary is cut into S = min(tiles, 256) balanced slices, a function of V
+// alone. A workgroup owns one token block and a run of consecutive slices
+// and walks their tiles in ascending order; after each tile its lanes fold
+// the tile into a running (max, sum of exp) per token (fold_column) and pick
+// out z[t, y_t] if y_t falls in the tile. The logits never leave registers. At each slice end the two lane halves that share a token
 // are merged and each wavefront writes one (max, sumexp) pair per token, then
 // starts the next slice afresh, so the 2 S partials of a token are the same
 // whether a workgroup walks one slice (small batches: every CU streams W) or
@@ -42,6 +43,7 @@
 #include "itl_launch.h"
 #include "lse_fold.h"
 #include "tile_engine.h"
+#include "tile_engine8.h"
 
 namespace itl {
 
@@ -113,102 +115,87 @@ __device__ __forceinline__ void store_logits(const LogitRows& rows, int bn, int 
   store_quad<3>(rows, voff, v0, half, vocab, z, partial);
 }
 
-// Store one accumulator block's logits, four registers at a time straight
-// from the accumulators (a separate pass before the fold: with the fold's
-// state live as well, the epilogue ran out of registers, and every spill
-// reload waited for all the stores and operand loads in flight).
-template <class kPartial>
-__device__ __forceinline__ void store_block(const LogitRows& rows, int bn, int v0, int half, int vocab,
-                                            const floatx16& a, kPartial partial) {
-  floatx16 z;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) z[i] = acc_read(a, i);
-  store_logits(rows, bn, v0, half, vocab, z, partial);
-}
-
+// Kernel 1 for calls of more than 64 tokens, on the eight-wavefront engine
+// (run_tiles8): a 512-thread workgroup per (256-token block, slice group).
+// Wavefront (wv, tq) holds W rows 128 wv .. + 127 of each tile against
+// tokens t0 + 64 tq .. + 63; after each tile each token column's four blocks
+// are folded in one step (fold_column), tiles in order, and at the slice's
+// end the two lane halves are merged, as in the narrow kernel, so a token's
+// partials have the same bits in both. With kKeep the tile's logits are
+// stored first (four 16-byte stores per block).
 template <int kDtype, bool kKeep, bool kBFar>
-__global__ __launch_bounds__(kThreads, 1) void lmhead_lse_partial_kernel(
+__global__ __launch_bounds__(kThreads8, 1) void lmhead_lse_partial8_kernel(
     const char* __restrict__ H, const char* __restrict__ W, const int32_t* __restrict__ tokens, int n_tok,
     int row_bytes, int vocab, int n_tb, int n_slices, int group, float2* __restrict__ part,
     float* __restrict__ zy_out, float* __restrict__ logits, long long ld) {
   __shared__ uint4 smem[kEngineSmemChunks];
-  const Lanes L = lanes();
-  const int wv = L.wv, wt = L.wt, half = L.half, col = L.col;
+  const Lanes8 L = lanes8();
+  const int wv = L.wv, tq = L.tq, half = L.half, col = L.col;
 
   const int S = n_slices;
   const WideWork work = wide_work(blockIdx.x, n_tb, S, group);
   const int t0 = work.tb * kBT;
   const int n_vt = (vocab + kBV - 1) / kBV;
-  const int slice_first = work.slice_first;
   const int tile_begin = slice_tile(work.slice_first, n_vt, S);
   const int tile_end = slice_tile(work.slice_end, n_vt, S);
   const int nks = row_bytes / kStepBytes;
 
-  // The engine's A operand is the W tile (vocabulary rows), its B operand
-  // the H block (tokens): lane l's accumulators are vocabulary rows of token
-  // t0 + 128 wt + 32 bn + (l mod 32).
-  Col c[4];
+  Col c[2];
 #pragma unroll
-  for (int bn = 0; bn < 4; ++bn) {
-    const int tok = t0 + wt * 128 + bn * 32 + col;
+  for (int bn = 0; bn < 2; ++bn) {
+    const int tok = t0 + tq * 64 + bn * 32 + col;
     c[bn] = Col{tok < n_tok ? tokens[tok] : -1, -INFINITY, 0.0f, 0.0f, false};
   }
-
   auto w_rsrc = [&](int tile) {
     const int v0 = tile * kBV;
     return rsrc_words(W + (size_t)v0 * row_bytes, (uint32_t)min(kBV, vocab - v0) * row_bytes);
   };
   const int4v hr = rsrc_words(H + (size_t)t0 * row_bytes, (uint32_t)min(kBT, n_tok - t0) * row_bytes);
 
-  int slice = slice_first;  // slice of the tiles being folded
+  int slice = work.slice_first;
   int slice_last_tile = slice_tile(slice + 1, n_vt, S) - 1;
-  auto epilogue = [&](int tile, floatx16 (&acc)[4][4]) {
+  auto epilogue = [&](int tile, floatx16 (&acc)[4][2]) {
     const int vw = tile * kBV + wv * 128;
-    mfma_result_wait();
-    LogitRows rows{};
-    if constexpr (kKeep) rows = logit_rows(logits, ld, t0 + wt * 128, 128, n_tok, col, half);
     auto fold_tile = [&](auto partial, auto pick) {
       if constexpr (kKeep) {
+        const LogitRows rows = logit_rows(logits, ld, t0 + tq * 64, 64, n_tok, col, half);
 #pragma unroll
-        for (int bn = 0; bn < 4; ++bn)
+        for (int bn = 0; bn < 2; ++bn)
 #pragma unroll
-          for (int bm = 0; bm < 4; ++bm) store_block(rows, bn, vw + bm * 32, half, vocab, acc[bm][bn], partial);
+          for (int bm = 0; bm < 4; ++bm) store_logits(rows, bn, vw + bm * 32, half, vocab, acc[bm][bn], partial);
       }
 #pragma unroll
-      for (int bn = 0; bn < 4; ++bn)
-#pragma unroll
-        for (int bm = 0; bm < 4; ++bm) fold_block(c[bn], acc[bm][bn], bm, vw, half, vocab, partial, pick);
+      for (int bn = 0; bn < 2; ++bn)
+        fold_column(c[bn], acc[0][bn], acc[1][bn], acc[2][bn], acc[3][bn], vw, half, vocab, partial, pick);
     };
     // A lane's sampled row lies in this wavefront's 128 rows of a given tile
     // for about one tile in V / 128, so most tiles skip the pick (a uniform
     // branch: the picked values are the same either way).
-    bool mine = false;
-#pragma unroll
-    for (int bn = 0; bn < 4; ++bn) mine = mine || (unsigned)(c[bn].y - vw) < 128u;
+    const bool mine = (unsigned)(c[0].y - vw) < 128u || (unsigned)(c[1].y - vw) < 128u;
     if (tile * kBV + kBV > vocab) fold_tile(std::true_type{}, std::true_type{});  // only the vocabulary's last tile
     else if (__builtin_amdgcn_ballot_w64(mine) != 0) fold_tile(std::false_type{}, std::true_type{});
     else fold_tile(std::false_type{}, std::false_type{});
     if (tile == slice_last_tile) {
 #pragma unroll
-      for (int bn = 0; bn < 4; ++bn) {
-        const int tok = t0 + wt * 128 + bn * 32 + col;
+      for (int bn = 0; bn < 2; ++bn) {
+        const int tok = t0 + tq * 64 + bn * 32 + col;
         flush_slice(c[bn], tok, n_tok, half, ((size_t)slice * 2 + wv) * n_tok + tok, part);
       }
       ++slice;
       slice_last_tile = slice_tile(slice + 1, n_vt, S) - 1;
     }
   };
-  run_tiles<kDtype, kBFar>(smem, L, row_bytes, tile_begin, tile_end, nks, w_rsrc, hr, epilogue);
+  run_tiles8<kDtype, kBFar>(smem, L, row_bytes, tile_begin, tile_end, nks, w_rsrc, hr, epilogue);
 
 #pragma unroll
-  for (int bn = 0; bn < 4; ++bn)
-    if (c[bn].found) zy_out[t0 + wt * 128 + bn * 32 + col] = c[bn].zy;
+  for (int bn = 0; bn < 2; ++bn)
+    if (c[bn].found) zy_out[t0 + tq * 64 + bn * 32 + col] = c[bn].zy;
 }
 
 // The same partials for few tokens: 64-token blocks, one workgroup per
 // (token block, slice), the workgroup's slice walked by run_tiles_narrow.
 // Lane l of wavefront (wv, wt) holds token t0 + 32 wt + (l mod 32) against
-// the same W rows, with the same fold, as in lmhead_lse_partial_kernel, so
+// the same W rows, with the same fold, as in lmhead_lse_partial8_kernel, so
 // the partials (and the logprobs) have the same bits.
 template <int kDtype, bool kKeep>
 __global__ __launch_bounds__(kThreads, 1) void lmhead_lse_partial_narrow_kernel(
@@ -238,14 +225,12 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_lse_partial_narrow_kernel(
   const LogitRows rows = logit_rows(logits, ld, t0 + wt * 32, 32, n_tok, col, half);
   auto epilogue = [&](int tile, floatx16 (&acc)[4]) {
     const int vw = tile * kBV + wv * 128;
-    mfma_result_wait();
     auto fold_tile = [&](auto partial) {
       if constexpr (kKeep) {
 #pragma unroll
-        for (int bm = 0; bm < 4; ++bm) store_block(rows, 0, vw + bm * 32, half, vocab, acc[bm], partial);
+        for (int bm = 0; bm < 4; ++bm) store_logits(rows, 0, vw + bm * 32, half, vocab, acc[bm], partial);
       }
-#pragma unroll
-      for (int bm = 0; bm < 4; ++bm) fold_block(c, acc[bm], bm, vw, half, vocab, partial);
+      fold_column(c, acc[0], acc[1], acc[2], acc[3], vw, half, vocab, partial, std::true_type{});
     };
     if (tile * kBV + kBV > vocab) fold_tile(std::true_type{});
     else fold_tile(std::false_type{});
@@ -297,7 +282,10 @@ __global__ __launch_bounds__(64 * kCombineWaves) void lse_combine_kernel(const f
   if (w != 0 || t >= n_tok) return;
 #pragma unroll
   for (int r = 1; r < kCombineWaves; ++r) lse_merge(m, s, run_state[r][lane].x, run_state[r][lane].y);
-  const float l = m + fast_log2(s) * kLn2;
+  // lse >= the largest logit holds mathematically; the fold's shared
+  // exponent offset can leave the sum a rounding below 1 when one logit
+  // dominates, so it is kept explicitly (and with it logprob <= 0)
+  const float l = fmaxf(m + fast_log2(s) * kLn2, m);
   logprob[t] = zy[t] - l;
   if (lse) lse[t] = l;
 }
@@ -330,12 +318,12 @@ void launch_partials(const char* H, const char* W, const int32_t* tokens, int n_
     const int G = slices_per_group(n_tok, vocab);
     const int ntb = (int)ceil_div(n_tok, kBT);
     const dim3 grid((unsigned)ntb * (unsigned)n_slice_groups(n_tok, vocab));
-    // Long K loops stage the token block two K steps ahead (see run_tiles).
+    // Long K loops stage the token block two K steps ahead (see run_tiles8).
     if (row_bytes / kStepBytes > kNearBMaxSteps)
-      hipLaunchKernelGGL((lmhead_lse_partial_kernel<kDtype, kKeep, true>), grid, dim3(kThreads), 0, stream, H, W,
+      hipLaunchKernelGGL((lmhead_lse_partial8_kernel<kDtype, kKeep, true>), grid, dim3(kThreads8), 0, stream, H, W,
                          tokens, n_tok, row_bytes, vocab, ntb, S, G, part, zy, logits, ld);
     else
-      hipLaunchKernelGGL((lmhead_lse_partial_kernel<kDtype, kKeep, false>), grid, dim3(kThreads), 0, stream, H, W,
+      hipLaunchKernelGGL((lmhead_lse_partial8_kernel<kDtype, kKeep, false>), grid, dim3(kThreads8), 0, stream, H, W,
                          tokens, n_tok, row_bytes, vocab, ntb, S, G, part, zy, logits, ld);
   }
 }

@@ -76,6 +76,62 @@ __device__ __forceinline__ void fold_values(Col& c, floatx16 z, int bm, int vw, 
   c.m = mnew;
 }
 
+// Fold one tile's four 32 x 32 blocks of one token column (block bm holds
+// rows 32 bm + 8 (i / 4) + 4 half + (i % 4) of the wavefront's 128 rows) into
+// the state, as one step: the bf16 and fp32 heads' fold, shared by their
+// wide and narrow kernels (the FP8 kernels fold block by block with
+// fold_values). The 64 logits' maximum M (exact in any order) moves the
+// running maximum to m' = max(m, M); every term of the tile is then
+// exp2(z log2e + b) with one rounded offset b = -m' log2e (a fused
+// multiply-add per logit), summed into eight partial sums in a fixed order
+// and added to the old sum rescaled by exp2(m log2e + b). The shared offset
+// moves every term of the tile by the same factor, within |m'| 2^-24 of 1
+// (the maximum's own term is not exactly 1: the combine keeps lse >= the
+// largest logit, so logprob <= 0 still holds in fp32).
+template <class kPartial, class kPick>
+__device__ __forceinline__ void fold_column(Col& c, floatx16 z0, floatx16 z1, floatx16 z2, floatx16 z3, int vw,
+                                            int half, int vocab, kPartial, kPick) {
+  floatx16 z[4] = {z0, z1, z2, z3};
+  if constexpr (kPartial::value) {
+#pragma unroll
+    for (int bm = 0; bm < 4; ++bm) {
+      const int lim = vocab - (vw + bm * 32 + 4 * half);  // rows at or past this offset do not exist
+#pragma unroll
+      for (int i = 0; i < 16; ++i) z[bm][i] = (8 * (i >> 2) + (i & 3) >= lim) ? -INFINITY : z[bm][i];
+    }
+  }
+  if constexpr (kPick::value) {
+    const int o = c.y - vw;  // sampled row relative to this wavefront's 128 rows
+    const bool b0 = (o & 1) != 0, b1 = (o & 2) != 0, b2 = (o & 8) != 0, b3 = (o & 16) != 0;
+    const bool here = (unsigned)o < 128u && ((o >> 2) & 1) == half;
+    const int bm = (o >> 5) & 3;
+    const float pick = select16(bm == 0 ? z[0] : bm == 1 ? z[1] : bm == 2 ? z[2] : z[3], b0, b1, b2, b3);
+    c.zy = here ? pick : c.zy;
+    c.found = c.found || here;
+  }
+  float mx[4];
+#pragma unroll
+  for (int bm = 0; bm < 4; ++bm) {
+    float a = fmaxf(z[bm][0], z[bm][1]);
+#pragma unroll
+    for (int i = 2; i < 16; ++i) a = fmaxf(a, z[bm][i]);
+    mx[bm] = a;
+  }
+  const float mnew = fmaxf(c.m, fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3])));
+  // A lane whose rows so far are all absent has mnew = -inf; it then works
+  // around 0 and keeps (m, s) = (-inf, 0).
+  const float mref = mnew == -INFINITY ? 0.0f : mnew;
+  const float b = -mref * kLog2e;
+  float s[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) s[k] = fast_exp2(__builtin_fmaf(z[0][k], kLog2e, b));
+#pragma unroll
+  for (int k = 8; k < 64; ++k) s[k & 7] += fast_exp2(__builtin_fmaf(z[k >> 4][k & 15], kLog2e, b));
+  const float sum = ((s[0] + s[1]) + (s[2] + s[3])) + ((s[4] + s[5]) + (s[6] + s[7]));
+  c.s = __builtin_fmaf(c.s, fast_exp2(__builtin_fmaf(c.m, kLog2e, b)), sum);
+  c.m = mnew;
+}
+
 // Slice end: lanes l and l ^ 32 hold the same token (different rows); the
 // lower lane merges the upper lane's state into its own and writes the
 // wavefront's partial of the slice; every lane starts the next slice afresh.
