@@ -114,6 +114,29 @@ __device__ __forceinline__ void dma16(int4v rsrc, uint32_t voff, uint32_t soff, 
       : "memory");
 }
 
+// Four such loads under one M0 value: load j fills LDS lds + 1024 j from
+// offset voff_j + 1024 j (the instruction's immediate offset is added to both
+// the memory and the LDS address), so the caller passes voff_j - 1024 j.
+__device__ __forceinline__ void dma16x4(int4v rsrc, const uint32_t (&voff)[4], uint32_t soff, uint32_t lds) {
+  const int4v r = {__builtin_amdgcn_readfirstlane(rsrc[0]), __builtin_amdgcn_readfirstlane(rsrc[1]),
+                   __builtin_amdgcn_readfirstlane(rsrc[2]), __builtin_amdgcn_readfirstlane(rsrc[3])};
+  const uint32_t so = __builtin_amdgcn_readfirstlane(soff);
+  const uint32_t l = __builtin_amdgcn_readfirstlane(lds);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %7\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %5, %6 offen lds\n\t"
+      "buffer_load_dwordx4 %2, %5, %6 offen offset:1024 lds\n\t"
+      "buffer_load_dwordx4 %3, %5, %6 offen offset:2048 lds\n\t"
+      "buffer_load_dwordx4 %4, %5, %6 offen offset:3072 lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]), "s"(r), "s"(so), "s"(l)
+      : "memory");
+}
+
 // Wait until at most kPending of this wavefront's loads are outstanding
 // (loads complete in issue order) and its LDS reads are done, then meet the
 // other wavefronts.

@@ -21,11 +21,12 @@
 // from LDS. One workgroup barrier per K step, after sub-step 2 (whose reads
 // are the step's last): it publishes step g + 1 (every wavefront has waited
 // for its own loads of it) and frees step g's slots; sub-step 3 loads the
-// near operand's step g + 2 into them, and sub-steps 0..2 of step g + 1 the
-// far operand's step g + 3 (spread over the step: issued all at once, the
-// workgroup's loads queued up and held the MFMAs back). Every wavefront
-// loads rows 32 w .. 32 w + 31 of both operands. The near operand (two slots) is the B block, the far one (three
-// slots) the walked A tiles; with kBFar the other way round. A tile's last
+// near operand's step g + 2 into them (after its second MFMA), and
+// sub-step 0 of step g + 1 the far operand's step g + 3 (after its fourth).
+// Every wavefront loads rows 32 w .. 32 w + 31 of both operands, four loads
+// of each step back to back under one M0 value. The near operand (two
+// slots) is the B block, the far one (three slots) the walked A tiles; with
+// kBFar the other way round. A tile's last
 // K step leaves the next tile's first fragments unread; they are read after
 // the epilogue, which then has those registers.
 #pragma once
@@ -73,30 +74,34 @@ __device__ __forceinline__ void run_tiles8(uint4* smem, const Lanes8& L, int row
   const int lane = L.lane, wave = L.wave, half = L.half, col = L.col;
 
   // Loader: wavefront w fills rows 32 w .. 32 w + 31 of both operands' slots
-  // with four 16-byte-per-lane loads each; lane i fetches row (i / 8) of an
-  // 8-row group at logical chunk (i % 8) ^ swz(row), which lands at its
-  // swizzled position (swz(32 w + 8 j + i / 8) = (i / 8) ^ (j & 1)).
+  // with four 16-byte-per-lane loads each, under one M0 value (dma16x4);
+  // lane i of load j fetches row 32 w + 8 j + i / 8 at logical chunk
+  // (i % 8) ^ swz(row), which lands at its swizzled position
+  // (swz(32 w + 8 j + i / 8) = (i / 8) ^ (j & 1)). voff[j] holds that offset
+  // less 1024 j, which it never underflows (8 j rows are at least 1024 j
+  // bytes: a row holds at least one 128-byte K step).
+  static_assert(kDma8PerWave == 4, "dma16x4 issues a wavefront's four loads of a step");
   const int lr = lane >> 3;
   uint32_t voff[kDma8PerWave];
 #pragma unroll
   for (int j = 0; j < kDma8PerWave; ++j)
-    voff[j] = (uint32_t)(wave * 32 + j * kDmaRows + lr) * (uint32_t)row_bytes + (((lane & 7) ^ lr ^ (j & 1)) * 16);
+    voff[j] = (uint32_t)(wave * 32 + j * kDmaRows + lr) * (uint32_t)row_bytes + (((lane & 7) ^ lr ^ (j & 1)) * 16) -
+              (uint32_t)j * 1024u;
   const uint32_t lds0 = (uint32_t)(size_t)((__attribute__((address_space(3))) uint4*)smem);
   const uint32_t my_rows = (uint32_t)wave * 32 * kStepBytes;
   const int n_steps = (tile_end - tile_begin) * nks;
-  // Load j (0..3) of step s of A / of B into its slot. A step past the end
+  // The four loads of step s of A / of B into its slot. A step past the end
   // loads the last step's data instead (a valid address) into slot s, which
   // is free and which nothing reads again.
-  auto a_load = [&](int s, int j) {
+  auto a_load = [&](int s) {
     const int c = s < n_steps ? s : n_steps - 1;
     const int q = c / nks;
-    dma16(a_rsrc(tile_begin + q), voff[j], (uint32_t)(c - q * nks) * kStepBytes,
-          lds0 + (uint32_t)(s % kAS) * kSlotBytes + my_rows + j * 1024);
+    dma16x4(a_rsrc(tile_begin + q), voff, (uint32_t)(c - q * nks) * kStepBytes,
+            lds0 + (uint32_t)(s % kAS) * kSlotBytes + my_rows);
   };
-  auto b_load = [&](int s, int j) {
+  auto b_load = [&](int s) {
     const int c = s < n_steps ? s : n_steps - 1;
-    dma16(b_rsrc, voff[j], (uint32_t)(c % nks) * kStepBytes,
-          lds0 + (uint32_t)(kAS + s % kBS) * kSlotBytes + my_rows + j * 1024);
+    dma16x4(b_rsrc, voff, (uint32_t)(c % nks) * kStepBytes, lds0 + (uint32_t)(kAS + s % kBS) * kSlotBytes + my_rows);
   };
 
   // MFMA operand reads of sub-step kk: A rows 128 wv + 32 bm + (l mod 32),
@@ -110,25 +115,21 @@ __device__ __forceinline__ void run_tiles8(uint4* smem, const Lanes8& L, int row
   }
 
   // The near operand (two slots) and the far one (three slots).
-  auto near_load = [&](int s, int j) {
-    if constexpr (kAS == 2) a_load(s, j);
-    else b_load(s, j);
+  auto near_load = [&](int s) {
+    if constexpr (kAS == 2) a_load(s);
+    else b_load(s);
   };
-  auto far_load = [&](int s, int j) {
-    if constexpr (kAS == 2) b_load(s, j);
-    else a_load(s, j);
+  auto far_load = [&](int s) {
+    if constexpr (kAS == 2) b_load(s);
+    else a_load(s);
   };
 
   // Prologue: near and far steps 0 and 1, in that order; then step 0 is
   // published (step 1 may be in flight).
-#pragma unroll
-  for (int j = 0; j < kDma8PerWave; ++j) near_load(0, j);
-#pragma unroll
-  for (int j = 0; j < kDma8PerWave; ++j) far_load(0, j);
-#pragma unroll
-  for (int j = 0; j < kDma8PerWave; ++j) near_load(1, j);
-#pragma unroll
-  for (int j = 0; j < kDma8PerWave; ++j) far_load(1, j);
+  near_load(0);
+  far_load(0);
+  near_load(1);
+  far_load(1);
   wait_and_barrier<2 * kDma8PerWave>();
   __builtin_amdgcn_sched_barrier(0);
 
@@ -153,13 +154,11 @@ __device__ __forceinline__ void run_tiles8(uint4* smem, const Lanes8& L, int row
   };
   // One sub-step: 8 MFMAs on set X; with kRead the reads of the next
   // sub-step (step rs, sub-step rkk, into set X ^ 1) go two after each of the
-  // first 3 MFMAs (their latency then has five MFMAs to pass). The K step's
-  // loads are spread over its sub-steps, so that the workgroup's 64 loads
-  // per K step do not queue up at once behind the barrier: kDma = 1, 2, 3:
-  // the far operand's step s + 2 (loads 0 and 1 / 2 / 3; its slot, that of
-  // step s - 1, was released at the previous barrier); kDma = 4: the near
-  // operand's step s + 2 (into the slot step s released at this step's
-  // barrier), one load every second MFMA. At each barrier exactly the far
+  // first 3 MFMAs (their latency then has five MFMAs to pass). kDma = 1: the
+  // far operand's step s + 2, after the fourth MFMA (its slot, that of step
+  // s - 1, was released at the previous barrier); kDma = 2: the near
+  // operand's step s + 2, after the second MFMA (into the slot step s
+  // released at this step's barrier). At each barrier exactly the far
   // operand's latest four loads may then still be in flight.
   auto sub = [&](auto X, auto read, auto dma, int rs, int rkk, int s) {
     constexpr int x = decltype(X)::value;
@@ -181,14 +180,9 @@ __device__ __forceinline__ void run_tiles8(uint4* smem, const Lanes8& L, int row
         }
       }
       if constexpr (kDma == 1) {
-        if (q == 1) far_load(s + 2, 0);
-        if (q == 5) far_load(s + 2, 1);
+        if (q == 3) far_load(s + 2);
       } else if constexpr (kDma == 2) {
-        if (q == 3) far_load(s + 2, 2);
-      } else if constexpr (kDma == 3) {
-        if (q == 3) far_load(s + 2, 3);
-      } else if constexpr (kDma == 4) {
-        if ((q & 1) == 0) near_load(s + 2, q >> 1);
+        if (q == 1) near_load(s + 2);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -199,20 +193,19 @@ __device__ __forceinline__ void run_tiles8(uint4* smem, const Lanes8& L, int row
   using I1 = std::integral_constant<int, 1>;
   // K step s; kNext: sub-step 3 reads step s + 1's first fragments (not in a
   // tile's last step: they are read after the epilogue).
+  using D0 = std::integral_constant<int, 0>;
   using D1 = std::integral_constant<int, 1>;
   using D2 = std::integral_constant<int, 2>;
-  using D3 = std::integral_constant<int, 3>;
-  using D4 = std::integral_constant<int, 4>;
   auto k_step = [&](int s, auto next) {
     sub(I0{}, T{}, D1{}, s, 1, s);
-    sub(I1{}, T{}, D2{}, s, 2, s);
-    sub(I0{}, T{}, D3{}, s, 3, s);
+    sub(I1{}, T{}, D0{}, s, 2, s);
+    sub(I0{}, T{}, D0{}, s, 3, s);
     // step s + 1 landed (the far operand's step s + 2, issued in this step's
-    // first three sub-steps, may be in flight); every wavefront is done
-    // reading step s
+    // first sub-step, may be in flight); every wavefront is done reading
+    // step s
     wait_and_barrier<kDma8PerWave>();
     __builtin_amdgcn_sched_barrier(0);
-    sub(I1{}, next, D4{}, s + 1, 0, s);
+    sub(I1{}, next, D2{}, s + 1, 0, s);
   };
 
   zero_acc();
