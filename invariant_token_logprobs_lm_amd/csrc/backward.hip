@@ -13,7 +13,8 @@
 //   dW[v]    += sum over tokens t with y_t = v, ascending t, of coef[t] H[t]
 // The dense part g[t, v] = -coef[t] p[t, v] is formed in the head's dtype
 // (bf16 for bf16 heads: the MFMA operand) and contracted on the matrix cores
-// with the tile engine, one chunk of kBwdChunk tokens at a time:
+// with the eight-wavefront tile engine (tile_engine8.h), one chunk of
+// kBwdChunk tokens at a time:
 //   1. dlogits: z recomputed by the forward's contraction, g written twice:
 //      token-major Gd [chunk, Vpad] (for dH) and vocabulary-major GdT
 //      [Vpad, chunk] (for dW); padding rows and columns hold zeros.
@@ -34,6 +35,7 @@
 
 #include "itl_launch.h"
 #include "tile_engine.h"
+#include "tile_engine8.h"
 
 namespace itl {
 
@@ -147,25 +149,27 @@ __device__ __forceinline__ void band_order(int b, int n_fast, int n_slow, int& f
 }
 
 // 1. dlogits. A = W tiles (vocabulary), B = the chunk's H block (tokens); as
-// in the forward. Grid: token blocks (fast) x vocabulary slices (slow).
+// in the forward, on the eight-wavefront engine. Grid: token blocks (fast) x
+// vocabulary slices (slow). Lane l of wavefront (wv, tq) holds vocabulary
+// rows 128 wv + ... of each tile at tokens t0 + 64 tq + 32 bn + (l mod 32).
 template <int kDtype, bool kBFar>
-__global__ __launch_bounds__(kThreads, 1) void dlogits_kernel(
+__global__ __launch_bounds__(kThreads8, 1) void dlogits_kernel(
     const char* __restrict__ Hc, int len, const char* __restrict__ W, int row_bytes, int vocab, int vpad,
     int n_tb, int n_slices, int group, const int32_t* __restrict__ y, const float* __restrict__ lse,
     const float* __restrict__ coef, typename Elem<kDtype>::T* __restrict__ Gd, typename Elem<kDtype>::T* __restrict__ GdT) {
   using E = Elem<kDtype>;
   __shared__ uint4 smem[kEngineSmemChunks];
-  const Lanes L = lanes();
+  const Lanes8 L = lanes8();
   int tb, grp;
   band_order(blockIdx.x, n_tb, (n_slices + group - 1) / group, tb, grp);
   const int t0 = tb * kBT;
   const int n_vt = vpad / kBV;
   const int tile_begin = slice_tile(grp * group, n_vt, n_slices);
   const int tile_end = slice_tile(min(grp * group + group, n_slices), n_vt, n_slices);
-  float l2e_lse[4], negc[4];
+  float l2e_lse[2], negc[2];
 #pragma unroll
-  for (int bn = 0; bn < 4; ++bn) {
-    const int t = t0 + L.wt * 128 + bn * 32 + L.col;
+  for (int bn = 0; bn < 2; ++bn) {
+    const int t = t0 + L.tq * 64 + bn * 32 + L.col;
     const bool ok = t < len;
     l2e_lse[bn] = ok ? lse[t] * kLog2e : 0.0f;
     negc[bn] = ok ? -coef[t] : 0.0f;  // padding tokens get g = 0
@@ -175,12 +179,11 @@ __global__ __launch_bounds__(kThreads, 1) void dlogits_kernel(
     return rsrc_words(W + (size_t)v0 * row_bytes, (uint32_t)max(0, min(kBV, vocab - v0)) * row_bytes);
   };
   const int4v hr = rsrc_words(Hc + (size_t)t0 * row_bytes, (uint32_t)min(kBT, len - t0) * row_bytes);
-  auto epilogue = [&](int tile, floatx16 (&acc)[4][4]) {
-    mfma_result_wait();
+  auto epilogue = [&](int tile, floatx16 (&acc)[4][2]) {
     const int vw = tile * kBV + L.wv * 128 + 4 * L.half;
 #pragma unroll
-    for (int bn = 0; bn < 4; ++bn) {
-      const int t = t0 + L.wt * 128 + bn * 32 + L.col;  // < chunk's padded length
+    for (int bn = 0; bn < 2; ++bn) {
+      const int t = t0 + L.tq * 64 + bn * 32 + L.col;  // < chunk's padded length
 #pragma unroll
       for (int bm = 0; bm < 4; ++bm) {
 #pragma unroll
@@ -189,7 +192,7 @@ __global__ __launch_bounds__(kThreads, 1) void dlogits_kernel(
           typename E::T g[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const float z = acc_read(acc[bm][bn], 4 * i4 + r);
+            const float z = acc[bm][bn][4 * i4 + r];
             const float p = fast_exp2(z * kLog2e - l2e_lse[bn]);
             g[r] = E::from_f(v + r < vocab ? negc[bn] * p : 0.0f);
             GdT[(size_t)(v + r) * kBwdChunk + t] = g[r];
@@ -207,7 +210,7 @@ __global__ __launch_bounds__(kThreads, 1) void dlogits_kernel(
       }
     }
   };
-  run_tiles<kDtype, kBFar>(smem, L, row_bytes, tile_begin, tile_end, row_bytes / kStepBytes, w_rsrc, hr, epilogue);
+  run_tiles8<kDtype, kBFar>(smem, L, row_bytes, tile_begin, tile_end, row_bytes / kStepBytes, w_rsrc, hr, epilogue);
 }
 
 // 1'. dlogits from kept logits: the same g as dlogits_kernel, for a tile of
@@ -290,18 +293,19 @@ __global__ __launch_bounds__(256) void dlogits_from_logits_kernel(
   }
 }
 
-// 2. dH for the chunk. A = W^T tile (d rows, K = Vpad), B = Gd token block.
-// Grid: token blocks (fast) x d tiles (slow). Lane l's accumulators are d
-// rows of token t0 + 128 wt + 32 bn + (l mod 32).
+// 2. dH for the chunk. A = W^T tile (d rows, K = Vpad), B = Gd token block,
+// on the eight-wavefront engine. Grid: token blocks (fast) x d tiles (slow).
+// Lane l of wavefront (wv, tq) holds d rows 128 wv + ... of the tile for
+// tokens t0 + 64 tq + 32 bn + (l mod 32).
 template <int kDtype, bool kBFar>
-__global__ __launch_bounds__(kThreads, 1) void dh_kernel(const char* __restrict__ WT, const char* __restrict__ Gd,
-                                                        int vpad, int d, int vocab, int len, int n_tb, int n_dt,
-                                                        const int32_t* __restrict__ y, const float* __restrict__ coef,
-                                                        const typename Elem<kDtype>::T* __restrict__ W,
-                                                        float* __restrict__ dH) {
+__global__ __launch_bounds__(kThreads8, 1) void dh_kernel(const char* __restrict__ WT, const char* __restrict__ Gd,
+                                                         int vpad, int d, int vocab, int len, int n_tb, int n_dt,
+                                                         const int32_t* __restrict__ y, const float* __restrict__ coef,
+                                                         const typename Elem<kDtype>::T* __restrict__ W,
+                                                         float* __restrict__ dH) {
   using E = Elem<kDtype>;
   __shared__ uint4 smem[kEngineSmemChunks];
-  const Lanes L = lanes();
+  const Lanes8 L = lanes8();
   int tb, dt;
   band_order(blockIdx.x, n_tb, n_dt, tb, dt);
   const int t0 = tb * kBT;
@@ -311,44 +315,37 @@ __global__ __launch_bounds__(kThreads, 1) void dh_kernel(const char* __restrict_
     return rsrc_words(WT + (size_t)k0 * row_bytes, (uint32_t)min(kBV, d - k0) * row_bytes);
   };
   const int4v br = rsrc_words(Gd + (size_t)t0 * row_bytes, (uint32_t)min(kBT, len - t0) * row_bytes);
-  auto epilogue = [&](int tile, floatx16 (&acc)[4][4]) {
-    mfma_result_wait();
+  auto epilogue = [&](int tile, floatx16 (&acc)[4][2]) {
     const int kw = tile * kBV + L.wv * 128 + 4 * L.half;
 #pragma unroll
-    for (int bn = 0; bn < 4; ++bn) {
-      const int t = t0 + L.wt * 128 + bn * 32 + L.col;
+    for (int bn = 0; bn < 2; ++bn) {
+      const int t = t0 + L.tq * 64 + bn * 32 + L.col;
       const bool ok = t < len;
       const int yr = ok ? y[t] : 0;
       const bool yok = (unsigned)yr < (unsigned)vocab;  // an invalid id contributes no sampled term
       const float c = ok && yok ? coef[t] : 0.0f;
       const int yt = yok ? yr : 0;
-      // The 16 groups of 4 W[y] values this lane needs for token t are
-      // loaded together (one memory round trip per token column, not one
-      // per group), then combined with the accumulators and stored.
-      float wyv[4][4][4];
 #pragma unroll
-      for (int bm = 0; bm < 4; ++bm)
+      for (int bm = 0; bm < 4; ++bm) {
+        // The block's 4 groups of 4 W[y] values, loaded together.
+        float wyv[4][4];
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
           const int k = kw + bm * 32 + 8 * i4;  // d rows k .. k + 3 (d is a multiple of 64)
           const typename E::T* wy = W + (size_t)yt * d + (k < d ? k : 0);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) wyv[bm][i4][r] = E::to_f(wy[r]);
+          for (int r = 0; r < 4; ++r) wyv[i4][r] = E::to_f(wy[r]);
         }
-#pragma unroll
-      for (int bm = 0; bm < 4; ++bm) {
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
           const int k = kw + bm * 32 + 8 * i4;
-          float o[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) o[r] = acc_read(acc[bm][bn], 4 * i4 + r);
           if (ok && k < d) {
+            const floatx16& o = acc[bm][bn];
             float4 out;
-            out.x = o[0] + c * wyv[bm][i4][0];
-            out.y = o[1] + c * wyv[bm][i4][1];
-            out.z = o[2] + c * wyv[bm][i4][2];
-            out.w = o[3] + c * wyv[bm][i4][3];
+            out.x = o[4 * i4 + 0] + c * wyv[i4][0];
+            out.y = o[4 * i4 + 1] + c * wyv[i4][1];
+            out.z = o[4 * i4 + 2] + c * wyv[i4][2];
+            out.w = o[4 * i4 + 3] + c * wyv[i4][3];
             *reinterpret_cast<float4*>(dH + (size_t)t * d + k) = out;
           }
         }
@@ -356,19 +353,20 @@ __global__ __launch_bounds__(kThreads, 1) void dh_kernel(const char* __restrict_
       }
     }
   };
-  run_tiles<kDtype, kBFar>(smem, L, row_bytes, dt, dt + 1, row_bytes / kStepBytes, a_rsrc, br, epilogue);
+  run_tiles8<kDtype, kBFar>(smem, L, row_bytes, dt, dt + 1, row_bytes / kStepBytes, a_rsrc, br, epilogue);
 }
 
 // 3. dW += the chunk's part. A = GdT vocabulary tile (K = chunk tokens), B =
-// H^T d block. Grid: vocabulary tiles (fast) x d tiles (slow). Lane l's
-// accumulators are vocabulary rows at d column 128 wt + 32 bn + (l mod 32).
+// H^T d block, on the eight-wavefront engine. Grid: vocabulary tiles (fast)
+// x d tiles (slow). Lane l of wavefront (wv, tq) holds vocabulary rows
+// 128 wv + ... of the tile at d column k0 + 64 tq + 32 bn + (l mod 32).
 template <int kDtype, bool kBFar>
-__global__ __launch_bounds__(kThreads, 1) void dw_kernel(const char* __restrict__ GdT, const char* __restrict__ HT,
-                                                        int kpad, int vocab, int d, int n_vt, int n_dt,
-                                                        float* __restrict__ dW) {
+__global__ __launch_bounds__(kThreads8, 1) void dw_kernel(const char* __restrict__ GdT, const char* __restrict__ HT,
+                                                         int kpad, int vocab, int d, int n_vt, int n_dt,
+                                                         float* __restrict__ dW) {
   using E = Elem<kDtype>;
   __shared__ uint4 smem[kEngineSmemChunks];
-  const Lanes L = lanes();
+  const Lanes8 L = lanes8();
   int vt, dt;
   band_order(blockIdx.x, n_vt, n_dt, vt, dt);
   const int row_bytes = kBwdChunk * E::kSize;
@@ -378,36 +376,31 @@ __global__ __launch_bounds__(kThreads, 1) void dw_kernel(const char* __restrict_
     return rsrc_words(GdT + (size_t)v0 * row_bytes, (uint32_t)kBV * row_bytes);
   };
   const int4v br = rsrc_words(HT + (size_t)k0 * row_bytes, (uint32_t)min(kBT, d - k0) * row_bytes);
-  auto epilogue = [&](int tile, floatx16 (&acc)[4][4]) {
-    mfma_result_wait();
+  auto epilogue = [&](int tile, floatx16 (&acc)[4][2]) {
     const int vw = tile * kBV + L.wv * 128 + 4 * L.half;
 #pragma unroll
-    for (int bn = 0; bn < 4; ++bn) {
-      const int k = k0 + L.wt * 128 + bn * 32 + L.col;
-      // The 64 dW values of this lane's column k are read together (one
-      // memory round trip per column, not one per 32 x 32 block), then
-      // updated and written back.
-      float old[4][16];
-#pragma unroll
-      for (int bm = 0; bm < 4; ++bm)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int v = vw + bm * 32 + 8 * (i >> 2) + (i & 3);
-          old[bm][i] = v < vocab && k < d ? dW[(size_t)v * d + k] : 0.0f;
-        }
+    for (int bn = 0; bn < 2; ++bn) {
+      const int k = k0 + L.tq * 64 + bn * 32 + L.col;
 #pragma unroll
       for (int bm = 0; bm < 4; ++bm) {
+        // The block's 16 dW values of this lane's column k, read together,
+        // then updated and written back.
+        float old[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float a = acc_read(acc[bm][bn], i);
           const int v = vw + bm * 32 + 8 * (i >> 2) + (i & 3);
-          if (v < vocab && k < d) dW[(size_t)v * d + k] = old[bm][i] + a;
+          old[i] = v < vocab && k < d ? dW[(size_t)v * d + k] : 0.0f;
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int v = vw + bm * 32 + 8 * (i >> 2) + (i & 3);
+          if (v < vocab && k < d) dW[(size_t)v * d + k] = old[i] + acc[bm][bn][i];
         }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
   };
-  run_tiles<kDtype, kBFar>(smem, L, row_bytes, vt, vt + 1, kpad * E::kSize / kStepBytes, a_rsrc, br, epilogue);
+  run_tiles8<kDtype, kBFar>(smem, L, row_bytes, vt, vt + 1, kpad * E::kSize / kStepBytes, a_rsrc, br, epilogue);
 }
 
 // Workspace layout of the backward (each region 256-byte aligned).
@@ -522,12 +515,12 @@ hipError_t run_backward(const void* H, const void* W, int n_tok, int d, int voca
                          coef + c0, Gd, GdT);
     else
       hipLaunchKernelGGL((dl_far ? dlogits_kernel<kDtype, true> : dlogits_kernel<kDtype, false>),
-                         dim3((unsigned)(n_tb * n_groups)), dim3(kThreads), 0, stream, Hc,
+                         dim3((unsigned)(n_tb * n_groups)), dim3(kThreads8), 0, stream, Hc,
                          len, static_cast<const char*>(W), row_bytes, vocab, vpad, n_tb, S, G, tokens + c0, lse + c0,
                          coef + c0, Gd, GdT);
     ITL_CHECK_LAUNCH();
     hipLaunchKernelGGL((dh_far ? dh_kernel<kDtype, true> : dh_kernel<kDtype, false>),
-                       dim3((unsigned)(n_tb * n_dt)), dim3(kThreads), 0, stream,
+                       dim3((unsigned)(n_tb * n_dt)), dim3(kThreads8), 0, stream,
                        reinterpret_cast<const char*>(WT), reinterpret_cast<const char*>(Gd), vpad, d, vocab, len, n_tb, n_dt,
                        tokens + c0, coef + c0, Wp, dH + (size_t)c0 * d);
     ITL_CHECK_LAUNCH();
@@ -536,7 +529,7 @@ hipError_t run_backward(const void* H, const void* W, int n_tok, int d, int voca
                        stream, Hp + (size_t)c0 * d, (long long)d, len, d, HT, kBwdChunk);
     ITL_CHECK_LAUNCH();
     hipLaunchKernelGGL((dw_kernel<kDtype, false>),
-                       dim3((unsigned)(n_vt * n_dt)), dim3(kThreads), 0, stream,
+                       dim3((unsigned)(n_vt * n_dt)), dim3(kThreads8), 0, stream,
                        reinterpret_cast<const char*>(GdT), reinterpret_cast<const char*>(HT), kpad, vocab, d, n_vt,
                        n_dt, dW);
     ITL_CHECK_LAUNCH();

@@ -1,9 +1,14 @@
-// Tile engine: the K loop shared by every contraction of the library
-// (gfx950 / CDNA4).
+// Tile engines (gfx950 / CDNA4): the pieces every contraction of the
+// library shares (MFMA steps, LDS slots and swizzle, direct-to-LDS loads,
+// waits) and the four-wavefront K loops: the narrow one for decode-shaped
+// calls and the FP8 / MXFP4 ones. The bf16 / fp32 wide contractions (the
+// forward and the backward) run on the eight-wavefront loop of
+// tile_engine8.h, which uses the same slots, swizzle and per-block MFMA
+// sequence.
 //
-// A 256-thread workgroup (4 wavefronts, 2 x 2) multiplies 256-row tiles of
-// an operand A, walked in order, with one fixed 256-row block of an operand
-// B: acc = A_tile B^T (both row-major and K-contiguous, fp32 accumulate,
+// Four-wavefront geometry: a 256-thread workgroup (2 x 2 wavefronts)
+// multiplies 256-row tiles of an operand A, walked in order, with one fixed
+// 256-row block of an operand B: acc = A_tile B^T (both row-major and K-contiguous, fp32 accumulate,
 // K ascending in steps of 128 bytes). After each tile an epilogue sees the
 // accumulators. Wavefront (wv, wt) holds rows 128 wv .. 128 wv + 127 of the
 // A tile against rows 128 wt .. 128 wt + 127 of the B block, as 4 x 4
@@ -62,7 +67,7 @@ struct Mma<1> {  // fp32: 4 elements per lane; instruction j takes element j (k2
 // of 16 bytes), so that every global load moves whole 128-byte lines. Five
 // slots fill the LDS: one operand rotates through three of them, loaded two
 // K steps ahead, the other through two, one step ahead. By default the
-// walked operand (A) is the far one (kWSlots = 3, kHSlots = 2); run_tiles'
+// walked operand (A) is the far one (kWSlots = 3, kHSlots = 2); run_tiles8's
 // kBFar swaps the roles. Which pays depends on the K loop's length: the
 // workgroups sharing an operand segment through an XCD's L2 drift apart
 // over a long loop, and the operand that fewer of them share then misses
@@ -194,241 +199,16 @@ __device__ __forceinline__ Lanes lanes() {
 // LDS the engine needs (uint4 elements): all of a CU's 160 KiB.
 constexpr int kEngineSmemChunks = (kWSlots + kHSlots) * kSlotChunks;
 
-// Runs tiles tile_begin .. tile_end - 1 (tile_end > tile_begin). a_rsrc(t)
-// gives the buffer resource of A tile t (its first row at offset 0, its
-// valid rows' bytes as the range); b_rsrc is the fixed B block's. Rows of
-// both operands are row_bytes apart; the contraction runs over their first
-// nks * kStepBytes bytes (nks >= 1, nks * kStepBytes <= row_bytes).
-// epi(t, acc) is called after tile t with its accumulators (read them with
-// acc_read after mfma_result_wait()). Every thread of the workgroup must
-// call this.
-template <int kDtype, bool kBFar = false, class ARsrc, class Epi>
-__device__ __forceinline__ void run_tiles(uint4* smem, const Lanes& L, int row_bytes, int tile_begin, int tile_end,
-                                          int nks, const ARsrc& a_rsrc, int4v b_rsrc, Epi&& epi) {
-  // kBFar: B two K steps ahead in three slots, A one step ahead in two
-  // (the default is the other way round); the same five slots of LDS.
-  constexpr int kAS = kBFar ? kHSlots : kWSlots;
-  constexpr int kBS = kBFar ? kWSlots : kHSlots;
-  const int lane = L.lane, wave = L.wave, wv = L.wv, wt = L.wt, half = L.half, col = L.col;
-  (void)lane;
-  // Loader: wavefront w fills rows 64 w .. 64 w + 63 of both operands with
-  // eight loads each; lane i fetches row (i / 8) of an 8-row group, logical
-  // chunk (i % 8) ^ swz(row), so that it lands in its swizzled position.
-  // swz(row) = (i / 8) ^ (j & 1) for load j (row = 64 w + 8 j + i / 8).
-  const int lr = lane >> 3;
-  uint32_t voff[kDmaPerWave];
-#pragma unroll
-  for (int j = 0; j < kDmaPerWave; ++j)
-    voff[j] = (uint32_t)(wave * 64 + j * kDmaRows + lr) * (uint32_t)row_bytes + (((lane & 7) ^ lr ^ (j & 1)) * 16);
-  const uint32_t lds_wave =
-      (uint32_t)(size_t)((__attribute__((address_space(3))) uint4*)smem) + wave * 64 * kStepBytes;
-  const int4v hr = b_rsrc;
-  auto w_rsrc = [&](int tile) { return a_rsrc(tile); };
-  auto w_slot_lds = [&](int slot) { return lds_wave + (uint32_t)slot * kSlotBytes; };
-  auto h_slot_lds = [&](int slot) { return lds_wave + (uint32_t)(kAS + slot) * kSlotBytes; };
-
-  // MFMA operand reads: lane l takes row (l mod 32) of each 32-row block at
-  // logical chunk 2 kk + l / 32 (kk = K sub-step 0..3); swz(row) = swz(l mod 32).
-  int a_off[4], b_off[4];
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    const int pc = (2 * kk + half) ^ swz(col);
-    a_off[kk] = (wv * 128 + col) * kRowChunks + pc;
-    b_off[kk] = (wt * 128 + col) * kRowChunks + pc;
-  }
-
-  // K-step pipeline over the workgroup's steps g (all its tiles, K
-  // fastest). In the names below W is the walked operand A and H the fixed
-  // operand B: W(g) sits in W slot g % 3, H(g) in H slot g % 2. A step is
-  // four sub-steps of 16 MFMAs; each sub-step's 8 operand fragments are read
-  // from LDS two sub-steps ahead, spread over the MFMAs in between, so that
-  // the LDS read pipe (about 64 B/clk per CU, which a 128 x 128 wavefront
-  // tile needs in full at the MFMA peak) is never waited on. The order is
-  // pinned with scheduling barriers: left alone, the compiler issues each
-  // sub-step's LDS reads after its MFMAs and then waits for them.
-  int w_tile = tile_begin, w_ks = 0;  // next W step to load
-  int h_ks = 0;                        // next H step to load (H rows do not depend on the tile)
-  int w_slot_next = 0, h_slot_next = 0;
-  auto next_w = [&]() {  // advance, clamped to a valid step past the end
-    if (++w_ks == nks) {
-      w_ks = 0;
-      w_tile = min(w_tile + 1, tile_end - 1);
-    }
-    w_slot_next = w_slot_next == kAS - 1 ? 0 : w_slot_next + 1;
-  };
-  auto next_h = [&]() {
-    h_ks = h_ks + 1 == nks ? 0 : h_ks + 1;
-    h_slot_next = h_slot_next == kBS - 1 ? 0 : h_slot_next + 1;
-  };
-  // One sub-step: MFMA q (q = 4 bm + bn) on (A, B), interleaved with the 8
-  // reads of the next operands (RA, RB; order A0 B0 B1 B2 B3 A1 A2 A3, the
-  // order the next sub-step needs them) from slots (wsl, hsl), sub-step rkk:
-  // one read every second MFMA, or in the first 8 MFMAs when kFront (the
-  // last sub-step's reads must land before the barrier). With kDma, the 8
-  // loads of H(g + 2) and then the 8 of W(g + 3) go one per MFMA (in that
-  // order: the barrier's vmcnt(8) lets exactly the W loads stay in flight).
-  // Without kRead the sub-step reads nothing.
-  auto phase = [&](floatx16 (&acc)[4][4], const uint4 (&A)[4], const uint4 (&B)[4], auto first, auto do_mma,
-                   auto front, auto dma, auto do_read, int wsl, int hsl, int rkk, uint4 (&RA)[4], uint4 (&RB)[4]) {
-    const uint4* sa = smem + wsl * kSlotChunks;
-    const uint4* sb = smem + (kAS + hsl) * kSlotChunks;
-    int4v wr;
-    uint32_t wsoff = 0, hsoff = 0, wm = 0, hm = 0;
-    if constexpr (decltype(dma)::value) {
-      wr = w_rsrc(w_tile);
-      wsoff = (uint32_t)w_ks * kStepBytes;
-      hsoff = (uint32_t)h_ks * kStepBytes;
-      wm = w_slot_lds(w_slot_next);
-      hm = h_slot_lds(h_slot_next);
-    }
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      if constexpr (decltype(do_mma)::value) {
-        if constexpr (decltype(first)::value) Mma<kDtype>::first(acc[q >> 2][q & 3], A[q >> 2], B[q & 3]);
-        else Mma<kDtype>::step(acc[q >> 2][q & 3], A[q >> 2], B[q & 3]);
-      }
-      constexpr bool kFront = decltype(front)::value;
-      if (decltype(do_read)::value && (kFront ? q < 8 : (q & 1) == 0)) {
-        const int r = kFront ? q : q >> 1;
-        if (r == 0) RA[0] = sa[a_off[rkk]];
-        else if (r <= 4) RB[r - 1] = sb[b_off[rkk] + (r - 1) * 32 * kRowChunks];
-        else RA[r - 4] = sa[a_off[rkk] + (r - 4) * 32 * kRowChunks];
-      }
-      if constexpr (decltype(dma)::value) {
-        if constexpr (!kBFar) {
-          if (q < 8) dma16(hr, voff[q], hsoff, hm + q * 1024);
-          else dma16(wr, voff[q - 8], wsoff, wm + (q - 8) * 1024);
-        } else {  // the one-ahead operand first, as above
-          if (q < 8) dma16(wr, voff[q], wsoff, wm + q * 1024);
-          else dma16(hr, voff[q - 8], hsoff, hm + (q - 8) * 1024);
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    if constexpr (decltype(dma)::value) {
-      next_h();
-      next_w();
-    }
-  };
-
-  using T = std::true_type;
-  using F = std::false_type;
-  // Prologue: W(0), H(0), W(1); publish step 0; H(1), W(2); read the first
-  // two sub-steps' operands.
-  if constexpr (!kBFar) {
-    const int4v wr0 = w_rsrc(w_tile);
-#pragma unroll
-    for (int j = 0; j < kDmaPerWave; ++j) dma16(wr0, voff[j], (uint32_t)w_ks * kStepBytes, w_slot_lds(0) + j * 1024);
-#pragma unroll
-    for (int j = 0; j < kDmaPerWave; ++j) dma16(hr, voff[j], 0, h_slot_lds(0) + j * 1024);
-    next_w();
-    next_h();
-    const int4v wr1 = w_rsrc(w_tile);
-#pragma unroll
-    for (int j = 0; j < kDmaPerWave; ++j) dma16(wr1, voff[j], (uint32_t)w_ks * kStepBytes, w_slot_lds(1) + j * 1024);
-    next_w();
-  } else {  // W(0), H(0), H(1)
-    const int4v wr0 = w_rsrc(w_tile);
-#pragma unroll
-    for (int j = 0; j < kDmaPerWave; ++j) dma16(wr0, voff[j], (uint32_t)w_ks * kStepBytes, w_slot_lds(0) + j * 1024);
-#pragma unroll
-    for (int j = 0; j < kDmaPerWave; ++j) dma16(hr, voff[j], 0, h_slot_lds(0) + j * 1024);
-    next_w();
-    next_h();
-#pragma unroll
-    for (int j = 0; j < kDmaPerWave; ++j) dma16(hr, voff[j], (uint32_t)h_ks * kStepBytes, h_slot_lds(1) + j * 1024);
-    next_h();
-  }
-  wait_and_barrier<kDmaPerWave>();  // W(0), H(0) landed
-  {
-    const int4v wr = w_rsrc(w_tile);
-    const uint32_t hm = h_slot_lds(h_slot_next), wm = w_slot_lds(w_slot_next);
-    if constexpr (!kBFar) {  // H(1), W(2)
-#pragma unroll
-      for (int j = 0; j < kDmaPerWave; ++j) dma16(hr, voff[j], (uint32_t)h_ks * kStepBytes, hm + j * 1024);
-#pragma unroll
-      for (int j = 0; j < kDmaPerWave; ++j) dma16(wr, voff[j], (uint32_t)w_ks * kStepBytes, wm + j * 1024);
-    } else {  // W(1), H(2)
-#pragma unroll
-      for (int j = 0; j < kDmaPerWave; ++j) dma16(wr, voff[j], (uint32_t)w_ks * kStepBytes, wm + j * 1024);
-#pragma unroll
-      for (int j = 0; j < kDmaPerWave; ++j) dma16(hr, voff[j], (uint32_t)h_ks * kStepBytes, hm + j * 1024);
-    }
-    next_h();
-    next_w();
-  }
-  // Operand sets of the four sub-steps of the current K step: S0 and S1 are
-  // read two sub-steps ahead, during the previous step's sub-steps 2 and 3.
-  uint4 a0[4], b0[4], a1[4], b1[4], a2[4], b2[4], a3[4], b3[4];
-  {
-    const uint4* sa = smem;
-    const uint4* sb = smem + kAS * kSlotChunks;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      a0[m] = sa[a_off[0] + m * 32 * kRowChunks];
-      b0[m] = sb[b_off[0] + m * 32 * kRowChunks];
-      a1[m] = sa[a_off[1] + m * 32 * kRowChunks];
-      b1[m] = sb[b_off[1] + m * 32 * kRowChunks];
-    }
-  }
-  int wslot = 0, hslot = 0;  // slots of the step being multiplied
-  // One K step g. Sub-steps 0 and 1 multiply S0, S1 while S2, S3 (this
-  // step's sub-steps 2, 3) are read; the barrier then publishes step g + 1,
-  // whose loads were issued one (H) or two (W) steps earlier; step g's slots
-  // are free after it (all of step g is in registers), so H(g + 2) and
-  // W(g + 3) are loaded into them during sub-step 2, while sub-steps 2 and 3
-  // read step g + 1's first two operand sets into S0, S1. kFirst = the
-  // tile's first step (fresh accumulators). Loads past the workgroup's last
-  // step re-read a valid step into a free slot, which nothing reads again.
-  //
-  // A tile's last step (kLast) leaves S0, S1 of the next step unread: they
-  // are read after the epilogue instead, so that the epilogue has the 64
-  // VGPRs they would hold (the slots of step g + 1 are not overwritten
-  // before every wavefront has passed step g + 1's barrier).
-  auto k_step = [&](floatx16 (&acc)[4][4], auto first, auto last) {
-    using R = std::integral_constant<bool, !decltype(last)::value>;
-    phase(acc, a0, b0, first, T{}, F{}, F{}, T{}, wslot, hslot, 2, a2, b2);
-    phase(acc, a1, b1, F{}, T{}, T{}, F{}, T{}, wslot, hslot, 3, a3, b3);
-    wait_and_barrier<kDmaPerWave>();  // W(g + 1), H(g + 1) landed; W(g + 2) may still be in flight
-    wslot = wslot == kAS - 1 ? 0 : wslot + 1;
-    hslot = hslot == kBS - 1 ? 0 : hslot + 1;
-    phase(acc, a2, b2, F{}, T{}, F{}, T{}, R{}, wslot, hslot, 0, a0, b0);
-    phase(acc, a3, b3, F{}, T{}, F{}, F{}, R{}, wslot, hslot, 1, a1, b1);
-  };
-  for (int tile = tile_begin; tile < tile_end; ++tile) {
-    floatx16 acc[4][4];
-    if (nks == 1) {
-      k_step(acc, T{}, T{});
-    } else {
-      k_step(acc, T{}, F{});
-      for (int ks = 2; ks < nks; ++ks) k_step(acc, F{}, F{});
-      k_step(acc, F{}, T{});
-    }
-    epi(tile, acc);
-    const uint4* sa = smem + wslot * kSlotChunks;
-    const uint4* sb = smem + (kAS + hslot) * kSlotChunks;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      a0[m] = sa[a_off[0] + m * 32 * kRowChunks];
-      b0[m] = sb[b_off[0] + m * 32 * kRowChunks];
-      a1[m] = sa[a_off[1] + m * 32 * kRowChunks];
-      b1[m] = sb[b_off[1] + m * 32 * kRowChunks];
-    }
-  }
-  // Every wavefront is done with the LDS ring (and its loads) on return.
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-}
-
-// Narrow variant for few B rows (decode-shaped calls): the same A tiles
+// Narrow engine for few B rows (decode-shaped calls): 256-row A tiles
 // against a 64-row B block. Wavefront (wv, wt) holds rows 128 wv .. 128 wv +
 // 127 of the A tile against B rows 32 wt .. 32 wt + 31 as 4 blocks of 32 x 32.
 // Every MFMA of an accumulator block takes the same operand fragments, in
-// the same order, as in run_tiles (same slot layout and swizzle, same K
-// sub-step order, fresh accumulators at a tile's first step), so an output
-// element has the same bits in both. The work per A tile is a quarter of
-// run_tiles': the loop streams A from memory, so both operands rotate through
-// four slots and are loaded three K steps ahead.
+// the same order, as in the eight-wavefront engine run_tiles8 (same slot
+// layout and swizzle, same K sub-step order, fresh accumulators at a tile's
+// first step), so an output element has the same bits in both. The work per
+// A tile is a quarter of the wide engine's: the loop streams A from memory,
+// so both operands rotate through four slots and are loaded three K steps
+// ahead.
 constexpr int kNarrowSlots = 4;
 constexpr int kNarrowBSlotChunks = kNarrowBRows * kRowChunks;  // 512 chunks = 8 KiB
 constexpr int kNarrowBDmaPerWave = kNarrowBRows / 4 / kDmaRows;  // 2
@@ -440,7 +220,7 @@ __device__ __forceinline__ void run_tiles_narrow(uint4* smem, const Lanes& L, in
   const int lane = L.lane, wave = L.wave, wv = L.wv, wt = L.wt, half = L.half, col = L.col;
   // Loader: wavefront w fills A rows 64 w .. 64 w + 63 (8 loads) and B rows
   // 16 w .. 16 w + 15 (2 loads) of a slot; lane i fetches row (i / 8) of an
-  // 8-row group at logical chunk (i % 8) ^ swz(row), as in run_tiles.
+  // 8-row group at logical chunk (i % 8) ^ swz(row), as in every engine here.
   const int lr = lane >> 3;
   uint32_t avoff[kDmaPerWave], bvoff[kNarrowBDmaPerWave];
 #pragma unroll
@@ -480,7 +260,7 @@ __device__ __forceinline__ void run_tiles_narrow(uint4* smem, const Lanes& L, in
     next_load();
   }
   // MFMA operand reads: row (l mod 32) of each 32-row block at logical chunk
-  // 2 kk + l / 32 of sub-step kk, as in run_tiles.
+  // 2 kk + l / 32 of sub-step kk, as in run_tiles8.
   int a_off[4], b_off[4];
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
@@ -529,8 +309,9 @@ __device__ __forceinline__ void run_tiles_narrow(uint4* smem, const Lanes& L, in
   __syncthreads();
 }
 
-// FP8 (E4M3) variant of run_tiles: the same slots, swizzle, loads and
-// barrier cadence, with v_mfma_scale_f32_32x32x64_f8f6f4 (both operands
+// FP8 (E4M3) wide engine, in the four-wavefront geometry above (each
+// wavefront 128 x 128 of the 256 x 256 tile as 4 x 4 blocks): the five
+// slots, swizzle and direct-to-LDS loads above, one barrier per K step, with v_mfma_scale_f32_32x32x64_f8f6f4 (both operands
 // E4M3, block scales 1). A 128-byte K step is 128 values: two sub-steps of
 // 64, each MFMA taking 32 bytes per lane (lane half h of sub-step j: chunks
 // 4 j + 2 h and 4 j + 2 h + 1 of its row, i.e. 32 consecutive K values).
@@ -697,7 +478,7 @@ __device__ __forceinline__ void run_tiles_f8(uint4* smem, const Lanes& L, int ro
   // slots are free); sub-step 1 (Y) while step g + 1's sub-step 0 is read
   // into X and H(g + 2), W(g + 3) are loaded into step g's slots.
   // A tile's last step (kLast) calls pre and leaves X unread: X is read
-  // after the epilogue (as in run_tiles).
+  // after the epilogue, where its registers are free.
   auto k_step = [&](floatx16 (&acc)[4][4], int tile, auto first, auto last) {
     using R = std::integral_constant<bool, !decltype(last)::value>;
     phase(acc, xa, xb, first, T{}, F{}, T{}, wslot, hslot, 1, ya, yb);
@@ -740,7 +521,7 @@ __device__ __forceinline__ void run_tiles_f8(uint4* smem, const Lanes& L, int ro
 //
 // LDS: W slots of 256 rows x 64 bytes (chunk c of row r at c ^ ((r >> 1) & 3)
 // so that 8 consecutive rows at one chunk hit distinct 16-byte bank groups)
-// followed by the slot's 256 x 4 scale bytes; H slots as in run_tiles.
+// followed by the slot's 256 x 4 scale bytes; H slots as in run_tiles_q.
 constexpr int kMx4RowChunks = 4;                        // 64-byte W rows
 constexpr int kMx4WDataBytes = kBV * 64;                // 16 KiB
 constexpr int kMx4WSlotBytes = kMx4WDataBytes + kBV * 4;  // + 1 KiB of scales
@@ -790,7 +571,7 @@ __device__ __forceinline__ void run_tiles_mx4(uint4* smem, const Lanes& L, int w
                                               const ARsrc& a_rsrc, const SRsrc& s_rsrc, int4v b_rsrc, Epi&& epi) {
   const int lane = L.lane, wave = L.wave, wv = L.wv, wt = L.wt, half = L.half, col = L.col;
   const int lr = lane >> 3;
-  // H loads (as run_tiles): rows 64 wave + 8 j + lane / 8.
+  // H loads (as in run_tiles_q): rows 64 wave + 8 j + lane / 8.
   uint32_t hvoff[kDmaPerWave];
 #pragma unroll
   for (int j = 0; j < kDmaPerWave; ++j)

@@ -1,16 +1,17 @@
-// Eight-wavefront tile engine (gfx950 / CDNA4): the K loop of the wide
-// logprob kernel with two wavefronts per SIMD.
+// Eight-wavefront tile engine (gfx950 / CDNA4): the K loop of the wide bf16
+// / fp32 contractions (the logprob forward, and the backward's dlogits, dH
+// and dW) with two wavefronts per SIMD.
 //
 // A 512-thread workgroup multiplies 256-row tiles of an operand A (walked in
 // order) with one fixed 256-row block of an operand B, acc = A_tile B^T,
 // both row-major and K-contiguous, fp32 accumulate, K ascending in steps of
-// 128 bytes, like run_tiles (tile_engine.h) and through the same five LDS
-// slots, swizzle and direct-to-LDS loads. Wavefront w = 4 g + r (g = 0, 1,
+// 128 bytes, through the five LDS slots, swizzle and direct-to-LDS loads
+// of tile_engine.h. Wavefront w = 4 g + r (g = 0, 1,
 // r = 0..3) holds A rows 128 (r & 1) .. + 127 of the tile against B rows
 // 64 ((r >> 1) + 2 g) .. + 63 of the block, as 4 x 2 blocks of 32 x 32: the
 // same per-block MFMA sequence (fragments, sub-step order, fresh
-// accumulators at a tile's first step) as run_tiles and run_tiles_narrow,
-// so an output element has the same bits in all three.
+// accumulators at a tile's first step) as run_tiles_narrow, so an output
+// element has the same bits in both.
 //
 // Schedule. Waves w and w + 4 share a SIMD (the workgroup's wavefronts go
 // to the four SIMDs in a rotating order, w and w + 4 on the same one, as
@@ -59,9 +60,11 @@ __device__ __forceinline__ Lanes8 lanes8() {
   return L;
 }
 
-// Runs tiles tile_begin .. tile_end - 1 (tile_end > tile_begin), like
-// run_tiles: a_rsrc(t) is A tile t's buffer resource, b_rsrc the B block's;
-// rows are row_bytes apart; nks K steps of 128 bytes (nks >= 1). epi(t, acc)
+// Runs tiles tile_begin .. tile_end - 1 (tile_end > tile_begin): a_rsrc(t)
+// is A tile t's buffer resource (its first row at offset 0, its valid rows'
+// bytes as the range: rows past it load as zeros), b_rsrc the B block's;
+// rows are row_bytes apart; nks K steps of 128 bytes (nks >= 1,
+// nks * 128 <= row_bytes). epi(t, acc)
 // sees tile t's accumulators acc[bm][bn] (A rows 32 bm, B rows 32 bn of the
 // wavefront's 128 x 64); it may read them directly. Every thread of the
 // 512-thread workgroup must call this.
