@@ -205,10 +205,16 @@ size_t itl_reinforce_zero_backward_workspace_bytes(int64_t n_tok, int64_t d, int
  * relative error of about 2^-9 per element). Every sum has a fixed order and
  * there are no atomics, so dH and dW are run-to-run deterministic; dW's sum
  * over tokens runs in ascending token order in chunks of a fixed size.
+ * The sampled entries' sum into dW[v] is fixed by the tokens sampling v
+ * alone: in ascending token order (a stable counting sort by id), in
+ * segments of 64 tokens, groups of 64 segments, then the groups, each in
+ * order, every product and sum rounded to fp32.
  * workspace: >= itl_reinforce_zero_backward_workspace_bytes(n_tok, d,
  * vocab, dtype) bytes, 256-byte aligned (it holds transposed copies of W
- * and of a chunk of H, two copies of the chunk's dense dlogits, and a sort
- * of the token ids). vocab above about 2.1e6 returns ITL_ERR_UNSUPPORTED.
+ * and of a chunk of H, two copies of the chunk's dense dlogits, the sorted
+ * token ids and the sampled term's segment and group sums). H, W, dH and
+ * dW must be 16-byte aligned (ITL_ERR_INVALID_ARG otherwise). vocab above
+ * about 2.1e6 returns ITL_ERR_UNSUPPORTED.
  * Out-of-range token ids give unspecified values, never an out-of-bounds
  * access. */
 itl_status itl_reinforce_zero_backward(const void* H, const void* W, itl_dtype dtype,

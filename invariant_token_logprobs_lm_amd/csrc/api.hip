@@ -13,6 +13,7 @@
 #include "itl.h"
 #include "itl_config.h"
 #include "itl_launch.h"
+#include "sampled_plan.h"
 
 namespace {
 
@@ -226,6 +227,9 @@ itl_status backward(const void* H, const void* W, itl_dtype dtype, int64_t n_tok
   if (n_tok > 0 && (!H || !tokens || !lse || !coef || !dH))
     return fail(ITL_ERR_INVALID_ARG, "null H, tokens, lse, coef or dH");
   if (vocab > itl::kBwdMaxVocab) return fail(ITL_ERR_UNSUPPORTED, "vocab too large for the backward");
+  if (((reinterpret_cast<uintptr_t>(H) | reinterpret_cast<uintptr_t>(W) | reinterpret_cast<uintptr_t>(dH) |
+        reinterpret_cast<uintptr_t>(dW)) & 15) != 0)
+    return fail(ITL_ERR_INVALID_ARG, "H, W, dH and dW must be 16-byte aligned");
   const size_t need = itl::backward_workspace_bytes(n_tok, d, vocab, (int)dtype);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(ITL_ERR_WORKSPACE, "workspace missing or smaller than itl_reinforce_zero_backward_workspace_bytes()");
@@ -405,14 +409,15 @@ const char* itl_build_info(void) {
   static const std::string info = [] {
     char buf[768];
     snprintf(buf, sizeof buf,
-             "itl 0.2 arch=gfx950 threads=%d token_block=%d vocab_tile=%d k_step_bytes=%d w_slots=%d h_slots=%d "
+             "itl 0.3 arch=gfx950 threads=%d wide_threads=%d token_block=%d vocab_tile=%d k_step_bytes=%d w_slots=%d h_slots=%d "
              "swap_slots_over_k_steps=%d max_slices=%d slices=balanced narrow_max_tokens=%d narrow_token_block=%d "
              "mfma_bf16=32x32x16 mfma_f32=32x32x2 fp8=e4m3_row_scaled mfma_fp8=32x32x64 mxfp4=e2m1_e8m0_32 "
              "bwd_chunk_tokens=%d loss_segment_tokens=%d loss_lane_segment=%d loss_wave_segment=%d loss_threads=%d "
-             "loss_mean_chunk=%d loss_sums=f64",
-             itl::kThreads, itl::kBT, itl::kBV, itl::kStepBytes, itl::kWSlots, itl::kHSlots, itl::kNearBMaxSteps,
+             "loss_mean_chunk=%d loss_sums=f64 bwd_sampled_sort=stable_counting bwd_sampled_segment=%d "
+             "bwd_sampled_group=%d",
+             itl::kThreads, itl::kThreads8, itl::kBT, itl::kBV, itl::kStepBytes, itl::kWSlots, itl::kHSlots, itl::kNearBMaxSteps,
              itl::kMaxSlices, itl::kNarrowMaxTokens, itl::kNarrowBRows, itl::kBwdChunkTokens, itl::kSegTokens,
-             itl::kLaneSeg, itl::kWaveSeg, itl::kLossThreads, itl::kFinishChunk);
+             itl::kLaneSeg, itl::kWaveSeg, itl::kLossThreads, itl::kFinishChunk, itl::kRunSeg, itl::kRunGroup);
     return std::string(buf);
   }();
   return info.c_str();

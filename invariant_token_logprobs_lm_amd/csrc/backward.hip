@@ -10,7 +10,9 @@
 // G splits into a dense part -coef[t] p[t, v] and one sampled entry
 // +coef[t] per token. The sampled entries are applied exactly, in fp32:
 //   dH[t]    += coef[t] W[y_t]
-//   dW[v]    += sum over tokens t with y_t = v, ascending t, of coef[t] H[t]
+//   dW[v]     = sum over tokens t with y_t = v of coef[t] H[t]
+// the latter (sampled.hip) in an order fixed by the tokens of id v alone,
+// before any dense part is added.
 // The dense part g[t, v] = -coef[t] p[t, v] is formed in the head's dtype
 // (bf16 for bf16 heads: the MFMA operand) and contracted on the matrix cores
 // with the eight-wavefront tile engine (tile_engine8.h), one chunk of
@@ -30,8 +32,6 @@
 // every contraction "both operands K-contiguous", the form the engine runs.
 
 #include <algorithm>
-
-#include <hipcub/hipcub.hpp>
 
 #include "itl_launch.h"
 #include "tile_engine.h"
@@ -84,55 +84,6 @@ __global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ in
   for (int i = ty; i < 64; i += 4) {
     const int c = c0 + i, r = r0 + tx;
     if (c < cols && r < out_cols) out[(size_t)c * out_cols + r] = tile[tx][i];
-  }
-}
-
-__global__ __launch_bounds__(256) void fill_zero_kernel(float4* __restrict__ p, size_t n4) {
-  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (size_t)gridDim.x * 256)
-    p[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-}
-
-__global__ __launch_bounds__(256) void iota_kernel(uint32_t* __restrict__ p, int n) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i < n) p[i] = (uint32_t)i;
-}
-
-// Sampled term of dW. ys/ts: token ids sorted by id, ties in ascending token
-// order (a stable sort). One wavefront per sorted position; the wavefront at
-// the first position of a run of equal ids sums coef[t] H[t] over the run, in
-// order, and writes the vocabulary row (dW is all zeros before).
-template <int kDtype>
-__global__ __launch_bounds__(256) void dw_sampled_kernel(const uint32_t* __restrict__ ys,
-                                                         const uint32_t* __restrict__ ts, int n_tok,
-                                                         const typename Elem<kDtype>::T* __restrict__ H,
-                                                         const float* __restrict__ coef, int d, int vocab,
-                                                         float* __restrict__ dW) {
-  const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (i >= n_tok) return;
-  const uint32_t v = ys[i];
-  if ((i > 0 && ys[i - 1] == v) || v >= (uint32_t)vocab) return;
-  int end = i + 1;
-  while (end < n_tok && ys[end] == v) ++end;
-  for (int k0 = 0; k0 < d; k0 += 64 * 8) {
-    float acc[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
-    for (int j = i; j < end; ++j) {
-      const uint32_t t = ts[j];
-      const float c = coef[t];
-      const typename Elem<kDtype>::T* h = H + (size_t)t * d;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int k = k0 + e * 64 + lane;
-        if (k < d) acc[e] = fmaf(c, Elem<kDtype>::to_f(h[k]), acc[e]);
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int k = k0 + e * 64 + lane;
-      if (k < d) dW[(size_t)v * d + k] = acc[e];
-    }
   }
 }
 
@@ -405,16 +356,8 @@ __global__ __launch_bounds__(kThreads8, 1) void dw_kernel(const char* __restrict
 
 // Workspace layout of the backward (each region 256-byte aligned).
 struct BwdLayout {
-  size_t wt, ht, gd, gdt, keys, vals, keys_out, vals_out, sort_tmp, sort_tmp_bytes, total;
+  size_t wt, ht, gd, gdt, sampled, total;
 };
-
-size_t sort_temp_bytes(long long n_tok) {
-  size_t bytes = 0;
-  // A size query (null temp storage): computes `bytes`, launches nothing.
-  (void)hipcub::DeviceRadixSort::SortPairs(nullptr, bytes, (const uint32_t*)nullptr, (uint32_t*)nullptr,
-                                     (const uint32_t*)nullptr, (uint32_t*)nullptr, (int)n_tok, 0, 32, nullptr);
-  return bytes;
-}
 
 BwdLayout bwd_layout(long long n_tok, long long d, long long vocab, int es) {
   BwdLayout L{};
@@ -429,12 +372,7 @@ BwdLayout bwd_layout(long long n_tok, long long d, long long vocab, int es) {
   L.ht = take((size_t)d * kBwdChunk * es);
   L.gd = take((size_t)kBwdChunk * vpad * es);
   L.gdt = take((size_t)vpad * kBwdChunk * es);
-  L.keys = take((size_t)n_tok * 4);
-  L.vals = take((size_t)n_tok * 4);
-  L.keys_out = take((size_t)n_tok * 4);
-  L.vals_out = take((size_t)n_tok * 4);
-  L.sort_tmp_bytes = sort_temp_bytes(n_tok);
-  L.sort_tmp = take(L.sort_tmp_bytes);
+  L.sampled = take(sampled_dw_workspace_bytes(n_tok, d, vocab));
   L.total = off;
   return L;
 }
@@ -462,28 +400,9 @@ hipError_t run_backward(const void* H, const void* W, int n_tok, int d, int voca
     if (e != hipSuccess) return e;   \
   } while (0)
 
-  // dW = 0, then the sampled term.
-  const size_t dw4 = (size_t)vocab * d / 4;  // d is a multiple of 64
-  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)std::min<size_t>(65536, (dw4 + 255) / 256)), dim3(256), 0, stream,
-                     reinterpret_cast<float4*>(dW), dw4);
-  ITL_CHECK_LAUNCH();
-  if (n_tok > 0) {
-    uint32_t* keys = reinterpret_cast<uint32_t*>(ws + Ly.keys);
-    uint32_t* vals = reinterpret_cast<uint32_t*>(ws + Ly.vals);
-    uint32_t* keys_out = reinterpret_cast<uint32_t*>(ws + Ly.keys_out);
-    uint32_t* vals_out = reinterpret_cast<uint32_t*>(ws + Ly.vals_out);
-    e = hipMemcpyAsync(keys, tokens, (size_t)n_tok * 4, hipMemcpyDeviceToDevice, stream);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(iota_kernel, dim3((unsigned)ceil_div(n_tok, 256)), dim3(256), 0, stream, vals, n_tok);
-    ITL_CHECK_LAUNCH();
-    size_t tmp = Ly.sort_tmp_bytes;
-    e = hipcub::DeviceRadixSort::SortPairs(ws + Ly.sort_tmp, tmp, keys, keys_out, vals, vals_out, n_tok, 0, 32,
-                                           stream);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(dw_sampled_kernel<kDtype>, dim3((unsigned)ceil_div(n_tok, 4)), dim3(256), 0, stream, keys_out,
-                       vals_out, n_tok, Hp, coef, d, vocab, dW);
-    ITL_CHECK_LAUNCH();
-  }
+  // dW = the sampled term (zeros in rows no token samples).
+  e = launch_sampled_dw(H, kDtype, n_tok, d, vocab, tokens, coef, dW, ws + Ly.sampled, stream);
+  if (e != hipSuccess) return e;
   if (n_tok == 0) return hipSuccess;
 
   // W^T [d, Vpad], zero-padded.

@@ -14,7 +14,8 @@
 
 namespace itl {
 
-constexpr int kThreads = 256;        // 4 wavefronts of 64 lanes
+constexpr int kThreads = 256;        // 4 wavefronts of 64 lanes (narrow and FP8 engines)
+constexpr int kThreads8 = 512;       // 8 wavefronts (the bf16 / fp32 wide engine)
 constexpr int kBT = 256;             // tokens per block (MFMA B operand)
 constexpr int kBV = 256;             // vocabulary rows per tile (MFMA A operand)
 constexpr int kStepBytes = 128;      // bytes of one operand row per K step (64 bf16 / 32 fp32)

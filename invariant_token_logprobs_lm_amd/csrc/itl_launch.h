@@ -45,6 +45,13 @@ constexpr int kBwdChunkTokens = 16384;
 // addressable by 32-bit buffer offsets over 256-row tiles).
 constexpr long long kBwdMaxVocab = (1LL << 31) / (256LL * 4) - 256;
 
+// The backward's sampled term: dW[v] = sum over tokens t with y_t = v of
+// coef[t] H[t] for every row v (zeros where no token samples v), in the
+// fixed order of sampled_plan.h.
+size_t sampled_dw_workspace_bytes(long long n_tok, long long d, long long vocab);
+hipError_t launch_sampled_dw(const void* H, int dtype, int n_tok, int d, int vocab, const int32_t* tokens,
+                             const float* coef, float* dW, void* workspace, hipStream_t stream);
+
 // logits (nullable): the forward's z[t, v] at logits[t * ld + v]; the dlogits
 // are then formed from them instead of recomputing the contraction (same bits).
 hipError_t launch_reinforce_zero_backward(const void* H, const void* W, int dtype, int n_tok, int d, int vocab,

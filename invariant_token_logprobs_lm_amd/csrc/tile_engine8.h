@@ -40,7 +40,6 @@
 
 namespace itl {
 
-constexpr int kThreads8 = 512;
 constexpr int kDma8PerWave = 4;  // loads per wavefront per K step of each operand (32 rows)
 
 struct Lanes8 {

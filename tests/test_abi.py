@@ -130,10 +130,15 @@ def test_loss_and_advantage_validation(lib):
                                            v(256), 1 << 30, None) == UNSUPPORTED
     assert lib.itl_reinforce_zero_backward(v(1), None, 0, 4, 64, 10, v(1), v(1), v(1), v(1), v(1),
                                            v(256), 1 << 30, None) == INVALID
+    # H, W, dH and dW 16-byte aligned (the sampled term's row loads and stores)
+    assert lib.itl_reinforce_zero_backward(v(1), v(16), 0, 4, 64, 10, v(1), v(1), v(1), v(16), v(16),
+                                           v(256), 1 << 40, None) == INVALID
+    assert lib.itl_reinforce_zero_backward(v(16), v(16), 0, 4, 64, 10, v(1), v(1), v(1), v(16), v(8),
+                                           v(256), 1 << 40, None) == INVALID
     # workspace checked before anything is launched
-    assert lib.itl_reinforce_zero_backward(v(1), v(1), 0, 4, 64, 10, v(1), v(1), v(1), v(1), v(1),
+    assert lib.itl_reinforce_zero_backward(v(16), v(16), 0, 4, 64, 10, v(1), v(1), v(1), v(16), v(16),
                                            v(256), 16, None) == WORKSPACE
-    assert lib.itl_reinforce_zero_backward(v(1), v(1), 0, 4, 64, 10, v(1), v(1), v(1), v(1), v(1),
+    assert lib.itl_reinforce_zero_backward(v(16), v(16), 0, 4, 64, 10, v(1), v(1), v(1), v(16), v(16),
                                            v(257), 1 << 40, None) == WORKSPACE
 
 
@@ -198,9 +203,10 @@ def _sources(folder, exts):
 
 
 # The only atomics allowed: integer counters of the diagnostics' exact median
-# (histogram counts and candidate slots), whose result cannot depend on the
-# order the additions land in. Every floating-point result has a fixed order.
-_INTEGER_ATOMIC_FILES = {"diagnostics.hip"}
+# (histogram counts and candidate slots) and of the backward's counting sort
+# (digit counts in LDS), whose result cannot depend on the order the
+# additions land in. Every floating-point result has a fixed order.
+_INTEGER_ATOMIC_FILES = {"diagnostics.hip", "sampled.hip"}
 
 
 def test_no_float_atomics_in_kernels():

@@ -208,3 +208,97 @@ def test_backward_full_size_determinism(cuda):
     scale = dW.double().abs().sum(dim=0).max().item()
     say(f"[backward full] max |column sum of dW| = {colsum:.3e} (column abs-sum up to {scale:.3e})")
     assert colsum <= 1e-2 * scale
+
+
+def _zipf_ids(n, vocab, rng, hot, share):
+    """Token ids with one id taking `share` of the tokens and the rest
+    Zipf-like (id k drawn with weight 1 / (k + 1)), as sampled text gives."""
+    w = 1.0 / np.arange(1, vocab + 1)
+    y = rng.choice(vocab, size=n, p=w / w.sum()).astype(np.int32)
+    y[rng.random(n) < share] = hot
+    return y
+
+
+def test_backward_zipf_tokens(cuda):
+    """Zipf-like ids with one id at about 35 % of the tokens (a run of
+    several thousand tokens: several segment groups in the sampled term),
+    over two token chunks: oracle parity and run-to-run bits."""
+    import torch
+
+    rng = np.random.default_rng(11)
+    H, W, _ = _random_head(20000, 128, 3000, torch.bfloat16, seed=123, device=cuda)
+    y = _zipf_ids(20000, 3000, rng, hot=1234, share=0.35)
+    say(f"[backward zipf] hot id share {(y == 1234).mean():.3f}, distinct ids {len(np.unique(y))}")
+    _check_full(H, W, torch.as_tensor(y, device=cuda), np.random.default_rng(6), label="zipf")
+
+
+def _emulate_sampled_rows(Hf, y, c, vocab, seg=64, group=64):
+    """dW's sampled term in the library's documented order, in float32 with
+    every product and sum rounded on its own: each id's tokens in ascending
+    order, summed in segments of `seg`, groups of `group` segments, then the
+    groups (a run of at most one segment is its own sum)."""
+    d = Hf.shape[1]
+    out = np.zeros((vocab, d), np.float32)
+    c = c.astype(np.float32)
+    for v in np.unique(y):
+        toks = np.nonzero(y == v)[0]
+        sums = []
+        for j in range(0, len(toks), seg):
+            acc = np.zeros(d, np.float32)
+            for t in toks[j:j + seg]:
+                acc = acc + c[t] * Hf[t]
+            sums.append(acc)
+        if len(sums) == 1:
+            out[v] = sums[0]
+            continue
+        groups = []
+        for g in range(0, len(sums), group):
+            acc = np.zeros(d, np.float32)
+            for s in sums[g:g + group]:
+                acc = acc + s
+            groups.append(acc)
+        if len(groups) == 1:
+            out[v] = groups[0]
+            continue
+        acc = np.zeros(d, np.float32)
+        for s in groups:
+            acc = acc + s
+        out[v] = acc
+    return out
+
+
+def test_sampled_term_follows_its_order(cuda):
+    """With lse far above every logit the dense part of the dlogits is
+    exactly zero, so dW is the sampled term alone and dH the sampled rows
+    coef[t] W[y_t]: both must equal, value for value, a float32 emulation of
+    the documented order (runs of 6,000 tokens: two groups; 500: one group of
+    8 segments; 65 and 64 tokens; single tokens; rows no token samples are
+    zero). Not an oracle comparison: this pins the summation order itself."""
+    import torch
+
+    itl = _itl()
+    rng = np.random.default_rng(3)
+    n, d, vocab = 12000, 128, 1000
+    y = rng.integers(100, vocab, size=n).astype(np.int32)
+    pos = rng.permutation(n)
+    y[pos[:6000]] = 5
+    y[pos[6000:6500]] = 17
+    y[pos[6500:6565]] = 31
+    y[pos[6565:6629]] = 40
+    y[(y >= 500) & (y < 520)] = 499  # ids 500..519 sampled by no token
+    H = torch.randn(n, d, generator=torch.Generator().manual_seed(4)).to(torch.bfloat16)
+    W = (torch.randn(vocab, d, generator=torch.Generator().manual_seed(5)) * 0.05).to(torch.bfloat16)
+    coef = rng.normal(0, 1e-3, n).astype(np.float32)
+    lse = np.full(n, 1e4, np.float32)
+    dH, dW = itl.reinforce_zero_backward(H.to(cuda), W.to(cuda), torch.as_tensor(y, device=cuda),
+                                         torch.as_tensor(lse, device=cuda), torch.as_tensor(coef, device=cuda))
+    torch.cuda.synchronize()
+    Hf, Wf = H.float().numpy(), W.float().numpy()
+    want_W = _emulate_sampled_rows(Hf, y, coef, vocab)
+    want_H = np.float32(0) + coef[:, None] * Wf[y]
+    got_W, got_H = dW.cpu().numpy(), dH.cpu().numpy()
+    bad_rows = np.nonzero(~np.all(got_W == want_W, axis=1))[0]
+    say(f"[sampled order] rows differing from the emulation: {len(bad_rows)} {bad_rows[:8]}")
+    assert len(bad_rows) == 0
+    assert np.array_equal(got_H, want_H)
+    assert not got_W[500:520].any()

@@ -1,9 +1,10 @@
 """Host-side checks of the kernels' work decomposition: the C++ functions
-the kernels use (itl_config.h, loss_plan.h), compiled into host programs
-with hipcc. The logprob kernels over a few thousand (n_tok, vocab) pairs:
-every (token block, slice) pair computed once, slices tiling the vocabulary,
-the narrow grid's coverage. The loss's token pass over seeded response
-layouts. No GPU needed."""
+the kernels use (itl_config.h, loss_plan.h, sampled_plan.h), compiled into
+host programs with hipcc. The logprob kernels over a few thousand (n_tok,
+vocab) pairs: every (token block, slice) pair computed once, slices tiling
+the vocabulary, the narrow grid's coverage. The loss's token pass over
+seeded response layouts. The backward's sampled term over seeded id arrays.
+No GPU needed."""
 
 import os
 import shutil
@@ -73,4 +74,29 @@ def test_loss_token_pass_decomposition(loss_plan_check, seed):
     segment-sum slots of different responses disjoint; 300 seeded layouts
     (tiny, short, around one segment, long, mixed, a single long response)."""
     r = subprocess.run([loss_plan_check, str(seed), "300"], capture_output=True, text=True)
+    assert r.returncode == 0 and r.stdout.startswith("ok"), r.stdout + r.stderr
+
+
+@pytest.fixture(scope="module")
+def sampled_plan_check(tmp_path_factory):
+    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(hipcc):
+        pytest.skip("hipcc not available")
+    out = str(tmp_path_factory.mktemp("sampled") / "sampled_plan_check")
+    cmd = [hipcc, "-O2", "-std=c++17", "-I", os.path.join(ROOT, "invariant_token_logprobs_lm_amd", "csrc"),
+           os.path.join(ROOT, "tests", "host", "sampled_plan_check.cpp"), "-o", out]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    return out
+
+
+@pytest.mark.parametrize("seed", [1, 2, 3])
+def test_sampled_term_decomposition(sampled_plan_check, seed):
+    """The backward's sampled term (sampled_plan.h): the counting sort's
+    per-block counts, digit-major scan and in-order placement give the
+    stable sort by id over every pass; every token of a valid id in exactly
+    one segment, every segment of a long run in one group; segment and group
+    slots of different runs disjoint and in range; 60 seeded id arrays (flat,
+    one id at 40 %, a single id, out-of-range ids, empty and tiny)."""
+    r = subprocess.run([sampled_plan_check, str(seed), "60"], capture_output=True, text=True)
     assert r.returncode == 0 and r.stdout.startswith("ok"), r.stdout + r.stderr
