@@ -7,6 +7,8 @@ Every response of the workload is evaluated
   * as a prefill chunk of random length followed by one-token decode steps
     (decode steps batched across the responses still decoding, as a rollout
     engine would, plus a few responses decoded alone at one token per call),
+  * on streams restricted to subsets of the CUs, alone and beside another
+    call,
 and every logprob and every per-response loss must carry identical bits in
 every evaluation ("vLLM Train-Inference Consistency Release Notes", section
 "Achieving Bitwise Consistency": batch independence, phase consistency).
@@ -135,3 +137,28 @@ def test_concurrent_stream_load(stress):
     torch.cuda.synchronize()
     for k, i in enumerate(ids):
         assert same_bits(lp[int(off[k]):int(off[k + 1])], s["lp"][_seg(s, i)])
+
+
+
+@pytest.mark.parametrize("mask", ["half the CUs", "8 of every 16 CUs", "32 CUs", "8 CUs"])
+def test_cu_masked_streams(cuda, mask):
+    """Scheduling perturbation ("vLLM Train-Inference Consistency Release
+    Notes", section "Achieving Bitwise Consistency": results must not depend
+    on how the work is scheduled): the whole packed batch and three permuted
+    batches on a stream restricted to a subset of the CUs
+    (hipExtStreamCreateWithCUMask: half, 8 of every 16, 32, 8, each spread
+    over the eight XCDs), alone and while another logprob call
+    runs on every CU of the default stream; every logprob and per-response
+    loss keeps the bits of the unrestricted run. A CU-masked stream takes a
+    hardware queue of its own, of which a process has few, so each mask runs
+    in a fresh child process (tests/cu_mask_child.py) holding only the
+    default stream and that one."""
+    import os
+    import subprocess
+    import sys
+
+    child = os.path.join(os.path.dirname(os.path.abspath(__file__)), "cu_mask_child.py")
+    r = subprocess.run([sys.executable, "-u", child, mask], capture_output=True, text=True, timeout=240)
+    for line in r.stdout.splitlines():
+        say(line)
+    assert r.returncode == 0, (r.stdout + r.stderr)[-3000:]
