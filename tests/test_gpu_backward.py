@@ -10,6 +10,8 @@ chunks, the tiny fp32 head, and the large-MoE head shape (reduced token
 count, sampled rows). Run-to-run bit equality of dH and dW is checked too.
 """
 
+import re
+
 import numpy as np
 import pytest
 
@@ -187,8 +189,11 @@ def test_backward_large_moe_head_rows(cuda):
 
 def test_backward_full_size_determinism(cuda):
     """The large-MoE head at full size (the benchmark's backward launch):
-    finite, run-to-run bit-identical, and every column of dW sums to about
-    zero over the vocabulary (each token's dlogits sum to zero)."""
+    finite, run-to-run bit-identical, every column of dW sums to about zero
+    over the vocabulary (each token's dlogits sum to zero), and dH rows of
+    tokens in every one of the backward's token chunks match the oracle
+    (given the GPU's coefficients: a dH row needs only its own token's
+    log-normaliser over the full vocabulary)."""
     import torch
     from synth import WORKLOADS, draw_head, draw_layout, sample_tokens
 
@@ -208,6 +213,22 @@ def test_backward_full_size_determinism(cuda):
     scale = dW.double().abs().sum(dim=0).max().item()
     say(f"[backward full] max |column sum of dW| = {colsum:.3e} (column abs-sum up to {scale:.3e})")
     assert colsum <= 1e-2 * scale
+    import oracle
+
+    chunk = int(re.search(r"bwd_chunk_tokens=(\d+)", itl.build_info()).group(1))
+    rng = np.random.default_rng(21)
+    n = lay.n_tok
+    tok = [int(rng.integers(c0, min(n, c0 + chunk))) for c0 in range(0, n, chunk)]
+    tok = np.unique(np.concatenate([tok, rng.choice(n, size=24 - len(tok) if len(tok) < 24 else 0, replace=False)]))
+    tt = torch.as_tensor(tok, device=cuda)
+    dH_o, _ = oracle.reinforce_zero_backward_rows(host_array(H.index_select(0, tt)), host_array(W),
+                                                   y.index_select(0, tt).cpu().numpy(),
+                                                   coef.index_select(0, tt).cpu().numpy().astype(np.float64),
+                                                   np.arange(len(tok)), np.zeros(0, np.int64))
+    eH = _fro_rel(dH.index_select(0, tt).cpu().numpy(), dH_o)
+    say(f"[backward full] {len(tok)} dH rows over {(n + chunk - 1) // chunk} chunks: fro rel {eH:.2e} "
+        f"(max row rel {_row_rel_max(dH.index_select(0, tt).cpu().numpy(), dH_o):.2e})")
+    assert eH <= TOL
 
 
 def _zipf_ids(n, vocab, rng, hot, share):
