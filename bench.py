@@ -565,11 +565,11 @@ def sustained_mfma_probe(device, blocks=1024, iters=40000):
     operands that change every instruction (random normal bf16 values, a
     4 x 4 block tile per wavefront, one wavefront per SIMD) and no memory
     traffic: the power-limited ceiling a real contraction meets, measured
-    with the probe library built beside libitl.so."""
+    with the probe library (bench_mfma_probe.hip) built beside this file."""
     import ctypes
     import torch
 
-    path = os.path.join(ROOT, "invariant_token_logprobs_lm_amd", "libitl_probe.so")
+    path = os.path.join(ROOT, "libitl_bench_probe.so")
     lib = ctypes.CDLL(path)
     lib.itl_probe_operand_bytes.restype = ctypes.c_size_t
     lib.itl_probe_flops.restype = ctypes.c_double

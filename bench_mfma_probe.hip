@@ -1,8 +1,9 @@
 // Sustained-throughput probe of the bf16 matrix cores (gfx950), for the
 // benchmark's roofline: what v_mfma_f32_32x32x16_bf16 sustains on this chip
 // with operand data that changes every instruction, as in a real contraction,
-// and no memory traffic at all. Built into libitl_probe.so, separate from the
-// library; the benchmark calls it through ctypes.
+// and no memory traffic at all. Benchmark infrastructure, not part of the
+// library: built into libitl_bench_probe.so beside bench.py, which calls it
+// through ctypes.
 //
 // Each 256-thread workgroup (one wavefront per SIMD) runs `iters` rounds of
 // 16 MFMAs into 16 accumulators; MFMA j of a round takes A fragment j / 4 and

@@ -4,9 +4,10 @@
 
 Each csrc/*.hip file is compiled separately (in parallel) with hipcc for
 gfx950 only, then linked into invariant_token_logprobs_lm_amd/libitl.so.
-The benchmark's matrix-core probe (probe/*.hip) is linked separately into
-libitl_probe.so; the library never uses it. Packed-fp32 instruction
-selection is disabled for device code.
+build_probe() links the benchmark's matrix-core probe (bench_mfma_probe.hip,
+beside bench.py) into its own libitl_bench_probe.so there; the library
+never uses it. Packed-fp32 instruction selection is disabled for device
+code.
 """
 
 import concurrent.futures
@@ -20,8 +21,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libitl.so")
-PROBE_LIB = os.path.join(PKG, "libitl_probe.so")
-PROBE_SRC = os.path.join(PKG, "probe")
+PROBE_LIB = os.path.join(ROOT, "libitl_bench_probe.so")
+PROBE_SRC = os.path.join(ROOT, "bench_mfma_probe.hip")
 ARCH = "gfx950"
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
@@ -76,17 +77,22 @@ def _link(objs, lib, verbose):
 
 
 def build(verbose=False):
-    """Compile every HIP source and link libitl.so (and the probe library).
-    Always recompiles."""
+    """Compile every HIP source and link libitl.so. Always recompiles."""
     os.makedirs(BUILD, exist_ok=True)
     srcs = sources()
-    probe = sources(PROBE_SRC)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs) + len(probe))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), srcs + probe))
-    _link(objs[:len(srcs)], LIB, verbose)
-    _link(objs[len(srcs):], PROBE_LIB, verbose)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
+    _link(objs, LIB, verbose)
     return LIB
+
+
+def build_probe(verbose=False):
+    """Compile the benchmark's matrix-core probe into libitl_bench_probe.so."""
+    os.makedirs(BUILD, exist_ok=True)
+    _link([_compile(PROBE_SRC, verbose)], PROBE_LIB, verbose)
+    return PROBE_LIB
 
 
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
+    print(build_probe(verbose="-v" in sys.argv))

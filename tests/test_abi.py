@@ -258,7 +258,7 @@ def test_mismatch_stat_fields_match_header_and_oracle():
 def test_probe_library_is_separate_and_loads():
     """The benchmark's matrix-core probe lives in its own library; libitl.so
     does not export it."""
-    probe = ctypes.CDLL(os.path.join(ROOT, "invariant_token_logprobs_lm_amd", "libitl_probe.so"))
+    probe = ctypes.CDLL(os.path.join(ROOT, "libitl_bench_probe.so"))
     for name in ("itl_probe_operand_bytes", "itl_probe_flops", "itl_probe_mfma_bf16"):
         assert hasattr(probe, name)
     probe.itl_probe_operand_bytes.restype = ctypes.c_size_t
