@@ -8,7 +8,8 @@ already resident in HBM: the fused LM-head logprob (contraction + online
 log-sum-exp + gather), the group advantage and the REINFORCE Zero loss with
 its per-token coefficients. The default workload is the Qwen3-4B-shaped head
 (d = 2560, vocab = 151936, 32 responses of 2048..16384 tokens). The JSON line
-also carries a forward + backward figure on the large-MoE-shaped head
+also carries the forward on the 1.5B-shaped head (d = 1536) and on the
+tiny fp32 head, and a forward + backward figure on the large-MoE-shaped head
 (d = 7168, vocab = 129280): with the forward's logits kept in HBM when they
 fit (159 GB), else with the backward recomputing them; both are timed when
 memory allows.
@@ -29,10 +30,12 @@ sys.path.insert(0, ROOT)
 METRIC = "sampled-token logprobs/sec (fwd, fwd+bwd) at 1 GPU; % bf16 MFMA peak"
 PEAK_FP8_TFLOPS = 5033.2  # MI355X dense FP8 matrix-core peak (2 x the bf16 figure)
 PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 dense bf16 flop/clk/CU (published 2.5 PFLOP/s)
+PEAK_F32_TFLOPS = 157.3  # MI355X dense fp32 matrix-core peak (published)
 PEAK_HBM_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["invariant_token_logprobs_lm_amd/csrc/lmhead.hip",
                   "invariant_token_logprobs_lm_amd/csrc/tile_engine.h",
+                  "invariant_token_logprobs_lm_amd/csrc/tile_engine8.h",
                   "invariant_token_logprobs_lm_amd/csrc/itl_config.h",
                   "invariant_token_logprobs_lm_amd/csrc/device_common.h",
                   "invariant_token_logprobs_lm_amd/csrc/lse_fold.h",
@@ -54,7 +57,7 @@ def kernel_source_hash():
 def measured_traffic(workload_key):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if
     it was taken on the current kernel source; otherwise None."""
-    path = os.path.join(PROFILES, f"lmhead_lse_partial_{workload_key}_traffic.json")
+    path = os.path.join(PROFILES, f"lmhead_lse_partial8_{workload_key}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -121,6 +124,32 @@ def time_steps(step, steps, warmup):
     total_ms = start.elapsed_time(end)
     head_ms = [a.elapsed_time(b) for a, b in head]
     return total_ms / steps, sum(head_ms) / steps, wall
+
+
+def forward_leg(key, device, steps):
+    """The forward step (logprob + advantage + loss) on another workload of
+    the table, timed like the headline: tokens/s and the logprob kernel's
+    fraction of its dtype's matrix-core peak."""
+    import torch
+    from synth import WORKLOADS
+
+    wl = WORKLOADS[key]
+    s = setup_forward(wl, device)
+    n_tok = s["lay"].n_tok
+    ms_step, ms_head, _ = time_steps(lambda ev: forward_step(s, ev), steps, 2)
+    flops = 2.0 * wl.d * wl.vocab * n_tok
+    tf = flops / (ms_head * 1e-3) / 1e12
+    peak = PEAK_F32_TFLOPS if wl.dtype == "f32" else PEAK_BF16_TFLOPS
+    log(f"[bench] {key}: step {ms_step:.3f} ms, logprob kernel {ms_head:.3f} ms -> {tf:.1f} TFLOP/s "
+        f"({100 * tf / peak:.1f}% of the {wl.dtype} peak)")
+    out = {"workload": f"{key} forward logprob + group advantage + REINFORCE Zero loss", "d": wl.d,
+           "vocab": wl.vocab, "dtype": wl.dtype, "responses": s["lay"].n_resp, "n_tok": n_tok, "steps": steps,
+           "ms_per_step": ms_step, "value": n_tok / (ms_step * 1e-3), "unit": "sampled-token logprobs/s",
+           "ms_logprob": ms_head, "tflops_logprob": tf, "frac_peak": tf / peak,
+           "peak": f"{peak} TFLOP/s dense {'fp32' if wl.dtype == 'f32' else 'bf16'}"}
+    del s
+    torch.cuda.empty_cache()
+    return out
 
 
 def setup_backward(wl, device):
@@ -655,6 +684,7 @@ def main():
     ap.add_argument("--no-loss", action="store_true")
     ap.add_argument("--no-mismatch", action="store_true")
     ap.add_argument("--no-fp8", action="store_true")
+    ap.add_argument("--no-other-forward", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="before timing, run one plain 1 GiB device-to-device copy: the reference whose "
                          "FETCH_SIZE / WRITE_SIZE counters calibrate the HBM traffic figures")
@@ -709,7 +739,7 @@ def main():
         },
         "roofline": {
             "bound": "mfma",
-            "kernel": "lmhead_lse_partial (+ lse_combine)",
+            "kernel": "lmhead_lse_partial8 (+ lse_combine)",
             "achieved": achieved,
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
@@ -736,6 +766,11 @@ def main():
         out["loss"] = loss_leg(s, device)
     del s
     torch.cuda.empty_cache()
+    if not args.no_other_forward:
+        # the other forward workloads of the table: the 1.5B-shaped head, and
+        # the tiny fp32 head (launch-bound: a few microseconds per call)
+        out["forward_other"] = {k: forward_leg(k, device, args.steps) for k in ("qwen2.5-1.5b-head", "tiny")
+                                if k != wl.key}
     if not args.no_decode:
         out["decode"] = decode_leg(wl, device)
         torch.cuda.empty_cache()
