@@ -1,7 +1,8 @@
-// Per-lane online log-sum-exp fold of the head's logits, shared by every
-// logprob kernel of the library: a token's partials, and so its logprob,
-// have the same bits whichever kernel produced them, as long as the
-// kernels feed the same logit values in the same block order.
+// Per-lane online log-sum-exp folds of the head's logits: fold_column for
+// the bf16 / fp32 heads (wide and narrow kernels), fold_values for the FP8 /
+// MXFP4 heads (block by block). Kernels that share a fold and feed it the
+// same logit values in the same order give a token the same partials, and
+// so the same logprob, bit for bit.
 #pragma once
 
 #include "device_common.h"
@@ -20,10 +21,10 @@ struct Col {
 
 // Fold one 32 x 32 block of logits (rows vw + 32 bm + ..., this lane's
 // token column; z[i] = row 32 bm + 8 (i / 4) + 4 half + (i % 4)) into the
-// state. The sampled logit is picked with a select tree keyed on the bits of
-// its row, without a branch. Every kernel folds with this one function, in
-// the same block order, so a token's state has the same bits whichever
-// kernel computed it.
+// state (the FP8 / MXFP4 kernels' fold). The sampled logit is picked with a
+// select tree keyed on the bits of its row, without a branch. Their wide and
+// narrow kernels fold with this one function, in the same block order, so a
+// token's state has the same bits whichever of them computed it.
 //
 // kPartial (a std::bool_constant): the block may hold rows past the
 // vocabulary, which are masked. Callers choose it once per tile, so that a
@@ -143,19 +144,6 @@ __device__ __forceinline__ void flush_slice(Col& c, int tok, int n_tok, int half
   if (half == 0 && tok < n_tok) part[part_index] = make_float2(c.m, c.s);
   c.m = -INFINITY;
   c.s = 0.0f;
-}
-
-
-// Fold one accumulator block as it stands (the bf16 / fp32 heads). The
-// lane's 16 logits are copied out of the matrix-core registers where they
-// are used (acc_read), so the fold needs few VGPRs next to the accumulators.
-template <class kPartial, class kPick = std::true_type>
-__device__ __forceinline__ void fold_block(Col& c, const floatx16& a, int bm, int vw, int half, int vocab,
-                                           kPartial partial, kPick pick = kPick{}) {
-  floatx16 z;  // a vector, not an array: it must stay in registers
-#pragma unroll
-  for (int i = 0; i < 16; ++i) z[i] = acc_read(a, i);
-  fold_values(c, z, bm, vw, half, vocab, partial, pick);
 }
 
 }  // namespace itl

@@ -521,7 +521,7 @@ __device__ __forceinline__ void run_tiles_f8(uint4* smem, const Lanes& L, int ro
 //
 // LDS: W slots of 256 rows x 64 bytes (chunk c of row r at c ^ ((r >> 1) & 3)
 // so that 8 consecutive rows at one chunk hit distinct 16-byte bank groups)
-// followed by the slot's 256 x 4 scale bytes; H slots as in run_tiles_q.
+// followed by the slot's 256 x 4 scale bytes; H slots as in run_tiles_f8.
 constexpr int kMx4RowChunks = 4;                        // 64-byte W rows
 constexpr int kMx4WDataBytes = kBV * 64;                // 16 KiB
 constexpr int kMx4WSlotBytes = kMx4WDataBytes + kBV * 4;  // + 1 KiB of scales
@@ -571,7 +571,7 @@ __device__ __forceinline__ void run_tiles_mx4(uint4* smem, const Lanes& L, int w
                                               const ARsrc& a_rsrc, const SRsrc& s_rsrc, int4v b_rsrc, Epi&& epi) {
   const int lane = L.lane, wave = L.wave, wv = L.wv, wt = L.wt, half = L.half, col = L.col;
   const int lr = lane >> 3;
-  // H loads (as in run_tiles_q): rows 64 wave + 8 j + lane / 8.
+  // H loads (as in run_tiles_f8): rows 64 wave + 8 j + lane / 8.
   uint32_t hvoff[kDmaPerWave];
 #pragma unroll
   for (int j = 0; j < kDmaPerWave; ++j)
