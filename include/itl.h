@@ -161,7 +161,9 @@ itl_status itl_group_advantage(const float* rewards, const int32_t* group_offset
 /* Bytes of device workspace itl_reinforce_zero_loss needs for (n_tok,
  * n_resp): about 8 n_resp + n_tok / 128 bytes (fp64 per-response losses,
  * fp64 sums of 2048-token segments of long responses, fp64 partial sums of
- * the mean). Returns 0 for n_resp == 0 and SIZE_MAX for invalid sizes. */
+ * the mean), plus 24 bytes per 2048 tokens for more than 512 responses (the
+ * response holding each 2048-token window's first token). Returns 0 for
+ * n_resp == 0 and SIZE_MAX for invalid sizes. */
 size_t itl_reinforce_zero_loss_workspace_bytes(int64_t n_tok, int32_t n_resp);
 
 /* REINFORCE Zero loss [RZ]. Response i owns tokens resp_offsets[i] ..

@@ -24,7 +24,11 @@
 // the batch. The mean's tree depends on the number of responses only.
 //
 // Work. Token pass: workgroup b owns the segments that start in tokens
-// [b kSeg, (b + 1) kSeg) of the packed batch. They tile a contiguous span of
+// [b kSeg, (b + 1) kSeg) of the packed batch; it finds the responses holding
+// tokens b kSeg and (b + 1) kSeg by a search of the offsets (batches of up to
+// kLossThreads responses: one round) or from a window map written by one
+// thread per response beforehand (larger batches: the search's dependent
+// rounds were most of a workgroup's time). They tile a contiguous span of
 // fewer than 2 kSeg tokens, which the workgroup reads once, coalesced, into
 // LDS as ratios, sums segment by segment (turning each segment's ratios into
 // its coefficients in place) and then writes the coefficients, coalesced.
@@ -161,10 +165,31 @@ __device__ __forceinline__ void emit_segment(int i, long long s, long long e, lo
   }
 }
 
+// The response holding token w kSeg (w = a window of the token pass), with
+// its token range: written by loss_window_kernel, one thread per response,
+// for batches of more than kLossThreads responses (smaller ones search the
+// offsets inside the token pass in one round).
+struct WinHolder {
+  long long s, e;
+  long long i;
+};
+
+__global__ __launch_bounds__(256) void loss_window_kernel(const int64_t* __restrict__ off, int n_resp,
+                                                          long long n_tok, long long n_win,
+                                                          WinHolder* __restrict__ win) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= n_resp) return;
+  long long s, e;
+  resp_bounds(off, i, n_tok, s, e);
+  for (long long w = (s + kSegTokens - 1) / kSegTokens; w < n_win && w * kSegTokens < e; ++w)
+    win[w] = WinHolder{s, e, i};
+}
+
 __global__ __launch_bounds__(kLossThreads) void loss_tokens_kernel(
     const float* __restrict__ lp, const float* __restrict__ lpr, const float* __restrict__ adv,
     const int64_t* __restrict__ off, int n_resp, long long n_tok, float* __restrict__ resp_loss,
-    float* __restrict__ coef, double* __restrict__ l64, double* __restrict__ segp, long long n_segp) {
+    float* __restrict__ coef, double* __restrict__ l64, double* __restrict__ segp, long long n_segp,
+    const WinHolder* __restrict__ win) {
   // the span's ratios; a segment's entries become its coefficients once the
   // segment is summed
   __shared__ float ratio_s[kSpan];
@@ -178,10 +203,21 @@ __global__ __launch_bounds__(kLossThreads) void loss_tokens_kernel(
   // first at or after W1 (the end of the batch if W1 is past it).
   const long long W0 = (long long)blockIdx.x * kSegTokens, W1 = W0 + kSegTokens;
   int ia, ib;
-  find_responses(off, n_resp, W0, W1 < n_tok ? W1 : W0, ia, ib);
   long long sa, ea, sb, eb;
-  resp_bounds(off, ia, n_tok, sa, ea);
-  resp_bounds(off, ib, n_tok, sb, eb);
+  if (win != nullptr) {  // the holders from the window map, clamped (bad offsets: unspecified, in bounds)
+    const WinHolder ha = win[blockIdx.x];
+    const WinHolder hb = W1 < n_tok ? win[blockIdx.x + 1] : ha;
+    ia = (int)plan_clamp(ha.i, 0, n_resp - 1);
+    ib = (int)plan_clamp(hb.i, 0, n_resp - 1);
+    sa = plan_clamp(ha.s, 0, n_tok);
+    ea = plan_clamp(ha.e, sa, n_tok);
+    sb = plan_clamp(hb.s, 0, n_tok);
+    eb = plan_clamp(hb.e, sb, n_tok);
+  } else {
+    find_responses(off, n_resp, W0, W1 < n_tok ? W1 : W0, ia, ib);
+    resp_bounds(off, ia, n_tok, sa, ea);
+    resp_bounds(off, ib, n_tok, sb, eb);
+  }
   const Span sp = window_span(W0, n_tok, sa, ea, sb, eb);
   const long long p = sp.p, q = sp.q;
   const int span = (int)(q - p);
@@ -416,10 +452,14 @@ hipError_t launch_group_advantage(const float* rewards, const int32_t* group_off
   return hipGetLastError();
 }
 
+long long n_windows(long long n_tok) { return ceil_div(n_tok, kSegTokens); }
+bool use_window_map(long long n_resp) { return n_resp > kLossThreads; }
+
 size_t loss_workspace_bytes(long long n_tok, long long n_resp) {
   if (n_resp <= 0) return 0;
   return align256((size_t)n_resp * sizeof(double)) + align256((size_t)n_segment_slots(n_tok) * sizeof(double)) +
-         align256((size_t)n_finish_chunks(n_resp) * sizeof(double));
+         align256((size_t)n_finish_chunks(n_resp) * sizeof(double)) +
+         (use_window_map(n_resp) ? align256((size_t)n_windows(n_tok) * sizeof(WinHolder)) : 0);
 }
 
 hipError_t launch_reinforce_zero_loss(const float* logprob, const float* rollout_logprob, const float* advantages,
@@ -430,10 +470,20 @@ hipError_t launch_reinforce_zero_loss(const float* logprob, const float* rollout
   double* segp = reinterpret_cast<double*>(ws + align256((size_t)n_resp * sizeof(double)));
   const long long n_segp = n_segment_slots(n_tok);
   double* part = reinterpret_cast<double*>(reinterpret_cast<char*>(segp) + align256((size_t)n_segp * sizeof(double)));
+  WinHolder* win = use_window_map(n_resp) ? reinterpret_cast<WinHolder*>(reinterpret_cast<char*>(part) +
+                                                                       align256((size_t)n_finish_chunks(n_resp) *
+                                                                                sizeof(double)))
+                                          : nullptr;
   if (n_tok > 0) {
-    hipLaunchKernelGGL(loss_tokens_kernel, dim3((unsigned)ceil_div(n_tok, kSegTokens)), dim3(kLossThreads), 0,
-                       stream, logprob, rollout_logprob, advantages, resp_offsets, n_resp, n_tok, resp_loss, coef,
-                       l64, segp, n_segp);
+    if (win != nullptr) {
+      hipLaunchKernelGGL(loss_window_kernel, dim3((unsigned)ceil_div(n_resp, 256)), dim3(256), 0, stream,
+                         resp_offsets, n_resp, n_tok, n_windows(n_tok), win);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(loss_tokens_kernel, dim3((unsigned)n_windows(n_tok)), dim3(kLossThreads), 0, stream, logprob,
+                       rollout_logprob, advantages, resp_offsets, n_resp, n_tok, resp_loss, coef, l64, segp, n_segp,
+                       win);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -106,9 +106,12 @@ def test_loss_workspace_sizes(lib):
     r = lambda x: -(-x // 256) * 256
     assert w(0, 0) == 0 and w(100, 0) == 0
     # fp64 per-response losses, two fp64 slots per 2048-token window (+2),
-    # one fp64 partial per 1024 responses
-    for n_tok, n_resp in ((10, 3), (294884, 32), (16 * 2 ** 20, 2 ** 21)):
+    # one fp64 partial per 1024 responses; above 512 responses, a 24-byte
+    # holder per 2048-token window
+    for n_tok, n_resp in ((10, 3), (294884, 32), (300000, 512), (300000, 513), (16 * 2 ** 20, 2 ** 21)):
         want = r(8 * n_resp) + r(8 * 2 * (-(-n_tok // 2048) + 1)) + r(8 * -(-n_resp // 1024))
+        if n_resp > 512:
+            want += r(24 * -(-n_tok // 2048))
         assert w(n_tok, n_resp) == want
     assert w(-1, 3) == ctypes.c_size_t(-1).value and w(3, -1) == ctypes.c_size_t(-1).value
 

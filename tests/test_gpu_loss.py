@@ -244,14 +244,17 @@ def test_response_loss_across_the_tree_boundaries(cuda):
     _alone_batch_permuted(lp, lpr, A, off, rl, np.arange(len(lens)), cuda, rng)
 
 
-def test_long_responses_at_every_window_phase(cuda):
+@pytest.mark.parametrize("pairs", [40, 300])
+def test_long_responses_at_every_window_phase(cuda, pairs):
     """Multi-segment responses starting at many offsets relative to the token
     pass's 2048-token windows (short fillers shift them): parity and the same
-    bits alone, in the batch and permuted."""
+    bits alone, in the batch and permuted. With 600 responses the batch finds
+    each window's responses through the window map, alone through the search
+    of the offsets: the two must agree bit for bit."""
     lane, wave, seg, _ = _loss_constants()
-    rng = np.random.default_rng(33)
+    rng = np.random.default_rng(33 + pairs)
     lens = []
-    for k in range(40):
+    for k in range(pairs):
         lens.append(int(rng.integers(1, seg)))             # a filler that shifts the phase
         lens.append(int(rng.integers(seg + 1, 4 * seg)))    # two to four segments
     T = np.array(lens)
@@ -259,7 +262,7 @@ def test_long_responses_at_every_window_phase(cuda):
     lp = -np.abs(rng.normal(6, 2, off[-1])).astype(np.float32)
     lpr = (lp + rng.normal(0, 0.05, off[-1])).astype(np.float32)
     A = rng.normal(0, 1, T.size).astype(np.float32)
-    rl, _, _ = _check_loss(lp, lpr, A, off, cuda, "window phases")
+    rl, _, _ = _check_loss(lp, lpr, A, off, cuda, f"window phases, {T.size} responses")
     _alone_batch_permuted(lp, lpr, A, off, rl, np.arange(1, T.size, 2)[:12], cuda, rng)
 
 
