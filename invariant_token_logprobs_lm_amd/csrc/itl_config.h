@@ -30,8 +30,9 @@ constexpr int kNarrowBRows = 64;      // tokens per block of the narrow (few-tok
 constexpr int kNarrowMaxTokens = 64;   // calls with at most this many tokens use the narrow kernel
 constexpr int kSuperBand = 64;       // token blocks walked together, slice group by slice group (workgroup order)
 constexpr int kBwdSuperBand = 32;    // the same for the backward kernels' walk (64 measured 3 % slower there)
-constexpr int kNearBMaxSteps = 64;   // load schedule only: K loops longer than this stage the fixed operand
-                                     // two K steps ahead (measured 7 % faster at 112 steps, 4 % slower at 40)
+constexpr int kNearBMaxSteps = 48;   // load schedule only: K loops longer than this stage the fixed operand
+                                     // two K steps ahead (eight-wavefront forward at 65,536 tokens, same bits:
+                                     // 64 steps (d = 4096) 2-3 % faster; 112 and 40 steps within 1 % either way)
 constexpr int kDMultiple = 64;       // d must be a multiple of this
 constexpr int kF8WideMinD = 256;     // the wide FP8 kernel needs two K steps of 128 values; smaller d runs narrow
 
