@@ -181,8 +181,8 @@ __global__ __launch_bounds__(256) void loss_window_kernel(const int64_t* __restr
   if (i >= n_resp) return;
   long long s, e;
   resp_bounds(off, i, n_tok, s, e);
-  for (long long w = (s + kSegTokens - 1) / kSegTokens; w < n_win && w * kSegTokens < e; ++w)
-    win[w] = WinHolder{s, e, i};
+  const long long w1 = end_window(e) < n_win ? end_window(e) : n_win;
+  for (long long w = first_window(s); w < w1; ++w) win[w] = WinHolder{s, e, i};
 }
 
 __global__ __launch_bounds__(kLossThreads) void loss_tokens_kernel(

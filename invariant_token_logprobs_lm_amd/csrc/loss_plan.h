@@ -46,6 +46,13 @@ __host__ __device__ inline Span window_span(long long w0, long long n_tok, long 
   return Span{p, q};
 }
 
+// Windows whose first token w kSeg the response [s, e) holds: w0 .. w1 - 1
+// (none for an empty range). The window map of large batches is written
+// from these, one response per thread, each window by the one response
+// holding its first token.
+__host__ __device__ inline long long first_window(long long s) { return (s + kSegTokens - 1) / kSegTokens; }
+__host__ __device__ inline long long end_window(long long e) { return (e + kSegTokens - 1) / kSegTokens; }
+
 // The segment start of the response [s, e) that lies in the span [p, q),
 // if any (there is at most one).
 __host__ __device__ inline bool segment_in_span(long long s, long long e, long long p, long long q, long long& c) {

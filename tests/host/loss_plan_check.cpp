@@ -5,7 +5,8 @@
 // kSegTokens from its response's start and lies inside its span, a span is
 // shorter than 2 kSegTokens and holds at most one start of a response, the
 // kernel's enumeration rounds reach every response that overlaps a span, and
-// the segment-sum slots of different responses never meet.
+// the segment-sum slots of different responses never meet, and the window
+// map names each window's holder.
 // Usage: loss_plan_check <seed> <n_layouts>. Prints "ok <layouts>" or the
 // first violation and exits 1.
 #include <stdint.h>
@@ -90,6 +91,17 @@ static int check(const std::vector<long long>& T) {
         }
       }
     }
+  }
+  // the window map: each window written once, by the holder of its first token
+  {
+    std::vector<int> writer(n_win, -1);
+    for (int i = 0; i < n_resp; ++i)
+      for (long long w = first_window(off[i]); w < std::min(end_window(off[i + 1]), n_win); ++w) {
+        if (writer[w] != -1) return printf("window %lld written by responses %d and %d\n", w, writer[w], i), 1;
+        writer[w] = i;
+      }
+    for (long long w = 0; w < n_win; ++w)
+      if (writer[w] != holder(w * kSegTokens)) return printf("window %lld mapped to %d, held by %d\n", w, writer[w], holder(w * kSegTokens)), 1;
   }
   // (tokens of a response never visited stay uncovered and fail below)
   if (prev_q != n_tok) return printf("spans end at %lld, batch at %lld\n", prev_q, n_tok), 1;
