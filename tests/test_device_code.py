@@ -7,9 +7,10 @@
   reuse placed there by the register allocator would act on a value that
   has not arrived. This test finds every such load in the generated
   assembly and checks the instructions up to the next vmcnt wait.
-* The logprob kernels compile without scratch (no register spills): a
-  spill reload makes the compiler wait for every outstanding load,
-  including the operand tiles in flight into LDS.
+* The logprob kernels and the backward's contractions compile without
+  scratch (no register spills): a spill reload makes the compiler wait for
+  every outstanding load, including the operand tiles in flight into LDS.
+  So do the sampled term's row-sum kernels.
 """
 
 import os
@@ -95,6 +96,14 @@ def test_asm_scale_loads_are_not_touched_before_their_wait(tmp_path):
     ("lmhead.hip", "lmhead_lse_partial_narrow_kernelILi0ELb0E"),
     ("fp8.hip", "lmhead_fp8_partial_kernel"),
     ("fp8.hip", "lmhead_mxfp4_partial_kernel"),
+    ("backward.hip", "dlogits_kernelILi0E"),  # the backward's contractions, on the eight-wavefront engine
+    ("backward.hip", "dh_kernelILi0E"),
+    ("backward.hip", "dw_kernelILi0E"),
+    ("backward.hip", "dlogits_kernelILi1E"),
+    ("backward.hip", "dh_kernelILi1E"),
+    ("backward.hip", "dw_kernelILi1E"),
+    ("sampled.hip", "short_rows_kernel"),  # the sampled term's row sums
+    ("sampled.hip", "segment_sums_kernel"),
 ])
 def test_wide_kernels_have_no_scratch(tmp_path, src, kernel):
     r = _compile(os.path.join(build.CSRC, src), str(tmp_path),
