@@ -4,6 +4,7 @@ host programs with hipcc. The logprob kernels over a few thousand (n_tok,
 vocab) pairs: every (token block, slice) pair computed once, slices tiling
 the vocabulary, the narrow grid's coverage. The loss's token pass over
 seeded response layouts. The backward's sampled term over seeded id arrays.
+The programs run under the host address and undefined-behaviour sanitizers.
 No GPU needed."""
 
 import os
@@ -16,17 +17,27 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-@pytest.fixture(scope="module")
-def grid_check(tmp_path_factory):
+# The checks are host programs (no device code); they are built with the
+# address and undefined-behaviour sanitizers on the host side, so an
+# out-of-range index or an overflow in the shared index arithmetic aborts.
+SANITIZE = ["-Xarch_host", "-fsanitize=address,undefined", "-Xarch_host", "-fno-sanitize-recover=all"]
+
+
+def _build_host_check(tmp_path_factory, name):
     hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     if not os.path.exists(hipcc):
         pytest.skip("hipcc not available")
-    out = str(tmp_path_factory.mktemp("grid") / "grid_check")
-    cmd = [hipcc, "-O2", "-std=c++17", "-I", os.path.join(ROOT, "invariant_token_logprobs_lm_amd", "csrc"),
-           os.path.join(ROOT, "tests", "host", "grid_check.cpp"), "-o", out]
+    out = str(tmp_path_factory.mktemp(name) / name)
+    cmd = [hipcc, "-O1", "-g", "-std=c++17", *SANITIZE, "-I", os.path.join(ROOT, "invariant_token_logprobs_lm_amd", "csrc"),
+           os.path.join(ROOT, "tests", "host", name + ".cpp"), "-o", out]
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-2000:]
     return out
+
+
+@pytest.fixture(scope="module")
+def grid_check(tmp_path_factory):
+    return _build_host_check(tmp_path_factory, "grid_check")
 
 
 def _run(exe, pairs):
@@ -55,15 +66,7 @@ def test_random_shapes(grid_check):
 
 @pytest.fixture(scope="module")
 def loss_plan_check(tmp_path_factory):
-    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
-    if not os.path.exists(hipcc):
-        pytest.skip("hipcc not available")
-    out = str(tmp_path_factory.mktemp("loss") / "loss_plan_check")
-    cmd = [hipcc, "-O2", "-std=c++17", "-I", os.path.join(ROOT, "invariant_token_logprobs_lm_amd", "csrc"),
-           os.path.join(ROOT, "tests", "host", "loss_plan_check.cpp"), "-o", out]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    assert r.returncode == 0, r.stderr[-2000:]
-    return out
+    return _build_host_check(tmp_path_factory, "loss_plan_check")
 
 
 @pytest.mark.parametrize("seed", [1, 2, 3])
@@ -79,15 +82,7 @@ def test_loss_token_pass_decomposition(loss_plan_check, seed):
 
 @pytest.fixture(scope="module")
 def sampled_plan_check(tmp_path_factory):
-    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
-    if not os.path.exists(hipcc):
-        pytest.skip("hipcc not available")
-    out = str(tmp_path_factory.mktemp("sampled") / "sampled_plan_check")
-    cmd = [hipcc, "-O2", "-std=c++17", "-I", os.path.join(ROOT, "invariant_token_logprobs_lm_amd", "csrc"),
-           os.path.join(ROOT, "tests", "host", "sampled_plan_check.cpp"), "-o", out]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    assert r.returncode == 0, r.stderr[-2000:]
-    return out
+    return _build_host_check(tmp_path_factory, "sampled_plan_check")
 
 
 @pytest.mark.parametrize("seed", [1, 2, 3])
