@@ -74,16 +74,22 @@
 extern "C" {
 #endif
 
-typedef enum itl_status {
+/* Status and dtype codes are plain int32_t values (an enum would make an
+ * unknown dtype code passed from C undefined behaviour in the C++ library;
+ * as an int32_t it is a value like any other, answered with
+ * ITL_ERR_UNSUPPORTED). */
+typedef int32_t itl_status;
+enum {
   ITL_OK = 0,
   ITL_ERR_INVALID_ARG = 1, /* null pointer, negative size, size overflow */
   ITL_ERR_UNSUPPORTED = 2, /* a shape or dtype this build does not handle */
   ITL_ERR_WORKSPACE = 3,   /* workspace missing or too small */
   ITL_ERR_HIP = 4,         /* a HIP runtime call or launch failed */
   ITL_ERR_BAD_INPUT = 5    /* itl_check_inputs found an invalid value */
-} itl_status;
+};
 
-typedef enum itl_dtype { ITL_BF16 = 0, ITL_F32 = 1 } itl_dtype;
+typedef int32_t itl_dtype;
+enum { ITL_BF16 = 0, ITL_F32 = 1 };
 
 /* Bytes of device workspace itl_lmhead_logprob needs for (n_tok, vocab):
  * about (16 S + 4) n_tok with S = min(ceil(vocab / 256), 256) vocabulary

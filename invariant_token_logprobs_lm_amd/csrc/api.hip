@@ -45,7 +45,7 @@ itl_status check_head(itl_dtype dtype, int64_t n_tok, int64_t d, int64_t vocab) 
   if (n_tok > kMaxTok) return fail(ITL_ERR_UNSUPPORTED, "n_tok too large for one call");
   if (vocab > kMaxVocab) return fail(ITL_ERR_UNSUPPORTED, "vocab too large");
   // a 256-row operand block must be addressable with 32-bit buffer offsets
-  if (d * elem_size(dtype) * (int64_t)itl::kBT >= ((int64_t)1 << 31)) return fail(ITL_ERR_UNSUPPORTED, "d too large");
+  if (d >= ((int64_t)1 << 31) / (elem_size(dtype) * (int64_t)itl::kBT)) return fail(ITL_ERR_UNSUPPORTED, "d too large");
   const int64_t grid = itl::ceil_div(n_tok, itl::kBT) * itl::n_slice_groups(n_tok, vocab);
   if (grid > INT32_MAX) return fail(ITL_ERR_UNSUPPORTED, "problem too large for one launch");
   return ITL_OK;
@@ -213,6 +213,8 @@ itl_status itl_reinforce_zero_loss(const float* logprob, const float* rollout_lo
 size_t itl_reinforce_zero_backward_workspace_bytes(int64_t n_tok, int64_t d, int64_t vocab, itl_dtype dtype) {
   if (n_tok < 0 || d <= 0 || vocab <= 0 || n_tok > kMaxTok || vocab > kMaxVocab) return SIZE_MAX;
   if (dtype != ITL_BF16 && dtype != ITL_F32) return SIZE_MAX;
+  // shapes the backward refuses get no size either (and no wrapped product)
+  if (d % itl::kDMultiple != 0 || d >= ((int64_t)1 << 31) / (elem_size(dtype) * (int64_t)itl::kBT)) return SIZE_MAX;
   return itl::backward_workspace_bytes(n_tok, d, vocab, (int)dtype);
 }
 
@@ -287,7 +289,7 @@ itl_status itl_lmhead_logprob_fp8(const uint8_t* Hq, const float* h_scale, const
   if (d % kFp8DMultiple != 0) return fail(ITL_ERR_UNSUPPORTED, "d must be a multiple of 128");
   if (n_tok > kMaxTok) return fail(ITL_ERR_UNSUPPORTED, "n_tok too large for one call");
   if (vocab > kMaxVocab) return fail(ITL_ERR_UNSUPPORTED, "vocab too large");
-  if (d * (int64_t)itl::kBT >= ((int64_t)1 << 31)) return fail(ITL_ERR_UNSUPPORTED, "d too large");
+  if (d >= ((int64_t)1 << 31) / (int64_t)itl::kBT) return fail(ITL_ERR_UNSUPPORTED, "d too large");
   if (vocab > (int64_t)(UINT32_MAX / 4)) return fail(ITL_ERR_UNSUPPORTED, "vocab too large");
   // the grid of the kernel that runs: narrow for few tokens or d = 128
   const bool narrow = n_tok <= itl::kNarrowMaxTokens || d < itl::kF8WideMinD;
@@ -313,7 +315,7 @@ itl_status itl_quantize_rows_mxfp4(const void* X, itl_dtype dtype, int64_t n_row
   if (n_rows < 0 || d <= 0) return fail(ITL_ERR_INVALID_ARG, "n_rows must be >= 0 and d > 0");
   if (dtype != ITL_BF16 && dtype != ITL_F32) return fail(ITL_ERR_UNSUPPORTED, "dtype must be ITL_BF16 or ITL_F32");
   if (d % kFp8DMultiple != 0) return fail(ITL_ERR_UNSUPPORTED, "d must be a multiple of 128");
-  if (n_rows * (d / 32) > (int64_t)INT32_MAX * 256) return fail(ITL_ERR_UNSUPPORTED, "too many rows");
+  if (d > INT32_MAX || n_rows > ((int64_t)INT32_MAX * 256) / (d / 32)) return fail(ITL_ERR_UNSUPPORTED, "too many rows");
   if (n_rows == 0) return ITL_OK;
   if (!X || !Xq || !scale_codes) return fail(ITL_ERR_INVALID_ARG, "null X, Xq or scale_codes");
   if ((reinterpret_cast<uintptr_t>(Xq) & 15) != 0) return fail(ITL_ERR_INVALID_ARG, "Xq must be 16-byte aligned");
@@ -331,7 +333,7 @@ itl_status itl_lmhead_logprob_mxfp4(const uint8_t* Hq, const float* h_scale, con
   if (d % kFp8DMultiple != 0) return fail(ITL_ERR_UNSUPPORTED, "d must be a multiple of 128");
   if (n_tok > kMaxTok) return fail(ITL_ERR_UNSUPPORTED, "n_tok too large for one call");
   if (vocab > kMaxVocab) return fail(ITL_ERR_UNSUPPORTED, "vocab too large");
-  if (d * (int64_t)itl::kBT >= ((int64_t)1 << 31)) return fail(ITL_ERR_UNSUPPORTED, "d too large");
+  if (d >= ((int64_t)1 << 31) / (int64_t)itl::kBT) return fail(ITL_ERR_UNSUPPORTED, "d too large");
   const int64_t grid = itl::ceil_div(n_tok, itl::kBT) * itl::n_slice_groups(n_tok, vocab);
   if (grid > INT32_MAX) return fail(ITL_ERR_UNSUPPORTED, "problem too large for one launch");
   if (n_tok == 0) return ITL_OK;
