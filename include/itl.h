@@ -212,7 +212,9 @@ size_t itl_reinforce_zero_backward_workspace_bytes(int64_t n_tok, int64_t d, int
  * rounded to the head's dtype before its contractions (for bf16 heads a
  * relative error of about 2^-9 per element). Every sum has a fixed order and
  * there are no atomics, so dH and dW are run-to-run deterministic; dW's sum
- * over tokens runs in ascending token order in chunks of a fixed size.
+ * over tokens runs in ascending token order in chunks of a fixed size. A
+ * row dH[t] involves token t alone and has the same bits whatever its
+ * batch-mates and position (given the same lse[t] and coef[t]).
  * The sampled entries' sum into dW[v] is fixed by the tokens sampling v
  * alone: in ascending token order (a stable counting sort by id), in
  * segments of 64 tokens, groups of 64 segments, then the groups, each in

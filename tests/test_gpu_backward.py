@@ -323,3 +323,29 @@ def test_sampled_term_follows_its_order(cuda):
     assert len(bad_rows) == 0
     assert np.array_equal(got_H, want_H)
     assert not got_W[500:520].any()
+
+
+def test_dh_rows_are_batch_invariant(cuda):
+    """dH[t] = sum_v G[t, v] W[v] + coef[t] W[y_t] involves token t alone, and
+    each token's column of the contraction is computed by the same
+    instruction sequence at any position: given the same lse and coef, a
+    token's dH row has the same bits in the full batch, alone, and in a
+    permuted sub-batch that straddles the backward's token chunks."""
+    import torch
+
+    itl = _itl()
+    H, W, y = _random_head(16384 + 700, 256, 3000, torch.bfloat16, seed=77, device=cuda)
+    lse = itl.lmhead_logprob(H, W, y)[1]
+    coef = torch.as_tensor(np.random.default_rng(8).normal(0, 1e-3, H.shape[0]).astype(np.float32), device=cuda)
+    dH, _ = itl.reinforce_zero_backward(H, W, y, lse, coef)
+    rng = np.random.default_rng(9)
+    pick = np.sort(rng.choice(H.shape[0], 40, replace=False))
+    for t in pick[:6]:
+        s = slice(int(t), int(t) + 1)
+        dH1, _ = itl.reinforce_zero_backward(H[s], W, y[s], lse[s], coef[s])
+        assert same_bits(dH1, dH[s]), int(t)
+    perm = torch.as_tensor(rng.permutation(np.concatenate([pick, np.arange(16000, 16900)])), device=cuda)
+    dH2, _ = itl.reinforce_zero_backward(H[perm].contiguous(), W, y[perm].contiguous(), lse[perm].contiguous(),
+                                         coef[perm].contiguous())
+    torch.cuda.synchronize()
+    assert same_bits(dH2, dH[perm])
