@@ -72,6 +72,9 @@ def test_tiny_workload_all_tokens(cuda):
         (513, 320, 8192 + 256, "bf16"),  # 33 slices of one tile, d not a multiple of 256
         (5200, 64, 150 * 256 - 17, "bf16"),  # 21 x 150 > 2048: 8 slices per workgroup, last group of 6
         (300, 4160, 3005, "bf16"),   # 65 K steps: the token block staged two K steps ahead
+        (300, 3072, 2000, "bf16"),   # 48 K steps: the last length with the token block one step ahead
+        (300, 3136, 2000, "bf16"),   # 49 K steps: the first with it two steps ahead
+        (260, 32768, 700, "bf16"),   # 256 K steps of 64 KiB rows: the largest d tested
         (300, 2112, 1000, "f32"),    # 66 K steps of fp32: the same ring order, fp32 MFMA
     ],
 )
