@@ -141,6 +141,7 @@ def test_tiny_workload_backward(cuda):
         (257, 64, 1000, "f32"),           # fp32 path, one K step per row
         (1, 192, 300, "bf16"),            # a single token
         (513, 320, 8192 + 256, "bf16"),   # d not a multiple of the 256-row tile
+        (300, 3136, 2000, "bf16"),        # 49 K steps: the recomputed logits' token block two steps ahead
     ],
 )
 def test_backward_shapes(cuda, n_tok, d, vocab, dtype_name):
