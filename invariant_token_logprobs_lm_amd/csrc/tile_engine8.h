@@ -155,8 +155,9 @@ __device__ __forceinline__ void run_tiles8(uint4* smem, const Lanes8& L, int row
       for (int bn = 0; bn < 2; ++bn) acc[bm][bn] = floatx16{};
   };
   // One sub-step: 8 MFMAs on set X; with kRead the reads of the next
-  // sub-step (step rs, sub-step rkk, into set X ^ 1) go two after each of the
-  // first 3 MFMAs (their latency then has five MFMAs to pass). kDma = 1: the
+  // sub-step (step rs, sub-step rkk, into set X ^ 1) go after the first four
+  // MFMAs: A blocks 0 and 1, then A block 2, then B block 0, then A block 3
+  // and B block 1 (the last two then have four MFMAs to pass). kDma = 1: the
   // far operand's step s + 2, after the fourth MFMA (its slot, that of step
   // s - 1, was released at the previous barrier); kDma = 2: the near
   // operand's step s + 2, after the second MFMA (into the slot step s
@@ -172,10 +173,13 @@ __device__ __forceinline__ void run_tiles8(uint4* smem, const Lanes8& L, int row
       const int bm = q >> 1, bn = q & 1;
       Mma<kDtype>::step(acc[bm][bn], FA[x][bm], FB[x][bn]);
       if constexpr (decltype(read)::value) {
-        if (q < 3) {
-          FA[x ^ 1][2 * q] = sa[a_off[rkk] + 2 * q * 32 * kRowChunks];
-          if (q < 2) FA[x ^ 1][2 * q + 1] = sa[a_off[rkk] + (2 * q + 1) * 32 * kRowChunks];
-          else FB[x ^ 1][0] = sb[b_off[rkk]];
+        if (q == 0) {
+          FA[x ^ 1][0] = sa[a_off[rkk]];
+          FA[x ^ 1][1] = sa[a_off[rkk] + 32 * kRowChunks];
+        } else if (q == 1) {
+          FA[x ^ 1][2] = sa[a_off[rkk] + 2 * 32 * kRowChunks];
+        } else if (q == 2) {
+          FB[x ^ 1][0] = sb[b_off[rkk]];
         } else if (q == 3) {
           FA[x ^ 1][3] = sa[a_off[rkk] + 3 * 32 * kRowChunks];
           FB[x ^ 1][1] = sb[b_off[rkk] + 32 * kRowChunks];
