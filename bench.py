@@ -671,6 +671,52 @@ def cpu_baseline(wl, n_sample=6144):
     }
 
 
+def cpu_baseline_fwd_bwd(s, wl, n_sample=192):
+    """The float64 oracle's forward + loss + backward timed on a seeded sample
+    of the backward workload's tokens: their logprobs over the full
+    vocabulary, the loss over the responses they fall in (with the sample's
+    own response structure), and dH / dW of that loss (every vocabulary
+    row), on the host's cores."""
+    import numpy as np
+    import torch
+    import oracle
+    from synth import token_subset
+
+    lay = s["lay"]
+    idx = token_subset(lay.n_tok, n_sample, seed=200 + wl.index)
+    it = torch.from_numpy(idx).to(s["H"].device)
+    Hs = s["H"].index_select(0, it).cpu().view(torch.int16).numpy().view(np.uint16)
+    Wh = s["W"].cpu().view(torch.int16).numpy().view(np.uint16)
+    ys = s["y"].index_select(0, it).cpu().numpy()
+    resp_of = np.searchsorted(lay.resp_offsets, idx, side="right") - 1
+    resp_ids, counts = np.unique(resp_of, return_counts=True)
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    noise = lay.lag_noise[idx].astype(np.float64)
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max((i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas"), default=None)
+    except Exception:
+        pass
+    t0 = time.perf_counter()
+    lp, _ = oracle.lmhead_logprob(Hs, Wh, ys)
+    A = oracle.group_advantage(lay.rewards, lay.group_offsets)[resp_ids]
+    _, _, coef = oracle.reinforce_zero_loss(lp, lp + noise, A, off)
+    oracle.reinforce_zero_backward(Hs, Wh, ys, coef)
+    el = time.perf_counter() - t0
+    return {
+        "value": n_sample / el,
+        "unit": "sampled tokens/s (forward + backward)",
+        "cores": threads if threads else len(os.sched_getaffinity(0)),
+        "kind": "oracle",
+        "sample": (f"{n_sample} seeded tokens of the {wl.key} workload (d={wl.d}, vocab={wl.vocab}): float64 "
+                   f"logprobs over the full vocabulary, the loss over the {resp_ids.size} responses they fall in, "
+                   f"and dH, dW of that loss (dW over every vocabulary row); {el:.1f} s"),
+        "seconds": el,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -827,6 +873,12 @@ def main():
             })
         else:
             log(f"[bench] kept-logits step skipped: {z_bytes / 2**30:.0f} GiB of logits, {free / 2**30:.0f} GiB free")
+        sb.pop("Z", None)
+        if not args.no_cpu_baseline:
+            log("[bench] timing the oracle's forward + backward on a bounded sample ...")
+            out["fwd_bwd"]["cpu_baseline"] = cpu_baseline_fwd_bwd(sb, wb)
+            log(f"[bench] oracle fwd+bwd {out['fwd_bwd']['cpu_baseline']['value']:.1f} tokens/s in "
+                f"{out['fwd_bwd']['cpu_baseline']['seconds']:.1f}s")
         del sb
         torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
