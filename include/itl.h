@@ -102,7 +102,8 @@ size_t itl_lmhead_logprob_workspace_bytes(int64_t n_tok, int64_t vocab);
  *   z[t, v]  = sum_k H[t, k] * W[v, k]           (fp32 accumulate, ascending k)
  *   lse[t]   = log sum_v exp(z[t, v])
  *   logprob[t] = z[t, tokens[t]] - lse[t]
- * H [n_tok, d], W [vocab, d] of `dtype`; tokens int32 [n_tok] with
+ * H [n_tok, d], W [vocab, d] of `dtype`, both 16-byte aligned
+ * (ITL_ERR_INVALID_ARG otherwise); tokens int32 [n_tok] with
  * 0 <= tokens[t] < vocab. Outputs fp32: logprob [n_tok]; lse [n_tok] may be
  * NULL. workspace: >= itl_lmhead_logprob_workspace_bytes(n_tok, vocab)
  * bytes, 256-byte aligned; its contents on entry do not matter.

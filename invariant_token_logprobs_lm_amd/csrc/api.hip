@@ -53,6 +53,11 @@ itl_status check_head(itl_dtype dtype, int64_t n_tok, int64_t d, int64_t vocab) 
 
 bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255) != 0; }
 
+// The head kernels move H and W rows in 16-byte pieces per lane.
+bool misaligned16(const void* a, const void* b) {
+  return ((reinterpret_cast<uintptr_t>(a) | reinterpret_cast<uintptr_t>(b)) & 15) != 0;
+}
+
 // Scratch of itl_lmhead_logprob_noalloc: a file-scope device array, one
 // copy per GPU, held until the process ends. Host code never uses its name
 // as an address: the device address comes from hipGetSymbolAddress, once per
@@ -113,6 +118,7 @@ itl_status itl_lmhead_logprob(const void* H, const void* W, itl_dtype dtype, int
   if (st != ITL_OK) return st;
   if (n_tok == 0) return ITL_OK;
   if (!H || !W || !tokens || !logprob) return fail(ITL_ERR_INVALID_ARG, "null H, W, tokens or logprob");
+  if (misaligned16(H, W)) return fail(ITL_ERR_INVALID_ARG, "H and W must be 16-byte aligned");
   if (!workspace || workspace_bytes < itl::lmhead_workspace_bytes(n_tok, vocab))
     return fail(ITL_ERR_WORKSPACE, "workspace missing or smaller than itl_lmhead_logprob_workspace_bytes()");
   if (misaligned(workspace)) return fail(ITL_ERR_WORKSPACE, "workspace must be 256-byte aligned");
@@ -128,6 +134,7 @@ itl_status itl_lmhead_logprob_noalloc(const void* H, const void* W, itl_dtype dt
   if (st != ITL_OK) return st;
   if (n_tok == 0) return ITL_OK;
   if (!H || !W || !tokens || !logprob) return fail(ITL_ERR_INVALID_ARG, "null H, W, tokens or logprob");
+  if (misaligned16(H, W)) return fail(ITL_ERR_INVALID_ARG, "H and W must be 16-byte aligned");
   if (itl::lmhead_workspace_bytes(n_tok, vocab) > kNoAllocScratchBytes)
     return fail(ITL_ERR_UNSUPPORTED,
                 "n_tok too large for itl_lmhead_logprob_noalloc's 64 MiB scratch (at most 16,368 tokens for "
@@ -166,6 +173,7 @@ itl_status itl_lmhead_logprob_keep_logits(const void* H, const void* W, itl_dtyp
   if (st != ITL_OK) return st;
   if (n_tok == 0) return ITL_OK;
   if (!H || !W || !tokens || !logprob) return fail(ITL_ERR_INVALID_ARG, "null H, W, tokens or logprob");
+  if (misaligned16(H, W)) return fail(ITL_ERR_INVALID_ARG, "H and W must be 16-byte aligned");
   st = check_logits(logits, ld_logits, n_tok, vocab);
   if (st != ITL_OK) return st;
   if (!workspace || workspace_bytes < itl::lmhead_workspace_bytes(n_tok, vocab))

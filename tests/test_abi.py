@@ -56,7 +56,7 @@ def test_build_info_and_status_strings(lib):
         assert lib.itl_status_string(s)
 
 
-def _lmhead(lib, H=1, W=1, dtype=0, n=4, d=64, V=10, y=1, lp=1, ws=256, wsb=1 << 20):
+def _lmhead(lib, H=256, W=256, dtype=0, n=4, d=64, V=10, y=1, lp=1, ws=256, wsb=1 << 20):
     v = ctypes.c_void_p
     return lib.itl_lmhead_logprob(v(H), v(W), dtype, n, d, V, v(y), v(lp), None, v(ws), wsb, None)
 
@@ -69,6 +69,9 @@ def test_lmhead_argument_validation(lib):
     assert _lmhead(lib, dtype=7) == UNSUPPORTED
     assert _lmhead(lib, H=0) == INVALID
     assert _lmhead(lib, y=0) == INVALID
+    assert _lmhead(lib, H=264) == INVALID  # H and W 16-byte aligned
+    assert _lmhead(lib, W=258) == INVALID
+    assert "16-byte" in lib.itl_last_error().decode()
     assert _lmhead(lib, ws=0) == WORKSPACE
     assert _lmhead(lib, wsb=16) == WORKSPACE
     assert _lmhead(lib, ws=255) == WORKSPACE
@@ -85,8 +88,9 @@ def test_noalloc_argument_validation(lib):
     assert f(v(1), v(1), 0, 4, 96, 10, v(1), v(1), None, None) == UNSUPPORTED
     assert f(None, v(1), 0, 4, 64, 10, v(1), v(1), None, None) == INVALID
     assert f(None, None, 0, 0, 64, 10, None, None, None, None) == OK
+    assert f(v(8), v(256), 0, 4, 64, 10, v(1), v(1), None, None) == INVALID  # H, W 16-byte aligned
     # the static scratch holds 64 MiB: 16,368 tokens at 256 slices
-    assert f(v(1), v(1), 0, 16369, 64, 151936, v(1), v(1), None, None) == UNSUPPORTED
+    assert f(v(256), v(256), 0, 16369, 64, 151936, v(1), v(1), None, None) == UNSUPPORTED
     assert "scratch" in lib.itl_last_error().decode()
     assert lib.itl_lmhead_logprob_workspace_bytes(16368, 151936) == 64 << 20
 
@@ -159,6 +163,8 @@ def test_kept_logits_argument_validation(lib):
     assert keep(ld=8) == INVALID          # below vocab
     assert keep(ld=14) == INVALID         # not a multiple of 4
     assert keep(Z=264) == INVALID         # not 16-byte aligned
+    assert lib.itl_lmhead_logprob_keep_logits(v(256), v(260), 0, 4, 64, 10, v(256), v(256), None, v(256), 12,
+                                              v(256), 1 << 20, None) == INVALID  # W not 16-byte aligned
     assert keep(ld=1 << 24) == UNSUPPORTED
     assert "ld_logits" in lib.itl_last_error().decode()
     assert keep(n=0, Z=0) == OK           # empty call is a no-op
