@@ -589,38 +589,49 @@ def fp8_leg(s, device, steps=5):
     }
 
 
-def sustained_mfma_probe(device, blocks=1024, iters=40000):
-    """TFLOP/s that v_mfma_f32_32x32x16_bf16 sustains on this chip with
-    operands that change every instruction (random normal bf16 values, a
-    4 x 4 block tile per wavefront, one wavefront per SIMD) and no memory
-    traffic: the power-limited ceiling a real contraction meets, measured
-    with the probe library (bench_mfma_probe.hip) built beside this file."""
+PROBE_SHAPES = {
+    0: "v_mfma_f32_32x32x16_bf16, 4x4 block tile per wavefront, one wavefront per SIMD",
+    1: "v_mfma_f32_16x16x32_bf16, 8x4 block tile per wavefront, two wavefronts per SIMD "
+       "(the bf16 forward's instruction and wavefront tile)",
+}
+
+
+def sustained_mfma_probe(device, shape, blocks=1024, iters=40000):
+    """TFLOP/s that a bf16 MFMA shape (PROBE_SHAPES) sustains on this chip
+    with operands that change every instruction (random normal bf16 values)
+    and no memory traffic: the power-limited ceiling a real contraction
+    meets, measured with the probe library (bench_mfma_probe.hip) built
+    beside this file."""
     import ctypes
     import torch
 
     path = os.path.join(ROOT, "libitl_bench_probe.so")
     lib = ctypes.CDLL(path)
     lib.itl_probe_operand_bytes.restype = ctypes.c_size_t
+    lib.itl_probe_threads.restype = ctypes.c_int
+    lib.itl_probe_threads.argtypes = [ctypes.c_int]
     lib.itl_probe_flops.restype = ctypes.c_double
-    lib.itl_probe_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.itl_probe_flops.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
     lib.itl_probe_mfma_bf16.restype = ctypes.c_int
-    lib.itl_probe_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.itl_probe_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_void_p]
     g = torch.Generator(device="cpu").manual_seed(5150)
     n = lib.itl_probe_operand_bytes() // 2
     ops = torch.randn(n, generator=g).to(torch.bfloat16).to(device)
-    out = torch.empty(blocks * 256, dtype=torch.float32, device=device)
+    out = torch.empty(blocks * lib.itl_probe_threads(shape), dtype=torch.float32, device=device)
     st = ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
-    assert lib.itl_probe_mfma_bf16(ctypes.c_void_p(ops.data_ptr()), ctypes.c_void_p(out.data_ptr()), blocks, 100, st) == 0
+    opp, outp = ctypes.c_void_p(ops.data_ptr()), ctypes.c_void_p(out.data_ptr())
+    assert lib.itl_probe_mfma_bf16(shape, opp, outp, blocks, 100, st) == 0
     torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
-    assert lib.itl_probe_mfma_bf16(ctypes.c_void_p(ops.data_ptr()), ctypes.c_void_p(out.data_ptr()), blocks, iters, st) == 0
+    assert lib.itl_probe_mfma_bf16(shape, opp, outp, blocks, iters, st) == 0
     b.record()
     torch.cuda.synchronize()
     ms = a.elapsed_time(b)
-    tf = lib.itl_probe_flops(blocks, iters) / (ms * 1e-3) / 1e12
-    log(f"[bench] matrix-core probe (random bf16 operands, no memory traffic): {tf:.1f} TFLOP/s "
-        f"({100 * tf / PEAK_BF16_TFLOPS:.1f}% of the published peak) in {ms:.1f} ms")
+    tf = lib.itl_probe_flops(shape, blocks, iters) / (ms * 1e-3) / 1e12
+    log(f"[bench] matrix-core probe ({PROBE_SHAPES[shape]}; random bf16 operands, no memory traffic): "
+        f"{tf:.1f} TFLOP/s ({100 * tf / PEAK_BF16_TFLOPS:.1f}% of the published peak) in {ms:.1f} ms")
     return tf
 
 
@@ -761,7 +772,8 @@ def main():
     log(f"[bench] step {ms_step:.3f} ms, lmhead {ms_head:.3f} ms -> {achieved:.1f} TFLOP/s "
         f"({100 * achieved / PEAK_BF16_TFLOPS:.1f}% of bf16 peak), wall {wall:.2f}s")
     traffic = measured_traffic(wl.key)
-    sustained = sustained_mfma_probe(device)
+    sustained = sustained_mfma_probe(device, 1)
+    sustained32 = sustained_mfma_probe(device, 0)
     out = {
         "metric": METRIC,
         "value": n_tok / (ms_step * 1e-3),
@@ -796,9 +808,10 @@ def main():
             "sustained_mfma_probe": {
                 "value": sustained,
                 "unit": "TFLOP/s",
-                "what": "v_mfma_f32_32x32x16_bf16 with random bf16 operands changing every instruction, "
-                        "4x4 block tile per wavefront, no memory traffic (power-limited clock)",
+                "what": PROBE_SHAPES[1] + "; random bf16 operands changing every instruction, no memory traffic "
+                        "(power-limited clock)",
                 "frac_of_probe": achieved / sustained,
+                "other_shape": {"what": PROBE_SHAPES[0], "value": sustained32},
             },
         },
     }

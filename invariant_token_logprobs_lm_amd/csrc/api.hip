@@ -421,7 +421,7 @@ const char* itl_build_info(void) {
     snprintf(buf, sizeof buf,
              "itl 0.3 arch=gfx950 threads=%d wide_threads=%d token_block=%d vocab_tile=%d k_step_bytes=%d w_slots=%d h_slots=%d "
              "swap_slots_over_k_steps=%d max_slices=%d slices=balanced narrow_max_tokens=%d narrow_token_block=%d "
-             "mfma_bf16=32x32x16 mfma_f32=32x32x2 fp8=e4m3_row_scaled mfma_fp8=32x32x64 mxfp4=e2m1_e8m0_32 "
+             "mfma_bf16=16x16x32 mfma_f32=16x16x4 fp8=e4m3_row_scaled mfma_fp8=32x32x64 mxfp4=e2m1_e8m0_32 "
              "bwd_chunk_tokens=%d loss_segment_tokens=%d loss_lane_segment=%d loss_wave_segment=%d loss_threads=%d "
              "loss_mean_chunk=%d loss_sums=f64 bwd_sampled_sort=stable_counting bwd_sampled_segment=%d "
              "bwd_sampled_group=%d",

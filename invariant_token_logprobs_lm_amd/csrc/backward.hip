@@ -102,7 +102,8 @@ __device__ __forceinline__ void band_order(int b, int n_fast, int n_slow, int& f
 // 1. dlogits. A = W tiles (vocabulary), B = the chunk's H block (tokens); as
 // in the forward, on the eight-wavefront engine. Grid: token blocks (fast) x
 // vocabulary slices (slow). Lane l of wavefront (wv, tq) holds vocabulary
-// rows 128 wv + ... of each tile at tokens t0 + 64 tq + 32 bn + (l mod 32).
+// rows 128 wv + 16 bm + 4 (l / 16) .. + 3 of each tile at tokens t0 + 64 tq +
+// 16 bn + (l mod 16).
 template <int kDtype, bool kBFar>
 __global__ __launch_bounds__(kThreads8, 1) void dlogits_kernel(
     const char* __restrict__ Hc, int len, const char* __restrict__ W, int row_bytes, int vocab, int vpad,
@@ -117,10 +118,10 @@ __global__ __launch_bounds__(kThreads8, 1) void dlogits_kernel(
   const int n_vt = vpad / kBV;
   const int tile_begin = slice_tile(grp * group, n_vt, n_slices);
   const int tile_end = slice_tile(min(grp * group + group, n_slices), n_vt, n_slices);
-  float l2e_lse[2], negc[2];
+  float l2e_lse[4], negc[4];
 #pragma unroll
-  for (int bn = 0; bn < 2; ++bn) {
-    const int t = t0 + L.tq * 64 + bn * 32 + L.col;
+  for (int bn = 0; bn < 4; ++bn) {
+    const int t = t0 + L.tq * 64 + bn * 16 + L.c16;
     const bool ok = t < len;
     l2e_lse[bn] = ok ? lse[t] * kLog2e : 0.0f;
     negc[bn] = ok ? -coef[t] : 0.0f;  // padding tokens get g = 0
@@ -130,34 +131,31 @@ __global__ __launch_bounds__(kThreads8, 1) void dlogits_kernel(
     return rsrc_words(W + (size_t)v0 * row_bytes, (uint32_t)max(0, min(kBV, vocab - v0)) * row_bytes);
   };
   const int4v hr = rsrc_words(Hc + (size_t)t0 * row_bytes, (uint32_t)min(kBT, len - t0) * row_bytes);
-  auto epilogue = [&](int tile, floatx16 (&acc)[4][2]) {
-    const int vw = tile * kBV + L.wv * 128 + 4 * L.half;
+  auto epilogue = [&](int tile, floatx4 (&acc)[8][4]) {
+    const int vw = tile * kBV + L.wv * 128 + 4 * L.quad;
 #pragma unroll
-    for (int bn = 0; bn < 2; ++bn) {
-      const int t = t0 + L.tq * 64 + bn * 32 + L.col;  // < chunk's padded length
+    for (int bn = 0; bn < 4; ++bn) {
+      const int t = t0 + L.tq * 64 + bn * 16 + L.c16;  // < chunk's padded length
 #pragma unroll
-      for (int bm = 0; bm < 4; ++bm) {
+      for (int bm = 0; bm < 8; ++bm) {
+        const int v = vw + bm * 16;  // rows v .. v + 3
+        typename E::T g[4];
 #pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const int v = vw + bm * 32 + 8 * i4;  // rows v .. v + 3
-          typename E::T g[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float z = acc[bm][bn][4 * i4 + r];
-            const float p = fast_exp2(z * kLog2e - l2e_lse[bn]);
-            g[r] = E::from_f(v + r < vocab ? negc[bn] * p : 0.0f);
-            GdT[(size_t)(v + r) * kBwdChunk + t] = g[r];
-          }
-          if constexpr (kDtype == 0) {
-            uint2 pk;
-            pk.x = (uint32_t)g[0] | ((uint32_t)g[1] << 16);
-            pk.y = (uint32_t)g[2] | ((uint32_t)g[3] << 16);
-            *reinterpret_cast<uint2*>(Gd + (size_t)t * vpad + v) = pk;
-          } else {
-            *reinterpret_cast<float4*>(Gd + (size_t)t * vpad + v) = make_float4(g[0], g[1], g[2], g[3]);
-          }
+        for (int r = 0; r < 4; ++r) {
+          const float z = acc[bm][bn][r];
+          const float p = fast_exp2(z * kLog2e - l2e_lse[bn]);
+          g[r] = E::from_f(v + r < vocab ? negc[bn] * p : 0.0f);
+          GdT[(size_t)(v + r) * kBwdChunk + t] = g[r];
         }
-        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (kDtype == 0) {
+          uint2 pk;
+          pk.x = (uint32_t)g[0] | ((uint32_t)g[1] << 16);
+          pk.y = (uint32_t)g[2] | ((uint32_t)g[3] << 16);
+          *reinterpret_cast<uint2*>(Gd + (size_t)t * vpad + v) = pk;
+        } else {
+          *reinterpret_cast<float4*>(Gd + (size_t)t * vpad + v) = make_float4(g[0], g[1], g[2], g[3]);
+        }
+        if ((bm & 3) == 3) __builtin_amdgcn_sched_barrier(0);
       }
     }
   };
@@ -246,8 +244,8 @@ __global__ __launch_bounds__(256) void dlogits_from_logits_kernel(
 
 // 2. dH for the chunk. A = W^T tile (d rows, K = Vpad), B = Gd token block,
 // on the eight-wavefront engine. Grid: token blocks (fast) x d tiles (slow).
-// Lane l of wavefront (wv, tq) holds d rows 128 wv + ... of the tile for
-// tokens t0 + 64 tq + 32 bn + (l mod 32).
+// Lane l of wavefront (wv, tq) holds d rows 128 wv + 16 bm + 4 (l / 16) ..
+// + 3 of the tile for tokens t0 + 64 tq + 16 bn + (l mod 16).
 template <int kDtype, bool kBFar>
 __global__ __launch_bounds__(kThreads8, 1) void dh_kernel(const char* __restrict__ WT, const char* __restrict__ Gd,
                                                          int vpad, int d, int vocab, int len, int n_tb, int n_dt,
@@ -266,37 +264,38 @@ __global__ __launch_bounds__(kThreads8, 1) void dh_kernel(const char* __restrict
     return rsrc_words(WT + (size_t)k0 * row_bytes, (uint32_t)min(kBV, d - k0) * row_bytes);
   };
   const int4v br = rsrc_words(Gd + (size_t)t0 * row_bytes, (uint32_t)min(kBT, len - t0) * row_bytes);
-  auto epilogue = [&](int tile, floatx16 (&acc)[4][2]) {
-    const int kw = tile * kBV + L.wv * 128 + 4 * L.half;
+  auto epilogue = [&](int tile, floatx4 (&acc)[8][4]) {
+    const int kw = tile * kBV + L.wv * 128 + 4 * L.quad;
 #pragma unroll
-    for (int bn = 0; bn < 2; ++bn) {
-      const int t = t0 + L.tq * 64 + bn * 32 + L.col;
+    for (int bn = 0; bn < 4; ++bn) {
+      const int t = t0 + L.tq * 64 + bn * 16 + L.c16;
       const bool ok = t < len;
       const int yr = ok ? y[t] : 0;
       const bool yok = (unsigned)yr < (unsigned)vocab;  // an invalid id contributes no sampled term
       const float c = ok && yok ? coef[t] : 0.0f;
       const int yt = yok ? yr : 0;
 #pragma unroll
-      for (int bm = 0; bm < 4; ++bm) {
-        // The block's 4 groups of 4 W[y] values, loaded together.
+      for (int bh = 0; bh < 2; ++bh) {
+        // Four blocks' groups of 4 W[y] values, loaded together.
         float wyv[4][4];
 #pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const int k = kw + bm * 32 + 8 * i4;  // d rows k .. k + 3 (d is a multiple of 64)
+        for (int j = 0; j < 4; ++j) {
+          const int k = kw + (4 * bh + j) * 16;  // d rows k .. k + 3 (d is a multiple of 64)
           const typename E::T* wy = W + (size_t)yt * d + (k < d ? k : 0);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) wyv[i4][r] = E::to_f(wy[r]);
+          for (int r = 0; r < 4; ++r) wyv[j][r] = E::to_f(wy[r]);
         }
 #pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const int k = kw + bm * 32 + 8 * i4;
+        for (int j = 0; j < 4; ++j) {
+          const int bm = 4 * bh + j;
+          const int k = kw + bm * 16;
           if (ok && k < d) {
-            const floatx16& o = acc[bm][bn];
+            const floatx4& o = acc[bm][bn];
             float4 out;
-            out.x = o[4 * i4 + 0] + c * wyv[i4][0];
-            out.y = o[4 * i4 + 1] + c * wyv[i4][1];
-            out.z = o[4 * i4 + 2] + c * wyv[i4][2];
-            out.w = o[4 * i4 + 3] + c * wyv[i4][3];
+            out.x = o[0] + c * wyv[j][0];
+            out.y = o[1] + c * wyv[j][1];
+            out.z = o[2] + c * wyv[j][2];
+            out.w = o[3] + c * wyv[j][3];
             *reinterpret_cast<float4*>(dH + (size_t)t * d + k) = out;
           }
         }
@@ -310,7 +309,8 @@ __global__ __launch_bounds__(kThreads8, 1) void dh_kernel(const char* __restrict
 // 3. dW += the chunk's part. A = GdT vocabulary tile (K = chunk tokens), B =
 // H^T d block, on the eight-wavefront engine. Grid: vocabulary tiles (fast)
 // x d tiles (slow). Lane l of wavefront (wv, tq) holds vocabulary rows
-// 128 wv + ... of the tile at d column k0 + 64 tq + 32 bn + (l mod 32).
+// 128 wv + 16 bm + 4 (l / 16) .. + 3 of the tile at d column k0 + 64 tq +
+// 16 bn + (l mod 16).
 template <int kDtype, bool kBFar>
 __global__ __launch_bounds__(kThreads8, 1) void dw_kernel(const char* __restrict__ GdT, const char* __restrict__ HT,
                                                          int kpad, int vocab, int d, int n_vt, int n_dt,
@@ -327,26 +327,30 @@ __global__ __launch_bounds__(kThreads8, 1) void dw_kernel(const char* __restrict
     return rsrc_words(GdT + (size_t)v0 * row_bytes, (uint32_t)kBV * row_bytes);
   };
   const int4v br = rsrc_words(HT + (size_t)k0 * row_bytes, (uint32_t)min(kBT, d - k0) * row_bytes);
-  auto epilogue = [&](int tile, floatx16 (&acc)[4][2]) {
-    const int vw = tile * kBV + L.wv * 128 + 4 * L.half;
+  auto epilogue = [&](int tile, floatx4 (&acc)[8][4]) {
+    const int vw = tile * kBV + L.wv * 128 + 4 * L.quad;
 #pragma unroll
-    for (int bn = 0; bn < 2; ++bn) {
-      const int k = k0 + L.tq * 64 + bn * 32 + L.col;
+    for (int bn = 0; bn < 4; ++bn) {
+      const int k = k0 + L.tq * 64 + bn * 16 + L.c16;
 #pragma unroll
-      for (int bm = 0; bm < 4; ++bm) {
-        // The block's 16 dW values of this lane's column k, read together,
+      for (int bh = 0; bh < 2; ++bh) {
+        // Four blocks' 16 dW values of this lane's column k, read together,
         // then updated and written back.
-        float old[16];
+        float old[4][4];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int v = vw + bm * 32 + 8 * (i >> 2) + (i & 3);
-          old[i] = v < vocab && k < d ? dW[(size_t)v * d + k] : 0.0f;
-        }
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int v = vw + bm * 32 + 8 * (i >> 2) + (i & 3);
-          if (v < vocab && k < d) dW[(size_t)v * d + k] = old[i] + acc[bm][bn][i];
-        }
+          for (int r = 0; r < 4; ++r) {
+            const int v = vw + (4 * bh + j) * 16 + r;
+            old[j][r] = v < vocab && k < d ? dW[(size_t)v * d + k] : 0.0f;
+          }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int v = vw + (4 * bh + j) * 16 + r;
+            if (v < vocab && k < d) dW[(size_t)v * d + k] = old[j][r] + acc[4 * bh + j][bn][r];
+          }
         __builtin_amdgcn_sched_barrier(0);
       }
     }

@@ -17,8 +17,9 @@
 // vocabulary is cut into S = min(tiles, 256) balanced slices, a function of V
 // alone. A workgroup owns one token block and a run of consecutive slices
 // and walks their tiles in ascending order; after each tile its lanes fold
-// the tile into a running (max, sum of exp) per token (fold_column) and pick
-// out z[t, y_t] if y_t falls in the tile. The logits never leave registers. At each slice end the two lane halves that share a token
+// the tile into a running (max, sum of exp) per token (fold_column16) and
+// pick out z[t, y_t] if y_t falls in the tile. The logits never leave
+// registers. At each slice end the four lane quarters that share a token
 // are merged and each wavefront writes one (max, sumexp) pair per token, then
 // starts the next slice afresh, so the 2 S partials of a token are the same
 // whether a workgroup walks one slice (small batches: every CU streams W) or
@@ -35,10 +36,11 @@
 // in the block, and rows beyond n_tok are loaded as zeros and never written.
 // There is no split-K and no atomic.
 //
-// MFMA layouts used (v_mfma_f32_32x32x16_bf16, and v_mfma_f32_32x32x2f32 for
-// fp32 heads): lane l supplies row (l mod 32) of A and column (l mod 32) of
-// B, with the k range chosen by l / 32; accumulator register i of lane l
-// holds row 8*(i/4) + 4*(l/32) + (i mod 4), column (l mod 32).
+// MFMA layouts used (16 x 16 blocks: v_mfma_f32_16x16x32_bf16, and
+// v_mfma_f32_16x16x4f32 for fp32 heads): lane l supplies row (l mod 16) of
+// an A block and column (l mod 16) of a B block, with the k range chosen by
+// l / 16; accumulator register i of lane l holds row 4*(l/16) + i, column
+// (l mod 16).
 
 #include "itl_launch.h"
 #include "lse_fold.h"
@@ -52,11 +54,11 @@ namespace {
 // Kept logits are written with buffer stores against a range that ends at
 // the wavefront's last valid token row, so rows past n_tok are dropped by
 // the hardware instead of a branch. LogitRows: the range (SGPRs) and this
-// lane's row offset in bytes, (col * ld + 4 half) * 4 (ld * 4 * 128 < 2^32).
+// lane's row offset in bytes, (c16 * ld + 4 quad) * 4 (ld * 4 * 128 < 2^32).
 struct LogitRows {
   __amdgpu_buffer_rsrc_t rsrc;
   uint32_t voff;
-  uint32_t bn_stride;  // bytes between the token columns of blocks bn and bn + 1 (32 rows)
+  uint32_t bn_stride;  // bytes between the token columns of blocks bn and bn + 1 (16 rows)
 };
 
 // Built in each epilogue, not once per kernel: kept live across the K loop,
@@ -64,7 +66,7 @@ struct LogitRows {
 // makes the inputs opaque, so the compiler cannot hoist the build out of
 // the tile loop.
 __device__ __forceinline__ LogitRows logit_rows(float* logits, long long ld, int tok_first, int n_rows, int n_tok,
-                                                int col, int half) {
+                                                int c16, int quad) {
   asm volatile("" : "+s"(tok_first));
   LogitRows r;
   const int valid = max(0, min(n_rows, n_tok - tok_first));
@@ -78,51 +80,42 @@ __device__ __forceinline__ LogitRows logit_rows(float* logits, long long ld, int
   const int nbytes = __builtin_amdgcn_readfirstlane((int)((uint32_t)valid * (uint32_t)ld * 4u));
   r.rsrc = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(((uint64_t)hi << 32) | lo), 0, nbytes,
                                              0x00020000);
-  r.voff = ((uint32_t)col * (uint32_t)ld + 4u * (uint32_t)half) * 4u;
-  r.bn_stride = __builtin_amdgcn_readfirstlane(32u * (uint32_t)ld * 4u);
+  r.voff = ((uint32_t)c16 * (uint32_t)ld + 4u * (uint32_t)quad) * 4u;
+  r.bn_stride = __builtin_amdgcn_readfirstlane(16u * (uint32_t)ld * 4u);
   return r;
 }
 
-// Write this lane's 16 logits of a 32 x 32 block: token column bn of the
-// rows, vocabulary rows v0 + 4 half + 8 i + r (r < 4) from register 4 i + r
-// (v0 = the block's first row, the same for the whole wavefront). Four
-// consecutive rows are 16 contiguous bytes of the token's row. In the
-// vocabulary's last tile, rows at or past the vocabulary are not written.
-template <int I, class kPartial>
-__device__ __forceinline__ void store_quad(const LogitRows& rows, uint32_t voff, int v0, int half, int vocab,
-                                           const floatx16& z, kPartial) {
-  const uint32_t so = (uint32_t)(v0 + 8 * I) * 4u;
+// Write this lane's 4 logits of a 16 x 16 block: token column bn of the
+// rows, vocabulary rows v0 + 4 quad + r (r < 4) from register r (v0 = the
+// block's first row, the same for the whole wavefront): 16 contiguous bytes
+// of the token's row. In the vocabulary's last tile, rows at or past the
+// vocabulary are not written.
+template <class kPartial>
+__device__ __forceinline__ void store_logits(const LogitRows& rows, int bn, int v0, int quad, int vocab,
+                                             const floatx4& z, kPartial) {
+  const uint32_t voff = rows.voff + (uint32_t)bn * rows.bn_stride;
+  const uint32_t so = (uint32_t)v0 * 4u;
   if constexpr (!kPartial::value) {
-    __builtin_amdgcn_raw_buffer_store_b128(
-        __builtin_bit_cast(int4v, __builtin_shufflevector(z, z, 4 * I, 4 * I + 1, 4 * I + 2, 4 * I + 3)), rows.rsrc,
-        voff, so, kLogitStorePolicy);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(int4v, z), rows.rsrc, voff, so, kLogitStorePolicy);
   } else {
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      if (v0 + 8 * I + 4 * half + r < vocab)
-        __builtin_amdgcn_raw_buffer_store_b32((int)__float_as_uint(z[4 * I + r]), rows.rsrc, voff + 4u * r, so,
+      if (v0 + 4 * quad + r < vocab)
+        __builtin_amdgcn_raw_buffer_store_b32((int)__float_as_uint(z[r]), rows.rsrc, voff + 4u * r, so,
                                               kLogitStorePolicy);
   }
-}
-
-template <class kPartial>
-__device__ __forceinline__ void store_logits(const LogitRows& rows, int bn, int v0, int half, int vocab,
-                                             const floatx16& z, kPartial partial) {
-  const uint32_t voff = rows.voff + (uint32_t)bn * rows.bn_stride;
-  store_quad<0>(rows, voff, v0, half, vocab, z, partial);
-  store_quad<1>(rows, voff, v0, half, vocab, z, partial);
-  store_quad<2>(rows, voff, v0, half, vocab, z, partial);
-  store_quad<3>(rows, voff, v0, half, vocab, z, partial);
 }
 
 // Kernel 1 for calls of more than 64 tokens, on the eight-wavefront engine
 // (run_tiles8): a 512-thread workgroup per (256-token block, slice group).
 // Wavefront (wv, tq) holds W rows 128 wv .. + 127 of each tile against
-// tokens t0 + 64 tq .. + 63; after each tile each token column's four blocks
-// are folded in one step (fold_column), tiles in order, and at the slice's
-// end the two lane halves are merged, as in the narrow kernel, so a token's
-// partials have the same bits in both. With kKeep the tile's logits are
-// stored first (four 16-byte stores per block).
+// tokens t0 + 64 tq .. + 63; lane l holds tokens t0 + 64 tq + 16 bn +
+// (l mod 16) (bn < 4), 32 of the wavefront's 128 rows each. After each tile
+// each token column's 32 logits are folded in one step (fold_column16),
+// tiles in order, and at the slice's end the four lane quarters are merged,
+// as in the narrow kernel, so a token's partials have the same bits in
+// both. With kKeep the tile's logits are stored first (one 16-byte store per
+// block).
 template <int kDtype, bool kKeep, bool kBFar>
 __global__ __launch_bounds__(kThreads8, 1) void lmhead_lse_partial8_kernel(
     const char* __restrict__ H, const char* __restrict__ W, const int32_t* __restrict__ tokens, int n_tok,
@@ -130,7 +123,7 @@ __global__ __launch_bounds__(kThreads8, 1) void lmhead_lse_partial8_kernel(
     float* __restrict__ zy_out, float* __restrict__ logits, long long ld) {
   __shared__ uint4 smem[kEngineSmemChunks];
   const Lanes8 L = lanes8();
-  const int wv = L.wv, tq = L.tq, half = L.half, col = L.col;
+  const int wv = L.wv, tq = L.tq, quad = L.quad, c16 = L.c16;
 
   const int S = n_slices;
   const WideWork work = wide_work(blockIdx.x, n_tb, S, group);
@@ -140,11 +133,11 @@ __global__ __launch_bounds__(kThreads8, 1) void lmhead_lse_partial8_kernel(
   const int tile_end = slice_tile(work.slice_end, n_vt, S);
   const int nks = row_bytes / kStepBytes;
 
-  Col c[2];
+  Col16 c[4];
 #pragma unroll
-  for (int bn = 0; bn < 2; ++bn) {
-    const int tok = t0 + tq * 64 + bn * 32 + col;
-    c[bn] = Col{tok < n_tok ? tokens[tok] : -1, -INFINITY, 0.0f, 0.0f, false};
+  for (int bn = 0; bn < 4; ++bn) {
+    const int tok = t0 + tq * 64 + bn * 16 + c16;
+    c[bn] = Col16{tok < n_tok ? tokens[tok] : -1, -INFINITY, 0.0f};
   }
   auto w_rsrc = [&](int tile) {
     const int v0 = tile * kBV;
@@ -154,49 +147,64 @@ __global__ __launch_bounds__(kThreads8, 1) void lmhead_lse_partial8_kernel(
 
   int slice = work.slice_first;
   int slice_last_tile = slice_tile(slice + 1, n_vt, S) - 1;
-  auto epilogue = [&](int tile, floatx16 (&acc)[4][2]) {
+  auto epilogue = [&](int tile, floatx4 (&acc)[8][4]) {
     const int vw = tile * kBV + wv * 128;
+    // This lane's token offset, made opaque here so that the per-lane
+    // addresses below are formed in each epilogue: hoisted out of the tile
+    // loop they would be live across the K loop and push values into scratch.
+    int lt = L.lane;
+    asm volatile("" : "+v"(lt));
+    lt = tq * 64 + (lt & 15);
     auto fold_tile = [&](auto partial, auto pick) {
-      if constexpr (kKeep) {
-        const LogitRows rows = logit_rows(logits, ld, t0 + tq * 64, 64, n_tok, col, half);
 #pragma unroll
-        for (int bn = 0; bn < 2; ++bn)
+      for (int bn = 0; bn < 4; ++bn) {
+        if constexpr (kKeep) {
+          const LogitRows rows = logit_rows(logits, ld, t0 + tq * 64, 64, n_tok, c16, quad);
 #pragma unroll
-          for (int bm = 0; bm < 4; ++bm) store_logits(rows, bn, vw + bm * 32, half, vocab, acc[bm][bn], partial);
+          for (int bm = 0; bm < 8; ++bm) store_logits(rows, bn, vw + bm * 16, quad, vocab, acc[bm][bn], partial);
+        }
+        floatx4 z[8];
+#pragma unroll
+        for (int bm = 0; bm < 8; ++bm) z[bm] = acc[bm][bn];
+        if constexpr (decltype(pick)::value) pick_sampled(c[bn], z, vw, quad, zy_out + (t0 + lt + bn * 16));
+        fold_column16(c[bn], z, vw, quad, vocab, partial);
+        __builtin_amdgcn_sched_barrier(0);  // one token column at a time (register pressure)
       }
-#pragma unroll
-      for (int bn = 0; bn < 2; ++bn)
-        fold_column(c[bn], acc[0][bn], acc[1][bn], acc[2][bn], acc[3][bn], vw, half, vocab, partial, pick);
     };
     // A lane's sampled row lies in this wavefront's 128 rows of a given tile
     // for about one tile in V / 128, so most tiles skip the pick (a uniform
     // branch: the picked values are the same either way).
-    const bool mine = (unsigned)(c[0].y - vw) < 128u || (unsigned)(c[1].y - vw) < 128u;
+    bool mine = false;
+#pragma unroll
+    for (int bn = 0; bn < 4; ++bn) {
+      int y = c[bn].y;
+      asm volatile("" : "+v"(y));  // (no test hoisted out of the tile loop)
+      mine = mine || (unsigned)(y - vw) < 128u;
+    }
     if (tile * kBV + kBV > vocab) fold_tile(std::true_type{}, std::true_type{});  // only the vocabulary's last tile
     else if (__builtin_amdgcn_ballot_w64(mine) != 0) fold_tile(std::false_type{}, std::true_type{});
     else fold_tile(std::false_type{}, std::false_type{});
     if (tile == slice_last_tile) {
 #pragma unroll
-      for (int bn = 0; bn < 2; ++bn) {
-        const int tok = t0 + tq * 64 + bn * 32 + col;
-        flush_slice(c[bn], tok, n_tok, half, ((size_t)slice * 2 + wv) * n_tok + tok, part);
+      for (int bn = 0; bn < 4; ++bn) {
+        const int tok = t0 + lt + bn * 16;
+        flush_slice16(c[bn], tok, n_tok, quad, ((size_t)slice * 2 + wv) * n_tok + tok, part);
       }
       ++slice;
-      slice_last_tile = slice_tile(slice + 1, n_vt, S) - 1;
+      int Sx = S;
+      asm volatile("" : "+s"(Sx));  // (the division's set-up stays here, not live across the K loop)
+      slice_last_tile = slice_tile(slice + 1, n_vt, Sx) - 1;
     }
   };
   run_tiles8<kDtype, kBFar>(smem, L, row_bytes, tile_begin, tile_end, nks, w_rsrc, hr, epilogue);
-
-#pragma unroll
-  for (int bn = 0; bn < 2; ++bn)
-    if (c[bn].found) zy_out[t0 + tq * 64 + bn * 32 + col] = c[bn].zy;
 }
 
 // The same partials for few tokens: 64-token blocks, one workgroup per
 // (token block, slice), the workgroup's slice walked by run_tiles_narrow.
-// Lane l of wavefront (wv, wt) holds token t0 + 32 wt + (l mod 32) against
-// the same W rows, with the same fold, as in lmhead_lse_partial8_kernel, so
-// the partials (and the logprobs) have the same bits.
+// Lane l of wavefront (wv, wt) holds tokens t0 + 32 wt + 16 bn + (l mod 16)
+// (bn < 2) against the same W rows, with the same fold, as in
+// lmhead_lse_partial8_kernel, so the partials (and the logprobs) have the
+// same bits.
 template <int kDtype, bool kKeep>
 __global__ __launch_bounds__(kThreads, 1) void lmhead_lse_partial_narrow_kernel(
     const char* __restrict__ H, const char* __restrict__ W, const int32_t* __restrict__ tokens, int n_tok,
@@ -204,7 +212,7 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_lse_partial_narrow_kernel(
     float* __restrict__ logits, long long ld) {
   __shared__ uint4 smem[kEngineSmemChunks];
   const Lanes L = lanes();
-  const int wv = L.wv, wt = L.wt, half = L.half, col = L.col;
+  const int wv = L.wv, wt = L.wt, quad = L.lane >> 4, c16 = L.lane & 15;
   // Token block fastest-varying after the slice: with 256 slices the token
   // blocks of a slice share an XCD (blockIdx mod 8) and its L2.
   const int S = n_slices;
@@ -214,30 +222,46 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_lse_partial_narrow_kernel(
   const int tile_begin = slice_tile(slice, n_vt, S);
   const int tile_end = slice_tile(slice + 1, n_vt, S);
   const int nks = row_bytes / kStepBytes;
-  const int tok = t0 + wt * 32 + col;
-  Col c = Col{tok < n_tok ? tokens[tok] : -1, -INFINITY, 0.0f, 0.0f, false};
+  Col16 c[2];
+#pragma unroll
+  for (int bn = 0; bn < 2; ++bn) {
+    const int tok = t0 + wt * 32 + bn * 16 + c16;
+    c[bn] = Col16{tok < n_tok ? tokens[tok] : -1, -INFINITY, 0.0f};
+  }
 
   auto w_rsrc = [&](int tile) {
     const int v0 = tile * kBV;
     return rsrc_words(W + (size_t)v0 * row_bytes, (uint32_t)min(kBV, vocab - v0) * row_bytes);
   };
   const int4v hr = rsrc_words(H + (size_t)t0 * row_bytes, (uint32_t)min(kNarrowBRows, n_tok - t0) * row_bytes);
-  const LogitRows rows = logit_rows(logits, ld, t0 + wt * 32, 32, n_tok, col, half);
-  auto epilogue = [&](int tile, floatx16 (&acc)[4]) {
+  const LogitRows rows = logit_rows(logits, ld, t0 + wt * 32, 32, n_tok, c16, quad);
+  auto epilogue = [&](int tile, floatx4 (&acc)[8][2]) {
     const int vw = tile * kBV + wv * 128;
     auto fold_tile = [&](auto partial) {
       if constexpr (kKeep) {
 #pragma unroll
-        for (int bm = 0; bm < 4; ++bm) store_logits(rows, 0, vw + bm * 32, half, vocab, acc[bm], partial);
+        for (int bn = 0; bn < 2; ++bn)
+#pragma unroll
+          for (int bm = 0; bm < 8; ++bm) store_logits(rows, bn, vw + bm * 16, quad, vocab, acc[bm][bn], partial);
       }
-      fold_column(c, acc[0], acc[1], acc[2], acc[3], vw, half, vocab, partial, std::true_type{});
+#pragma unroll
+      for (int bn = 0; bn < 2; ++bn) {
+        floatx4 z[8];
+#pragma unroll
+        for (int bm = 0; bm < 8; ++bm) z[bm] = acc[bm][bn];
+        pick_sampled(c[bn], z, vw, quad, zy_out + (t0 + wt * 32 + bn * 16 + c16));
+        fold_column16(c[bn], z, vw, quad, vocab, partial);
+      }
     };
     if (tile * kBV + kBV > vocab) fold_tile(std::true_type{});
     else fold_tile(std::false_type{});
   };
   run_tiles_narrow<kDtype>(smem, L, row_bytes, tile_begin, tile_end, nks, w_rsrc, hr, epilogue);
-  flush_slice(c, tok, n_tok, half, ((size_t)slice * 2 + wv) * n_tok + tok, part);
-  if (c.found) zy_out[tok] = c.zy;
+#pragma unroll
+  for (int bn = 0; bn < 2; ++bn) {
+    const int tok = t0 + wt * 32 + bn * 16 + c16;
+    flush_slice16(c[bn], tok, n_tok, quad, ((size_t)slice * 2 + wv) * n_tok + tok, part);
+  }
 }
 
 }  // namespace
@@ -319,10 +343,14 @@ void launch_partials(const char* H, const char* W, const int32_t* tokens, int n_
     const int ntb = (int)ceil_div(n_tok, kBT);
     const dim3 grid((unsigned)ntb * (unsigned)n_slice_groups(n_tok, vocab));
     // Long K loops stage the token block two K steps ahead (see run_tiles8).
-    if (row_bytes / kStepBytes > kNearBMaxSteps)
+    // The fp32 head's kept-logits kernel always does (the other load order
+    // needs one register more than it has): the load order changes no
+    // arithmetic, so the bits are the same either way.
+    constexpr bool kFarOnly = kDtype == 1 && kKeep;
+    if (kFarOnly || row_bytes / kStepBytes > kNearBMaxSteps)
       hipLaunchKernelGGL((lmhead_lse_partial8_kernel<kDtype, kKeep, true>), grid, dim3(kThreads8), 0, stream, H, W,
                          tokens, n_tok, row_bytes, vocab, ntb, S, G, part, zy, logits, ld);
-    else
+    else if constexpr (!kFarOnly)
       hipLaunchKernelGGL((lmhead_lse_partial8_kernel<kDtype, kKeep, false>), grid, dim3(kThreads8), 0, stream, H, W,
                          tokens, n_tok, row_bytes, vocab, ntb, S, G, part, zy, logits, ld);
   }

@@ -1,8 +1,9 @@
-// Per-lane online log-sum-exp folds of the head's logits: fold_column for
-// the bf16 / fp32 heads (wide and narrow kernels), fold_values for the FP8 /
-// MXFP4 heads (block by block). Kernels that share a fold and feed it the
-// same logit values in the same order give a token the same partials, and
-// so the same logprob, bit for bit.
+// Per-lane online log-sum-exp folds of the head's logits: fold_column16 for
+// the bf16 / fp32 heads (wide and narrow kernels, 16 x 16 blocks),
+// fold_values for the FP8 / MXFP4 heads (32 x 32 blocks, block by block).
+// Kernels that share a fold and feed it the same logit values in the same
+// order give a token the same partials, and so the same logprob, bit for
+// bit.
 #pragma once
 
 #include "device_common.h"
@@ -17,6 +18,13 @@ struct Col {
   float m, s;     // running max and sum of exp(z - m)
   float zy;       // the sampled logit
   bool found;
+};
+
+// The same state for the 16 x 16 fold: the sampled logit is not carried
+// (pick_sampled writes it out from the tile that holds it).
+struct Col16 {
+  int y;       // sampled row, -1 past the last token
+  float m, s;  // running max and sum of exp(z - m)
 };
 
 // Fold one 32 x 32 block of logits (rows vw + 32 bm + ..., this lane's
@@ -77,11 +85,38 @@ __device__ __forceinline__ void fold_values(Col& c, floatx16 z, int bm, int vw, 
   c.m = mnew;
 }
 
-// Fold one tile's four 32 x 32 blocks of one token column (block bm holds
-// rows 32 bm + 8 (i / 4) + 4 half + (i % 4) of the wavefront's 128 rows) into
-// the state, as one step: the bf16 and fp32 heads' fold, shared by their
-// wide and narrow kernels (the FP8 kernels fold block by block with
-// fold_values). The 64 logits' maximum M (exact in any order) moves the
+// Of a lane's 32 values of one token (block bm register i: row offset
+// 16 bm + 4 quad + i), the one at row offset o: block bits 4-6 of o,
+// register bits 0-1 (bits 2-3 name the lane quarter), by a tree of selects.
+__device__ __forceinline__ float select32(const floatx4 (&z)[8], int o) {
+  const bool b0 = (o & 1) != 0, b1 = (o & 2) != 0, b4 = (o & 16) != 0, b5 = (o & 32) != 0, b6 = (o & 64) != 0;
+  float v[8];
+#pragma unroll
+  for (int bm = 0; bm < 8; ++bm) v[bm] = b1 ? (b0 ? z[bm][3] : z[bm][2]) : (b0 ? z[bm][1] : z[bm][0]);
+  const float w0 = b4 ? v[1] : v[0], w1 = b4 ? v[3] : v[2], w2 = b4 ? v[5] : v[4], w3 = b4 ? v[7] : v[6];
+  const float x0 = b5 ? w1 : w0, x1 = b5 ? w3 : w2;
+  return b6 ? x1 : x0;
+}
+
+// The lane of a wavefront that holds token column c's sampled row in this
+// tile (row offset o = y - vw in [0, 128), lane quarter (o / 4) mod 4)
+// writes that logit to *zy. It is read from the same accumulators the fold
+// reads, before any masking (a sampled row lies inside the vocabulary).
+__device__ __forceinline__ void pick_sampled(const Col16& c, const floatx4 (&z)[8], int vw, int quad, float* zy) {
+  // y made opaque here: otherwise the compiler forms the select bits of the
+  // row (loop-invariant) once, ahead of the K loop, and keeps them live
+  // across it.
+  int y = c.y;
+  asm volatile("" : "+v"(y));
+  const int o = y - vw;
+  if ((unsigned)o < 128u && ((o >> 2) & 3) == quad) *zy = select32(z, o);
+}
+
+// Fold one tile's logits of one token column (this lane's 32 of the
+// wavefront's 128 rows: block bm register i holds row 16 bm + 4 quad + i)
+// into the state, as one step: the bf16 and fp32 heads' fold, shared by
+// their wide and narrow kernels (the FP8 kernels fold block by block with
+// fold_values). The 32 logits' maximum M (exact in any order) moves the
 // running maximum to m' = max(m, M); every term of the tile is then
 // exp2(z log2e + b) with one rounded offset b = -m' log2e (a fused
 // multiply-add per logit), summed into eight partial sums in a fixed order
@@ -89,52 +124,56 @@ __device__ __forceinline__ void fold_values(Col& c, floatx16 z, int bm, int vw, 
 // moves every term of the tile by the same factor, within |m'| 2^-24 of 1
 // (the maximum's own term is not exactly 1: the combine keeps lse >= the
 // largest logit, so logprob <= 0 still holds in fp32).
-template <class kPartial, class kPick>
-__device__ __forceinline__ void fold_column(Col& c, floatx16 z0, floatx16 z1, floatx16 z2, floatx16 z3, int vw,
-                                            int half, int vocab, kPartial, kPick) {
-  floatx16 z[4] = {z0, z1, z2, z3};
+//
+// kPartial (a std::bool_constant): the tile may hold rows past the
+// vocabulary, which are masked. Callers choose it once per tile, so that a
+// full tile's epilogue has no masking and no branches.
+template <class kPartial>
+__device__ __forceinline__ void fold_column16(Col16& c, floatx4 (&z)[8], int vw, int quad, int vocab, kPartial) {
   if constexpr (kPartial::value) {
+    const int lim = vocab - (vw + 4 * quad);  // row offsets 16 bm + i at or past this do not exist
 #pragma unroll
-    for (int bm = 0; bm < 4; ++bm) {
-      const int lim = vocab - (vw + bm * 32 + 4 * half);  // rows at or past this offset do not exist
+    for (int bm = 0; bm < 8; ++bm)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) z[bm][i] = (8 * (i >> 2) + (i & 3) >= lim) ? -INFINITY : z[bm][i];
-    }
+      for (int i = 0; i < 4; ++i) z[bm][i] = (16 * bm + i >= lim) ? -INFINITY : z[bm][i];
   }
-  if constexpr (kPick::value) {
-    const int o = c.y - vw;  // sampled row relative to this wavefront's 128 rows
-    const bool b0 = (o & 1) != 0, b1 = (o & 2) != 0, b2 = (o & 8) != 0, b3 = (o & 16) != 0;
-    const bool here = (unsigned)o < 128u && ((o >> 2) & 1) == half;
-    const int bm = (o >> 5) & 3;
-    const float pick = select16(bm == 0 ? z[0] : bm == 1 ? z[1] : bm == 2 ? z[2] : z[3], b0, b1, b2, b3);
-    c.zy = here ? pick : c.zy;
-    c.found = c.found || here;
-  }
-  float mx[4];
+  // (a chain: the compiler pairs it into three-operand maxima)
+  float mnew = c.m;
 #pragma unroll
-  for (int bm = 0; bm < 4; ++bm) {
-    float a = fmaxf(z[bm][0], z[bm][1]);
-#pragma unroll
-    for (int i = 2; i < 16; ++i) a = fmaxf(a, z[bm][i]);
-    mx[bm] = a;
-  }
-  const float mnew = fmaxf(c.m, fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3])));
+  for (int k = 0; k < 32; ++k) mnew = fmaxf(mnew, z[k >> 2][k & 3]);
   // A lane whose rows so far are all absent has mnew = -inf; it then works
   // around 0 and keeps (m, s) = (-inf, 0).
   const float mref = mnew == -INFINITY ? 0.0f : mnew;
   const float b = -mref * kLog2e;
   float s[8];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) s[k] = fast_exp2(__builtin_fmaf(z[0][k], kLog2e, b));
+  for (int k = 0; k < 8; ++k) s[k] = fast_exp2(__builtin_fmaf(z[k >> 2][k & 3], kLog2e, b));
 #pragma unroll
-  for (int k = 8; k < 64; ++k) s[k & 7] += fast_exp2(__builtin_fmaf(z[k >> 4][k & 15], kLog2e, b));
+  for (int k = 8; k < 32; ++k) s[k & 7] += fast_exp2(__builtin_fmaf(z[k >> 2][k & 3], kLog2e, b));
   const float sum = ((s[0] + s[1]) + (s[2] + s[3])) + ((s[4] + s[5]) + (s[6] + s[7]));
   c.s = __builtin_fmaf(c.s, fast_exp2(__builtin_fmaf(c.m, kLog2e, b)), sum);
   c.m = mnew;
 }
 
-// Slice end: lanes l and l ^ 32 hold the same token (different rows); the
-// lower lane merges the upper lane's state into its own and writes the
+// Slice end of fold_column16's states: lanes l, l ^ 16, l ^ 32 and l ^ 48
+// hold the same token (different rows); they are merged as (q0 q1)(q2 q3)
+// (lane quarters l / 16), the lowest lane writes the wavefront's partial of
+// the slice, and every lane starts the next slice afresh.
+__device__ __forceinline__ void flush_slice16(Col16& c, int tok, int n_tok, int quad, size_t part_index,
+                                              float2* __restrict__ part) {
+  float m2 = __shfl_xor(c.m, 16, 64);
+  float s2 = __shfl_xor(c.s, 16, 64);
+  lse_merge(c.m, c.s, m2, s2);
+  m2 = __shfl_xor(c.m, 32, 64);
+  s2 = __shfl_xor(c.s, 32, 64);
+  lse_merge(c.m, c.s, m2, s2);
+  if (quad == 0 && tok < n_tok) part[part_index] = make_float2(c.m, c.s);
+  c.m = -INFINITY;
+  c.s = 0.0f;
+}
+
+// Slice end of fold_values's states: lanes l and l ^ 32 hold the same token
+// (different rows); the lower lane merges the upper lane's state into its own and writes the
 // wavefront's partial of the slice; every lane starts the next slice afresh.
 __device__ __forceinline__ void flush_slice(Col& c, int tok, int n_tok, int half, size_t part_index,
                                             float2* __restrict__ part) {

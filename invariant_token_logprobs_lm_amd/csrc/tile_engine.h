@@ -4,18 +4,23 @@
 // calls and the FP8 / MXFP4 ones. The bf16 / fp32 wide contractions (the
 // forward and the backward) run on the eight-wavefront loop of
 // tile_engine8.h, which uses the same slots, swizzle and per-block MFMA
-// sequence.
+// sequence as the narrow loop.
 //
-// Four-wavefront geometry: a 256-thread workgroup (2 x 2 wavefronts)
+// bf16 / fp32 blocks are 16 x 16 (Mma16): in sub-step kk (0, 1) of a
+// 128-byte K step lane l supplies row (l mod 16) of an A block and of a B
+// block with logical 16-byte chunk 4 kk + lane_chunk(l / 16); accumulator
+// register i of lane l holds A row 4 (l / 16) + i against B row (l mod 16).
+//
+// FP8 / MXFP4 geometry: a 256-thread workgroup (2 x 2 wavefronts)
 // multiplies 256-row tiles of an operand A, walked in order, with one fixed
-// 256-row block of an operand B: acc = A_tile B^T (both row-major and K-contiguous, fp32 accumulate,
-// K ascending in steps of 128 bytes). After each tile an epilogue sees the
-// accumulators. Wavefront (wv, wt) holds rows 128 wv .. 128 wv + 127 of the
-// A tile against rows 128 wt .. 128 wt + 127 of the B block, as 4 x 4
-// blocks of 32 x 32 (v_mfma_f32_32x32x16_bf16, or v_mfma_f32_32x32x2f32 for
-// fp32 operands): lane l supplies row (l mod 32) of A and of B with the k
-// range chosen by l / 32, and accumulator register i of lane l holds A row
-// 8 (i / 4) + 4 (l / 32) + (i mod 4) against B row (l mod 32).
+// 256-row block of an operand B: acc = A_tile B^T (both row-major and
+// K-contiguous, fp32 accumulate, K ascending in steps of 128 bytes). After
+// each tile an epilogue sees the accumulators. Wavefront (wv, wt) holds rows
+// 128 wv .. 128 wv + 127 of the A tile against rows 128 wt .. 128 wt + 127
+// of the B block, as 4 x 4 blocks of 32 x 32: lane l supplies row (l mod 32)
+// of A and of B with the k range chosen by l / 32, and accumulator register
+// i of lane l holds A row 8 (i / 4) + 4 (l / 32) + (i mod 4) against B row
+// (l mod 32).
 //
 // Fixed tile shapes, K order and instruction sequence: an output element's
 // bits depend only on its A row, its B row and K, never on the launch shape
@@ -30,36 +35,26 @@
 
 namespace itl {
 
-// One 16-byte fragment per lane and operand feeds one K sub-step. first()
-// starts a tile's accumulation from zero (the MFMA takes a zero C operand).
+// One 16-byte fragment per lane and operand feeds one 16 x 16 block for one
+// sub-step (32 bf16 or 16 fp32 values of K).
 template <int kDtype>
-struct Mma;
+struct Mma16;
 
 template <>
-struct Mma<0> {  // bf16: 8 elements per lane, k16 per instruction
-  __device__ static __forceinline__ void step(floatx16& acc, uint4 a, uint4 b) {
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                  __builtin_bit_cast(bf16x8_t, b), acc, 0, 0, 0);
-  }
-  __device__ static __forceinline__ void first(floatx16& acc, uint4 a, uint4 b) {
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                  __builtin_bit_cast(bf16x8_t, b), floatx16{}, 0, 0, 0);
+struct Mma16<0> {  // bf16: 8 elements per lane, k32 per instruction
+  __device__ static __forceinline__ void step(floatx4& acc, uint4 a, uint4 b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                  acc, 0, 0, 0);
   }
 };
 
 template <>
-struct Mma<1> {  // fp32: 4 elements per lane; instruction j takes element j (k2 each)
-  __device__ static __forceinline__ void step(floatx16& acc, uint4 a, uint4 b) {
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.x), __uint_as_float(b.x), acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.y), __uint_as_float(b.y), acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.z), __uint_as_float(b.z), acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.w), __uint_as_float(b.w), acc, 0, 0, 0);
-  }
-  __device__ static __forceinline__ void first(floatx16& acc, uint4 a, uint4 b) {
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.x), __uint_as_float(b.x), floatx16{}, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.y), __uint_as_float(b.y), acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.z), __uint_as_float(b.z), acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.w), __uint_as_float(b.w), acc, 0, 0, 0);
+struct Mma16<1> {  // fp32: 4 elements per lane; instruction j takes element j (k4 each)
+  __device__ static __forceinline__ void step(floatx4& acc, uint4 a, uint4 b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.x), __uint_as_float(b.x), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.y), __uint_as_float(b.y), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.z), __uint_as_float(b.z), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w), __uint_as_float(b.w), acc, 0, 0, 0);
   }
 };
 
@@ -84,6 +79,14 @@ static_assert(kBV == kBT && kThreads == 256 && kStepBytes == 128 && kWSlots == 3
               "the loop below assumes this geometry (5 slots = 160 KiB, all of a CU's LDS)");
 
 __device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+// 16 x 16 blocks: the 16-byte chunk of a sub-step's four that lane quarter
+// q = l / 16 supplies (A and B alike, so the instruction still sums the
+// sub-step's whole K range). Quarters 0 and 2, and 1 and 3, take chunks
+// that differ in bit 0: an LDS read serves lanes 8 g .. 8 g + 7 together
+// with lanes 32 + 8 g .. + 7, and with the row swizzle above such pairs hit
+// distinct banks (quarters 0 and 2 two chunks apart conflicted: measured).
+__device__ __forceinline__ int lane_chunk(int q) { return 2 * (q & 1) + (q >> 1); }
 
 // Raw buffer resource words over [base, base + nbytes) (gfx9-family raw
 // buffer: no stride, no swizzle, 32-bit data format). Loads whose row lies
@@ -201,23 +204,26 @@ constexpr int kEngineSmemChunks = (kWSlots + kHSlots) * kSlotChunks;
 
 // Narrow engine for few B rows (decode-shaped calls): 256-row A tiles
 // against a 64-row B block. Wavefront (wv, wt) holds rows 128 wv .. 128 wv +
-// 127 of the A tile against B rows 32 wt .. 32 wt + 31 as 4 blocks of 32 x 32.
-// Every MFMA of an accumulator block takes the same operand fragments, in
-// the same order, as in the eight-wavefront engine run_tiles8 (same slot
-// layout and swizzle, same K sub-step order, fresh accumulators at a tile's
-// first step), so an output element has the same bits in both. The work per
-// A tile is a quarter of the wide engine's: the loop streams A from memory,
-// so both operands rotate through four slots and are loaded three K steps
-// ahead.
+// 127 of the A tile against B rows 32 wt .. 32 wt + 31 as 8 x 2 blocks of
+// 16 x 16. Every MFMA of an accumulator block takes the same operand
+// fragments, in the same order, as in the eight-wavefront engine run_tiles8
+// (same slot layout and swizzle, same K sub-step order, fresh accumulators
+// at a tile's first step), so an output element has the same bits in both.
+// The work per A tile is a quarter of the wide engine's: the loop streams A
+// from memory, so both operands rotate through four slots and are loaded
+// three K steps ahead.
 constexpr int kNarrowSlots = 4;
 constexpr int kNarrowBSlotChunks = kNarrowBRows * kRowChunks;  // 512 chunks = 8 KiB
 constexpr int kNarrowBDmaPerWave = kNarrowBRows / 4 / kDmaRows;  // 2
 static_assert(kNarrowSlots * (kSlotChunks + kNarrowBSlotChunks) <= kEngineSmemChunks, "LDS budget");
 
+// epi(t, acc) sees tile t's accumulators acc[bm][bn] (A rows 16 bm + 4 (l /
+// 16) + i, B row 16 bn + (l mod 16) of the wavefront's 128 x 32).
 template <int kDtype, class ARsrc, class Epi>
 __device__ __forceinline__ void run_tiles_narrow(uint4* smem, const Lanes& L, int row_bytes, int tile_begin,
                                                  int tile_end, int nks, const ARsrc& a_rsrc, int4v b_rsrc, Epi&& epi) {
-  const int lane = L.lane, wave = L.wave, wv = L.wv, wt = L.wt, half = L.half, col = L.col;
+  const int lane = L.lane, wave = L.wave, wv = L.wv, wt = L.wt;
+  const int quad = lane >> 4, c16 = lane & 15;
   // Loader: wavefront w fills A rows 64 w .. 64 w + 63 (8 loads) and B rows
   // 16 w .. 16 w + 15 (2 loads) of a slot; lane i fetches row (i / 8) of an
   // 8-row group at logical chunk (i % 8) ^ swz(row), as in every engine here.
@@ -259,19 +265,19 @@ __device__ __forceinline__ void run_tiles_narrow(uint4* smem, const Lanes& L, in
     load_step(ld_tile, ld_ks, p);
     next_load();
   }
-  // MFMA operand reads: row (l mod 32) of each 32-row block at logical chunk
-  // 2 kk + l / 32 of sub-step kk, as in run_tiles8.
-  int a_off[4], b_off[4];
+  // MFMA operand reads: row (l mod 16) of each 16-row block at logical chunk
+  // 4 kk + lane_chunk(l / 16) of sub-step kk, as in run_tiles8.
+  int a_off[2], b_off[2];
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    const int pc = (2 * kk + half) ^ swz(col);
-    a_off[kk] = (wv * 128 + col) * kRowChunks + pc;
-    b_off[kk] = (wt * 32 + col) * kRowChunks + pc;
+  for (int kk = 0; kk < 2; ++kk) {
+    const int pc = (4 * kk + lane_chunk(quad)) ^ swz(c16);
+    a_off[kk] = (wv * 128 + c16) * kRowChunks + pc;
+    b_off[kk] = (wt * 32 + c16) * kRowChunks + pc;
   }
   constexpr int kPending = (kNarrowSlots - 2) * (kDmaPerWave + kNarrowBDmaPerWave);
   int slot = 0;
-  // One K step; kFirst = the tile's first (fresh accumulators).
-  auto k_step = [&](floatx16 (&acc)[4], auto first) {
+  // One K step.
+  auto k_step = [&](floatx4 (&acc)[8][2]) {
     // This step's loads landed (the next two steps' may be in flight);
     // every wavefront is done reading the previous step's slot.
     wait_and_barrier<kPending>();
@@ -280,29 +286,32 @@ __device__ __forceinline__ void run_tiles_narrow(uint4* smem, const Lanes& L, in
     const uint4* sa = smem + slot * kSlotChunks;
     const uint4* sb = smem + kNarrowSlots * kSlotChunks + slot * kNarrowBSlotChunks;
     // All 20 fragments of the step are read up front (one LDS round trip
-    // per step rather than one per sub-step), then the 16 MFMAs.
-    uint4 A[4][4], B[4];
+    // per step rather than one per sub-step), then the 32 MFMAs.
+    uint4 A[2][8], B[2][2];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
+    for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
-      for (int m = 0; m < 4; ++m) A[kk][m] = sa[a_off[kk] + m * 32 * kRowChunks];
-      B[kk] = sb[b_off[kk]];
+      for (int m = 0; m < 8; ++m) A[kk][m] = sa[a_off[kk] + m * 16 * kRowChunks];
+#pragma unroll
+      for (int n = 0; n < 2; ++n) B[kk][n] = sb[b_off[kk] + n * 16 * kRowChunks];
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
+    for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        if (decltype(first)::value && kk == 0) Mma<kDtype>::first(acc[m], A[kk][m], B[kk]);
-        else Mma<kDtype>::step(acc[m], A[kk][m], B[kk]);
-      }
-    }
+      for (int m = 0; m < 8; ++m)
+#pragma unroll
+        for (int n = 0; n < 2; ++n) Mma16<kDtype>::step(acc[m][n], A[kk][m], B[kk][n]);
     slot = slot == kNarrowSlots - 1 ? 0 : slot + 1;
   };
   for (int tile = tile_begin; tile < tile_end; ++tile) {
-    floatx16 acc[4];
-    k_step(acc, std::true_type{});
-    for (int ks = 1; ks < nks; ++ks) k_step(acc, std::false_type{});
+    // A tile's accumulators start as +0.0 registers, as in run_tiles8.
+    floatx4 acc[8][2];
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+      for (int n = 0; n < 2; ++n) acc[m][n] = floatx4{};
+    for (int ks = 0; ks < nks; ++ks) k_step(acc);
     epi(tile, acc);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");

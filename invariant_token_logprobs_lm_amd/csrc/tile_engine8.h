@@ -1,35 +1,49 @@
 // Eight-wavefront tile engine (gfx950 / CDNA4): the K loop of the wide bf16
 // / fp32 contractions (the logprob forward, and the backward's dlogits, dH
-// and dW) with two wavefronts per SIMD.
+// and dW) with two wavefronts per SIMD, on 16 x 16 MFMA blocks.
 //
 // A 512-thread workgroup multiplies 256-row tiles of an operand A (walked in
 // order) with one fixed 256-row block of an operand B, acc = A_tile B^T,
 // both row-major and K-contiguous, fp32 accumulate, K ascending in steps of
 // 128 bytes, through the five LDS slots, swizzle and direct-to-LDS loads
-// of tile_engine.h. Wavefront w = 4 g + r (g = 0, 1,
-// r = 0..3) holds A rows 128 (r & 1) .. + 127 of the tile against B rows
-// 64 ((r >> 1) + 2 g) .. + 63 of the block, as 4 x 2 blocks of 32 x 32: the
-// same per-block MFMA sequence (fragments, sub-step order, fresh
-// accumulators at a tile's first step) as run_tiles_narrow, so an output
-// element has the same bits in both.
+// of tile_engine.h. Wavefront w = 4 g + r (g = 0, 1, r = 0..3) holds A rows
+// 128 (r & 1) .. + 127 of the tile against B rows 64 ((r >> 1) + 2 g) .. +
+// 63 of the block, as 8 x 4 blocks of 16 x 16 (Mma16: v_mfma_f32_16x16x32_bf16;
+// v_mfma_f32_16x16x4f32 for fp32 operands). The 16 x 16 x 32 instruction
+// keeps the matrix cores at a higher clock under the part's power limit
+// than the 32 x 32 x 16 one for the same flops (a register-only loop: about
+// 2.05 against 1.8 GHz), which is why the blocks are 16 x 16.
+//
+// MFMA layout: in sub-step kk (0, 1) of a K step lane l supplies row
+// (l mod 16) of an A block and of a B block with logical 16-byte chunk
+// 4 kk + lane_chunk(l / 16) of the row's 128-byte K step (lane quarters 0,
+// 1, 2, 3 take chunks 0, 2, 1, 3; bf16: k = 64 s + 8 chunk .. + 7);
+// accumulator register i of lane l holds A row
+// 4 (l / 16) + i of the block against B row (l mod 16). Every block takes
+// its K step as sub-step 0 then sub-step 1, one instruction each (four for
+// fp32), with fresh accumulators at a tile's first step: the same sequence
+// as run_tiles_narrow, so an output element has the same bits in both.
 //
 // Schedule. Waves w and w + 4 share a SIMD (the workgroup's wavefronts go
 // to the four SIMDs in a rotating order, w and w + 4 on the same one, as
 // read from the hardware-id register), so each SIMD's matrix core is fed by
 // two instruction streams and one wavefront's waits are covered by the
-// other's MFMAs. Each wavefront runs a K step as four sub-steps of 8 MFMAs;
-// during each sub-step it reads the next sub-step's 6 operand fragments
-// from LDS. One workgroup barrier per K step, after sub-step 2 (whose reads
-// are the step's last): it publishes step g + 1 (every wavefront has waited
-// for its own loads of it) and frees step g's slots; sub-step 3 loads the
-// near operand's step g + 2 into them (after its second MFMA), and
-// sub-step 0 of step g + 1 the far operand's step g + 3 (after its fourth).
-// Every wavefront loads rows 32 w .. 32 w + 31 of both operands, four loads
-// of each step back to back under one M0 value. The near operand (two
-// slots) is the B block, the far one (three slots) the walked A tiles; with
-// kBFar the other way round. A tile's last
-// K step leaves the next tile's first fragments unread; they are read after
-// the epilogue, which then has those registers.
+// other's MFMAs. A K step is eight sub-steps of 8 MFMAs (K half 0 with A
+// blocks 0, 1, then 2, 3, ...; then K half 1 likewise, each pair against
+// the four B blocks); each reads, into registers no earlier one still uses,
+// the next sub-step's A pair and a share of the B blocks of the next K
+// half, so two A pairs and two sets of four B blocks (48 registers) serve
+// and the LDS reads are spread over the step. One workgroup barrier per K
+// step, in sub-step 6 (after the step's last reads): it publishes step
+// s + 1 (every wavefront has waited for its own loads of it) and frees step
+// s's slots; sub-step 7 loads the near operand's step s + 2 into them, and
+// the next step's sub-step 0 the far operand's step s + 3 (its slot was
+// freed one barrier earlier). Every
+// wavefront loads rows 32 w .. 32 w + 31 of both operands, four loads of
+// each step back to back under one M0 value. The near operand (two slots) is the B block, the
+// far one (three slots) the walked A tiles; with kBFar the other way round.
+// A tile's last K step leaves the next tile's first fragments unread; they
+// are read after the epilogue, which then has those registers.
 #pragma once
 
 #include <type_traits>
@@ -43,7 +57,7 @@ namespace itl {
 constexpr int kDma8PerWave = 4;  // loads per wavefront per K step of each operand (32 rows)
 
 struct Lanes8 {
-  int lane, wave, grp, r, wv, tq, half, col;
+  int lane, wave, grp, r, wv, tq, quad, c16;
 };
 
 __device__ __forceinline__ Lanes8 lanes8() {
@@ -54,8 +68,8 @@ __device__ __forceinline__ Lanes8 lanes8() {
   L.r = L.wave & 3;
   L.wv = L.r & 1;                     // which 128 rows of the A tile
   L.tq = (L.r >> 1) | (L.grp << 1);   // which 64 rows of the B block
-  L.half = L.lane >> 5;
-  L.col = L.lane & 31;
+  L.quad = L.lane >> 4;               // which 4 rows of each 16-row A block the accumulators hold
+  L.c16 = L.lane & 15;                // which row of each 16-row B block
   return L;
 }
 
@@ -63,8 +77,8 @@ __device__ __forceinline__ Lanes8 lanes8() {
 // is A tile t's buffer resource (its first row at offset 0, its valid rows'
 // bytes as the range: rows past it load as zeros), b_rsrc the B block's;
 // rows are row_bytes apart; nks K steps of 128 bytes (nks >= 1,
-// nks * 128 <= row_bytes). epi(t, acc)
-// sees tile t's accumulators acc[bm][bn] (A rows 32 bm, B rows 32 bn of the
+// nks * 128 <= row_bytes). epi(t, acc) sees tile t's accumulators
+// acc[bm][bn] (A rows 16 bm + 4 quad + i, B row 16 bn + c16 of the
 // wavefront's 128 x 64); it may read them directly. Every thread of the
 // 512-thread workgroup must call this.
 template <int kDtype, bool kBFar, class ARsrc, class Epi>
@@ -73,7 +87,7 @@ __device__ __forceinline__ void run_tiles8(uint4* smem, const Lanes8& L, int row
   constexpr int kAS = kBFar ? kHSlots : kWSlots;  // slots of A
   constexpr int kBS = kBFar ? kWSlots : kHSlots;  // slots of B
   static_assert(kAS + kBS == 5 && (kAS == 2 || kAS == 3), "five slots: two near, three far");
-  const int lane = L.lane, wave = L.wave, half = L.half, col = L.col;
+  const int lane = L.lane, wave = L.wave, quad = L.quad, c16 = L.c16;
 
   // Loader: wavefront w fills rows 32 w .. 32 w + 31 of both operands' slots
   // with four 16-byte-per-lane loads each, under one M0 value (dma16x4);
@@ -91,29 +105,35 @@ __device__ __forceinline__ void run_tiles8(uint4* smem, const Lanes8& L, int row
               (uint32_t)j * 1024u;
   const uint32_t lds0 = (uint32_t)(size_t)((__attribute__((address_space(3))) uint4*)smem);
   const uint32_t my_rows = (uint32_t)wave * 32 * kStepBytes;
-  const int n_steps = (tile_end - tile_begin) * nks;
-  // The four loads of step s of A / of B into its slot. A step past the end
-  // loads the last step's data instead (a valid address) into slot s, which
-  // is free and which nothing reads again.
+  // The four loads of step s of A / of B into its slot; each operand's
+  // loads come in step order, so the step's (tile, K step) is kept as a
+  // running count (no division). A step past the end loads the last step's
+  // data instead (a valid address) into slot s, which is free and which
+  // nothing reads again.
+  int a_tile = tile_begin, a_ks = 0, b_ks = 0, b_left = (tile_end - tile_begin) * nks;
   auto a_load = [&](int s) {
-    const int c = s < n_steps ? s : n_steps - 1;
-    const int q = c / nks;
-    dma16x4(a_rsrc(tile_begin + q), voff, (uint32_t)(c - q * nks) * kStepBytes,
-            lds0 + (uint32_t)(s % kAS) * kSlotBytes + my_rows);
+    dma16x4(a_rsrc(a_tile), voff, (uint32_t)a_ks * kStepBytes, lds0 + (uint32_t)(s % kAS) * kSlotBytes + my_rows);
+    if (a_ks + 1 < nks) ++a_ks;
+    else if (a_tile + 1 < tile_end) a_ks = 0, ++a_tile;
+    a_ks = __builtin_amdgcn_readfirstlane(a_ks);  // wave-uniform: kept in SGPRs
+    a_tile = __builtin_amdgcn_readfirstlane(a_tile);
   };
   auto b_load = [&](int s) {
-    const int c = s < n_steps ? s : n_steps - 1;
-    dma16x4(b_rsrc, voff, (uint32_t)(c % nks) * kStepBytes, lds0 + (uint32_t)(kAS + s % kBS) * kSlotBytes + my_rows);
+    dma16x4(b_rsrc, voff, (uint32_t)b_ks * kStepBytes, lds0 + (uint32_t)(kAS + s % kBS) * kSlotBytes + my_rows);
+    if (--b_left > 0) b_ks = b_ks + 1 < nks ? b_ks + 1 : 0;
+    b_ks = __builtin_amdgcn_readfirstlane(b_ks);
   };
 
-  // MFMA operand reads of sub-step kk: A rows 128 wv + 32 bm + (l mod 32),
-  // B rows 64 tq + 32 bn + (l mod 32), logical chunk 2 kk + l / 32.
-  int a_off[4], b_off[4];
+  // MFMA operand reads of sub-step kk: A rows 128 wv + 16 bm + (l mod 16),
+  // B rows 64 tq + 16 bn + (l mod 16), logical chunk 4 kk +
+  // lane_chunk(l / 16) (the swizzle of a row depends on its low four bits
+  // only).
+  int a_off[2], b_off[2];
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    const int pc = (2 * kk + half) ^ swz(col);
-    a_off[kk] = (L.wv * 128 + col) * kRowChunks + pc;
-    b_off[kk] = (L.tq * 64 + col) * kRowChunks + pc;
+  for (int kk = 0; kk < 2; ++kk) {
+    const int pc = (4 * kk + lane_chunk(quad)) ^ swz(c16);
+    a_off[kk] = (L.wv * 128 + c16) * kRowChunks + pc;
+    b_off[kk] = (L.tq * 64 + c16) * kRowChunks + pc;
   }
 
   // The near operand (two slots) and the far one (three slots).
@@ -135,87 +155,95 @@ __device__ __forceinline__ void run_tiles8(uint4* smem, const Lanes8& L, int row
   wait_and_barrier<2 * kDma8PerWave>();
   __builtin_amdgcn_sched_barrier(0);
 
-  // Fragment sets: F[x] holds one sub-step's 4 A and 2 B fragments.
-  uint4 FA[2][4], FB[2][2];
-  auto read_sub = [&](int x, int s, int kk) {
-    const uint4* sa = smem + (s % kAS) * kSlotChunks;
-    const uint4* sb = smem + (kAS + s % kBS) * kSlotChunks;
-#pragma unroll
-    for (int bm = 0; bm < 4; ++bm) FA[x][bm] = sa[a_off[kk] + bm * 32 * kRowChunks];
-#pragma unroll
-    for (int bn = 0; bn < 2; ++bn) FB[x][bn] = sb[b_off[kk] + bn * 32 * kRowChunks];
+  // Fragments: FA[x][b] A block 2 p + b of a sub-step's pair p (x = p mod
+  // 2), FB[kk][bn] B block bn of K half kk.
+  uint4 FA[2][2], FB[2][4];
+  auto read_a = [&](int s, int kk, int bm) {
+    FA[(bm >> 1) & 1][bm & 1] = smem[(s % kAS) * kSlotChunks + a_off[kk] + bm * 16 * kRowChunks];
+  };
+  auto read_b = [&](int s, int kk, int bn) {
+    FB[kk][bn] = smem[(kAS + s % kBS) * kSlotChunks + b_off[kk] + bn * 16 * kRowChunks];
   };
   // A tile's accumulators start as +0.0 registers (the same sums as an MFMA
   // whose C operand is the constant 0).
-  floatx16 acc[4][2];
+  floatx4 acc[8][4];
   auto zero_acc = [&]() {
 #pragma unroll
-    for (int bm = 0; bm < 4; ++bm)
+    for (int bm = 0; bm < 8; ++bm)
 #pragma unroll
-      for (int bn = 0; bn < 2; ++bn) acc[bm][bn] = floatx16{};
+      for (int bn = 0; bn < 4; ++bn) acc[bm][bn] = floatx4{};
   };
-  // One sub-step: 8 MFMAs on set X; with kRead the reads of the next
-  // sub-step (step rs, sub-step rkk, into set X ^ 1) go after the first four
-  // MFMAs: A blocks 0 and 1, then A block 2, then B block 0, then A block 3
-  // and B block 1 (the last two then have four MFMAs to pass). kDma = 1: the
-  // far operand's step s + 2, after the fourth MFMA (its slot, that of step
-  // s - 1, was released at the previous barrier); kDma = 2: the near
-  // operand's step s + 2, after the second MFMA (into the slot step s
+  // Sub-step j (0..7) of K step s: K half kk = j / 4, A blocks 2 p and
+  // 2 p + 1 (p = j mod 4) against the four B blocks, 8 MFMAs (MFMA q on A
+  // block 2 p + q / 4 and B block q mod 4). It reads what later sub-steps
+  // need into registers no earlier one still uses: the next sub-step's A
+  // pair (after its MFMAs 0 and 1) and, in sub-steps 0-3, B block j of half
+  // 1 (after MFMA 2). Sub-step 6's A pair is the step's last read; the
+  // barrier that publishes step s + 1 follows after MFMA 5, then B blocks
+  // 0, 1 of step s + 1's half 0; sub-step 7 reads step s + 1's first A pair
+  // and its B blocks 2, 3. A tile's last step (kNext false) leaves step s + 1's reads to the
+  // code after the epilogue. kDma: the far operand's step s + 2 in sub-step
+  // 0 (its slot, that of step s - 1, was released at the previous barrier),
+  // the near operand's step s + 2 in sub-step 7 (into the slot step s
   // released at this step's barrier). At each barrier exactly the far
   // operand's latest four loads may then still be in flight.
-  auto sub = [&](auto X, auto read, auto dma, int rs, int rkk, int s) {
-    constexpr int x = decltype(X)::value;
-    constexpr int kDma = decltype(dma)::value;
-    const uint4* sa = smem + (rs % kAS) * kSlotChunks;
-    const uint4* sb = smem + (kAS + rs % kBS) * kSlotChunks;
+  auto sub = [&](auto J, auto next, int s) {
+    constexpr int j = decltype(J)::value;
+    constexpr int kk = j >> 2, p = j & 3;
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-      const int bm = q >> 1, bn = q & 1;
-      Mma<kDtype>::step(acc[bm][bn], FA[x][bm], FB[x][bn]);
-      if constexpr (decltype(read)::value) {
-        if (q == 0) {
-          FA[x ^ 1][0] = sa[a_off[rkk]];
-          FA[x ^ 1][1] = sa[a_off[rkk] + 32 * kRowChunks];
-        } else if (q == 1) {
-          FA[x ^ 1][2] = sa[a_off[rkk] + 2 * 32 * kRowChunks];
-        } else if (q == 2) {
-          FB[x ^ 1][0] = sb[b_off[rkk]];
-        } else if (q == 3) {
-          FA[x ^ 1][3] = sa[a_off[rkk] + 3 * 32 * kRowChunks];
-          FB[x ^ 1][1] = sb[b_off[rkk] + 32 * kRowChunks];
+      const int b = q >> 2, bn = q & 3;
+      Mma16<kDtype>::step(acc[2 * p + b][bn], FA[p & 1][b], FB[kk][bn]);
+      if constexpr (j < 6) {
+        // the next sub-step's A pair, then (sub-steps 0-3) B block j of
+        // half 1
+        if (q < 2) read_a(s, (j + 1) >> 2, 2 * ((j + 1) & 3) + q);
+        if (j < 4 && q == 2) read_b(s, 1, j);
+      } else if constexpr (j == 6) {
+        if (q < 2) read_a(s, 1, 6 + q);  // the step's last reads
+        if (q == 5) {
+          // step s + 1 landed (the far operand's step s + 2 may be in
+          // flight); every wavefront is done reading step s
+          wait_and_barrier<kDma8PerWave>();
         }
+        if (decltype(next)::value && q >= 6) read_b(s + 1, 0, q - 6);
+      } else {
+        if (decltype(next)::value && q < 2) read_a(s + 1, 0, q);
+        if (decltype(next)::value && (q == 2 || q == 3)) read_b(s + 1, 0, q);
       }
-      if constexpr (kDma == 1) {
+      if constexpr (j == 0) {
         if (q == 3) far_load(s + 2);
-      } else if constexpr (kDma == 2) {
-        if (q == 1) near_load(s + 2);
+      } else if constexpr (j == 7) {
+        if (q == 4) near_load(s + 2);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
   using T = std::true_type;
   using F = std::false_type;
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  // K step s; kNext: sub-step 3 reads step s + 1's first fragments (not in a
-  // tile's last step: they are read after the epilogue).
-  using D0 = std::integral_constant<int, 0>;
-  using D1 = std::integral_constant<int, 1>;
-  using D2 = std::integral_constant<int, 2>;
+  // K step s; kNext: its last sub-steps read step s + 1's first fragments
+  // (not in a tile's last step: they are read after the epilogue).
   auto k_step = [&](int s, auto next) {
-    sub(I0{}, T{}, D1{}, s, 1, s);
-    sub(I1{}, T{}, D0{}, s, 2, s);
-    sub(I0{}, T{}, D0{}, s, 3, s);
-    // step s + 1 landed (the far operand's step s + 2, issued in this step's
-    // first sub-step, may be in flight); every wavefront is done reading
-    // step s
-    wait_and_barrier<kDma8PerWave>();
-    __builtin_amdgcn_sched_barrier(0);
-    sub(I1{}, next, D2{}, s + 1, 0, s);
+    sub(std::integral_constant<int, 0>{}, next, s);
+    sub(std::integral_constant<int, 1>{}, next, s);
+    sub(std::integral_constant<int, 2>{}, next, s);
+    sub(std::integral_constant<int, 3>{}, next, s);
+    sub(std::integral_constant<int, 4>{}, next, s);
+    sub(std::integral_constant<int, 5>{}, next, s);
+    sub(std::integral_constant<int, 6>{}, next, s);
+    sub(std::integral_constant<int, 7>{}, next, s);
+  };
+  // The fragments of a step's first sub-step: A blocks 0, 1 and the B
+  // blocks of half 0.
+  auto read_first = [&](int s) {
+    read_a(s, 0, 0);
+    read_a(s, 0, 1);
+#pragma unroll
+    for (int bn = 0; bn < 4; ++bn) read_b(s, 0, bn);
   };
 
   zero_acc();
-  read_sub(0, 0, 0);
+  read_first(0);
   int s = 0;
   for (int tile = tile_begin; tile < tile_end; ++tile) {
     for (int ks = 0; ks + 1 < nks; ++ks, ++s) k_step(s, T{});
@@ -225,7 +253,7 @@ __device__ __forceinline__ void run_tiles8(uint4* smem, const Lanes8& L, int row
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("" ::: "memory");
     zero_acc();
-    if (tile + 1 < tile_end) read_sub(0, s, 0);
+    if (tile + 1 < tile_end) read_first(s);
   }
   // Every wavefront is done with the LDS ring (and its loads) on return.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");

@@ -268,10 +268,20 @@ def test_probe_library_is_separate_and_loads():
     """The benchmark's matrix-core probe lives in its own library; libitl.so
     does not export it."""
     probe = ctypes.CDLL(os.path.join(ROOT, "libitl_bench_probe.so"))
-    for name in ("itl_probe_operand_bytes", "itl_probe_flops", "itl_probe_mfma_bf16"):
+    for name in ("itl_probe_operand_bytes", "itl_probe_threads", "itl_probe_flops", "itl_probe_mfma_bf16"):
         assert hasattr(probe, name)
     probe.itl_probe_operand_bytes.restype = ctypes.c_size_t
-    assert probe.itl_probe_operand_bytes() == 4096 * 8 * 16
+    assert probe.itl_probe_operand_bytes() == 4096 * 16 * 16
+    assert [probe.itl_probe_threads(s) for s in (0, 1, 2)] == [256, 512, 0]
+    probe.itl_probe_flops.restype = ctypes.c_double
+    probe.itl_probe_flops.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    # per round: 4 wavefronts x 16 MFMAs of 32x32x16, or 8 x 32 of 16x16x32
+    assert probe.itl_probe_flops(0, 3, 5) == 3 * 5 * 4 * 16 * (2 * 32 * 32 * 16)
+    assert probe.itl_probe_flops(1, 3, 5) == 3 * 5 * 8 * 32 * (2 * 16 * 16 * 32)
+    probe.itl_probe_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                          ctypes.c_void_p]
+    # an unknown shape is refused before any launch
+    assert probe.itl_probe_mfma_bf16(2, 1, 1, 1, 1, None) != 0
     import invariant_token_logprobs_lm_amd as itl
 
     assert not hasattr(itl.lib, "itl_probe_mfma_bf16")
