@@ -299,8 +299,8 @@ itl_status itl_lmhead_logprob_fp8(const uint8_t* Hq, const float* h_scale, const
   if (vocab > kMaxVocab) return fail(ITL_ERR_UNSUPPORTED, "vocab too large");
   if (d >= ((int64_t)1 << 31) / (int64_t)itl::kBT) return fail(ITL_ERR_UNSUPPORTED, "d too large");
   if (vocab > (int64_t)(UINT32_MAX / 4)) return fail(ITL_ERR_UNSUPPORTED, "vocab too large");
-  // the grid of the kernel that runs: narrow for few tokens or d = 128
-  const bool narrow = n_tok <= itl::kNarrowMaxTokens || d < itl::kF8WideMinD;
+  // the grid of the kernel that runs: narrow for few tokens
+  const bool narrow = n_tok <= itl::kNarrowMaxTokens;
   const int64_t grid = narrow ? itl::ceil_div(n_tok, itl::kNarrowBRows) * itl::n_slices(vocab)
                               : itl::ceil_div(n_tok, itl::kBT) * itl::n_slice_groups(n_tok, vocab);
   if (grid > INT32_MAX) return fail(ITL_ERR_UNSUPPORTED, "problem too large for one launch");
@@ -421,7 +421,7 @@ const char* itl_build_info(void) {
     snprintf(buf, sizeof buf,
              "itl 0.3 arch=gfx950 threads=%d wide_threads=%d token_block=%d vocab_tile=%d k_step_bytes=%d w_slots=%d h_slots=%d "
              "swap_slots_over_k_steps=%d max_slices=%d slices=balanced narrow_max_tokens=%d narrow_token_block=%d "
-             "mfma_bf16=16x16x32 mfma_f32=16x16x4 fp8=e4m3_row_scaled mfma_fp8=32x32x64 mxfp4=e2m1_e8m0_32 "
+             "mfma_bf16=16x16x32 mfma_f32=16x16x4 fp8=e4m3_row_scaled mfma_fp8=16x16x128 mxfp4=e2m1_e8m0_32 mfma_mxfp4=32x32x64 "
              "bwd_chunk_tokens=%d loss_segment_tokens=%d loss_lane_segment=%d loss_wave_segment=%d loss_threads=%d "
              "loss_mean_chunk=%d loss_sums=f64 bwd_sampled_sort=stable_counting bwd_sampled_segment=%d "
              "bwd_sampled_group=%d",

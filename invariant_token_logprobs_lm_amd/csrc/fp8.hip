@@ -24,6 +24,7 @@
 #include "itl_launch.h"
 #include "lse_fold.h"
 #include "tile_engine.h"
+#include "tile_engine8.h"
 
 namespace itl {
 
@@ -124,106 +125,230 @@ __global__ __launch_bounds__(256) void quantize_rows_fp8_kernel(const void* __re
   }
 }
 
-// The bf16 head's partial kernel with E4M3 operands: same workgroup order,
-// slices and fold; the epilogue scales each accumulator by its vocabulary
-// row's and its token's scale before folding.
-__global__ __launch_bounds__(kThreads, 1) void lmhead_fp8_partial_kernel(
+// z = (z * w) * h, element by element, each product rounded to fp32: the
+// logits of four rows of one token from their accumulators, the rows'
+// scales w and the token's scale h (the wide and the narrow kernels both use
+// it, so their logits have the same bits).
+__device__ __forceinline__ void scale_logits(floatx4& z, const float4& w, float h) {
+  const floatx4 wv = {w.x, w.y, w.z, w.w};
+  z = (z * wv) * h;
+}
+
+// The bf16 head's wide partial kernel with E4M3 operands, on the
+// eight-wavefront engine's FP8 schedule (run_tiles8<2>): the same workgroup
+// order, slices, lane layout and fold (fold_column16); the epilogue scales
+// each accumulator by its vocabulary row's and its token's scale,
+//   z = (acc * w_scale[v]) * h_scale[t],
+// before folding. The wavefront's 128 row scales of a tile come into LDS by
+// the engine's side load (two 4-byte-per-lane loads into the wavefront's own
+// rows of a free slot), so the epilogue reads them without waiting on the
+// operand loads in flight.
+template <bool kBFar>
+__global__ __launch_bounds__(kThreads8, 1) void lmhead_fp8_partial8_kernel(
     const uint8_t* __restrict__ Hq, const float* __restrict__ h_scale, const uint8_t* __restrict__ Wq,
     const float* __restrict__ w_scale, const int32_t* __restrict__ tokens, int n_tok, int d, int vocab, int n_tb,
     int n_slices, int group, float2* __restrict__ part, float* __restrict__ zy_out) {
   __shared__ uint4 smem[kEngineSmemChunks];
-  const Lanes L = lanes();
-  const int wv = L.wv, wt = L.wt, half = L.half, col = L.col;
+  const Lanes8 L = lanes8();
+  const int wv = L.wv, tq = L.tq, quad = L.quad, c16 = L.c16;
   const int S = n_slices;
   const WideWork work = wide_work(blockIdx.x, n_tb, S, group);
   const int t0 = work.tb * kBT;
   const int n_vt = (vocab + kBV - 1) / kBV;
-  const int slice_first = work.slice_first;
   const int tile_begin = slice_tile(work.slice_first, n_vt, S);
   const int tile_end = slice_tile(work.slice_end, n_vt, S);
   const int row_bytes = d;
   const int nks = row_bytes / kStepBytes;
 
-  Col c[4];
-  float hs[4];
+  Col16 c[4];
 #pragma unroll
   for (int bn = 0; bn < 4; ++bn) {
-    const int tok = t0 + wt * 128 + bn * 32 + col;
-    c[bn] = Col{tok < n_tok ? tokens[tok] : -1, -INFINITY, 0.0f, 0.0f, false};
-    hs[bn] = tok < n_tok ? h_scale[tok] : 0.0f;
+    const int tok = t0 + tq * 64 + bn * 16 + c16;
+    c[bn] = Col16{tok < n_tok ? tokens[tok] : -1, -INFINITY, 0.0f};
   }
   auto w_rsrc = [&](int tile) {
     const int v0 = tile * kBV;
     return rsrc_words(Wq + (size_t)v0 * row_bytes, (uint32_t)min(kBV, vocab - v0) * row_bytes);
   };
   const int4v hr = rsrc_words(Hq + (size_t)t0 * row_bytes, (uint32_t)min(kBT, n_tok - t0) * row_bytes);
-  // Row scales: lane l of wavefront (wv, wt) fetches the scales of rows
-  // vw + l and vw + 64 + l of each tile (vw = the wavefront's first row)
-  // into ws_lo, ws_hi, through a bounded buffer (rows past the vocabulary
-  // read 0). The loads are issued from inline assembly in the tile's last K
-  // step, before that step's loads into LDS, and waited for with
-  // vmcnt(kF8LoadsAfterPre) in the epilogue: a load the compiler can see
-  // would make it wait for every load in flight (vmcnt(0)) and stall on the
-  // next steps' operands at every tile.
+  // Side load: lane l fetches the scales of rows vw + l and vw + 64 + l (vw
+  // = the wavefront's first row of the tile) to bytes 4 l and 256 + 4 l of
+  // its LDS rows, so that row r of the 128 sits at float r, and the scale of
+  // token t0 + 64 tq + l to byte 512 + 4 l (kept in registers across the K
+  // loop, the token scales would push the loop's operands out of them).
+  // Rows past the vocabulary and tokens past n_tok read 0 through the
+  // buffers' ranges.
   const int4v ws_words = rsrc_words(w_scale, (uint32_t)vocab * 4u);
-  float ws_lo = 0.0f, ws_hi = 0.0f;
-  auto pre = [&](int tile) {
+  const int4v hs_words = rsrc_words(h_scale + t0, (uint32_t)min(kBT, n_tok - t0) * 4u);
+  int scale_chunk = 0;
+  auto side = [&](int tile, uint32_t lds, int chunk) {
     const uint32_t off = (uint32_t)(tile * kBV + wv * 128 + L.lane) * 4u;
-    const uint32_t off_hi = off + 256u;
-    const int4v r = {__builtin_amdgcn_readfirstlane(ws_words[0]), __builtin_amdgcn_readfirstlane(ws_words[1]),
-                     __builtin_amdgcn_readfirstlane(ws_words[2]), __builtin_amdgcn_readfirstlane(ws_words[3])};
-    asm volatile(
-        "buffer_load_dword %0, %2, %4, 0 offen\n\t"
-        "buffer_load_dword %1, %3, %4, 0 offen"
-        : "=&v"(ws_lo), "=&v"(ws_hi)
-        : "v"(off), "v"(off_hi), "s"(r)
-        : "memory");
+    dma4(ws_words, off, 0u, lds);
+    dma4(ws_words, off + 256u, 0u, lds + 256u);
+    dma4(hs_words, (uint32_t)(tq * 64 + L.lane) * 4u, 0u, lds + 512u);
+    scale_chunk = chunk;
   };
 
-  int slice = slice_first;
+  int slice = work.slice_first;
   int slice_last_tile = slice_tile(slice + 1, n_vt, S) - 1;
-  auto epilogue = [&](int tile, floatx16 (&acc)[4][4]) {
+  auto epilogue = [&](int tile, floatx4 (&acc)[8][4]) {
     const int vw = tile * kBV + wv * 128;
-    asm volatile("s_waitcnt vmcnt(%2)" : "+v"(ws_lo), "+v"(ws_hi) : "n"(kF8LoadsAfterPre) : "memory");
-    mfma_result_wait();
-    auto fold_tile = [&](auto partial) {
+    // the side load landed (the engine issued kDma8PerWave loads after it)
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kDma8PerWave) : "memory");
+    // The logits, in place: acc[bm][bn] row 16 bm + 4 quad + i, token
+    // 64 tq + 16 bn + c16 (scales at floats 16 bm + 4 quad + i and
+    // 128 + 16 bn + c16 of the side rows).
+    {
+      const float4* sw = reinterpret_cast<const float4*>(smem) + scale_chunk + quad;
+      const float* sh = reinterpret_cast<const float*>(smem) + scale_chunk * 4 + 128 + c16;
+      float hs[4];
+#pragma unroll
+      for (int bn = 0; bn < 4; ++bn) hs[bn] = sh[bn * 16];
+#pragma unroll
+      for (int bm = 0; bm < 8; ++bm) {
+        const float4 w = sw[4 * bm];
+#pragma unroll
+        for (int bn = 0; bn < 4; ++bn) scale_logits(acc[bm][bn], w, hs[bn]);
+      }
+    }
+    int lt = L.lane;
+    asm volatile("" : "+v"(lt));  // (per-lane addresses formed here, not kept across the K loop)
+    lt = tq * 64 + (lt & 15);
+    auto fold_tile = [&](auto partial, auto pick) {
 #pragma unroll
       for (int bn = 0; bn < 4; ++bn) {
+        floatx4 z[8];
 #pragma unroll
-        for (int bm = 0; bm < 4; ++bm) {
-          // z = (acc * scale of the row) * scale of the token. Register i
-          // of this lane holds row 32 bm + 8 (i / 4) + 4 half + (i % 4) of
-          // the wavefront's 128: its scale sits in lane (row mod 64) of
-          // ws_lo (rows below 64) or of ws_hi.
-          const int src = __float_as_int(bm < 2 ? ws_lo : ws_hi);
-          floatx16 z;
+        for (int bm = 0; bm < 8; ++bm) z[bm] = acc[bm][bn];
+        if constexpr (decltype(pick)::value) pick_sampled(c[bn], z, vw, quad, zy_out + (t0 + lt + bn * 16));
+        fold_column16(c[bn], z, vw, quad, vocab, partial);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    bool mine = false;
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const float w = __int_as_float(
-                __builtin_amdgcn_ds_bpermute((32 * (bm & 1) + 8 * (i >> 2) + 4 * half + (i & 3)) * 4, src));
-            z[i] = (acc_read(acc[bm][bn], i) * w) * hs[bn];
-          }
-          fold_values(c[bn], z, bm, vw, half, vocab, partial);
+    for (int bn = 0; bn < 4; ++bn) {
+      int y = c[bn].y;
+      asm volatile("" : "+v"(y));
+      mine = mine || (unsigned)(y - vw) < 128u;
+    }
+    if (tile * kBV + kBV > vocab) fold_tile(std::true_type{}, std::true_type{});
+    else if (__builtin_amdgcn_ballot_w64(mine) != 0) fold_tile(std::false_type{}, std::true_type{});
+    else fold_tile(std::false_type{}, std::false_type{});
+    if (tile == slice_last_tile) {
+#pragma unroll
+      for (int bn = 0; bn < 4; ++bn) {
+        const int tok = t0 + lt + bn * 16;
+        flush_slice16(c[bn], tok, n_tok, quad, ((size_t)slice * 2 + wv) * n_tok + tok, part);
+      }
+      ++slice;
+      int Sx = S;
+      asm volatile("" : "+s"(Sx));
+      slice_last_tile = slice_tile(slice + 1, n_vt, Sx) - 1;
+    }
+  };
+  run_tiles8<2, kBFar>(smem, L, row_bytes, tile_begin, tile_end, nks, w_rsrc, hr, epilogue, side);
+}
+
+// Decode-shaped FP8 calls (at most kNarrowMaxTokens tokens): 64-token
+// blocks, one workgroup per (token block, slice), the narrow engine's FP8
+// steps (run_tiles_narrow<2>). Lane l of wavefront (wv, wt) holds tokens
+// t0 + 32 wt + 16 bn + (l mod 16) (bn < 2) against the same W rows, with the
+// same MFMA sequence, scales and fold as lmhead_fp8_partial8_kernel, so the
+// partials and logprobs have the same bits. The row scales of up to
+// kNarrowScaleTiles tiles are fetched at a time into two registers per tile
+// (lane l: rows vw + l, vw + 64 + l) and spread to the lanes that need them
+// with ds_bpermute; the first group before the first operand load, so that
+// waiting for them waits for nothing else.
+constexpr int kNarrowScaleTiles = 4;
+
+__global__ __launch_bounds__(kThreads, 1) void lmhead_fp8_partial_narrow_kernel(
+    const uint8_t* __restrict__ Hq, const float* __restrict__ h_scale, const uint8_t* __restrict__ Wq,
+    const float* __restrict__ w_scale, const int32_t* __restrict__ tokens, int n_tok, int d, int vocab, int n_slices,
+    float2* __restrict__ part, float* __restrict__ zy_out) {
+  __shared__ uint4 smem[kEngineSmemChunks];
+  const Lanes L = lanes();
+  const int wv = L.wv, wt = L.wt, quad = L.lane >> 4, c16 = L.lane & 15;
+  const int S = n_slices;
+  const int slice = blockIdx.x % S;
+  const int t0 = (blockIdx.x / S) * kNarrowBRows;
+  const int n_vt = (vocab + kBV - 1) / kBV;
+  const int tile_begin = slice_tile(slice, n_vt, S);
+  const int tile_end = slice_tile(slice + 1, n_vt, S);
+  const int row_bytes = d;
+  const int nks = row_bytes / kStepBytes;
+  Col16 c[2];
+  float hs[2];
+#pragma unroll
+  for (int bn = 0; bn < 2; ++bn) {
+    const int tok = t0 + wt * 32 + bn * 16 + c16;
+    c[bn] = Col16{tok < n_tok ? tokens[tok] : -1, -INFINITY, 0.0f};
+    hs[bn] = tok < n_tok ? h_scale[tok] : 0.0f;
+  }
+  float g_lo[kNarrowScaleTiles], g_hi[kNarrowScaleTiles];
+  // Scales of tiles first .. first + kNarrowScaleTiles - 1 (0 past the
+  // slice or the vocabulary), waited for here.
+  auto load_scales = [&](int first) {
+#pragma unroll
+    for (int j = 0; j < kNarrowScaleTiles; ++j) {
+      const int row = (first + j) * kBV + wv * 128 + L.lane;
+      const bool in = first + j < tile_end;
+      g_lo[j] = in && row < vocab ? w_scale[row] : 0.0f;
+      g_hi[j] = in && row + 64 < vocab ? w_scale[row + 64] : 0.0f;
+    }
+    asm volatile("" ::"v"(g_lo[0]), "v"(g_lo[1]), "v"(g_lo[2]), "v"(g_lo[3]), "v"(g_hi[0]), "v"(g_hi[1]),
+                 "v"(g_hi[2]), "v"(g_hi[3]), "v"(c[0].y), "v"(c[1].y), "v"(hs[0]), "v"(hs[1]));
+  };
+  static_assert(kNarrowScaleTiles == 4, "load_scales waits for four tiles' scales");
+  load_scales(tile_begin);
+
+  auto w_rsrc = [&](int tile) {
+    const int v0 = tile * kBV;
+    return rsrc_words(Wq + (size_t)v0 * row_bytes, (uint32_t)min(kBV, vocab - v0) * row_bytes);
+  };
+  const int4v hr = rsrc_words(Hq + (size_t)t0 * row_bytes, (uint32_t)min(kNarrowBRows, n_tok - t0) * row_bytes);
+  auto epilogue = [&](int tile, floatx4 (&acc)[8][2]) {
+    const int vw = tile * kBV + wv * 128;
+    const int j = (tile - tile_begin) % kNarrowScaleTiles;
+    const float lo = j == 0 ? g_lo[0] : j == 1 ? g_lo[1] : j == 2 ? g_lo[2] : g_lo[3];
+    const float hi = j == 0 ? g_hi[0] : j == 1 ? g_hi[1] : j == 2 ? g_hi[2] : g_hi[3];
+    // Scales of rows 16 bm + 4 quad + i: row r of the 128 sits in lane r of
+    // lo (r < 64) or lane r - 64 of hi.
+    float4 wsc[8];
+#pragma unroll
+    for (int bm = 0; bm < 8; ++bm) {
+      const int src = __float_as_int(bm < 4 ? lo : hi);
+      const int base = (16 * (bm & 3) + 4 * quad) * 4;
+      wsc[bm].x = __int_as_float(__builtin_amdgcn_ds_bpermute(base, src));
+      wsc[bm].y = __int_as_float(__builtin_amdgcn_ds_bpermute(base + 4, src));
+      wsc[bm].z = __int_as_float(__builtin_amdgcn_ds_bpermute(base + 8, src));
+      wsc[bm].w = __int_as_float(__builtin_amdgcn_ds_bpermute(base + 12, src));
+    }
+    auto fold_tile = [&](auto partial) {
+#pragma unroll
+      for (int bn = 0; bn < 2; ++bn) {
+        floatx4 z[8];
+#pragma unroll
+        for (int bm = 0; bm < 8; ++bm) {
+          z[bm] = acc[bm][bn];
+          scale_logits(z[bm], wsc[bm], hs[bn]);
         }
+        pick_sampled(c[bn], z, vw, quad, zy_out + (t0 + wt * 32 + bn * 16 + c16));
+        fold_column16(c[bn], z, vw, quad, vocab, partial);
       }
     };
     if (tile * kBV + kBV > vocab) fold_tile(std::true_type{});
     else fold_tile(std::false_type{});
-    if (tile == slice_last_tile) {
-#pragma unroll
-      for (int bn = 0; bn < 4; ++bn) {
-        const int tok = t0 + wt * 128 + bn * 32 + col;
-        flush_slice(c[bn], tok, n_tok, half, ((size_t)slice * 2 + wv) * n_tok + tok, part);
-      }
-      ++slice;
-      slice_last_tile = slice_tile(slice + 1, n_vt, S) - 1;
-    }
+    // more than kNarrowScaleTiles tiles in the slice (vocabularies above
+    // 256 kNarrowScaleTiles tiles): the next group
+    if (j == kNarrowScaleTiles - 1 && tile + 1 < tile_end) load_scales(tile + 1);
   };
-  run_tiles_f8(smem, L, row_bytes, tile_begin, tile_end, nks, w_rsrc, hr, epilogue, pre);
-
+  run_tiles_narrow<2>(smem, L, row_bytes, tile_begin, tile_end, nks, w_rsrc, hr, epilogue);
 #pragma unroll
-  for (int bn = 0; bn < 4; ++bn)
-    if (c[bn].found) zy_out[t0 + wt * 128 + bn * 32 + col] = c[bn].zy;
+  for (int bn = 0; bn < 2; ++bn) {
+    const int tok = t0 + wt * 32 + bn * 16 + c16;
+    flush_slice16(c[bn], tok, n_tok, quad, ((size_t)slice * 2 + wv) * n_tok + tok, part);
+  }
 }
 
 // ---- MXFP4 weights ("FP8 and MXFP4 weights", same section) ----
@@ -350,15 +475,15 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_mxfp4_partial_kernel(
     if (c[bn].found) zy_out[t0 + wt * 128 + bn * 32 + col] = c[bn].zy;
 }
 
-// Decode-shaped calls (at most kNarrowMaxTokens tokens) on the quantised
-// heads: 64-token blocks, one workgroup per (token block, slice), the narrow
-// engine. Lane l of wavefront (wv, wt) holds token t0 + 32 wt + (l mod 32)
-// against the same W rows, with the same MFMA fragments, scales and fold, as
-// in the wide kernels, so the partials and logprobs have the same bits.
-template <bool kMx4>
-__global__ __launch_bounds__(kThreads, 1) void lmhead_q_partial_narrow_kernel(
-    const uint8_t* __restrict__ Hq, const float* __restrict__ h_scale, const uint8_t* __restrict__ Wq,
-    const void* __restrict__ w_sc, const int32_t* __restrict__ tokens, int n_tok, int d, int vocab, int n_slices,
+// Decode-shaped MXFP4 calls (at most kNarrowMaxTokens tokens): 64-token
+// blocks, one workgroup per (token block, slice), run_tiles_narrow_mx4.
+// Lane l of wavefront (wv, wt) holds token t0 + 32 wt + (l mod 32) against
+// the same W rows, with the same MFMA fragments, scales and fold, as in
+// lmhead_mxfp4_partial_kernel, so the partials and logprobs have the same
+// bits.
+__global__ __launch_bounds__(kThreads, 1) void lmhead_mxfp4_partial_narrow_kernel(
+    const uint8_t* __restrict__ Hq, const float* __restrict__ h_scale, const uint8_t* __restrict__ Wq4,
+    const uint8_t* __restrict__ w_sc, const int32_t* __restrict__ tokens, int n_tok, int d, int vocab, int n_slices,
     float2* __restrict__ part, float* __restrict__ zy_out) {
   __shared__ uint4 smem[kEngineSmemChunks];
   const Lanes L = lanes();
@@ -369,69 +494,38 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_q_partial_narrow_kernel(
   const int n_vt = (vocab + kBV - 1) / kBV;
   const int tile_begin = slice_tile(slice, n_vt, S);
   const int tile_end = slice_tile(slice + 1, n_vt, S);
-  const int w_row_bytes = kMx4 ? d / 2 : d, s_row_bytes = d / 32, h_row_bytes = d;
+  const int w_row_bytes = d / 2, s_row_bytes = d / 32, h_row_bytes = d;
   const int nks = d / 128;
   const int tok = t0 + wt * 32 + col;
   Col c = Col{tok < n_tok ? tokens[tok] : -1, -INFINITY, 0.0f, 0.0f, false};
   const float hs = tok < n_tok ? h_scale[tok] : 0.0f;
   auto w_rsrc = [&](int tile) {
     const int v0 = tile * kBV;
-    return rsrc_words(Wq + (size_t)v0 * w_row_bytes, (uint32_t)min(kBV, vocab - v0) * w_row_bytes);
+    return rsrc_words(Wq4 + (size_t)v0 * w_row_bytes, (uint32_t)min(kBV, vocab - v0) * w_row_bytes);
   };
   auto s_rsrc = [&](int tile) {
     const int v0 = tile * kBV;
-    return rsrc_words(static_cast<const uint8_t*>(w_sc) + (size_t)v0 * s_row_bytes,
-                      (uint32_t)min(kBV, vocab - v0) * s_row_bytes);
+    return rsrc_words(w_sc + (size_t)v0 * s_row_bytes, (uint32_t)min(kBV, vocab - v0) * s_row_bytes);
   };
   const int4v hr =
       rsrc_words(Hq + (size_t)t0 * h_row_bytes, (uint32_t)min(kNarrowBRows, n_tok - t0) * h_row_bytes);
-  // FP8: per-row float scales, fetched in each tile's last K step and spread
-  // to lanes as in the wide kernel (lane l: rows vw + l, vw + 64 + l).
-  const int4v ws_words = rsrc_words(w_sc, kMx4 ? 0u : (uint32_t)vocab * 4u);
-  float ws_lo = 0.0f, ws_hi = 0.0f;
-  auto pre = [&](int tile) {
-    if constexpr (!kMx4) {
-      const uint32_t off = (uint32_t)(tile * kBV + wv * 128 + L.lane) * 4u;
-      const uint32_t off_hi = off + 256u;
-      const int4v r = {__builtin_amdgcn_readfirstlane(ws_words[0]), __builtin_amdgcn_readfirstlane(ws_words[1]),
-                       __builtin_amdgcn_readfirstlane(ws_words[2]), __builtin_amdgcn_readfirstlane(ws_words[3])};
-      asm volatile(
-          "buffer_load_dword %0, %2, %4, 0 offen\n\t"
-          "buffer_load_dword %1, %3, %4, 0 offen"
-          : "=&v"(ws_lo), "=&v"(ws_hi)
-          : "v"(off), "v"(off_hi), "s"(r)
-          : "memory");
-    }
-  };
   auto epilogue = [&](int tile, floatx16 (&acc)[4]) {
     const int vw = tile * kBV + wv * 128;
-    if constexpr (!kMx4)
-      asm volatile("s_waitcnt vmcnt(%2)" : "+v"(ws_lo), "+v"(ws_hi) : "n"(kNarrowQLoadsAfterPre<false>) : "memory");
     mfma_result_wait();
     auto fold_tile = [&](auto partial) {
 #pragma unroll
       for (int bm = 0; bm < 4; ++bm) {
         floatx16 z;
-        if constexpr (kMx4) {
 #pragma unroll
-          for (int i = 0; i < 16; ++i) z[i] = acc_read(acc[bm], i) * hs;
-        } else {
-          const int src = __float_as_int(bm < 2 ? ws_lo : ws_hi);
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const float w = __int_as_float(
-                __builtin_amdgcn_ds_bpermute((32 * (bm & 1) + 8 * (i >> 2) + 4 * half + (i & 3)) * 4, src));
-            z[i] = (acc_read(acc[bm], i) * w) * hs;
-          }
-        }
+        for (int i = 0; i < 16; ++i) z[i] = acc_read(acc[bm], i) * hs;
         fold_values(c, z, bm, vw, half, vocab, partial);
       }
     };
     if (tile * kBV + kBV > vocab) fold_tile(std::true_type{});
     else fold_tile(std::false_type{});
   };
-  run_tiles_narrow_q<kMx4>(smem, L, w_row_bytes, s_row_bytes, h_row_bytes, tile_begin, tile_end, nks, w_rsrc, s_rsrc,
-                           hr, epilogue, pre);
+  run_tiles_narrow_mx4(smem, L, w_row_bytes, s_row_bytes, h_row_bytes, tile_begin, tile_end, nks, w_rsrc, s_rsrc, hr,
+                       epilogue);
   flush_slice(c, tok, n_tok, half, ((size_t)slice * 2 + wv) * n_tok + tok, part);
   if (c.found) zy_out[tok] = c.zy;
 }
@@ -457,16 +551,20 @@ hipError_t launch_lmhead_logprob_fp8(const uint8_t* Hq, const float* h_scale, co
   float2* part = static_cast<float2*>(workspace);
   float* zy = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                        align256((size_t)2 * S * (size_t)n_tok * sizeof(float2)));
-  // The wide kernel needs two K steps of 128 values (d >= 256); the narrow
-  // kernel gives the same bits and takes any number of token blocks.
-  if (n_tok <= kNarrowMaxTokens || d < kF8WideMinD) {
+  if (n_tok <= kNarrowMaxTokens) {
     const dim3 grid((unsigned)ceil_div(n_tok, kNarrowBRows) * (unsigned)S);
-    hipLaunchKernelGGL(lmhead_q_partial_narrow_kernel<false>, grid, dim3(kThreads), 0, stream, Hq, h_scale, Wq,
-                       static_cast<const void*>(w_scale), tokens, n_tok, d, vocab, S, part, zy);
+    hipLaunchKernelGGL(lmhead_fp8_partial_narrow_kernel, grid, dim3(kThreads), 0, stream, Hq, h_scale, Wq, w_scale,
+                       tokens, n_tok, d, vocab, S, part, zy);
   } else {
     const dim3 grid((unsigned)ntb * (unsigned)n_slice_groups(n_tok, vocab));
-    hipLaunchKernelGGL(lmhead_fp8_partial_kernel, grid, dim3(kThreads), 0, stream, Hq, h_scale, Wq, w_scale, tokens,
-                       n_tok, d, vocab, ntb, S, G, part, zy);
+    // Long K loops stage the token block two K steps ahead, as in the bf16
+    // head (the load order changes no arithmetic).
+    if (d / kStepBytes > kNearBMaxSteps)
+      hipLaunchKernelGGL((lmhead_fp8_partial8_kernel<true>), grid, dim3(kThreads8), 0, stream, Hq, h_scale, Wq,
+                         w_scale, tokens, n_tok, d, vocab, ntb, S, G, part, zy);
+    else
+      hipLaunchKernelGGL((lmhead_fp8_partial8_kernel<false>), grid, dim3(kThreads8), 0, stream, Hq, h_scale, Wq,
+                         w_scale, tokens, n_tok, d, vocab, ntb, S, G, part, zy);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -499,8 +597,8 @@ hipError_t launch_lmhead_logprob_mxfp4(const uint8_t* Hq, const float* h_scale, 
                                        align256((size_t)2 * S * (size_t)n_tok * sizeof(float2)));
   if (n_tok <= kNarrowMaxTokens) {
     const dim3 grid((unsigned)ceil_div(n_tok, kNarrowBRows) * (unsigned)S);
-    hipLaunchKernelGGL(lmhead_q_partial_narrow_kernel<true>, grid, dim3(kThreads), 0, stream, Hq, h_scale, Wq4,
-                       static_cast<const void*>(w_sc), tokens, n_tok, d, vocab, S, part, zy);
+    hipLaunchKernelGGL(lmhead_mxfp4_partial_narrow_kernel, grid, dim3(kThreads), 0, stream, Hq, h_scale, Wq4, w_sc,
+                       tokens, n_tok, d, vocab, S, part, zy);
   } else {
     const dim3 grid((unsigned)ntb * (unsigned)n_slice_groups(n_tok, vocab));
     hipLaunchKernelGGL(lmhead_mxfp4_partial_kernel, grid, dim3(kThreads), 0, stream, Hq, h_scale, Wq4, w_sc, tokens,

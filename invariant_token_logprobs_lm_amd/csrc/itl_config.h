@@ -14,8 +14,8 @@
 
 namespace itl {
 
-constexpr int kThreads = 256;        // 4 wavefronts of 64 lanes (narrow and FP8 engines)
-constexpr int kThreads8 = 512;       // 8 wavefronts (the bf16 / fp32 wide engine)
+constexpr int kThreads = 256;        // 4 wavefronts of 64 lanes (narrow and MXFP4 engines)
+constexpr int kThreads8 = 512;       // 8 wavefronts (the bf16 / fp32 / FP8 wide engine)
 constexpr int kBT = 256;             // tokens per block (MFMA B operand)
 constexpr int kBV = 256;             // vocabulary rows per tile (MFMA A operand)
 constexpr int kStepBytes = 128;      // bytes of one operand row per K step (64 bf16 / 32 fp32)
@@ -34,7 +34,6 @@ constexpr int kNearBMaxSteps = 48;   // load schedule only: K loops longer than 
                                      // two K steps ahead (eight-wavefront forward at 65,536 tokens, same bits:
                                      // 64 steps (d = 4096) 2-3 % faster; 112 and 40 steps within 1 % either way)
 constexpr int kDMultiple = 64;       // d must be a multiple of this
-constexpr int kF8WideMinD = 256;     // the wide FP8 kernel needs two K steps of 128 values; smaller d runs narrow
 
 // REINFORCE Zero loss. A response is cut into segments of kSegTokens tokens
 // counted from its first token; a segment is summed by one of three trees

@@ -1,17 +1,18 @@
 // Tile engines (gfx950 / CDNA4): the pieces every contraction of the
 // library shares (MFMA steps, LDS slots and swizzle, direct-to-LDS loads,
 // waits) and the four-wavefront K loops: the narrow one for decode-shaped
-// calls and the FP8 / MXFP4 ones. The bf16 / fp32 wide contractions (the
+// calls and the MXFP4 ones. The bf16 / fp32 / FP8 wide contractions (the
 // forward and the backward) run on the eight-wavefront loop of
 // tile_engine8.h, which uses the same slots, swizzle and per-block MFMA
 // sequence as the narrow loop.
 //
-// bf16 / fp32 blocks are 16 x 16 (Mma16): in sub-step kk (0, 1) of a
-// 128-byte K step lane l supplies row (l mod 16) of an A block and of a B
-// block with logical 16-byte chunk 4 kk + lane_chunk(l / 16); accumulator
-// register i of lane l holds A row 4 (l / 16) + i against B row (l mod 16).
+// bf16 / fp32 / FP8 blocks are 16 x 16: in sub-step kk (0, 1) of a 128-byte
+// K step (Mma16; FP8: the two halves of one mma_f8_16 instruction) lane l
+// supplies row (l mod 16) of an A block and of a B block with logical
+// 16-byte chunk 4 kk + lane_chunk(l / 16); accumulator register i of lane l
+// holds A row 4 (l / 16) + i against B row (l mod 16).
 //
-// FP8 / MXFP4 geometry: a 256-thread workgroup (2 x 2 wavefronts)
+// MXFP4 geometry: a 256-thread workgroup (2 x 2 wavefronts)
 // multiplies 256-row tiles of an operand A, walked in order, with one fixed
 // 256-row block of an operand B: acc = A_tile B^T (both row-major and
 // K-contiguous, fp32 accumulate, K ascending in steps of 128 bytes). After
@@ -57,6 +58,24 @@ struct Mma16<1> {  // fp32: 4 elements per lane; instruction j takes element j (
     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w), __uint_as_float(b.w), acc, 0, 0, 0);
   }
 };
+
+// A 32-byte FP8 fragment: two 16-byte chunks of one lane.
+struct Frag8 {
+  uint4 lo, hi;
+};
+
+typedef int intx8 __attribute__((ext_vector_type(8)));
+
+// v_mfma_scale_f32_16x16x128_f8f6f4, both operands E4M3, block scales 1
+// (E8M0 127): acc += one 16 x 16 block over a whole 128-value K step, lane l
+// supplying 32 values of row (l mod 16) of each operand. The instruction
+// sums its 128 products as one dot product whatever K values sit in which
+// lane (A and B use the same placement), so the result is
+// sum_k A[r, k] B[c, k] in a fixed order.
+__device__ __forceinline__ void mma_f8_16(floatx4& acc, const Frag8& a, const Frag8& b) {
+  acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(__builtin_bit_cast(intx8, a), __builtin_bit_cast(intx8, b),
+                                                         acc, 0, 0, 0, 127, 0, 127);
+}
 
 // LDS slots hold one K step of one operand: 256 rows x 128 bytes (8 chunks
 // of 16 bytes), so that every global load moves whole 128-byte lines. Five
@@ -296,12 +315,21 @@ __device__ __forceinline__ void run_tiles_narrow(uint4* smem, const Lanes& L, in
       for (int n = 0; n < 2; ++n) B[kk][n] = sb[b_off[kk] + n * 16 * kRowChunks];
     }
     __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
+    if constexpr (kDtype == 2) {
+      // FP8: one instruction per block and step, on the two halves' chunks
+      // (the fragments of run_tiles8's FP8 schedule)
 #pragma unroll
       for (int m = 0; m < 8; ++m)
 #pragma unroll
-        for (int n = 0; n < 2; ++n) Mma16<kDtype>::step(acc[m][n], A[kk][m], B[kk][n]);
+        for (int n = 0; n < 2; ++n) mma_f8_16(acc[m][n], Frag8{A[0][m], A[1][m]}, Frag8{B[0][n], B[1][n]});
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+#pragma unroll
+          for (int n = 0; n < 2; ++n) Mma16<kDtype>::step(acc[m][n], A[kk][m], B[kk][n]);
+    }
     slot = slot == kNarrowSlots - 1 ? 0 : slot + 1;
   };
   for (int tile = tile_begin; tile < tile_end; ++tile) {
@@ -313,205 +341,6 @@ __device__ __forceinline__ void run_tiles_narrow(uint4* smem, const Lanes& L, in
       for (int n = 0; n < 2; ++n) acc[m][n] = floatx4{};
     for (int ks = 0; ks < nks; ++ks) k_step(acc);
     epi(tile, acc);
-  }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-}
-
-// FP8 (E4M3) wide engine, in the four-wavefront geometry above (each
-// wavefront 128 x 128 of the 256 x 256 tile as 4 x 4 blocks): the five
-// slots, swizzle and direct-to-LDS loads above, one barrier per K step, with v_mfma_scale_f32_32x32x64_f8f6f4 (both operands
-// E4M3, block scales 1). A 128-byte K step is 128 values: two sub-steps of
-// 64, each MFMA taking 32 bytes per lane (lane half h of sub-step j: chunks
-// 4 j + 2 h and 4 j + 2 h + 1 of its row, i.e. 32 consecutive K values).
-// The instruction sums its 64 products as one dot product whatever order
-// the K values sit in the lanes (A and B use the same placement), so the
-// result is sum_k A[r, k] B[c, k]; the K order of the accumulation is fixed.
-struct Frag8 {
-  uint4 lo, hi;
-};
-
-typedef int intx8 __attribute__((ext_vector_type(8)));
-
-__device__ __forceinline__ void mma_f8(floatx16& acc, const Frag8& a, const Frag8& b) {
-  acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(__builtin_bit_cast(intx8, a), __builtin_bit_cast(intx8, b),
-                                                        acc, 0, 0, 0, 127, 0, 127);
-}
-__device__ __forceinline__ void mma_f8_first(floatx16& acc, const Frag8& a, const Frag8& b) {
-  acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(__builtin_bit_cast(intx8, a), __builtin_bit_cast(intx8, b),
-                                                        floatx16{}, 0, 0, 0, 127, 0, 127);
-}
-
-//
-// pre(t) is called in tile t's last K step after its barrier, before the
-// step's kF8LoadsAfterPre loads (H(g + 2), W(g + 3)) are issued: loads it
-// issues there complete before the epilogue once the epilogue waits for
-// vmcnt(kF8LoadsAfterPre).
-// Needs nks >= 2 (a tile's first and last K steps are distinct code: one
-// path for both would cost the register allocation of the whole loop).
-constexpr int kF8LoadsAfterPre = 2 * kDmaPerWave;
-
-template <class ARsrc, class Epi, class Pre>
-__device__ __forceinline__ void run_tiles_f8(uint4* smem, const Lanes& L, int row_bytes, int tile_begin, int tile_end,
-                                             int nks, const ARsrc& a_rsrc, int4v b_rsrc, Epi&& epi, Pre&& pre) {
-  const int lane = L.lane, wave = L.wave, wv = L.wv, wt = L.wt, half = L.half, col = L.col;
-  const int lr = lane >> 3;
-  uint32_t voff[kDmaPerWave];
-#pragma unroll
-  for (int j = 0; j < kDmaPerWave; ++j)
-    voff[j] = (uint32_t)(wave * 64 + j * kDmaRows + lr) * (uint32_t)row_bytes + (((lane & 7) ^ lr ^ (j & 1)) * 16);
-  const uint32_t lds_wave =
-      (uint32_t)(size_t)((__attribute__((address_space(3))) uint4*)smem) + wave * 64 * kStepBytes;
-  const int4v hr = b_rsrc;
-  auto w_slot_lds = [&](int slot) { return lds_wave + (uint32_t)slot * kSlotBytes; };
-  auto h_slot_lds = [&](int slot) { return lds_wave + (uint32_t)(kWSlots + slot) * kSlotBytes; };
-
-  // Fragment reads: sub-step j, piece p (0 = low 16 bytes, 1 = high) of
-  // lane (half, col) is logical chunk 4 j + 2 half + p of row col.
-  int a_off[2][2], b_off[2][2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j)
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const int pc = (4 * j + 2 * half + p) ^ swz(col);
-      a_off[j][p] = (wv * 128 + col) * kRowChunks + pc;
-      b_off[j][p] = (wt * 128 + col) * kRowChunks + pc;
-    }
-
-  int w_tile = tile_begin, w_ks = 0;
-  int h_ks = 0;
-  int w_slot_next = 0, h_slot_next = 0;
-  auto next_w = [&]() {
-    if (++w_ks == nks) {
-      w_ks = 0;
-      w_tile = min(w_tile + 1, tile_end - 1);
-    }
-    w_slot_next = w_slot_next == kWSlots - 1 ? 0 : w_slot_next + 1;
-  };
-  auto next_h = [&]() {
-    h_ks = h_ks + 1 == nks ? 0 : h_ks + 1;
-    h_slot_next ^= 1;
-  };
-  // One sub-step: MFMA q (q = 4 bm + bn) on (A, B), interleaved with the 16
-  // reads of the next sub-step's fragments (order A0 B0 B1 B2 B3 A1 A2 A3,
-  // low then high half) from slots (wsl, hsl), sub-step rj: one per MFMA, or
-  // two per MFMA in the first 8 when kFront (they must land before the
-  // barrier). With kDma, the 8 loads of H(g + 2) and then the 8 of W(g + 3)
-  // go one per MFMA.
-  auto phase = [&](floatx16 (&acc)[4][4], const Frag8 (&A)[4], const Frag8 (&B)[4], auto first, auto front,
-                   auto dma, auto do_read, int wsl, int hsl, int rj, Frag8 (&RA)[4], Frag8 (&RB)[4]) {
-    const uint4* sa = smem + wsl * kSlotChunks;
-    const uint4* sb = smem + (kWSlots + hsl) * kSlotChunks;
-    int4v wr;
-    uint32_t wsoff = 0, hsoff = 0, wm = 0, hm = 0;
-    if constexpr (decltype(dma)::value) {
-      wr = a_rsrc(w_tile);
-      wsoff = (uint32_t)w_ks * kStepBytes;
-      hsoff = (uint32_t)h_ks * kStepBytes;
-      wm = w_slot_lds(w_slot_next);
-      hm = h_slot_lds(h_slot_next);
-    }
-    auto read = [&](int r) {  // read number r = 0..15 of the next sub-step
-      const int f = r >> 1, p = r & 1;
-      if (f == 0) (p ? RA[0].hi : RA[0].lo) = sa[a_off[rj][p]];
-      else if (f <= 4) (p ? RB[f - 1].hi : RB[f - 1].lo) = sb[b_off[rj][p] + (f - 1) * 32 * kRowChunks];
-      else (p ? RA[f - 4].hi : RA[f - 4].lo) = sa[a_off[rj][p] + (f - 4) * 32 * kRowChunks];
-    };
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      if constexpr (decltype(first)::value) mma_f8_first(acc[q >> 2][q & 3], A[q >> 2], B[q & 3]);
-      else mma_f8(acc[q >> 2][q & 3], A[q >> 2], B[q & 3]);
-      if constexpr (!decltype(do_read)::value) {
-      } else if constexpr (decltype(front)::value) {
-        if (q < 8) {
-          read(2 * q);
-          read(2 * q + 1);
-        }
-      } else {
-        read(q);
-      }
-      if constexpr (decltype(dma)::value) {
-        if (q < 8) dma16(hr, voff[q], hsoff, hm + q * 1024);
-        else dma16(wr, voff[q - 8], wsoff, wm + (q - 8) * 1024);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    if constexpr (decltype(dma)::value) {
-      next_h();
-      next_w();
-    }
-  };
-
-  using T = std::true_type;
-  using F = std::false_type;
-  {
-    const int4v wr0 = a_rsrc(w_tile);
-#pragma unroll
-    for (int j = 0; j < kDmaPerWave; ++j) dma16(wr0, voff[j], (uint32_t)w_ks * kStepBytes, w_slot_lds(0) + j * 1024);
-#pragma unroll
-    for (int j = 0; j < kDmaPerWave; ++j) dma16(hr, voff[j], 0, h_slot_lds(0) + j * 1024);
-    next_w();
-    next_h();
-    const int4v wr1 = a_rsrc(w_tile);
-#pragma unroll
-    for (int j = 0; j < kDmaPerWave; ++j) dma16(wr1, voff[j], (uint32_t)w_ks * kStepBytes, w_slot_lds(1) + j * 1024);
-    next_w();
-  }
-  wait_and_barrier<kDmaPerWave>();  // W(0), H(0) landed
-  {
-    const int4v wr = a_rsrc(w_tile);
-    const uint32_t hm = h_slot_lds(h_slot_next), wm = w_slot_lds(w_slot_next);
-#pragma unroll
-    for (int j = 0; j < kDmaPerWave; ++j) dma16(hr, voff[j], (uint32_t)h_ks * kStepBytes, hm + j * 1024);
-#pragma unroll
-    for (int j = 0; j < kDmaPerWave; ++j) dma16(wr, voff[j], (uint32_t)w_ks * kStepBytes, wm + j * 1024);
-    next_h();
-    next_w();
-  }
-  // X: the current sub-step's fragments, Y: the next one's.
-  Frag8 xa[4], xb[4], ya[4], yb[4];
-  {
-    const uint4* sa = smem;
-    const uint4* sb = smem + kWSlots * kSlotChunks;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      xa[m].lo = sa[a_off[0][0] + m * 32 * kRowChunks];
-      xa[m].hi = sa[a_off[0][1] + m * 32 * kRowChunks];
-      xb[m].lo = sb[b_off[0][0] + m * 32 * kRowChunks];
-      xb[m].hi = sb[b_off[0][1] + m * 32 * kRowChunks];
-    }
-  }
-  int wslot = 0, hslot = 0;
-  // One K step g: sub-step 0 (X) while sub-step 1 is read into Y; the
-  // barrier then publishes step g + 1 (step g is all in registers, so its
-  // slots are free); sub-step 1 (Y) while step g + 1's sub-step 0 is read
-  // into X and H(g + 2), W(g + 3) are loaded into step g's slots.
-  // A tile's last step (kLast) calls pre and leaves X unread: X is read
-  // after the epilogue, where its registers are free.
-  auto k_step = [&](floatx16 (&acc)[4][4], int tile, auto first, auto last) {
-    using R = std::integral_constant<bool, !decltype(last)::value>;
-    phase(acc, xa, xb, first, T{}, F{}, T{}, wslot, hslot, 1, ya, yb);
-    wait_and_barrier<kDmaPerWave>();  // W(g + 1), H(g + 1) landed; W(g + 2) may still be in flight
-    wslot = wslot == kWSlots - 1 ? 0 : wslot + 1;
-    hslot ^= 1;
-    if constexpr (decltype(last)::value) pre(tile);
-    phase(acc, ya, yb, F{}, F{}, T{}, R{}, wslot, hslot, 0, xa, xb);
-  };
-  for (int tile = tile_begin; tile < tile_end; ++tile) {
-    floatx16 acc[4][4];
-    k_step(acc, tile, T{}, F{});
-    for (int ks = 2; ks < nks; ++ks) k_step(acc, tile, F{}, F{});
-    k_step(acc, tile, F{}, T{});
-    epi(tile, acc);
-    const uint4* sa = smem + wslot * kSlotChunks;
-    const uint4* sb = smem + (kWSlots + hslot) * kSlotChunks;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      xa[m].lo = sa[a_off[0][0] + m * 32 * kRowChunks];
-      xa[m].hi = sa[a_off[0][1] + m * 32 * kRowChunks];
-      xb[m].lo = sb[b_off[0][0] + m * 32 * kRowChunks];
-      xb[m].hi = sb[b_off[0][1] + m * 32 * kRowChunks];
-    }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
@@ -530,7 +359,8 @@ __device__ __forceinline__ void run_tiles_f8(uint4* smem, const Lanes& L, int ro
 //
 // LDS: W slots of 256 rows x 64 bytes (chunk c of row r at c ^ ((r >> 1) & 3)
 // so that 8 consecutive rows at one chunk hit distinct 16-byte bank groups)
-// followed by the slot's 256 x 4 scale bytes; H slots as in run_tiles_f8.
+// followed by the slot's 256 x 4 scale bytes; H slots of 256 rows x 128 bytes as in the
+// other engines.
 constexpr int kMx4RowChunks = 4;                        // 64-byte W rows
 constexpr int kMx4WDataBytes = kBV * 64;                // 16 KiB
 constexpr int kMx4WSlotBytes = kMx4WDataBytes + kBV * 4;  // + 1 KiB of scales
@@ -580,7 +410,7 @@ __device__ __forceinline__ void run_tiles_mx4(uint4* smem, const Lanes& L, int w
                                               const ARsrc& a_rsrc, const SRsrc& s_rsrc, int4v b_rsrc, Epi&& epi) {
   const int lane = L.lane, wave = L.wave, wv = L.wv, wt = L.wt, half = L.half, col = L.col;
   const int lr = lane >> 3;
-  // H loads (as in run_tiles_f8): rows 64 wave + 8 j + lane / 8.
+  // H loads: rows 64 wave + 8 j + lane / 8, logical chunk (lane % 8) ^ swz(row).
   uint32_t hvoff[kDmaPerWave];
 #pragma unroll
   for (int j = 0; j < kDmaPerWave; ++j)
@@ -735,42 +565,28 @@ __device__ __forceinline__ void run_tiles_mx4(uint4* smem, const Lanes& L, int w
   __syncthreads();
 }
 
-// Narrow variants of run_tiles_f8 (kMx4 = false: E4M3 W) and run_tiles_mx4
-// (kMx4 = true: MXFP4 W) for decode-shaped calls: the same W tiles against
-// a 64-row block of E4M3 token rows, wavefront (wv, wt) = 128 W rows x 32
-// token rows. Every MFMA of an accumulator takes the same fragments (and
-// scale bytes), in the same order, as in the wide engine (same W slot
-// layout and swizzle, same H chunk choice, same sub-step order), so each
-// output element has the same bits. Both operands rotate through 4 slots,
-// loaded three K steps ahead; all of a step's fragments are read up front.
-// pre(t) is called in tile t's last K step after its barrier, before the
-// step's loads (kNarrowQLoadsAfterPre<kMx4> of them) are issued; the
-// epilogue may wait for pre's loads with vmcnt(that count).
-template <bool kMx4>
-constexpr int kNarrowQLoadsAfterPre = (kMx4 ? kMx4WDataLoads + 1 : kDmaPerWave) + kNarrowBDmaPerWave;
-
-template <bool kMx4, class ARsrc, class SRsrc, class Epi, class Pre>
-__device__ __forceinline__ void run_tiles_narrow_q(uint4* smem, const Lanes& L, int w_row_bytes, int s_row_bytes,
-                                                   int h_row_bytes, int tile_begin, int tile_end, int nks,
-                                                   const ARsrc& a_rsrc, const SRsrc& s_rsrc, int4v b_rsrc,
-                                                   Epi&& epi, Pre&& pre) {
+// Narrow variant of run_tiles_mx4 for decode-shaped calls: the same W tiles
+// against a 64-row block of E4M3 token rows, wavefront (wv, wt) = 128 W rows
+// x 32 token rows. Every MFMA of an accumulator takes the same fragments and
+// scale bytes, in the same order, as in the wide engine (same W slot layout
+// and swizzle, same H chunk choice, same sub-step order), so each output
+// element has the same bits. Both operands rotate through 4 slots, loaded
+// three K steps ahead; all of a step's fragments are read up front.
+template <class ARsrc, class SRsrc, class Epi>
+__device__ __forceinline__ void run_tiles_narrow_mx4(uint4* smem, const Lanes& L, int w_row_bytes, int s_row_bytes,
+                                                     int h_row_bytes, int tile_begin, int tile_end, int nks,
+                                                     const ARsrc& a_rsrc, const SRsrc& s_rsrc, int4v b_rsrc,
+                                                     Epi&& epi) {
   const int lane = L.lane, wave = L.wave, wv = L.wv, wt = L.wt, half = L.half, col = L.col;
   const int lr = lane >> 3;
-  constexpr int kWSlotBytes = kMx4 ? kMx4WSlotBytes : kSlotBytes;
-  constexpr int kWLoads = kMx4 ? kMx4WDataLoads : kDmaPerWave;      // W code loads per wavefront per step
-  constexpr int kLoads = kWLoads + (kMx4 ? 1 : 0) + kNarrowBDmaPerWave;
-  static_assert(kLoads == kNarrowQLoadsAfterPre<kMx4>, "loads per step");
-  constexpr int kHBase = kNarrowSlots * kWSlotBytes;
+  constexpr int kLoads = kMx4WDataLoads + 1 + kNarrowBDmaPerWave;  // loads per wavefront per step
+  constexpr int kHBase = kNarrowSlots * kMx4WSlotBytes;
   static_assert(kHBase + kNarrowSlots * kNarrowBSlotChunks * 16 <= kEngineSmemChunks * 16, "LDS budget");
-  uint32_t wvoff[kWLoads];
+  uint32_t wvoff[kMx4WDataLoads];
 #pragma unroll
-  for (int j = 0; j < kWLoads; ++j) {
-    if constexpr (kMx4) {
-      const int row = wave * 64 + j * 16 + (lane >> 2);
-      wvoff[j] = (uint32_t)row * (uint32_t)w_row_bytes + (uint32_t)(((lane & 3) ^ swz4(row)) * 16);
-    } else {
-      wvoff[j] = (uint32_t)(wave * 64 + j * kDmaRows + lr) * (uint32_t)w_row_bytes + (((lane & 7) ^ lr ^ (j & 1)) * 16);
-    }
+  for (int j = 0; j < kMx4WDataLoads; ++j) {
+    const int row = wave * 64 + j * 16 + (lane >> 2);
+    wvoff[j] = (uint32_t)row * (uint32_t)w_row_bytes + (uint32_t)(((lane & 3) ^ swz4(row)) * 16);
   }
   const uint32_t svoff = (uint32_t)(wave * 64 + lane) * (uint32_t)s_row_bytes;
   uint32_t hvoff[kNarrowBDmaPerWave];
@@ -778,18 +594,18 @@ __device__ __forceinline__ void run_tiles_narrow_q(uint4* smem, const Lanes& L, 
   for (int j = 0; j < kNarrowBDmaPerWave; ++j)
     hvoff[j] = (uint32_t)(wave * 16 + j * kDmaRows + lr) * (uint32_t)h_row_bytes + (((lane & 7) ^ lr ^ (j & 1)) * 16);
   const uint32_t lds0 = (uint32_t)(size_t)((__attribute__((address_space(3))) uint4*)smem);
-  auto w_slot = [&](int slot) { return lds0 + (uint32_t)slot * kWSlotBytes; };
+  auto w_slot = [&](int slot) { return lds0 + (uint32_t)slot * kMx4WSlotBytes; };
   auto h_slot = [&](int slot) { return lds0 + (uint32_t)kHBase + (uint32_t)slot * kNarrowBSlotChunks * 16; };
-  constexpr uint32_t kWStepBytes = kMx4 ? 64 : kStepBytes;  // W bytes per row per K step
+  constexpr uint32_t kWStepBytes = 64;  // W bytes per row per K step
   auto load_step = [&](int tile, int ks, int slot) {
     const int4v ar = a_rsrc(tile);
 #pragma unroll
     for (int j = 0; j < kNarrowBDmaPerWave; ++j)
       dma16(b_rsrc, hvoff[j], (uint32_t)ks * kStepBytes, h_slot(slot) + (uint32_t)wave * 16 * kStepBytes + j * 1024);
 #pragma unroll
-    for (int j = 0; j < kWLoads; ++j)
+    for (int j = 0; j < kMx4WDataLoads; ++j)
       dma16(ar, wvoff[j], (uint32_t)ks * kWStepBytes, w_slot(slot) + (uint32_t)wave * 64 * kWStepBytes + j * 1024);
-    if constexpr (kMx4) dma4(s_rsrc(tile), svoff, (uint32_t)ks * 4, w_slot(slot) + kMx4WDataBytes + (uint32_t)wave * 256);
+    dma4(s_rsrc(tile), svoff, (uint32_t)ks * 4, w_slot(slot) + kMx4WDataBytes + (uint32_t)wave * 256);
   };
   int ld_tile = tile_begin, ld_ks = 0;
   auto next_load = [&]() {
@@ -804,62 +620,44 @@ __device__ __forceinline__ void run_tiles_narrow_q(uint4* smem, const Lanes& L, 
     load_step(ld_tile, ld_ks, p);
     next_load();
   }
-  // Fragment offsets (uint4 units from a slot's base), as in the wide engines.
-  int a_off[2][2], b_off[2][2];
+  // Fragment offsets (uint4 units from a slot's base), as in run_tiles_mx4.
+  int a_off[2], b_off[2][2];
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+  for (int j = 0; j < 2; ++j) {
+    const int ra = wv * 128 + col;
+    a_off[j] = ra * kMx4RowChunks + ((2 * j + half) ^ swz4(ra));
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      if constexpr (kMx4) {
-        const int ra = wv * 128 + col;
-        a_off[j][p] = ra * kMx4RowChunks + ((2 * j + half) ^ swz4(ra));  // p unused: one chunk per fragment
-        b_off[j][p] = (wt * 32 + col) * kRowChunks + ((4 * j + 2 * p + half) ^ swz(col));
-      } else {
-        const int pc = (4 * j + 2 * half + p) ^ swz(col);
-        a_off[j][p] = (wv * 128 + col) * kRowChunks + pc;
-        b_off[j][p] = (wt * 32 + col) * kRowChunks + pc;
-      }
-    }
+    for (int p = 0; p < 2; ++p) b_off[j][p] = (wt * 32 + col) * kRowChunks + ((4 * j + 2 * p + half) ^ swz(col));
+  }
   constexpr int kPending = (kNarrowSlots - 2) * kLoads;
-  constexpr int kARowChunks = kMx4 ? kMx4RowChunks : kRowChunks;
   int slot = 0;
-  auto k_step = [&](floatx16 (&acc)[4], int tile, auto first, auto last) {
+  auto k_step = [&](floatx16 (&acc)[4], auto first) {
     wait_and_barrier<kPending>();
-    if constexpr (decltype(last)::value) pre(tile);
     load_step(ld_tile, ld_ks, slot == 0 ? kNarrowSlots - 1 : slot - 1);
     next_load();
-    const uint4* sa = smem + (slot * kWSlotBytes) / 16;
+    const uint4* sa = smem + (slot * kMx4WSlotBytes) / 16;
     const uint4* sb = smem + (kHBase + slot * kNarrowBSlotChunks * 16) / 16;
-    Frag8 A[2][4], B[2];
+    uint4 A[2][4];
+    Frag8 B[2];
     uint32_t SC[4];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        A[j][m].lo = sa[a_off[j][0] + m * 32 * kARowChunks];
-        if constexpr (!kMx4) A[j][m].hi = sa[a_off[j][1] + m * 32 * kARowChunks];
-      }
+      for (int m = 0; m < 4; ++m) A[j][m] = sa[a_off[j] + m * 32 * kMx4RowChunks];
       B[j].lo = sb[b_off[j][0]];
       B[j].hi = sb[b_off[j][1]];
     }
-    if constexpr (kMx4) {
-      const uint32_t* ss = reinterpret_cast<const uint32_t*>(smem) + (slot * kWSlotBytes + kMx4WDataBytes) / 4;
+    const uint32_t* ss = reinterpret_cast<const uint32_t*>(smem) + (slot * kMx4WSlotBytes + kMx4WDataBytes) / 4;
 #pragma unroll
-      for (int m = 0; m < 4; ++m) SC[m] = ss[wv * 128 + m * 32 + col];
-    }
+    for (int m = 0; m < 4; ++m) SC[m] = ss[wv * 128 + m * 32 + col];
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        if constexpr (kMx4) {
-          const int sbyte = (int)((SC[m] >> (8 * (2 * j + half))) & 0xffu);
-          if (decltype(first)::value && j == 0) mma_mx4_first(acc[m], A[j][m].lo, B[j], sbyte);
-          else mma_mx4(acc[m], A[j][m].lo, B[j], sbyte);
-        } else {
-          if (decltype(first)::value && j == 0) mma_f8_first(acc[m], A[j][m], B[j]);
-          else mma_f8(acc[m], A[j][m], B[j]);
-        }
+        const int sbyte = (int)((SC[m] >> (8 * (2 * j + half))) & 0xffu);
+        if (decltype(first)::value && j == 0) mma_mx4_first(acc[m], A[j][m], B[j], sbyte);
+        else mma_mx4(acc[m], A[j][m], B[j], sbyte);
       }
     slot = slot == kNarrowSlots - 1 ? 0 : slot + 1;
   };
@@ -867,13 +665,8 @@ __device__ __forceinline__ void run_tiles_narrow_q(uint4* smem, const Lanes& L, 
   using F = std::false_type;
   for (int tile = tile_begin; tile < tile_end; ++tile) {
     floatx16 acc[4];
-    if (nks == 1) {
-      k_step(acc, tile, T{}, T{});
-    } else {
-      k_step(acc, tile, T{}, F{});
-      for (int ks = 2; ks < nks; ++ks) k_step(acc, tile, F{}, F{});
-      k_step(acc, tile, F{}, T{});
-    }
+    k_step(acc, T{});
+    for (int ks = 1; ks < nks; ++ks) k_step(acc, F{});
     epi(tile, acc);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");

@@ -1,6 +1,6 @@
 // Eight-wavefront tile engine (gfx950 / CDNA4): the K loop of the wide bf16
-// / fp32 contractions (the logprob forward, and the backward's dlogits, dH
-// and dW) with two wavefronts per SIMD, on 16 x 16 MFMA blocks.
+// / fp32 / FP8 contractions (the logprob forward, and the backward's
+// dlogits, dH and dW) with two wavefronts per SIMD, on 16 x 16 MFMA blocks.
 //
 // A 512-thread workgroup multiplies 256-row tiles of an operand A (walked in
 // order) with one fixed 256-row block of an operand B, acc = A_tile B^T,
@@ -44,6 +44,27 @@
 // far one (three slots) the walked A tiles; with kBFar the other way round.
 // A tile's last K step leaves the next tile's first fragments unread; they
 // are read after the epilogue, which then has those registers.
+//
+// FP8 (kDtype 2: E4M3 operands, v_mfma_scale_f32_16x16x128_f8f6f4 with
+// block scales 1): one instruction takes a block's whole 128-value K step,
+// lane l supplying the two 16-byte chunks lane_chunk(l / 16) and
+// 4 + lane_chunk(l / 16) of its row (A and B alike, so every product pairs
+// the same k). A K step is four sub-steps of 8 MFMAs (A blocks 2 p, 2 p + 1
+// against the four B blocks); two A fragments (16 registers), each refilled
+// right after its last use, and the four B fragments (32) serve the step.
+// The barrier is in sub-step 3 after its second MFMA (the step's last
+// read); sub-step 3 then reads step s + 1's A block 0 and, each after its
+// last use, its four B fragments. The loads keep the bf16 schedule's
+// places: the far operand's step s + 2 in sub-step 0, the near operand's
+// after the barrier in sub-step 3.
+//
+// side(t, lds, chunk), if given, is called in tile t's last K step right
+// after the barrier: the far operand's slot of that step is free from there
+// until the next step's sub-step 0, and this wavefront's own rows of it
+// (4 KiB at LDS byte address lds, smem chunk index chunk) are written by no
+// other wavefront's loads; side may fill them with loads into LDS (the
+// epilogue may read them once it has waited for them: the step issues
+// kDma8PerWave more loads after side returns).
 #pragma once
 
 #include <type_traits>
@@ -81,9 +102,9 @@ __device__ __forceinline__ Lanes8 lanes8() {
 // acc[bm][bn] (A rows 16 bm + 4 quad + i, B row 16 bn + c16 of the
 // wavefront's 128 x 64); it may read them directly. Every thread of the
 // 512-thread workgroup must call this.
-template <int kDtype, bool kBFar, class ARsrc, class Epi>
+template <int kDtype, bool kBFar, class ARsrc, class Epi, class Side>
 __device__ __forceinline__ void run_tiles8(uint4* smem, const Lanes8& L, int row_bytes, int tile_begin, int tile_end,
-                                           int nks, const ARsrc& a_rsrc, int4v b_rsrc, Epi&& epi) {
+                                           int nks, const ARsrc& a_rsrc, int4v b_rsrc, Epi&& epi, Side&& side) {
   constexpr int kAS = kBFar ? kHSlots : kWSlots;  // slots of A
   constexpr int kBS = kBFar ? kWSlots : kHSlots;  // slots of B
   static_assert(kAS + kBS == 5 && (kAS == 2 || kAS == 3), "five slots: two near, three far");
@@ -145,6 +166,12 @@ __device__ __forceinline__ void run_tiles8(uint4* smem, const Lanes8& L, int row
     if constexpr (kAS == 2) b_load(s);
     else a_load(s);
   };
+  // This wavefront's rows of the far operand's slot of step s: LDS byte
+  // address and smem chunk index.
+  auto far_rows = [&](int s) {
+    const int slot = kAS == 2 ? kAS + s % kBS : s % kAS;
+    return slot * kSlotChunks + wave * 32 * kRowChunks;
+  };
 
   // Prologue: near and far steps 0 and 1, in that order; then step 0 is
   // published (step 1 may be in flight).
@@ -193,7 +220,7 @@ __device__ __forceinline__ void run_tiles8(uint4* smem, const Lanes8& L, int row
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       const int b = q >> 2, bn = q & 3;
-      Mma16<kDtype>::step(acc[2 * p + b][bn], FA[p & 1][b], FB[kk][bn]);
+      if constexpr (kDtype != 2) Mma16<kDtype>::step(acc[2 * p + b][bn], FA[p & 1][b], FB[kk][bn]);
       if constexpr (j < 6) {
         // the next sub-step's A pair, then (sub-steps 0-3) B block j of
         // half 1
@@ -242,22 +269,109 @@ __device__ __forceinline__ void run_tiles8(uint4* smem, const Lanes8& L, int row
     for (int bn = 0; bn < 4; ++bn) read_b(s, 0, bn);
   };
 
+  // FP8: 32-byte fragments GA[b] (the A block of MFMAs 4 b .. 4 b + 3 of
+  // a sub-step: block 2 p + b) and GB[bn]; half h of a fragment is logical
+  // chunk 4 h + lane_chunk(l / 16), read at a_off[h] / b_off[h].
+  Frag8 GA[2], GB[4];
+  auto read_a8 = [&](int s, int bm, int h) {
+    const uint4 v = smem[(s % kAS) * kSlotChunks + a_off[h] + bm * 16 * kRowChunks];
+    if (h == 0) GA[bm & 1].lo = v;
+    else GA[bm & 1].hi = v;
+  };
+  auto read_b8 = [&](int s, int bn, int h) {
+    const uint4 v = smem[(kAS + s % kBS) * kSlotChunks + b_off[h] + bn * 16 * kRowChunks];
+    if (h == 0) GB[bn].lo = v;
+    else GB[bn].hi = v;
+  };
+  // FP8 sub-step p (0..3) of K step s: MFMA q on A block 2 p + q / 4 and B
+  // block q mod 4. Each A register is refilled right after the MFMAs that
+  // use it: A block 2 p + 1 after MFMAs 0, 1 (its register last held block
+  // 2 p - 1), block 2 p + 2 after MFMAs 4, 5 (sub-steps 0-2). Sub-step 3
+  // meets the barrier after MFMA 1 (its A block 7, read there, is the step's
+  // last read), then, with kNext, reads step s + 1's A block 0 (after MFMAs
+  // 4, 5) and B block bn after MFMA 4 + bn, its last use.
+  auto sub8 = [&](auto P, auto next, int s, int tile) {
+    constexpr int p = decltype(P)::value;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      mma_f8_16(acc[2 * p + (q >> 2)][q & 3], GA[q >> 2], GB[q & 3]);
+      if (q < 2) read_a8(s, 2 * p + 1, q);
+      if constexpr (p < 3) {
+        if (q == 4 || q == 5) read_a8(s, 2 * p + 2, q - 4);
+      } else {
+        if (q == 1) {
+          wait_and_barrier<kDma8PerWave>();
+          if constexpr (!decltype(next)::value) {
+            const int chunk = far_rows(s);
+            side(tile, lds0 + (uint32_t)chunk * 16u, chunk);
+          }
+        }
+        if constexpr (decltype(next)::value) {
+          if (q == 4 || q == 5) read_a8(s + 1, 0, q - 4);
+          if (q >= 4) {
+            read_b8(s + 1, q - 4, 0);
+            read_b8(s + 1, q - 4, 1);
+          }
+        }
+      }
+      if constexpr (p == 0) {
+        if (q == 3) far_load(s + 2);
+      } else if constexpr (p == 3) {
+        if (q == 6) near_load(s + 2);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  auto k_step8 = [&](int s, auto next, int tile) {
+    sub8(std::integral_constant<int, 0>{}, next, s, tile);
+    sub8(std::integral_constant<int, 1>{}, next, s, tile);
+    sub8(std::integral_constant<int, 2>{}, next, s, tile);
+    sub8(std::integral_constant<int, 3>{}, next, s, tile);
+  };
+  // A step's first fragments: A block 0 and the B blocks (block 1 comes in
+  // sub-step 0).
+  auto read_first8 = [&](int s) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      read_a8(s, 0, h);
+#pragma unroll
+      for (int bn = 0; bn < 4; ++bn) read_b8(s, bn, h);
+    }
+  };
+
   zero_acc();
-  read_first(0);
+  if constexpr (kDtype == 2) read_first8(0);
+  else read_first(0);
   int s = 0;
   for (int tile = tile_begin; tile < tile_end; ++tile) {
-    for (int ks = 0; ks + 1 < nks; ++ks, ++s) k_step(s, T{});
-    k_step(s, F{});
+    if constexpr (kDtype == 2) {
+      for (int ks = 0; ks + 1 < nks; ++ks, ++s) k_step8(s, T{}, tile);
+      k_step8(s, F{}, tile);
+    } else {
+      for (int ks = 0; ks + 1 < nks; ++ks, ++s) k_step(s, T{});
+      k_step(s, F{});
+    }
     ++s;
     epi(tile, acc);
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("" ::: "memory");
     zero_acc();
-    if (tile + 1 < tile_end) read_first(s);
+    if (tile + 1 < tile_end) {
+      if constexpr (kDtype == 2) read_first8(s);
+      else read_first(s);
+    }
   }
   // Every wavefront is done with the LDS ring (and its loads) on return.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
+}
+
+// run_tiles8 without a side load (the bf16 / fp32 kernels).
+template <int kDtype, bool kBFar, class ARsrc, class Epi>
+__device__ __forceinline__ void run_tiles8(uint4* smem, const Lanes8& L, int row_bytes, int tile_begin, int tile_end,
+                                           int nks, const ARsrc& a_rsrc, int4v b_rsrc, Epi&& epi) {
+  run_tiles8<kDtype, kBFar>(smem, L, row_bytes, tile_begin, tile_end, nks, a_rsrc, b_rsrc, epi,
+                            [](int, uint32_t, int) {});
 }
 
 }  // namespace itl

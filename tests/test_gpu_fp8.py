@@ -98,11 +98,11 @@ def _to_dev(cuda, *arrays):
 
 @pytest.mark.parametrize("n_tok,d,vocab", [
     (700, 256, 5000),          # 3 token blocks (ragged), 20 tiles
-    (300, 128, 4096 + 37),     # one K step (narrow kernel, 5 token blocks); last tile of 37 rows
+    (300, 128, 4096 + 37),     # one K step per tile (wide kernel, 2 token blocks); last tile of 37 rows
     (1, 128, 300),             # one token (narrow kernel)
     (64, 256, 3000),           # a full narrow block
     (513, 384, 8192 + 256),    # d = 3 K steps
-    (5200, 128, 150 * 256 - 17),  # d = 128 with many tokens: the narrow kernel, 82 token blocks
+    (5200, 128, 150 * 256 - 17),  # d = 128 with many tokens: the wide kernel, 21 token blocks
     (3400, 256, 150 * 256 - 17),  # 14 x 150 > 2048: several slices per workgroup (wide kernel)
 ])
 def test_lmhead_fp8_parity(cuda, n_tok, d, vocab):
@@ -120,12 +120,13 @@ def test_lmhead_fp8_parity(cuda, n_tok, d, vocab):
     assert float(lp.max()) <= 0.0
 
 
-def test_lmhead_fp8_invariance(cuda):
+@pytest.mark.parametrize("d", [256, 128, 6272])  # 6272: 49 K steps, the token block staged two steps ahead
+def test_lmhead_fp8_invariance(cuda, d):
     """The same token gives the same bits alone, at every row of a block, in
-    any sub-batch; and run to run."""
+    any sub-batch (wide and narrow kernels); and run to run."""
     import torch
 
-    Hq, hs, Wq, ws, y = _oracle_quantized_head(600, 256, 3000, seed=5)
+    Hq, hs, Wq, ws, y = _oracle_quantized_head(600, d, 3000, seed=5)
     itl = _itl()
     Hq_d, hs_d, Wq_d, ws_d, y_d = _to_dev(cuda, Hq, hs, Wq, ws, y)
     lp, lse = itl.lmhead_logprob_fp8(Hq_d, hs_d, Wq_d, ws_d, y_d)
