@@ -1,6 +1,6 @@
 // Per-lane online log-sum-exp folds of the head's logits: fold_column16 for
-// the bf16 / fp32 heads (wide and narrow kernels, 16 x 16 blocks),
-// fold_values for the FP8 / MXFP4 heads (32 x 32 blocks, block by block).
+// the bf16 / fp32 / FP8 heads (wide and narrow kernels, 16 x 16 blocks),
+// fold_values for the MXFP4 head (32 x 32 blocks, block by block).
 // Kernels that share a fold and feed it the same logit values in the same
 // order give a token the same partials, and so the same logprob, bit for
 // bit.
@@ -29,7 +29,7 @@ struct Col16 {
 
 // Fold one 32 x 32 block of logits (rows vw + 32 bm + ..., this lane's
 // token column; z[i] = row 32 bm + 8 (i / 4) + 4 half + (i % 4)) into the
-// state (the FP8 / MXFP4 kernels' fold). The sampled logit is picked with a
+// state (the MXFP4 kernels' fold). The sampled logit is picked with a
 // select tree keyed on the bits of its row, without a branch. Their wide and
 // narrow kernels fold with this one function, in the same block order, so a
 // token's state has the same bits whichever of them computed it.
@@ -114,8 +114,8 @@ __device__ __forceinline__ void pick_sampled(const Col16& c, const floatx4 (&z)[
 
 // Fold one tile's logits of one token column (this lane's 32 of the
 // wavefront's 128 rows: block bm register i holds row 16 bm + 4 quad + i)
-// into the state, as one step: the bf16 and fp32 heads' fold, shared by
-// their wide and narrow kernels (the FP8 kernels fold block by block with
+// into the state, as one step: the bf16, fp32 and FP8 heads' fold, shared by
+// their wide and narrow kernels (the MXFP4 kernels fold block by block with
 // fold_values). The 32 logits' maximum M (exact in any order) moves the
 // running maximum to m' = max(m, M); every term of the tile is then
 // exp2(z log2e + b) with one rounded offset b = -m' log2e (a fused
