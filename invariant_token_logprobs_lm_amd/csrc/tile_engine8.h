@@ -36,9 +36,10 @@
 // and the LDS reads are spread over the step. One workgroup barrier per K
 // step, in sub-step 6 (after the step's last reads): it publishes step
 // s + 1 (every wavefront has waited for its own loads of it) and frees step
-// s's slots; sub-step 7 loads the near operand's step s + 2 into them, and
-// the next step's sub-step 0 the far operand's step s + 3 (its slot was
-// freed one barrier earlier). Every
+// s's slots; the near operand's step s + 2 is loaded into its slot right
+// after the barrier (2 % faster than after the next sub-step's first
+// MFMAs), and the next step's sub-step 0 loads the far operand's step s + 3
+// (its slot was freed one barrier earlier). Every
 // wavefront loads rows 32 w .. 32 w + 31 of both operands, four loads of
 // each step back to back under one M0 value. The near operand (two slots) is the B block, the
 // far one (three slots) the walked A tiles; with kBFar the other way round.
@@ -56,7 +57,7 @@
 // read); sub-step 3 then reads step s + 1's A block 0 and, each after its
 // last use, its four B fragments. The loads keep the bf16 schedule's
 // places: the far operand's step s + 2 in sub-step 0, the near operand's
-// after the barrier in sub-step 3.
+// right after the barrier (after the side load, if any).
 //
 // side(t, lds, chunk), if given, is called in tile t's last K step right
 // after the barrier: the far operand's slot of that step is free from there
@@ -209,10 +210,10 @@ __device__ __forceinline__ void run_tiles8(uint4* smem, const Lanes8& L, int row
   // barrier that publishes step s + 1 follows after MFMA 5, then B blocks
   // 0, 1 of step s + 1's half 0; sub-step 7 reads step s + 1's first A pair
   // and its B blocks 2, 3. A tile's last step (kNext false) leaves step s + 1's reads to the
-  // code after the epilogue. kDma: the far operand's step s + 2 in sub-step
-  // 0 (its slot, that of step s - 1, was released at the previous barrier),
-  // the near operand's step s + 2 in sub-step 7 (into the slot step s
-  // released at this step's barrier). At each barrier exactly the far
+  // code after the epilogue. Loads: the far operand's step s + 2 in
+  // sub-step 0 (its slot, that of step s - 1, was released at the previous
+  // barrier), the near operand's step s + 2 right after this step's barrier
+  // (into the slot step s released there). At each barrier exactly the far
   // operand's latest four loads may then still be in flight.
   auto sub = [&](auto J, auto next, int s) {
     constexpr int j = decltype(J)::value;
@@ -230,8 +231,10 @@ __device__ __forceinline__ void run_tiles8(uint4* smem, const Lanes8& L, int row
         if (q < 2) read_a(s, 1, 6 + q);  // the step's last reads
         if (q == 5) {
           // step s + 1 landed (the far operand's step s + 2 may be in
-          // flight); every wavefront is done reading step s
+          // flight); every wavefront is done reading step s, whose near
+          // slot takes the near operand's step s + 2 at once
           wait_and_barrier<kDma8PerWave>();
+          near_load(s + 2);
         }
         if (decltype(next)::value && q >= 6) read_b(s + 1, 0, q - 6);
       } else {
@@ -240,8 +243,6 @@ __device__ __forceinline__ void run_tiles8(uint4* smem, const Lanes8& L, int row
       }
       if constexpr (j == 0) {
         if (q == 3) far_load(s + 2);
-      } else if constexpr (j == 7) {
-        if (q == 4) near_load(s + 2);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -305,6 +306,7 @@ __device__ __forceinline__ void run_tiles8(uint4* smem, const Lanes8& L, int row
             const int chunk = far_rows(s);
             side(tile, lds0 + (uint32_t)chunk * 16u, chunk);
           }
+          near_load(s + 2);
         }
         if constexpr (decltype(next)::value) {
           if (q == 4 || q == 5) read_a8(s + 1, 0, q - 4);
@@ -316,8 +318,6 @@ __device__ __forceinline__ void run_tiles8(uint4* smem, const Lanes8& L, int row
       }
       if constexpr (p == 0) {
         if (q == 3) far_load(s + 2);
-      } else if constexpr (p == 3) {
-        if (q == 6) near_load(s + 2);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
