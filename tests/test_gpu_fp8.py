@@ -120,6 +120,28 @@ def test_lmhead_fp8_parity(cuda, n_tok, d, vocab):
     assert float(lp.max()) <= 0.0
 
 
+def test_lmhead_fp8_many_tiles_per_slice(cuda):
+    """A vocabulary of 1,290 tiles (5-6 per slice of 256): the narrow kernel
+    fetches its row scales four tiles at a time, so a slice takes two
+    groups. The logprobs match the oracle, and a token has the same bits in
+    a narrow call (3 tokens) as in a wide one (70)."""
+    from oracle import fp8
+
+    vocab = 1290 * 256 - 101
+    Hq, hs, Wq, ws, y = _oracle_quantized_head(70, 128, vocab, seed=41)
+    y[:3] = [vocab - 1, 4 * 256 * 256 + 5, 17]  # sampled rows in the last tile, a high one, the first
+    itl = _itl()
+    Hq_d, hs_d, Wq_d, ws_d, y_d = _to_dev(cuda, Hq, hs, Wq, ws, y)
+    lp_n, lse_n = itl.lmhead_logprob_fp8(Hq_d[:3], hs_d[:3], Wq_d, ws_d, y_d[:3])
+    lp_o, lse_o = fp8.lmhead_logprob_fp8(Hq[:3], hs[:3], Wq, ws, y[:3])
+    e_lp = float(np.max(np.abs(lp_n.cpu().numpy() - lp_o)))
+    e_lse = float(np.max(np.abs(lse_n.cpu().numpy() - lse_o)))
+    say(f"[fp8 many tiles per slice] max|dlp|={e_lp:.3e} max|dlse|={e_lse:.3e}")
+    assert e_lp <= TOL_LP and e_lse <= TOL_LP
+    lp_w, lse_w = itl.lmhead_logprob_fp8(Hq_d, hs_d, Wq_d, ws_d, y_d)
+    assert same_bits(lp_w[:3], lp_n) and same_bits(lse_w[:3], lse_n)
+
+
 @pytest.mark.parametrize("d", [256, 128, 6272])  # 6272: 49 K steps, the token block staged two steps ahead
 def test_lmhead_fp8_invariance(cuda, d):
     """The same token gives the same bits alone, at every row of a block, in
