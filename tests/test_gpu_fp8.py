@@ -104,6 +104,8 @@ def _to_dev(cuda, *arrays):
     (513, 384, 8192 + 256),    # d = 3 K steps
     (5200, 128, 150 * 256 - 17),  # d = 128 with many tokens: the wide kernel, 21 token blocks
     (3400, 256, 150 * 256 - 17),  # 14 x 150 > 2048: several slices per workgroup (wide kernel)
+    (100, 256, 200),           # one partial vocabulary tile, one slice (wide kernel)
+    (65, 128, 1000),           # the fewest tokens the wide kernel takes
 ])
 def test_lmhead_fp8_parity(cuda, n_tok, d, vocab):
     from oracle import fp8
