@@ -420,13 +420,13 @@ const char* itl_build_info(void) {
     char buf[768];
     snprintf(buf, sizeof buf,
              "itl 0.3 arch=gfx950 threads=%d wide_threads=%d token_block=%d vocab_tile=%d k_step_bytes=%d w_slots=%d h_slots=%d "
-             "swap_slots_over_k_steps=%d max_slices=%d slices=balanced narrow_max_tokens=%d narrow_token_block=%d "
+             "swap_slots_over_k_steps=%d max_slices=%d slices=balanced narrow_max_tokens=%d narrow_token_block=%d narrow128_max_tokens=%d "
              "mfma_bf16=16x16x32 mfma_f32=16x16x4 fp8=e4m3_row_scaled mfma_fp8=16x16x128 mxfp4=e2m1_e8m0_32 mfma_mxfp4=32x32x64 "
              "bwd_chunk_tokens=%d loss_segment_tokens=%d loss_lane_segment=%d loss_wave_segment=%d loss_threads=%d "
              "loss_mean_chunk=%d loss_sums=f64 bwd_sampled_sort=stable_counting bwd_sampled_segment=%d "
              "bwd_sampled_group=%d",
              itl::kThreads, itl::kThreads8, itl::kBT, itl::kBV, itl::kStepBytes, itl::kWSlots, itl::kHSlots, itl::kNearBMaxSteps,
-             itl::kMaxSlices, itl::kNarrowMaxTokens, itl::kNarrowBRows, itl::kBwdChunkTokens, itl::kSegTokens,
+             itl::kMaxSlices, itl::kNarrowMaxTokens, itl::kNarrowBRows, itl::kNarrow128MaxTokens, itl::kBwdChunkTokens, itl::kSegTokens,
              itl::kLaneSeg, itl::kWaveSeg, itl::kLossThreads, itl::kFinishChunk, itl::kRunSeg, itl::kRunGroup);
     return std::string(buf);
   }();

@@ -28,6 +28,7 @@ constexpr int kWideTilesPerGroup = 4;  // the same for the forward kernels: with
                                        // (>= 512 tiles) one slice per workgroup, the fastest order measured
 constexpr int kNarrowBRows = 64;      // tokens per block of the narrow (few-token) kernel
 constexpr int kNarrowMaxTokens = 64;   // calls with at most this many tokens use the narrow kernel
+constexpr int kNarrow128MaxTokens = 128;  // calls of 65 to this many tokens: the narrow kernel on one 128-token block
 constexpr int kSuperBand = 64;       // token blocks walked together, slice group by slice group (workgroup order)
 constexpr int kBwdSuperBand = 32;    // the same for the backward kernels' walk (64 measured 3 % slower there)
 constexpr int kNearBMaxSteps = 48;   // load schedule only: K loops longer than this stage the fixed operand

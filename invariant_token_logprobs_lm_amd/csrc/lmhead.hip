@@ -199,13 +199,15 @@ __global__ __launch_bounds__(kThreads8, 1) void lmhead_lse_partial8_kernel(
   run_tiles8<kDtype, kBFar>(smem, L, row_bytes, tile_begin, tile_end, nks, w_rsrc, hr, epilogue);
 }
 
-// The same partials for few tokens: 64-token blocks, one workgroup per
-// (token block, slice), the workgroup's slice walked by run_tiles_narrow.
-// Lane l of wavefront (wv, wt) holds tokens t0 + 32 wt + 16 bn + (l mod 16)
-// (bn < 2) against the same W rows, with the same fold, as in
+// The same partials for few tokens: kBRows-token blocks (64, or 128 for
+// calls of 65 to 128 tokens, where one wide 256-token block would do twice
+// the contraction work), one workgroup per (token block, slice), the
+// workgroup's slice walked by run_tiles_narrow. Lane l of wavefront (wv, wt)
+// holds tokens t0 + (kBRows / 2) wt + 16 bn + (l mod 16) (bn < kBRows / 32)
+// against the same W rows, with the same fold, as in
 // lmhead_lse_partial8_kernel, so the partials (and the logprobs) have the
 // same bits.
-template <int kDtype, bool kKeep>
+template <int kDtype, bool kKeep, int kBRows>
 __global__ __launch_bounds__(kThreads, 1) void lmhead_lse_partial_narrow_kernel(
     const char* __restrict__ H, const char* __restrict__ W, const int32_t* __restrict__ tokens, int n_tok,
     int row_bytes, int vocab, int n_slices, float2* __restrict__ part, float* __restrict__ zy_out,
@@ -217,15 +219,17 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_lse_partial_narrow_kernel(
   // blocks of a slice share an XCD (blockIdx mod 8) and its L2.
   const int S = n_slices;
   const int slice = blockIdx.x % S;
-  const int t0 = (blockIdx.x / S) * kNarrowBRows;
+  constexpr int kBN = kBRows / 32;  // token columns per lane
+  constexpr int kWaveToks = kBRows / 2;
+  const int t0 = (blockIdx.x / S) * kBRows;
   const int n_vt = (vocab + kBV - 1) / kBV;
   const int tile_begin = slice_tile(slice, n_vt, S);
   const int tile_end = slice_tile(slice + 1, n_vt, S);
   const int nks = row_bytes / kStepBytes;
-  Col16 c[2];
+  Col16 c[kBN];
 #pragma unroll
-  for (int bn = 0; bn < 2; ++bn) {
-    const int tok = t0 + wt * 32 + bn * 16 + c16;
+  for (int bn = 0; bn < kBN; ++bn) {
+    const int tok = t0 + wt * kWaveToks + bn * 16 + c16;
     c[bn] = Col16{tok < n_tok ? tokens[tok] : -1, -INFINITY, 0.0f};
   }
 
@@ -233,33 +237,33 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_lse_partial_narrow_kernel(
     const int v0 = tile * kBV;
     return rsrc_words(W + (size_t)v0 * row_bytes, (uint32_t)min(kBV, vocab - v0) * row_bytes);
   };
-  const int4v hr = rsrc_words(H + (size_t)t0 * row_bytes, (uint32_t)min(kNarrowBRows, n_tok - t0) * row_bytes);
-  const LogitRows rows = logit_rows(logits, ld, t0 + wt * 32, 32, n_tok, c16, quad);
-  auto epilogue = [&](int tile, floatx4 (&acc)[8][2]) {
+  const int4v hr = rsrc_words(H + (size_t)t0 * row_bytes, (uint32_t)min(kBRows, n_tok - t0) * row_bytes);
+  const LogitRows rows = logit_rows(logits, ld, t0 + wt * kWaveToks, kWaveToks, n_tok, c16, quad);
+  auto epilogue = [&](int tile, floatx4 (&acc)[8][kBN]) {
     const int vw = tile * kBV + wv * 128;
     auto fold_tile = [&](auto partial) {
       if constexpr (kKeep) {
 #pragma unroll
-        for (int bn = 0; bn < 2; ++bn)
+        for (int bn = 0; bn < kBN; ++bn)
 #pragma unroll
           for (int bm = 0; bm < 8; ++bm) store_logits(rows, bn, vw + bm * 16, quad, vocab, acc[bm][bn], partial);
       }
 #pragma unroll
-      for (int bn = 0; bn < 2; ++bn) {
+      for (int bn = 0; bn < kBN; ++bn) {
         floatx4 z[8];
 #pragma unroll
         for (int bm = 0; bm < 8; ++bm) z[bm] = acc[bm][bn];
-        pick_sampled(c[bn], z, vw, quad, zy_out + (t0 + wt * 32 + bn * 16 + c16));
+        pick_sampled(c[bn], z, vw, quad, zy_out + (t0 + wt * kWaveToks + bn * 16 + c16));
         fold_column16(c[bn], z, vw, quad, vocab, partial);
       }
     };
     if (tile * kBV + kBV > vocab) fold_tile(std::true_type{});
     else fold_tile(std::false_type{});
   };
-  run_tiles_narrow<kDtype>(smem, L, row_bytes, tile_begin, tile_end, nks, w_rsrc, hr, epilogue);
+  run_tiles_narrow<kDtype, kBRows>(smem, L, row_bytes, tile_begin, tile_end, nks, w_rsrc, hr, epilogue);
 #pragma unroll
-  for (int bn = 0; bn < 2; ++bn) {
-    const int tok = t0 + wt * 32 + bn * 16 + c16;
+  for (int bn = 0; bn < kBN; ++bn) {
+    const int tok = t0 + wt * kWaveToks + bn * 16 + c16;
     flush_slice16(c[bn], tok, n_tok, quad, ((size_t)slice * 2 + wv) * n_tok + tok, part);
   }
 }
@@ -336,8 +340,12 @@ void launch_partials(const char* H, const char* W, const int32_t* tokens, int n_
   const int S = n_slices(vocab);
   if (n_tok <= kNarrowMaxTokens) {
     const dim3 grid((unsigned)ceil_div(n_tok, kNarrowBRows) * (unsigned)S);
-    hipLaunchKernelGGL((lmhead_lse_partial_narrow_kernel<kDtype, kKeep>), grid, dim3(kThreads), 0, stream, H, W,
-                       tokens, n_tok, row_bytes, vocab, S, part, zy, logits, ld);
+    hipLaunchKernelGGL((lmhead_lse_partial_narrow_kernel<kDtype, kKeep, kNarrowBRows>), grid, dim3(kThreads), 0,
+                       stream, H, W, tokens, n_tok, row_bytes, vocab, S, part, zy, logits, ld);
+  } else if (n_tok <= kNarrow128MaxTokens) {
+    const dim3 grid((unsigned)S);
+    hipLaunchKernelGGL((lmhead_lse_partial_narrow_kernel<kDtype, kKeep, kNarrow128MaxTokens>), grid, dim3(kThreads), 0,
+                       stream, H, W, tokens, n_tok, row_bytes, vocab, S, part, zy, logits, ld);
   } else {
     const int G = slices_per_group(n_tok, vocab);
     const int ntb = (int)ceil_div(n_tok, kBT);

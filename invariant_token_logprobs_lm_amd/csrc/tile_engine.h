@@ -222,9 +222,9 @@ __device__ __forceinline__ Lanes lanes() {
 constexpr int kEngineSmemChunks = (kWSlots + kHSlots) * kSlotChunks;
 
 // Narrow engine for few B rows (decode-shaped calls): 256-row A tiles
-// against a 64-row B block. Wavefront (wv, wt) holds rows 128 wv .. 128 wv +
-// 127 of the A tile against B rows 32 wt .. 32 wt + 31 as 8 x 2 blocks of
-// 16 x 16. Every MFMA of an accumulator block takes the same operand
+// against a 64-row B block (or 128 rows, below). Wavefront (wv, wt) holds
+// rows 128 wv .. 128 wv + 127 of the A tile against B rows 32 wt .. 32 wt +
+// 31 as 8 x 2 blocks of 16 x 16. Every MFMA of an accumulator block takes the same operand
 // fragments, in the same order, as in the eight-wavefront engine run_tiles8
 // (same slot layout and swizzle, same K sub-step order, fresh accumulators
 // at a tile's first step), so an output element has the same bits in both.
@@ -236,36 +236,48 @@ constexpr int kNarrowBSlotChunks = kNarrowBRows * kRowChunks;  // 512 chunks = 8
 constexpr int kNarrowBDmaPerWave = kNarrowBRows / 4 / kDmaRows;  // 2
 static_assert(kNarrowSlots * (kSlotChunks + kNarrowBSlotChunks) <= kEngineSmemChunks, "LDS budget");
 
-// epi(t, acc) sees tile t's accumulators acc[bm][bn] (A rows 16 bm + 4 (l /
-// 16) + i, B row 16 bn + (l mod 16) of the wavefront's 128 x 32).
-template <int kDtype, class ARsrc, class Epi>
+// kBRows = 64 or 128 token rows per B block: wavefront (wv, wt) holds B rows
+// (kBRows / 2) wt .. + kBRows / 2 - 1, as kBRows / 32 blocks per A block.
+// The 128-row block (calls of 65 to 128 tokens) has three slots, loaded two
+// K steps ahead (four of its slots would not fit the LDS). epi(t, acc) sees
+// tile t's accumulators acc[bm][bn] (A rows 16 bm + 4 (l / 16) + i, B row
+// 16 bn + (l mod 16) of the wavefront's 128 x kBRows / 2).
+template <int kDtype, int kBRows = kNarrowBRows, class ARsrc, class Epi>
 __device__ __forceinline__ void run_tiles_narrow(uint4* smem, const Lanes& L, int row_bytes, int tile_begin,
                                                  int tile_end, int nks, const ARsrc& a_rsrc, int4v b_rsrc, Epi&& epi) {
+  static_assert(kBRows == 64 || kBRows == 128, "64- or 128-row token blocks");
+  constexpr int kBN = kBRows / 32;                      // B blocks per wavefront
+  constexpr int kSlots = kBRows == 64 ? kNarrowSlots : 3;
+  constexpr int kBSlotChunks = kBRows * kRowChunks;
+  constexpr int kBDma = kBRows / 4 / kDmaRows;          // B loads per wavefront per step
+  static_assert(kSlots * (kSlotChunks + kBSlotChunks) <= kEngineSmemChunks, "LDS budget");
   const int lane = L.lane, wave = L.wave, wv = L.wv, wt = L.wt;
   const int quad = lane >> 4, c16 = lane & 15;
   // Loader: wavefront w fills A rows 64 w .. 64 w + 63 (8 loads) and B rows
-  // 16 w .. 16 w + 15 (2 loads) of a slot; lane i fetches row (i / 8) of an
-  // 8-row group at logical chunk (i % 8) ^ swz(row), as in every engine here.
+  // (kBRows / 4) w .. + kBRows / 4 - 1 of a slot; lane i fetches row (i / 8)
+  // of an 8-row group at logical chunk (i % 8) ^ swz(row), as in every
+  // engine here.
   const int lr = lane >> 3;
-  uint32_t avoff[kDmaPerWave], bvoff[kNarrowBDmaPerWave];
+  uint32_t avoff[kDmaPerWave], bvoff[kBDma];
 #pragma unroll
   for (int j = 0; j < kDmaPerWave; ++j)
     avoff[j] = (uint32_t)(wave * 64 + j * kDmaRows + lr) * (uint32_t)row_bytes + (((lane & 7) ^ lr ^ (j & 1)) * 16);
 #pragma unroll
-  for (int j = 0; j < kNarrowBDmaPerWave; ++j)
-    bvoff[j] = (uint32_t)(wave * 16 + j * kDmaRows + lr) * (uint32_t)row_bytes + (((lane & 7) ^ lr ^ (j & 1)) * 16);
+  for (int j = 0; j < kBDma; ++j)
+    bvoff[j] = (uint32_t)(wave * (kBRows / 4) + j * kDmaRows + lr) * (uint32_t)row_bytes +
+               (((lane & 7) ^ lr ^ (j & 1)) * 16);
   const uint32_t lds0 = (uint32_t)(size_t)((__attribute__((address_space(3))) uint4*)smem);
   auto a_lds = [&](int slot) { return lds0 + (uint32_t)slot * kSlotBytes + (uint32_t)wave * 64 * kStepBytes; };
   auto b_lds = [&](int slot) {
-    return lds0 + (uint32_t)kNarrowSlots * kSlotBytes + (uint32_t)slot * kNarrowBSlotChunks * 16 +
-           (uint32_t)wave * 16 * kStepBytes;
+    return lds0 + (uint32_t)kSlots * kSlotBytes + (uint32_t)slot * kBSlotChunks * 16 +
+           (uint32_t)wave * (kBRows / 4) * kStepBytes;
   };
   // Load K step (tile, ks) of both operands into a slot: B first, then A.
   auto load_step = [&](int tile, int ks, int slot) {
     const int4v ar = a_rsrc(tile);
     const uint32_t so = (uint32_t)ks * kStepBytes;
 #pragma unroll
-    for (int j = 0; j < kNarrowBDmaPerWave; ++j) dma16(b_rsrc, bvoff[j], so, b_lds(slot) + j * 1024);
+    for (int j = 0; j < kBDma; ++j) dma16(b_rsrc, bvoff[j], so, b_lds(slot) + j * 1024);
 #pragma unroll
     for (int j = 0; j < kDmaPerWave; ++j) dma16(ar, avoff[j], so, a_lds(slot) + j * 1024);
   };
@@ -280,7 +292,7 @@ __device__ __forceinline__ void run_tiles_narrow(uint4* smem, const Lanes& L, in
     }
   };
 #pragma unroll
-  for (int p = 0; p < kNarrowSlots - 1; ++p) {
+  for (int p = 0; p < kSlots - 1; ++p) {
     load_step(ld_tile, ld_ks, p);
     next_load();
   }
@@ -291,28 +303,28 @@ __device__ __forceinline__ void run_tiles_narrow(uint4* smem, const Lanes& L, in
   for (int kk = 0; kk < 2; ++kk) {
     const int pc = (4 * kk + lane_chunk(quad)) ^ swz(c16);
     a_off[kk] = (wv * 128 + c16) * kRowChunks + pc;
-    b_off[kk] = (wt * 32 + c16) * kRowChunks + pc;
+    b_off[kk] = (wt * (kBRows / 2) + c16) * kRowChunks + pc;
   }
-  constexpr int kPending = (kNarrowSlots - 2) * (kDmaPerWave + kNarrowBDmaPerWave);
+  constexpr int kPending = (kSlots - 2) * (kDmaPerWave + kBDma);
   int slot = 0;
   // One K step.
-  auto k_step = [&](floatx4 (&acc)[8][2]) {
-    // This step's loads landed (the next two steps' may be in flight);
-    // every wavefront is done reading the previous step's slot.
+  auto k_step = [&](floatx4 (&acc)[8][kBN]) {
+    // This step's loads landed (the later steps' may be in flight); every
+    // wavefront is done reading the previous step's slot.
     wait_and_barrier<kPending>();
-    load_step(ld_tile, ld_ks, slot == 0 ? kNarrowSlots - 1 : slot - 1);
+    load_step(ld_tile, ld_ks, slot == 0 ? kSlots - 1 : slot - 1);
     next_load();
     const uint4* sa = smem + slot * kSlotChunks;
-    const uint4* sb = smem + kNarrowSlots * kSlotChunks + slot * kNarrowBSlotChunks;
-    // All 20 fragments of the step are read up front (one LDS round trip
-    // per step rather than one per sub-step), then the 32 MFMAs.
-    uint4 A[2][8], B[2][2];
+    const uint4* sb = smem + kSlots * kSlotChunks + slot * kBSlotChunks;
+    // All of the step's fragments are read up front (one LDS round trip per
+    // step rather than one per sub-step), then its MFMAs.
+    uint4 A[2][8], B[2][kBN];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
       for (int m = 0; m < 8; ++m) A[kk][m] = sa[a_off[kk] + m * 16 * kRowChunks];
 #pragma unroll
-      for (int n = 0; n < 2; ++n) B[kk][n] = sb[b_off[kk] + n * 16 * kRowChunks];
+      for (int n = 0; n < kBN; ++n) B[kk][n] = sb[b_off[kk] + n * 16 * kRowChunks];
     }
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (kDtype == 2) {
@@ -321,24 +333,24 @@ __device__ __forceinline__ void run_tiles_narrow(uint4* smem, const Lanes& L, in
 #pragma unroll
       for (int m = 0; m < 8; ++m)
 #pragma unroll
-        for (int n = 0; n < 2; ++n) mma_f8_16(acc[m][n], Frag8{A[0][m], A[1][m]}, Frag8{B[0][n], B[1][n]});
+        for (int n = 0; n < kBN; ++n) mma_f8_16(acc[m][n], Frag8{A[0][m], A[1][m]}, Frag8{B[0][n], B[1][n]});
     } else {
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
         for (int m = 0; m < 8; ++m)
 #pragma unroll
-          for (int n = 0; n < 2; ++n) Mma16<kDtype>::step(acc[m][n], A[kk][m], B[kk][n]);
+          for (int n = 0; n < kBN; ++n) Mma16<kDtype>::step(acc[m][n], A[kk][m], B[kk][n]);
     }
-    slot = slot == kNarrowSlots - 1 ? 0 : slot + 1;
+    slot = slot == kSlots - 1 ? 0 : slot + 1;
   };
   for (int tile = tile_begin; tile < tile_end; ++tile) {
     // A tile's accumulators start as +0.0 registers, as in run_tiles8.
-    floatx4 acc[8][2];
+    floatx4 acc[8][kBN];
 #pragma unroll
     for (int m = 0; m < 8; ++m)
 #pragma unroll
-      for (int n = 0; n < 2; ++n) acc[m][n] = floatx4{};
+      for (int n = 0; n < kBN; ++n) acc[m][n] = floatx4{};
     for (int ks = 0; ks < nks; ++ks) k_step(acc);
     epi(tile, acc);
   }

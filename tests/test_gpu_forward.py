@@ -149,9 +149,10 @@ def test_row_position_invariance(cuda):
 )
 def test_narrow_and_wide_kernels_agree(cuda, d, vocab, dtype_name):
     """Calls of at most narrow_max_tokens tokens (build info) run the narrow
-    kernel (64-token blocks), larger ones the 256-token block kernel: the
-    same tokens give the same bits either way, at every row of a narrow
-    block and across blocks."""
+    kernel on 64-token blocks, calls of up to narrow128_max_tokens on one
+    128-token block, larger ones the 256-token block kernel: the same tokens
+    give the same bits either way, at every row of a narrow block and across
+    blocks."""
     import re
     import torch
 
@@ -159,20 +160,24 @@ def test_narrow_and_wide_kernels_agree(cuda, d, vocab, dtype_name):
     H, W, y = _random_head(600, d, vocab, dt, seed=d + vocab, device=cuda)
     itl = _itl()
     limit = int(re.search(r"narrow_max_tokens=(\d+)", itl.build_info()).group(1))
-    assert limit >= 1
+    limit128 = int(re.search(r"narrow128_max_tokens=(\d+)", itl.build_info()).group(1))
+    assert 1 <= limit < limit128
     lp, lse = itl.lmhead_logprob(H, W, y)  # wide kernel
-    for lo, n in ((0, 1), (5, 7), (100, min(limit, 33)), (300, limit), (472, limit + 1), (200, 129)):
+    for lo, n in ((0, 1), (5, 7), (100, min(limit, 33)), (300, limit), (472, limit + 1), (200, 100),
+                  (210, limit128), (200, limit128 + 1)):
         lp_n, lse_n = itl.lmhead_logprob(H[lo:lo + n], W, y[lo:lo + n])
         assert same_bits(lp_n, lp[lo:lo + n]) and same_bits(lse_n, lse[lo:lo + n]), (lo, n)
-    # a narrow call at every row position of the 64-token block
+    # a narrow call at every row position of the 64-token block, and of the
+    # 128-token one
     probe_lp = lp[17:18]
-    for pos in range(min(limit, 64)):
-        Hp = H[:min(limit, 64)].clone()
-        yp = y[:min(limit, 64)].clone()
-        Hp[pos] = H[17]
-        yp[pos] = y[17]
-        lp_p, _ = itl.lmhead_logprob(Hp, W, yp)
-        assert same_bits(lp_p[pos:pos + 1], probe_lp), pos
+    for size in (min(limit, 64), limit128):
+        for pos in range(size):
+            Hp = H[:size].clone()
+            yp = y[:size].clone()
+            Hp[pos] = H[17]
+            yp[pos] = y[17]
+            lp_p, _ = itl.lmhead_logprob(Hp, W, yp)
+            assert same_bits(lp_p[pos:pos + 1], probe_lp), (size, pos)
 
 
 def test_run_to_run_determinism(cuda):

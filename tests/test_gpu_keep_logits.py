@@ -44,7 +44,9 @@ def _random_head(n_tok, d, vocab, dtype, seed, device, w_std=0.05):
     [
         (40, 128, 1000, 0, "bf16"),          # narrow kernel, vocab a multiple of 4 but not of 256
         (64, 256, 4096 + 37, 12, "bf16"),    # narrow, last tile of 37 rows, vocab not a multiple of 4, padded rows
-        (65, 192, 3001, 3, "bf16"),          # wide kernel from 65 tokens on, 1 row past the last token block start
+        (65, 192, 3001, 3, "bf16"),          # the 128-token narrow block from 65 tokens on, 1 row past 64
+        (128, 64, 1030, 2, "f32"),           # a full 128-token narrow block, fp32 head
+        (129, 192, 3001, 0, "bf16"),         # the wide kernel from 129 tokens on
         (700, 256, 5000, 0, "bf16"),         # 3 token blocks (ragged), 20 vocabulary tiles
         (300, 64, 1030, 2, "f32"),           # fp32 head
     ],
