@@ -268,7 +268,7 @@ itl_status itl_quantize_rows_fp8(const void* X, itl_dtype dtype, int64_t n_rows,
  *   logprob[t] = z[t, tokens[t]] - log sum_v exp(z[t, v])
  * with the same fused log-sum-exp, vocabulary slices and combine as
  * itl_lmhead_logprob, and the same determinism contract (calls of at most
- * 64 tokens run a narrow kernel with the same per-token arithmetic). d must
+ * 128 tokens run a narrow kernel with the same per-token arithmetic). d must
  * be a multiple of 128; Hq, Wq 16-byte aligned.
  * workspace: >= itl_lmhead_logprob_workspace_bytes(n_tok, vocab) bytes,
  * 256-byte aligned. lse may be NULL. */

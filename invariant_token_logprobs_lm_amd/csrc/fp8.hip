@@ -250,18 +250,21 @@ __global__ __launch_bounds__(kThreads8, 1) void lmhead_fp8_partial8_kernel(
   run_tiles8<2, kBFar>(smem, L, row_bytes, tile_begin, tile_end, nks, w_rsrc, hr, epilogue, side);
 }
 
-// Decode-shaped FP8 calls (at most kNarrowMaxTokens tokens): 64-token
-// blocks, one workgroup per (token block, slice), the narrow engine's FP8
-// steps (run_tiles_narrow<2>). Lane l of wavefront (wv, wt) holds tokens
-// t0 + 32 wt + 16 bn + (l mod 16) (bn < 2) against the same W rows, with the
-// same MFMA sequence, scales and fold as lmhead_fp8_partial8_kernel, so the
-// partials and logprobs have the same bits. The row scales of up to
-// kNarrowScaleTiles tiles are fetched at a time into two registers per tile
-// (lane l: rows vw + l, vw + 64 + l) and spread to the lanes that need them
-// with ds_bpermute; the first group before the first operand load, so that
-// waiting for them waits for nothing else.
+// Decode-shaped FP8 calls (at most kNarrow128MaxTokens tokens): kBRows-token
+// blocks (64, or one block of 128 for calls of 65 to 128 tokens), one
+// workgroup per (token block, slice), the narrow engine's FP8 steps
+// (run_tiles_narrow<2, kBRows>). Lane l of wavefront (wv, wt) holds tokens
+// t0 + (kBRows / 2) wt + 16 bn + (l mod 16) (bn < kBRows / 32) against the
+// same W rows, with the same MFMA sequence, scales and fold as
+// lmhead_fp8_partial8_kernel, so the partials and logprobs have the same
+// bits. The row scales of up to kNarrowScaleTiles tiles are fetched at a
+// time into two registers per tile (lane l: rows vw + l, vw + 64 + l) and
+// spread to the lanes that need them with ds_bpermute; the first group
+// before the first operand load, so that waiting for them waits for nothing
+// else.
 constexpr int kNarrowScaleTiles = 4;
 
+template <int kBRows>
 __global__ __launch_bounds__(kThreads, 1) void lmhead_fp8_partial_narrow_kernel(
     const uint8_t* __restrict__ Hq, const float* __restrict__ h_scale, const uint8_t* __restrict__ Wq,
     const float* __restrict__ w_scale, const int32_t* __restrict__ tokens, int n_tok, int d, int vocab, int n_slices,
@@ -271,17 +274,19 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_fp8_partial_narrow_kernel(
   const int wv = L.wv, wt = L.wt, quad = L.lane >> 4, c16 = L.lane & 15;
   const int S = n_slices;
   const int slice = blockIdx.x % S;
-  const int t0 = (blockIdx.x / S) * kNarrowBRows;
+  constexpr int kBN = kBRows / 32;  // token columns per lane
+  constexpr int kWaveToks = kBRows / 2;
+  const int t0 = (blockIdx.x / S) * kBRows;
   const int n_vt = (vocab + kBV - 1) / kBV;
   const int tile_begin = slice_tile(slice, n_vt, S);
   const int tile_end = slice_tile(slice + 1, n_vt, S);
   const int row_bytes = d;
   const int nks = row_bytes / kStepBytes;
-  Col16 c[2];
-  float hs[2];
+  Col16 c[kBN];
+  float hs[kBN];
 #pragma unroll
-  for (int bn = 0; bn < 2; ++bn) {
-    const int tok = t0 + wt * 32 + bn * 16 + c16;
+  for (int bn = 0; bn < kBN; ++bn) {
+    const int tok = t0 + wt * kWaveToks + bn * 16 + c16;
     c[bn] = Col16{tok < n_tok ? tokens[tok] : -1, -INFINITY, 0.0f};
     hs[bn] = tok < n_tok ? h_scale[tok] : 0.0f;
   }
@@ -297,7 +302,9 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_fp8_partial_narrow_kernel(
       g_hi[j] = in && row + 64 < vocab ? w_scale[row + 64] : 0.0f;
     }
     asm volatile("" ::"v"(g_lo[0]), "v"(g_lo[1]), "v"(g_lo[2]), "v"(g_lo[3]), "v"(g_hi[0]), "v"(g_hi[1]),
-                 "v"(g_hi[2]), "v"(g_hi[3]), "v"(c[0].y), "v"(c[1].y), "v"(hs[0]), "v"(hs[1]));
+                 "v"(g_hi[2]), "v"(g_hi[3]));
+#pragma unroll
+    for (int bn = 0; bn < kBN; ++bn) asm volatile("" ::"v"(c[bn].y), "v"(hs[bn]));
   };
   static_assert(kNarrowScaleTiles == 4, "load_scales waits for four tiles' scales");
   load_scales(tile_begin);
@@ -306,8 +313,8 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_fp8_partial_narrow_kernel(
     const int v0 = tile * kBV;
     return rsrc_words(Wq + (size_t)v0 * row_bytes, (uint32_t)min(kBV, vocab - v0) * row_bytes);
   };
-  const int4v hr = rsrc_words(Hq + (size_t)t0 * row_bytes, (uint32_t)min(kNarrowBRows, n_tok - t0) * row_bytes);
-  auto epilogue = [&](int tile, floatx4 (&acc)[8][2]) {
+  const int4v hr = rsrc_words(Hq + (size_t)t0 * row_bytes, (uint32_t)min(kBRows, n_tok - t0) * row_bytes);
+  auto epilogue = [&](int tile, floatx4 (&acc)[8][kBN]) {
     const int vw = tile * kBV + wv * 128;
     const int j = (tile - tile_begin) % kNarrowScaleTiles;
     const float lo = j == 0 ? g_lo[0] : j == 1 ? g_lo[1] : j == 2 ? g_lo[2] : g_lo[3];
@@ -326,14 +333,14 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_fp8_partial_narrow_kernel(
     }
     auto fold_tile = [&](auto partial) {
 #pragma unroll
-      for (int bn = 0; bn < 2; ++bn) {
+      for (int bn = 0; bn < kBN; ++bn) {
         floatx4 z[8];
 #pragma unroll
         for (int bm = 0; bm < 8; ++bm) {
           z[bm] = acc[bm][bn];
           scale_logits(z[bm], wsc[bm], hs[bn]);
         }
-        pick_sampled(c[bn], z, vw, quad, zy_out + (t0 + wt * 32 + bn * 16 + c16));
+        pick_sampled(c[bn], z, vw, quad, zy_out + (t0 + wt * kWaveToks + bn * 16 + c16));
         fold_column16(c[bn], z, vw, quad, vocab, partial);
       }
     };
@@ -343,10 +350,10 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_fp8_partial_narrow_kernel(
     // 256 kNarrowScaleTiles tiles): the next group
     if (j == kNarrowScaleTiles - 1 && tile + 1 < tile_end) load_scales(tile + 1);
   };
-  run_tiles_narrow<2>(smem, L, row_bytes, tile_begin, tile_end, nks, w_rsrc, hr, epilogue);
+  run_tiles_narrow<2, kBRows>(smem, L, row_bytes, tile_begin, tile_end, nks, w_rsrc, hr, epilogue);
 #pragma unroll
-  for (int bn = 0; bn < 2; ++bn) {
-    const int tok = t0 + wt * 32 + bn * 16 + c16;
+  for (int bn = 0; bn < kBN; ++bn) {
+    const int tok = t0 + wt * kWaveToks + bn * 16 + c16;
     flush_slice16(c[bn], tok, n_tok, quad, ((size_t)slice * 2 + wv) * n_tok + tok, part);
   }
 }
@@ -553,8 +560,11 @@ hipError_t launch_lmhead_logprob_fp8(const uint8_t* Hq, const float* h_scale, co
                                        align256((size_t)2 * S * (size_t)n_tok * sizeof(float2)));
   if (n_tok <= kNarrowMaxTokens) {
     const dim3 grid((unsigned)ceil_div(n_tok, kNarrowBRows) * (unsigned)S);
-    hipLaunchKernelGGL(lmhead_fp8_partial_narrow_kernel, grid, dim3(kThreads), 0, stream, Hq, h_scale, Wq, w_scale,
-                       tokens, n_tok, d, vocab, S, part, zy);
+    hipLaunchKernelGGL((lmhead_fp8_partial_narrow_kernel<kNarrowBRows>), grid, dim3(kThreads), 0, stream, Hq, h_scale,
+                       Wq, w_scale, tokens, n_tok, d, vocab, S, part, zy);
+  } else if (n_tok <= kNarrow128MaxTokens) {
+    hipLaunchKernelGGL((lmhead_fp8_partial_narrow_kernel<kNarrow128MaxTokens>), dim3((unsigned)S), dim3(kThreads), 0,
+                       stream, Hq, h_scale, Wq, w_scale, tokens, n_tok, d, vocab, S, part, zy);
   } else {
     const dim3 grid((unsigned)ntb * (unsigned)n_slice_groups(n_tok, vocab));
     // Long K loops stage the token block two K steps ahead, as in the bf16

@@ -104,8 +104,10 @@ def _to_dev(cuda, *arrays):
     (513, 384, 8192 + 256),    # d = 3 K steps
     (5200, 128, 150 * 256 - 17),  # d = 128 with many tokens: the wide kernel, 21 token blocks
     (3400, 256, 150 * 256 - 17),  # 14 x 150 > 2048: several slices per workgroup (wide kernel)
-    (100, 256, 200),           # one partial vocabulary tile, one slice (wide kernel)
-    (65, 128, 1000),           # the fewest tokens the wide kernel takes
+    (100, 256, 200),           # one partial vocabulary tile, one slice (narrow kernel, one 128-token block)
+    (65, 128, 1000),           # the fewest tokens of the 128-token narrow block
+    (128, 384, 3000),          # a full 128-token narrow block
+    (129, 128, 1000),          # the fewest tokens the wide kernel takes
 ])
 def test_lmhead_fp8_parity(cuda, n_tok, d, vocab):
     from oracle import fp8
@@ -154,7 +156,7 @@ def test_lmhead_fp8_invariance(cuda, d):
     itl = _itl()
     Hq_d, hs_d, Wq_d, ws_d, y_d = _to_dev(cuda, Hq, hs, Wq, ws, y)
     lp, lse = itl.lmhead_logprob_fp8(Hq_d, hs_d, Wq_d, ws_d, y_d)
-    for lo, n in ((0, 1), (17, 5), (100, 64), (300, 257)):
+    for lo, n in ((0, 1), (17, 5), (100, 64), (150, 65), (200, 128), (330, 129), (300, 257)):
         a, b = itl.lmhead_logprob_fp8(Hq_d[lo:lo + n], hs_d[lo:lo + n], Wq_d, ws_d, y_d[lo:lo + n])
         assert same_bits(a, lp[lo:lo + n]) and same_bits(b, lse[lo:lo + n]), (lo, n)
     for pos in (0, 1, 31, 32, 127, 128, 200, 255):
@@ -162,12 +164,14 @@ def test_lmhead_fp8_invariance(cuda, d):
         Hp[pos], hp[pos], yp[pos] = Hq_d[17], hs_d[17], y_d[17]
         a, _ = itl.lmhead_logprob_fp8(Hp, hp, Wq_d, ws_d, yp)
         assert same_bits(a[pos:pos + 1], lp[17:18]), pos
-    # narrow kernel (calls of at most 64 tokens): every row of a 64-token block
-    for pos in range(64):
-        Hp, hp, yp = Hq_d[:64].clone(), hs_d[:64].clone(), y_d[:64].clone()
-        Hp[pos], hp[pos], yp[pos] = Hq_d[17], hs_d[17], y_d[17]
-        a, _ = itl.lmhead_logprob_fp8(Hp, hp, Wq_d, ws_d, yp)
-        assert same_bits(a[pos:pos + 1], lp[17:18]), ("narrow", pos)
+    # narrow kernel: every row of a 64-token block (calls of at most 64
+    # tokens) and of the 128-token block (calls of 65 to 128)
+    for size in (64, 128):
+        for pos in range(size):
+            Hp, hp, yp = Hq_d[:size].clone(), hs_d[:size].clone(), y_d[:size].clone()
+            Hp[pos], hp[pos], yp[pos] = Hq_d[17], hs_d[17], y_d[17]
+            a, _ = itl.lmhead_logprob_fp8(Hp, hp, Wq_d, ws_d, yp)
+            assert same_bits(a[pos:pos + 1], lp[17:18]), ("narrow", size, pos)
     again = itl.lmhead_logprob_fp8(Hq_d, hs_d, Wq_d, ws_d, y_d)
     torch.cuda.synchronize()
     assert same_bits(again[0], lp) and same_bits(again[1], lse)
