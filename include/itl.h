@@ -297,7 +297,8 @@ itl_status itl_quantize_rows_mxfp4(const void* X, itl_dtype dtype, int64_t n_row
  *   z[t, v] = acc[t, v] * h_scale[t],
  *   acc[t, v] = sum_k e2m1(W)[v, k] 2^(e[v, k / 32]) e4m3(Hq[t, k]) (fp32)
  * then as itl_lmhead_logprob_fp8 (same slices, fold, combine and
- * determinism). d a multiple of 128; Hq, Wq4 16-byte aligned; workspace >=
+ * determinism; calls of at most 128 tokens run a narrow kernel with the same
+ * per-token arithmetic). d a multiple of 128; Hq, Wq4 16-byte aligned; workspace >=
  * itl_lmhead_logprob_workspace_bytes(n_tok, vocab), 256-byte aligned. */
 itl_status itl_lmhead_logprob_mxfp4(const uint8_t* Hq, const float* h_scale,
                                     const uint8_t* Wq4, const uint8_t* w_scale_codes,

@@ -482,12 +482,14 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_mxfp4_partial_kernel(
     if (c[bn].found) zy_out[t0 + wt * 128 + bn * 32 + col] = c[bn].zy;
 }
 
-// Decode-shaped MXFP4 calls (at most kNarrowMaxTokens tokens): 64-token
-// blocks, one workgroup per (token block, slice), run_tiles_narrow_mx4.
-// Lane l of wavefront (wv, wt) holds token t0 + 32 wt + (l mod 32) against
-// the same W rows, with the same MFMA fragments, scales and fold, as in
-// lmhead_mxfp4_partial_kernel, so the partials and logprobs have the same
-// bits.
+// Decode-shaped MXFP4 calls (at most kNarrow128MaxTokens tokens): kBRows-token
+// blocks (64, or one block of 128 for calls of 65 to 128 tokens), one
+// workgroup per (token block, slice), run_tiles_narrow_mx4<kBRows>. Lane l
+// of wavefront (wv, wt) holds tokens t0 + (kBRows / 2) wt + 32 bn + (l mod 32)
+// (bn < kBRows / 64) against the same W rows, with the same MFMA fragments,
+// scales and fold, as in lmhead_mxfp4_partial_kernel, so the partials and
+// logprobs have the same bits.
+template <int kBRows>
 __global__ __launch_bounds__(kThreads, 1) void lmhead_mxfp4_partial_narrow_kernel(
     const uint8_t* __restrict__ Hq, const float* __restrict__ h_scale, const uint8_t* __restrict__ Wq4,
     const uint8_t* __restrict__ w_sc, const int32_t* __restrict__ tokens, int n_tok, int d, int vocab, int n_slices,
@@ -497,15 +499,21 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_mxfp4_partial_narrow_kerne
   const int wv = L.wv, wt = L.wt, half = L.half, col = L.col;
   const int S = n_slices;
   const int slice = blockIdx.x % S;
-  const int t0 = (blockIdx.x / S) * kNarrowBRows;
+  constexpr int kBN = kBRows / 64;
+  const int t0 = (blockIdx.x / S) * kBRows;
   const int n_vt = (vocab + kBV - 1) / kBV;
   const int tile_begin = slice_tile(slice, n_vt, S);
   const int tile_end = slice_tile(slice + 1, n_vt, S);
   const int w_row_bytes = d / 2, s_row_bytes = d / 32, h_row_bytes = d;
   const int nks = d / 128;
-  const int tok = t0 + wt * 32 + col;
-  Col c = Col{tok < n_tok ? tokens[tok] : -1, -INFINITY, 0.0f, 0.0f, false};
-  const float hs = tok < n_tok ? h_scale[tok] : 0.0f;
+  Col c[kBN];
+  float hs[kBN];
+#pragma unroll
+  for (int bn = 0; bn < kBN; ++bn) {
+    const int tok = t0 + wt * (kBRows / 2) + bn * 32 + col;
+    c[bn] = Col{tok < n_tok ? tokens[tok] : -1, -INFINITY, 0.0f, 0.0f, false};
+    hs[bn] = tok < n_tok ? h_scale[tok] : 0.0f;
+  }
   auto w_rsrc = [&](int tile) {
     const int v0 = tile * kBV;
     return rsrc_words(Wq4 + (size_t)v0 * w_row_bytes, (uint32_t)min(kBV, vocab - v0) * w_row_bytes);
@@ -514,27 +522,32 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_mxfp4_partial_narrow_kerne
     const int v0 = tile * kBV;
     return rsrc_words(w_sc + (size_t)v0 * s_row_bytes, (uint32_t)min(kBV, vocab - v0) * s_row_bytes);
   };
-  const int4v hr =
-      rsrc_words(Hq + (size_t)t0 * h_row_bytes, (uint32_t)min(kNarrowBRows, n_tok - t0) * h_row_bytes);
-  auto epilogue = [&](int tile, floatx16 (&acc)[4]) {
+  const int4v hr = rsrc_words(Hq + (size_t)t0 * h_row_bytes, (uint32_t)min(kBRows, n_tok - t0) * h_row_bytes);
+  auto epilogue = [&](int tile, floatx16 (&acc)[4][kBN]) {
     const int vw = tile * kBV + wv * 128;
     mfma_result_wait();
     auto fold_tile = [&](auto partial) {
 #pragma unroll
-      for (int bm = 0; bm < 4; ++bm) {
-        floatx16 z;
+      for (int bn = 0; bn < kBN; ++bn)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) z[i] = acc_read(acc[bm], i) * hs;
-        fold_values(c, z, bm, vw, half, vocab, partial);
-      }
+        for (int bm = 0; bm < 4; ++bm) {
+          floatx16 z;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) z[i] = acc_read(acc[bm][bn], i) * hs[bn];
+          fold_values(c[bn], z, bm, vw, half, vocab, partial);
+        }
     };
     if (tile * kBV + kBV > vocab) fold_tile(std::true_type{});
     else fold_tile(std::false_type{});
   };
-  run_tiles_narrow_mx4(smem, L, w_row_bytes, s_row_bytes, h_row_bytes, tile_begin, tile_end, nks, w_rsrc, s_rsrc, hr,
-                       epilogue);
-  flush_slice(c, tok, n_tok, half, ((size_t)slice * 2 + wv) * n_tok + tok, part);
-  if (c.found) zy_out[tok] = c.zy;
+  run_tiles_narrow_mx4<kBRows>(smem, L, w_row_bytes, s_row_bytes, h_row_bytes, tile_begin, tile_end, nks, w_rsrc,
+                               s_rsrc, hr, epilogue);
+#pragma unroll
+  for (int bn = 0; bn < kBN; ++bn) {
+    const int tok = t0 + wt * (kBRows / 2) + bn * 32 + col;
+    flush_slice(c[bn], tok, n_tok, half, ((size_t)slice * 2 + wv) * n_tok + tok, part);
+    if (c[bn].found) zy_out[tok] = c[bn].zy;
+  }
 }
 
 }  // namespace
@@ -607,8 +620,11 @@ hipError_t launch_lmhead_logprob_mxfp4(const uint8_t* Hq, const float* h_scale, 
                                        align256((size_t)2 * S * (size_t)n_tok * sizeof(float2)));
   if (n_tok <= kNarrowMaxTokens) {
     const dim3 grid((unsigned)ceil_div(n_tok, kNarrowBRows) * (unsigned)S);
-    hipLaunchKernelGGL(lmhead_mxfp4_partial_narrow_kernel, grid, dim3(kThreads), 0, stream, Hq, h_scale, Wq4, w_sc,
-                       tokens, n_tok, d, vocab, S, part, zy);
+    hipLaunchKernelGGL((lmhead_mxfp4_partial_narrow_kernel<kNarrowBRows>), grid, dim3(kThreads), 0, stream, Hq,
+                       h_scale, Wq4, w_sc, tokens, n_tok, d, vocab, S, part, zy);
+  } else if (n_tok <= kNarrow128MaxTokens) {
+    hipLaunchKernelGGL((lmhead_mxfp4_partial_narrow_kernel<kNarrow128MaxTokens>), dim3((unsigned)S), dim3(kThreads), 0,
+                       stream, Hq, h_scale, Wq4, w_sc, tokens, n_tok, d, vocab, S, part, zy);
   } else {
     const dim3 grid((unsigned)ntb * (unsigned)n_slice_groups(n_tok, vocab));
     hipLaunchKernelGGL(lmhead_mxfp4_partial_kernel, grid, dim3(kThreads), 0, stream, Hq, h_scale, Wq4, w_sc, tokens,

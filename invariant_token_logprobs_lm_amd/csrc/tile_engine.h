@@ -578,22 +578,27 @@ __device__ __forceinline__ void run_tiles_mx4(uint4* smem, const Lanes& L, int w
 }
 
 // Narrow variant of run_tiles_mx4 for decode-shaped calls: the same W tiles
-// against a 64-row block of E4M3 token rows, wavefront (wv, wt) = 128 W rows
-// x 32 token rows. Every MFMA of an accumulator takes the same fragments and
-// scale bytes, in the same order, as in the wide engine (same W slot layout
-// and swizzle, same H chunk choice, same sub-step order), so each output
-// element has the same bits. Both operands rotate through 4 slots, loaded
-// three K steps ahead; all of a step's fragments are read up front.
-template <class ARsrc, class SRsrc, class Epi>
+// against a block of kBRows (64 or 128) E4M3 token rows, wavefront (wv, wt)
+// = 128 W rows x kBRows / 2 token rows (kBRows / 64 column blocks of 32).
+// Every MFMA of an accumulator takes the same fragments and scale bytes, in
+// the same order, as in the wide engine (same W slot layout and swizzle,
+// same H chunk choice, same sub-step order), so each output element has the
+// same bits. Both operands rotate through 4 slots, loaded three K steps
+// ahead; all of a step's fragments are read up front.
+template <int kBRows, class ARsrc, class SRsrc, class Epi>
 __device__ __forceinline__ void run_tiles_narrow_mx4(uint4* smem, const Lanes& L, int w_row_bytes, int s_row_bytes,
                                                      int h_row_bytes, int tile_begin, int tile_end, int nks,
                                                      const ARsrc& a_rsrc, const SRsrc& s_rsrc, int4v b_rsrc,
                                                      Epi&& epi) {
   const int lane = L.lane, wave = L.wave, wv = L.wv, wt = L.wt, half = L.half, col = L.col;
   const int lr = lane >> 3;
-  constexpr int kLoads = kMx4WDataLoads + 1 + kNarrowBDmaPerWave;  // loads per wavefront per step
+  static_assert(kBRows == 64 || kBRows == 128, "token block of 64 or 128 rows");
+  constexpr int kBN = kBRows / 64;                     // 32-row column blocks per wavefront
+  constexpr int kBDma = kBRows / 4 / kDmaRows;         // token-row loads per wavefront per step
+  constexpr int kBSlotChunks = kBRows * kRowChunks;
+  constexpr int kLoads = kMx4WDataLoads + 1 + kBDma;  // loads per wavefront per step
   constexpr int kHBase = kNarrowSlots * kMx4WSlotBytes;
-  static_assert(kHBase + kNarrowSlots * kNarrowBSlotChunks * 16 <= kEngineSmemChunks * 16, "LDS budget");
+  static_assert(kHBase + kNarrowSlots * kBSlotChunks * 16 <= kEngineSmemChunks * 16, "LDS budget");
   uint32_t wvoff[kMx4WDataLoads];
 #pragma unroll
   for (int j = 0; j < kMx4WDataLoads; ++j) {
@@ -601,19 +606,21 @@ __device__ __forceinline__ void run_tiles_narrow_mx4(uint4* smem, const Lanes& L
     wvoff[j] = (uint32_t)row * (uint32_t)w_row_bytes + (uint32_t)(((lane & 3) ^ swz4(row)) * 16);
   }
   const uint32_t svoff = (uint32_t)(wave * 64 + lane) * (uint32_t)s_row_bytes;
-  uint32_t hvoff[kNarrowBDmaPerWave];
+  uint32_t hvoff[kBDma];
 #pragma unroll
-  for (int j = 0; j < kNarrowBDmaPerWave; ++j)
-    hvoff[j] = (uint32_t)(wave * 16 + j * kDmaRows + lr) * (uint32_t)h_row_bytes + (((lane & 7) ^ lr ^ (j & 1)) * 16);
+  for (int j = 0; j < kBDma; ++j)
+    hvoff[j] = (uint32_t)(wave * (kBRows / 4) + j * kDmaRows + lr) * (uint32_t)h_row_bytes +
+               (((lane & 7) ^ lr ^ (j & 1)) * 16);
   const uint32_t lds0 = (uint32_t)(size_t)((__attribute__((address_space(3))) uint4*)smem);
   auto w_slot = [&](int slot) { return lds0 + (uint32_t)slot * kMx4WSlotBytes; };
-  auto h_slot = [&](int slot) { return lds0 + (uint32_t)kHBase + (uint32_t)slot * kNarrowBSlotChunks * 16; };
+  auto h_slot = [&](int slot) { return lds0 + (uint32_t)kHBase + (uint32_t)slot * kBSlotChunks * 16; };
   constexpr uint32_t kWStepBytes = 64;  // W bytes per row per K step
   auto load_step = [&](int tile, int ks, int slot) {
     const int4v ar = a_rsrc(tile);
 #pragma unroll
-    for (int j = 0; j < kNarrowBDmaPerWave; ++j)
-      dma16(b_rsrc, hvoff[j], (uint32_t)ks * kStepBytes, h_slot(slot) + (uint32_t)wave * 16 * kStepBytes + j * 1024);
+    for (int j = 0; j < kBDma; ++j)
+      dma16(b_rsrc, hvoff[j], (uint32_t)ks * kStepBytes,
+            h_slot(slot) + (uint32_t)wave * (kBRows / 4) * kStepBytes + j * 1024);
 #pragma unroll
     for (int j = 0; j < kMx4WDataLoads; ++j)
       dma16(ar, wvoff[j], (uint32_t)ks * kWStepBytes, w_slot(slot) + (uint32_t)wave * 64 * kWStepBytes + j * 1024);
@@ -633,31 +640,37 @@ __device__ __forceinline__ void run_tiles_narrow_mx4(uint4* smem, const Lanes& L
     next_load();
   }
   // Fragment offsets (uint4 units from a slot's base), as in run_tiles_mx4.
-  int a_off[2], b_off[2][2];
+  int a_off[2], b_off[kBN][2][2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int ra = wv * 128 + col;
     a_off[j] = ra * kMx4RowChunks + ((2 * j + half) ^ swz4(ra));
 #pragma unroll
-    for (int p = 0; p < 2; ++p) b_off[j][p] = (wt * 32 + col) * kRowChunks + ((4 * j + 2 * p + half) ^ swz(col));
+    for (int n = 0; n < kBN; ++n)
+#pragma unroll
+      for (int p = 0; p < 2; ++p)
+        b_off[n][j][p] = (wt * (kBRows / 2) + n * 32 + col) * kRowChunks + ((4 * j + 2 * p + half) ^ swz(col));
   }
   constexpr int kPending = (kNarrowSlots - 2) * kLoads;
   int slot = 0;
-  auto k_step = [&](floatx16 (&acc)[4], auto first) {
+  auto k_step = [&](floatx16 (&acc)[4][kBN], auto first) {
     wait_and_barrier<kPending>();
     load_step(ld_tile, ld_ks, slot == 0 ? kNarrowSlots - 1 : slot - 1);
     next_load();
     const uint4* sa = smem + (slot * kMx4WSlotBytes) / 16;
-    const uint4* sb = smem + (kHBase + slot * kNarrowBSlotChunks * 16) / 16;
+    const uint4* sb = smem + (kHBase + slot * kBSlotChunks * 16) / 16;
     uint4 A[2][4];
-    Frag8 B[2];
+    Frag8 B[2][kBN];
     uint32_t SC[4];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
 #pragma unroll
       for (int m = 0; m < 4; ++m) A[j][m] = sa[a_off[j] + m * 32 * kMx4RowChunks];
-      B[j].lo = sb[b_off[j][0]];
-      B[j].hi = sb[b_off[j][1]];
+#pragma unroll
+      for (int n = 0; n < kBN; ++n) {
+        B[j][n].lo = sb[b_off[n][j][0]];
+        B[j][n].hi = sb[b_off[n][j][1]];
+      }
     }
     const uint32_t* ss = reinterpret_cast<const uint32_t*>(smem) + (slot * kMx4WSlotBytes + kMx4WDataBytes) / 4;
 #pragma unroll
@@ -668,15 +681,18 @@ __device__ __forceinline__ void run_tiles_narrow_mx4(uint4* smem, const Lanes& L
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         const int sbyte = (int)((SC[m] >> (8 * (2 * j + half))) & 0xffu);
-        if (decltype(first)::value && j == 0) mma_mx4_first(acc[m], A[j][m], B[j], sbyte);
-        else mma_mx4(acc[m], A[j][m], B[j], sbyte);
+#pragma unroll
+        for (int n = 0; n < kBN; ++n) {
+          if (decltype(first)::value && j == 0) mma_mx4_first(acc[m][n], A[j][m], B[j][n], sbyte);
+          else mma_mx4(acc[m][n], A[j][m], B[j][n], sbyte);
+        }
       }
     slot = slot == kNarrowSlots - 1 ? 0 : slot + 1;
   };
   using T = std::true_type;
   using F = std::false_type;
   for (int tile = tile_begin; tile < tile_end; ++tile) {
-    floatx16 acc[4];
+    floatx16 acc[4][kBN];
     k_step(acc, T{});
     for (int ks = 1; ks < nks; ++ks) k_step(acc, F{});
     epi(tile, acc);

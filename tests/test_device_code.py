@@ -69,6 +69,7 @@ def test_inline_asm_loads_write_lds_only(tmp_path, src):
     ("fp8.hip", "lmhead_fp8_partial8_kernelILb1E"),
     ("fp8.hip", "lmhead_fp8_partial_narrow_kernel"),
     ("fp8.hip", "lmhead_mxfp4_partial_kernel"),
+    ("fp8.hip", "lmhead_mxfp4_partial_narrow_kernel"),
     ("backward.hip", "dlogits_kernelILi0E"),  # the backward's contractions, on the eight-wavefront engine
     ("backward.hip", "dh_kernelILi0E"),
     ("backward.hip", "dw_kernelILi0E"),

@@ -252,7 +252,9 @@ def _oracle_mxfp4_head(n_tok, d, vocab, seed, w_std=0.05):
 
 @pytest.mark.parametrize("n_tok,d,vocab", [
     (700, 256, 5000), (300, 128, 4096 + 37), (1, 128, 300), (64, 256, 3000), (513, 384, 8192 + 256),
-    (5200, 128, 150 * 256 - 17)])
+    (5200, 128, 150 * 256 - 17),
+    (65, 128, 1000), (100, 256, 200), (128, 384, 3000),  # the 128-token narrow block
+    (129, 128, 1000)])                                   # the fewest tokens of the wide kernel
 def test_lmhead_mxfp4_parity(cuda, n_tok, d, vocab):
     from oracle import fp8
 
@@ -275,7 +277,7 @@ def test_lmhead_mxfp4_invariance(cuda):
     itl = _itl()
     Hq_d, hs_d, Wq_d, ws_d, y_d = _to_dev(cuda, Hq, hs, Wq, ws, y)
     lp, lse = itl.lmhead_logprob_mxfp4(Hq_d, hs_d, Wq_d, ws_d, y_d)
-    for lo, n in ((0, 1), (17, 5), (100, 64), (300, 257)):
+    for lo, n in ((0, 1), (17, 5), (100, 64), (150, 65), (200, 128), (330, 129), (300, 257)):
         a, b = itl.lmhead_logprob_mxfp4(Hq_d[lo:lo + n], hs_d[lo:lo + n], Wq_d, ws_d, y_d[lo:lo + n])
         assert same_bits(a, lp[lo:lo + n]) and same_bits(b, lse[lo:lo + n]), (lo, n)
     for pos in (0, 31, 32, 128, 255):
@@ -283,12 +285,14 @@ def test_lmhead_mxfp4_invariance(cuda):
         Hp[pos], hp[pos], yp[pos] = Hq_d[17], hs_d[17], y_d[17]
         a, _ = itl.lmhead_logprob_mxfp4(Hp, hp, Wq_d, ws_d, yp)
         assert same_bits(a[pos:pos + 1], lp[17:18]), pos
-    # narrow kernel (calls of at most 64 tokens): every row of a 64-token block
-    for pos in range(64):
-        Hp, hp, yp = Hq_d[:64].clone(), hs_d[:64].clone(), y_d[:64].clone()
-        Hp[pos], hp[pos], yp[pos] = Hq_d[17], hs_d[17], y_d[17]
-        a, _ = itl.lmhead_logprob_mxfp4(Hp, hp, Wq_d, ws_d, yp)
-        assert same_bits(a[pos:pos + 1], lp[17:18]), ("narrow", pos)
+    # narrow kernel: every row of a 64-token block (calls of at most 64
+    # tokens) and of the 128-token block (calls of 65 to 128)
+    for size in (64, 128):
+        for pos in range(size):
+            Hp, hp, yp = Hq_d[:size].clone(), hs_d[:size].clone(), y_d[:size].clone()
+            Hp[pos], hp[pos], yp[pos] = Hq_d[17], hs_d[17], y_d[17]
+            a, _ = itl.lmhead_logprob_mxfp4(Hp, hp, Wq_d, ws_d, yp)
+            assert same_bits(a[pos:pos + 1], lp[17:18]), ("narrow", size, pos)
     again = itl.lmhead_logprob_mxfp4(Hq_d, hs_d, Wq_d, ws_d, y_d)
     torch.cuda.synchronize()
     assert same_bits(again[0], lp) and same_bits(again[1], lse)
