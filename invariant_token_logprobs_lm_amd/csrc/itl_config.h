@@ -1,13 +1,15 @@
 // Compile-time shape constants of the library's arithmetic.
 //
 // Everything that fixes a reduction order lives here and nowhere else: the
-// token block, the vocabulary tile, the K step, and the vocabulary slice
-// width. None of them depends on the number of tokens in a call, which is
-// what makes a token's result independent of its batch-mates and of the
-// prefill/decode split ("vLLM Train-Inference Consistency Release Notes",
-// section "Achieving Bitwise Consistency": batch independence and phase
-// consistency). Changing any of them changes result bits, so they are part
-// of itl_build_info().
+// vocabulary tile and the vocabulary slice width (the order in which a
+// token's logits are folded), the K step, and the token block, which only
+// shapes the schedule (the narrow kernels' 64- and 128-token blocks give
+// the 256-token block's bits). None of them depends on the number of tokens
+// in a call, which is what makes a token's result independent of its
+// batch-mates and of the prefill/decode split ("vLLM Train-Inference
+// Consistency Release Notes", section "Achieving Bitwise Consistency": batch
+// independence and phase consistency). They are part of itl_build_info(),
+// since a change to the tile or the slices changes result bits.
 #pragma once
 
 #include <hip/hip_runtime.h>
